@@ -1,0 +1,211 @@
+"""fp64 CPU oracle of the KDA decode step (ctypes wrapper of kda_oracle.c).
+
+TEST INFRASTRUCTURE ONLY: imported by the test suite, by the package smoke
+check and by the benchmark's cpu_baseline leg, never by the product path.
+It shares no code with the HIP path; it imports neither the package nor its
+C library.
+
+Every function takes host arrays (numpy, or CPU torch tensors which are
+viewed as numpy without arithmetic), copies what it updates, and returns
+the results.  bf16 data travel as their uint16 bit patterns.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "kda_oracle.c")
+_LIB = os.path.join(_HERE, "libkda_oracle.so")
+
+F32, BF16, F64 = 0, 1, 2
+D = 128
+SCALE = 1.0 / math.sqrt(D)   # fixed output scale (packed decode exact contract)
+L2_EPS = 1e-6                # fixed L2 epsilon (packed decode exact contract)
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc -O2 (no fast-math)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.run(["gcc", "-O2", "-std=c11", "-Wall", "-fPIC", "-shared",
+                        "-o", tmp, _SRC, "-lm"], check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        lib = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        I64 = ctypes.c_int64
+        Dbl = ctypes.c_double
+        Int = ctypes.c_int
+        lib.kdao_recurrent.restype = Int
+        lib.kdao_recurrent.argtypes = [I64, I64, I64, P, P, P, P, P, P, P, Dbl, Dbl,
+                                       P, P, I64, Int, P, P, P, Int, P, P]
+        lib.kdao_fused.restype = Int
+        lib.kdao_fused.argtypes = [I64, I64, P, P, I64, P, I64, P, P, P, P, P, Int, P,
+                                   P, P, Dbl, Dbl, Dbl, P, P, P, P]
+        lib.kdao_bf16_from_f64_n.restype = None
+        lib.kdao_bf16_from_f64_n.argtypes = [P, P, I64]
+        _lib = lib
+    return _lib
+
+
+# ---- array helpers (no arithmetic) -------------------------------------------
+
+def as_np(x):
+    """numpy view of a CPU array / tensor; bf16 tensors become uint16 bits."""
+    if x is None:
+        return None
+    if isinstance(x, np.ndarray):
+        return x
+    import torch  # only for converting CPU tensors
+    t = x.detach()
+    if t.device.type != "cpu":
+        raise ValueError("the oracle takes host arrays")
+    if t.dtype == torch.bfloat16:
+        return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+    return t.contiguous().numpy()
+
+
+def _c(a, dtype):
+    a = np.ascontiguousarray(as_np(a))
+    if a.dtype != dtype:
+        raise TypeError(f"expected {np.dtype(dtype)}, got {a.dtype}")
+    return a
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _dtype_code(a):
+    if a.dtype == np.float32:
+        return F32
+    if a.dtype == np.uint16:
+        return BF16
+    if a.dtype == np.float64:
+        return F64
+    raise TypeError(f"unsupported state dtype {a.dtype}")
+
+
+_NP_OF = {F32: np.float32, BF16: np.uint16, F64: np.float64}
+
+
+def bf16_from_f64(x) -> np.ndarray:
+    """Round doubles to bf16 (nearest, ties to even); returns uint16 bits."""
+    x = np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+    out = np.empty(x.shape, dtype=np.uint16)
+    _load().kdao_bf16_from_f64_n(_ptr(x), _ptr(out), x.size)
+    return out
+
+
+def bf16_to_f64(bits) -> np.ndarray:
+    """Exact widening of bf16 bit patterns."""
+    b = np.asarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+# ---- entry points --------------------------------------------------------------
+
+def recurrent(q, k, v, g, beta, A_log, dt_bias, state, state_indices,
+              cu_seqlens=None, *, scale=SCALE, l2_eps=L2_EPS, ckpt_dtype=None,
+              want_ckpt64=False):
+    """Recurrent KDA (T=1, or ragged packed T>=0 when cu_seqlens is given).
+
+    q, k, v, g: bf16 [T, H, 128]; beta: bf16 [T, H]; A_log fp32 [H];
+    dt_bias fp32 [H*128]; state [slots, H, 128, 128] (fp32, bf16 bits or
+    float64); state_indices int32 [N]; cu_seqlens int32 [N+1] or None.
+    Returns dict(out64, out_bf16, state, ckpt, ckpt64).
+    """
+    q = _c(q, np.uint16); k = _c(k, np.uint16); v = _c(v, np.uint16)
+    g = _c(g, np.uint16); beta = _c(beta, np.uint16)
+    A_log = _c(A_log, np.float32); dt_bias = _c(dt_bias, np.float32)
+    st = np.array(as_np(state), copy=True, order="C")
+    sdt = _dtype_code(st)
+    idx = _c(state_indices, np.int32)
+    cu = None if cu_seqlens is None else _c(cu_seqlens, np.int32)
+    T, H = q.shape[0], q.shape[1]
+    N = idx.shape[0]
+    assert q.shape == (T, H, D) and beta.shape == (T, H) and st.shape[1:] == (H, D, D)
+    out64 = np.zeros((T, H, D), np.float64)
+    outb = np.zeros((T, H, D), np.uint16)
+    ckpt = None
+    cdt = 0
+    if ckpt_dtype is not None:
+        cdt = ckpt_dtype
+        ckpt = np.zeros((T, H, D, D), _NP_OF[cdt])
+    ck64 = np.zeros((T, H, D, D), np.float64) if want_ckpt64 else None
+    rc = _load().kdao_recurrent(T, N, H, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                _ptr(A_log), _ptr(dt_bias), float(scale), float(l2_eps),
+                                _ptr(cu), _ptr(idx), st.shape[0], sdt, _ptr(st),
+                                _ptr(out64), _ptr(outb), cdt, _ptr(ckpt), _ptr(ck64))
+    if rc != 0:
+        raise ValueError(f"kdao_recurrent rejected its arguments ({rc})")
+    return dict(out64=out64, out_bf16=outb, state=st, ckpt=ckpt, ckpt64=ck64)
+
+
+def packed(mixed_qkv, raw_gate, raw_beta, A_log, dt_bias, state, state_indices):
+    """Packed T=1 decode: split the q|k|v projection row (q at [0, H*128),
+    k at [H*128, 2*H*128), v at [2*H*128, 3*H*128)) and run the recurrence
+    with the fixed scale and L2 epsilon; -1 rows are inactive."""
+    qkv = as_np(mixed_qkv)
+    B = qkv.shape[0]
+    H = np.asarray(as_np(A_log)).shape[0]
+    HC = H * D
+    q = qkv[:, 0:HC].reshape(B, H, D)
+    k = qkv[:, HC:2 * HC].reshape(B, H, D)
+    v = qkv[:, 2 * HC:3 * HC].reshape(B, H, D)
+    g = as_np(raw_gate).reshape(B, H, D)
+    beta = as_np(raw_beta).reshape(B, H)
+    return recurrent(q, k, v, g, beta, A_log, dt_bias, state, state_indices)
+
+
+def fused(x, weight, conv_state, raw_gate, raw_beta, A_log, dt_bias, state_indices,
+          state, output_gate, norm_weight, *, norm_eps=1e-5, scale=SCALE,
+          l2_eps=L2_EPS):
+    """Fused decode: conv + SiLU, one KDA token, gated RMSNorm.
+
+    conv_state is the logical [slots, 3*H*128, 3] cache; it is handed to C as
+    a contiguous [slots, 3, 3*H*128] copy (position-major, the pages' layout).
+    Returns dict(out64, out_bf16, o_pre64, act64, state, conv_state) where
+    conv_state is again logical [slots, 3*H*128, 3].
+    """
+    xa = _c(x, np.uint16)
+    rows, C3 = xa.shape
+    H = C3 // (3 * D)
+    cs_log = as_np(conv_state)                       # [slots, C3, 3]
+    cs = np.ascontiguousarray(np.transpose(cs_log, (0, 2, 1)))  # [slots, 3, C3]
+    st = np.array(as_np(state), copy=True, order="C")
+    sdt = _dtype_code(st)
+    w = _c(weight, np.float32)
+    gr = _c(as_np(raw_gate).reshape(rows, H, D), np.uint16)
+    br = _c(as_np(raw_beta).reshape(rows, H), np.uint16)
+    og = _c(as_np(output_gate).reshape(rows, H, D), np.uint16)
+    nw = _c(norm_weight, np.float32)
+    idx = _c(state_indices, np.int32)
+    A_log = _c(A_log, np.float32); dt_bias = _c(dt_bias, np.float32)
+    out64 = np.zeros((rows, H, D), np.float64)
+    outb = np.zeros((rows, H, D), np.uint16)
+    opre = np.zeros((rows, H, D), np.float64)
+    act = np.zeros((rows, C3), np.float64)
+    rc = _load().kdao_fused(rows, H, _ptr(xa), _ptr(w), cs.shape[0], _ptr(cs), 3 * C3,
+                            _ptr(gr), _ptr(br), _ptr(A_log), _ptr(dt_bias), _ptr(idx),
+                            sdt, _ptr(st), _ptr(og), _ptr(nw), float(norm_eps),
+                            float(scale), float(l2_eps), _ptr(out64), _ptr(outb),
+                            _ptr(opre), _ptr(act))
+    if rc != 0:
+        raise ValueError(f"kdao_fused rejected its arguments ({rc})")
+    return dict(out64=out64, out_bf16=outb, o_pre64=opre, act64=act, state=st,
+                conv_state=np.transpose(cs, (0, 2, 1)))

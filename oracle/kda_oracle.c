@@ -1,0 +1,369 @@
+/*
+ * kda_oracle.c -- plain fp64 CPU reference of the KDA decode step.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the package smoke check
+ * and the benchmark's cpu_baseline leg may load this library.  It shares
+ * no code, header, table or helper with the HIP path and must never be
+ * used to produce a product result.
+ *
+ * Everything is evaluated in double precision with straightforward loops,
+ * in the order the method states it; there is no blocking, fusion or
+ * reordering.  bf16 inputs are widened exactly; results are rounded to the
+ * storage format (bf16 round-to-nearest-even, or fp32 round-to-nearest)
+ * only when they are written back, and are also returned unrounded.
+ *
+ * Sources (the flashinfer KDA decode pages):
+ *  - "flashinfer.kda_decode" API page: recurrent_kda / packed_kda_decode /
+ *    fused_kda_decode function table; the backend="cake" section (Kimi-Linear
+ *    equal-head schedules evaluate -exp(A_log) * softplus(g + dt_bias) and a
+ *    beta sigmoid in-kernel); the "Serving-native packed Kimi K3 decode"
+ *    section (fused Q/K extraction and L2 normalisation, -1 inactive rows
+ *    emit zeros without touching state).
+ *  - "flashinfer.kda_decode.fused_kda_decode" page, Parameters: conv weight
+ *    [3, 4, H*128], conv_state [num_slots, 3*H*128, 3] with strides
+ *    [slot_stride, 1, 3*H*128], non-positive indices are null, the state is
+ *    evaluated in fp32 and a bf16 state is rounded when written back,
+ *    gated RMSNorm with output_gate logits and norm_weight[128].
+ *  - "feat(cake_kda): add serving-native packed decode backend", Exact
+ *    contract: scale 1/sqrt(128), L2 epsilon 1e-6.
+ *  - "feat(kda): add fused speculative decode kernel" (#4809), Description and
+ *    walkthrough: packed ragged T>=2 decode with per-token state checkpoints.
+ *
+ * The recurrence is Kimi Delta Attention (a gated delta rule with one decay
+ * per key channel).  With S the K x V state of one (sequence, head):
+ *     S <- diag(exp(g)) S;   u = v - S^T k;   S <- S + beta k u^T;
+ *     o = scale * S^T q
+ * with q, k L2-normalised.  Readings where the pages are silent:
+ *  - the pool stores S transposed: pool[slot][h][v][k] = S[k][v]
+ *    (the pages speak of value rows / value-row splits of the state);
+ *  - L2 norm is x / sqrt(sum x^2 + eps);
+ *  - the readout uses the updated state;
+ *  - conv: history [c0, c1, c2, x] (oldest first) against taps 0..3, no
+ *    bias, SiLU after; the cache afterwards holds [c1, c2, x];
+ *  - gated RMSNorm: y = o / sqrt(mean(o^2) + eps) * w * sigmoid(gate) on the
+ *    unrounded o;
+ *  - a null row (index < 0, or <= 0 for the fused call, or >= num_slots)
+ *    yields +0 outputs and writes no state, cache or checkpoint.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define KD 128 /* K = V = 128 */
+
+enum { KDAO_F32 = 0, KDAO_BF16 = 1, KDAO_F64 = 2 };
+
+/* ---- bf16 storage format ------------------------------------------------ */
+
+static double bf16_to_f64(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* Nearest bf16 (8 significant bits, fp32 exponent range) to x, ties to
+ * even, computed directly from the double (no intermediate fp32 rounding). */
+uint16_t kdao_bf16_from_f64(double x)
+{
+    double r;
+    if (isnan(x)) return 0x7FC0;
+    if (x == 0.0 || isinf(x)) {
+        r = x;
+    } else {
+        double ax = fabs(x);
+        if (ax < 0x1p-126) {
+            /* subnormal range: quantum 2^-133 */
+            r = nearbyint(x * 0x1p133) * 0x1p-133;
+        } else {
+            int e;
+            double m = frexp(x, &e);          /* x = m * 2^e, 0.5 <= |m| < 1 */
+            double q = nearbyint(m * 256.0);  /* 8 significant bits, RNE */
+            r = ldexp(q, e - 8);
+        }
+        /* 0x1.FEp127 is the largest bf16; anything rounding above it is inf */
+        if (fabs(r) > 0x1.FEp127) r = copysign(INFINITY, x);
+    }
+    float f = (float)r; /* exact: r is representable in bf16 */
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return (uint16_t)(u >> 16);
+}
+
+static double load_elem(const void *p, int dt, size_t i)
+{
+    switch (dt) {
+    case KDAO_F32: return (double)((const float *)p)[i];
+    case KDAO_BF16: return bf16_to_f64(((const uint16_t *)p)[i]);
+    default: return ((const double *)p)[i];
+    }
+}
+
+static void store_elem(void *p, int dt, size_t i, double x)
+{
+    switch (dt) {
+    case KDAO_F32: ((float *)p)[i] = (float)x; break; /* round to nearest */
+    case KDAO_BF16: ((uint16_t *)p)[i] = kdao_bf16_from_f64(x); break;
+    default: ((double *)p)[i] = x; break;
+    }
+}
+
+/* ---- scalar functions ---------------------------------------------------- */
+
+static double softplus(double x) { return fmax(x, 0.0) + log1p(exp(-fabs(x))); }
+static double sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
+
+/* x / sqrt(sum x^2 + eps) over one 128-vector */
+static void l2_normalise(const double *x, double eps, double *out)
+{
+    double ss = 0.0;
+    for (int i = 0; i < KD; ++i) ss += x[i] * x[i];
+    double inv = 1.0 / sqrt(ss + eps);
+    for (int i = 0; i < KD; ++i) out[i] = x[i] * inv;
+}
+
+/* Gate transform of the Kimi-Linear KDA layer:
+ *   g_k = -exp(A_log[h]) * softplus(raw_k + dt_bias[h*128 + k]),  decay = exp(g) */
+static void gate_decay(const double *raw, double A_log_h, const float *dt_bias_h,
+                       double *decay)
+{
+    double a = exp(A_log_h);
+    for (int i = 0; i < KD; ++i) {
+        double g = -a * softplus(raw[i] + (double)dt_bias_h[i]);
+        decay[i] = exp(g);
+    }
+}
+
+/* One token of the recurrence on S[k][v] (math orientation, K x V).
+ * qh, kh are the L2-normalised vectors; o receives scale * S'^T q. */
+static void kda_token(double S[KD][KD], const double *qh, const double *kh,
+                      const double *v, const double *decay, double beta,
+                      double scale, double *o)
+{
+    /* S <- diag(exp g) S : row k of S scaled by decay[k] */
+    for (int k = 0; k < KD; ++k)
+        for (int j = 0; j < KD; ++j) S[k][j] *= decay[k];
+    /* u = v - S^T k */
+    double u[KD];
+    for (int j = 0; j < KD; ++j) {
+        double acc = 0.0;
+        for (int k = 0; k < KD; ++k) acc += S[k][j] * kh[k];
+        u[j] = v[j] - acc;
+    }
+    /* S <- S + beta k u^T */
+    for (int k = 0; k < KD; ++k)
+        for (int j = 0; j < KD; ++j) S[k][j] += beta * kh[k] * u[j];
+    /* o = scale * S^T q */
+    for (int j = 0; j < KD; ++j) {
+        double acc = 0.0;
+        for (int k = 0; k < KD; ++k) acc += S[k][j] * qh[k];
+        o[j] = scale * acc;
+    }
+}
+
+/* pool[slot][h][v][k] holds S[k][v] */
+static void gather_state(const void *pool, int dt, size_t head_base, double S[KD][KD])
+{
+    for (int v = 0; v < KD; ++v)
+        for (int k = 0; k < KD; ++k)
+            S[k][v] = load_elem(pool, dt, head_base + (size_t)v * KD + k);
+}
+
+static void scatter_state(void *pool, int dt, size_t head_base, double S[KD][KD])
+{
+    for (int v = 0; v < KD; ++v)
+        for (int k = 0; k < KD; ++k)
+            store_elem(pool, dt, head_base + (size_t)v * KD + k, S[k][v]);
+}
+
+static void widen_bf16(const uint16_t *src, double *dst, int n)
+{
+    for (int i = 0; i < n; ++i) dst[i] = bf16_to_f64(src[i]);
+}
+
+/*
+ * Recurrent KDA: T=1 (cu_seqlens == NULL, one token per sequence) or packed
+ * ragged T>=0 per sequence (cu_seqlens [n_seqs+1], tokens processed in
+ * order with the state carried between them).
+ *
+ * Layouts (all contiguous, host memory):
+ *   q, k, v, graw: bf16 [n_tokens][H][128];  braw: bf16 [n_tokens][H]
+ *   A_log fp32 [H];  dt_bias fp32 [H*128]
+ *   state: [num_slots][H][128 v][128 k] of state_dtype, updated in place
+ *   out64 (may be NULL) double [n_tokens][H][128];  out_bf16 (may be NULL)
+ *   ckpt (may be NULL): [n_tokens][H][128 v][128 k] of ckpt_dtype, the state
+ *   after each token;  ckpt64 (may be NULL) the same in double.
+ * Returns 0, or -1 on inconsistent metadata.
+ */
+int kdao_recurrent(int64_t n_tokens, int64_t n_seqs, int64_t H,
+                   const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                   const uint16_t *graw, const uint16_t *braw,
+                   const float *A_log, const float *dt_bias,
+                   double scale, double l2_eps,
+                   const int32_t *cu_seqlens, const int32_t *state_indices,
+                   int64_t num_slots, int state_dtype, void *state,
+                   double *out64, uint16_t *out_bf16,
+                   int ckpt_dtype, void *ckpt, double *ckpt64)
+{
+    if (n_tokens < 0 || n_seqs < 0 || H <= 0) return -1;
+    if (!cu_seqlens && n_tokens != n_seqs) return -1;
+    if (cu_seqlens) {
+        if (cu_seqlens[0] != 0 || cu_seqlens[n_seqs] != n_tokens) return -1;
+        for (int64_t i = 0; i < n_seqs; ++i)
+            if (cu_seqlens[i + 1] < cu_seqlens[i]) return -1;
+    }
+    double (*S)[KD] = malloc(sizeof(double) * KD * KD);
+    if (!S) return -2;
+    double qv[KD], kv[KD], vv[KD], gv[KD], qh[KD], kh[KD], dec[KD], o[KD];
+
+    const size_t head_elems = (size_t)KD * KD;
+    for (int64_t i = 0; i < n_seqs; ++i) {
+        int64_t t0 = cu_seqlens ? cu_seqlens[i] : i;
+        int64_t t1 = cu_seqlens ? cu_seqlens[i + 1] : i + 1;
+        int32_t idx = state_indices[i];
+        int null_row = idx < 0 || (int64_t)idx >= num_slots;
+        for (int64_t h = 0; h < H; ++h) {
+            if (null_row) {
+                for (int64_t t = t0; t < t1; ++t)
+                    for (int j = 0; j < KD; ++j) {
+                        size_t oi = ((size_t)t * H + h) * KD + j;
+                        if (out64) out64[oi] = 0.0;
+                        if (out_bf16) out_bf16[oi] = 0;
+                    }
+                continue;
+            }
+            if (t1 == t0) continue; /* empty sequence: nothing read or written */
+            size_t head_base = ((size_t)idx * H + h) * head_elems;
+            gather_state(state, state_dtype, head_base, S);
+            for (int64_t t = t0; t < t1; ++t) {
+                size_t vec = ((size_t)t * H + h) * KD;
+                widen_bf16(q + vec, qv, KD);
+                widen_bf16(k + vec, kv, KD);
+                widen_bf16(v + vec, vv, KD);
+                widen_bf16(graw + vec, gv, KD);
+                double beta = sigmoid(bf16_to_f64(braw[(size_t)t * H + h]));
+                l2_normalise(qv, l2_eps, qh);
+                l2_normalise(kv, l2_eps, kh);
+                gate_decay(gv, (double)A_log[h], dt_bias + h * KD, dec);
+                kda_token(S, qh, kh, vv, dec, beta, scale, o);
+                for (int j = 0; j < KD; ++j) {
+                    if (out64) out64[vec + j] = o[j];
+                    if (out_bf16) out_bf16[vec + j] = kdao_bf16_from_f64(o[j]);
+                }
+                size_t cb = ((size_t)t * H + h) * head_elems;
+                if (ckpt) scatter_state(ckpt, ckpt_dtype, cb, S);
+                if (ckpt64) scatter_state(ckpt64, KDAO_F64, cb, S);
+            }
+            scatter_state(state, state_dtype, head_base, S);
+        }
+    }
+    free(S);
+    return 0;
+}
+
+/*
+ * Fused decode: width-4 depthwise causal conv + SiLU over the packed
+ * q|k|v projection, one KDA token, gated RMSNorm.
+ *
+ *   x bf16 [rows][3*H*128];  weight fp32 [3][4][H*128]
+ *   conv_state bf16, slot s, position p, channel c at
+ *       conv_state[s*conv_slot_stride + p*3*H*128 + c]   (updated in place)
+ *   graw bf16 [rows][H][128];  braw bf16 [rows][H]
+ *   state [num_slots][H][128 v][128 k] of state_dtype (updated in place)
+ *   ogate bf16 [rows][H][128];  norm_weight fp32 [128]
+ *   out64 / out_bf16: [rows][H][128] (either may be NULL)
+ *   o_pre64 (may be NULL): [rows][H][128] the recurrence output before norm
+ *   act64 (may be NULL): [rows][3*H*128] the post-SiLU conv activations
+ */
+int kdao_fused(int64_t rows, int64_t H, const uint16_t *x, const float *weight,
+               int64_t num_slots, uint16_t *conv_state, int64_t conv_slot_stride,
+               const uint16_t *graw, const uint16_t *braw,
+               const float *A_log, const float *dt_bias,
+               const int32_t *state_indices, int state_dtype, void *state,
+               const uint16_t *ogate, const float *norm_weight, double norm_eps,
+               double scale, double l2_eps,
+               double *out64, uint16_t *out_bf16, double *o_pre64, double *act64)
+{
+    if (rows < 0 || H <= 0) return -1;
+    const int64_t HC = H * KD;     /* channels per q/k/v group */
+    const int64_t C3 = 3 * HC;     /* channels of the packed projection */
+    if (conv_slot_stride < 3 * C3) return -1;
+    double (*S)[KD] = malloc(sizeof(double) * KD * KD);
+    double *act = malloc(sizeof(double) * (size_t)C3);
+    if (!S || !act) { free(S); free(act); return -2; }
+    double qh[KD], kh[KD], gv[KD], dec[KD], o[KD];
+    const size_t head_elems = (size_t)KD * KD;
+
+    for (int64_t b = 0; b < rows; ++b) {
+        int32_t idx = state_indices[b];
+        int null_row = idx <= 0 || (int64_t)idx >= num_slots;
+        if (null_row) {
+            for (int64_t i = 0; i < HC; ++i) {
+                size_t oi = (size_t)b * HC + i;
+                if (out64) out64[oi] = 0.0;
+                if (out_bf16) out_bf16[oi] = 0;
+                if (o_pre64) o_pre64[oi] = 0.0;
+            }
+            if (act64)
+                for (int64_t c = 0; c < C3; ++c) act64[(size_t)b * C3 + c] = 0.0;
+            continue;
+        }
+        /* depthwise causal conv, width 4, then SiLU; shift the cache */
+        uint16_t *cs = conv_state + (size_t)idx * conv_slot_stride;
+        for (int64_t c = 0; c < C3; ++c) {
+            int64_t grp = c / HC, cc = c % HC;
+            double hist[4];
+            hist[0] = bf16_to_f64(cs[0 * C3 + c]);
+            hist[1] = bf16_to_f64(cs[1 * C3 + c]);
+            hist[2] = bf16_to_f64(cs[2 * C3 + c]);
+            hist[3] = bf16_to_f64(x[(size_t)b * C3 + c]);
+            double y = 0.0;
+            for (int j = 0; j < 4; ++j)
+                y += (double)weight[(grp * 4 + j) * HC + cc] * hist[j];
+            act[c] = y * sigmoid(y);
+            cs[0 * C3 + c] = cs[1 * C3 + c];
+            cs[1 * C3 + c] = cs[2 * C3 + c];
+            cs[2 * C3 + c] = x[(size_t)b * C3 + c];
+        }
+        if (act64)
+            for (int64_t c = 0; c < C3; ++c) act64[(size_t)b * C3 + c] = act[c];
+        for (int64_t h = 0; h < H; ++h) {
+            const double *qa = act + 0 * HC + h * KD;
+            const double *ka = act + 1 * HC + h * KD;
+            const double *va = act + 2 * HC + h * KD;
+            size_t vec = ((size_t)b * H + h) * KD;
+            widen_bf16(graw + vec, gv, KD);
+            double beta = sigmoid(bf16_to_f64(braw[(size_t)b * H + h]));
+            l2_normalise(qa, l2_eps, qh);
+            l2_normalise(ka, l2_eps, kh);
+            gate_decay(gv, (double)A_log[h], dt_bias + h * KD, dec);
+            size_t head_base = ((size_t)idx * H + h) * head_elems;
+            gather_state(state, state_dtype, head_base, S);
+            kda_token(S, qh, kh, va, dec, beta, scale, o);
+            scatter_state(state, state_dtype, head_base, S);
+            /* gated RMSNorm over the 128 values of this head */
+            double ms = 0.0;
+            for (int j = 0; j < KD; ++j) ms += o[j] * o[j];
+            ms /= (double)KD;
+            double inv = 1.0 / sqrt(ms + norm_eps);
+            for (int j = 0; j < KD; ++j) {
+                double y = o[j] * inv * (double)norm_weight[j] *
+                           sigmoid(bf16_to_f64(ogate[vec + j]));
+                if (out64) out64[vec + j] = y;
+                if (out_bf16) out_bf16[vec + j] = kdao_bf16_from_f64(y);
+                if (o_pre64) o_pre64[vec + j] = o[j];
+            }
+        }
+    }
+    free(S);
+    free(act);
+    return 0;
+}
+
+/* Element-wise kdao_bf16_from_f64 over an array (test helper). */
+void kdao_bf16_from_f64_n(const double *x, uint16_t *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = kdao_bf16_from_f64(x[i]);
+}
