@@ -1,0 +1,374 @@
+#!/usr/bin/env python3
+"""Benchmark of the KDA decode hot path on one MI355X.
+
+Default workload (the headline line): recurrent_kda T=1, H=HV=32, K=V=128,
+fp32 state pool [4096, 32, 128, 128] (8 GiB) ~N(0, 0.05), B=256 rows on
+random unique slots, bf16 inputs ~N(0,1), A_log ~U(-2,0), dt_bias
+~N(0,0.1), softplus gate, scale 1/sqrt(128).  One step = one kernel launch
+that gathers, updates and scatters the 256 x 32 head states.
+
+Printed: one JSON line with rows/s (value), the live roofline of the
+kernel (HIP events on the launch stream over the timed region), the fp64
+oracle timed on the host cores over a bounded sample (cpu_baseline), and
+the other workloads of the path (batch sweeps, packed H=12 bf16, fused,
+ragged) with their own timings.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode rows/sec and achieved state HBM GB/s (% of peak), H=12/32, B=1..512"
+HBM_PEAK_GBPS = 8000.0
+D = 128
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_recurrent_t1_h32_fp32_b256.json")
+KERNEL_SRC = os.path.join(ROOT, "gated_delta_rule_decode_amd", "csrc", "kda_kernels.hip")
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------ byte model ----
+# Algorithmic HBM bytes (each byte the method must move once):
+#   per live (row, head), T=1: state read + write 2*128*128*s, q,k,v 3*256 B,
+#   raw gate 256 B, beta 2 B, output 256 B; per row the 4-byte index; per call
+#   A_log and dt_bias.  Null rows move their index and output only.
+
+def t1_bytes(B_live, B_null, H, state_bytes):
+    per_head = 2 * D * D * state_bytes + 3 * 2 * D + 2 * D + 2 + 2 * D
+    return (B_live * (H * per_head + 4) + B_null * (4 + H * 2 * D) + H * 4 + H * D * 4)
+
+
+def t1_state_bytes(B_live, H, state_bytes):
+    return B_live * H * 2 * D * D * state_bytes
+
+
+def fused_bytes(R_live, R_null, H, state_bytes):
+    C3 = 3 * H * D
+    per_row = (H * 2 * D * D * state_bytes      # state read + write
+               + C3 * 2                           # x
+               + 2 * 3 * C3 * 2                   # conv cache read 3 positions + write 3
+               + H * D * 2 + H * 2                # raw gate, beta
+               + H * D * 2 + H * D * 2 + 4)       # output gate, output, index
+    return R_live * per_row + R_null * (4 + H * D * 2) + 12 * H * D * 4 + H * 4 + H * D * 4 + D * 4
+
+
+def varlen_bytes(lengths, H, state_bytes, ckpt=True):
+    live_seqs = sum(1 for n in lengths if n > 0)
+    T = sum(lengths)
+    head = D * D * state_bytes
+    b = live_seqs * H * 2 * head + T * H * (4 * 2 * D + 2 + 2 * D)
+    if ckpt:
+        b += T * H * head
+    return b + (len(lengths) + 1) * 4 + len(lengths) * 4 + H * 4 + H * D * 4
+
+
+# ---------------------------------------------------------- CPU baseline ----
+
+_SAMPLE = None  # (inputs per worker) set in the parent before the pool forks
+
+
+def _oracle_slice(w):
+    import oracle
+    q, k, v, g, beta, A_log, dt_bias, st, idx = _SAMPLE[w]
+    oracle.recurrent(q, k, v, g, beta, A_log, dt_bias, st, idx)
+    return q.shape[0]
+
+
+def cpu_baseline(budget_s=12.0, rows_per_worker=8, H=32):
+    """The fp64 oracle as it stands, on the host cores, over a bounded sample
+    of the headline workload (T=1, H=32, fp32 state): each worker process
+    decodes its own 8 rows on their own slots, repeatedly, until the budget
+    is spent.  Inputs are drawn once in the parent (seeded) before the pool
+    forks; nothing here touches the GPU."""
+    global _SAMPLE
+    import multiprocessing as mp
+
+    import oracle
+    from gated_delta_rule_decode_amd import synth
+    workers = max(1, min(16, os.cpu_count() or 1))
+    sample = []
+    for w in range(workers):
+        c = synth.recurrent_case(9000 + w, n_seqs=rows_per_worker, H=H, num_slots=rows_per_worker)
+        sample.append(tuple(oracle.as_np(t) for t in (c.q, c.k, c.v, c.g, c.beta, c.A_log,
+                                                      c.dt_bias, c.state, c.state_indices)))
+    _SAMPLE = sample
+    ctx = mp.get_context("fork")
+    done_rows = 0
+    with ctx.Pool(workers) as pool:
+        pool.map(_oracle_slice, range(workers))  # warm the workers up
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < budget_s:
+            done_rows += sum(pool.map(_oracle_slice, range(workers)))
+        wall = time.perf_counter() - t0
+    _SAMPLE = None
+    return {"value": done_rows / wall, "unit": "rows/s", "cores": workers, "kind": "oracle",
+            "sample": f"{done_rows} rows of T=1 H=32 fp32-state decode ({done_rows * H} head "
+                      f"updates) in {wall:.1f} s: {workers} worker processes, each repeating "
+                      f"its own {rows_per_worker} rows; gcc -O2 fp64 oracle"}
+
+
+# ---------------------------------------------------------- GPU helpers ----
+
+def sha256_of(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def load_traffic(bytes_per_launch):
+    """HBM traffic measured with rocprofv3 counters, if it was taken on the
+    current kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+        if t.get("kernel_source_sha256") != sha256_of(KERNEL_SRC):
+            return None
+        return float(t["hbm_bytes_per_launch"])
+    except Exception:
+        return None
+
+
+class Timer:
+    """HIP events on the launch stream around a region."""
+
+    def __init__(self, torch, stream):
+        self.torch = torch
+        self.stream = stream
+
+    def run(self, fn, n):
+        torch = self.torch
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        s.record(self.stream)
+        for _ in range(n):
+            fn()
+        e.record(self.stream)
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / n * 1e3  # us per call
+
+
+def flush_l2(torch, buf):
+    buf.add_(1.0)  # streams 512 MiB through L2 and the MALL
+
+
+def time_cold(torch, fn, n, flush_buf):
+    """Per-call HIP-event time with the caches flushed before every call."""
+    tot = []
+    for _ in range(n):
+        flush_l2(torch, flush_buf)
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        fn()
+        e.record()
+        torch.cuda.synchronize()
+        tot.append(s.elapsed_time(e) * 1e3)
+    tot.sort()
+    return tot[len(tot) // 2]
+
+
+# ------------------------------------------------------------------ main ----
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--B", type=int, default=256)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="headline workload only")
+    ap.add_argument("--copy-calibrate", action="store_true",
+                    help="also run a 1 GiB device copy (for counter scaling under rocprofv3)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path "
+              f"(requested --gpus {args.gpus}); the decode shards with no communication "
+              f"(rows or heads per GPU), so run one process per GPU.", file=sys.stderr)
+        sys.exit(2)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        cpu = cpu_baseline()
+        log(f"cpu baseline {cpu['value']:.1f} rows/s on {cpu['cores']} cores")
+
+    import torch
+
+    from gated_delta_rule_decode_amd import (fused_kda_decode, packed_kda_decode, recurrent_kda,
+                                             synth)
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    timer = Timer(torch, stream)
+    log("device:", torch.cuda.get_device_name(dev))
+
+    # ---- headline: recurrent T=1, H=32, fp32 pool [4096,32,128,128], B ----
+    H, B, SLOTS = 32, args.B, 4096
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1000 + B)
+    log(f"building fp32 pool [{SLOTS},{H},128,128] ...")
+    pool = synth._randn_big(gen, (SLOTS, H, D, D), dev, 0.05, torch.float32)
+    c = synth.recurrent_case(1000 + B, n_seqs=B, H=H, num_slots=1, device=dev)
+    idx = synth.unique_slots(gen, B, 0, SLOTS, dev)
+    q4 = lambda t: t.reshape(B, 1, H, D)  # noqa: E731
+    out = torch.empty((B, 1, H, D), dtype=torch.bfloat16, device=dev)
+    qq, kk, vv, gg, bb = q4(c.q), q4(c.k), q4(c.v), q4(c.g), c.beta.reshape(B, 1, H)
+
+    def step():
+        recurrent_kda(qq, kk, vv, gg, bb, c.A_log, c.dt_bias, initial_state=pool,
+                      state_indices=idx, output=out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps ...")
+    t_wall0 = time.perf_counter()
+    us = timer.run(step, args.steps)
+    t_wall = time.perf_counter() - t_wall0
+    bytes_launch = t1_bytes(B, 0, H, 4)
+    state_bytes = t1_state_bytes(B, H, 4)
+    achieved = bytes_launch / (us * 1e-6) / 1e9
+    log(f"B={B}: {us:.1f} us/step, {achieved:.0f} GB/s algorithmic "
+        f"({100 * achieved / HBM_PEAK_GBPS:.1f}% of 8 TB/s), wall {t_wall:.3f}s")
+
+    if args.copy_calibrate:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        cus = timer.run(lambda: dst.copy_(src), 10)
+        log(f"copy 1 GiB -> 1 GiB: {cus:.1f} us, {2 * (1 << 30) / (cus * 1e-6) / 1e9:.0f} GB/s")
+        del src, dst
+
+    traffic = load_traffic(bytes_launch)
+    result = {
+        "metric": METRIC,
+        "value": B * 1e6 / us,
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": us / 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "data": "synthetic (seeded N(0,1) bf16 inputs, N(0,0.05) state)",
+        "config": {"workload": f"recurrent_kda T=1 H=HV=32 K=V=128 fp32 state pool "
+                               f"[4096,32,128,128], B={B} random unique slots, softplus gate",
+                   "B": B, "H": H, "state_dtype": "fp32", "num_slots": SLOTS},
+        "state_GBps": state_bytes / (us * 1e-6) / 1e9,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
+                     "kernel": "kda_recurrent_kernel<G=8, fp32, T=1>",
+                     "bytes_per_launch": bytes_launch},
+        "cpu_baseline": cpu,
+    }
+
+    if not args.no_extra:
+        extra = {}
+        flush = torch.empty(1 << 27, dtype=torch.float32, device=dev)
+        # H=32 fp32 batch sweep (same pool; fresh random slots per B)
+        sweep = []
+        for Bs in (1, 8, 32, 128, 256, 512):
+            cs = synth.recurrent_case(1000 + Bs, n_seqs=Bs, H=H, num_slots=1, device=dev)
+            g2 = torch.Generator(device=dev)
+            g2.manual_seed(1000 + Bs)
+            ids = synth.unique_slots(g2, Bs, 0, SLOTS, dev)
+            o = torch.empty((Bs, 1, H, D), dtype=torch.bfloat16, device=dev)
+            r4 = lambda t, n=Bs: t.reshape(n, 1, H, D)  # noqa: E731
+            fn = (lambda cs=cs, ids=ids, o=o, r4=r4, n=Bs: recurrent_kda(
+                r4(cs.q), r4(cs.k), r4(cs.v), r4(cs.g), cs.beta.reshape(n, 1, H), cs.A_log,
+                cs.dt_bias, initial_state=pool, state_indices=ids, output=o))
+            fn()
+            t_us = time_cold(torch, fn, 20, flush)
+            bts = t1_bytes(Bs, 0, H, 4)
+            sweep.append({"B": Bs, "us": t_us, "rows_per_s": Bs / (t_us * 1e-6),
+                          "state_GBps": t1_state_bytes(Bs, H, 4) / (t_us * 1e-6) / 1e9,
+                          "GBps": bts / (t_us * 1e-6) / 1e9,
+                          "frac": bts / (t_us * 1e-6) / 1e9 / HBM_PEAK_GBPS})
+            log(f"sweep H=32 fp32 B={Bs}: {t_us:.1f} us cold, {sweep[-1]['GBps']:.0f} GB/s")
+        extra["recurrent_t1_h32_fp32_cold"] = sweep
+        del pool
+        torch.cuda.empty_cache()
+
+        # packed H=12 bf16 pool [1024,12,128,128], 1/8 rows inactive
+        sweep = []
+        for Bs in (1, 8, 16, 31, 32, 64, 128, 256, 512):
+            nslots = max(1024, Bs + 1)
+            pc = synth.packed_case(2000 + Bs, B=Bs, H=12, num_slots=nslots, device=dev,
+                                   null_rows=Bs // 8)
+            o = torch.empty((Bs, 1, 12, D), dtype=torch.bfloat16, device=dev)
+            fn = (lambda pc=pc, o=o: packed_kda_decode(pc.mixed_qkv, pc.raw_gate, pc.raw_beta,
+                                                       pc.A_log, pc.dt_bias, pc.state,
+                                                       pc.state_indices, output=o))
+            fn()
+            t_us = time_cold(torch, fn, 20, flush)
+            live = Bs - Bs // 8
+            bts = t1_bytes(live, Bs // 8, 12, 2)
+            sweep.append({"B": Bs, "live": live, "us": t_us, "rows_per_s": live / (t_us * 1e-6),
+                          "state_GBps": t1_state_bytes(live, 12, 2) / (t_us * 1e-6) / 1e9,
+                          "GBps": bts / (t_us * 1e-6) / 1e9,
+                          "frac": bts / (t_us * 1e-6) / 1e9 / HBM_PEAK_GBPS})
+            log(f"sweep packed H=12 bf16 B={Bs}: {t_us:.1f} us cold, {sweep[-1]['GBps']:.0f} GB/s")
+            del pc
+        extra["packed_t1_h12_bf16_cold"] = sweep
+
+        # fused, rows=256, H=32, fp32 pool [2048,32,128,128], 16 null rows
+        fc = synth.fused_case(3000, rows=256, H=32, num_slots=2048, device=dev, null_zero=8,
+                              null_neg=8)
+        o = torch.empty((1, 256, 32, D), dtype=torch.bfloat16, device=dev)
+        fn = (lambda: fused_kda_decode(fc.x, fc.weight, fc.conv_state, fc.raw_gate, fc.raw_beta,
+                                       fc.A_log, fc.dt_bias, fc.state_indices, fc.state,
+                                       fc.output_gate, fc.norm_weight, output=o))
+        fn()
+        t_us = time_cold(torch, fn, 20, flush)
+        bts = fused_bytes(240, 16, 32, 4)
+        extra["fused_h32_rows256_fp32_cold"] = {"us": t_us, "rows_per_s": 240 / (t_us * 1e-6),
+                                                "GBps": bts / (t_us * 1e-6) / 1e9,
+                                                "frac": bts / (t_us * 1e-6) / 1e9 / HBM_PEAK_GBPS}
+        log(f"fused H=32 rows=256: {t_us:.1f} us cold, {bts / (t_us * 1e-6) / 1e9:.0f} GB/s")
+        del fc
+        torch.cuda.empty_cache()
+
+        # ragged T>=2: H=16, N=64, lengths U{0..6}, fp32 checkpoints
+        lengths = synth.ragged_lengths(4000, 64, 0, 6)
+        vc = synth.recurrent_case(4000, n_seqs=64, H=16, num_slots=65, device=dev, lengths=lengths,
+                                  slot_lo=1)
+        T = sum(lengths)
+        ck = torch.empty((T, 16, D, D), dtype=torch.float32, device=dev)
+        o = torch.empty((1, T, 16, D), dtype=torch.bfloat16, device=dev)
+        r1 = lambda t: t.reshape(1, T, *t.shape[1:])  # noqa: E731
+        fn = (lambda: recurrent_kda(r1(vc.q), r1(vc.k), r1(vc.v), r1(vc.g), r1(vc.beta), vc.A_log,
+                                    vc.dt_bias, initial_state=vc.state,
+                                    state_indices=vc.state_indices, cu_seqlens=vc.cu_seqlens,
+                                    output=o, intermediate_states=ck))
+        fn()
+        t_us = time_cold(torch, fn, 20, flush)
+        bts = varlen_bytes(lengths, 16, 4)
+        extra["varlen_h16_n64_fp32_ckpt_cold"] = {"us": t_us, "tokens": T,
+                                                  "tokens_per_s": T / (t_us * 1e-6),
+                                                  "GBps": bts / (t_us * 1e-6) / 1e9,
+                                                  "frac": bts / (t_us * 1e-6) / 1e9 / HBM_PEAK_GBPS}
+        log(f"varlen H=16 N=64 T={T}: {t_us:.1f} us cold, {bts / (t_us * 1e-6) / 1e9:.0f} GB/s")
+        result["workloads"] = extra
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,275 @@
+"""Python facade of libkda_mi355x.so (torch tensors in, C ABI underneath).
+
+Only argument marshalling happens here: shapes, strides and dtypes are read
+from the tensors, the output is allocated when the caller passes none, and
+the call goes to the C library on the caller's current HIP stream.  Every
+step of the decode runs in the library's gfx950 kernels; there is no
+PyTorch or CPU fallback.
+
+Call names and argument order follow the flashinfer KDA decode pages
+("flashinfer.kda_decode" function table, "flashinfer.kda_decode.
+fused_kda_decode" signature).  Deliberate differences: ``lower_bound``
+defaults to None (the pages do not define the bounded gate, so passing a
+number raises), and there is no ``backend`` / ``state_indices_mode``
+selector because there is exactly one implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+
+import torch
+
+from . import _lib
+
+D = 128
+_SCALE = 1.0 / math.sqrt(D)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream(dev):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _need(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _state_dtype(state):
+    if state.dtype == torch.float32:
+        return _lib.DTYPE_F32
+    if state.dtype == torch.bfloat16:
+        return _lib.DTYPE_BF16
+    raise ValueError(f"state dtype must be float32 or bfloat16, got {state.dtype}")
+
+
+def _check_pool(state, H):
+    _need(state.dim() == 4 and tuple(state.shape[1:]) == (H, D, D),
+          f"state must be [num_slots, {H}, 128, 128], got {tuple(state.shape)}")
+    _need(state.stride(3) == 1 and state.stride(2) == D and state.stride(1) == D * D,
+          "each slot's [H, 128, 128] block must be contiguous")
+    _need(state.is_cuda, "state must be a device tensor")
+
+
+def _check_indices(idx, n):
+    _need(idx.dtype == torch.int32 and idx.is_contiguous() and idx.numel() == n,
+          f"state_indices must be a contiguous int32 tensor with {n} elements")
+
+
+def _gate_mode(lower_bound):
+    if lower_bound is None:
+        return _lib.GATE_SOFTPLUS, 0.0
+    # Forwarded so the library reports KDA_ERR_UNSUPPORTED with its reason.
+    return _lib.GATE_LOWER_BOUND, float(lower_bound)
+
+
+def _token_view(t, name, T, H, width, cu):
+    """(row stride, tensor) of a per-token [.., H, width] input whose inner
+    [H, width] block is contiguous; accepts [T,H,w], [T,1,H,w] (T=1) or
+    [1,T,H,w] (packed)."""
+    if width == 1:
+        _need(t.shape[-1] == H and t.stride(-1) == 1, f"{name} must end in a contiguous [H] dim")
+    else:
+        _need(t.shape[-1] == width and t.shape[-2] == H and t.stride(-1) == 1 and t.stride(-2) == width,
+              f"{name} must end in a contiguous [H, {width}] block")
+    lead = t.shape[:-1] if width == 1 else t.shape[:-2]
+    strides = t.stride()[:len(lead)]
+    if len(lead) == 1:
+        _need(lead[0] == T, f"{name} has {lead[0]} tokens, expected {T}")
+        return strides[0]
+    _need(len(lead) == 2, f"{name} has an unsupported rank")
+    if cu is None:
+        _need(lead[0] == T and lead[1] == 1, f"{name} must be [B, 1, ...] for T=1")
+        return strides[0]
+    _need(lead[0] == 1 and lead[1] == T, f"{name} must be [1, T, ...] for packed tokens")
+    return strides[1]
+
+
+def recurrent_kda(q, k, v, g, beta, A_log, dt_bias, *, initial_state, state_indices,
+                  cu_seqlens=None, n_tokens=None, scale=None, output=None, intermediate_states=None,
+                  lower_bound=None, use_qk_l2norm_in_kernel=True, l2_eps=1e-6):
+    """Recurrent KDA decode ("flashinfer.kda_decode" function table).
+
+    T=1: q, k, v, g are bf16 [B, 1, H, 128] (or [B, H, 128]); beta logits
+    [B, 1, H]; one sequence per row.  Packed T>=2: q, k, v, g are
+    [1, T, H, 128], beta [1, T, H] and ``cu_seqlens`` int32 [N+1] gives the
+    ragged sequences (empty ones allowed); ``n_tokens`` defaults to T.
+    ``g`` is the raw gate, A_log fp32 [H], dt_bias fp32 [H*128].  The pool
+    ``initial_state`` [num_slots, H, 128, 128] (fp32 or bf16) is updated in
+    place at ``state_indices`` (int32, negative = null row).
+    ``intermediate_states`` (optional, [T, H, 128, 128], pool dtype) receives
+    the state after every token.  Returns the bf16 output, shaped like q.
+    """
+    _need(use_qk_l2norm_in_kernel, "only the in-kernel q/k L2 normalisation is implemented")
+    H = A_log.numel()
+    state = initial_state
+    _check_pool(state, H)
+    N = state_indices.numel()
+    if cu_seqlens is None:
+        T = N
+    else:
+        _need(cu_seqlens.dtype == torch.int32 and cu_seqlens.is_contiguous() and cu_seqlens.numel() == N + 1,
+              "cu_seqlens must be a contiguous int32 tensor with N+1 elements")
+        T = int(n_tokens) if n_tokens is not None else q.shape[-3]
+    _check_indices(state_indices, N)
+    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta)):
+        _need(t.dtype == torch.bfloat16 and t.is_cuda, f"{name} must be a bf16 device tensor")
+    strides = [_token_view(t, n, T, H, D, cu_seqlens) for n, t in (("q", q), ("k", k), ("v", v), ("g", g))]
+    sb = _token_view(beta, "beta", T, H, 1, cu_seqlens)
+    _need(A_log.dtype == torch.float32 and A_log.is_contiguous(), "A_log must be contiguous fp32 [H]")
+    _need(dt_bias.dtype == torch.float32 and dt_bias.is_contiguous() and dt_bias.numel() == H * D,
+          "dt_bias must be contiguous fp32 [H*128]")
+    out_shape = q.shape
+    if output is None:
+        output = torch.empty(out_shape, dtype=torch.bfloat16, device=q.device)
+    else:
+        _need(output.dtype == torch.bfloat16 and output.is_contiguous() and output.numel() == T * H * D,
+              "output must be a contiguous bf16 tensor with T*H*128 elements")
+    ck = intermediate_states
+    if ck is not None:
+        _need(ck.dtype == state.dtype and ck.is_contiguous() and ck.numel() == T * H * D * D,
+              "intermediate_states must be contiguous [T, H, 128, 128] in the pool dtype")
+    gm, lb = _gate_mode(lower_bound)
+    a = _lib.RecurrentArgs()
+    a.struct_size = ctypes.sizeof(_lib.RecurrentArgs)
+    a.n_seqs, a.n_tokens, a.H, a.HV, a.K, a.V = N, T, H, H, D, D
+    a.q, a.k, a.v, a.g, a.beta = _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta)
+    a.q_stride, a.k_stride, a.v_stride, a.g_stride = strides
+    a.beta_stride = sb
+    a.A_log, a.dt_bias = _ptr(A_log), _ptr(dt_bias)
+    a.scale = _SCALE if scale is None else float(scale)
+    a.l2_eps = float(l2_eps)
+    a.gate_mode, a.lower_bound = gm, lb
+    a.state, a.state_dtype, a.ckpt_dtype = _ptr(state), _state_dtype(state), _state_dtype(state)
+    a.num_slots, a.slot_stride = state.shape[0], state.stride(0)
+    a.state_indices = _ptr(state_indices)
+    a.cu_seqlens = _ptr(cu_seqlens)
+    a.checkpoints = _ptr(ck)
+    a.out = _ptr(output)
+    lib = _lib.load()
+    with torch.cuda.device(q.device):
+        _lib.check(lib.kda_recurrent(ctypes.byref(a), _stream(q.device)))
+    return output
+
+
+def packed_kda_decode(mixed_qkv, raw_gate, raw_beta, A_log, dt_bias, state, state_indices,
+                      output=None, *, lower_bound=None):
+    """Packed T=1 decode ("Serving-native packed Kimi K3 decode").
+
+    mixed_qkv bf16 [B, 3*H*128] (q|k|v, channel-contiguous, any row stride),
+    raw_gate bf16 [B, H*128], raw_beta bf16 [B, H], A_log fp32 [H],
+    dt_bias fp32 [H*128], state [num_slots, H, 128, 128] (bf16 or fp32),
+    state_indices int32 [B] (-1 inactive).  Returns bf16 [B, 1, H, 128].
+    """
+    H = A_log.numel()
+    B = mixed_qkv.shape[0]
+    _check_pool(state, H)
+    _check_indices(state_indices, B)
+    _need(mixed_qkv.dtype == torch.bfloat16 and mixed_qkv.dim() == 2 and mixed_qkv.shape[1] == 3 * H * D
+          and mixed_qkv.stride(1) == 1, "mixed_qkv must be bf16 [B, 3*H*128] with contiguous channels")
+    rg = raw_gate.reshape(B, H * D) if raw_gate.is_contiguous() else raw_gate
+    _need(rg.dtype == torch.bfloat16 and rg.dim() == 2 and tuple(rg.shape) == (B, H * D) and rg.stride(1) == 1,
+          "raw_gate must be bf16 [B, H*128] with contiguous channels")
+    rb = raw_beta.reshape(B, H) if raw_beta.is_contiguous() else raw_beta
+    _need(rb.dtype == torch.bfloat16 and rb.dim() == 2 and tuple(rb.shape) == (B, H) and rb.stride(1) == 1,
+          "raw_beta must be bf16 [B, H]")
+    _need(A_log.dtype == torch.float32 and A_log.is_contiguous(), "A_log must be contiguous fp32 [H]")
+    _need(dt_bias.dtype == torch.float32 and dt_bias.is_contiguous() and dt_bias.numel() == H * D,
+          "dt_bias must be contiguous fp32 [H*128]")
+    if output is None:
+        output = torch.empty((B, 1, H, D), dtype=torch.bfloat16, device=mixed_qkv.device)
+    else:
+        _need(output.dtype == torch.bfloat16 and output.is_contiguous() and output.numel() == B * H * D,
+              "output must be contiguous bf16 [B, 1, H, 128]")
+    gm, lb = _gate_mode(lower_bound)
+    a = _lib.PackedArgs()
+    a.struct_size = ctypes.sizeof(_lib.PackedArgs)
+    a.B, a.H = B, H
+    a.mixed_qkv, a.qkv_stride = _ptr(mixed_qkv), mixed_qkv.stride(0)
+    a.raw_gate, a.gate_stride = _ptr(rg), rg.stride(0)
+    a.raw_beta, a.beta_stride = _ptr(rb), rb.stride(0)
+    a.A_log, a.dt_bias = _ptr(A_log), _ptr(dt_bias)
+    a.gate_mode, a.lower_bound = gm, lb
+    a.state, a.state_dtype = _ptr(state), _state_dtype(state)
+    a.num_slots, a.slot_stride = state.shape[0], state.stride(0)
+    a.state_indices = _ptr(state_indices)
+    a.out = _ptr(output)
+    lib = _lib.load()
+    with torch.cuda.device(mixed_qkv.device):
+        _lib.check(lib.kda_packed_decode(ctypes.byref(a), _stream(mixed_qkv.device)))
+    return output
+
+
+def fused_kda_decode(x, weight, conv_state, raw_gate, raw_beta, A_log, dt_bias, state_indices,
+                     state, output_gate, norm_weight, lower_bound=None, norm_eps=1e-5, output=None):
+    """Fused decode ("flashinfer.kda_decode.fused_kda_decode"): width-4
+    depthwise causal conv + SiLU over x, one KDA update, gated RMSNorm.
+
+    x bf16 [rows, 3*H*128]; weight fp32 [3, 4, H*128]; conv_state bf16
+    [num_slots, 3*H*128, 3] with strides [slot_stride, 1, 3*H*128]; raw_gate
+    bf16 [1, rows, H, 128] or [rows, H, 128]; raw_beta bf16 [1, rows, H] or
+    [rows, H]; state_indices int32 [rows] (non-positive = null); state
+    [num_slots, H, 128, 128] fp32/bf16; output_gate bf16 [rows, H, 128] or
+    [1, rows, H, 128]; norm_weight fp32 [128].  Returns bf16 [1, rows, H, 128].
+    """
+    H = A_log.numel()
+    HC = H * D
+    rows = x.shape[0]
+    _check_pool(state, H)
+    _check_indices(state_indices, rows)
+    _need(x.dtype == torch.bfloat16 and x.dim() == 2 and x.shape[1] == 3 * HC and x.stride(1) == 1,
+          "x must be bf16 [rows, 3*H*128] with contiguous channels")
+    _need(weight.dtype == torch.float32 and weight.is_contiguous() and tuple(weight.shape) == (3, 4, HC),
+          "weight must be contiguous fp32 [3, 4, H*128]")
+    _need(conv_state.dtype == torch.bfloat16 and conv_state.dim() == 3
+          and tuple(conv_state.shape[1:]) == (3 * HC, 3) and conv_state.stride(1) == 1
+          and conv_state.stride(2) == 3 * HC, "conv_state must be bf16 [num_slots, 3*H*128, 3] "
+          "with strides [slot_stride, 1, 3*H*128]")
+    _need(conv_state.shape[0] == state.shape[0], "state and conv_state must have the same num_slots")
+
+    def rows2d(t, name, width):
+        _need(t.dtype == torch.bfloat16, f"{name} must be bf16")
+        t2 = t.reshape(rows, width) if t.is_contiguous() else t
+        _need(t2.dim() == 2 and tuple(t2.shape) == (rows, width) and t2.stride(1) == 1,
+              f"{name} must be [rows, {width}] with a contiguous inner dimension")
+        return t2
+
+    rg = rows2d(raw_gate, "raw_gate", HC)
+    rb = rows2d(raw_beta, "raw_beta", H)
+    og = rows2d(output_gate, "output_gate", HC)
+    _need(norm_weight.dtype == torch.float32 and norm_weight.is_contiguous() and norm_weight.numel() == D,
+          "norm_weight must be contiguous fp32 [128]")
+    _need(A_log.dtype == torch.float32 and A_log.is_contiguous(), "A_log must be contiguous fp32 [H]")
+    _need(dt_bias.dtype == torch.float32 and dt_bias.is_contiguous() and dt_bias.numel() == HC,
+          "dt_bias must be contiguous fp32 [H*128]")
+    _need(norm_eps >= 0, "norm_eps must be non-negative")
+    if output is None:
+        output = torch.empty((1, rows, H, D), dtype=torch.bfloat16, device=x.device)
+    else:
+        _need(output.dtype == torch.bfloat16 and output.is_contiguous() and output.numel() == rows * HC,
+              "output must be contiguous bf16 [1, rows, H, 128]")
+    gm, lb = _gate_mode(lower_bound)
+    a = _lib.FusedArgs()
+    a.struct_size = ctypes.sizeof(_lib.FusedArgs)
+    a.rows, a.H = rows, H
+    a.x, a.x_stride = _ptr(x), x.stride(0)
+    a.weight = _ptr(weight)
+    a.conv_state, a.conv_slot_stride = _ptr(conv_state), conv_state.stride(0)
+    a.raw_gate, a.gate_stride = _ptr(rg), rg.stride(0)
+    a.raw_beta, a.beta_stride = _ptr(rb), rb.stride(0)
+    a.A_log, a.dt_bias = _ptr(A_log), _ptr(dt_bias)
+    a.gate_mode, a.lower_bound = gm, lb
+    a.state_indices = _ptr(state_indices)
+    a.state, a.state_dtype = _ptr(state), _state_dtype(state)
+    a.num_slots, a.slot_stride = state.shape[0], state.stride(0)
+    a.output_gate, a.ogate_stride = _ptr(og), og.stride(0)
+    a.norm_weight, a.norm_eps = _ptr(norm_weight), float(norm_eps)
+    a.out = _ptr(output)
+    lib = _lib.load()
+    with torch.cuda.device(x.device):
+        _lib.check(lib.kda_fused_decode(ctypes.byref(a), _stream(x.device)))
+    return output

@@ -1,0 +1,470 @@
+// kda_api.cpp -- C entry points of libkda_mi355x.so: argument validation,
+// launch planning from host-visible metadata, and the hand-off to the gfx950
+// kernels.  Pure C++: every HIP runtime call lives in kda_kernels.hip.
+//
+// Rules taken from the pages: one kernel launch per call and no fallback to
+// another implementation ("flashinfer.kda_decode", backend="cake" section);
+// the schedule is chosen from host-visible sizes only and device tensors are
+// never read on the host ("Serving-native packed Kimi K3 decode"; the
+// fused_kda_decode Parameters on state_indices_mode); strict tensor and alias
+// validation ("feat(cake_kda): add serving-native packed decode backend",
+// walkthrough of the CUDA binding).
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/kda.h"
+#include "kda_internal.h"
+
+using namespace kda_detail;
+
+namespace {
+
+thread_local char g_err[512];
+
+int fail(int code, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int ok()
+{
+    g_err[0] = 0;
+    return KDA_OK;
+}
+
+// Byte range [lo, hi) of a buffer; empty when lo == hi.
+struct Range {
+    uintptr_t lo, hi;
+    const char *name;
+};
+
+Range span(const void *p, uint64_t bytes, const char *name)
+{
+    uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return Range{lo, lo + (uintptr_t)bytes, name};
+}
+
+bool overlap(const Range &a, const Range &b)
+{
+    if (a.lo == a.hi || b.lo == b.hi) return false;
+    return a.lo < b.hi && b.lo < a.hi;
+}
+
+// Each written range must not overlap any other range (written or read).
+int check_alias(const Range *w, int nw, const Range *r, int nr)
+{
+    for (int i = 0; i < nw; ++i) {
+        for (int j = i + 1; j < nw; ++j)
+            if (overlap(w[i], w[j]))
+                return fail(KDA_ERR_ALIAS, "%s overlaps %s", w[i].name, w[j].name);
+        for (int j = 0; j < nr; ++j)
+            if (overlap(w[i], r[j]))
+                return fail(KDA_ERR_ALIAS, "%s overlaps %s", w[i].name, r[j].name);
+    }
+    return KDA_OK;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned2(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 1u) == 0; }
+bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+constexpr int64_t HEAD_ELEMS = (int64_t)KD * KD;
+constexpr int64_t MAX_INDEX = 0x7fffffffLL;
+
+int elem_size(int32_t dtype) { return dtype == KDA_DTYPE_F32 ? 4 : 2; }
+
+// Extent in elements of a row-strided [rows, width] tensor.
+uint64_t rows_extent(int64_t rows, int64_t stride, int64_t width)
+{
+    return rows <= 0 ? 0 : (uint64_t)(rows - 1) * (uint64_t)stride + (uint64_t)width;
+}
+
+int check_gate(int32_t mode)
+{
+    if (mode == KDA_GATE_SOFTPLUS) return KDA_OK;
+    if (mode == KDA_GATE_LOWER_BOUND)
+        return fail(KDA_ERR_UNSUPPORTED,
+                    "the bounded (lower_bound) gate is not defined by the method's pages; "
+                    "only the softplus gate is implemented");
+    return fail(KDA_ERR_UNSUPPORTED, "unknown gate_mode %d", (int)mode);
+}
+
+int check_pool(const void *state, int32_t dtype, int64_t num_slots, int64_t slot_stride, int32_t H)
+{
+    if (dtype != KDA_DTYPE_F32 && dtype != KDA_DTYPE_BF16)
+        return fail(KDA_ERR_DTYPE, "state_dtype %d is neither F32 nor BF16", (int)dtype);
+    if (num_slots < 1 || num_slots > MAX_INDEX)
+        return fail(KDA_ERR_SHAPE, "num_slots %lld out of range", (long long)num_slots);
+    if (slot_stride < (int64_t)H * HEAD_ELEMS)
+        return fail(KDA_ERR_STRIDE, "slot_stride %lld < H*128*128", (long long)slot_stride);
+    if (!aligned16(state) || ((slot_stride * elem_size(dtype)) & 15) != 0)
+        return fail(KDA_ERR_ALIGN, "state base and slot stride must be 16-byte aligned");
+    return KDA_OK;
+}
+
+uint64_t pool_bytes(int32_t dtype, int64_t num_slots, int64_t slot_stride, int32_t H)
+{
+    return ((uint64_t)(num_slots - 1) * (uint64_t)slot_stride + (uint64_t)H * HEAD_ELEMS) *
+           (uint64_t)elem_size(dtype);
+}
+
+// Value rows per workgroup: a (row, head) item is split into vsplit
+// workgroups of 128/vsplit value rows so that small batches still put
+// enough workgroups on the 256 CUs; large batches keep whole heads.
+int choose_vsplit(int64_t items)
+{
+    const int64_t target = 2048;  // ~8 workgroups per CU
+    int v = 1;
+    while (v < 8 && items * v < target) v *= 2;
+    return v;
+}
+
+void fill_plan(kda_launch_plan *plan, const Launch &l, int64_t items)
+{
+    if (!plan) return;
+    plan->struct_size = sizeof(kda_launch_plan);
+    plan->kernel = l.family;
+    plan->grid_x = l.grid;
+    plan->block = l.block;
+    plan->rows_per_block = l.rows_per_block;
+    plan->vsplit = l.vsplit;
+    plan->items = items;
+}
+
+// ------------------------------------------------------------ recurrent ----
+
+int prepare_recurrent(const kda_recurrent_args *a, RecParams *p, Launch *l)
+{
+    if (!a) return fail(KDA_ERR_NULLPTR, "args is NULL");
+    if (a->struct_size != sizeof(kda_recurrent_args))
+        return fail(KDA_ERR_ABI, "struct_size %u != %zu", a->struct_size, sizeof(kda_recurrent_args));
+    if (a->K != KD || a->V != KD)
+        return fail(KDA_ERR_UNSUPPORTED, "K=%d V=%d: only K=V=128", a->K, a->V);
+    if (a->H < 1) return fail(KDA_ERR_SHAPE, "H=%d must be >= 1", a->H);
+    if (a->HV != a->H) return fail(KDA_ERR_UNSUPPORTED, "HV=%d != H=%d (grouped heads)", a->HV, a->H);
+    if (a->n_seqs < 1) return fail(KDA_ERR_SHAPE, "n_seqs=%d must be >= 1", a->n_seqs);
+    const bool varlen = a->cu_seqlens != nullptr;
+    if (!varlen && a->n_tokens != a->n_seqs)
+        return fail(KDA_ERR_SHAPE, "T=1 call: n_tokens=%d != n_seqs=%d", a->n_tokens, a->n_seqs);
+    if (a->n_tokens < 0) return fail(KDA_ERR_SHAPE, "n_tokens=%d < 0", a->n_tokens);
+    int rc = check_gate(a->gate_mode);
+    if (rc) return rc;
+    if (!a->A_log || !a->dt_bias || !a->state || !a->state_indices)
+        return fail(KDA_ERR_NULLPTR, "a required pointer is NULL");
+    if (a->n_tokens > 0 && (!a->q || !a->k || !a->v || !a->g || !a->beta || !a->out))
+        return fail(KDA_ERR_NULLPTR, "a required per-token pointer is NULL");
+    const int64_t HC = (int64_t)a->H * KD;
+    if (a->q_stride < HC || a->k_stride < HC || a->v_stride < HC || a->g_stride < HC)
+        return fail(KDA_ERR_STRIDE, "q/k/v/g token strides must be >= H*128");
+    if (a->beta_stride < a->H) return fail(KDA_ERR_STRIDE, "beta_stride must be >= H");
+    if (!aligned2(a->q) || !aligned2(a->k) || !aligned2(a->v) || !aligned2(a->g) || !aligned2(a->beta) ||
+        !aligned4(a->A_log) || !aligned4(a->dt_bias) || !aligned4(a->state_indices) ||
+        (varlen && !aligned4(a->cu_seqlens)))
+        return fail(KDA_ERR_ALIGN, "inputs must be aligned to their element size");
+    if (!aligned16(a->out)) return fail(KDA_ERR_ALIGN, "out must be 16-byte aligned");
+    if (!(a->l2_eps >= 0.0f) || !isfinite(a->scale))
+        return fail(KDA_ERR_SHAPE, "l2_eps must be >= 0 and scale finite");
+    rc = check_pool(a->state, a->state_dtype, a->num_slots, a->slot_stride, a->H);
+    if (rc) return rc;
+    if (a->checkpoints) {
+        if (a->ckpt_dtype != a->state_dtype)
+            return fail(KDA_ERR_UNSUPPORTED, "checkpoints must use the state dtype");
+        if (!aligned16(a->checkpoints)) return fail(KDA_ERR_ALIGN, "checkpoints must be 16-byte aligned");
+    }
+    const int64_t T = a->n_tokens;
+    const int es = elem_size(a->state_dtype);
+    Range w[3] = {span(a->out, (uint64_t)T * HC * 2, "out"),
+                  span(a->state, pool_bytes(a->state_dtype, a->num_slots, a->slot_stride, a->H), "state"),
+                  span(a->checkpoints, a->checkpoints ? (uint64_t)T * a->H * HEAD_ELEMS * es : 0,
+                       "checkpoints")};
+    Range r[9] = {span(a->q, rows_extent(T, a->q_stride, HC) * 2, "q"),
+                  span(a->k, rows_extent(T, a->k_stride, HC) * 2, "k"),
+                  span(a->v, rows_extent(T, a->v_stride, HC) * 2, "v"),
+                  span(a->g, rows_extent(T, a->g_stride, HC) * 2, "g"),
+                  span(a->beta, rows_extent(T, a->beta_stride, a->H) * 2, "beta"),
+                  span(a->A_log, (uint64_t)a->H * 4, "A_log"),
+                  span(a->dt_bias, (uint64_t)HC * 4, "dt_bias"),
+                  span(a->state_indices, (uint64_t)a->n_seqs * 4, "state_indices"),
+                  span(a->cu_seqlens, varlen ? (uint64_t)(a->n_seqs + 1) * 4 : 0, "cu_seqlens")};
+    rc = check_alias(w, 3, r, 9);
+    if (rc) return rc;
+
+    const int64_t items = (int64_t)a->n_seqs * a->H;
+    const int vsplit = choose_vsplit(items);
+    if (items * vsplit > 0x7fffffffLL) return fail(KDA_ERR_SHAPE, "too many work items");
+    l->family = varlen ? KERNEL_RECURRENT_VARLEN : KERNEL_RECURRENT_T1;
+    l->vsplit = vsplit;
+    l->rows_per_block = KD / vsplit;
+    l->grid = (int32_t)(items * vsplit);
+    l->block = 256;
+    l->bf16_state = a->state_dtype == KDA_DTYPE_BF16;
+
+    p->q = static_cast<const uint16_t *>(a->q);
+    p->k = static_cast<const uint16_t *>(a->k);
+    p->v = static_cast<const uint16_t *>(a->v);
+    p->g = static_cast<const uint16_t *>(a->g);
+    p->beta = static_cast<const uint16_t *>(a->beta);
+    p->q_stride = a->q_stride;
+    p->k_stride = a->k_stride;
+    p->v_stride = a->v_stride;
+    p->g_stride = a->g_stride;
+    p->beta_stride = a->beta_stride;
+    p->A_log = a->A_log;
+    p->dt_bias = a->dt_bias;
+    p->scale = a->scale;
+    p->l2_eps = a->l2_eps;
+    p->state = a->state;
+    p->num_slots = a->num_slots;
+    p->slot_stride = a->slot_stride;
+    p->state_indices = a->state_indices;
+    p->cu_seqlens = a->cu_seqlens;
+    p->ckpt = a->checkpoints;
+    p->out = static_cast<uint16_t *>(a->out);
+    p->n_seqs = a->n_seqs;
+    p->n_tokens = a->n_tokens;
+    p->H = a->H;
+    p->vsplit = vsplit;
+    return ok();
+}
+
+int packed_to_recurrent(const kda_packed_args *a, kda_recurrent_args *r)
+{
+    if (!a) return fail(KDA_ERR_NULLPTR, "args is NULL");
+    if (a->struct_size != sizeof(kda_packed_args))
+        return fail(KDA_ERR_ABI, "struct_size %u != %zu", a->struct_size, sizeof(kda_packed_args));
+    if (a->H < 1) return fail(KDA_ERR_SHAPE, "H=%d must be >= 1", a->H);
+    if (a->B < 1) return fail(KDA_ERR_SHAPE, "B=%d must be >= 1", a->B);
+    const int64_t HC = (int64_t)a->H * KD;
+    if (a->qkv_stride < 3 * HC) return fail(KDA_ERR_STRIDE, "qkv_stride must be >= 3*H*128");
+    if (a->gate_stride < HC) return fail(KDA_ERR_STRIDE, "gate_stride must be >= H*128");
+    if (a->beta_stride < a->H) return fail(KDA_ERR_STRIDE, "beta_stride must be >= H");
+    if (!a->mixed_qkv) return fail(KDA_ERR_NULLPTR, "mixed_qkv is NULL");
+    memset(r, 0, sizeof *r);
+    r->struct_size = sizeof *r;
+    r->n_seqs = a->B;
+    r->n_tokens = a->B;
+    r->H = r->HV = a->H;
+    r->K = r->V = KD;
+    const uint16_t *qkv = static_cast<const uint16_t *>(a->mixed_qkv);
+    r->q = qkv;
+    r->k = qkv + HC;
+    r->v = qkv + 2 * HC;
+    r->q_stride = r->k_stride = r->v_stride = a->qkv_stride;
+    r->g = a->raw_gate;
+    r->g_stride = a->gate_stride;
+    r->beta = a->raw_beta;
+    r->beta_stride = a->beta_stride;
+    r->A_log = a->A_log;
+    r->dt_bias = a->dt_bias;
+    r->scale = 1.0f / sqrtf((float)KD);
+    r->l2_eps = 1e-6f;
+    r->gate_mode = a->gate_mode;
+    r->lower_bound = a->lower_bound;
+    r->state = a->state;
+    r->state_dtype = a->state_dtype;
+    r->ckpt_dtype = a->state_dtype;
+    r->num_slots = a->num_slots;
+    r->slot_stride = a->slot_stride;
+    r->state_indices = a->state_indices;
+    r->out = a->out;
+    return KDA_OK;
+}
+
+// ---------------------------------------------------------------- fused ----
+
+int prepare_fused(const kda_fused_args *a, FusedParams *p, Launch *l)
+{
+    if (!a) return fail(KDA_ERR_NULLPTR, "args is NULL");
+    if (a->struct_size != sizeof(kda_fused_args))
+        return fail(KDA_ERR_ABI, "struct_size %u != %zu", a->struct_size, sizeof(kda_fused_args));
+    if (a->H < 1) return fail(KDA_ERR_SHAPE, "H=%d must be >= 1", a->H);
+    if (a->rows < 1) return fail(KDA_ERR_SHAPE, "rows=%d must be >= 1", a->rows);
+    int rc = check_gate(a->gate_mode);
+    if (rc) return rc;
+    if (!a->x || !a->weight || !a->conv_state || !a->raw_gate || !a->raw_beta || !a->A_log ||
+        !a->dt_bias || !a->state_indices || !a->state || !a->output_gate || !a->norm_weight || !a->out)
+        return fail(KDA_ERR_NULLPTR, "a required pointer is NULL");
+    const int64_t HC = (int64_t)a->H * KD;
+    const int64_t C3 = 3 * HC;
+    if (a->x_stride < C3) return fail(KDA_ERR_STRIDE, "x_stride must be >= 3*H*128");
+    if (a->conv_slot_stride < 3 * C3) return fail(KDA_ERR_STRIDE, "conv_slot_stride must be >= 3*3*H*128");
+    if (a->gate_stride < HC || a->ogate_stride < HC)
+        return fail(KDA_ERR_STRIDE, "raw_gate/output_gate row strides must be >= H*128");
+    if (a->beta_stride < a->H) return fail(KDA_ERR_STRIDE, "beta_stride must be >= H");
+    if (!(a->norm_eps >= 0.0f)) return fail(KDA_ERR_SHAPE, "norm_eps must be >= 0");
+    if (!aligned2(a->x) || !aligned2(a->conv_state) || !aligned2(a->raw_gate) || !aligned2(a->raw_beta) ||
+        !aligned2(a->output_gate) || !aligned4(a->weight) || !aligned4(a->A_log) ||
+        !aligned4(a->dt_bias) || !aligned4(a->norm_weight) || !aligned4(a->state_indices))
+        return fail(KDA_ERR_ALIGN, "inputs must be aligned to their element size");
+    if (!aligned16(a->out)) return fail(KDA_ERR_ALIGN, "out must be 16-byte aligned");
+    rc = check_pool(a->state, a->state_dtype, a->num_slots, a->slot_stride, a->H);
+    if (rc) return rc;
+    const int64_t R = a->rows;
+    Range w[3] = {span(a->out, (uint64_t)R * HC * 2, "out"),
+                  span(a->state, pool_bytes(a->state_dtype, a->num_slots, a->slot_stride, a->H), "state"),
+                  span(a->conv_state, rows_extent(a->num_slots, a->conv_slot_stride, 3 * C3) * 2,
+                       "conv_state")};
+    Range r[10] = {span(a->x, rows_extent(R, a->x_stride, C3) * 2, "x"),
+                   span(a->weight, (uint64_t)12 * HC * 4, "weight"),
+                   span(a->raw_gate, rows_extent(R, a->gate_stride, HC) * 2, "raw_gate"),
+                   span(a->raw_beta, rows_extent(R, a->beta_stride, a->H) * 2, "raw_beta"),
+                   span(a->A_log, (uint64_t)a->H * 4, "A_log"),
+                   span(a->dt_bias, (uint64_t)HC * 4, "dt_bias"),
+                   span(a->state_indices, (uint64_t)R * 4, "state_indices"),
+                   span(a->output_gate, rows_extent(R, a->ogate_stride, HC) * 2, "output_gate"),
+                   span(a->norm_weight, (uint64_t)KD * 4, "norm_weight"),
+                   Range{0, 0, ""}};
+    rc = check_alias(w, 3, r, 9);
+    if (rc) return rc;
+    const int64_t items = R * a->H;
+    if (items > 0x7fffffffLL) return fail(KDA_ERR_SHAPE, "too many work items");
+    l->family = KERNEL_FUSED;
+    l->vsplit = 1;
+    l->rows_per_block = KD;
+    l->grid = (int32_t)items;
+    l->block = 256;
+    l->bf16_state = a->state_dtype == KDA_DTYPE_BF16;
+
+    p->x = static_cast<const uint16_t *>(a->x);
+    p->x_stride = a->x_stride;
+    p->weight = a->weight;
+    p->conv_state = static_cast<uint16_t *>(a->conv_state);
+    p->conv_slot_stride = a->conv_slot_stride;
+    p->graw = static_cast<const uint16_t *>(a->raw_gate);
+    p->g_stride = a->gate_stride;
+    p->braw = static_cast<const uint16_t *>(a->raw_beta);
+    p->beta_stride = a->beta_stride;
+    p->A_log = a->A_log;
+    p->dt_bias = a->dt_bias;
+    p->state_indices = a->state_indices;
+    p->state = a->state;
+    p->num_slots = a->num_slots;
+    p->slot_stride = a->slot_stride;
+    p->ogate = static_cast<const uint16_t *>(a->output_gate);
+    p->ogate_stride = a->ogate_stride;
+    p->norm_weight = a->norm_weight;
+    p->norm_eps = a->norm_eps;
+    p->scale = 1.0f / sqrtf((float)KD);
+    p->l2_eps = 1e-6f;
+    p->out = static_cast<uint16_t *>(a->out);
+    p->rows = a->rows;
+    p->H = a->H;
+    return ok();
+}
+
+int check_current_device()
+{
+    int dev = -1;
+    int r = current_device_is_gfx950(&dev);
+    if (r < 0) return fail(KDA_ERR_DEVICE, "HIP error while querying the device: %s", last_hip_error());
+    if (r == 0) return fail(KDA_ERR_DEVICE, "device %d is not a gfx950 (MI355X)", dev);
+    return KDA_OK;
+}
+
+int launched(int rc)
+{
+    if (rc) return fail(KDA_ERR_LAUNCH, "kernel launch failed: %s", last_hip_error());
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+KDA_API int kda_recurrent_plan(const kda_recurrent_args *args, kda_launch_plan *plan)
+{
+    RecParams p;
+    Launch l;
+    int rc = prepare_recurrent(args, &p, &l);
+    if (rc) return rc;
+    fill_plan(plan, l, (int64_t)args->n_seqs * args->H);
+    return KDA_OK;
+}
+
+KDA_API int kda_recurrent(const kda_recurrent_args *args, void *stream)
+{
+    RecParams p;
+    Launch l;
+    int rc = prepare_recurrent(args, &p, &l);
+    if (rc) return rc;
+    if (args->n_tokens == 0) return ok();  // every sequence is empty: nothing to do
+    rc = check_current_device();
+    if (rc) return rc;
+    return launched(launch_recurrent(p, l, stream));
+}
+
+KDA_API int kda_packed_plan(const kda_packed_args *args, kda_launch_plan *plan)
+{
+    kda_recurrent_args r;
+    int rc = packed_to_recurrent(args, &r);
+    if (rc) return rc;
+    return kda_recurrent_plan(&r, plan);
+}
+
+KDA_API int kda_packed_decode(const kda_packed_args *args, void *stream)
+{
+    kda_recurrent_args r;
+    int rc = packed_to_recurrent(args, &r);
+    if (rc) return rc;
+    return kda_recurrent(&r, stream);
+}
+
+KDA_API int kda_fused_plan(const kda_fused_args *args, kda_launch_plan *plan)
+{
+    FusedParams p;
+    Launch l;
+    int rc = prepare_fused(args, &p, &l);
+    if (rc) return rc;
+    fill_plan(plan, l, (int64_t)args->rows * args->H);
+    return KDA_OK;
+}
+
+KDA_API int kda_fused_decode(const kda_fused_args *args, void *stream)
+{
+    FusedParams p;
+    Launch l;
+    int rc = prepare_fused(args, &p, &l);
+    if (rc) return rc;
+    rc = check_current_device();
+    if (rc) return rc;
+    return launched(launch_fused(p, l, stream));
+}
+
+KDA_API const char *kda_status_string(int status)
+{
+    switch (status) {
+    case KDA_OK: return "ok";
+    case KDA_ERR_NULLPTR: return "null pointer";
+    case KDA_ERR_SHAPE: return "invalid shape";
+    case KDA_ERR_DTYPE: return "invalid dtype";
+    case KDA_ERR_STRIDE: return "invalid stride";
+    case KDA_ERR_ALIGN: return "misaligned pointer or stride";
+    case KDA_ERR_ALIAS: return "aliasing buffers";
+    case KDA_ERR_UNSUPPORTED: return "unsupported mode";
+    case KDA_ERR_DEVICE: return "unsupported device";
+    case KDA_ERR_LAUNCH: return "kernel launch failed";
+    case KDA_ERR_ABI: return "ABI struct size mismatch";
+    default: return "unknown status";
+    }
+}
+
+KDA_API const char *kda_last_error(void) { return g_err; }
+
+KDA_API int kda_version(void) { return KDA_ABI_VERSION; }
+
+KDA_API int kda_check_device(int device)
+{
+    int r = device_is_gfx950(device);
+    if (r < 0) return fail(KDA_ERR_DEVICE, "HIP error while querying device %d: %s", device, last_hip_error());
+    if (r == 0) return fail(KDA_ERR_DEVICE, "device %d is not a gfx950 (MI355X)", device);
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,71 @@
+// kda_internal.h -- parameter blocks passed from the host validator to the
+// gfx950 kernels of libkda_mi355x.so (not part of the public ABI).
+#pragma once
+#include <stdint.h>
+
+namespace kda_detail {
+
+constexpr int KD = 128;  // K = V = 128
+
+enum KernelFamily : int32_t {
+    KERNEL_RECURRENT_T1 = 1,   // one token per sequence
+    KERNEL_RECURRENT_VARLEN = 2,  // ragged token loop with the state held in registers
+    KERNEL_FUSED = 3,          // conv + SiLU -> KDA -> gated RMSNorm
+};
+
+// Recurrence over (sequence, head, value slice) work items; serves
+// recurrent_kda (T=1 and ragged T>=0) and packed_kda_decode.
+struct RecParams {
+    const uint16_t *q, *k, *v, *g, *beta;  // bf16
+    int64_t q_stride, k_stride, v_stride, g_stride, beta_stride;  // per token, elements
+    const float *A_log, *dt_bias;
+    float scale, l2_eps;
+    void *state;                 // fp32 or bf16 pool, [slot][h][v][k]
+    int64_t num_slots, slot_stride;
+    const int32_t *state_indices;
+    const int32_t *cu_seqlens;   // nullptr: token i belongs to sequence i
+    void *ckpt;                  // nullptr or [n_tokens][H][128][128], state dtype
+    uint16_t *out;               // bf16 [n_tokens][H][128]
+    int32_t n_seqs, n_tokens, H;
+    int32_t vsplit;              // workgroups per (sequence, head)
+};
+
+struct FusedParams {
+    const uint16_t *x;
+    int64_t x_stride;
+    const float *weight;         // [3][4][H*128]
+    uint16_t *conv_state;
+    int64_t conv_slot_stride;
+    const uint16_t *graw;
+    int64_t g_stride;
+    const uint16_t *braw;
+    int64_t beta_stride;
+    const float *A_log, *dt_bias;
+    const int32_t *state_indices;
+    void *state;
+    int64_t num_slots, slot_stride;
+    const uint16_t *ogate;
+    int64_t ogate_stride;
+    const float *norm_weight;
+    float norm_eps, scale, l2_eps;
+    uint16_t *out;               // bf16 [rows][H][128]
+    int32_t rows, H;
+};
+
+struct Launch {
+    int32_t family;
+    int32_t rows_per_block;  // 16 * G
+    int32_t vsplit;
+    int32_t grid;
+    int32_t block;
+    int32_t bf16_state;
+};
+
+// Implemented in kda_kernels.hip.  Return 0 or a negative kda_status.
+int launch_recurrent(const RecParams &p, const Launch &l, void *stream);
+int launch_fused(const FusedParams &p, const Launch &l, void *stream);
+int current_device_is_gfx950(int *device_out);  // 1 yes, 0 no, <0 HIP error
+int device_is_gfx950(int device);
+const char *last_hip_error();
+
+}  // namespace kda_detail

@@ -1,0 +1,562 @@
+// kda_kernels.hip -- gfx950 (CDNA4) kernels of the KDA decode step.
+//
+// The step is matrix-vector work on a 128 x 128 state per (row, head): per
+// value row it needs two 128-long dot products (k.S and q.S), a rank-1
+// update and one output value, i.e. ~7 flop per state element against 8
+// (fp32) or 4 (bf16) bytes of HBM read+write.  That is far below the
+// MFMA/VALU ridge, so the kernels are built for HBM streaming, not matrix
+// cores:
+//
+//  * A workgroup of 256 threads (4 wave64) owns one (row, head) and a slice
+//    of VT = 16*G value rows.  Inside a wave the 16 lanes of one DPP row own
+//    one value row at a time; lane m holds 8 key channels of it, so one
+//    value row's dot products reduce with four DPP adds inside the DPP row
+//    (quad_perm x2, row_half_mirror, row_mirror) and no LDS traffic.
+//  * The state slice is loaded once with dwordx4 accesses into VGPRs
+//    (64 VGPRs at G=8 fp32, 32 packed at bf16), updated in registers and
+//    written back with dwordx4 stores.  For fp32 a lane owns key channels
+//    {4m..4m+3} and {64+4m..64+4m+3}, so each load instruction of the 16
+//    lanes covers 256 contiguous bytes of one value row; for bf16 a lane owns
+//    {8m..8m+7} and one instruction covers a whole 256-byte value row.
+//  * Per token, threads 0..255 stage q, k, v and the per-channel decay in
+//    LDS (the gate transform is evaluated once per channel), one barrier,
+//    then every lane reads its 8 channels.  The L2 norms reduce in the DPP
+//    row as well.  The LDS stage is double-buffered by token parity, so the
+//    ragged token loop needs one barrier per token.
+//  * The slot base is one 64-bit pointer per workgroup; everything inside a
+//    head is 32-bit offsets.
+//  * Null rows (index below the call's first live index, or >= num_slots)
+//    write zeros and touch no state.
+//
+// Pages: "flashinfer.kda_decode" (recurrent_kda T=1 and packed T>=2;
+// Kimi-Linear in-kernel gate -exp(A_log)*softplus(g+dt_bias), beta sigmoid;
+// packed Kimi K3 decode with -1 inactive rows), "flashinfer.kda_decode.
+// fused_kda_decode" (Parameters), "feat(cake_kda): add serving-native packed
+// decode backend" (Exact contract: scale 1/sqrt(128), L2 eps 1e-6) and
+// "feat(kda): add fused speculative decode kernel" (per-token checkpoints).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kda_internal.h"
+
+namespace kda_detail {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------- bf16 ----
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Two floats -> two bf16 (round to nearest even), low half first.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    const __bf16 a = (__bf16)lo;
+    const __bf16 b = (__bf16)hi;
+    return (uint32_t)__builtin_bit_cast(uint16_t, a) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+// ---------------------------------------------------------- reductions ----
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x)
+{
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the 16 lanes of a DPP row.  Every lane of the row ends with the
+// same bits (each step adds two equal-valued partners, and + commutes).
+__device__ __forceinline__ float row_sum16(float x)
+{
+    x += dpp_mov<0xB1>(x);   // quad_perm [1,0,3,2]
+    x += dpp_mov<0x4E>(x);   // quad_perm [2,3,0,1]
+    x += dpp_mov<0x141>(x);  // row_half_mirror
+    x += dpp_mov<0x140>(x);  // row_mirror
+    return x;
+}
+
+__device__ __forceinline__ void row_sum16x2(float &a, float &b)
+{
+    a += dpp_mov<0xB1>(a); b += dpp_mov<0xB1>(b);
+    a += dpp_mov<0x4E>(a); b += dpp_mov<0x4E>(b);
+    a += dpp_mov<0x141>(a); b += dpp_mov<0x141>(b);
+    a += dpp_mov<0x140>(a); b += dpp_mov<0x140>(b);
+}
+
+__device__ __forceinline__ void row_sum16x3(float &a, float &b, float &c)
+{
+    a += dpp_mov<0xB1>(a); b += dpp_mov<0xB1>(b); c += dpp_mov<0xB1>(c);
+    a += dpp_mov<0x4E>(a); b += dpp_mov<0x4E>(b); c += dpp_mov<0x4E>(c);
+    a += dpp_mov<0x141>(a); b += dpp_mov<0x141>(b); c += dpp_mov<0x141>(c);
+    a += dpp_mov<0x140>(a); b += dpp_mov<0x140>(b); c += dpp_mov<0x140>(c);
+}
+
+// ---------------------------------------------------------- scalar math ----
+
+__device__ __forceinline__ float softplus_f(float x) { return fmaxf(x, 0.0f) + log1pf(__expf(-fabsf(x))); }
+__device__ __forceinline__ float sigmoid_f(float x) { return 1.0f / (1.0f + __expf(-x)); }
+
+// --------------------------------------------------------- state tiles ----
+//
+// A lane's share of one value row: 8 fp32 values (key channels kc(0..7)).
+// StateIO<bf16> maps a lane to channels 8m..8m+7 (one 16-byte access of a
+// 256-byte bf16 row); StateIO<fp32> maps it to 4m..4m+3 and 64+4m..64+4m+3
+// (two 16-byte accesses, each instruction covering 256 contiguous bytes).
+
+template <bool BF16> struct StateIO;
+
+template <> struct StateIO<false> {
+    typedef float elem;
+    struct Raw { f32x4 a, b; };
+    static __device__ __forceinline__ int chan(int m, int e) { return e < 4 ? 4 * m + e : 64 + 4 * m + (e - 4); }
+    static __device__ __forceinline__ Raw load(const float *row, int m)
+    {
+        Raw r;
+        r.a = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(row + 4 * m));
+        r.b = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(row + 64 + 4 * m));
+        return r;
+    }
+    static __device__ __forceinline__ void unpack(const Raw &r, float s[8])
+    {
+        s[0] = r.a.x; s[1] = r.a.y; s[2] = r.a.z; s[3] = r.a.w;
+        s[4] = r.b.x; s[5] = r.b.y; s[6] = r.b.z; s[7] = r.b.w;
+    }
+    static __device__ __forceinline__ Raw pack(const float s[8])
+    {
+        Raw r;
+        r.a = f32x4{s[0], s[1], s[2], s[3]};
+        r.b = f32x4{s[4], s[5], s[6], s[7]};
+        return r;
+    }
+    static __device__ __forceinline__ void store(float *row, int m, const Raw &r)
+    {
+        __builtin_nontemporal_store(r.a, reinterpret_cast<f32x4 *>(row + 4 * m));
+        __builtin_nontemporal_store(r.b, reinterpret_cast<f32x4 *>(row + 64 + 4 * m));
+    }
+};
+
+template <> struct StateIO<true> {
+    typedef uint16_t elem;
+    struct Raw { u32x4 w; };
+    static __device__ __forceinline__ int chan(int m, int e) { return 8 * m + e; }
+    static __device__ __forceinline__ Raw load(const uint16_t *row, int m)
+    {
+        Raw r;
+        r.w = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(row + 8 * m));
+        return r;
+    }
+    static __device__ __forceinline__ void unpack(const Raw &r, float s[8])
+    {
+        s[0] = bf16_lo(r.w.x); s[1] = bf16_hi(r.w.x);
+        s[2] = bf16_lo(r.w.y); s[3] = bf16_hi(r.w.y);
+        s[4] = bf16_lo(r.w.z); s[5] = bf16_hi(r.w.z);
+        s[6] = bf16_lo(r.w.w); s[7] = bf16_hi(r.w.w);
+    }
+    static __device__ __forceinline__ Raw pack(const float s[8])
+    {
+        Raw r;
+        r.w = u32x4{pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3]),
+                    pack_bf16x2(s[4], s[5]), pack_bf16x2(s[6], s[7])};
+        return r;
+    }
+    static __device__ __forceinline__ void store(uint16_t *row, int m, const Raw &r)
+    {
+        __builtin_nontemporal_store(r.w, reinterpret_cast<u32x4 *>(row + 8 * m));
+    }
+};
+
+// Store G consecutive bf16 outputs (G in {1,2,4,8}) from one lane.
+template <int G>
+__device__ __forceinline__ void store_out_bf16(uint16_t *dst, const float *o)
+{
+    if constexpr (G == 8) {
+        *reinterpret_cast<u32x4 *>(dst) =
+            u32x4{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
+                  pack_bf16x2(o[6], o[7])};
+    } else if constexpr (G == 4) {
+        *reinterpret_cast<u32x2 *>(dst) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+    } else if constexpr (G == 2) {
+        *reinterpret_cast<uint32_t *>(dst) = pack_bf16x2(o[0], o[1]);
+    } else {
+        *dst = (uint16_t)(pack_bf16x2(o[0], 0.0f) & 0xffffu);
+    }
+}
+
+template <int G>
+__device__ __forceinline__ void store_zero_bf16(uint16_t *dst)
+{
+    float z[G];
+#pragma unroll
+    for (int i = 0; i < G; ++i) z[i] = 0.0f;
+    store_out_bf16<G>(dst, z);
+}
+
+// Per-lane operands of one token: normalised q (scale folded in), normalised
+// k and the decay, at the lane's 8 key channels, plus beta and q_hat.k_hat.
+struct TokenOps {
+    float q[8], k[8], d[8];
+    float beta, qk;
+};
+
+template <bool BF16>
+__device__ __forceinline__ void read_token_ops(TokenOps &t, const float *sq, const float *sk,
+                                               const float *sd, int m, float scale, float eps,
+                                               float beta)
+{
+    float ss_q = 0.f, ss_k = 0.f, s_qk = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int c = StateIO<BF16>::chan(m, e);
+        t.q[e] = sq[c];
+        t.k[e] = sk[c];
+        t.d[e] = sd[c];
+        ss_q = fmaf(t.q[e], t.q[e], ss_q);
+        ss_k = fmaf(t.k[e], t.k[e], ss_k);
+        s_qk = fmaf(t.q[e], t.k[e], s_qk);
+    }
+    row_sum16x3(ss_q, ss_k, s_qk);
+    const float rq = rsqrtf(ss_q + eps) * scale;
+    const float rk = rsqrtf(ss_k + eps);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        t.q[e] *= rq;
+        t.k[e] *= rk;
+    }
+    t.qk = s_qk * rq * rk;
+    t.beta = beta;
+}
+
+// One token on one value row held as 8 fp32 values per lane:
+//   s <- d*s;  a = k.s;  c = q.s;  u = v - a;  s <- s + beta*u*k;
+//   o = c + beta*u*(q.k)       (= scale * q_hat . s_new)
+__device__ __forceinline__ float row_update(float s[8], const TokenOps &t, float v)
+{
+    float pa = 0.f, pc = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        s[e] *= t.d[e];
+        pa = fmaf(t.k[e], s[e], pa);
+        pc = fmaf(t.q[e], s[e], pc);
+    }
+    row_sum16x2(pa, pc);
+    const float bu = t.beta * (v - pa);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s[e] = fmaf(bu, t.k[e], s[e]);
+    return fmaf(bu, t.qk, pc);
+}
+
+// Stage one token of channel data into LDS: threads 0..127 handle q, k and
+// the gate of channel tid; threads 128..255 copy v of channel tid-128.
+__device__ __forceinline__ void stage_token(int tid, const uint16_t *q, const uint16_t *k,
+                                            const uint16_t *v, const uint16_t *g,
+                                            const float *dt_bias_h, float a_h, float *sq, float *sk,
+                                            float *sd, float *sv)
+{
+    if (tid < KD) {
+        sq[tid] = bf16_bits_to_f32(q[tid]);
+        sk[tid] = bf16_bits_to_f32(k[tid]);
+        const float x = bf16_bits_to_f32(g[tid]) + dt_bias_h[tid];
+        sd[tid] = __expf(-a_h * softplus_f(x));
+    } else {
+        sv[tid - KD] = bf16_bits_to_f32(v[tid - KD]);
+    }
+}
+
+// ------------------------------------------------------- recurrent kernel ----
+
+template <int G, bool BF16, bool VARLEN>
+__global__ void __launch_bounds__(256) kda_recurrent_kernel(const RecParams p)
+{
+    using IO = StateIO<BF16>;
+    using E = typename IO::elem;
+    constexpr int VT = 16 * G;  // value rows per workgroup
+
+    __shared__ float s_q[2][KD], s_k[2][KD], s_d[2][KD], s_v[2][KD];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int m = lane & 15;   // position inside the DPP row
+    const int qd = lane >> 4;  // DPP row inside the wave
+
+    const int blk = blockIdx.x;
+    const int vs = blk % p.vsplit;
+    const int item = blk / p.vsplit;
+    const int seq = item / p.H;
+    const int h = item - seq * p.H;
+    const int r_base = vs * VT + wave * (4 * G) + qd * G;  // this lane's first value row
+
+    int t0, t1;
+    if constexpr (VARLEN) {
+        t0 = max(p.cu_seqlens[seq], 0);
+        t1 = min(p.cu_seqlens[seq + 1], p.n_tokens);
+    } else {
+        t0 = seq;
+        t1 = seq + 1;
+    }
+    const int idx = p.state_indices[seq];
+    if (idx < 0 || (int64_t)idx >= p.num_slots) {
+        if (m == 0)
+            for (int t = t0; t < t1; ++t)
+                store_zero_bf16<G>(p.out + ((int64_t)t * p.H + h) * KD + r_base);
+        return;
+    }
+    if (t1 <= t0) return;
+
+    E *head = reinterpret_cast<E *>(p.state) + (int64_t)idx * p.slot_stride + (int64_t)h * (KD * KD);
+
+    // Issue every state load of this lane before anything else.
+    typename IO::Raw raw[G];
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi) raw[gi] = IO::load(head + (r_base + gi) * KD, m);
+
+    const float a_h = __expf(p.A_log[h]);
+    const float *dtb = p.dt_bias + (int64_t)h * KD;
+
+    if constexpr (!VARLEN) {
+        // T=1: stage the token while the state loads are in flight, then
+        // update and store value row by value row.
+        const int t = t0;
+        stage_token(tid, p.q + (int64_t)t * p.q_stride + h * KD, p.k + (int64_t)t * p.k_stride + h * KD,
+                    p.v + (int64_t)t * p.v_stride + h * KD, p.g + (int64_t)t * p.g_stride + h * KD,
+                    dtb, a_h, s_q[0], s_k[0], s_d[0], s_v[0]);
+        const float beta = sigmoid_f(bf16_bits_to_f32(p.beta[(int64_t)t * p.beta_stride + h]));
+        __syncthreads();
+        TokenOps ops;
+        read_token_ops<BF16>(ops, s_q[0], s_k[0], s_d[0], m, p.scale, p.l2_eps, beta);
+        float o[G];
+#pragma unroll
+        for (int gi = 0; gi < G; ++gi) {
+            float s[8];
+            IO::unpack(raw[gi], s);
+            o[gi] = row_update(s, ops, s_v[0][r_base + gi]);
+            IO::store(head + (r_base + gi) * KD, m, IO::pack(s));
+        }
+        if (m == 0) store_out_bf16<G>(p.out + ((int64_t)t * p.H + h) * KD + r_base, o);
+    } else {
+        // Ragged token loop: the state stays in registers across the tokens
+        // of the sequence; after each token the checkpoint (if requested) and
+        // the output are written; the pool slot is written once at the end.
+        float st[G][8];
+#pragma unroll
+        for (int gi = 0; gi < G; ++gi) IO::unpack(raw[gi], st[gi]);
+        for (int t = t0; t < t1; ++t) {
+            const int buf = (t - t0) & 1;
+            stage_token(tid, p.q + (int64_t)t * p.q_stride + h * KD,
+                        p.k + (int64_t)t * p.k_stride + h * KD, p.v + (int64_t)t * p.v_stride + h * KD,
+                        p.g + (int64_t)t * p.g_stride + h * KD, dtb, a_h, s_q[buf], s_k[buf],
+                        s_d[buf], s_v[buf]);
+            const float beta = sigmoid_f(bf16_bits_to_f32(p.beta[(int64_t)t * p.beta_stride + h]));
+            __syncthreads();
+            TokenOps ops;
+            read_token_ops<BF16>(ops, s_q[buf], s_k[buf], s_d[buf], m, p.scale, p.l2_eps, beta);
+            float o[G];
+#pragma unroll
+            for (int gi = 0; gi < G; ++gi) o[gi] = row_update(st[gi], ops, s_v[buf][r_base + gi]);
+            if (m == 0) store_out_bf16<G>(p.out + ((int64_t)t * p.H + h) * KD + r_base, o);
+            if (p.ckpt) {
+                E *ck = reinterpret_cast<E *>(p.ckpt) + ((int64_t)t * p.H + h) * (KD * KD);
+#pragma unroll
+                for (int gi = 0; gi < G; ++gi) IO::store(ck + (r_base + gi) * KD, m, IO::pack(st[gi]));
+            }
+        }
+#pragma unroll
+        for (int gi = 0; gi < G; ++gi) IO::store(head + (r_base + gi) * KD, m, IO::pack(st[gi]));
+    }
+}
+
+// ---------------------------------------------------------- fused kernel ----
+//
+// One workgroup per (row, head) with the full V=128 (the gated RMSNorm needs
+// all 128 outputs of the head).  Threads 0..383 (two passes of 256) own one
+// of the head's 384 q|k|v channels for the conv: each reads its 3 cached
+// positions and x, writes the SiLU activation to LDS and shifts its own cache
+// column, so no other thread touches that channel.
+
+template <bool BF16>
+__global__ void __launch_bounds__(256) kda_fused_kernel(const FusedParams p)
+{
+    using IO = StateIO<BF16>;
+    using E = typename IO::elem;
+    constexpr int G = 8;
+
+    __shared__ float s_act[3 * KD];  // q | k | v activations of this head
+    __shared__ float s_d[KD];
+    __shared__ float s_red[16];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int m = lane & 15;
+    const int qd = lane >> 4;
+    const int row = blockIdx.x / p.H;
+    const int h = blockIdx.x - row * p.H;
+    const int r_base = wave * (4 * G) + qd * G;
+    uint16_t *out = p.out + ((int64_t)row * p.H + h) * KD;
+
+    const int idx = p.state_indices[row];
+    if (idx <= 0 || (int64_t)idx >= p.num_slots) {
+        if (m == 0) store_zero_bf16<G>(out + r_base);
+        return;
+    }
+
+    E *head = reinterpret_cast<E *>(p.state) + (int64_t)idx * p.slot_stride + (int64_t)h * (KD * KD);
+    typename IO::Raw raw[G];
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi) raw[gi] = IO::load(head + (r_base + gi) * KD, m);
+
+    // depthwise causal conv (width 4) + SiLU, cache shift
+    const int HC = p.H * KD;
+    const int C3 = 3 * HC;
+    uint16_t *cs = p.conv_state + (int64_t)idx * p.conv_slot_stride;
+    const uint16_t *xr = p.x + (int64_t)row * p.x_stride;
+    for (int cl = tid; cl < 3 * KD; cl += 256) {
+        const int grp = cl >> 7;
+        const int d = cl & (KD - 1);
+        const int c = grp * HC + h * KD + d;
+        const uint16_t c0 = cs[c], c1 = cs[C3 + c], c2 = cs[2 * C3 + c];
+        const uint16_t xv = xr[c];
+        const float *w = p.weight + (int64_t)grp * 4 * HC + h * KD + d;
+        float y = w[0] * bf16_bits_to_f32(c0);
+        y = fmaf(w[HC], bf16_bits_to_f32(c1), y);
+        y = fmaf(w[2 * HC], bf16_bits_to_f32(c2), y);
+        y = fmaf(w[3 * HC], bf16_bits_to_f32(xv), y);
+        s_act[cl] = y * sigmoid_f(y);
+        cs[c] = c1;
+        cs[C3 + c] = c2;
+        cs[2 * C3 + c] = xv;
+    }
+    if (tid < KD) {
+        const float x = bf16_bits_to_f32(p.graw[(int64_t)row * p.g_stride + h * KD + tid]) +
+                        p.dt_bias[(int64_t)h * KD + tid];
+        s_d[tid] = __expf(-__expf(p.A_log[h]) * softplus_f(x));
+    }
+    const float beta = sigmoid_f(bf16_bits_to_f32(p.braw[(int64_t)row * p.beta_stride + h]));
+    __syncthreads();
+
+    TokenOps ops;
+    read_token_ops<BF16>(ops, s_act, s_act + KD, s_d, m, p.scale, p.l2_eps, beta);
+    float o[G];
+    float st[8];
+    float ss = 0.f;
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi) {
+        IO::unpack(raw[gi], st);
+        o[gi] = row_update(st, ops, s_act[2 * KD + r_base + gi]);
+        IO::store(head + (r_base + gi) * KD, m, IO::pack(st));
+        ss = fmaf(o[gi], o[gi], ss);
+    }
+    // gated RMSNorm over the 128 outputs of the head
+    if (m == 0) s_red[wave * 4 + qd] = ss;
+    __syncthreads();
+    float tot = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) tot += s_red[i];
+    const float inv = rsqrtf(tot * (1.0f / KD) + p.norm_eps);
+    if (m == 0) {
+        const uint16_t *gate = p.ogate + (int64_t)row * p.ogate_stride + h * KD + r_base;
+        float y[G];
+#pragma unroll
+        for (int gi = 0; gi < G; ++gi)
+            y[gi] = o[gi] * inv * p.norm_weight[r_base + gi] * sigmoid_f(bf16_bits_to_f32(gate[gi]));
+        store_out_bf16<G>(out + r_base, y);
+    }
+}
+
+// ------------------------------------------------------------ dispatch ----
+
+template <int G, bool BF16>
+hipError_t launch_rec_g(const RecParams &p, const Launch &l, hipStream_t s)
+{
+    if (l.family == KERNEL_RECURRENT_VARLEN)
+        hipLaunchKernelGGL((kda_recurrent_kernel<G, BF16, true>), dim3(l.grid), dim3(l.block), 0, s, p);
+    else
+        hipLaunchKernelGGL((kda_recurrent_kernel<G, BF16, false>), dim3(l.grid), dim3(l.block), 0, s, p);
+    return hipGetLastError();
+}
+
+template <bool BF16>
+hipError_t launch_rec_dt(const RecParams &p, const Launch &l, hipStream_t s)
+{
+    switch (l.rows_per_block) {
+    case 128: return launch_rec_g<8, BF16>(p, l, s);
+    case 64: return launch_rec_g<4, BF16>(p, l, s);
+    case 32: return launch_rec_g<2, BF16>(p, l, s);
+    case 16: return launch_rec_g<1, BF16>(p, l, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+thread_local char g_hip_err[256];
+
+int record(hipError_t e)
+{
+    if (e == hipSuccess) return 0;
+    const char *n = hipGetErrorString(e);
+    int i = 0;
+    for (; n && n[i] && i < 255; ++i) g_hip_err[i] = n[i];
+    g_hip_err[i] = 0;
+    return -9;  // KDA_ERR_LAUNCH
+}
+
+}  // namespace
+
+const char *last_hip_error() { return g_hip_err; }
+
+int launch_recurrent(const RecParams &p, const Launch &l, void *stream)
+{
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();  // a stale error must not be blamed on this launch
+    hipError_t e = l.bf16_state ? launch_rec_dt<true>(p, l, s) : launch_rec_dt<false>(p, l, s);
+    return record(e);
+}
+
+int launch_fused(const FusedParams &p, const Launch &l, void *stream)
+{
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    if (l.bf16_state)
+        hipLaunchKernelGGL(kda_fused_kernel<true>, dim3(l.grid), dim3(l.block), 0, s, p);
+    else
+        hipLaunchKernelGGL(kda_fused_kernel<false>, dim3(l.grid), dim3(l.block), 0, s, p);
+    return record(hipGetLastError());
+}
+
+int device_is_gfx950(int device)
+{
+    static int known[64];  // 0 unknown, 1 gfx950, 2 other
+    if (device < 0) return -1;
+    if (device < 64 && known[device]) return known[device] == 1;
+    hipDeviceProp_t prop;
+    hipError_t e = hipGetDeviceProperties(&prop, device);
+    if (e != hipSuccess) {
+        record(e);
+        return -1;
+    }
+    int ok = 1;
+    const char want[] = "gfx950";
+    for (int i = 0; i < 6; ++i)
+        if (prop.gcnArchName[i] != want[i]) ok = 0;
+    if (device < 64) known[device] = ok ? 1 : 2;
+    return ok;
+}
+
+int current_device_is_gfx950(int *device_out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        record(e);
+        return -1;
+    }
+    if (device_out) *device_out = dev;
+    return device_is_gfx950(dev);
+}
+
+}  // namespace kda_detail

@@ -1,0 +1,270 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) KDA decode library, libkda_mi355x.so.
+ *
+ * KDA (Kimi Delta Attention) decode: per (sequence, head) a 128 x 128 state
+ * S (K x V) is updated by a gated delta rule with one decay per key channel,
+ *     S <- diag(exp g) S;  u = v - S^T k;  S <- S + beta k u^T;  o = scale S^T q,
+ * with q and k L2-normalised in the kernel, g = -exp(A_log[h]) *
+ * softplus(raw_g + dt_bias) and beta = sigmoid(raw_beta).  Pages followed:
+ * "flashinfer.kda_decode" (function table; backend="cake" section for the
+ * in-kernel gate; "Serving-native packed Kimi K3 decode"), the
+ * "flashinfer.kda_decode.fused_kda_decode" Parameters list, and the PRs
+ * "feat(cake_kda): add serving-native packed decode backend" (Exact
+ * contract) and "feat(kda): add fused speculative decode kernel" (#4809,
+ * packed ragged T>=2 decode with per-token state checkpoints).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Pointers in the argument structs are DEVICE pointers owned by the
+ *    caller, unless stated otherwise.  The library allocates nothing, never
+ *    synchronises and never reads device memory on the host, so every call
+ *    can be captured into a HIP graph.  Each successful call enqueues exactly
+ *    one kernel on `stream` (a hipStream_t; NULL = the null stream), except a
+ *    ragged recurrent call with n_tokens == 0, which enqueues nothing.
+ *  - State pools have logical shape [num_slots, H, 128, 128] and store the
+ *    state transposed: element (slot, h, v, k) = S[k][v], at
+ *        state + slot*slot_stride + (h*128 + v)*128 + k     (elements).
+ *    The inner [H, 128, 128] block of each slot is contiguous; slot_stride
+ *    (in elements) is any value >= H*128*128 that keeps the 16-byte
+ *    alignment.  State dtype is fp32 or bf16; the recurrence runs in fp32 and
+ *    a bf16 state is rounded to nearest-even when written back
+ *    ("fused_kda_decode" Parameters: state).
+ *  - state_indices is a contiguous int32 array, one per row / sequence.
+ *    Null rows produce +0 outputs and leave every cache untouched
+ *    ("Serving-native packed Kimi K3 decode": -1 is inactive padding;
+ *    "fused_kda_decode" Parameters: non-positive indices are null, slot 0 is
+ *    reserved).  Indices >= num_slots also take the null path (no memory
+ *    access).  Active slots must be unique within one call (caller contract).
+ *  - bf16 data are IEEE-754 binary32 upper halves (uint16 bit patterns).
+ *  - Strides are in elements.  Errors are decided from the host-visible
+ *    arguments only; a failed call launches nothing and returns a negative
+ *    kda_status; kda_last_error() then gives a message (thread-local).
+ *    There is no fallback path.
+ */
+#ifndef KDA_MI355X_H
+#define KDA_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_API __attribute__((visibility("default")))
+#define KDA_ABI_VERSION 1
+#define KDA_HEAD_DIM 128
+
+typedef enum kda_status {
+    KDA_OK = 0,
+    KDA_ERR_NULLPTR = -1,     /* a required pointer is NULL */
+    KDA_ERR_SHAPE = -2,       /* sizes out of range or inconsistent */
+    KDA_ERR_DTYPE = -3,       /* unknown dtype code */
+    KDA_ERR_STRIDE = -4,      /* a stride is too small */
+    KDA_ERR_ALIGN = -5,       /* a base or stride breaks 16-byte alignment */
+    KDA_ERR_ALIAS = -6,       /* an output overlaps an input or another output */
+    KDA_ERR_UNSUPPORTED = -7, /* a mode the library does not implement */
+    KDA_ERR_DEVICE = -8,      /* the current device is not gfx950 */
+    KDA_ERR_LAUNCH = -9,      /* the HIP launch failed */
+    KDA_ERR_ABI = -10         /* struct_size does not match this library */
+} kda_status;
+
+typedef enum kda_dtype { KDA_DTYPE_F32 = 0, KDA_DTYPE_BF16 = 1 } kda_dtype;
+
+/* Gate transform.  SOFTPLUS: g = -exp(A_log[h]) * softplus(raw + dt_bias)
+ * (the Kimi-Linear gate, lower_bound=None on the pages).  LOWER_BOUND: the
+ * bounded Kimi K3 gate; the pages name it but do not define it, so every
+ * call asking for it returns KDA_ERR_UNSUPPORTED. */
+typedef enum kda_gate_mode { KDA_GATE_SOFTPLUS = 0, KDA_GATE_LOWER_BOUND = 1 } kda_gate_mode;
+
+/* Launch geometry chosen from host metadata only (for inspection/tests). */
+typedef struct kda_launch_plan {
+    uint32_t struct_size;
+    int32_t kernel;          /* internal kernel family id */
+    int32_t grid_x;          /* workgroups */
+    int32_t block;           /* threads per workgroup */
+    int32_t rows_per_block;  /* value rows of one (row, head) per workgroup */
+    int32_t vsplit;          /* workgroups per (row, head) = 128 / rows_per_block */
+    int64_t items;           /* (row or sequence) x head work items */
+} kda_launch_plan;
+
+/*
+ * recurrent_kda ("flashinfer.kda_decode" function table: recurrent_kda with
+ * one token per sequence (T=1) and packed speculative decode with T>=2).
+ *
+ *  n_seqs            sequences (rows), >= 1.
+ *  n_tokens          tokens: == n_seqs when cu_seqlens is NULL (T=1);
+ *                    otherwise cu_seqlens[n_seqs], >= 0.
+ *  H, HV             q/k heads and value heads; HV must equal H.
+ *  K, V              must both be 128.
+ *  q, k, v, g        bf16, token t head h at ptr + t*X_stride + h*128 (the
+ *                    inner [H,128] is contiguous); g is the raw gate.
+ *  beta              bf16 logits, token t head h at beta + t*beta_stride + h.
+ *  A_log, dt_bias    fp32 [H] and fp32 [H*128], contiguous.
+ *  scale             output scale (the pages use 1/sqrt(128)).
+ *  l2_eps            q/k L2-norm epsilon (the pages use 1e-6), >= 0.
+ *  gate_mode         kda_gate_mode (LOWER_BOUND is unsupported).
+ *  lower_bound       ignored for SOFTPLUS.
+ *  state             pool as described above; state_dtype its kda_dtype.
+ *  num_slots         slots in the pool, >= 1; slot_stride in elements.
+ *  state_indices     int32 [n_seqs]; idx < 0 or idx >= num_slots is null.
+ *  cu_seqlens        NULL (T=1) or int32 [n_seqs+1], cu_seqlens[0] == 0,
+ *                    non-decreasing (read on the device at every launch, so a
+ *                    captured graph follows new lengths; n_tokens must match
+ *                    its last entry).  Empty sequences touch nothing.
+ *  checkpoints       NULL or [n_tokens, H, 128, 128] contiguous in the pool's
+ *                    [v][k] layout, dtype ckpt_dtype: the state after each
+ *                    token.  Null sequences write no checkpoint.
+ *  out               bf16 [n_tokens, H, 128] contiguous.
+ */
+typedef struct kda_recurrent_args {
+    uint32_t struct_size;
+    int32_t n_seqs;
+    int32_t n_tokens;
+    int32_t H;
+    int32_t HV;
+    int32_t K;
+    int32_t V;
+    const void *q;
+    const void *k;
+    const void *v;
+    const void *g;
+    const void *beta;
+    int64_t q_stride;
+    int64_t k_stride;
+    int64_t v_stride;
+    int64_t g_stride;
+    int64_t beta_stride;
+    const float *A_log;
+    const float *dt_bias;
+    float scale;
+    float l2_eps;
+    int32_t gate_mode;
+    float lower_bound;
+    void *state;
+    int32_t state_dtype;
+    int32_t ckpt_dtype;
+    int64_t num_slots;
+    int64_t slot_stride;
+    const int32_t *state_indices;
+    const int32_t *cu_seqlens;
+    void *checkpoints;
+    void *out;
+} kda_recurrent_args;
+
+/*
+ * packed_kda_decode ("Serving-native packed Kimi K3 decode" on the
+ * flashinfer.kda_decode page; Exact contract of "feat(cake_kda): add
+ * serving-native packed decode backend").  T=1.  Fixed scale 1/sqrt(128)
+ * and L2 epsilon 1e-6.  The pages fix H=12 and a bf16 pool; this library
+ * accepts any H >= 1 and an fp32 or bf16 pool.
+ *
+ *  B                 rows, >= 1.
+ *  mixed_qkv         bf16 [B, 3*H*128] post-convolution projection: q at
+ *                    [0, H*128), k at [H*128, 2*H*128), v at [2*H*128,
+ *                    3*H*128); row stride qkv_stride >= 3*H*128.
+ *  raw_gate          bf16 [B, H*128], row stride gate_stride.
+ *  raw_beta          bf16 [B, H], row stride beta_stride.
+ *  state_indices     int32 [B]; -1 (any negative) is an inactive row.
+ *  out               bf16 [B, 1, H, 128] contiguous.
+ */
+typedef struct kda_packed_args {
+    uint32_t struct_size;
+    int32_t B;
+    int32_t H;
+    const void *mixed_qkv;
+    int64_t qkv_stride;
+    const void *raw_gate;
+    int64_t gate_stride;
+    const void *raw_beta;
+    int64_t beta_stride;
+    const float *A_log;
+    const float *dt_bias;
+    int32_t gate_mode;
+    float lower_bound;
+    void *state;
+    int32_t state_dtype;
+    int64_t num_slots;
+    int64_t slot_stride;
+    const int32_t *state_indices;
+    void *out;
+} kda_packed_args;
+
+/*
+ * fused_kda_decode ("flashinfer.kda_decode.fused_kda_decode": width-4
+ * depthwise causal conv + SiLU, one KDA update, gated RMSNorm).
+ *
+ *  rows              decode rows, >= 1.
+ *  x                 bf16 [rows, 3*H*128], channel-contiguous, row stride
+ *                    x_stride.
+ *  weight            fp32 [3, 4, H*128] contiguous: group (q|k|v), tap, channel.
+ *                    Tap 3 multiplies the current x, taps 0..2 the cache.
+ *  conv_state        bf16 cache [num_slots, 3*H*128, 3] with strides
+ *                    [conv_slot_stride, 1, 3*H*128]: position p (0 = oldest)
+ *                    of channel c at conv_state + slot*conv_slot_stride +
+ *                    p*3*H*128 + c.  Shifted by one position for live rows.
+ *  raw_gate          bf16 [rows, H*128] (row stride gate_stride).
+ *  raw_beta          bf16 [rows, H] (row stride beta_stride).
+ *  state_indices     int32 [rows]; live indices in [1, num_slots); idx <= 0
+ *                    (and idx >= num_slots) are null.
+ *  state             fp32 or bf16 pool, same num_slots as conv_state.
+ *  output_gate       bf16 [rows, H*128] logits (row stride ogate_stride).
+ *  norm_weight       fp32 [128].  norm_eps >= 0.
+ *  out               bf16 [rows, H, 128] contiguous:
+ *                    y = o / sqrt(mean(o^2) + eps) * w * sigmoid(gate).
+ *  Scale 1/sqrt(128) and L2 epsilon 1e-6 as in the packed call.
+ */
+typedef struct kda_fused_args {
+    uint32_t struct_size;
+    int32_t rows;
+    int32_t H;
+    const void *x;
+    int64_t x_stride;
+    const float *weight;
+    void *conv_state;
+    int64_t conv_slot_stride;
+    const void *raw_gate;
+    int64_t gate_stride;
+    const void *raw_beta;
+    int64_t beta_stride;
+    const float *A_log;
+    const float *dt_bias;
+    int32_t gate_mode;
+    float lower_bound;
+    const int32_t *state_indices;
+    void *state;
+    int32_t state_dtype;
+    int64_t num_slots;
+    int64_t slot_stride;
+    const void *output_gate;
+    int64_t ogate_stride;
+    const float *norm_weight;
+    float norm_eps;
+    void *out;
+} kda_fused_args;
+
+/* Validate and enqueue.  Return KDA_OK or a negative kda_status. */
+KDA_API int kda_recurrent(const kda_recurrent_args *args, void *stream);
+KDA_API int kda_packed_decode(const kda_packed_args *args, void *stream);
+KDA_API int kda_fused_decode(const kda_fused_args *args, void *stream);
+
+/* Validate only (no HIP call, no device access) and report the launch
+ * geometry the matching entry point would use.  `plan` may be NULL. */
+KDA_API int kda_recurrent_plan(const kda_recurrent_args *args, kda_launch_plan *plan);
+KDA_API int kda_packed_plan(const kda_packed_args *args, kda_launch_plan *plan);
+KDA_API int kda_fused_plan(const kda_fused_args *args, kda_launch_plan *plan);
+
+/* Static text of a status code. */
+KDA_API const char *kda_status_string(int status);
+/* Detail of the last failure on the calling thread ("" if none). */
+KDA_API const char *kda_last_error(void);
+/* KDA_ABI_VERSION of the loaded library. */
+KDA_API int kda_version(void);
+/* KDA_OK if HIP device `device` is a gfx950, else KDA_ERR_DEVICE. */
+KDA_API int kda_check_device(int device);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_MI355X_H */

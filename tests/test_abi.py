@@ -1,0 +1,280 @@
+"""Host-only checks of the C ABI: the library loads, exports every entry point
+include/kda.h declares, and validates arguments from host metadata alone
+(the *_plan entry points never touch a device, so fake device addresses are
+fine here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from gated_delta_rule_decode_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+D = 128
+
+
+def lib():
+    return _lib.load()
+
+
+def test_header_symbols_exported():
+    text = open(HEADER).read()
+    declared = re.findall(r"KDA_API\s+[\w\s\*]+?\b(kda_\w+)\s*\(", text)
+    assert set(declared) == set(_lib.EXPORTS)
+    L = lib()
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def test_version_and_status_strings():
+    L = lib()
+    assert L.kda_version() == 1
+    for code in _lib.STATUS:
+        assert L.kda_status_string(code).decode()
+    assert L.kda_status_string(12345).decode() == "unknown status"
+
+
+def test_struct_layouts_match_header():
+    """The C side rejects any struct_size other than its own sizeof, so a
+    valid plan call proves the ctypes mirrors have the C layout."""
+    r = rec_args()
+    assert plan_rec(r)[0] == 0
+    r.struct_size += 8
+    assert plan_rec(r)[0] == -10
+    p = packed_args()
+    assert plan_packed(p)[0] == 0
+    f = fused_args()
+    assert plan_fused(f)[0] == 0
+
+
+# ---- fake address space: disjoint, 16-byte aligned "device" buffers --------------
+
+class Arena:
+    def __init__(self):
+        self.next = 1 << 32
+
+    def take(self, nbytes):
+        a = self.next
+        self.next += (nbytes + 4096 + 255) & ~255
+        return a
+
+
+def rec_args(N=4, H=4, T=None, slots=8, bf16=False, varlen=False):
+    A = Arena()
+    T = N if T is None else T
+    a = _lib.RecurrentArgs()
+    a.struct_size = ctypes.sizeof(_lib.RecurrentArgs)
+    a.n_seqs, a.n_tokens, a.H, a.HV, a.K, a.V = N, T, H, H, D, D
+    for f in ("q", "k", "v", "g"):
+        setattr(a, f, A.take(T * H * D * 2))
+        setattr(a, f + "_stride", H * D)
+    a.beta = A.take(T * H * 2)
+    a.beta_stride = H
+    a.A_log = A.take(H * 4)
+    a.dt_bias = A.take(H * D * 4)
+    a.scale, a.l2_eps = 0.08838834764831845, 1e-6
+    es = 2 if bf16 else 4
+    a.state = A.take(slots * H * D * D * es)
+    a.state_dtype = a.ckpt_dtype = 1 if bf16 else 0
+    a.num_slots, a.slot_stride = slots, H * D * D
+    a.state_indices = A.take(N * 4)
+    if varlen:
+        a.cu_seqlens = A.take((N + 1) * 4)
+    a.out = A.take(T * H * D * 2)
+    return a
+
+
+def packed_args(B=8, H=12, slots=16):
+    A = Arena()
+    a = _lib.PackedArgs()
+    a.struct_size = ctypes.sizeof(_lib.PackedArgs)
+    a.B, a.H = B, H
+    a.mixed_qkv, a.qkv_stride = A.take(B * 3 * H * D * 2), 3 * H * D
+    a.raw_gate, a.gate_stride = A.take(B * H * D * 2), H * D
+    a.raw_beta, a.beta_stride = A.take(B * H * 2), H
+    a.A_log, a.dt_bias = A.take(H * 4), A.take(H * D * 4)
+    a.state, a.state_dtype = A.take(slots * H * D * D * 2), 1
+    a.num_slots, a.slot_stride = slots, H * D * D
+    a.state_indices = A.take(B * 4)
+    a.out = A.take(B * H * D * 2)
+    return a
+
+
+def fused_args(rows=4, H=8, slots=16):
+    A = Arena()
+    C3 = 3 * H * D
+    a = _lib.FusedArgs()
+    a.struct_size = ctypes.sizeof(_lib.FusedArgs)
+    a.rows, a.H = rows, H
+    a.x, a.x_stride = A.take(rows * C3 * 2), C3
+    a.weight = A.take(12 * H * D * 4)
+    a.conv_state, a.conv_slot_stride = A.take(slots * 3 * C3 * 2), 3 * C3
+    a.raw_gate, a.gate_stride = A.take(rows * H * D * 2), H * D
+    a.raw_beta, a.beta_stride = A.take(rows * H * 2), H
+    a.A_log, a.dt_bias = A.take(H * 4), A.take(H * D * 4)
+    a.state_indices = A.take(rows * 4)
+    a.state, a.state_dtype = A.take(slots * H * D * D * 4), 0
+    a.num_slots, a.slot_stride = slots, H * D * D
+    a.output_gate, a.ogate_stride = A.take(rows * H * D * 2), H * D
+    a.norm_weight, a.norm_eps = A.take(D * 4), 1e-5
+    a.out = A.take(rows * H * D * 2)
+    return a
+
+
+def plan_rec(a):
+    p = _lib.LaunchPlan()
+    rc = lib().kda_recurrent_plan(ctypes.byref(a), ctypes.byref(p))
+    return rc, p
+
+
+def plan_packed(a):
+    p = _lib.LaunchPlan()
+    rc = lib().kda_packed_plan(ctypes.byref(a), ctypes.byref(p))
+    return rc, p
+
+
+def plan_fused(a):
+    p = _lib.LaunchPlan()
+    rc = lib().kda_fused_plan(ctypes.byref(a), ctypes.byref(p))
+    return rc, p
+
+
+def err():
+    return lib().kda_last_error().decode()
+
+
+# ---- launch geometry ---------------------------------------------------------------------
+
+@pytest.mark.parametrize("N,H,vsplit", [(1, 32, 8), (8, 32, 8), (32, 32, 2), (64, 32, 1),
+                                        (256, 32, 1), (512, 12, 1), (64, 12, 4), (4, 4, 8)])
+def test_recurrent_plan_geometry(N, H, vsplit):
+    rc, p = plan_rec(rec_args(N=N, H=H, slots=max(N, 8)))
+    assert rc == 0, err()
+    assert p.vsplit == vsplit
+    assert p.rows_per_block * p.vsplit == D
+    assert p.grid_x == N * H * vsplit and p.block == 256 and p.items == N * H
+    assert p.kernel == 1
+
+
+def test_varlen_and_fused_plans():
+    rc, p = plan_rec(rec_args(N=64, H=16, T=190, slots=65, varlen=True))
+    assert rc == 0, err()
+    assert p.kernel == 2
+    rc, p = plan_fused(fused_args(rows=256, H=32, slots=2048))
+    assert rc == 0, err()
+    assert (p.kernel, p.grid_x, p.vsplit, p.rows_per_block) == (3, 256 * 32, 1, 128)
+
+
+def test_packed_plan_matches_recurrent():
+    rc, p = plan_packed(packed_args(B=64, H=12, slots=1024))
+    assert rc == 0, err()
+    assert p.items == 64 * 12 and p.kernel == 1
+
+
+# ---- validation -----------------------------------------------------------------------------
+
+def expect(rc_p, code, fragment=""):
+    rc = rc_p[0]
+    assert rc == code, (rc, err())
+    assert fragment in err()
+
+
+def test_recurrent_validation_errors():
+    a = rec_args(); a.q = 0
+    expect(plan_rec(a), -1)
+    a = rec_args(); a.K = 64
+    expect(plan_rec(a), -7, "K=64")
+    a = rec_args(); a.HV = 8
+    expect(plan_rec(a), -7, "HV")
+    a = rec_args(); a.n_tokens = 5
+    expect(plan_rec(a), -2, "n_tokens")
+    a = rec_args(); a.n_seqs = 0; a.n_tokens = 0
+    expect(plan_rec(a), -2)
+    a = rec_args(); a.state_dtype = 7
+    expect(plan_rec(a), -3)
+    a = rec_args(); a.q_stride = 100
+    expect(plan_rec(a), -4)
+    a = rec_args(); a.beta_stride = 1
+    expect(plan_rec(a), -4)
+    a = rec_args(); a.slot_stride = 4 * D * D - 4
+    expect(plan_rec(a), -4)
+    a = rec_args(); a.slot_stride = 4 * D * D + 1
+    expect(plan_rec(a), -5)
+    a = rec_args(); a.state += 4
+    expect(plan_rec(a), -5)
+    a = rec_args(); a.out += 2
+    expect(plan_rec(a), -5)
+    a = rec_args(); a.q += 1
+    expect(plan_rec(a), -5)
+    a = rec_args(); a.gate_mode = 1; a.lower_bound = -5.0
+    expect(plan_rec(a), -7, "lower_bound")
+    a = rec_args(); a.l2_eps = -1.0
+    expect(plan_rec(a), -2)
+    a = rec_args(); a.num_slots = 0
+    expect(plan_rec(a), -2)
+
+
+def test_recurrent_alias_detection():
+    a = rec_args(); a.out = a.q
+    expect(plan_rec(a), -6, "out overlaps")
+    a = rec_args(); a.state = a.q - 16 * 4 * D * 0  # state starts where q starts
+    expect(plan_rec(a), -6)
+    a = rec_args(varlen=True, T=4); a.checkpoints = a.state; a.ckpt_dtype = 0
+    expect(plan_rec(a), -6, "checkpoints")
+    a = rec_args(); a.out = a.state + 16
+    expect(plan_rec(a), -6)
+
+
+def test_checkpoint_rules():
+    a = rec_args(varlen=True, T=6)
+    a.checkpoints = 1 << 40
+    a.ckpt_dtype = 1
+    expect(plan_rec(a), -7, "checkpoints")
+    a.ckpt_dtype = 0
+    assert plan_rec(a)[0] == 0, err()
+
+
+def test_empty_varlen_is_valid():
+    a = rec_args(N=3, T=0, varlen=True)
+    a.q = a.k = a.v = a.g = a.beta = a.out = 0
+    assert plan_rec(a)[0] == 0, err()
+
+
+def test_packed_validation():
+    a = packed_args(); a.qkv_stride = 3 * 12 * D - 1
+    expect(plan_packed(a), -4)
+    a = packed_args(); a.mixed_qkv = 0
+    expect(plan_packed(a), -1)
+    a = packed_args(); a.B = 0
+    expect(plan_packed(a), -2)
+    a = packed_args(); a.gate_mode = 1
+    expect(plan_packed(a), -7)
+    a = packed_args(); a.struct_size = 8
+    expect(plan_packed(a), -10)
+
+
+def test_fused_validation():
+    a = fused_args(); a.conv_slot_stride = 10
+    expect(plan_fused(a), -4)
+    a = fused_args(); a.out = a.x
+    expect(plan_fused(a), -6)
+    a = fused_args(); a.conv_state = a.state
+    expect(plan_fused(a), -6, "conv_state")
+    a = fused_args(); a.norm_eps = -1.0
+    expect(plan_fused(a), -2)
+    a = fused_args(); a.norm_weight = 0
+    expect(plan_fused(a), -1)
+    a = fused_args(); a.state_dtype = 1
+    assert plan_fused(a)[0] == 0, err()
+    a = fused_args(); a.gate_mode = 1
+    expect(plan_fused(a), -7)
+
+
+def test_device_check_without_gpu_is_an_error_not_a_crash():
+    """On a host without a GPU the device query fails cleanly."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert lib().kda_check_device(0) == -8
