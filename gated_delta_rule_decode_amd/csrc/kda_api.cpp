@@ -118,8 +118,14 @@ uint64_t pool_bytes(int32_t dtype, int64_t num_slots, int64_t slot_stride, int32
 // Value rows per workgroup: a (row, head) item is split into vsplit
 // workgroups of 128/vsplit value rows so that small batches still put
 // enough workgroups on the 256 CUs; large batches keep whole heads.
+#ifndef KDA_FORCE_VSPLIT
+#define KDA_FORCE_VSPLIT 0  // build-time override used when tuning the policy
+#endif
+
 int choose_vsplit(int64_t items)
 {
+    if (KDA_FORCE_VSPLIT == 1 || KDA_FORCE_VSPLIT == 2 || KDA_FORCE_VSPLIT == 4 || KDA_FORCE_VSPLIT == 8)
+        return KDA_FORCE_VSPLIT;
     const int64_t target = 2048;  // ~8 workgroups per CU
     int v = 1;
     while (v < 8 && items * v < target) v *= 2;

@@ -111,15 +111,30 @@ __device__ __forceinline__ float sigmoid_f(float x) { return 1.0f / (1.0f + __ex
 
 template <bool BF16> struct StateIO;
 
+// Loads and stores address one head tile from its (workgroup-uniform) base
+// with 32-bit byte offsets, so the 64-bit slot address is formed once.
+template <typename V>
+__device__ __forceinline__ V ld_nt(const char *base, uint32_t off)
+{
+    return __builtin_nontemporal_load(reinterpret_cast<const V *>(base + off));
+}
+template <typename V>
+__device__ __forceinline__ void st_nt(char *base, uint32_t off, V v)
+{
+    __builtin_nontemporal_store(v, reinterpret_cast<V *>(base + off));
+}
+
 template <> struct StateIO<false> {
-    typedef float elem;
+    static constexpr uint32_t ROW_BYTES = KD * 4;
     struct Raw { f32x4 a, b; };
     static __device__ __forceinline__ int chan(int m, int e) { return e < 4 ? 4 * m + e : 64 + 4 * m + (e - 4); }
-    static __device__ __forceinline__ Raw load(const float *row, int m)
+    // byte offset of the lane's first access in value row `row`
+    static __device__ __forceinline__ uint32_t off(int row, int m) { return (uint32_t)row * ROW_BYTES + 16u * m; }
+    static __device__ __forceinline__ Raw load(const char *head, uint32_t o)
     {
         Raw r;
-        r.a = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(row + 4 * m));
-        r.b = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(row + 64 + 4 * m));
+        r.a = ld_nt<f32x4>(head, o);
+        r.b = ld_nt<f32x4>(head, o + 256u);
         return r;
     }
     static __device__ __forceinline__ void unpack(const Raw &r, float s[8])
@@ -134,21 +149,22 @@ template <> struct StateIO<false> {
         r.b = f32x4{s[4], s[5], s[6], s[7]};
         return r;
     }
-    static __device__ __forceinline__ void store(float *row, int m, const Raw &r)
+    static __device__ __forceinline__ void store(char *head, uint32_t o, const Raw &r)
     {
-        __builtin_nontemporal_store(r.a, reinterpret_cast<f32x4 *>(row + 4 * m));
-        __builtin_nontemporal_store(r.b, reinterpret_cast<f32x4 *>(row + 64 + 4 * m));
+        st_nt<f32x4>(head, o, r.a);
+        st_nt<f32x4>(head, o + 256u, r.b);
     }
 };
 
 template <> struct StateIO<true> {
-    typedef uint16_t elem;
+    static constexpr uint32_t ROW_BYTES = KD * 2;
     struct Raw { u32x4 w; };
     static __device__ __forceinline__ int chan(int m, int e) { return 8 * m + e; }
-    static __device__ __forceinline__ Raw load(const uint16_t *row, int m)
+    static __device__ __forceinline__ uint32_t off(int row, int m) { return (uint32_t)row * ROW_BYTES + 16u * m; }
+    static __device__ __forceinline__ Raw load(const char *head, uint32_t o)
     {
         Raw r;
-        r.w = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(row + 8 * m));
+        r.w = ld_nt<u32x4>(head, o);
         return r;
     }
     static __device__ __forceinline__ void unpack(const Raw &r, float s[8])
@@ -165,9 +181,9 @@ template <> struct StateIO<true> {
                     pack_bf16x2(s[4], s[5]), pack_bf16x2(s[6], s[7])};
         return r;
     }
-    static __device__ __forceinline__ void store(uint16_t *row, int m, const Raw &r)
+    static __device__ __forceinline__ void store(char *head, uint32_t o, const Raw &r)
     {
-        __builtin_nontemporal_store(r.w, reinterpret_cast<u32x4 *>(row + 8 * m));
+        st_nt<u32x4>(head, o, r.w);
     }
 };
 
@@ -251,20 +267,40 @@ __device__ __forceinline__ float row_update(float s[8], const TokenOps &t, float
     return fmaf(bu, t.qk, pc);
 }
 
-// Stage one token of channel data into LDS: threads 0..127 handle q, k and
-// the gate of channel tid; threads 128..255 copy v of channel tid-128.
-__device__ __forceinline__ void stage_token(int tid, const uint16_t *q, const uint16_t *k,
-                                            const uint16_t *v, const uint16_t *g,
-                                            const float *dt_bias_h, float a_h, float *sq, float *sk,
+// One token's channel inputs, held in registers between their load and the
+// LDS stage.  Every thread loads channel tid & 127 of q, k, v, the raw gate
+// and dt_bias (no divergent branch around the loads, so the compiler does
+// not wait on them before the state loads are issued); threads 0..127 then
+// stage q, k and the decay, threads 128..255 stage v.
+struct StageIn {
+    uint32_t q, k, v, g;  // bf16 bits
+    float dt;
+};
+
+__device__ __forceinline__ StageIn load_stage(int tid, const uint16_t *q, const uint16_t *k,
+                                              const uint16_t *v, const uint16_t *g,
+                                              const float *dt_bias_h)
+{
+    const int c = tid & (KD - 1);
+    StageIn s;
+    s.q = q[c];
+    s.k = k[c];
+    s.v = v[c];
+    s.g = g[c];
+    s.dt = dt_bias_h[c];
+    return s;
+}
+
+// Gate transform once per channel: decay = exp(-exp(A_log) * softplus(g + dt_bias)).
+__device__ __forceinline__ void write_stage(int tid, const StageIn &s, float a_h, float *sq, float *sk,
                                             float *sd, float *sv)
 {
     if (tid < KD) {
-        sq[tid] = bf16_bits_to_f32(q[tid]);
-        sk[tid] = bf16_bits_to_f32(k[tid]);
-        const float x = bf16_bits_to_f32(g[tid]) + dt_bias_h[tid];
-        sd[tid] = __expf(-a_h * softplus_f(x));
+        sq[tid] = bf16_bits_to_f32(s.q);
+        sk[tid] = bf16_bits_to_f32(s.k);
+        sd[tid] = __expf(-a_h * softplus_f(bf16_bits_to_f32(s.g) + s.dt));
     } else {
-        sv[tid - KD] = bf16_bits_to_f32(v[tid - KD]);
+        sv[tid - KD] = bf16_bits_to_f32(s.v);
     }
 }
 
@@ -274,7 +310,6 @@ template <int G, bool BF16, bool VARLEN>
 __global__ void __launch_bounds__(256) kda_recurrent_kernel(const RecParams p)
 {
     using IO = StateIO<BF16>;
-    using E = typename IO::elem;
     constexpr int VT = 16 * G;  // value rows per workgroup
 
     __shared__ float s_q[2][KD], s_k[2][KD], s_d[2][KD], s_v[2][KD];
@@ -309,50 +344,63 @@ __global__ void __launch_bounds__(256) kda_recurrent_kernel(const RecParams p)
     }
     if (t1 <= t0) return;
 
-    E *head = reinterpret_cast<E *>(p.state) + (int64_t)idx * p.slot_stride + (int64_t)h * (KD * KD);
-
-    // Issue every state load of this lane before anything else.
-    typename IO::Raw raw[G];
-#pragma unroll
-    for (int gi = 0; gi < G; ++gi) raw[gi] = IO::load(head + (r_base + gi) * KD, m);
-
-    const float a_h = __expf(p.A_log[h]);
+    const size_t es = BF16 ? 2 : 4;
+    char *head = reinterpret_cast<char *>(p.state) + ((int64_t)idx * p.slot_stride + (int64_t)h * (KD * KD)) * es;
     const float *dtb = p.dt_bias + (int64_t)h * KD;
+    const int64_t hk = (int64_t)h * KD;
+
+    // Token inputs first: waiting for them later must not wait for the state.
+    StageIn in = load_stage(tid, p.q + (int64_t)t0 * p.q_stride + hk, p.k + (int64_t)t0 * p.k_stride + hk,
+                            p.v + (int64_t)t0 * p.v_stride + hk, p.g + (int64_t)t0 * p.g_stride + hk, dtb);
+    uint32_t braw = p.beta[(int64_t)t0 * p.beta_stride + h];
+    const float a_h = __expf(p.A_log[h]);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // Then every state load of this lane.
+    typename IO::Raw raw[G];
+    uint32_t off[G];
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi) {
+        off[gi] = IO::off(r_base + gi, m);
+        raw[gi] = IO::load(head, off[gi]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
 
     if constexpr (!VARLEN) {
-        // T=1: stage the token while the state loads are in flight, then
-        // update and store value row by value row.
-        const int t = t0;
-        stage_token(tid, p.q + (int64_t)t * p.q_stride + h * KD, p.k + (int64_t)t * p.k_stride + h * KD,
-                    p.v + (int64_t)t * p.v_stride + h * KD, p.g + (int64_t)t * p.g_stride + h * KD,
-                    dtb, a_h, s_q[0], s_k[0], s_d[0], s_v[0]);
-        const float beta = sigmoid_f(bf16_bits_to_f32(p.beta[(int64_t)t * p.beta_stride + h]));
+        // T=1: the gate transform and the norms overlap the state fetch.
+        write_stage(tid, in, a_h, s_q[0], s_k[0], s_d[0], s_v[0]);
+        const float beta = sigmoid_f(bf16_bits_to_f32(braw));
         __syncthreads();
         TokenOps ops;
         read_token_ops<BF16>(ops, s_q[0], s_k[0], s_d[0], m, p.scale, p.l2_eps, beta);
         float o[G];
 #pragma unroll
         for (int gi = 0; gi < G; ++gi) {
-            float s[8];
-            IO::unpack(raw[gi], s);
-            o[gi] = row_update(s, ops, s_v[0][r_base + gi]);
-            IO::store(head + (r_base + gi) * KD, m, IO::pack(s));
+            float st[8];
+            IO::unpack(raw[gi], st);
+            o[gi] = row_update(st, ops, s_v[0][r_base + gi]);
+            IO::store(head, off[gi], IO::pack(st));
         }
-        if (m == 0) store_out_bf16<G>(p.out + ((int64_t)t * p.H + h) * KD + r_base, o);
+        if (m == 0) store_out_bf16<G>(p.out + ((int64_t)t0 * p.H + h) * KD + r_base, o);
     } else {
         // Ragged token loop: the state stays in registers across the tokens
-        // of the sequence; after each token the checkpoint (if requested) and
-        // the output are written; the pool slot is written once at the end.
+        // of the sequence; the next token's inputs are fetched while the
+        // current one is computed; after each token the checkpoint (if
+        // requested) and the output are written; the pool slot is written
+        // once at the end.
         float st[G][8];
 #pragma unroll
         for (int gi = 0; gi < G; ++gi) IO::unpack(raw[gi], st[gi]);
         for (int t = t0; t < t1; ++t) {
             const int buf = (t - t0) & 1;
-            stage_token(tid, p.q + (int64_t)t * p.q_stride + h * KD,
-                        p.k + (int64_t)t * p.k_stride + h * KD, p.v + (int64_t)t * p.v_stride + h * KD,
-                        p.g + (int64_t)t * p.g_stride + h * KD, dtb, a_h, s_q[buf], s_k[buf],
-                        s_d[buf], s_v[buf]);
-            const float beta = sigmoid_f(bf16_bits_to_f32(p.beta[(int64_t)t * p.beta_stride + h]));
+            write_stage(tid, in, a_h, s_q[buf], s_k[buf], s_d[buf], s_v[buf]);
+            const float beta = sigmoid_f(bf16_bits_to_f32(braw));
+            if (t + 1 < t1) {
+                const int64_t n = t + 1;
+                in = load_stage(tid, p.q + n * p.q_stride + hk, p.k + n * p.k_stride + hk,
+                                p.v + n * p.v_stride + hk, p.g + n * p.g_stride + hk, dtb);
+                braw = p.beta[n * p.beta_stride + h];
+            }
             __syncthreads();
             TokenOps ops;
             read_token_ops<BF16>(ops, s_q[buf], s_k[buf], s_d[buf], m, p.scale, p.l2_eps, beta);
@@ -361,13 +409,13 @@ __global__ void __launch_bounds__(256) kda_recurrent_kernel(const RecParams p)
             for (int gi = 0; gi < G; ++gi) o[gi] = row_update(st[gi], ops, s_v[buf][r_base + gi]);
             if (m == 0) store_out_bf16<G>(p.out + ((int64_t)t * p.H + h) * KD + r_base, o);
             if (p.ckpt) {
-                E *ck = reinterpret_cast<E *>(p.ckpt) + ((int64_t)t * p.H + h) * (KD * KD);
+                char *ck = reinterpret_cast<char *>(p.ckpt) + ((int64_t)t * p.H + h) * (KD * KD) * es;
 #pragma unroll
-                for (int gi = 0; gi < G; ++gi) IO::store(ck + (r_base + gi) * KD, m, IO::pack(st[gi]));
+                for (int gi = 0; gi < G; ++gi) IO::store(ck, off[gi], IO::pack(st[gi]));
             }
         }
 #pragma unroll
-        for (int gi = 0; gi < G; ++gi) IO::store(head + (r_base + gi) * KD, m, IO::pack(st[gi]));
+        for (int gi = 0; gi < G; ++gi) IO::store(head, off[gi], IO::pack(st[gi]));
     }
 }
 
@@ -379,11 +427,51 @@ __global__ void __launch_bounds__(256) kda_recurrent_kernel(const RecParams p)
 // positions and x, writes the SiLU activation to LDS and shifts its own cache
 // column, so no other thread touches that channel.
 
+// One conv channel's inputs: the three cached positions (oldest first), the
+// current x and the four taps.
+struct ConvIn {
+    uint32_t c0, c1, c2, x;  // bf16 bits
+    float w0, w1, w2, w3;
+};
+
+__device__ __forceinline__ ConvIn load_conv(const uint16_t *cs, const uint16_t *xr, const float *weight,
+                                            int cl, int h, int HC, int C3)
+{
+    const int grp = cl >> 7;
+    const int d = cl & (KD - 1);
+    const int c = grp * HC + h * KD + d;
+    ConvIn in;
+    in.c0 = cs[c];
+    in.c1 = cs[C3 + c];
+    in.c2 = cs[2 * C3 + c];
+    in.x = xr[c];
+    const float *w = weight + (int64_t)grp * 4 * HC + h * KD + d;
+    in.w0 = w[0];
+    in.w1 = w[HC];
+    in.w2 = w[2 * HC];
+    in.w3 = w[3 * HC];
+    return in;
+}
+
+// y = sum_j w_j hist_j over [c0, c1, c2, x], then SiLU; the channel's cache
+// column is shifted to [c1, c2, x] by the same thread that read it.
+__device__ __forceinline__ float conv_silu_shift(const ConvIn &in, uint16_t *cs, int cl, int h, int HC, int C3)
+{
+    const int c = (cl >> 7) * HC + h * KD + (cl & (KD - 1));
+    float y = in.w0 * bf16_bits_to_f32(in.c0);
+    y = fmaf(in.w1, bf16_bits_to_f32(in.c1), y);
+    y = fmaf(in.w2, bf16_bits_to_f32(in.c2), y);
+    y = fmaf(in.w3, bf16_bits_to_f32(in.x), y);
+    cs[c] = (uint16_t)in.c1;
+    cs[C3 + c] = (uint16_t)in.c2;
+    cs[2 * C3 + c] = (uint16_t)in.x;
+    return y * sigmoid_f(y);
+}
+
 template <bool BF16>
 __global__ void __launch_bounds__(256) kda_fused_kernel(const FusedParams p)
 {
     using IO = StateIO<BF16>;
-    using E = typename IO::elem;
     constexpr int G = 8;
 
     __shared__ float s_act[3 * KD];  // q | k | v activations of this head
@@ -406,50 +494,50 @@ __global__ void __launch_bounds__(256) kda_fused_kernel(const FusedParams p)
         return;
     }
 
-    E *head = reinterpret_cast<E *>(p.state) + (int64_t)idx * p.slot_stride + (int64_t)h * (KD * KD);
-    typename IO::Raw raw[G];
-#pragma unroll
-    for (int gi = 0; gi < G; ++gi) raw[gi] = IO::load(head + (r_base + gi) * KD, m);
-
-    // depthwise causal conv (width 4) + SiLU, cache shift
+    // Channel inputs first (conv history, x, taps, gate), then the state.
     const int HC = p.H * KD;
     const int C3 = 3 * HC;
     uint16_t *cs = p.conv_state + (int64_t)idx * p.conv_slot_stride;
     const uint16_t *xr = p.x + (int64_t)row * p.x_stride;
-    for (int cl = tid; cl < 3 * KD; cl += 256) {
-        const int grp = cl >> 7;
-        const int d = cl & (KD - 1);
-        const int c = grp * HC + h * KD + d;
-        const uint16_t c0 = cs[c], c1 = cs[C3 + c], c2 = cs[2 * C3 + c];
-        const uint16_t xv = xr[c];
-        const float *w = p.weight + (int64_t)grp * 4 * HC + h * KD + d;
-        float y = w[0] * bf16_bits_to_f32(c0);
-        y = fmaf(w[HC], bf16_bits_to_f32(c1), y);
-        y = fmaf(w[2 * HC], bf16_bits_to_f32(c2), y);
-        y = fmaf(w[3 * HC], bf16_bits_to_f32(xv), y);
-        s_act[cl] = y * sigmoid_f(y);
-        cs[c] = c1;
-        cs[C3 + c] = c2;
-        cs[2 * C3 + c] = xv;
+    const int c_lo = tid & (KD - 1);
+    const ConvIn in0 = load_conv(cs, xr, p.weight, tid, h, HC, C3);
+    const ConvIn in1 = load_conv(cs, xr, p.weight, 256 + c_lo, h, HC, C3);  // used by tid < 128
+    const uint32_t graw = p.graw[(int64_t)row * p.g_stride + h * KD + c_lo];
+    const float dt = p.dt_bias[(int64_t)h * KD + c_lo];
+    const uint32_t braw = p.braw[(int64_t)row * p.beta_stride + h];
+    const float a_h = __expf(p.A_log[h]);
+    __builtin_amdgcn_sched_barrier(0);
+
+    const size_t es = BF16 ? 2 : 4;
+    char *head = reinterpret_cast<char *>(p.state) + ((int64_t)idx * p.slot_stride + (int64_t)h * (KD * KD)) * es;
+    typename IO::Raw raw[G];
+    uint32_t off[G];
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi) {
+        off[gi] = IO::off(r_base + gi, m);
+        raw[gi] = IO::load(head, off[gi]);
     }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // depthwise causal conv (width 4) + SiLU and the gate, overlapping the state fetch
+    s_act[tid] = conv_silu_shift(in0, cs, tid, h, HC, C3);
     if (tid < KD) {
-        const float x = bf16_bits_to_f32(p.graw[(int64_t)row * p.g_stride + h * KD + tid]) +
-                        p.dt_bias[(int64_t)h * KD + tid];
-        s_d[tid] = __expf(-__expf(p.A_log[h]) * softplus_f(x));
+        s_act[tid + 256] = conv_silu_shift(in1, cs, tid + 256, h, HC, C3);
+        s_d[tid] = __expf(-a_h * softplus_f(bf16_bits_to_f32(graw) + dt));
     }
-    const float beta = sigmoid_f(bf16_bits_to_f32(p.braw[(int64_t)row * p.beta_stride + h]));
+    const float beta = sigmoid_f(bf16_bits_to_f32(braw));
     __syncthreads();
 
     TokenOps ops;
     read_token_ops<BF16>(ops, s_act, s_act + KD, s_d, m, p.scale, p.l2_eps, beta);
     float o[G];
-    float st[8];
     float ss = 0.f;
 #pragma unroll
     for (int gi = 0; gi < G; ++gi) {
+        float st[8];
         IO::unpack(raw[gi], st);
         o[gi] = row_update(st, ops, s_act[2 * KD + r_base + gi]);
-        IO::store(head + (r_base + gi) * KD, m, IO::pack(st));
+        IO::store(head, off[gi], IO::pack(st));
         ss = fmaf(o[gi], o[gi], ss);
     }
     // gated RMSNorm over the 128 outputs of the head

@@ -11,6 +11,7 @@ the results.  bf16 data travel as their uint16 bit patterns.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import math
 import os
@@ -40,12 +41,14 @@ def build(force: bool = True) -> str:
     return _LIB
 
 
-def _load():
+def _load(path=None):
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
-            build()
-        lib = ctypes.CDLL(_LIB)
+        if path is None:
+            path = _LIB
+            if not os.path.exists(path):
+                build()
+        lib = ctypes.CDLL(path)
         P = ctypes.c_void_p
         I64 = ctypes.c_int64
         Dbl = ctypes.c_double
@@ -60,6 +63,20 @@ def _load():
         lib.kdao_bf16_from_f64_n.argtypes = [P, P, I64]
         _lib = lib
     return _lib
+
+
+@contextlib.contextmanager
+def using_library(path):
+    """Temporarily route every call to another build of kda_oracle.c (used by
+    the tests that plant mistakes in copies of the oracle)."""
+    global _lib
+    saved = _lib
+    _lib = None
+    try:
+        _load(path)
+        yield
+    finally:
+        _lib = saved
 
 
 # ---- array helpers (no arithmetic) -------------------------------------------

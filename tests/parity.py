@@ -6,7 +6,10 @@ Tolerances:
     where half a bf16 ulp alone exceeds 2e-3), and internally
     |gpu - bf16(ref64)| <= 1 ulp of bf16(ref64) + 1e-6.
   * fp32 state / checkpoints: |gpu - ref64| <= 1e-4.
-  * bf16 state: |gpu - ref64| <= 4e-3 and within 1 ulp of bf16(ref64).
+  * bf16 state: |gpu - ref64| <= 4e-3, and internally within 1 ulp of
+    bf16(ref64) or 1e-6 absolute: a near-zero element comes out of a sum of
+    terms of size ~0.05 whose fp32 rounding (~1e-8) is many bf16 ulps of the
+    tiny result, so a pure ulp gate does not apply there.
   * indices, null rows, untouched slots and conv caches: bit-exact.
 """
 from __future__ import annotations
@@ -60,7 +63,11 @@ def check_state(got_t, ref, what="state"):
         err = np.abs(got - want)
         worst = float(err.max()) if err.size else 0.0
         assert worst <= BF16_STATE_ATOL, f"{what}: max err {worst:.3e} > 4e-3"
-        assert np.all(err <= bf16_ulp(want) + 1e-30), f"{what}: more than 1 bf16 ulp off"
+        bad = err > np.maximum(bf16_ulp(want), 1e-6)
+        if bad.any():
+            i = np.flatnonzero(bad.reshape(-1))[0]
+            raise AssertionError(f"{what}: {int(bad.sum())} elements beyond 1 bf16 ulp / 1e-6; first: "
+                                 f"gpu {got.reshape(-1)[i]!r} ref {want.reshape(-1)[i]!r}")
         return worst
     got = g.numpy().astype(np.float64)
     want = np.asarray(ref, np.float64)

@@ -48,7 +48,7 @@ def run_recurrent_case(c, *, ckpt=False, n_tokens=None):
     else:
         shp = lambda t: t.reshape(1, T, *t.shape[1:])  # noqa: E731
     state = c.state if c.state.is_cuda else g(c.state)
-    ck = torch.empty((T, c.H, D, D), dtype=state.dtype, device=DEV) if ckpt else None
+    ck = torch.zeros((T, c.H, D, D), dtype=state.dtype, device=DEV) if ckpt else None
     out = recurrent_kda(shp(g(c.q)), shp(g(c.k)), shp(g(c.v)), shp(g(c.g)), shp(g(c.beta)),
                         g(c.A_log), g(c.dt_bias), initial_state=state,
                         state_indices=g(c.state_indices), cu_seqlens=g(c.cu_seqlens),
@@ -306,6 +306,49 @@ def test_varlen_all_empty_and_zero_tokens():
 
 # ------------------------------------------------- invariants on the device --------
 
+@pytest.mark.parametrize("kind", ["t1", "varlen", "fused"])
+def test_bf16_store_is_rne_of_the_fp32_computation(kind):
+    """With beta = 0 every state element becomes s * decay: one fp32 multiply
+    whose value does not depend on how lanes split the key channels.  Starting
+    from the same bf16-representable state, a bf16 pool must then end as the
+    round-to-nearest-even (torch's fp32->bf16 conversion) of what an fp32
+    pool ends with, and so must the ragged call's checkpoints.  Outputs
+    (whose dot products the two layouts sum in different orders) must agree
+    to one bf16 ulp."""
+    say(f"bf16 store rounding vs fp32 pool ({kind}) seed=5100")
+    if kind == "fused":
+        c = synth.fused_case(5100, rows=9, H=4, num_slots=12, state_dtype=torch.bfloat16, device=DEV,
+                             null_zero=1, null_neg=1)
+        c.raw_beta.fill_(-math.inf)
+        s32 = c.state.float()
+        cs32 = c.conv_state.clone()
+        args = lambda st, cs: (c.x, c.weight, cs, c.raw_gate, c.raw_beta, c.A_log, c.dt_bias,  # noqa: E731
+                               c.state_indices, st, c.output_gate, c.norm_weight)
+        o16 = fused_kda_decode(*args(c.state, c.conv_state))
+        o32 = fused_kda_decode(*args(s32, cs32))
+        torch.cuda.synchronize()
+        assert torch.equal(P.bits(c.state), P.bits(s32.to(torch.bfloat16)))
+        a, b = o16.double().cpu().numpy(), o32.double().cpu().numpy()
+        assert np.all(np.abs(a - b) <= P.bf16_ulp(b) + 1e-30)
+        return
+    lengths = None if kind == "t1" else [2, 0, 3, 1, 2]
+    c = synth.recurrent_case(5100, n_seqs=5, H=3, num_slots=8, state_dtype=torch.bfloat16,
+                             device=DEV, lengths=lengths, indices="random", null_rows=1)
+    c.beta.fill_(-math.inf)
+    c32 = synth.RecurrentCase(**{**c.__dict__, "state": c.state.float()})
+    o16, s16, k16 = run_recurrent_case(c, ckpt=kind == "varlen")
+    o32, s32, k32 = run_recurrent_case(c32, ckpt=kind == "varlen")
+    assert torch.equal(P.bits(s16), P.bits(s32.to(torch.bfloat16)))
+    if kind == "varlen":
+        assert torch.equal(P.bits(k16), P.bits(k32.to(torch.bfloat16)))
+        cu = c.cu_seqlens.tolist()
+        for i, s in enumerate(c.state_indices.tolist()):
+            if s < 0:  # a null sequence writes no checkpoint
+                assert not P.bits(k16[cu[i]:cu[i + 1]]).any()
+    a, b = o16.double().cpu().numpy(), o32.double().cpu().numpy()
+    assert np.all(np.abs(a - b) <= P.bf16_ulp(b) + 1e-30)
+
+
 @pytest.mark.parametrize("state_dtype", [torch.float32, torch.bfloat16])
 def test_beta_zero_unit_decay_leaves_state_bitwise(state_dtype):
     say(f"invariant beta=0 unit decay {state_dtype} seed=5000")
@@ -344,7 +387,7 @@ def test_beta_one_unit_decay_stores_value():
 
 def test_null_only_batch():
     say("all rows null seed=5002")
-    c = synth.packed_case(5002, B=5, H=3, num_slots=4, device=DEV, state_dtype=torch.float32)
+    c = synth.packed_case(5002, B=5, H=3, num_slots=8, device=DEV, state_dtype=torch.float32)
     c.state_indices.fill_(-1)
     before = c.state.clone()
     out = packed_kda_decode(c.mixed_qkv, c.raw_gate, c.raw_beta, c.A_log, c.dt_bias, c.state,

@@ -1,0 +1,91 @@
+"""The oracle pins must catch plausible mistakes.
+
+Each case plants one mistake in a copy of oracle/kda_oracle.c (on the CPU),
+builds it, routes the oracle wrapper to that build and runs the pins: at
+least one pin must fail.  This shows the pins constrain every part of the
+oracle (orientation, decay, gate, delta rule, readout, conv, norm, null
+rows, rounding), not only its happy path.
+"""
+import os
+import subprocess
+
+import pytest
+
+import oracle
+from tests import test_oracle_pins as pins
+
+MUTANTS = [
+    ("state orientation transposed",
+     "S[k][v] = load_elem(pool, dt, head_base + (size_t)v * KD + k);",
+     "S[v][k] = load_elem(pool, dt, head_base + (size_t)v * KD + k);"),
+    ("decay dropped", "S[k][j] *= decay[k];", "S[k][j] *= 1.0;"),
+    ("decay indexed by value", "S[k][j] *= decay[k];", "S[k][j] *= decay[j];"),
+    ("delta sign", "u[j] = v[j] - acc;", "u[j] = v[j] + acc;"),
+    ("beta dropped from update", "S[k][j] += beta * kh[k] * u[j];", "S[k][j] += kh[k] * u[j];"),
+    ("readout with k", "for (int k = 0; k < KD; ++k) acc += S[k][j] * qh[k];\n        o[j]",
+     "for (int k = 0; k < KD; ++k) acc += S[k][j] * kh[k];\n        o[j]"),
+    ("scale dropped", "o[j] = scale * acc;", "o[j] = acc;"),
+    ("readout before update",
+     "    /* S <- S + beta k u^T */\n    for (int k = 0; k < KD; ++k)\n        for (int j = 0; j < KD; ++j) S[k][j] += beta * kh[k] * u[j];\n",
+     "    double Sn[KD][KD];\n    for (int k = 0; k < KD; ++k)\n        for (int j = 0; j < KD; ++j) Sn[k][j] = S[k][j] + beta * kh[k] * u[j];\n"),
+    ("softplus sign", "log1p(exp(-fabs(x)))", "log1p(exp(fabs(x)))"),
+    ("gate sign", "double g = -a * softplus", "double g = a * softplus"),
+    ("A_log not exponentiated", "double a = exp(A_log_h);", "double a = A_log_h;"),
+    ("dt_bias head offset", "gate_decay(gv, (double)A_log[h], dt_bias + h * KD, dec);\n                kda_token",
+     "gate_decay(gv, (double)A_log[h], dt_bias, dec);\n                kda_token"),
+    ("beta not squashed", "double beta = sigmoid(bf16_to_f64(braw[(size_t)t * H + h]));",
+     "double beta = bf16_to_f64(braw[(size_t)t * H + h]);"),
+    ("l2 norm dropped", "double inv = 1.0 / sqrt(ss + eps);", "double inv = 1.0;"),
+    ("null row output not zero", "if (out64) out64[oi] = 0.0;\n                        if (out_bf16)",
+     "if (out64) out64[oi] = 1.0;\n                        if (out_bf16)"),
+    ("state not carried across tokens",
+     "            for (int64_t t = t0; t < t1; ++t) {\n                size_t vec",
+     "            for (int64_t t = t0; t < t1; ++t) {\n                gather_state(state, state_dtype, head_base, S);\n                size_t vec"),
+    ("conv taps reversed", "weight[(grp * 4 + j) * HC + cc]", "weight[(grp * 4 + (3 - j)) * HC + cc]"),
+    ("conv group ignored", "weight[(grp * 4 + j) * HC + cc]", "weight[j * HC + cc]"),
+    ("conv cache not shifted", "cs[0 * C3 + c] = cs[1 * C3 + c];", "cs[0 * C3 + c] = cs[0 * C3 + c];"),
+    ("silu dropped", "act[c] = y * sigmoid(y);", "act[c] = y;"),
+    ("rms uses sum", "ms /= (double)KD;", "ms /= 1.0;"),
+    ("norm gate not squashed", "sigmoid(bf16_to_f64(ogate[vec + j]))", "bf16_to_f64(ogate[vec + j])"),
+    ("fused slot 0 live", "int null_row = idx <= 0 ||", "int null_row = idx < 0 ||"),
+    ("bf16 rounding truncates", "double q = nearbyint(m * 256.0);", "double q = trunc(m * 256.0);"),
+    ("bf16 ties away", "double q = nearbyint(m * 256.0);", "double q = round(m * 256.0);"),
+]
+
+PINS = [
+    pins.test_bf16_rounding_ties_and_double_rounding,
+    lambda: pins.test_beta_zero_unit_decay_keeps_state_and_reads_out(pins.torch.float32),
+    pins.test_beta_one_unit_decay_writes_value_exactly,
+    pins.test_zero_state_closed_form,
+    pins.test_decay_is_per_key_channel_along_the_contiguous_dim,
+    pins.test_half_decay_special_value,
+    pins.test_softplus_extremes,
+    pins.test_null_rows_zero_output_and_untouched_slots,
+    pins.test_two_tokens_orthogonal_keys_closed_form,
+    pins.test_same_key_beta_one_overwrites,
+    pins.test_product_form_cross_formulation,
+    pins.test_conv_one_hot_taps_reproduce_lagged_inputs,
+    pins.test_conv_output_feeds_recurrence_as_qkv,
+    pins.test_gated_rmsnorm_invariants,
+    pins.test_fused_null_rows,
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_planted_mistake_is_caught(name, old, new, tmp_path):
+    src = open(oracle._SRC).read()
+    assert old in src, f"mutation anchor for '{name}' not found"
+    mutated = src.replace(old, new)
+    c = tmp_path / "mut.c"
+    c.write_text(mutated)
+    so = tmp_path / "libmut.so"
+    subprocess.run(["gcc", "-O1", "-std=c11", "-w", "-fPIC", "-shared", "-o", str(so), str(c), "-lm"],
+                   check=True)
+    caught = []
+    with oracle.using_library(str(so)):
+        for pin in PINS:
+            try:
+                pin()
+            except Exception:  # an assertion, or a shape/NaN error of the broken oracle
+                caught.append(getattr(pin, "__name__", "pin"))
+    assert caught, f"no pin catches the planted mistake '{name}'"
