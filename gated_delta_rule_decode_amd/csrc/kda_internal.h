@@ -28,6 +28,7 @@ struct RecParams {
     uint16_t *out;               // bf16 [n_tokens][H][128]
     int32_t n_seqs, n_tokens, H;
     int32_t vsplit;              // workgroups per (sequence, head)
+    int32_t n_work;              // n_seqs * H * vsplit (grid is padded to a multiple of 8)
 };
 
 struct FusedParams {

@@ -320,9 +320,14 @@ __global__ void __launch_bounds__(256) kda_recurrent_kernel(const RecParams p)
     const int m = lane & 15;   // position inside the DPP row
     const int qd = lane >> 4;  // DPP row inside the wave
 
-    const int blk = blockIdx.x;
-    const int vs = blk % p.vsplit;
-    const int item = blk / p.vsplit;
+    // Workgroups are handed to the 8 XCDs round-robin by block id; number
+    // them so that each XCD walks one contiguous range of work and the
+    // vsplit slices of one (sequence, head), which read the same q/k/v/g,
+    // share an XCD and its L2.  The grid is padded to a multiple of 8.
+    const int work = (int)(blockIdx.x & 7u) * (int)(gridDim.x >> 3) + (int)(blockIdx.x >> 3);
+    if (work >= p.n_work) return;
+    const int vs = work % p.vsplit;
+    const int item = work / p.vsplit;
     const int seq = item / p.H;
     const int h = item - seq * p.H;
     const int r_base = vs * VT + wave * (4 * G) + qd * G;  // this lane's first value row

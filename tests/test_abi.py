@@ -147,14 +147,15 @@ def err():
 
 # ---- launch geometry ---------------------------------------------------------------------
 
-@pytest.mark.parametrize("N,H,vsplit", [(1, 32, 8), (8, 32, 8), (32, 32, 2), (64, 32, 1),
-                                        (256, 32, 1), (512, 12, 1), (64, 12, 4), (4, 4, 8)])
-def test_recurrent_plan_geometry(N, H, vsplit):
-    rc, p = plan_rec(rec_args(N=N, H=H, slots=max(N, 8)))
+@pytest.mark.parametrize("N,H,bf16,vsplit", [(1, 32, False, 4), (8, 32, False, 4), (256, 32, False, 4),
+                                             (512, 12, True, 4), (64, 12, True, 2), (42, 12, True, 4),
+                                             (96, 12, True, 2), (128, 12, True, 4), (4, 4, False, 4)])
+def test_recurrent_plan_geometry(N, H, bf16, vsplit):
+    rc, p = plan_rec(rec_args(N=N, H=H, slots=max(N, 8), bf16=bf16))
     assert rc == 0, err()
     assert p.vsplit == vsplit
     assert p.rows_per_block * p.vsplit == D
-    assert p.grid_x == N * H * vsplit and p.block == 256 and p.items == N * H
+    assert p.grid_x == (N * H * vsplit + 7) // 8 * 8 and p.block == 256 and p.items == N * H
     assert p.kernel == 1
 
 

@@ -520,3 +520,115 @@ def test_512_step_drift_against_fp64():
     say(f"after {steps} steps: max |state - fp64| = {drift:.3e}, sampled max |out - fp64| = {worst_o:.3e}")
     assert drift <= 1e-4
     assert worst_o <= 2e-3
+
+
+def test_varlen_graph_replay_with_changed_cu_seqlens():
+    """The ragged call reads cu_seqlens and state_indices on the device at
+    every launch: a captured graph replayed with other lengths (same token
+    total, trailing empty sequences, a null sequence) matches eager calls."""
+    say("hip graph replay varlen H=4 N=6 seed=5200")
+    N, H, T = 6, 4, 12
+    c = synth.recurrent_case(5200, n_seqs=N, H=H, num_slots=10, device=DEV,
+                             lengths=[2, 2, 2, 2, 2, 2], indices="random")
+    r1 = lambda t: t.reshape(1, T, *t.shape[1:])  # noqa: E731
+    out = torch.zeros((1, T, H, D), dtype=torch.bfloat16, device=DEV)
+    ck = torch.zeros((T, H, D, D), dtype=torch.float32, device=DEV)
+    call = lambda st, o, k: recurrent_kda(  # noqa: E731
+        r1(c.q), r1(c.k), r1(c.v), r1(c.g), r1(c.beta), c.A_log, c.dt_bias, initial_state=st,
+        state_indices=c.state_indices, cu_seqlens=c.cu_seqlens, n_tokens=T, output=o,
+        intermediate_states=k)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(c.state.clone(), out, ck)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(c.state, out, ck)
+    torch.cuda.synchronize()
+    layouts = [([0, 1, 2, 9, 12, 12, 12], [3, -1, 5, 0, 7, 8]),
+               ([0, 0, 6, 6, 12, 12, 12], [1, 2, 3, 4, 5, 6]),
+               ([0, 12, 12, 12, 12, 12, 12], [9, -1, -1, 2, 3, 4])]
+    for rep, (cu, idx) in enumerate(layouts):
+        c.cu_seqlens.copy_(torch.tensor(cu, dtype=torch.int32))
+        c.state_indices.copy_(torch.tensor(idx, dtype=torch.int32))
+        st0 = c.state.clone()
+        out.zero_()
+        ck.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        g_out, g_st, g_ck = out.clone(), c.state.clone(), ck.clone()
+        e_st = st0.clone()
+        e_out = torch.zeros_like(out)
+        e_ck = torch.zeros_like(ck)
+        call(e_st, e_out, e_ck)
+        torch.cuda.synchronize()
+        assert torch.equal(P.bits(g_out), P.bits(e_out)), f"replay {rep}: output"
+        assert torch.equal(P.bits(g_st), P.bits(e_st)), f"replay {rep}: state"
+        assert torch.equal(P.bits(g_ck), P.bits(e_ck)), f"replay {rep}: checkpoints"
+        want = oracle.recurrent(np_(c.q), np_(c.k), np_(c.v), np_(c.g), np_(c.beta), np_(c.A_log),
+                                np_(c.dt_bias), np_(st0), np.array(idx, np.int32),
+                                np.array(cu, np.int32), ckpt_dtype=oracle.F32)
+        P.check_bf16_out(g_out, want["out64"], f"replay {rep}")
+        P.check_state(g_st, want["state"], f"replay {rep} state")
+        P.check_state(g_ck, want["ckpt"], f"replay {rep} checkpoints")
+
+
+def test_fused_graph_replay():
+    say("hip graph replay fused H=8 rows=6 seed=5300")
+    rows, H, S = 6, 8, 12
+    c = synth.fused_case(5300, rows=rows, H=H, num_slots=S, device=DEV, null_zero=1, null_neg=1)
+    out = torch.empty((1, rows, H, D), dtype=torch.bfloat16, device=DEV)
+    call = lambda: fused_kda_decode(c.x, c.weight, c.conv_state, c.raw_gate, c.raw_beta, c.A_log,  # noqa: E731
+                                    c.dt_bias, c.state_indices, c.state, c.output_gate,
+                                    c.norm_weight, output=out)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        n = synth.fused_case(5400 + rep, rows=rows, H=H, num_slots=S, device=DEV, null_zero=1,
+                             null_neg=rep)
+        c.x.copy_(n.x)
+        c.state_indices.copy_(n.state_indices)
+        st0, cs0 = c.state.clone(), c.conv_state.clone()
+        torch.cuda.synchronize()
+        want = oracle.fused(P.host(c.x), P.host(c.weight), P.host(cs0), P.host(c.raw_gate),
+                            P.host(c.raw_beta), P.host(c.A_log), P.host(c.dt_bias),
+                            P.host(c.state_indices), np_(st0), P.host(c.output_gate),
+                            P.host(c.norm_weight))
+        graph.replay()
+        torch.cuda.synchronize()
+        P.check_bf16_out(out, want["out64"], f"fused replay {rep}")
+        P.check_state(c.state, want["state"], f"fused replay {rep} state")
+        got_cs = c.conv_state.cpu().contiguous().view(torch.int16)
+        want_cs = torch.from_numpy(np.ascontiguousarray(want["conv_state"]).view(np.int16))
+        assert torch.equal(got_cs, want_cs), f"fused replay {rep}: conv cache"
+
+
+@pytest.mark.parametrize("row_pad", [1, 3])
+def test_packed_odd_row_strides_and_independent_gate_strides(row_pad):
+    """Zero-copy views: an odd QKV row stride (2-byte aligned rows) and raw
+    gate / beta views with their own row strides."""
+    say(f"packed odd strides row_pad={row_pad} seed=5500")
+    B, H, S = 13, 12, 40
+    c = synth.packed_case(5500 + row_pad, B=B, H=H, num_slots=S, device=DEV, null_rows=2,
+                          row_pad=row_pad)
+    gate_wide = torch.randn((B, H * D + 5), device=DEV).to(torch.bfloat16)
+    beta_wide = torch.randn((B, H + 7), device=DEV).to(torch.bfloat16)
+    rg, rb = gate_wide[:, 2:2 + H * D], beta_wide[:, 3:3 + H]
+    assert rg.stride(0) == H * D + 5 and rb.stride(0) == H + 7
+    want = oracle.packed(P.host(c.mixed_qkv), P.host(rg), P.host(rb), P.host(c.A_log),
+                         P.host(c.dt_bias), np_(c.state), np_(c.state_indices))
+    out = packed_kda_decode(c.mixed_qkv, rg, rb, c.A_log, c.dt_bias, c.state, c.state_indices)
+    torch.cuda.synchronize()
+    P.check_bf16_out(out, want["out64"])
+    P.check_state(c.state, want["state"])
