@@ -140,6 +140,31 @@ def load_traffic(bytes_per_launch):
         return None
 
 
+def launch_plan(c, idx, pool, out_t, B, H):
+    """Launch geometry the library picks for the headline call (host-only query)."""
+    import ctypes
+
+    from gated_delta_rule_decode_amd import _lib
+    a = _lib.RecurrentArgs()
+    a.struct_size = ctypes.sizeof(_lib.RecurrentArgs)
+    a.n_seqs, a.n_tokens, a.H, a.HV, a.K, a.V = B, B, H, H, D, D
+    a.q, a.k, a.v, a.g, a.beta = (c.q.data_ptr(), c.k.data_ptr(), c.v.data_ptr(), c.g.data_ptr(),
+                                  c.beta.data_ptr())
+    a.q_stride = a.k_stride = a.v_stride = a.g_stride = H * D
+    a.beta_stride = H
+    a.A_log, a.dt_bias = c.A_log.data_ptr(), c.dt_bias.data_ptr()
+    a.scale, a.l2_eps = 1.0 / math.sqrt(D), 1e-6
+    a.state, a.state_dtype, a.ckpt_dtype = pool.data_ptr(), 0, 0
+    a.num_slots, a.slot_stride = pool.shape[0], pool.stride(0)
+    a.state_indices = idx.data_ptr()
+    a.out = out_t.data_ptr()
+    p = _lib.LaunchPlan()
+    rc = _lib.load().kda_recurrent_plan(ctypes.byref(a), ctypes.byref(p))
+    if rc != 0:
+        return {"rows_per_block": None, "grid_x": None}
+    return {"rows_per_block": p.rows_per_block, "grid_x": p.grid_x}
+
+
 class Timer:
     """HIP events on the launch stream around a region."""
 
@@ -176,6 +201,132 @@ def time_cold(torch, fn, n, flush_buf):
         tot.append(s.elapsed_time(e) * 1e3)
     tot.sort()
     return tot[len(tot) // 2]
+
+
+# --------------------------------------------------------- other workloads ----
+
+def rotating(torch, timer, calls, reps=8):
+    """Average GPU time per call of `calls` (each touching its own slots, so
+    consecutive calls find their state cold in L2 and the MALL), captured once
+    into a HIP graph and replayed back to back: host launch overhead does not
+    enter the measurement."""
+    cur = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    side.wait_stream(cur)
+    with torch.cuda.stream(side):
+        for f in calls:
+            f()
+    cur.wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for f in calls:
+            f()
+    graph.replay()
+    torch.cuda.synchronize()
+    return timer.run(graph.replay, reps) / len(calls)
+
+
+def extra_workloads(torch, dev, timer, pool32):
+    from gated_delta_rule_decode_amd import fused_kda_decode, packed_kda_decode, recurrent_kda, synth
+    out = {}
+    H = 32
+    SLOTS = pool32.shape[0]
+    # H=32 fp32 batch sweep on the 8 GiB pool: 4 disjoint slot sets per B
+    sweep = []
+    g2 = torch.Generator(device=dev)
+    for Bs in (1, 8, 32, 128, 256, 512):
+        cs = synth.recurrent_case(1000 + Bs, n_seqs=Bs, H=H, num_slots=1, device=dev)
+        g2.manual_seed(1000 + Bs)
+        perm = torch.randperm(SLOTS, generator=g2, device=dev).to(torch.int32)
+        o = torch.empty((Bs, 1, H, D), dtype=torch.bfloat16, device=dev)
+        r4 = lambda t, n=Bs: t.reshape(n, 1, H, D)  # noqa: E731
+        calls = []
+        for j in range(4):
+            ids = perm[j * Bs:(j + 1) * Bs].contiguous()
+            calls.append(lambda cs=cs, ids=ids, o=o, r4=r4, n=Bs: recurrent_kda(
+                r4(cs.q), r4(cs.k), r4(cs.v), r4(cs.g), cs.beta.reshape(n, 1, H), cs.A_log,
+                cs.dt_bias, initial_state=pool32, state_indices=ids, output=o))
+        t_us = rotating(torch, timer, calls)
+        bts = t1_bytes(Bs, 0, H, 4)
+        sweep.append({"B": Bs, "us": t_us, "rows_per_s": Bs / (t_us * 1e-6),
+                      "state_GBps": t1_state_bytes(Bs, H, 4) / (t_us * 1e-6) / 1e9,
+                      "GBps": bts / (t_us * 1e-6) / 1e9,
+                      "frac": bts / (t_us * 1e-6) / 1e9 / HBM_PEAK_GBPS})
+        log(f"H=32 fp32 B={Bs}: {t_us:.1f} us, {sweep[-1]['GBps']:.0f} GB/s")
+    out["recurrent_t1_h32_fp32"] = sweep
+
+    # packed H=12, bf16 pool [8192,12,128,128] (3 GiB), 1/8 of the rows inactive,
+    # 8 disjoint slot sets per B
+    pcase = synth.packed_case(2000, B=512, H=12, num_slots=8192, device=dev)
+    perm = torch.randperm(8192 - 1, generator=g2, device=dev).to(torch.int32) + 1
+    sweep = []
+    for Bs in (1, 8, 16, 31, 32, 64, 128, 256, 512):
+        nnull = Bs // 8
+        o = torch.empty((Bs, 1, 12, D), dtype=torch.bfloat16, device=dev)
+        calls = []
+        for j in range(8):
+            ids = perm[j * Bs:(j + 1) * Bs].clone()
+            ids[:nnull] = -1
+            calls.append(lambda ids=ids, o=o, n=Bs: packed_kda_decode(
+                pcase.mixed_qkv[:n], pcase.raw_gate[:n], pcase.raw_beta[:n], pcase.A_log,
+                pcase.dt_bias, pcase.state, ids, output=o))
+        t_us = rotating(torch, timer, calls)
+        live = Bs - nnull
+        bts = t1_bytes(live, nnull, 12, 2)
+        sweep.append({"B": Bs, "live": live, "us": t_us, "rows_per_s": live / (t_us * 1e-6),
+                      "state_GBps": t1_state_bytes(live, 12, 2) / (t_us * 1e-6) / 1e9,
+                      "GBps": bts / (t_us * 1e-6) / 1e9,
+                      "frac": bts / (t_us * 1e-6) / 1e9 / HBM_PEAK_GBPS})
+        log(f"packed H=12 bf16 B={Bs} ({live} live): {t_us:.1f} us, {sweep[-1]['GBps']:.0f} GB/s")
+    out["packed_t1_h12_bf16"] = sweep
+    del pcase
+    torch.cuda.empty_cache()
+
+    # fused, rows=256, H=32, fp32 pool [2048,32,128,128], 16 null rows; two
+    # disjoint slot sets
+    fc = synth.fused_case(3000, rows=256, H=32, num_slots=2048, device=dev, null_zero=8, null_neg=8)
+    idx2 = fc.state_indices.clone()
+    live_mask = idx2 > 0
+    free = torch.ones(2048, dtype=torch.bool, device=dev)
+    free[0] = False
+    free[idx2[live_mask].long()] = False
+    spare = torch.nonzero(free).flatten()[:int(live_mask.sum())].to(torch.int32)
+    idx2[live_mask] = spare
+    o = torch.empty((1, 256, 32, D), dtype=torch.bfloat16, device=dev)
+    calls = [lambda ids=ids: fused_kda_decode(fc.x, fc.weight, fc.conv_state, fc.raw_gate, fc.raw_beta,
+                                              fc.A_log, fc.dt_bias, ids, fc.state, fc.output_gate,
+                                              fc.norm_weight, output=o)
+             for ids in (fc.state_indices, idx2)]
+    t_us = rotating(torch, timer, calls)
+    bts = fused_bytes(240, 16, 32, 4)
+    out["fused_h32_rows256_fp32"] = {"us": t_us, "rows_per_s": 240 / (t_us * 1e-6),
+                                     "GBps": bts / (t_us * 1e-6) / 1e9,
+                                     "frac": bts / (t_us * 1e-6) / 1e9 / HBM_PEAK_GBPS}
+    log(f"fused H=32 rows=256: {t_us:.1f} us, {bts / (t_us * 1e-6) / 1e9:.0f} GB/s")
+    del fc
+    torch.cuda.empty_cache()
+
+    # ragged T>=2: H=16, N=64, lengths U{0..6}, fp32 checkpoints; the pool has
+    # 4 disjoint slot sets
+    lengths = synth.ragged_lengths(4000, 64, 0, 6)
+    vc = synth.recurrent_case(4000, n_seqs=64, H=16, num_slots=4 * 64 + 1, device=dev,
+                              lengths=lengths, slot_lo=1)
+    T = sum(lengths)
+    ck = torch.empty((T, 16, D, D), dtype=torch.float32, device=dev)
+    o = torch.empty((1, T, 16, D), dtype=torch.bfloat16, device=dev)
+    r1 = lambda t: t.reshape(1, T, *t.shape[1:])  # noqa: E731
+    calls = [lambda ids=(vc.state_indices + 64 * j).contiguous(): recurrent_kda(
+        r1(vc.q), r1(vc.k), r1(vc.v), r1(vc.g), r1(vc.beta), vc.A_log, vc.dt_bias,
+        initial_state=vc.state, state_indices=ids, cu_seqlens=vc.cu_seqlens, output=o,
+        intermediate_states=ck) for j in range(4)]
+    t_us = rotating(torch, timer, calls)
+    bts = varlen_bytes(lengths, 16, 4)
+    out["varlen_h16_n64_fp32_ckpt"] = {"us": t_us, "tokens": T, "tokens_per_s": T / (t_us * 1e-6),
+                                       "GBps": bts / (t_us * 1e-6) / 1e9,
+                                       "frac": bts / (t_us * 1e-6) / 1e9 / HBM_PEAK_GBPS}
+    log(f"varlen H=16 N=64 T={T}: {t_us:.1f} us, {bts / (t_us * 1e-6) / 1e9:.0f} GB/s")
+    return out
 
 
 # ------------------------------------------------------------------ main ----
@@ -254,7 +405,8 @@ def main():
         log(f"copy 1 GiB -> 1 GiB: {cus:.1f} us, {2 * (1 << 30) / (cus * 1e-6) / 1e9:.0f} GB/s")
         del src, dst
 
-    traffic = load_traffic(bytes_launch)
+    traffic_bytes = load_traffic(bytes_launch)
+    plan = launch_plan(c, idx, pool, out, B, H)
     result = {
         "metric": METRIC,
         "value": B * 1e6 / us,
@@ -273,99 +425,18 @@ def main():
                    "B": B, "H": H, "state_dtype": "fp32", "num_slots": SLOTS},
         "state_GBps": state_bytes / (us * 1e-6) / 1e9,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
-                     "kernel": "kda_recurrent_kernel<G=8, fp32, T=1>",
-                     "bytes_per_launch": bytes_launch},
+                     "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": None if traffic_bytes is None else traffic_bytes / (us * 1e-6) / 1e9,
+                     "traffic_bytes_per_launch": traffic_bytes,
+                     "algorithmic_bytes_per_launch": bytes_launch,
+                     "kernel": f"kda_recurrent_kernel (T=1, fp32 state, {plan['rows_per_block']} value "
+                               f"rows per workgroup, {plan['grid_x']} workgroups)",
+                     "practical_ceiling_GBps": 6100.0},
         "cpu_baseline": cpu,
     }
 
     if not args.no_extra:
-        extra = {}
-        flush = torch.empty(1 << 27, dtype=torch.float32, device=dev)
-        # H=32 fp32 batch sweep (same pool; fresh random slots per B)
-        sweep = []
-        for Bs in (1, 8, 32, 128, 256, 512):
-            cs = synth.recurrent_case(1000 + Bs, n_seqs=Bs, H=H, num_slots=1, device=dev)
-            g2 = torch.Generator(device=dev)
-            g2.manual_seed(1000 + Bs)
-            ids = synth.unique_slots(g2, Bs, 0, SLOTS, dev)
-            o = torch.empty((Bs, 1, H, D), dtype=torch.bfloat16, device=dev)
-            r4 = lambda t, n=Bs: t.reshape(n, 1, H, D)  # noqa: E731
-            fn = (lambda cs=cs, ids=ids, o=o, r4=r4, n=Bs: recurrent_kda(
-                r4(cs.q), r4(cs.k), r4(cs.v), r4(cs.g), cs.beta.reshape(n, 1, H), cs.A_log,
-                cs.dt_bias, initial_state=pool, state_indices=ids, output=o))
-            fn()
-            t_us = time_cold(torch, fn, 20, flush)
-            bts = t1_bytes(Bs, 0, H, 4)
-            sweep.append({"B": Bs, "us": t_us, "rows_per_s": Bs / (t_us * 1e-6),
-                          "state_GBps": t1_state_bytes(Bs, H, 4) / (t_us * 1e-6) / 1e9,
-                          "GBps": bts / (t_us * 1e-6) / 1e9,
-                          "frac": bts / (t_us * 1e-6) / 1e9 / HBM_PEAK_GBPS})
-            log(f"sweep H=32 fp32 B={Bs}: {t_us:.1f} us cold, {sweep[-1]['GBps']:.0f} GB/s")
-        extra["recurrent_t1_h32_fp32_cold"] = sweep
-        del pool
-        torch.cuda.empty_cache()
-
-        # packed H=12 bf16 pool [1024,12,128,128], 1/8 rows inactive
-        sweep = []
-        for Bs in (1, 8, 16, 31, 32, 64, 128, 256, 512):
-            nslots = max(1024, Bs + 1)
-            pc = synth.packed_case(2000 + Bs, B=Bs, H=12, num_slots=nslots, device=dev,
-                                   null_rows=Bs // 8)
-            o = torch.empty((Bs, 1, 12, D), dtype=torch.bfloat16, device=dev)
-            fn = (lambda pc=pc, o=o: packed_kda_decode(pc.mixed_qkv, pc.raw_gate, pc.raw_beta,
-                                                       pc.A_log, pc.dt_bias, pc.state,
-                                                       pc.state_indices, output=o))
-            fn()
-            t_us = time_cold(torch, fn, 20, flush)
-            live = Bs - Bs // 8
-            bts = t1_bytes(live, Bs // 8, 12, 2)
-            sweep.append({"B": Bs, "live": live, "us": t_us, "rows_per_s": live / (t_us * 1e-6),
-                          "state_GBps": t1_state_bytes(live, 12, 2) / (t_us * 1e-6) / 1e9,
-                          "GBps": bts / (t_us * 1e-6) / 1e9,
-                          "frac": bts / (t_us * 1e-6) / 1e9 / HBM_PEAK_GBPS})
-            log(f"sweep packed H=12 bf16 B={Bs}: {t_us:.1f} us cold, {sweep[-1]['GBps']:.0f} GB/s")
-            del pc
-        extra["packed_t1_h12_bf16_cold"] = sweep
-
-        # fused, rows=256, H=32, fp32 pool [2048,32,128,128], 16 null rows
-        fc = synth.fused_case(3000, rows=256, H=32, num_slots=2048, device=dev, null_zero=8,
-                              null_neg=8)
-        o = torch.empty((1, 256, 32, D), dtype=torch.bfloat16, device=dev)
-        fn = (lambda: fused_kda_decode(fc.x, fc.weight, fc.conv_state, fc.raw_gate, fc.raw_beta,
-                                       fc.A_log, fc.dt_bias, fc.state_indices, fc.state,
-                                       fc.output_gate, fc.norm_weight, output=o))
-        fn()
-        t_us = time_cold(torch, fn, 20, flush)
-        bts = fused_bytes(240, 16, 32, 4)
-        extra["fused_h32_rows256_fp32_cold"] = {"us": t_us, "rows_per_s": 240 / (t_us * 1e-6),
-                                                "GBps": bts / (t_us * 1e-6) / 1e9,
-                                                "frac": bts / (t_us * 1e-6) / 1e9 / HBM_PEAK_GBPS}
-        log(f"fused H=32 rows=256: {t_us:.1f} us cold, {bts / (t_us * 1e-6) / 1e9:.0f} GB/s")
-        del fc
-        torch.cuda.empty_cache()
-
-        # ragged T>=2: H=16, N=64, lengths U{0..6}, fp32 checkpoints
-        lengths = synth.ragged_lengths(4000, 64, 0, 6)
-        vc = synth.recurrent_case(4000, n_seqs=64, H=16, num_slots=65, device=dev, lengths=lengths,
-                                  slot_lo=1)
-        T = sum(lengths)
-        ck = torch.empty((T, 16, D, D), dtype=torch.float32, device=dev)
-        o = torch.empty((1, T, 16, D), dtype=torch.bfloat16, device=dev)
-        r1 = lambda t: t.reshape(1, T, *t.shape[1:])  # noqa: E731
-        fn = (lambda: recurrent_kda(r1(vc.q), r1(vc.k), r1(vc.v), r1(vc.g), r1(vc.beta), vc.A_log,
-                                    vc.dt_bias, initial_state=vc.state,
-                                    state_indices=vc.state_indices, cu_seqlens=vc.cu_seqlens,
-                                    output=o, intermediate_states=ck))
-        fn()
-        t_us = time_cold(torch, fn, 20, flush)
-        bts = varlen_bytes(lengths, 16, 4)
-        extra["varlen_h16_n64_fp32_ckpt_cold"] = {"us": t_us, "tokens": T,
-                                                  "tokens_per_s": T / (t_us * 1e-6),
-                                                  "GBps": bts / (t_us * 1e-6) / 1e9,
-                                                  "frac": bts / (t_us * 1e-6) / 1e9 / HBM_PEAK_GBPS}
-        log(f"varlen H=16 N=64 T={T}: {t_us:.1f} us cold, {bts / (t_us * 1e-6) / 1e9:.0f} GB/s")
-        result["workloads"] = extra
+        result["workloads"] = extra_workloads(torch, dev, timer, pool)
 
     print(json.dumps(result), flush=True)
 

@@ -99,8 +99,26 @@ __device__ __forceinline__ void row_sum16x3(float &a, float &b, float &c)
 
 // ---------------------------------------------------------- scalar math ----
 
-__device__ __forceinline__ float softplus_f(float x) { return fmaxf(x, 0.0f) + log1pf(__expf(-fabsf(x))); }
-__device__ __forceinline__ float sigmoid_f(float x) { return 1.0f / (1.0f + __expf(-x)); }
+// softplus(x) = max(x, 0) + log(1 + e^-|x|) with the hardware exp/log (the
+// absolute error stays near 1e-7; for e^-|x| below 2^-24 the log term is
+// lost, an absolute error under 6e-8).
+__device__ __forceinline__ float softplus_f(float x) { return fmaxf(x, 0.0f) + __logf(1.0f + __expf(-fabsf(x))); }
+__device__ __forceinline__ float sigmoid_f(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
+
+__device__ __forceinline__ float lane_value(float x, int lane)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
+}
+
+// Sums over the 64 lanes of a wave (three at once); the results are
+// wave-uniform.
+__device__ __forceinline__ void wave_sum3(float &a, float &b, float &c)
+{
+    row_sum16x3(a, b, c);
+    a = (lane_value(a, 0) + lane_value(a, 16)) + (lane_value(a, 32) + lane_value(a, 48));
+    b = (lane_value(b, 0) + lane_value(b, 16)) + (lane_value(b, 32) + lane_value(b, 48));
+    c = (lane_value(c, 0) + lane_value(c, 16)) + (lane_value(c, 32) + lane_value(c, 48));
+}
 
 // --------------------------------------------------------- state tiles ----
 //
@@ -213,44 +231,55 @@ __device__ __forceinline__ void store_zero_bf16(uint16_t *dst)
     store_out_bf16<G>(dst, z);
 }
 
-// Per-lane operands of one token: normalised q (scale folded in), normalised
-// k and the decay, at the lane's 8 key channels, plus beta and q_hat.k_hat.
+// Per-lane operands of one token: q, k (not normalised) and the decay at
+// the lane's 8 key channels, plus the per-token scalars: beta,
+// rk = 1/sqrt(|k|^2 + eps), rqs = scale/sqrt(|q|^2 + eps) and
+// qk = scale * q_hat.k_hat.  The L2 normalisation is folded into these
+// scalars instead of being applied to every channel.
 struct TokenOps {
     float q[8], k[8], d[8];
-    float beta, qk;
+    float beta, rk, rqs, qk;
 };
 
+// Channel values from LDS; the three norm sums either come from the
+// staging waves (norms != nullptr: partials of waves 2 and 3) or are reduced
+// here over the DPP row.
 template <bool BF16>
 __device__ __forceinline__ void read_token_ops(TokenOps &t, const float *sq, const float *sk,
-                                               const float *sd, int m, float scale, float eps,
-                                               float beta)
+                                               const float *sd, const float *norms, int m, float scale,
+                                               float eps, float beta)
 {
-    float ss_q = 0.f, ss_k = 0.f, s_qk = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         const int c = StateIO<BF16>::chan(m, e);
         t.q[e] = sq[c];
         t.k[e] = sk[c];
         t.d[e] = sd[c];
-        ss_q = fmaf(t.q[e], t.q[e], ss_q);
-        ss_k = fmaf(t.k[e], t.k[e], ss_k);
-        s_qk = fmaf(t.q[e], t.k[e], s_qk);
     }
-    row_sum16x3(ss_q, ss_k, s_qk);
-    const float rq = rsqrtf(ss_q + eps) * scale;
-    const float rk = rsqrtf(ss_k + eps);
+    float ss_q, ss_k, s_qk;
+    if (norms) {
+        ss_q = norms[0] + norms[4];
+        ss_k = norms[1] + norms[5];
+        s_qk = norms[2] + norms[6];
+    } else {
+        ss_q = 0.f, ss_k = 0.f, s_qk = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        t.q[e] *= rq;
-        t.k[e] *= rk;
+        for (int e = 0; e < 8; ++e) {
+            ss_q = fmaf(t.q[e], t.q[e], ss_q);
+            ss_k = fmaf(t.k[e], t.k[e], ss_k);
+            s_qk = fmaf(t.q[e], t.k[e], s_qk);
+        }
+        row_sum16x3(ss_q, ss_k, s_qk);
     }
-    t.qk = s_qk * rq * rk;
+    t.rqs = rsqrtf(ss_q + eps) * scale;
+    t.rk = rsqrtf(ss_k + eps);
+    t.qk = s_qk * t.rqs * t.rk;
     t.beta = beta;
 }
 
 // One token on one value row held as 8 fp32 values per lane:
-//   s <- d*s;  a = k.s;  c = q.s;  u = v - a;  s <- s + beta*u*k;
-//   o = c + beta*u*(q.k)       (= scale * q_hat . s_new)
+//   s <- d*s;  a = k_hat.s;  c = scale*q_hat.s;  u = v - a;
+//   s <- s + beta*u*k_hat;  o = c + beta*u*scale*(q_hat.k_hat)  (= scale*q_hat.s_new)
 __device__ __forceinline__ float row_update(float s[8], const TokenOps &t, float v)
 {
     float pa = 0.f, pc = 0.f;
@@ -261,10 +290,11 @@ __device__ __forceinline__ float row_update(float s[8], const TokenOps &t, float
         pc = fmaf(t.q[e], s[e], pc);
     }
     row_sum16x2(pa, pc);
-    const float bu = t.beta * (v - pa);
+    const float bu = t.beta * (v - pa * t.rk);
+    const float bk = bu * t.rk;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) s[e] = fmaf(bu, t.k[e], s[e]);
-    return fmaf(bu, t.qk, pc);
+    for (int e = 0; e < 8; ++e) s[e] = fmaf(bk, t.k[e], s[e]);
+    return fmaf(bu, t.qk, pc * t.rqs);
 }
 
 // One token's channel inputs, held in registers between their load and the
@@ -291,16 +321,29 @@ __device__ __forceinline__ StageIn load_stage(int tid, const uint16_t *q, const 
     return s;
 }
 
-// Gate transform once per channel: decay = exp(-exp(A_log) * softplus(g + dt_bias)).
+// Gate transform once per channel, decay = exp(-exp(A_log) * softplus(g +
+// dt_bias), by threads 0..127; threads 128..255 stage v and reduce the three
+// norm sums (|q|^2, |k|^2, q.k) over their wave, writing one partial per
+// wave to norms[4 * (wave - 2) + {0, 1, 2}].
 __device__ __forceinline__ void write_stage(int tid, const StageIn &s, float a_h, float *sq, float *sk,
-                                            float *sd, float *sv)
+                                            float *sd, float *sv, float *norms)
 {
+    const float q = bf16_bits_to_f32(s.q);
+    const float k = bf16_bits_to_f32(s.k);
     if (tid < KD) {
-        sq[tid] = bf16_bits_to_f32(s.q);
-        sk[tid] = bf16_bits_to_f32(s.k);
+        sq[tid] = q;
+        sk[tid] = k;
         sd[tid] = __expf(-a_h * softplus_f(bf16_bits_to_f32(s.g) + s.dt));
     } else {
         sv[tid - KD] = bf16_bits_to_f32(s.v);
+        float pq = q * q, pk = k * k, pqk = q * k;
+        wave_sum3(pq, pk, pqk);
+        if ((tid & 63) == 0) {
+            float *n = norms + 4 * ((tid >> 6) - 2);
+            n[0] = pq;
+            n[1] = pk;
+            n[2] = pqk;
+        }
     }
 }
 
@@ -313,6 +356,7 @@ __global__ void __launch_bounds__(256) kda_recurrent_kernel(const RecParams p)
     constexpr int VT = 16 * G;  // value rows per workgroup
 
     __shared__ float s_q[2][KD], s_k[2][KD], s_d[2][KD], s_v[2][KD];
+    __shared__ float s_norm[2][8];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -373,11 +417,11 @@ __global__ void __launch_bounds__(256) kda_recurrent_kernel(const RecParams p)
 
     if constexpr (!VARLEN) {
         // T=1: the gate transform and the norms overlap the state fetch.
-        write_stage(tid, in, a_h, s_q[0], s_k[0], s_d[0], s_v[0]);
+        write_stage(tid, in, a_h, s_q[0], s_k[0], s_d[0], s_v[0], s_norm[0]);
         const float beta = sigmoid_f(bf16_bits_to_f32(braw));
         __syncthreads();
         TokenOps ops;
-        read_token_ops<BF16>(ops, s_q[0], s_k[0], s_d[0], m, p.scale, p.l2_eps, beta);
+        read_token_ops<BF16>(ops, s_q[0], s_k[0], s_d[0], s_norm[0], m, p.scale, p.l2_eps, beta);
         float o[G];
 #pragma unroll
         for (int gi = 0; gi < G; ++gi) {
@@ -398,7 +442,7 @@ __global__ void __launch_bounds__(256) kda_recurrent_kernel(const RecParams p)
         for (int gi = 0; gi < G; ++gi) IO::unpack(raw[gi], st[gi]);
         for (int t = t0; t < t1; ++t) {
             const int buf = (t - t0) & 1;
-            write_stage(tid, in, a_h, s_q[buf], s_k[buf], s_d[buf], s_v[buf]);
+            write_stage(tid, in, a_h, s_q[buf], s_k[buf], s_d[buf], s_v[buf], s_norm[buf]);
             const float beta = sigmoid_f(bf16_bits_to_f32(braw));
             if (t + 1 < t1) {
                 const int64_t n = t + 1;
@@ -408,7 +452,8 @@ __global__ void __launch_bounds__(256) kda_recurrent_kernel(const RecParams p)
             }
             __syncthreads();
             TokenOps ops;
-            read_token_ops<BF16>(ops, s_q[buf], s_k[buf], s_d[buf], m, p.scale, p.l2_eps, beta);
+            read_token_ops<BF16>(ops, s_q[buf], s_k[buf], s_d[buf], s_norm[buf], m, p.scale, p.l2_eps,
+                                 beta);
             float o[G];
 #pragma unroll
             for (int gi = 0; gi < G; ++gi) o[gi] = row_update(st[gi], ops, s_v[buf][r_base + gi]);
@@ -534,7 +579,7 @@ __global__ void __launch_bounds__(256) kda_fused_kernel(const FusedParams p)
     __syncthreads();
 
     TokenOps ops;
-    read_token_ops<BF16>(ops, s_act, s_act + KD, s_d, m, p.scale, p.l2_eps, beta);
+    read_token_ops<BF16>(ops, s_act, s_act + KD, s_d, nullptr, m, p.scale, p.l2_eps, beta);
     float o[G];
     float ss = 0.f;
 #pragma unroll
