@@ -56,6 +56,9 @@ def _load(path=None):
         lib.kdao_recurrent.restype = Int
         lib.kdao_recurrent.argtypes = [I64, I64, I64, P, P, P, P, P, P, P, Dbl, Dbl,
                                        P, P, I64, Int, P, P, P, Int, P, P]
+        lib.kdao_recurrent2.restype = Int
+        lib.kdao_recurrent2.argtypes = [I64, I64, I64, I64, P, P, P, P, Int, P, Int, Int, P, P,
+                                        Dbl, Dbl, P, I64, P, I64, Int, P, Int, P, P, Int, P, P]
         lib.kdao_fused.restype = Int
         lib.kdao_fused.argtypes = [I64, I64, P, P, I64, P, I64, P, P, P, P, P, Int, P,
                                    P, P, Dbl, Dbl, Dbl, P, P, P, P]
@@ -136,40 +139,62 @@ def bf16_to_f64(bits) -> np.ndarray:
 
 # ---- entry points --------------------------------------------------------------
 
+def _gate_input(a, what):
+    a = np.ascontiguousarray(as_np(a))
+    if a.dtype == np.uint16:
+        return a, 0
+    if a.dtype == np.float32:
+        return a, 1
+    raise TypeError(f"{what} must be bf16 (uint16 bits) or float32, got {a.dtype}")
+
+
 def recurrent(q, k, v, g, beta, A_log, dt_bias, state, state_indices,
               cu_seqlens=None, *, scale=SCALE, l2_eps=L2_EPS, ckpt_dtype=None,
-              want_ckpt64=False):
-    """Recurrent KDA (T=1, or ragged packed T>=0 when cu_seqlens is given).
+              want_ckpt64=False, gate="in_kernel", update_state=True, tokens_per_seq=1):
+    """Recurrent KDA: T=1, uniform batches of tokens_per_seq tokens, or ragged
+    (cu_seqlens given).
 
-    q, k, v, g: bf16 [T, H, 128]; beta: bf16 [T, H]; A_log fp32 [H];
-    dt_bias fp32 [H*128]; state [slots, H, 128, 128] (fp32, bf16 bits or
-    float64); state_indices int32 [N]; cu_seqlens int32 [N+1] or None.
+    q, k: bf16 [T, H, 128]; v: bf16 [T, HV, 128] (HV a multiple of H; value
+    head hv reads q/k head hv // (HV // H)); g: [T, HV, 128] and beta: [T, HV],
+    bf16 bits or float32.  gate="in_kernel": g is the raw gate, beta logits,
+    A_log fp32 [HV] and dt_bias fp32 [HV*128] are used; gate="precomputed": g
+    is the log-decay and beta is beta itself (A_log, dt_bias may be None).
+    state [slots, HV, 128, 128] (fp32, bf16 bits or float64), state_indices
+    int32 [N].  update_state=False leaves the pool as it was (read-only verify).
     Returns dict(out64, out_bf16, state, ckpt, ckpt64).
     """
     q = _c(q, np.uint16); k = _c(k, np.uint16); v = _c(v, np.uint16)
-    g = _c(g, np.uint16); beta = _c(beta, np.uint16)
-    A_log = _c(A_log, np.float32); dt_bias = _c(dt_bias, np.float32)
+    g, g_f32 = _gate_input(g, "g")
+    beta, b_f32 = _gate_input(beta, "beta")
+    mode = {"in_kernel": 0, "precomputed": 1}[gate]
+    A_log = None if A_log is None else _c(A_log, np.float32)
+    dt_bias = None if dt_bias is None else _c(dt_bias, np.float32)
+    if mode == 0 and (A_log is None or dt_bias is None):
+        raise ValueError("the in-kernel gate needs A_log and dt_bias")
     st = np.array(as_np(state), copy=True, order="C")
     sdt = _dtype_code(st)
     idx = _c(state_indices, np.int32)
     cu = None if cu_seqlens is None else _c(cu_seqlens, np.int32)
     T, H = q.shape[0], q.shape[1]
+    HV = v.shape[1]
     N = idx.shape[0]
-    assert q.shape == (T, H, D) and beta.shape == (T, H) and st.shape[1:] == (H, D, D)
-    out64 = np.zeros((T, H, D), np.float64)
-    outb = np.zeros((T, H, D), np.uint16)
+    assert k.shape == q.shape and v.shape == (T, HV, D) and g.shape == (T, HV, D)
+    assert beta.shape == (T, HV) and st.shape[1:] == (HV, D, D)
+    out64 = np.zeros((T, HV, D), np.float64)
+    outb = np.zeros((T, HV, D), np.uint16)
     ckpt = None
     cdt = 0
     if ckpt_dtype is not None:
         cdt = ckpt_dtype
-        ckpt = np.zeros((T, H, D, D), _NP_OF[cdt])
-    ck64 = np.zeros((T, H, D, D), np.float64) if want_ckpt64 else None
-    rc = _load().kdao_recurrent(T, N, H, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                                _ptr(A_log), _ptr(dt_bias), float(scale), float(l2_eps),
-                                _ptr(cu), _ptr(idx), st.shape[0], sdt, _ptr(st),
-                                _ptr(out64), _ptr(outb), cdt, _ptr(ckpt), _ptr(ck64))
+        ckpt = np.zeros((T, HV, D, D), _NP_OF[cdt])
+    ck64 = np.zeros((T, HV, D, D), np.float64) if want_ckpt64 else None
+    rc = _load().kdao_recurrent2(T, N, H, HV, _ptr(q), _ptr(k), _ptr(v), _ptr(g), g_f32,
+                                 _ptr(beta), b_f32, mode, _ptr(A_log), _ptr(dt_bias),
+                                 float(scale), float(l2_eps), _ptr(cu), int(tokens_per_seq),
+                                 _ptr(idx), st.shape[0], sdt, _ptr(st), 1 if update_state else 0,
+                                 _ptr(out64), _ptr(outb), cdt, _ptr(ckpt), _ptr(ck64))
     if rc != 0:
-        raise ValueError(f"kdao_recurrent rejected its arguments ({rc})")
+        raise ValueError(f"kdao_recurrent2 rejected its arguments ({rc})")
     return dict(out64=out64, out_bf16=outb, state=st, ckpt=ckpt, ckpt64=ck64)
 
 

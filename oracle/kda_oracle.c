@@ -184,19 +184,116 @@ static void widen_bf16(const uint16_t *src, double *dst, int n)
 }
 
 /*
- * Recurrent KDA: T=1 (cu_seqlens == NULL, one token per sequence) or packed
- * ragged T>=0 per sequence (cu_seqlens [n_seqs+1], tokens processed in
- * order with the state carried between them).
+ * Recurrent KDA: T=1 (cu_seqlens == NULL and tokens_per_seq <= 1, one token
+ * per sequence), uniform batches of tokens_per_seq tokens per sequence, or
+ * packed ragged T>=0 per sequence (cu_seqlens [n_seqs+1]); tokens are
+ * processed in order with the state carried between them.
+ *
+ * Heads: H q/k heads and HV value heads, HV a multiple of H; value head hv
+ * reads q/k head hv / (HV/H) (grouped value heads).  The state, v, the gate,
+ * beta, A_log and dt_bias are per value head.
+ *
+ * gate_mode 0 (in-kernel gate): g is the raw gate, decay = exp(-exp(A_log) *
+ * softplus(g + dt_bias)) and beta holds logits, beta = sigmoid(logit).
+ * gate_mode 1 (precomputed): g is the log-decay (decay = exp(g)) and beta is
+ * beta itself; A_log and dt_bias are not read.
+ * update_state 0: the pool is read only (speculative verify); outputs and
+ * checkpoints are produced as usual.
  *
  * Layouts (all contiguous, host memory):
- *   q, k, v, graw: bf16 [n_tokens][H][128];  braw: bf16 [n_tokens][H]
- *   A_log fp32 [H];  dt_bias fp32 [H*128]
- *   state: [num_slots][H][128 v][128 k] of state_dtype, updated in place
- *   out64 (may be NULL) double [n_tokens][H][128];  out_bf16 (may be NULL)
- *   ckpt (may be NULL): [n_tokens][H][128 v][128 k] of ckpt_dtype, the state
+ *   q, k: bf16 [n_tokens][H][128];  v: bf16 [n_tokens][HV][128]
+ *   g: [n_tokens][HV][128] and beta: [n_tokens][HV], each bf16 or fp32
+ *   (g_f32, beta_f32);  A_log fp32 [HV];  dt_bias fp32 [HV*128]
+ *   state: [num_slots][HV][128 v][128 k] of state_dtype
+ *   out64 (may be NULL) double [n_tokens][HV][128];  out_bf16 (may be NULL)
+ *   ckpt (may be NULL): [n_tokens][HV][128 v][128 k] of ckpt_dtype, the state
  *   after each token;  ckpt64 (may be NULL) the same in double.
  * Returns 0, or -1 on inconsistent metadata.
  */
+static double load_in(const void *p, int is_f32, size_t i)
+{
+    return is_f32 ? (double)((const float *)p)[i] : bf16_to_f64(((const uint16_t *)p)[i]);
+}
+
+int kdao_recurrent2(int64_t n_tokens, int64_t n_seqs, int64_t H, int64_t HV,
+                    const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                    const void *g, int g_f32, const void *beta, int beta_f32, int gate_mode,
+                    const float *A_log, const float *dt_bias,
+                    double scale, double l2_eps,
+                    const int32_t *cu_seqlens, int64_t tokens_per_seq,
+                    const int32_t *state_indices, int64_t num_slots, int state_dtype,
+                    void *state, int update_state,
+                    double *out64, uint16_t *out_bf16,
+                    int ckpt_dtype, void *ckpt, double *ckpt64)
+{
+    if (n_tokens < 0 || n_seqs < 0 || H <= 0 || HV <= 0 || HV % H != 0) return -1;
+    const int64_t tps = tokens_per_seq > 1 ? tokens_per_seq : 1;
+    if (!cu_seqlens && n_tokens != n_seqs * tps) return -1;
+    if (cu_seqlens) {
+        if (cu_seqlens[0] != 0 || cu_seqlens[n_seqs] != n_tokens) return -1;
+        for (int64_t i = 0; i < n_seqs; ++i)
+            if (cu_seqlens[i + 1] < cu_seqlens[i]) return -1;
+    }
+    const int64_t group = HV / H;
+    double (*S)[KD] = malloc(sizeof(double) * KD * KD);
+    if (!S) return -2;
+    double qv[KD], kv[KD], vv[KD], gv[KD], qh[KD], kh[KD], dec[KD], o[KD];
+
+    const size_t head_elems = (size_t)KD * KD;
+    for (int64_t i = 0; i < n_seqs; ++i) {
+        int64_t t0 = cu_seqlens ? cu_seqlens[i] : i * tps;
+        int64_t t1 = cu_seqlens ? cu_seqlens[i + 1] : (i + 1) * tps;
+        int32_t idx = state_indices[i];
+        int null_row = idx < 0 || (int64_t)idx >= num_slots;
+        for (int64_t hv = 0; hv < HV; ++hv) {
+            const int64_t hk = hv / group;
+            if (null_row) {
+                for (int64_t t = t0; t < t1; ++t)
+                    for (int j = 0; j < KD; ++j) {
+                        size_t oi = ((size_t)t * HV + hv) * KD + j;
+                        if (out64) out64[oi] = 0.0;
+                        if (out_bf16) out_bf16[oi] = 0;
+                    }
+                continue;
+            }
+            if (t1 == t0) continue; /* empty sequence: nothing read or written */
+            size_t head_base = ((size_t)idx * HV + hv) * head_elems;
+            gather_state(state, state_dtype, head_base, S);
+            for (int64_t t = t0; t < t1; ++t) {
+                size_t vq = ((size_t)t * H + hk) * KD;   /* q/k head of this value head */
+                size_t vh = ((size_t)t * HV + hv) * KD;  /* value-head vectors */
+                widen_bf16(q + vq, qv, KD);
+                widen_bf16(k + vq, kv, KD);
+                widen_bf16(v + vh, vv, KD);
+                for (int j = 0; j < KD; ++j) gv[j] = load_in(g, g_f32, vh + j);
+                double bin = load_in(beta, beta_f32, (size_t)t * HV + hv);
+                double b;
+                if (gate_mode == 0) {
+                    b = sigmoid(bin);
+                    gate_decay(gv, (double)A_log[hv], dt_bias + hv * KD, dec);
+                } else {
+                    b = bin;
+                    for (int j = 0; j < KD; ++j) dec[j] = exp(gv[j]);
+                }
+                l2_normalise(qv, l2_eps, qh);
+                l2_normalise(kv, l2_eps, kh);
+                kda_token(S, qh, kh, vv, dec, b, scale, o);
+                for (int j = 0; j < KD; ++j) {
+                    if (out64) out64[vh + j] = o[j];
+                    if (out_bf16) out_bf16[vh + j] = kdao_bf16_from_f64(o[j]);
+                }
+                size_t cb = ((size_t)t * HV + hv) * head_elems;
+                if (ckpt) scatter_state(ckpt, ckpt_dtype, cb, S);
+                if (ckpt64) scatter_state(ckpt64, KDAO_F64, cb, S);
+            }
+            if (update_state) scatter_state(state, state_dtype, head_base, S);
+        }
+    }
+    free(S);
+    return 0;
+}
+
+/* The equal-head, in-kernel-gate, state-updating form of kdao_recurrent2. */
 int kdao_recurrent(int64_t n_tokens, int64_t n_seqs, int64_t H,
                    const uint16_t *q, const uint16_t *k, const uint16_t *v,
                    const uint16_t *graw, const uint16_t *braw,
@@ -207,60 +304,9 @@ int kdao_recurrent(int64_t n_tokens, int64_t n_seqs, int64_t H,
                    double *out64, uint16_t *out_bf16,
                    int ckpt_dtype, void *ckpt, double *ckpt64)
 {
-    if (n_tokens < 0 || n_seqs < 0 || H <= 0) return -1;
-    if (!cu_seqlens && n_tokens != n_seqs) return -1;
-    if (cu_seqlens) {
-        if (cu_seqlens[0] != 0 || cu_seqlens[n_seqs] != n_tokens) return -1;
-        for (int64_t i = 0; i < n_seqs; ++i)
-            if (cu_seqlens[i + 1] < cu_seqlens[i]) return -1;
-    }
-    double (*S)[KD] = malloc(sizeof(double) * KD * KD);
-    if (!S) return -2;
-    double qv[KD], kv[KD], vv[KD], gv[KD], qh[KD], kh[KD], dec[KD], o[KD];
-
-    const size_t head_elems = (size_t)KD * KD;
-    for (int64_t i = 0; i < n_seqs; ++i) {
-        int64_t t0 = cu_seqlens ? cu_seqlens[i] : i;
-        int64_t t1 = cu_seqlens ? cu_seqlens[i + 1] : i + 1;
-        int32_t idx = state_indices[i];
-        int null_row = idx < 0 || (int64_t)idx >= num_slots;
-        for (int64_t h = 0; h < H; ++h) {
-            if (null_row) {
-                for (int64_t t = t0; t < t1; ++t)
-                    for (int j = 0; j < KD; ++j) {
-                        size_t oi = ((size_t)t * H + h) * KD + j;
-                        if (out64) out64[oi] = 0.0;
-                        if (out_bf16) out_bf16[oi] = 0;
-                    }
-                continue;
-            }
-            if (t1 == t0) continue; /* empty sequence: nothing read or written */
-            size_t head_base = ((size_t)idx * H + h) * head_elems;
-            gather_state(state, state_dtype, head_base, S);
-            for (int64_t t = t0; t < t1; ++t) {
-                size_t vec = ((size_t)t * H + h) * KD;
-                widen_bf16(q + vec, qv, KD);
-                widen_bf16(k + vec, kv, KD);
-                widen_bf16(v + vec, vv, KD);
-                widen_bf16(graw + vec, gv, KD);
-                double beta = sigmoid(bf16_to_f64(braw[(size_t)t * H + h]));
-                l2_normalise(qv, l2_eps, qh);
-                l2_normalise(kv, l2_eps, kh);
-                gate_decay(gv, (double)A_log[h], dt_bias + h * KD, dec);
-                kda_token(S, qh, kh, vv, dec, beta, scale, o);
-                for (int j = 0; j < KD; ++j) {
-                    if (out64) out64[vec + j] = o[j];
-                    if (out_bf16) out_bf16[vec + j] = kdao_bf16_from_f64(o[j]);
-                }
-                size_t cb = ((size_t)t * H + h) * head_elems;
-                if (ckpt) scatter_state(ckpt, ckpt_dtype, cb, S);
-                if (ckpt64) scatter_state(ckpt64, KDAO_F64, cb, S);
-            }
-            scatter_state(state, state_dtype, head_base, S);
-        }
-    }
-    free(S);
-    return 0;
+    return kdao_recurrent2(n_tokens, n_seqs, H, H, q, k, v, graw, 0, braw, 0, 0, A_log, dt_bias,
+                           scale, l2_eps, cu_seqlens, 1, state_indices, num_slots, state_dtype,
+                           state, 1, out64, out_bf16, ckpt_dtype, ckpt, ckpt64);
 }
 
 /*

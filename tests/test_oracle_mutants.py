@@ -31,16 +31,20 @@ MUTANTS = [
     ("softplus sign", "log1p(exp(-fabs(x)))", "log1p(exp(fabs(x)))"),
     ("gate sign", "double g = -a * softplus", "double g = a * softplus"),
     ("A_log not exponentiated", "double a = exp(A_log_h);", "double a = A_log_h;"),
-    ("dt_bias head offset", "gate_decay(gv, (double)A_log[h], dt_bias + h * KD, dec);\n                kda_token",
-     "gate_decay(gv, (double)A_log[h], dt_bias, dec);\n                kda_token"),
-    ("beta not squashed", "double beta = sigmoid(bf16_to_f64(braw[(size_t)t * H + h]));",
-     "double beta = bf16_to_f64(braw[(size_t)t * H + h]);"),
+    ("dt_bias head offset", "gate_decay(gv, (double)A_log[hv], dt_bias + hv * KD, dec);",
+     "gate_decay(gv, (double)A_log[hv], dt_bias, dec);"),
+    ("beta not squashed", "b = sigmoid(bin);", "b = bin;"),
+    ("q/k head not grouped", "const int64_t hk = hv / group;", "const int64_t hk = hv % H;"),
+    ("precomputed decay taken as the gate", "for (int j = 0; j < KD; ++j) dec[j] = exp(gv[j]);",
+     "for (int j = 0; j < KD; ++j) dec[j] = gv[j];"),
+    ("read-only pool written", "if (update_state) scatter_state(state, state_dtype, head_base, S);",
+     "scatter_state(state, state_dtype, head_base, S);"),
     ("l2 norm dropped", "double inv = 1.0 / sqrt(ss + eps);", "double inv = 1.0;"),
     ("null row output not zero", "if (out64) out64[oi] = 0.0;\n                        if (out_bf16)",
      "if (out64) out64[oi] = 1.0;\n                        if (out_bf16)"),
     ("state not carried across tokens",
-     "            for (int64_t t = t0; t < t1; ++t) {\n                size_t vec",
-     "            for (int64_t t = t0; t < t1; ++t) {\n                gather_state(state, state_dtype, head_base, S);\n                size_t vec"),
+     "            for (int64_t t = t0; t < t1; ++t) {\n                size_t vq",
+     "            for (int64_t t = t0; t < t1; ++t) {\n                gather_state(state, state_dtype, head_base, S);\n                size_t vq"),
     ("conv taps reversed", "weight[(grp * 4 + j) * HC + cc]", "weight[(grp * 4 + (3 - j)) * HC + cc]"),
     ("conv group ignored", "weight[(grp * 4 + j) * HC + cc]", "weight[j * HC + cc]"),
     ("conv cache not shifted", "cs[0 * C3 + c] = cs[1 * C3 + c];", "cs[0 * C3 + c] = cs[0 * C3 + c];"),
@@ -68,6 +72,11 @@ PINS = [
     pins.test_conv_output_feeds_recurrence_as_qkv,
     pins.test_gated_rmsnorm_invariants,
     pins.test_fused_null_rows,
+    pins.test_grouped_heads_equal_repeated_qk,
+    pins.test_precomputed_gate_is_log_decay_per_key_channel,
+    pins.test_precomputed_beta_is_used_as_is,
+    pins.test_read_only_pool,
+    pins.test_batched_form_equals_uniform_cu_seqlens,
 ]
 
 

@@ -435,3 +435,118 @@ def test_fused_null_rows():
     for s in range(6):
         assert np.array_equal(r["state"][s], st0[s]) == (s != 3)
         assert np.array_equal(r["conv_state"][s], cs0[s]) == (s != 3)
+
+
+# ---- grouped value heads, precomputed gate, read-only pool, batched form ----------------
+
+def _gqa_case(seed, n=3, H=2, group=3, slots=5, lengths=None):
+    """Inputs with HV = group * H value heads (q, k at H heads)."""
+    HV = H * group
+    c = synth.recurrent_case(seed, n_seqs=n, H=HV, num_slots=slots, indices="random",
+                             lengths=lengths)
+    T = c.q.shape[0]
+    q = _np(c.q)[:, :H].copy()
+    k = _np(c.k)[:, :H].copy()
+    return c, q, k, HV
+
+
+def test_grouped_heads_equal_repeated_qk():
+    """HV = 3H value heads reading q/k head hv // 3 equal an equal-head run on
+    q and k repeated three times along the head axis (exactly)."""
+    for lengths in (None, [2, 0, 3]):
+        c, q, k, HV = _gqa_case(30, lengths=lengths)
+        a = oracle.recurrent(q, k, c.v, c.g, c.beta, c.A_log, c.dt_bias, _np(c.state).astype(np.float64),
+                             c.state_indices, c.cu_seqlens, ckpt_dtype=oracle.F64)
+        qr, kr = np.repeat(q, 3, axis=1), np.repeat(k, 3, axis=1)
+        b = oracle.recurrent(qr, kr, c.v, c.g, c.beta, c.A_log, c.dt_bias, _np(c.state).astype(np.float64),
+                             c.state_indices, c.cu_seqlens, ckpt_dtype=oracle.F64)
+        for key in ("out64", "state", "ckpt"):
+            np.testing.assert_array_equal(a[key], b[key])
+        # and the grouping is hv // group, not hv % H: heads 0..2 share q/k head 0
+        c1 = oracle.recurrent(np.stack([q[:, 1], q[:, 0]], 1), np.stack([k[:, 1], k[:, 0]], 1), c.v,
+                              c.g, c.beta, c.A_log, c.dt_bias, _np(c.state).astype(np.float64),
+                              c.state_indices, c.cu_seqlens)
+        assert not np.array_equal(c1["out64"][:, :3], a["out64"][:, :3])
+        np.testing.assert_array_equal(c1["out64"][:, :3], oracle.recurrent(
+            np.repeat(q[:, 1:2], 2, 1), np.repeat(k[:, 1:2], 2, 1), c.v, c.g, c.beta, c.A_log,
+            c.dt_bias, _np(c.state).astype(np.float64), c.state_indices, c.cu_seqlens)["out64"][:, :3])
+
+
+def test_precomputed_gate_is_log_decay_per_key_channel():
+    """Precomputed mode: beta = 0 and a log-decay varying over k scale every
+    pool element [v][k] by exp(g_k) (library exp)."""
+    c = _case(seed=31, n=2, H=2, slots=3)
+    T, H = c.q.shape[0], c.H
+    gpre = np.tile(np.linspace(-4.0, 0.0, D, dtype=np.float32), (T, H, 1))
+    st = _np(c.state).astype(np.float64)
+    r = oracle.recurrent(c.q, c.k, c.v, gpre, np.zeros((T, H), np.float32), None, None, st,
+                         c.state_indices, gate="precomputed")
+    d = np.array([math.exp(float(x)) for x in gpre[0, 0]])
+    for i in range(T):
+        slot = int(c.state_indices[i])
+        np.testing.assert_allclose(r["state"][slot], st[slot] * d[None, None, :], rtol=1e-15, atol=0)
+
+
+def test_precomputed_beta_is_used_as_is():
+    """Precomputed mode: beta = 1 with unit decay stores v under k exactly;
+    zero state with beta = 0.25 gives S' = 0.25 k_hat v^T."""
+    c = _case(seed=32, n=3, H=2, slots=4)
+    T, H = c.q.shape[0], c.H
+    zeros = np.zeros((T, H, D), np.float32)
+    r = oracle.recurrent(c.q, c.k, c.v, zeros, np.ones((T, H), np.float32), None, None,
+                         _np(c.state).astype(np.float64), c.state_indices, gate="precomputed",
+                         l2_eps=0.0)
+    k = _np(c.k.float()).astype(np.float64)
+    v = _np(c.v.float()).astype(np.float64)
+    for i in range(T):
+        slot = int(c.state_indices[i])
+        for h in range(H):
+            kh = k[i, h] / np.linalg.norm(k[i, h])
+            np.testing.assert_allclose(r["state"][slot, h] @ kh, v[i, h], rtol=0, atol=1e-12)
+    r = oracle.recurrent(c.q, c.k, c.v, zeros, np.full((T, H), 0.25, np.float32), None, None,
+                         np.zeros((4, H, D, D)), c.state_indices, gate="precomputed")
+    for i in range(T):
+        slot = int(c.state_indices[i])
+        for h in range(H):
+            np.testing.assert_allclose(r["state"][slot, h], 0.25 * np.outer(v[i, h], _unit(k[i, h])),
+                                       rtol=1e-12, atol=1e-15)
+
+
+def test_precomputed_gate_matches_in_kernel_gate_values():
+    """Feeding the in-kernel gate's own values (computed here with library
+    exp/log1p, rounded to fp32) as precomputed inputs reproduces the
+    in-kernel run to fp32 input rounding."""
+    c = _case(seed=33, n=3, H=2, slots=4)
+    graw = oracle.bf16_to_f64(_np(c.g))
+    dtb = _np(c.dt_bias).astype(np.float64).reshape(c.H, D)
+    A = _np(c.A_log).astype(np.float64)
+    x = graw + dtb[None]
+    sp = np.maximum(x, 0) + np.log1p(np.exp(-np.abs(x)))
+    gpre = (-np.exp(A)[None, :, None] * sp).astype(np.float32)
+    bpre = (1.0 / (1.0 + np.exp(-oracle.bf16_to_f64(_np(c.beta))))).astype(np.float32)
+    st = _np(c.state).astype(np.float64)
+    a = oracle.recurrent(c.q, c.k, c.v, c.g, c.beta, c.A_log, c.dt_bias, st, c.state_indices)
+    b = oracle.recurrent(c.q, c.k, c.v, gpre, bpre, None, None, st, c.state_indices, gate="precomputed")
+    np.testing.assert_allclose(b["out64"], a["out64"], rtol=0, atol=1e-8)
+    np.testing.assert_allclose(b["state"], a["state"], rtol=0, atol=1e-7)
+
+
+def test_read_only_pool():
+    """update_state=False: the pool is bit-identical afterwards; outputs and
+    checkpoints equal those of the state-updating call."""
+    c = _case(seed=34, n=4, H=2, slots=6, indices="random", lengths=[3, 0, 2, 1], null_rows=1)
+    a = _run(c, ckpt_dtype=oracle.F32)
+    b = _run(c, ckpt_dtype=oracle.F32, update_state=False)
+    np.testing.assert_array_equal(b["state"], _np(c.state))
+    np.testing.assert_array_equal(b["out64"], a["out64"])
+    np.testing.assert_array_equal(b["ckpt"], a["ckpt"])
+    assert not np.array_equal(a["state"], _np(c.state))
+
+
+def test_batched_form_equals_uniform_cu_seqlens():
+    """tokens_per_seq = T without cu_seqlens equals cu_seqlens = [0, T, 2T, ...]."""
+    c = _case(seed=35, n=3, H=2, slots=4, indices="random", lengths=[4, 4, 4])
+    a = _run(c, ckpt_dtype=oracle.F32)
+    b = _run(c, cu_seqlens=None, tokens_per_seq=4, ckpt_dtype=oracle.F32)
+    for key in ("out64", "state", "ckpt"):
+        np.testing.assert_array_equal(a[key], b[key])
