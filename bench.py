@@ -158,6 +158,8 @@ def launch_plan(c, idx, pool, out_t, B, H):
     a.num_slots, a.slot_stride = pool.shape[0], pool.stride(0)
     a.state_indices = idx.data_ptr()
     a.out = out_t.data_ptr()
+    a.g_dtype = a.beta_dtype = _lib.DTYPE_BF16
+    a.tokens_per_seq = 1
     p = _lib.LaunchPlan()
     rc = _lib.load().kda_recurrent_plan(ctypes.byref(a), ctypes.byref(p))
     if rc != 0:

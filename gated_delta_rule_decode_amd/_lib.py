@@ -19,7 +19,8 @@ STATUS = {
     -8: "KDA_ERR_DEVICE", -9: "KDA_ERR_LAUNCH", -10: "KDA_ERR_ABI",
 }
 DTYPE_F32, DTYPE_BF16 = 0, 1
-GATE_SOFTPLUS, GATE_LOWER_BOUND = 0, 1
+GATE_SOFTPLUS, GATE_LOWER_BOUND, GATE_PRECOMPUTED = 0, 1, 2
+FLAG_NO_STATE_UPDATE = 1
 
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
@@ -44,7 +45,8 @@ class RecurrentArgs(ctypes.Structure):
         ("gate_mode", _I32), ("lower_bound", _F32),
         ("state", _P), ("state_dtype", _I32), ("ckpt_dtype", _I32), ("num_slots", _I64),
         ("slot_stride", _I64), ("state_indices", _P), ("cu_seqlens", _P), ("checkpoints", _P),
-        ("out", _P),
+        ("out", _P), ("g_dtype", _I32), ("beta_dtype", _I32), ("tokens_per_seq", _I32),
+        ("flags", _U32),
     ]
 
 

@@ -67,79 +67,112 @@ def _gate_mode(lower_bound):
     return _lib.GATE_LOWER_BOUND, float(lower_bound)
 
 
-def _token_view(t, name, T, H, width, cu):
-    """(row stride, tensor) of a per-token [.., H, width] input whose inner
-    [H, width] block is contiguous; accepts [T,H,w], [T,1,H,w] (T=1) or
-    [1,T,H,w] (packed)."""
-    if width == 1:
-        _need(t.shape[-1] == H and t.stride(-1) == 1, f"{name} must end in a contiguous [H] dim")
+def _dtype_code(t, name):
+    if t.dtype == torch.bfloat16:
+        return _lib.DTYPE_BF16
+    if t.dtype == torch.float32:
+        return _lib.DTYPE_F32
+    raise ValueError(f"{name} must be bfloat16 or float32, got {t.dtype}")
+
+
+def _tokens(t, name, heads, width, ragged):
+    """(n_tokens, tokens_per_seq, token stride) of a per-token input whose
+    inner [heads, width] block (or [heads] when width is None) is contiguous.
+    Accepted: [T, ...]; [B, T, ...] (T tokens per sequence, T=1 is plain
+    decode; the [B, T] dims must collapse to one stride); [1, T, ...] with
+    cu_seqlens."""
+    inner = 1 if width is None else 2
+    if width is None:
+        _need(t.shape[-1] == heads and t.stride(-1) == 1, f"{name} must end in a contiguous [{heads}] dim")
     else:
-        _need(t.shape[-1] == width and t.shape[-2] == H and t.stride(-1) == 1 and t.stride(-2) == width,
-              f"{name} must end in a contiguous [H, {width}] block")
-    lead = t.shape[:-1] if width == 1 else t.shape[:-2]
+        _need(t.shape[-1] == width and t.shape[-2] == heads and t.stride(-1) == 1
+              and t.stride(-2) == width, f"{name} must end in a contiguous [{heads}, {width}] block")
+    lead = tuple(t.shape[:-inner])
     strides = t.stride()[:len(lead)]
     if len(lead) == 1:
-        _need(lead[0] == T, f"{name} has {lead[0]} tokens, expected {T}")
-        return strides[0]
+        return lead[0], 1, strides[0]
     _need(len(lead) == 2, f"{name} has an unsupported rank")
-    if cu is None:
-        _need(lead[0] == T and lead[1] == 1, f"{name} must be [B, 1, ...] for T=1")
-        return strides[0]
-    _need(lead[0] == 1 and lead[1] == T, f"{name} must be [1, T, ...] for packed tokens")
-    return strides[1]
+    B, T = lead
+    if ragged:
+        _need(B == 1, f"{name} must be [1, T, ...] with cu_seqlens")
+        return T, 1, strides[1]
+    if T == 1:
+        return B, 1, strides[0]
+    _need(strides[0] == T * strides[1], f"{name}: the [B, T] dims must collapse to one token stride")
+    return B * T, T, strides[1]
 
 
-def recurrent_kda(q, k, v, g, beta, A_log, dt_bias, *, initial_state, state_indices,
+def recurrent_kda(q, k, v, g, beta, A_log=None, dt_bias=None, *, initial_state, state_indices,
                   cu_seqlens=None, n_tokens=None, scale=None, output=None, intermediate_states=None,
-                  lower_bound=None, use_qk_l2norm_in_kernel=True, l2_eps=1e-6):
+                  lower_bound=None, use_qk_l2norm_in_kernel=True, use_gate_in_kernel=None,
+                  disable_state_update=False, l2_eps=1e-6):
     """Recurrent KDA decode ("flashinfer.kda_decode" function table).
 
-    T=1: q, k, v, g are bf16 [B, 1, H, 128] (or [B, H, 128]); beta logits
-    [B, 1, H]; one sequence per row.  Packed T>=2: q, k, v, g are
-    [1, T, H, 128], beta [1, T, H] and ``cu_seqlens`` int32 [N+1] gives the
-    ragged sequences (empty ones allowed); ``n_tokens`` defaults to T.
-    ``g`` is the raw gate, A_log fp32 [H], dt_bias fp32 [H*128].  The pool
-    ``initial_state`` [num_slots, H, 128, 128] (fp32 or bf16) is updated in
-    place at ``state_indices`` (int32, negative = null row).
-    ``intermediate_states`` (optional, [T, H, 128, 128], pool dtype) receives
-    the state after every token.  Returns the bf16 output, shaped like q.
+    Forms: T=1 (q [B, 1, H, 128] or [B, H, 128]); batched T tokens per
+    sequence (q [B, T, H, 128]); packed ragged (q [1, T, H, 128] with
+    ``cu_seqlens`` int32 [N+1], empty sequences allowed; ``n_tokens`` defaults
+    to T).  q, k have H heads; v, g [.., HV, 128] and beta [.., HV] have HV
+    value heads, HV a multiple of H (value head hv reads q/k head
+    hv // (HV // H)).  With ``use_gate_in_kernel`` (the default when A_log is
+    given) g is the raw gate and beta the logits, A_log fp32 [HV] and
+    dt_bias fp32 [HV*128]; otherwise g is the log-decay and beta is beta
+    itself (bf16 or fp32 each).  The pool ``initial_state`` [num_slots, HV,
+    128, 128] (fp32 or bf16) is updated in place at ``state_indices`` (int32,
+    negative = null row) unless ``disable_state_update``.
+    ``intermediate_states`` (optional, [T, HV, 128, 128], pool dtype) receives
+    the state after every token.  Returns the bf16 output [.., HV, 128].
     """
     _need(use_qk_l2norm_in_kernel, "only the in-kernel q/k L2 normalisation is implemented")
-    H = A_log.numel()
+    if use_gate_in_kernel is None:
+        use_gate_in_kernel = A_log is not None
+    H = q.shape[-2]
+    HV = v.shape[-2]
     state = initial_state
-    _check_pool(state, H)
+    _check_pool(state, HV)
     N = state_indices.numel()
-    if cu_seqlens is None:
-        T = N
-    else:
+    _check_indices(state_indices, N)
+    ragged = cu_seqlens is not None
+    if ragged:
         _need(cu_seqlens.dtype == torch.int32 and cu_seqlens.is_contiguous() and cu_seqlens.numel() == N + 1,
               "cu_seqlens must be a contiguous int32 tensor with N+1 elements")
-        T = int(n_tokens) if n_tokens is not None else q.shape[-3]
-    _check_indices(state_indices, N)
-    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta)):
+    for name, t in (("q", q), ("k", k), ("v", v)):
         _need(t.dtype == torch.bfloat16 and t.is_cuda, f"{name} must be a bf16 device tensor")
-    strides = [_token_view(t, n, T, H, D, cu_seqlens) for n, t in (("q", q), ("k", k), ("v", v), ("g", g))]
-    sb = _token_view(beta, "beta", T, H, 1, cu_seqlens)
-    _need(A_log.dtype == torch.float32 and A_log.is_contiguous(), "A_log must be contiguous fp32 [H]")
-    _need(dt_bias.dtype == torch.float32 and dt_bias.is_contiguous() and dt_bias.numel() == H * D,
-          "dt_bias must be contiguous fp32 [H*128]")
-    out_shape = q.shape
+    _need(g.is_cuda and beta.is_cuda, "g and beta must be device tensors")
+    T, tps, sq = _tokens(q, "q", H, D, ragged)
+    views = [_tokens(t, n, hh, D, ragged) for n, t, hh in (("k", k, H), ("v", v, HV), ("g", g, HV))]
+    views.append(_tokens(beta, "beta", HV, None, ragged))
+    for (Tn, tpn, _), n in zip(views, ("k", "v", "g", "beta")):
+        _need(Tn == T and tpn == tps, f"{n} does not have the token layout of q")
+    if ragged and n_tokens is not None:
+        T = int(n_tokens)
+    if use_gate_in_kernel:
+        _need(A_log is not None and dt_bias is not None, "the in-kernel gate needs A_log and dt_bias")
+        _need(g.dtype == torch.bfloat16 and beta.dtype == torch.bfloat16,
+              "with the in-kernel gate, g and beta are bf16")
+        _need(A_log.dtype == torch.float32 and A_log.is_contiguous() and A_log.numel() == HV,
+              "A_log must be contiguous fp32 [HV]")
+        _need(dt_bias.dtype == torch.float32 and dt_bias.is_contiguous() and dt_bias.numel() == HV * D,
+              "dt_bias must be contiguous fp32 [HV*128]")
+        gm, lb = _gate_mode(lower_bound)
+    else:
+        _need(lower_bound is None, "lower_bound applies to the in-kernel gate only")
+        gm, lb = _lib.GATE_PRECOMPUTED, 0.0
+    out_shape = tuple(v.shape)
     if output is None:
         output = torch.empty(out_shape, dtype=torch.bfloat16, device=q.device)
     else:
-        _need(output.dtype == torch.bfloat16 and output.is_contiguous() and output.numel() == T * H * D,
-              "output must be a contiguous bf16 tensor with T*H*128 elements")
+        _need(output.dtype == torch.bfloat16 and output.is_contiguous() and output.numel() == T * HV * D,
+              "output must be a contiguous bf16 tensor with T*HV*128 elements")
     ck = intermediate_states
     if ck is not None:
-        _need(ck.dtype == state.dtype and ck.is_contiguous() and ck.numel() == T * H * D * D,
-              "intermediate_states must be contiguous [T, H, 128, 128] in the pool dtype")
-    gm, lb = _gate_mode(lower_bound)
+        _need(ck.dtype == state.dtype and ck.is_contiguous() and ck.numel() == T * HV * D * D,
+              "intermediate_states must be contiguous [T, HV, 128, 128] in the pool dtype")
     a = _lib.RecurrentArgs()
     a.struct_size = ctypes.sizeof(_lib.RecurrentArgs)
-    a.n_seqs, a.n_tokens, a.H, a.HV, a.K, a.V = N, T, H, H, D, D
+    a.n_seqs, a.n_tokens, a.H, a.HV, a.K, a.V = N, T, H, HV, D, D
     a.q, a.k, a.v, a.g, a.beta = _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta)
-    a.q_stride, a.k_stride, a.v_stride, a.g_stride = strides
-    a.beta_stride = sb
+    a.q_stride = sq
+    a.k_stride, a.v_stride, a.g_stride, a.beta_stride = (vw[2] for vw in views)
     a.A_log, a.dt_bias = _ptr(A_log), _ptr(dt_bias)
     a.scale = _SCALE if scale is None else float(scale)
     a.l2_eps = float(l2_eps)
@@ -150,6 +183,9 @@ def recurrent_kda(q, k, v, g, beta, A_log, dt_bias, *, initial_state, state_indi
     a.cu_seqlens = _ptr(cu_seqlens)
     a.checkpoints = _ptr(ck)
     a.out = _ptr(output)
+    a.g_dtype, a.beta_dtype = _dtype_code(g, "g"), _dtype_code(beta, "beta")
+    a.tokens_per_seq = tps
+    a.flags = _lib.FLAG_NO_STATE_UPDATE if disable_state_update else 0
     lib = _lib.load()
     with torch.cuda.device(q.device):
         _lib.check(lib.kda_recurrent(ctypes.byref(a), _stream(q.device)))

@@ -148,6 +148,8 @@ void fill_plan(kda_launch_plan *plan, const Launch &l, int64_t items)
 
 // ------------------------------------------------------------ recurrent ----
 
+int dtype_ok(int32_t d) { return d == KDA_DTYPE_F32 || d == KDA_DTYPE_BF16; }
+
 int prepare_recurrent(const kda_recurrent_args *a, RecParams *p, Launch *l)
 {
     if (!a) return fail(KDA_ERR_NULLPTR, "args is NULL");
@@ -155,59 +157,75 @@ int prepare_recurrent(const kda_recurrent_args *a, RecParams *p, Launch *l)
         return fail(KDA_ERR_ABI, "struct_size %u != %zu", a->struct_size, sizeof(kda_recurrent_args));
     if (a->K != KD || a->V != KD)
         return fail(KDA_ERR_UNSUPPORTED, "K=%d V=%d: only K=V=128", a->K, a->V);
-    if (a->H < 1) return fail(KDA_ERR_SHAPE, "H=%d must be >= 1", a->H);
-    if (a->HV != a->H) return fail(KDA_ERR_UNSUPPORTED, "HV=%d != H=%d (grouped heads)", a->HV, a->H);
+    if (a->H < 1 || a->HV < 1) return fail(KDA_ERR_SHAPE, "H=%d HV=%d must be >= 1", a->H, a->HV);
+    if (a->HV % a->H != 0)
+        return fail(KDA_ERR_UNSUPPORTED, "HV=%d is not a multiple of H=%d", a->HV, a->H);
     if (a->n_seqs < 1) return fail(KDA_ERR_SHAPE, "n_seqs=%d must be >= 1", a->n_seqs);
-    const bool varlen = a->cu_seqlens != nullptr;
-    if (!varlen && a->n_tokens != a->n_seqs)
-        return fail(KDA_ERR_SHAPE, "T=1 call: n_tokens=%d != n_seqs=%d", a->n_tokens, a->n_seqs);
+    if (a->flags & ~KDA_FLAG_NO_STATE_UPDATE) return fail(KDA_ERR_UNSUPPORTED, "unknown flags 0x%x", a->flags);
+    if (a->tokens_per_seq < 0) return fail(KDA_ERR_SHAPE, "tokens_per_seq=%d < 0", a->tokens_per_seq);
+    const bool ragged = a->cu_seqlens != nullptr;
+    const int64_t tps = a->tokens_per_seq > 1 ? a->tokens_per_seq : 1;
+    if (!ragged && (int64_t)a->n_tokens != (int64_t)a->n_seqs * tps)
+        return fail(KDA_ERR_SHAPE, "n_tokens=%d != n_seqs=%d * tokens_per_seq=%lld", a->n_tokens, a->n_seqs,
+                    (long long)tps);
     if (a->n_tokens < 0) return fail(KDA_ERR_SHAPE, "n_tokens=%d < 0", a->n_tokens);
-    int rc = check_gate(a->gate_mode);
+    const bool precomputed = a->gate_mode == KDA_GATE_PRECOMPUTED;
+    int rc = precomputed ? KDA_OK : check_gate(a->gate_mode);
     if (rc) return rc;
-    if (!a->A_log || !a->dt_bias || !a->state || !a->state_indices)
+    if (!dtype_ok(a->g_dtype) || !dtype_ok(a->beta_dtype))
+        return fail(KDA_ERR_DTYPE, "g_dtype %d / beta_dtype %d must be F32 or BF16", a->g_dtype, a->beta_dtype);
+    if (!a->state || !a->state_indices || (!precomputed && (!a->A_log || !a->dt_bias)))
         return fail(KDA_ERR_NULLPTR, "a required pointer is NULL");
     if (a->n_tokens > 0 && (!a->q || !a->k || !a->v || !a->g || !a->beta || !a->out))
         return fail(KDA_ERR_NULLPTR, "a required per-token pointer is NULL");
-    const int64_t HC = (int64_t)a->H * KD;
-    if (a->q_stride < HC || a->k_stride < HC || a->v_stride < HC || a->g_stride < HC)
-        return fail(KDA_ERR_STRIDE, "q/k/v/g token strides must be >= H*128");
-    if (a->beta_stride < a->H) return fail(KDA_ERR_STRIDE, "beta_stride must be >= H");
-    if (!aligned2(a->q) || !aligned2(a->k) || !aligned2(a->v) || !aligned2(a->g) || !aligned2(a->beta) ||
-        !aligned4(a->A_log) || !aligned4(a->dt_bias) || !aligned4(a->state_indices) ||
-        (varlen && !aligned4(a->cu_seqlens)))
+    const int64_t HQ = (int64_t)a->H * KD;
+    const int64_t HVC = (int64_t)a->HV * KD;
+    if (a->q_stride < HQ || a->k_stride < HQ)
+        return fail(KDA_ERR_STRIDE, "q/k token strides must be >= H*128");
+    if (a->v_stride < HVC || a->g_stride < HVC)
+        return fail(KDA_ERR_STRIDE, "v/g token strides must be >= HV*128");
+    if (a->beta_stride < a->HV) return fail(KDA_ERR_STRIDE, "beta_stride must be >= HV");
+    const int g_es = a->g_dtype == KDA_DTYPE_F32 ? 4 : 2;
+    const int b_es = a->beta_dtype == KDA_DTYPE_F32 ? 4 : 2;
+    auto aligned_to = [](const void *ptr, int n) { return (reinterpret_cast<uintptr_t>(ptr) & (uintptr_t)(n - 1)) == 0; };
+    if (!aligned2(a->q) || !aligned2(a->k) || !aligned2(a->v) || !aligned_to(a->g, g_es) ||
+        !aligned_to(a->beta, b_es) || !aligned4(a->A_log) || !aligned4(a->dt_bias) ||
+        !aligned4(a->state_indices) || (ragged && !aligned4(a->cu_seqlens)))
         return fail(KDA_ERR_ALIGN, "inputs must be aligned to their element size");
     if (!aligned16(a->out)) return fail(KDA_ERR_ALIGN, "out must be 16-byte aligned");
     if (!(a->l2_eps >= 0.0f) || !isfinite(a->scale))
         return fail(KDA_ERR_SHAPE, "l2_eps must be >= 0 and scale finite");
-    rc = check_pool(a->state, a->state_dtype, a->num_slots, a->slot_stride, a->H);
+    rc = check_pool(a->state, a->state_dtype, a->num_slots, a->slot_stride, a->HV);
     if (rc) return rc;
     if (a->checkpoints) {
         if (a->ckpt_dtype != a->state_dtype)
             return fail(KDA_ERR_UNSUPPORTED, "checkpoints must use the state dtype");
         if (!aligned16(a->checkpoints)) return fail(KDA_ERR_ALIGN, "checkpoints must be 16-byte aligned");
     }
+    const bool update = !(a->flags & KDA_FLAG_NO_STATE_UPDATE);
     const int64_t T = a->n_tokens;
     const int es = elem_size(a->state_dtype);
-    Range w[3] = {span(a->out, (uint64_t)T * HC * 2, "out"),
-                  span(a->state, pool_bytes(a->state_dtype, a->num_slots, a->slot_stride, a->H), "state"),
-                  span(a->checkpoints, a->checkpoints ? (uint64_t)T * a->H * HEAD_ELEMS * es : 0,
-                       "checkpoints")};
-    Range r[9] = {span(a->q, rows_extent(T, a->q_stride, HC) * 2, "q"),
-                  span(a->k, rows_extent(T, a->k_stride, HC) * 2, "k"),
-                  span(a->v, rows_extent(T, a->v_stride, HC) * 2, "v"),
-                  span(a->g, rows_extent(T, a->g_stride, HC) * 2, "g"),
-                  span(a->beta, rows_extent(T, a->beta_stride, a->H) * 2, "beta"),
-                  span(a->A_log, (uint64_t)a->H * 4, "A_log"),
-                  span(a->dt_bias, (uint64_t)HC * 4, "dt_bias"),
-                  span(a->state_indices, (uint64_t)a->n_seqs * 4, "state_indices"),
-                  span(a->cu_seqlens, varlen ? (uint64_t)(a->n_seqs + 1) * 4 : 0, "cu_seqlens")};
-    rc = check_alias(w, 3, r, 9);
+    const Range state_r = span(a->state, pool_bytes(a->state_dtype, a->num_slots, a->slot_stride, a->HV), "state");
+    Range w[3] = {span(a->out, (uint64_t)T * HVC * 2, "out"),
+                  span(a->checkpoints, a->checkpoints ? (uint64_t)T * a->HV * HEAD_ELEMS * es : 0, "checkpoints"),
+                  update ? state_r : Range{0, 0, ""}};
+    Range r[10] = {span(a->q, rows_extent(T, a->q_stride, HQ) * 2, "q"),
+                   span(a->k, rows_extent(T, a->k_stride, HQ) * 2, "k"),
+                   span(a->v, rows_extent(T, a->v_stride, HVC) * 2, "v"),
+                   span(a->g, rows_extent(T, a->g_stride, HVC) * g_es, "g"),
+                   span(a->beta, rows_extent(T, a->beta_stride, a->HV) * b_es, "beta"),
+                   span(a->A_log, a->A_log ? (uint64_t)a->HV * 4 : 0, "A_log"),
+                   span(a->dt_bias, a->dt_bias ? (uint64_t)HVC * 4 : 0, "dt_bias"),
+                   span(a->state_indices, (uint64_t)a->n_seqs * 4, "state_indices"),
+                   span(a->cu_seqlens, ragged ? (uint64_t)(a->n_seqs + 1) * 4 : 0, "cu_seqlens"),
+                   update ? Range{0, 0, ""} : state_r};
+    rc = check_alias(w, 3, r, 10);
     if (rc) return rc;
 
-    const int64_t items = (int64_t)a->n_seqs * a->H;
+    const int64_t items = (int64_t)a->n_seqs * a->HV;
     const int vsplit = choose_vsplit(items, a->state_dtype == KDA_DTYPE_BF16);
     if (items * vsplit > 0x7ffffff0LL) return fail(KDA_ERR_SHAPE, "too many work items");
-    l->family = varlen ? KERNEL_RECURRENT_VARLEN : KERNEL_RECURRENT_T1;
+    l->family = (ragged || tps > 1) ? KERNEL_RECURRENT_VARLEN : KERNEL_RECURRENT_T1;
     l->vsplit = vsplit;
     l->rows_per_block = KD / vsplit;
     l->grid = (int32_t)((items * vsplit + 7) & ~7LL);  // padded to whole XCD rounds
@@ -217,8 +235,8 @@ int prepare_recurrent(const kda_recurrent_args *a, RecParams *p, Launch *l)
     p->q = static_cast<const uint16_t *>(a->q);
     p->k = static_cast<const uint16_t *>(a->k);
     p->v = static_cast<const uint16_t *>(a->v);
-    p->g = static_cast<const uint16_t *>(a->g);
-    p->beta = static_cast<const uint16_t *>(a->beta);
+    p->g = a->g;
+    p->beta = a->beta;
     p->q_stride = a->q_stride;
     p->k_stride = a->k_stride;
     p->v_stride = a->v_stride;
@@ -238,6 +256,13 @@ int prepare_recurrent(const kda_recurrent_args *a, RecParams *p, Launch *l)
     p->n_seqs = a->n_seqs;
     p->n_tokens = a->n_tokens;
     p->H = a->H;
+    p->HV = a->HV;
+    p->group = a->HV / a->H;
+    p->tps = (int32_t)tps;
+    p->g_f32 = a->g_dtype == KDA_DTYPE_F32;
+    p->beta_f32 = a->beta_dtype == KDA_DTYPE_F32;
+    p->precomputed = precomputed;
+    p->update_state = update;
     p->vsplit = vsplit;
     p->n_work = (int32_t)(items * vsplit);
     return ok();
@@ -257,6 +282,9 @@ int packed_to_recurrent(const kda_packed_args *a, kda_recurrent_args *r)
     if (!a->mixed_qkv) return fail(KDA_ERR_NULLPTR, "mixed_qkv is NULL");
     memset(r, 0, sizeof *r);
     r->struct_size = sizeof *r;
+    r->g_dtype = KDA_DTYPE_BF16;
+    r->beta_dtype = KDA_DTYPE_BF16;
+    r->tokens_per_seq = 1;
     r->n_seqs = a->B;
     r->n_tokens = a->B;
     r->H = r->HV = a->H;
@@ -393,7 +421,7 @@ KDA_API int kda_recurrent_plan(const kda_recurrent_args *args, kda_launch_plan *
     Launch l;
     int rc = prepare_recurrent(args, &p, &l);
     if (rc) return rc;
-    fill_plan(plan, l, (int64_t)args->n_seqs * args->H);
+    fill_plan(plan, l, (int64_t)args->n_seqs * args->HV);
     return KDA_OK;
 }
 

@@ -13,22 +13,30 @@ enum KernelFamily : int32_t {
     KERNEL_FUSED = 3,          // conv + SiLU -> KDA -> gated RMSNorm
 };
 
-// Recurrence over (sequence, head, value slice) work items; serves
-// recurrent_kda (T=1 and ragged T>=0) and packed_kda_decode.
+// Recurrence over (sequence, value head, value slice) work items; serves
+// recurrent_kda (T=1, uniform batches, ragged T>=0, grouped value heads,
+// in-kernel or precomputed gate, state-updating or read-only) and
+// packed_kda_decode.
 struct RecParams {
-    const uint16_t *q, *k, *v, *g, *beta;  // bf16
+    const uint16_t *q, *k, *v;   // bf16
+    const void *g, *beta;        // bf16 or fp32 (g_f32, beta_f32)
     int64_t q_stride, k_stride, v_stride, g_stride, beta_stride;  // per token, elements
-    const float *A_log, *dt_bias;
+    const float *A_log, *dt_bias;  // in-kernel gate only
     float scale, l2_eps;
-    void *state;                 // fp32 or bf16 pool, [slot][h][v][k]
+    void *state;                 // fp32 or bf16 pool, [slot][hv][v][k]
     int64_t num_slots, slot_stride;
     const int32_t *state_indices;
-    const int32_t *cu_seqlens;   // nullptr: token i belongs to sequence i
-    void *ckpt;                  // nullptr or [n_tokens][H][128][128], state dtype
-    uint16_t *out;               // bf16 [n_tokens][H][128]
-    int32_t n_seqs, n_tokens, H;
-    int32_t vsplit;              // workgroups per (sequence, head)
-    int32_t n_work;              // n_seqs * H * vsplit (grid is padded to a multiple of 8)
+    const int32_t *cu_seqlens;   // nullptr: sequence i owns tokens [i*tps, (i+1)*tps)
+    void *ckpt;                  // nullptr or [n_tokens][HV][128][128], state dtype
+    uint16_t *out;               // bf16 [n_tokens][HV][128]
+    int32_t n_seqs, n_tokens, H, HV;
+    int32_t group;               // HV / H: value heads per q/k head
+    int32_t tps;                 // tokens per sequence without cu_seqlens (>= 1)
+    int32_t g_f32, beta_f32;     // input dtypes of g and beta
+    int32_t precomputed;         // 1: g is the log-decay and beta is beta itself
+    int32_t update_state;        // 0: the pool is read only
+    int32_t vsplit;              // workgroups per (sequence, value head)
+    int32_t n_work;              // n_seqs * HV * vsplit (grid is padded to a multiple of 8)
 };
 
 struct FusedParams {

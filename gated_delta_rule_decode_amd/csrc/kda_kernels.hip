@@ -303,12 +303,13 @@ __device__ __forceinline__ float row_update(float s[8], const TokenOps &t, float
 // not wait on them before the state loads are issued); threads 0..127 then
 // stage q, k and the decay, threads 128..255 stage v.
 struct StageIn {
-    uint32_t q, k, v, g;  // bf16 bits
+    uint32_t q, k, v;  // bf16 bits
+    uint32_t g;        // bf16 or fp32 bits
     float dt;
 };
 
 __device__ __forceinline__ StageIn load_stage(int tid, const uint16_t *q, const uint16_t *k,
-                                              const uint16_t *v, const uint16_t *g,
+                                              const uint16_t *v, const void *g, bool g_f32,
                                               const float *dt_bias_h)
 {
     const int c = tid & (KD - 1);
@@ -316,24 +317,32 @@ __device__ __forceinline__ StageIn load_stage(int tid, const uint16_t *q, const 
     s.q = q[c];
     s.k = k[c];
     s.v = v[c];
-    s.g = g[c];
-    s.dt = dt_bias_h[c];
+    s.g = g_f32 ? static_cast<const uint32_t *>(g)[c] : static_cast<const uint16_t *>(g)[c];
+    s.dt = dt_bias_h ? dt_bias_h[c] : 0.f;
     return s;
+}
+
+__device__ __forceinline__ float input_value(uint32_t bits, bool is_f32)
+{
+    return is_f32 ? __uint_as_float(bits) : bf16_bits_to_f32(bits);
 }
 
 // Gate transform once per channel, decay = exp(-exp(A_log) * softplus(g +
 // dt_bias), by threads 0..127; threads 128..255 stage v and reduce the three
 // norm sums (|q|^2, |k|^2, q.k) over their wave, writing one partial per
 // wave to norms[4 * (wave - 2) + {0, 1, 2}].
-__device__ __forceinline__ void write_stage(int tid, const StageIn &s, float a_h, float *sq, float *sk,
-                                            float *sd, float *sv, float *norms)
+// With a precomputed gate, g already is the log-decay: decay = exp(g).
+__device__ __forceinline__ void write_stage(int tid, const StageIn &s, float a_h, bool g_f32,
+                                            bool precomputed, float *sq, float *sk, float *sd,
+                                            float *sv, float *norms)
 {
     const float q = bf16_bits_to_f32(s.q);
     const float k = bf16_bits_to_f32(s.k);
     if (tid < KD) {
         sq[tid] = q;
         sk[tid] = k;
-        sd[tid] = __expf(-a_h * softplus_f(bf16_bits_to_f32(s.g) + s.dt));
+        const float g = input_value(s.g, g_f32);
+        sd[tid] = precomputed ? __expf(g) : __expf(-a_h * softplus_f(g + s.dt));
     } else {
         sv[tid - KD] = bf16_bits_to_f32(s.v);
         float pq = q * q, pk = k * k, pqk = q * k;
@@ -372,14 +381,20 @@ __global__ void __launch_bounds__(256) kda_recurrent_kernel(const RecParams p)
     if (work >= p.n_work) return;
     const int vs = work % p.vsplit;
     const int item = work / p.vsplit;
-    const int seq = item / p.H;
-    const int h = item - seq * p.H;
+    const int seq = item / p.HV;
+    const int hv = item - seq * p.HV;  // value head: state, v, gate, beta, output
+    const int hq = hv / p.group;       // q/k head read by this value head
     const int r_base = vs * VT + wave * (4 * G) + qd * G;  // this lane's first value row
 
     int t0, t1;
     if constexpr (VARLEN) {
-        t0 = max(p.cu_seqlens[seq], 0);
-        t1 = min(p.cu_seqlens[seq + 1], p.n_tokens);
+        if (p.cu_seqlens) {
+            t0 = max(p.cu_seqlens[seq], 0);
+            t1 = min(p.cu_seqlens[seq + 1], p.n_tokens);
+        } else {
+            t0 = seq * p.tps;
+            t1 = min(t0 + p.tps, p.n_tokens);
+        }
     } else {
         t0 = seq;
         t1 = seq + 1;
@@ -388,21 +403,34 @@ __global__ void __launch_bounds__(256) kda_recurrent_kernel(const RecParams p)
     if (idx < 0 || (int64_t)idx >= p.num_slots) {
         if (m == 0)
             for (int t = t0; t < t1; ++t)
-                store_zero_bf16<G>(p.out + ((int64_t)t * p.H + h) * KD + r_base);
+                store_zero_bf16<G>(p.out + ((int64_t)t * p.HV + hv) * KD + r_base);
         return;
     }
     if (t1 <= t0) return;
 
     const size_t es = BF16 ? 2 : 4;
-    char *head = reinterpret_cast<char *>(p.state) + ((int64_t)idx * p.slot_stride + (int64_t)h * (KD * KD)) * es;
-    const float *dtb = p.dt_bias + (int64_t)h * KD;
-    const int64_t hk = (int64_t)h * KD;
+    char *head = reinterpret_cast<char *>(p.state) + ((int64_t)idx * p.slot_stride + (int64_t)hv * (KD * KD)) * es;
+    const bool precomputed = p.precomputed != 0;
+    const bool g_f32 = p.g_f32 != 0;
+    const bool beta_f32 = p.beta_f32 != 0;
+    const float *dtb = precomputed ? nullptr : p.dt_bias + (int64_t)hv * KD;
+    const int64_t oq = (int64_t)hq * KD;
+    const int64_t ov = (int64_t)hv * KD;
+    const char *gbase = static_cast<const char *>(p.g);
+    const char *bbase = static_cast<const char *>(p.beta);
+    const int g_es = g_f32 ? 4 : 2;
+    const int b_es = beta_f32 ? 4 : 2;
+    auto g_at = [&](int64_t t) { return gbase + (t * p.g_stride + ov) * g_es; };
+    auto beta_at = [&](int64_t t) -> uint32_t {
+        const char *b = bbase + (t * p.beta_stride + hv) * b_es;
+        return beta_f32 ? *reinterpret_cast<const uint32_t *>(b) : *reinterpret_cast<const uint16_t *>(b);
+    };
 
     // Token inputs first: waiting for them later must not wait for the state.
-    StageIn in = load_stage(tid, p.q + (int64_t)t0 * p.q_stride + hk, p.k + (int64_t)t0 * p.k_stride + hk,
-                            p.v + (int64_t)t0 * p.v_stride + hk, p.g + (int64_t)t0 * p.g_stride + hk, dtb);
-    uint32_t braw = p.beta[(int64_t)t0 * p.beta_stride + h];
-    const float a_h = __expf(p.A_log[h]);
+    StageIn in = load_stage(tid, p.q + (int64_t)t0 * p.q_stride + oq, p.k + (int64_t)t0 * p.k_stride + oq,
+                            p.v + (int64_t)t0 * p.v_stride + ov, g_at(t0), g_f32, dtb);
+    uint32_t braw = beta_at(t0);
+    const float a_h = precomputed ? 0.f : __expf(p.A_log[hv]);
     __builtin_amdgcn_sched_barrier(0);
 
     // Then every state load of this lane.
@@ -415,10 +443,17 @@ __global__ void __launch_bounds__(256) kda_recurrent_kernel(const RecParams p)
     }
     __builtin_amdgcn_sched_barrier(0);
 
+    // beta: sigmoid of the logits, or the precomputed value itself
+    auto beta_of = [&](uint32_t bits) {
+        const float b = input_value(bits, beta_f32);
+        return precomputed ? b : sigmoid_f(b);
+    };
+    const bool update = p.update_state != 0;
+
     if constexpr (!VARLEN) {
         // T=1: the gate transform and the norms overlap the state fetch.
-        write_stage(tid, in, a_h, s_q[0], s_k[0], s_d[0], s_v[0], s_norm[0]);
-        const float beta = sigmoid_f(bf16_bits_to_f32(braw));
+        write_stage(tid, in, a_h, g_f32, precomputed, s_q[0], s_k[0], s_d[0], s_v[0], s_norm[0]);
+        const float beta = beta_of(braw);
         __syncthreads();
         TokenOps ops;
         read_token_ops<BF16>(ops, s_q[0], s_k[0], s_d[0], s_norm[0], m, p.scale, p.l2_eps, beta);
@@ -428,27 +463,28 @@ __global__ void __launch_bounds__(256) kda_recurrent_kernel(const RecParams p)
             float st[8];
             IO::unpack(raw[gi], st);
             o[gi] = row_update(st, ops, s_v[0][r_base + gi]);
-            IO::store(head, off[gi], IO::pack(st));
+            if (update) IO::store(head, off[gi], IO::pack(st));
         }
-        if (m == 0) store_out_bf16<G>(p.out + ((int64_t)t0 * p.H + h) * KD + r_base, o);
+        if (m == 0) store_out_bf16<G>(p.out + ((int64_t)t0 * p.HV + hv) * KD + r_base, o);
     } else {
-        // Ragged token loop: the state stays in registers across the tokens
-        // of the sequence; the next token's inputs are fetched while the
-        // current one is computed; after each token the checkpoint (if
-        // requested) and the output are written; the pool slot is written
-        // once at the end.
+        // Token loop: the state stays in registers across the tokens of the
+        // sequence; the next token's inputs are fetched while the current one
+        // is computed; after each token the checkpoint (if requested) and the
+        // output are written; the pool slot is written once at the end
+        // (unless the pool is read only).
         float st[G][8];
 #pragma unroll
         for (int gi = 0; gi < G; ++gi) IO::unpack(raw[gi], st[gi]);
         for (int t = t0; t < t1; ++t) {
             const int buf = (t - t0) & 1;
-            write_stage(tid, in, a_h, s_q[buf], s_k[buf], s_d[buf], s_v[buf], s_norm[buf]);
-            const float beta = sigmoid_f(bf16_bits_to_f32(braw));
+            write_stage(tid, in, a_h, g_f32, precomputed, s_q[buf], s_k[buf], s_d[buf], s_v[buf],
+                        s_norm[buf]);
+            const float beta = beta_of(braw);
             if (t + 1 < t1) {
                 const int64_t n = t + 1;
-                in = load_stage(tid, p.q + n * p.q_stride + hk, p.k + n * p.k_stride + hk,
-                                p.v + n * p.v_stride + hk, p.g + n * p.g_stride + hk, dtb);
-                braw = p.beta[n * p.beta_stride + h];
+                in = load_stage(tid, p.q + n * p.q_stride + oq, p.k + n * p.k_stride + oq,
+                                p.v + n * p.v_stride + ov, g_at(n), g_f32, dtb);
+                braw = beta_at(n);
             }
             __syncthreads();
             TokenOps ops;
@@ -457,15 +493,17 @@ __global__ void __launch_bounds__(256) kda_recurrent_kernel(const RecParams p)
             float o[G];
 #pragma unroll
             for (int gi = 0; gi < G; ++gi) o[gi] = row_update(st[gi], ops, s_v[buf][r_base + gi]);
-            if (m == 0) store_out_bf16<G>(p.out + ((int64_t)t * p.H + h) * KD + r_base, o);
+            if (m == 0) store_out_bf16<G>(p.out + ((int64_t)t * p.HV + hv) * KD + r_base, o);
             if (p.ckpt) {
-                char *ck = reinterpret_cast<char *>(p.ckpt) + ((int64_t)t * p.H + h) * (KD * KD) * es;
+                char *ck = reinterpret_cast<char *>(p.ckpt) + ((int64_t)t * p.HV + hv) * (KD * KD) * es;
 #pragma unroll
                 for (int gi = 0; gi < G; ++gi) IO::store(ck, off[gi], IO::pack(st[gi]));
             }
         }
+        if (update) {
 #pragma unroll
-        for (int gi = 0; gi < G; ++gi) IO::store(head, off[gi], IO::pack(st[gi]));
+            for (int gi = 0; gi < G; ++gi) IO::store(head, off[gi], IO::pack(st[gi]));
+        }
     }
 }
 

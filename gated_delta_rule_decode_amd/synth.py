@@ -76,12 +76,12 @@ def gate_params(gen, H, device):
 class RecurrentCase:
     q: torch.Tensor          # bf16 [T, H, 128]   (T = n_tokens)
     k: torch.Tensor
-    v: torch.Tensor
-    g: torch.Tensor          # bf16 raw gate [T, H, 128]
-    beta: torch.Tensor       # bf16 logits [T, H]
-    A_log: torch.Tensor      # fp32 [H]
-    dt_bias: torch.Tensor    # fp32 [H*128]
-    state: torch.Tensor      # [num_slots, H, 128, 128] fp32 or bf16
+    v: torch.Tensor          # bf16 [T, HV, 128]
+    g: torch.Tensor          # raw gate bf16 [T, HV, 128] (or precomputed log-decay)
+    beta: torch.Tensor       # logits bf16 [T, HV] (or precomputed beta)
+    A_log: torch.Tensor      # fp32 [HV] (None for a precomputed gate)
+    dt_bias: torch.Tensor    # fp32 [HV*128] (None for a precomputed gate)
+    state: torch.Tensor      # [num_slots, HV, 128, 128] fp32 or bf16
     state_indices: torch.Tensor  # int32 [n_seqs]
     cu_seqlens: torch.Tensor | None  # int32 [n_seqs+1] or None (T=1)
 
@@ -92,15 +92,28 @@ class RecurrentCase:
 
 def recurrent_case(seed, *, n_seqs, H, num_slots, state_dtype=torch.float32,
                    device="cpu", indices="identity", lengths=None,
-                   null_rows=0, slot_lo=0):
+                   null_rows=0, slot_lo=0, HV=None, gate="in_kernel",
+                   gate_dtype=torch.float32):
     """Inputs of a recurrent KDA call.
 
     ``lengths`` None means T=1 (one token per sequence, no cu_seqlens);
     otherwise a list of per-sequence token counts (zero allowed).
     ``indices``: "identity" (slot i for sequence i, shifted by slot_lo) or
     "random" (unique slots from [slot_lo, num_slots)). ``null_rows`` rows
-    chosen at random are set to -1.
+    chosen at random are set to -1.  ``HV`` value heads (default H; q and k
+    keep H heads).  ``gate="precomputed"`` draws the log-decay g ~ U(-3, 0)
+    and beta ~ U(0, 1) directly, in ``gate_dtype``.
     """
+    if HV is not None and HV != H:
+        return _grouped_case(seed, n_seqs=n_seqs, H=H, HV=HV, num_slots=num_slots,
+                             state_dtype=state_dtype, device=device, indices=indices,
+                             lengths=lengths, null_rows=null_rows, slot_lo=slot_lo, gate=gate,
+                             gate_dtype=gate_dtype)
+    if gate != "in_kernel":
+        return _grouped_case(seed, n_seqs=n_seqs, H=H, HV=H, num_slots=num_slots,
+                             state_dtype=state_dtype, device=device, indices=indices,
+                             lengths=lengths, null_rows=null_rows, slot_lo=slot_lo, gate=gate,
+                             gate_dtype=gate_dtype)
     gen = _gen(seed, device)
     if lengths is None:
         n_tokens = n_seqs
@@ -118,6 +131,38 @@ def recurrent_case(seed, *, n_seqs, H, num_slots, state_dtype=torch.float32,
     beta = _randn(gen, (n_tokens, H), device)
     A_log, dt_bias = gate_params(gen, H, device)
     state = _randn_big(gen, (num_slots, H, D, D), device, 0.05, state_dtype)
+    if indices == "identity":
+        idx = (torch.arange(n_seqs, device=device) + slot_lo).to(torch.int32)
+    else:
+        idx = unique_slots(gen, n_seqs, slot_lo, num_slots, device)
+    if null_rows:
+        rows = torch.randperm(n_seqs, generator=gen, device=device)[:null_rows]
+        idx[rows] = -1
+    return RecurrentCase(q, k, v, g, beta, A_log, dt_bias, state, idx, cu)
+
+
+def _grouped_case(seed, *, n_seqs, H, HV, num_slots, state_dtype, device, indices, lengths,
+                  null_rows, slot_lo, gate, gate_dtype):
+    gen = _gen(seed, device)
+    if lengths is None:
+        n_tokens, cu = n_seqs, None
+    else:
+        n_tokens = int(sum(lengths))
+        cu = torch.zeros(n_seqs + 1, dtype=torch.int32)
+        cu[1:] = torch.cumsum(torch.tensor(lengths, dtype=torch.int64), 0).to(torch.int32)
+        cu = cu.to(device)
+    q = _randn(gen, (n_tokens, H, D), device)
+    k = _randn(gen, (n_tokens, H, D), device)
+    v = _randn(gen, (n_tokens, HV, D), device)
+    if gate == "in_kernel":
+        g = _randn(gen, (n_tokens, HV, D), device)
+        beta = _randn(gen, (n_tokens, HV), device)
+        A_log, dt_bias = gate_params(gen, HV, device)
+    else:
+        g = _uniform(gen, (n_tokens, HV, D), device, -3.0, 0.0).to(gate_dtype)
+        beta = _uniform(gen, (n_tokens, HV), device, 0.0, 1.0).to(gate_dtype)
+        A_log = dt_bias = None
+    state = _randn_big(gen, (num_slots, HV, D, D), device, 0.05, state_dtype)
     if indices == "identity":
         idx = (torch.arange(n_seqs, device=device) + slot_lo).to(torch.int32)
     else:

@@ -52,7 +52,7 @@ extern "C" {
 #endif
 
 #define KDA_API __attribute__((visibility("default")))
-#define KDA_ABI_VERSION 1
+#define KDA_ABI_VERSION 2
 #define KDA_HEAD_DIM 128
 
 typedef enum kda_status {
@@ -72,10 +72,20 @@ typedef enum kda_status {
 typedef enum kda_dtype { KDA_DTYPE_F32 = 0, KDA_DTYPE_BF16 = 1 } kda_dtype;
 
 /* Gate transform.  SOFTPLUS: g = -exp(A_log[h]) * softplus(raw + dt_bias)
- * (the Kimi-Linear gate, lower_bound=None on the pages).  LOWER_BOUND: the
- * bounded Kimi K3 gate; the pages name it but do not define it, so every
- * call asking for it returns KDA_ERR_UNSUPPORTED. */
-typedef enum kda_gate_mode { KDA_GATE_SOFTPLUS = 0, KDA_GATE_LOWER_BOUND = 1 } kda_gate_mode;
+ * and beta = sigmoid(logit) (the Kimi-Linear in-kernel gate, lower_bound=None
+ * on the pages).  PRECOMPUTED (recurrent_kda only; use_gate_in_kernel=False
+ * on the flashinfer.kda_decode page): g is the log-decay itself (decay =
+ * exp(g)) and beta is beta itself; A_log and dt_bias are not read.
+ * LOWER_BOUND: the bounded Kimi K3 gate; the pages name it but do not define
+ * it, so every call asking for it returns KDA_ERR_UNSUPPORTED. */
+typedef enum kda_gate_mode {
+    KDA_GATE_SOFTPLUS = 0,
+    KDA_GATE_LOWER_BOUND = 1,
+    KDA_GATE_PRECOMPUTED = 2
+} kda_gate_mode;
+
+/* kda_recurrent_args.flags */
+#define KDA_FLAG_NO_STATE_UPDATE 1u /* read-only pool (speculative verify) */
 
 /* Launch geometry chosen from host metadata only (for inspection/tests). */
 typedef struct kda_launch_plan {
@@ -90,32 +100,50 @@ typedef struct kda_launch_plan {
 
 /*
  * recurrent_kda ("flashinfer.kda_decode" function table: recurrent_kda with
- * one token per sequence (T=1) and packed speculative decode with T>=2).
+ * one token per sequence (T=1) and packed speculative decode with T>=2;
+ * "Frozen / speculative-verify mode": disable_state_update=True reads a
+ * committed pool and never writes it back, for the batched [B, T, ...] form
+ * and the packed cu_seqlens form).
  *
  *  n_seqs            sequences (rows), >= 1.
- *  n_tokens          tokens: == n_seqs when cu_seqlens is NULL (T=1);
- *                    otherwise cu_seqlens[n_seqs], >= 0.
- *  H, HV             q/k heads and value heads; HV must equal H.
+ *  n_tokens          tokens: n_seqs * max(1, tokens_per_seq) when cu_seqlens
+ *                    is NULL; otherwise cu_seqlens[n_seqs], >= 0.
+ *  H, HV             q/k heads and value heads; HV must be a multiple of H.
+ *                    Value head hv reads q/k head hv / (HV / H); the state,
+ *                    v, g, beta, A_log, dt_bias and the output are per value
+ *                    head.
  *  K, V              must both be 128.
- *  q, k, v, g        bf16, token t head h at ptr + t*X_stride + h*128 (the
- *                    inner [H,128] is contiguous); g is the raw gate.
- *  beta              bf16 logits, token t head h at beta + t*beta_stride + h.
- *  A_log, dt_bias    fp32 [H] and fp32 [H*128], contiguous.
+ *  q, k              bf16, token t head h at ptr + t*X_stride + h*128 (the
+ *                    inner [H,128] is contiguous).
+ *  v, g              v bf16, g in g_dtype; token t value head hv at
+ *                    ptr + t*X_stride + hv*128 (inner [HV,128] contiguous).
+ *                    g is the raw gate (SOFTPLUS) or the log-decay
+ *                    (PRECOMPUTED).
+ *  beta              in beta_dtype, token t value head hv at
+ *                    beta + t*beta_stride + hv: logits (SOFTPLUS) or beta
+ *                    itself (PRECOMPUTED).
+ *  A_log, dt_bias    fp32 [HV] and fp32 [HV*128], contiguous (SOFTPLUS only;
+ *                    may be NULL for PRECOMPUTED).
  *  scale             output scale (the pages use 1/sqrt(128)).
  *  l2_eps            q/k L2-norm epsilon (the pages use 1e-6), >= 0.
  *  gate_mode         kda_gate_mode (LOWER_BOUND is unsupported).
- *  lower_bound       ignored for SOFTPLUS.
- *  state             pool as described above; state_dtype its kda_dtype.
+ *  lower_bound       ignored unless LOWER_BOUND.
+ *  state             pool [num_slots, HV, 128, 128] as described above;
+ *                    state_dtype its kda_dtype.
  *  num_slots         slots in the pool, >= 1; slot_stride in elements.
  *  state_indices     int32 [n_seqs]; idx < 0 or idx >= num_slots is null.
- *  cu_seqlens        NULL (T=1) or int32 [n_seqs+1], cu_seqlens[0] == 0,
+ *  cu_seqlens        NULL, or int32 [n_seqs+1], cu_seqlens[0] == 0,
  *                    non-decreasing (read on the device at every launch, so a
  *                    captured graph follows new lengths; n_tokens must match
  *                    its last entry).  Empty sequences touch nothing.
- *  checkpoints       NULL or [n_tokens, H, 128, 128] contiguous in the pool's
- *                    [v][k] layout, dtype ckpt_dtype: the state after each
- *                    token.  Null sequences write no checkpoint.
- *  out               bf16 [n_tokens, H, 128] contiguous.
+ *  checkpoints       NULL or [n_tokens, HV, 128, 128] contiguous in the
+ *                    pool's [v][k] layout, dtype ckpt_dtype (= state_dtype):
+ *                    the state after each token.  Null sequences write none.
+ *  out               bf16 [n_tokens, HV, 128] contiguous.
+ *  g_dtype, beta_dtype  kda_dtype of g and beta (bf16 or fp32).
+ *  tokens_per_seq    without cu_seqlens: 0 or 1 is T=1, T > 1 is the uniform
+ *                    batched form (sequence i owns tokens [i*T, (i+1)*T)).
+ *  flags             KDA_FLAG_NO_STATE_UPDATE: the pool is only read.
  */
 typedef struct kda_recurrent_args {
     uint32_t struct_size;
@@ -150,6 +178,10 @@ typedef struct kda_recurrent_args {
     const int32_t *cu_seqlens;
     void *checkpoints;
     void *out;
+    int32_t g_dtype;
+    int32_t beta_dtype;
+    int32_t tokens_per_seq;
+    uint32_t flags;
 } kda_recurrent_args;
 
 /*

@@ -30,7 +30,7 @@ def test_header_symbols_exported():
 
 def test_version_and_status_strings():
     L = lib()
-    assert L.kda_version() == 1
+    assert L.kda_version() == 2
     for code in _lib.STATUS:
         assert L.kda_status_string(code).decode()
     assert L.kda_status_string(12345).decode() == "unknown status"
@@ -61,28 +61,31 @@ class Arena:
         return a
 
 
-def rec_args(N=4, H=4, T=None, slots=8, bf16=False, varlen=False):
+def rec_args(N=4, H=4, T=None, slots=8, bf16=False, varlen=False, HV=None, tps=1):
     A = Arena()
-    T = N if T is None else T
+    HV = H if HV is None else HV
+    T = N * tps if T is None else T
     a = _lib.RecurrentArgs()
     a.struct_size = ctypes.sizeof(_lib.RecurrentArgs)
-    a.n_seqs, a.n_tokens, a.H, a.HV, a.K, a.V = N, T, H, H, D, D
-    for f in ("q", "k", "v", "g"):
-        setattr(a, f, A.take(T * H * D * 2))
-        setattr(a, f + "_stride", H * D)
-    a.beta = A.take(T * H * 2)
-    a.beta_stride = H
-    a.A_log = A.take(H * 4)
-    a.dt_bias = A.take(H * D * 4)
+    a.n_seqs, a.n_tokens, a.H, a.HV, a.K, a.V = N, T, H, HV, D, D
+    for f, hh in (("q", H), ("k", H), ("v", HV), ("g", HV)):
+        setattr(a, f, A.take(T * hh * D * 2))
+        setattr(a, f + "_stride", hh * D)
+    a.beta = A.take(T * HV * 2)
+    a.beta_stride = HV
+    a.A_log = A.take(HV * 4)
+    a.dt_bias = A.take(HV * D * 4)
     a.scale, a.l2_eps = 0.08838834764831845, 1e-6
     es = 2 if bf16 else 4
-    a.state = A.take(slots * H * D * D * es)
+    a.state = A.take(slots * HV * D * D * es)
     a.state_dtype = a.ckpt_dtype = 1 if bf16 else 0
-    a.num_slots, a.slot_stride = slots, H * D * D
+    a.num_slots, a.slot_stride = slots, HV * D * D
     a.state_indices = A.take(N * 4)
     if varlen:
         a.cu_seqlens = A.take((N + 1) * 4)
-    a.out = A.take(T * H * D * 2)
+    a.out = A.take(T * HV * D * 2)
+    a.g_dtype = a.beta_dtype = 1
+    a.tokens_per_seq = tps
     return a
 
 
@@ -187,7 +190,7 @@ def test_recurrent_validation_errors():
     expect(plan_rec(a), -1)
     a = rec_args(); a.K = 64
     expect(plan_rec(a), -7, "K=64")
-    a = rec_args(); a.HV = 8
+    a = rec_args(); a.HV = 6
     expect(plan_rec(a), -7, "HV")
     a = rec_args(); a.n_tokens = 5
     expect(plan_rec(a), -2, "n_tokens")
@@ -279,3 +282,53 @@ def test_device_check_without_gpu_is_an_error_not_a_crash():
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
     assert lib().kda_check_device(0) == -8
+
+
+# ---- grouped value heads, precomputed gate, batched form, read-only pool --------
+
+def test_grouped_heads_plan():
+    rc, p = plan_rec(rec_args(N=64, H=4, HV=16, slots=64))
+    assert rc == 0, err()
+    assert p.items == 64 * 16 and p.kernel == 1
+    a = rec_args(N=4, H=4, HV=16)
+    a.v_stride = 4 * D  # v holds HV heads
+    expect(plan_rec(a), -4, "v/g")
+    a = rec_args(N=4, H=4, HV=16)
+    a.beta_stride = 4
+    expect(plan_rec(a), -4, "beta_stride")
+
+
+def test_precomputed_gate_needs_no_gate_params():
+    a = rec_args()
+    a.gate_mode = 2
+    a.A_log = a.dt_bias = 0
+    a.g_dtype = a.beta_dtype = 0  # fp32 inputs; the arena left room for them
+    assert plan_rec(a)[0] == 0, err()
+    a = rec_args()
+    a.A_log = 0
+    expect(plan_rec(a), -1)
+    a = rec_args()
+    a.g_dtype = 5
+    expect(plan_rec(a), -3)
+
+
+def test_batched_form_and_flags():
+    rc, p = plan_rec(rec_args(N=8, tps=4))
+    assert rc == 0, err()
+    assert p.kernel == 2  # token loop
+    a = rec_args(N=8, tps=4)
+    a.n_tokens = 31
+    expect(plan_rec(a), -2, "tokens_per_seq")
+    a = rec_args()
+    a.flags = 2
+    expect(plan_rec(a), -7, "flags")
+    a = rec_args()
+    a.flags = 1
+    assert plan_rec(a)[0] == 0, err()
+
+
+def test_read_only_pool_still_may_not_alias_outputs():
+    a = rec_args(varlen=True, T=4)
+    a.flags = 1
+    a.out = a.state
+    expect(plan_rec(a), -6, "state")
