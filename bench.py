@@ -63,6 +63,18 @@ def fused_bytes(R_live, R_null, H, state_bytes):
     return R_live * per_row + R_null * (4 + H * D * 2) + 12 * H * D * 4 + H * 4 + H * D * 4 + D * 4
 
 
+def modes_bytes(n_live_seqs, tokens, H, HV, state_bytes, *, write_state=True, gate_bytes=2,
+                beta_bytes=2, gate_params=True):
+    """Recurrent call with HV value heads over H q/k heads: per live (sequence,
+    value head) the state is read (and written unless read-only); per token
+    q, k per q/k head and v, g, beta, output per value head."""
+    head = D * D * state_bytes
+    b = n_live_seqs * HV * head * (2 if write_state else 1)
+    b += tokens * (H * 2 * D * 2 + HV * (D * 2 + D * gate_bytes + beta_bytes + D * 2))
+    b += n_live_seqs * 4 + (HV * 4 + HV * D * 4 if gate_params else 0)
+    return b
+
+
 def varlen_bytes(lengths, H, state_bytes, ckpt=True):
     live_seqs = sum(1 for n in lengths if n > 0)
     T = sum(lengths)
@@ -328,6 +340,45 @@ def extra_workloads(torch, dev, timer, pool32):
                                        "GBps": bts / (t_us * 1e-6) / 1e9,
                                        "frac": bts / (t_us * 1e-6) / 1e9 / HBM_PEAK_GBPS}
     log(f"varlen H=16 N=64 T={T}: {t_us:.1f} us, {bts / (t_us * 1e-6) / 1e9:.0f} GB/s")
+    del vc, ck
+    torch.cuda.empty_cache()
+
+    def modes_entry(name, calls, bts, rows):
+        t = rotating(torch, timer, calls)
+        out[name] = {"us": t, "rows_per_s": rows / (t * 1e-6), "GBps": bts / (t * 1e-6) / 1e9,
+                     "frac": bts / (t * 1e-6) / 1e9 / HBM_PEAK_GBPS}
+        log(f"{name}: {t:.1f} us, {out[name]['GBps']:.0f} GB/s")
+
+    # grouped value heads: H=16 q/k heads, HV=32 value heads, fp32 pool, T=1, B=256
+    B = 256
+    gc = synth.recurrent_case(7000, n_seqs=B, H=16, HV=32, num_slots=1, device=dev)
+    perm = torch.randperm(SLOTS, generator=g2, device=dev).to(torch.int32)
+    o = torch.empty((B, 1, 32, D), dtype=torch.bfloat16, device=dev)
+    r = lambda t: t.reshape(B, 1, *t.shape[1:])  # noqa: E731
+    calls = [lambda ids=perm[j * B:(j + 1) * B].contiguous(): recurrent_kda(
+        r(gc.q), r(gc.k), r(gc.v), r(gc.g), r(gc.beta), gc.A_log, gc.dt_bias, initial_state=pool32,
+        state_indices=ids, output=o) for j in range(4)]
+    modes_entry("grouped_t1_h16_hv32_fp32_b256", calls, modes_bytes(B, B, 16, 32, 4), B)
+
+    # precomputed gate (fp32 log-decay and beta), H=32, fp32 pool, T=1, B=256
+    pc = synth.recurrent_case(7100, n_seqs=B, H=32, num_slots=1, device=dev, gate="precomputed")
+    calls = [lambda ids=perm[j * B:(j + 1) * B].contiguous(): recurrent_kda(
+        r(pc.q), r(pc.k), r(pc.v), r(pc.g), r(pc.beta), initial_state=pool32, state_indices=ids,
+        output=o) for j in range(4)]
+    modes_entry("precomputed_t1_h32_fp32_b256", calls,
+                modes_bytes(B, B, 32, 32, 4, gate_bytes=4, beta_bytes=4, gate_params=False), B)
+
+    # speculative verify: read-only pool, batched [64, 4, 32, 128], H=32 fp32
+    Bv, Tv = 64, 4
+    vv = synth.recurrent_case(7200, n_seqs=Bv, H=32, num_slots=1, device=dev, lengths=[Tv] * Bv)
+    ov = torch.empty((Bv, Tv, 32, D), dtype=torch.bfloat16, device=dev)
+    rb = lambda t: t.reshape(Bv, Tv, *t.shape[1:])  # noqa: E731
+    calls = [lambda ids=perm[j * Bv:(j + 1) * Bv].contiguous(): recurrent_kda(
+        rb(vv.q), rb(vv.k), rb(vv.v), rb(vv.g), rb(vv.beta), vv.A_log, vv.dt_bias,
+        initial_state=pool32, state_indices=ids, output=ov, disable_state_update=True)
+        for j in range(8)]
+    modes_entry("verify_readonly_b64_t4_h32_fp32", calls,
+                modes_bytes(Bv, Bv * Tv, 32, 32, 4, write_state=False), Bv)
     return out
 
 
