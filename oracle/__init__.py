@@ -59,6 +59,10 @@ def _load(path=None):
         lib.kdao_recurrent2.restype = Int
         lib.kdao_recurrent2.argtypes = [I64, I64, I64, I64, P, P, P, P, Int, P, Int, Int, P, P,
                                         Dbl, Dbl, P, I64, P, I64, Int, P, Int, P, P, Int, P, P]
+        lib.kdao_recurrent3.restype = Int
+        lib.kdao_recurrent3.argtypes = [I64, I64, I64, I64, P, P, P, P, Int, P, Int, Int, P, P,
+                                        Dbl, Dbl, P, I64, P, I64, Int, P, Int, P, P, Int, P, P,
+                                        I64, P, P]
         lib.kdao_fused.restype = Int
         lib.kdao_fused.argtypes = [I64, I64, P, P, I64, P, I64, P, P, P, P, P, Int, P,
                                    P, P, Dbl, Dbl, Dbl, P, P, P, P]
@@ -150,7 +154,8 @@ def _gate_input(a, what):
 
 def recurrent(q, k, v, g, beta, A_log, dt_bias, state, state_indices,
               cu_seqlens=None, *, scale=SCALE, l2_eps=L2_EPS, ckpt_dtype=None,
-              want_ckpt64=False, gate="in_kernel", update_state=True, tokens_per_seq=1):
+              want_ckpt64=False, gate="in_kernel", update_state=True, tokens_per_seq=1,
+              t_max=None):
     """Recurrent KDA: T=1, uniform batches of tokens_per_seq tokens, or ragged
     (cu_seqlens given).
 
@@ -161,7 +166,10 @@ def recurrent(q, k, v, g, beta, A_log, dt_bias, state, state_indices,
     is the log-decay and beta is beta itself (A_log, dt_bias may be None).
     state [slots, HV, 128, 128] (fp32, bf16 bits or float64), state_indices
     int32 [N].  update_state=False leaves the pool as it was (read-only verify).
-    Returns dict(out64, out_bf16, state, ckpt, ckpt64).
+    t_max: also return the verify caches corr [slots, HV, t_max, 128] (the
+    correction beta*u of each token) and kg [slots, HV, t_max, 256] (raw key |
+    raw gate), in float64, zero where nothing was recorded.
+    Returns dict(out64, out_bf16, state, ckpt, ckpt64, corr, kg).
     """
     q = _c(q, np.uint16); k = _c(k, np.uint16); v = _c(v, np.uint16)
     g, g_f32 = _gate_input(g, "g")
@@ -188,14 +196,21 @@ def recurrent(q, k, v, g, beta, A_log, dt_bias, state, state_indices,
         cdt = ckpt_dtype
         ckpt = np.zeros((T, HV, D, D), _NP_OF[cdt])
     ck64 = np.zeros((T, HV, D, D), np.float64) if want_ckpt64 else None
-    rc = _load().kdao_recurrent2(T, N, H, HV, _ptr(q), _ptr(k), _ptr(v), _ptr(g), g_f32,
+    corr = kg = None
+    tm = 0
+    if t_max is not None:
+        tm = int(t_max)
+        corr = np.zeros((st.shape[0], HV, tm, D), np.float64)
+        kg = np.zeros((st.shape[0], HV, tm, 2 * D), np.float64)
+    rc = _load().kdao_recurrent3(T, N, H, HV, _ptr(q), _ptr(k), _ptr(v), _ptr(g), g_f32,
                                  _ptr(beta), b_f32, mode, _ptr(A_log), _ptr(dt_bias),
                                  float(scale), float(l2_eps), _ptr(cu), int(tokens_per_seq),
                                  _ptr(idx), st.shape[0], sdt, _ptr(st), 1 if update_state else 0,
-                                 _ptr(out64), _ptr(outb), cdt, _ptr(ckpt), _ptr(ck64))
+                                 _ptr(out64), _ptr(outb), cdt, _ptr(ckpt), _ptr(ck64),
+                                 tm, _ptr(corr), _ptr(kg))
     if rc != 0:
-        raise ValueError(f"kdao_recurrent2 rejected its arguments ({rc})")
-    return dict(out64=out64, out_bf16=outb, state=st, ckpt=ckpt, ckpt64=ck64)
+        raise ValueError(f"kdao_recurrent3 rejected its arguments ({rc})")
+    return dict(out64=out64, out_bf16=outb, state=st, ckpt=ckpt, ckpt64=ck64, corr=corr, kg=kg)
 
 
 def packed(mixed_qkv, raw_gate, raw_beta, A_log, dt_bias, state, state_indices):

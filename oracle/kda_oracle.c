@@ -137,10 +137,12 @@ static void gate_decay(const double *raw, double A_log_h, const float *dt_bias_h
 }
 
 /* One token of the recurrence on S[k][v] (math orientation, K x V).
- * qh, kh are the L2-normalised vectors; o receives scale * S'^T q. */
+ * qh, kh are the L2-normalised vectors; o receives scale * S'^T q; corr (may
+ * be NULL) receives the delta-rule correction beta * u, the vector the
+ * update adds along k: S' = D S + k corr^T. */
 static void kda_token(double S[KD][KD], const double *qh, const double *kh,
                       const double *v, const double *decay, double beta,
-                      double scale, double *o)
+                      double scale, double *o, double *corr)
 {
     /* S <- diag(exp g) S : row k of S scaled by decay[k] */
     for (int k = 0; k < KD; ++k)
@@ -155,6 +157,8 @@ static void kda_token(double S[KD][KD], const double *qh, const double *kh,
     /* S <- S + beta k u^T */
     for (int k = 0; k < KD; ++k)
         for (int j = 0; j < KD; ++j) S[k][j] += beta * kh[k] * u[j];
+    if (corr)
+        for (int j = 0; j < KD; ++j) corr[j] = beta * u[j];
     /* o = scale * S^T q */
     for (int j = 0; j < KD; ++j) {
         double acc = 0.0;
@@ -199,6 +203,13 @@ static void widen_bf16(const uint16_t *src, double *dst, int n)
  * beta itself; A_log and dt_bias are not read.
  * update_state 0: the pool is read only (speculative verify); outputs and
  * checkpoints are produced as usual.
+ * Verify caches (slot-indexed, position j = t - t0 inside the sequence, only
+ * for j < t_max, live sequences only):
+ *   corr [num_slots][HV][t_max][128]: the delta-rule correction beta * u of
+ *   the token, so that S_t = D_t S_{t-1} + k_hat_t corr_t^T;
+ *   kg   [num_slots][HV][t_max][256]: the raw key of the value head's q/k
+ *   head (before L2 normalisation) and the raw gate as given (the log-decay
+ *   in precomputed mode).
  *
  * Layouts (all contiguous, host memory):
  *   q, k: bf16 [n_tokens][H][128];  v: bf16 [n_tokens][HV][128]
@@ -215,7 +226,7 @@ static double load_in(const void *p, int is_f32, size_t i)
     return is_f32 ? (double)((const float *)p)[i] : bf16_to_f64(((const uint16_t *)p)[i]);
 }
 
-int kdao_recurrent2(int64_t n_tokens, int64_t n_seqs, int64_t H, int64_t HV,
+int kdao_recurrent3(int64_t n_tokens, int64_t n_seqs, int64_t H, int64_t HV,
                     const uint16_t *q, const uint16_t *k, const uint16_t *v,
                     const void *g, int g_f32, const void *beta, int beta_f32, int gate_mode,
                     const float *A_log, const float *dt_bias,
@@ -224,7 +235,8 @@ int kdao_recurrent2(int64_t n_tokens, int64_t n_seqs, int64_t H, int64_t HV,
                     const int32_t *state_indices, int64_t num_slots, int state_dtype,
                     void *state, int update_state,
                     double *out64, uint16_t *out_bf16,
-                    int ckpt_dtype, void *ckpt, double *ckpt64)
+                    int ckpt_dtype, void *ckpt, double *ckpt64,
+                    int64_t t_max, double *corr, double *kg)
 {
     if (n_tokens < 0 || n_seqs < 0 || H <= 0 || HV <= 0 || HV % H != 0) return -1;
     const int64_t tps = tokens_per_seq > 1 ? tokens_per_seq : 1;
@@ -277,7 +289,19 @@ int kdao_recurrent2(int64_t n_tokens, int64_t n_seqs, int64_t H, int64_t HV,
                 }
                 l2_normalise(qv, l2_eps, qh);
                 l2_normalise(kv, l2_eps, kh);
-                kda_token(S, qh, kh, vv, dec, b, scale, o);
+                double c[KD];
+                kda_token(S, qh, kh, vv, dec, b, scale, o, c);
+                const int64_t pos = t - t0; /* token position inside the sequence */
+                if (pos < t_max) {
+                    size_t cs = (((size_t)idx * HV + hv) * t_max + pos);
+                    if (corr)
+                        for (int j = 0; j < KD; ++j) corr[cs * KD + j] = c[j];
+                    if (kg)
+                        for (int j = 0; j < KD; ++j) {
+                            kg[cs * 2 * KD + j] = kv[j];      /* raw key of the q/k head */
+                            kg[cs * 2 * KD + KD + j] = gv[j]; /* raw gate (or log-decay) */
+                        }
+                }
                 for (int j = 0; j < KD; ++j) {
                     if (out64) out64[vh + j] = o[j];
                     if (out_bf16) out_bf16[vh + j] = kdao_bf16_from_f64(o[j]);
@@ -291,6 +315,24 @@ int kdao_recurrent2(int64_t n_tokens, int64_t n_seqs, int64_t H, int64_t HV,
     }
     free(S);
     return 0;
+}
+
+/* kdao_recurrent3 without the verify caches. */
+int kdao_recurrent2(int64_t n_tokens, int64_t n_seqs, int64_t H, int64_t HV,
+                    const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                    const void *g, int g_f32, const void *beta, int beta_f32, int gate_mode,
+                    const float *A_log, const float *dt_bias,
+                    double scale, double l2_eps,
+                    const int32_t *cu_seqlens, int64_t tokens_per_seq,
+                    const int32_t *state_indices, int64_t num_slots, int state_dtype,
+                    void *state, int update_state,
+                    double *out64, uint16_t *out_bf16,
+                    int ckpt_dtype, void *ckpt, double *ckpt64)
+{
+    return kdao_recurrent3(n_tokens, n_seqs, H, HV, q, k, v, g, g_f32, beta, beta_f32, gate_mode,
+                           A_log, dt_bias, scale, l2_eps, cu_seqlens, tokens_per_seq,
+                           state_indices, num_slots, state_dtype, state, update_state, out64,
+                           out_bf16, ckpt_dtype, ckpt, ckpt64, 0, NULL, NULL);
 }
 
 /* The equal-head, in-kernel-gate, state-updating form of kdao_recurrent2. */
@@ -387,7 +429,7 @@ int kdao_fused(int64_t rows, int64_t H, const uint16_t *x, const float *weight,
             gate_decay(gv, (double)A_log[h], dt_bias + h * KD, dec);
             size_t head_base = ((size_t)idx * H + h) * head_elems;
             gather_state(state, state_dtype, head_base, S);
-            kda_token(S, qh, kh, va, dec, beta, scale, o);
+            kda_token(S, qh, kh, va, dec, beta, scale, o, NULL);
             scatter_state(state, state_dtype, head_base, S);
             /* gated RMSNorm over the 128 values of this head */
             double ms = 0.0;

@@ -37,6 +37,10 @@ MUTANTS = [
     ("q/k head not grouped", "const int64_t hk = hv / group;", "const int64_t hk = hv % H;"),
     ("precomputed decay taken as the gate", "for (int j = 0; j < KD; ++j) dec[j] = exp(gv[j]);",
      "for (int j = 0; j < KD; ++j) dec[j] = gv[j];"),
+    ("correction without beta", "for (int j = 0; j < KD; ++j) corr[j] = beta * u[j];",
+     "for (int j = 0; j < KD; ++j) corr[j] = u[j];"),
+    ("gate cache holds the decay", "kg[cs * 2 * KD + KD + j] = gv[j];",
+     "kg[cs * 2 * KD + KD + j] = dec[j];"),
     ("read-only pool written", "if (update_state) scatter_state(state, state_dtype, head_base, S);",
      "scatter_state(state, state_dtype, head_base, S);"),
     ("l2 norm dropped", "double inv = 1.0 / sqrt(ss + eps);", "double inv = 1.0;"),
@@ -77,6 +81,9 @@ PINS = [
     pins.test_precomputed_beta_is_used_as_is,
     pins.test_read_only_pool,
     pins.test_batched_form_equals_uniform_cu_seqlens,
+    lambda: pins.test_verify_caches_rebuild_every_checkpoint("in_kernel"),
+    lambda: pins.test_verify_caches_rebuild_every_checkpoint("precomputed"),
+    pins.test_verify_caches_positions_and_null_rows,
 ]
 
 

@@ -550,3 +550,65 @@ def test_batched_form_equals_uniform_cu_seqlens():
     b = _run(c, cu_seqlens=None, tokens_per_seq=4, ckpt_dtype=oracle.F32)
     for key in ("out64", "state", "ckpt"):
         np.testing.assert_array_equal(a[key], b[key])
+
+
+# ---- verify caches: per-token corrections and raw key | gate -----------------------------
+
+def _commit_from_caches(S0, corr, kg, n, gate, A_log=None, dt_bias=None, eps=oracle.L2_EPS):
+    """Rebuild the state after the first n tokens of one (slot, head) from the
+    caches alone: S_t = D_t S_{t-1} + k_hat_t c_t^T (math orientation K x V)."""
+    S = S0.T.copy()
+    for t in range(n):
+        kraw, graw = kg[t, :D], kg[t, D:]
+        kh = kraw / math.sqrt(float((kraw * kraw).sum()) + eps)
+        if gate == "in_kernel":
+            x = graw + dt_bias
+            d = np.exp(-math.exp(A_log) * (np.maximum(x, 0) + np.log1p(np.exp(-np.abs(x)))))
+        else:
+            d = np.exp(graw)
+        S = d[:, None] * S + np.outer(kh, corr[t])
+    return S.T
+
+
+@pytest.mark.parametrize("gate", ["in_kernel", "precomputed"])
+def test_verify_caches_rebuild_every_checkpoint(gate):
+    """From the initial state and the two caches alone, every prefix state of
+    every live sequence is rebuilt: the correction is exactly the vector the
+    delta rule adds along k_hat, and kg holds the key and gate the step used."""
+    lengths = [3, 0, 4, 1]
+    c = synth.recurrent_case(40, n_seqs=4, H=6, HV=6, num_slots=7, indices="random",
+                             lengths=lengths, null_rows=0, gate=gate)
+    st0 = _np(c.state).astype(np.float64)
+    r = oracle.recurrent(c.q, c.k, c.v, c.g, c.beta, c.A_log, c.dt_bias, st0, c.state_indices,
+                         c.cu_seqlens, want_ckpt64=True, gate=gate, update_state=False, t_max=4)
+    cu = _np(c.cu_seqlens)
+    idx = _np(c.state_indices)
+    for i in range(4):
+        s = int(idx[i])
+        for h in range(6):
+            for n in range(1, lengths[i] + 1):
+                S = _commit_from_caches(st0[s, h], r["corr"][s, h], r["kg"][s, h], n, gate,
+                                        None if gate != "in_kernel" else float(_np(c.A_log)[h]),
+                                        None if gate != "in_kernel" else
+                                        _np(c.dt_bias)[h * D:(h + 1) * D].astype(np.float64))
+                np.testing.assert_allclose(S, r["ckpt64"][cu[i] + n - 1, h], rtol=0, atol=1e-12)
+    np.testing.assert_array_equal(r["state"], st0)
+
+
+def test_verify_caches_positions_and_null_rows():
+    """Tokens at positions >= t_max are not recorded; null sequences record
+    nothing; the key half of kg is the raw (unnormalised) key of the q/k head."""
+    c = synth.recurrent_case(41, n_seqs=3, H=2, HV=4, num_slots=5, indices="random",
+                             lengths=[3, 2, 1])
+    idx = _np(c.state_indices).copy()
+    idx[2] = -1
+    r = oracle.recurrent(c.q, c.k, c.v, c.g, c.beta, c.A_log, c.dt_bias,
+                         _np(c.state).astype(np.float64), idx, c.cu_seqlens, t_max=2)
+    k = oracle.bf16_to_f64(_np(c.k))
+    s0, s1 = int(idx[0]), int(idx[1])
+    np.testing.assert_array_equal(r["kg"][s0, 3, 1, :D], k[1, 3 // 2])
+    assert np.abs(r["corr"][s0, :, :2]).min(axis=-1).max() > 0  # positions 0, 1 recorded
+    live = {s0, s1}
+    for s in range(5):
+        if s not in live:
+            assert not r["corr"][s].any() and not r["kg"][s].any()
