@@ -379,6 +379,18 @@ def extra_workloads(torch, dev, timer, pool32):
         for j in range(8)]
     modes_entry("verify_readonly_b64_t4_h32_fp32", calls,
                 modes_bytes(Bv, Bv * Tv, 32, 32, 4, write_state=False), Bv)
+
+    # the same verify call recording the per-token corrections (fp32) and raw
+    # key | gate (fp32) into slot-indexed caches
+    corr = torch.empty((SLOTS, 32, Tv, D), dtype=torch.float32, device=dev)
+    kgc = torch.empty((SLOTS, 32, Tv, 2 * D), dtype=torch.float32, device=dev)
+    calls = [lambda ids=perm[j * Bv:(j + 1) * Bv].contiguous(): recurrent_kda(
+        rb(vv.q), rb(vv.k), rb(vv.v), rb(vv.g), rb(vv.beta), vv.A_log, vv.dt_bias,
+        initial_state=pool32, state_indices=ids, output=ov, disable_state_update=True,
+        correction_cache=corr, kg_cache=kgc) for j in range(8)]
+    modes_entry("verify_caches_b64_t4_h32_fp32", calls,
+                modes_bytes(Bv, Bv * Tv, 32, 32, 4, write_state=False) + Bv * Tv * 32 * 3 * D * 4, Bv)
+    del corr, kgc
     return out
 
 

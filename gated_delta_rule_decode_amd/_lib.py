@@ -46,7 +46,8 @@ class RecurrentArgs(ctypes.Structure):
         ("state", _P), ("state_dtype", _I32), ("ckpt_dtype", _I32), ("num_slots", _I64),
         ("slot_stride", _I64), ("state_indices", _P), ("cu_seqlens", _P), ("checkpoints", _P),
         ("out", _P), ("g_dtype", _I32), ("beta_dtype", _I32), ("tokens_per_seq", _I32),
-        ("flags", _U32),
+        ("flags", _U32), ("correction_cache", _P), ("kg_cache", _P), ("kg_dtype", _I32),
+        ("cache_t_max", _I32),
     ]
 
 

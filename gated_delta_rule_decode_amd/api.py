@@ -105,7 +105,7 @@ def _tokens(t, name, heads, width, ragged):
 def recurrent_kda(q, k, v, g, beta, A_log=None, dt_bias=None, *, initial_state, state_indices,
                   cu_seqlens=None, n_tokens=None, scale=None, output=None, intermediate_states=None,
                   lower_bound=None, use_qk_l2norm_in_kernel=True, use_gate_in_kernel=None,
-                  disable_state_update=False, l2_eps=1e-6):
+                  disable_state_update=False, l2_eps=1e-6, correction_cache=None, kg_cache=None):
     """Recurrent KDA decode ("flashinfer.kda_decode" function table).
 
     Forms: T=1 (q [B, 1, H, 128] or [B, H, 128]); batched T tokens per
@@ -120,7 +120,12 @@ def recurrent_kda(q, k, v, g, beta, A_log=None, dt_bias=None, *, initial_state, 
     128, 128] (fp32 or bf16) is updated in place at ``state_indices`` (int32,
     negative = null row) unless ``disable_state_update``.
     ``intermediate_states`` (optional, [T, HV, 128, 128], pool dtype) receives
-    the state after every token.  Returns the bf16 output [.., HV, 128].
+    the state after every token.  Verify caches ("Frozen / speculative-verify
+    mode"), each optional and indexed by pool slot: ``correction_cache`` fp32
+    [num_slots, HV, T_max, 128] receives beta*u of token j of the sequence
+    in that slot, ``kg_cache`` [num_slots, HV, T_max, 256] (fp32 or bf16) its
+    raw key | raw gate; tokens j >= T_max and null rows record nothing.
+    Returns the bf16 output [.., HV, 128].
     """
     _need(use_qk_l2norm_in_kernel, "only the in-kernel q/k L2 normalisation is implemented")
     if use_gate_in_kernel is None:
@@ -167,6 +172,17 @@ def recurrent_kda(q, k, v, g, beta, A_log=None, dt_bias=None, *, initial_state, 
     if ck is not None:
         _need(ck.dtype == state.dtype and ck.is_contiguous() and ck.numel() == T * HV * D * D,
               "intermediate_states must be contiguous [T, HV, 128, 128] in the pool dtype")
+    t_max = None
+    for name, c, w in (("correction_cache", correction_cache, D), ("kg_cache", kg_cache, 2 * D)):
+        if c is None:
+            continue
+        _need(c.is_cuda and c.is_contiguous() and c.dim() == 4 and c.shape[0] == state.shape[0]
+              and c.shape[1] == HV and c.shape[3] == w,
+              f"{name} must be contiguous [num_slots, HV, T_max, {w}]")
+        _need(t_max is None or c.shape[2] == t_max, "the verify caches must share T_max")
+        t_max = c.shape[2]
+    if correction_cache is not None:
+        _need(correction_cache.dtype == torch.float32, "correction_cache must be fp32")
     a = _lib.RecurrentArgs()
     a.struct_size = ctypes.sizeof(_lib.RecurrentArgs)
     a.n_seqs, a.n_tokens, a.H, a.HV, a.K, a.V = N, T, H, HV, D, D
@@ -186,6 +202,9 @@ def recurrent_kda(q, k, v, g, beta, A_log=None, dt_bias=None, *, initial_state, 
     a.g_dtype, a.beta_dtype = _dtype_code(g, "g"), _dtype_code(beta, "beta")
     a.tokens_per_seq = tps
     a.flags = _lib.FLAG_NO_STATE_UPDATE if disable_state_update else 0
+    a.correction_cache, a.kg_cache = _ptr(correction_cache), _ptr(kg_cache)
+    a.kg_dtype = _dtype_code(kg_cache, "kg_cache") if kg_cache is not None else _lib.DTYPE_F32
+    a.cache_t_max = t_max or 0
     lib = _lib.load()
     with torch.cuda.device(q.device):
         _lib.check(lib.kda_recurrent(ctypes.byref(a), _stream(q.device)))

@@ -203,12 +203,23 @@ int prepare_recurrent(const kda_recurrent_args *a, RecParams *p, Launch *l)
         if (!aligned16(a->checkpoints)) return fail(KDA_ERR_ALIGN, "checkpoints must be 16-byte aligned");
     }
     const bool update = !(a->flags & KDA_FLAG_NO_STATE_UPDATE);
+    const bool caches = a->correction_cache || a->kg_cache;
+    if (caches) {
+        if (a->cache_t_max < 1) return fail(KDA_ERR_SHAPE, "cache_t_max must be >= 1 with a verify cache");
+        if (a->kg_cache && !dtype_ok(a->kg_dtype)) return fail(KDA_ERR_DTYPE, "kg_dtype %d", a->kg_dtype);
+        if (!aligned16(a->correction_cache) || !aligned4(a->kg_cache))
+            return fail(KDA_ERR_ALIGN, "correction_cache must be 16-byte and kg_cache 4-byte aligned");
+    }
+    const uint64_t cache_rows = caches ? (uint64_t)a->num_slots * a->HV * a->cache_t_max : 0;
+    const int kg_es = a->kg_dtype == KDA_DTYPE_F32 ? 4 : 2;
     const int64_t T = a->n_tokens;
     const int es = elem_size(a->state_dtype);
     const Range state_r = span(a->state, pool_bytes(a->state_dtype, a->num_slots, a->slot_stride, a->HV), "state");
-    Range w[3] = {span(a->out, (uint64_t)T * HVC * 2, "out"),
+    Range w[5] = {span(a->out, (uint64_t)T * HVC * 2, "out"),
                   span(a->checkpoints, a->checkpoints ? (uint64_t)T * a->HV * HEAD_ELEMS * es : 0, "checkpoints"),
-                  update ? state_r : Range{0, 0, ""}};
+                  update ? state_r : Range{0, 0, ""},
+                  span(a->correction_cache, a->correction_cache ? cache_rows * KD * 4 : 0, "correction_cache"),
+                  span(a->kg_cache, a->kg_cache ? cache_rows * 2 * KD * kg_es : 0, "kg_cache")};
     Range r[10] = {span(a->q, rows_extent(T, a->q_stride, HQ) * 2, "q"),
                    span(a->k, rows_extent(T, a->k_stride, HQ) * 2, "k"),
                    span(a->v, rows_extent(T, a->v_stride, HVC) * 2, "v"),
@@ -219,7 +230,7 @@ int prepare_recurrent(const kda_recurrent_args *a, RecParams *p, Launch *l)
                    span(a->state_indices, (uint64_t)a->n_seqs * 4, "state_indices"),
                    span(a->cu_seqlens, ragged ? (uint64_t)(a->n_seqs + 1) * 4 : 0, "cu_seqlens"),
                    update ? Range{0, 0, ""} : state_r};
-    rc = check_alias(w, 3, r, 10);
+    rc = check_alias(w, 5, r, 10);
     if (rc) return rc;
 
     const int64_t items = (int64_t)a->n_seqs * a->HV;
@@ -265,6 +276,10 @@ int prepare_recurrent(const kda_recurrent_args *a, RecParams *p, Launch *l)
     p->update_state = update;
     p->vsplit = vsplit;
     p->n_work = (int32_t)(items * vsplit);
+    p->corr = static_cast<float *>(a->correction_cache);
+    p->kg = a->kg_cache;
+    p->kg_f32 = a->kg_dtype == KDA_DTYPE_F32;
+    p->t_max = caches ? a->cache_t_max : 0;
     return ok();
 }
 

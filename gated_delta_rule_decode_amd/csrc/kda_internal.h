@@ -37,6 +37,10 @@ struct RecParams {
     int32_t update_state;        // 0: the pool is read only
     int32_t vsplit;              // workgroups per (sequence, value head)
     int32_t n_work;              // n_seqs * HV * vsplit (grid is padded to a multiple of 8)
+    float *corr;                 // nullptr or fp32 [num_slots][HV][t_max][128]
+    void *kg;                    // nullptr or [num_slots][HV][t_max][256], kg_f32 ? fp32 : bf16
+    int32_t kg_f32;
+    int32_t t_max;
 };
 
 struct FusedParams {

@@ -280,7 +280,7 @@ __device__ __forceinline__ void read_token_ops(TokenOps &t, const float *sq, con
 // One token on one value row held as 8 fp32 values per lane:
 //   s <- d*s;  a = k_hat.s;  c = scale*q_hat.s;  u = v - a;
 //   s <- s + beta*u*k_hat;  o = c + beta*u*scale*(q_hat.k_hat)  (= scale*q_hat.s_new)
-__device__ __forceinline__ float row_update(float s[8], const TokenOps &t, float v)
+__device__ __forceinline__ float row_update(float s[8], const TokenOps &t, float v, float &bu_out)
 {
     float pa = 0.f, pc = 0.f;
 #pragma unroll
@@ -294,7 +294,30 @@ __device__ __forceinline__ float row_update(float s[8], const TokenOps &t, float
     const float bk = bu * t.rk;
 #pragma unroll
     for (int e = 0; e < 8; ++e) s[e] = fmaf(bk, t.k[e], s[e]);
+    bu_out = bu;
     return fmaf(bu, t.qk, pc * t.rqs);
+}
+
+__device__ __forceinline__ float row_update(float s[8], const TokenOps &t, float v)
+{
+    float bu;
+    return row_update(s, t, v, bu);
+}
+
+// Store G consecutive fp32 values (G in {1,2,4,8}) from one lane.
+template <int G>
+__device__ __forceinline__ void store_f32(float *dst, const float *x)
+{
+    if constexpr (G == 8) {
+        reinterpret_cast<f32x4 *>(dst)[0] = f32x4{x[0], x[1], x[2], x[3]};
+        reinterpret_cast<f32x4 *>(dst)[1] = f32x4{x[4], x[5], x[6], x[7]};
+    } else if constexpr (G == 4) {
+        *reinterpret_cast<f32x4 *>(dst) = f32x4{x[0], x[1], x[2], x[3]};
+    } else if constexpr (G == 2) {
+        *reinterpret_cast<float2 *>(dst) = float2{x[0], x[1]};
+    } else {
+        *dst = x[0];
+    }
 }
 
 // One token's channel inputs, held in registers between their load and the
@@ -353,6 +376,23 @@ __device__ __forceinline__ void write_stage(int tid, const StageIn &s, float a_h
             n[1] = pk;
             n[2] = pqk;
         }
+    }
+}
+
+// Verify cache row of one token: [raw key (128) | raw gate (128)], from the
+// staging registers of threads 0..127 (channel tid), as fp32 or bf16.
+__device__ __forceinline__ void store_kg(void *kg, bool kg_f32, int64_t row, int tid, const StageIn &s,
+                                         bool g_f32)
+{
+    const int64_t at = row * (2 * KD) + tid;
+    if (kg_f32) {
+        float *d = static_cast<float *>(kg) + at;
+        d[0] = bf16_bits_to_f32(s.k);
+        d[KD] = input_value(s.g, g_f32);
+    } else {
+        uint16_t *d = static_cast<uint16_t *>(kg) + at;
+        d[0] = (uint16_t)s.k;
+        d[KD] = g_f32 ? (uint16_t)(pack_bf16x2(__uint_as_float(s.g), 0.0f) & 0xffffu) : (uint16_t)s.g;
     }
 }
 
@@ -457,15 +497,20 @@ __global__ void __launch_bounds__(256) kda_recurrent_kernel(const RecParams p)
         __syncthreads();
         TokenOps ops;
         read_token_ops<BF16>(ops, s_q[0], s_k[0], s_d[0], s_norm[0], m, p.scale, p.l2_eps, beta);
-        float o[G];
+        float o[G], c[G];
 #pragma unroll
         for (int gi = 0; gi < G; ++gi) {
             float st[8];
             IO::unpack(raw[gi], st);
-            o[gi] = row_update(st, ops, s_v[0][r_base + gi]);
+            o[gi] = row_update(st, ops, s_v[0][r_base + gi], c[gi]);
             if (update) IO::store(head, off[gi], IO::pack(st));
         }
         if (m == 0) store_out_bf16<G>(p.out + ((int64_t)t0 * p.HV + hv) * KD + r_base, o);
+        if (p.t_max > 0) {
+            const int64_t row = ((int64_t)idx * p.HV + hv) * p.t_max;
+            if (p.corr && m == 0) store_f32<G>(p.corr + row * KD + r_base, c);
+            if (p.kg && vs == 0 && tid < KD) store_kg(p.kg, p.kg_f32 != 0, row, tid, in, g_f32);
+        }
     } else {
         // Token loop: the state stays in registers across the tokens of the
         // sequence; the next token's inputs are fetched while the current one
@@ -480,6 +525,10 @@ __global__ void __launch_bounds__(256) kda_recurrent_kernel(const RecParams p)
             write_stage(tid, in, a_h, g_f32, precomputed, s_q[buf], s_k[buf], s_d[buf], s_v[buf],
                         s_norm[buf]);
             const float beta = beta_of(braw);
+            const int pos = t - t0;
+            const bool cache = pos < p.t_max;  // t_max is 0 without verify caches
+            const int64_t crow = ((int64_t)idx * p.HV + hv) * p.t_max + pos;
+            if (cache && p.kg && vs == 0 && tid < KD) store_kg(p.kg, p.kg_f32 != 0, crow, tid, in, g_f32);
             if (t + 1 < t1) {
                 const int64_t n = t + 1;
                 in = load_stage(tid, p.q + n * p.q_stride + oq, p.k + n * p.k_stride + oq,
@@ -490,10 +539,11 @@ __global__ void __launch_bounds__(256) kda_recurrent_kernel(const RecParams p)
             TokenOps ops;
             read_token_ops<BF16>(ops, s_q[buf], s_k[buf], s_d[buf], s_norm[buf], m, p.scale, p.l2_eps,
                                  beta);
-            float o[G];
+            float o[G], c[G];
 #pragma unroll
-            for (int gi = 0; gi < G; ++gi) o[gi] = row_update(st[gi], ops, s_v[buf][r_base + gi]);
+            for (int gi = 0; gi < G; ++gi) o[gi] = row_update(st[gi], ops, s_v[buf][r_base + gi], c[gi]);
             if (m == 0) store_out_bf16<G>(p.out + ((int64_t)t * p.HV + hv) * KD + r_base, o);
+            if (cache && p.corr && m == 0) store_f32<G>(p.corr + crow * KD + r_base, c);
             if (p.ckpt) {
                 char *ck = reinterpret_cast<char *>(p.ckpt) + ((int64_t)t * p.HV + hv) * (KD * KD) * es;
 #pragma unroll

@@ -52,7 +52,7 @@ extern "C" {
 #endif
 
 #define KDA_API __attribute__((visibility("default")))
-#define KDA_ABI_VERSION 2
+#define KDA_ABI_VERSION 3
 #define KDA_HEAD_DIM 128
 
 typedef enum kda_status {
@@ -144,6 +144,21 @@ typedef struct kda_launch_plan {
  *  tokens_per_seq    without cu_seqlens: 0 or 1 is T=1, T > 1 is the uniform
  *                    batched form (sequence i owns tokens [i*T, (i+1)*T)).
  *  flags             KDA_FLAG_NO_STATE_UPDATE: the pool is only read.
+ *  correction_cache  NULL or fp32 [num_slots, HV, cache_t_max, 128], contiguous,
+ *                    16-byte aligned ("Frozen / speculative-verify mode":
+ *                    slot-indexed per-token delta-rule corrections): for token
+ *                    j of a live sequence in slot s, [s, hv, j, :] receives
+ *                    beta * u, the vector the update adds along k_hat
+ *                    (S_j = D_j S_{j-1} + k_hat_j c_j^T).
+ *  kg_cache          NULL or [num_slots, HV, cache_t_max, 256] of kg_dtype,
+ *                    contiguous: [s, hv, j, 0:128] the raw key of the value
+ *                    head's q/k head (before L2 normalisation), [.., 128:256]
+ *                    the raw gate as given (the log-decay when PRECOMPUTED).
+ *                    Positions j >= cache_t_max are not recorded; null and
+ *                    empty sequences record nothing.
+ *  kg_dtype          kda_dtype of kg_cache (fp32 keeps fp32 gates exactly).
+ *  cache_t_max       tokens recorded per (slot, value head), >= 1 when a cache
+ *                    is given.
  */
 typedef struct kda_recurrent_args {
     uint32_t struct_size;
@@ -182,6 +197,10 @@ typedef struct kda_recurrent_args {
     int32_t beta_dtype;
     int32_t tokens_per_seq;
     uint32_t flags;
+    void *correction_cache;
+    void *kg_cache;
+    int32_t kg_dtype;
+    int32_t cache_t_max;
 } kda_recurrent_args;
 
 /*

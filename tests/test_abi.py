@@ -30,7 +30,7 @@ def test_header_symbols_exported():
 
 def test_version_and_status_strings():
     L = lib()
-    assert L.kda_version() == 2
+    assert L.kda_version() == 3
     for code in _lib.STATUS:
         assert L.kda_status_string(code).decode()
     assert L.kda_status_string(12345).decode() == "unknown status"
@@ -332,3 +332,35 @@ def test_read_only_pool_still_may_not_alias_outputs():
     a.flags = 1
     a.out = a.state
     expect(plan_rec(a), -6, "state")
+
+
+def with_caches(a, t_max=4, kg_dtype=0, corr=True, kg=True):
+    A = Arena()
+    A.next = 1 << 40  # far from rec_args' buffers
+    rows = a.num_slots * a.HV * t_max
+    a.correction_cache = A.take(rows * D * 4) if corr else None
+    a.kg_cache = A.take(rows * 2 * D * (4 if kg_dtype == 0 else 2)) if kg else None
+    a.kg_dtype, a.cache_t_max = kg_dtype, t_max
+    return a
+
+
+def test_verify_cache_rules():
+    for kw in ({}, {"kg_dtype": 1}, {"corr": False}, {"kg": False}):
+        a = with_caches(rec_args(varlen=True, T=8), **kw)
+        a.flags = 1
+        assert plan_rec(a)[0] == 0, (kw, err())
+    assert plan_rec(with_caches(rec_args()))[0] == 0, err()  # T=1 with caches
+    expect(plan_rec(with_caches(rec_args(), t_max=0)), -2, "cache_t_max")
+    expect(plan_rec(with_caches(rec_args(), kg_dtype=7)), -3, "kg_dtype")
+    a = with_caches(rec_args())
+    a.correction_cache += 4
+    expect(plan_rec(a), -5, "correction_cache")
+    a = with_caches(rec_args())
+    a.correction_cache = a.state  # a cache may not overlap the pool
+    expect(plan_rec(a), -6, "state")
+    a = with_caches(rec_args())
+    a.kg_cache = a.correction_cache + 64  # nor the other cache
+    expect(plan_rec(a), -6, "cache")
+    a = with_caches(rec_args(), corr=False)
+    a.kg_cache = a.q  # nor an input
+    expect(plan_rec(a), -6, "kg_cache")
