@@ -256,3 +256,53 @@ def ragged_lengths(seed, n_seqs, lo=0, hi=6):
     gen = _gen(seed, "cpu")
     return torch.randint(lo, hi + 1, (n_seqs,), generator=gen).tolist()
 
+
+
+@dataclass
+class PackedFusedCase:
+    x: torch.Tensor            # bf16 [rows, 3*H*128] (rows = sum(lengths) + pad_rows)
+    weight: torch.Tensor       # fp32 [3, 4, H*128]
+    conv_state: torch.Tensor   # bf16 [num_slots, 3*H*128, 3], strides [ss, 1, 3*H*128]
+    raw_gate: torch.Tensor     # bf16 [rows, H, 128]
+    raw_beta: torch.Tensor     # bf16 [rows, H]
+    A_log: torch.Tensor
+    dt_bias: torch.Tensor
+    state_indices: torch.Tensor        # int32 [N, max_tokens]
+    query_start_loc: torch.Tensor      # int32 [N+1]
+    num_accepted_tokens: torch.Tensor  # int32 [N], 1..max_tokens
+    state: torch.Tensor        # [num_slots, H, 128, 128]
+    output_gate: torch.Tensor  # bf16 [rows, H, 128]
+    norm_weight: torch.Tensor  # fp32 [128]
+    lengths: list
+
+
+def packed_fused_case(seed, *, lengths, H, num_slots, max_tokens=None, state_dtype=torch.float32,
+                      device="cpu", accepted="random", pad_rows=0, slot_pad=0):
+    """Packed speculative rows: sequence i owns lengths[i] consecutive rows;
+    every (sequence, column) gets its own slot from [1, num_slots) (so no
+    two sequences share a slot); num_accepted_tokens ~ U{1..max_tokens}
+    ("random") or all 1 ("one"); pad_rows trailing rows belong to no
+    sequence."""
+    N = len(lengths)
+    T_max = int(max_tokens or max(max(lengths), 1))
+    rows = int(sum(lengths)) + pad_rows
+    gen = _gen(seed, device)
+    C = 3 * H * D
+    x = _randn(gen, (rows, C), device)
+    weight = _randn(gen, (3, 4, H * D), device, 0.5, torch.float32)
+    cs = conv_cache(gen, num_slots, C, device, slot_pad)
+    raw_gate = _randn(gen, (rows, H, D), device)
+    raw_beta = _randn(gen, (rows, H), device)
+    A_log, dt_bias = gate_params(gen, H, device)
+    idx = unique_slots(gen, N * T_max, 1, num_slots, device).reshape(N, T_max)
+    if accepted == "random":
+        acc = torch.randint(1, T_max + 1, (N,), generator=gen, device=device).to(torch.int32)
+    else:
+        acc = torch.ones(N, dtype=torch.int32, device=device)
+    qsl = torch.zeros(N + 1, dtype=torch.int32)
+    qsl[1:] = torch.cumsum(torch.tensor(lengths, dtype=torch.int64), 0).to(torch.int32)
+    state = _randn_big(gen, (num_slots, H, D, D), device, 0.05, state_dtype)
+    ogate = _randn(gen, (rows, H, D), device)
+    norm_weight = _uniform(gen, (D,), device, 0.5, 1.5)
+    return PackedFusedCase(x, weight, cs, raw_gate, raw_beta, A_log, dt_bias, idx, qsl.to(device),
+                           acc, state, ogate, norm_weight, list(lengths))

@@ -66,6 +66,9 @@ def _load(path=None):
         lib.kdao_fused.restype = Int
         lib.kdao_fused.argtypes = [I64, I64, P, P, I64, P, I64, P, P, P, P, P, Int, P,
                                    P, P, Dbl, Dbl, Dbl, P, P, P, P]
+        lib.kdao_packed_fused.restype = Int
+        lib.kdao_packed_fused.argtypes = [I64, I64, I64, I64, P, P, I64, P, I64, P, P, P, P, P, P,
+                                          P, Int, P, P, P, Dbl, Dbl, Dbl, P, P, P, P, P]
         lib.kdao_bf16_from_f64_n.restype = None
         lib.kdao_bf16_from_f64_n.argtypes = [P, P, I64]
         _lib = lib
@@ -266,3 +269,51 @@ def fused(x, weight, conv_state, raw_gate, raw_beta, A_log, dt_bias, state_indic
         raise ValueError(f"kdao_fused rejected its arguments ({rc})")
     return dict(out64=out64, out_bf16=outb, o_pre64=opre, act64=act, state=st,
                 conv_state=np.transpose(cs, (0, 2, 1)))
+
+
+def packed_fused(x, weight, conv_state, raw_gate, raw_beta, A_log, dt_bias, state_indices,
+                 state, output_gate, norm_weight, *, query_start_loc, num_accepted_tokens,
+                 norm_eps=1e-5, scale=SCALE, l2_eps=L2_EPS, want_ckpt64=False):
+    """Packed fused decode with T >= 1 tokens per sequence.
+
+    x [rows, 3*H*128]; raw_gate [rows, H, 128]; raw_beta [rows, H];
+    output_gate [rows, H, 128]; state_indices int32 [N, max_tokens] (column j:
+    the slot for the checkpoint after token j; the sequence starts from column
+    num_accepted_tokens[i] - 1); query_start_loc int32 [N+1]; conv_state the
+    logical [slots, 3*H*128, 3] cache.  Returns dict(out64, out_bf16,
+    o_pre64, act64, state, conv_state, ckpt64).
+    """
+    xa = _c(x, np.uint16)
+    rows, C3 = xa.shape
+    H = C3 // (3 * D)
+    cs_log = as_np(conv_state)
+    cs = np.ascontiguousarray(np.transpose(cs_log, (0, 2, 1)))  # [slots, 3, C3]
+    st = np.array(as_np(state), copy=True, order="C")
+    sdt = _dtype_code(st)
+    w = _c(weight, np.float32)
+    gr = _c(as_np(raw_gate).reshape(rows, H, D), np.uint16)
+    br = _c(as_np(raw_beta).reshape(rows, H), np.uint16)
+    og = _c(as_np(output_gate).reshape(rows, H, D), np.uint16)
+    nw = _c(norm_weight, np.float32)
+    si = _c(state_indices, np.int32)
+    if si.ndim == 1:
+        si = si.reshape(-1, 1)
+    N, max_tokens = si.shape
+    qsl = _c(query_start_loc, np.int32)
+    acc = _c(num_accepted_tokens, np.int32)
+    assert qsl.shape == (N + 1,) and acc.shape == (N,)
+    A_log = _c(A_log, np.float32); dt_bias = _c(dt_bias, np.float32)
+    out64 = np.zeros((rows, H, D), np.float64)
+    outb = np.zeros((rows, H, D), np.uint16)
+    opre = np.zeros((rows, H, D), np.float64)
+    act = np.zeros((rows, C3), np.float64)
+    ck64 = np.zeros((rows, H, D, D), np.float64) if want_ckpt64 else None
+    rc = _load().kdao_packed_fused(rows, N, H, max_tokens, _ptr(xa), _ptr(w), cs.shape[0], _ptr(cs),
+                                   3 * C3, _ptr(gr), _ptr(br), _ptr(A_log), _ptr(dt_bias), _ptr(si),
+                                   _ptr(qsl), _ptr(acc), sdt, _ptr(st), _ptr(og), _ptr(nw),
+                                   float(norm_eps), float(scale), float(l2_eps), _ptr(out64),
+                                   _ptr(outb), _ptr(opre), _ptr(act), _ptr(ck64))
+    if rc != 0:
+        raise ValueError(f"kdao_packed_fused rejected its arguments ({rc})")
+    return dict(out64=out64, out_bf16=outb, o_pre64=opre, act64=act, state=st,
+                conv_state=np.transpose(cs, (0, 2, 1)), ckpt64=ck64)

@@ -450,6 +450,130 @@ int kdao_fused(int64_t rows, int64_t H, const uint16_t *x, const float *weight,
     return 0;
 }
 
+/*
+ * Packed fused decode with T >= 1 tokens per sequence ("feat(kda): add fused
+ * speculative decode kernel": packed ragged rows from query_start_loc,
+ * caches updated from accepted-token metadata, per-token conv and state
+ * checkpoints, empty and padding rows; the bf16-pool follow-up: the
+ * recurrence stays unrounded across the token loop and each checkpoint is
+ * rounded when stored).
+ *
+ * Readings (the pages give the signature and these behaviours, not the
+ * index arithmetic):
+ *  - sequence i owns packed rows [qsl[i], qsl[i+1]) (clipped to the rows);
+ *  - state_indices is [n_seqs][max_tokens]: column j names the slot that
+ *    receives the conv window and the state after token j; the sequence
+ *    starts from the slot of column a-1, a = num_accepted[i] (the last
+ *    accepted checkpoint of the previous step);
+ *  - a start slot that is <= 0, >= num_slots, or a outside 1..max_tokens
+ *    makes the sequence null: its rows give +0 and nothing is written;
+ *  - a checkpoint column <= 0 or >= num_slots (or a token j >= max_tokens)
+ *    is padding: that token writes no cache, the loop goes on;
+ *  - rows that belong to no sequence give +0.
+ * conv_state is position-major [slots][3][3*H*128] (the fused call's
+ * layout); ckpt64 (optional) receives the unrounded state after each token,
+ * pool layout [row][h][v][k].
+ */
+int kdao_packed_fused(int64_t n_rows, int64_t n_seqs, int64_t H, int64_t max_tokens,
+                      const uint16_t *x, const float *weight,
+                      int64_t num_slots, uint16_t *conv_state, int64_t conv_slot_stride,
+                      const uint16_t *graw, const uint16_t *braw,
+                      const float *A_log, const float *dt_bias,
+                      const int32_t *state_indices, const int32_t *query_start_loc,
+                      const int32_t *num_accepted, int state_dtype, void *state,
+                      const uint16_t *ogate, const float *norm_weight, double norm_eps,
+                      double scale, double l2_eps,
+                      double *out64, uint16_t *out_bf16, double *o_pre64, double *act64,
+                      double *ckpt64)
+{
+    if (n_rows < 0 || n_seqs < 0 || H <= 0 || max_tokens < 1) return -1;
+    const int64_t HC = H * KD;
+    const int64_t C3 = 3 * HC;
+    if (conv_slot_stride < 3 * C3) return -1;
+    const size_t head_elems = (size_t)KD * KD;
+
+    /* every row starts as +0; live sequences overwrite theirs */
+    for (size_t i = 0; i < (size_t)n_rows * HC; ++i) {
+        if (out64) out64[i] = 0.0;
+        if (out_bf16) out_bf16[i] = 0;
+        if (o_pre64) o_pre64[i] = 0.0;
+    }
+    if (act64) memset(act64, 0, sizeof(double) * (size_t)n_rows * C3);
+    if (ckpt64) memset(ckpt64, 0, sizeof(double) * (size_t)n_rows * H * head_elems);
+
+    double (*S)[KD][KD] = malloc(sizeof(double) * (size_t)H * head_elems);
+    uint16_t *win = malloc(sizeof(uint16_t) * 3 * (size_t)C3);  /* [3][C3], oldest first */
+    double *act = malloc(sizeof(double) * (size_t)C3);
+    if (!S || !win || !act) { free(S); free(win); free(act); return -2; }
+    double qh[KD], kh[KD], gv[KD], dec[KD], o[KD];
+
+    for (int64_t i = 0; i < n_seqs; ++i) {
+        int64_t t0 = query_start_loc[i], t1 = query_start_loc[i + 1];
+        t0 = t0 < 0 ? 0 : (t0 > n_rows ? n_rows : t0);
+        t1 = t1 < t0 ? t0 : (t1 > n_rows ? n_rows : t1);
+        const int32_t *cols = state_indices + (size_t)i * max_tokens;
+        int32_t a = num_accepted[i];
+        int32_t src = (a >= 1 && a <= max_tokens) ? cols[a - 1] : -1;
+        if (src <= 0 || (int64_t)src >= num_slots || t1 <= t0) continue;
+
+        /* the accepted checkpoint: conv window and every head's state */
+        memcpy(win, conv_state + (size_t)src * conv_slot_stride, sizeof(uint16_t) * 3 * (size_t)C3);
+        for (int64_t h = 0; h < H; ++h)
+            gather_state(state, state_dtype, ((size_t)src * H + h) * head_elems, S[h]);
+
+        for (int64_t r = t0; r < t1; ++r) {
+            const int64_t j = r - t0;  /* token position inside the sequence */
+            /* conv over [window, x_r], SiLU; the window advances by x_r */
+            for (int64_t c = 0; c < C3; ++c) {
+                int64_t grp = c / HC, cc = c % HC;
+                double hist[4] = {bf16_to_f64(win[c]), bf16_to_f64(win[C3 + c]),
+                                  bf16_to_f64(win[2 * C3 + c]), bf16_to_f64(x[(size_t)r * C3 + c])};
+                double y = 0.0;
+                for (int t = 0; t < 4; ++t) y += (double)weight[(grp * 4 + t) * HC + cc] * hist[t];
+                act[c] = y * sigmoid(y);
+                win[c] = win[C3 + c];
+                win[C3 + c] = win[2 * C3 + c];
+                win[2 * C3 + c] = x[(size_t)r * C3 + c];
+            }
+            if (act64) memcpy(act64 + (size_t)r * C3, act, sizeof(double) * (size_t)C3);
+            for (int64_t h = 0; h < H; ++h) {
+                size_t vec = ((size_t)r * H + h) * KD;
+                widen_bf16(graw + vec, gv, KD);
+                double beta = sigmoid(bf16_to_f64(braw[(size_t)r * H + h]));
+                l2_normalise(act + h * KD, l2_eps, qh);
+                l2_normalise(act + HC + h * KD, l2_eps, kh);
+                gate_decay(gv, (double)A_log[h], dt_bias + h * KD, dec);
+                kda_token(S[h], qh, kh, act + 2 * HC + h * KD, dec, beta, scale, o, NULL);
+                double ms = 0.0;
+                for (int v = 0; v < KD; ++v) ms += o[v] * o[v];
+                double inv = 1.0 / sqrt(ms / (double)KD + norm_eps);
+                for (int v = 0; v < KD; ++v) {
+                    double y = o[v] * inv * (double)norm_weight[v] * sigmoid(bf16_to_f64(ogate[vec + v]));
+                    if (out64) out64[vec + v] = y;
+                    if (out_bf16) out_bf16[vec + v] = kdao_bf16_from_f64(y);
+                    if (o_pre64) o_pre64[vec + v] = o[v];
+                }
+                if (ckpt64) {
+                    double *ck = ckpt64 + ((size_t)r * H + h) * head_elems;
+                    for (int v = 0; v < KD; ++v)
+                        for (int k = 0; k < KD; ++k) ck[(size_t)v * KD + k] = S[h][k][v];
+                }
+            }
+            /* checkpoint of token j: window and state (rounded on store) */
+            int32_t dst = j < max_tokens ? cols[j] : -1;
+            if (dst > 0 && (int64_t)dst < num_slots) {
+                memcpy(conv_state + (size_t)dst * conv_slot_stride, win, sizeof(uint16_t) * 3 * (size_t)C3);
+                for (int64_t h = 0; h < H; ++h)
+                    scatter_state(state, state_dtype, ((size_t)dst * H + h) * head_elems, S[h]);
+            }
+        }
+    }
+    free(S);
+    free(win);
+    free(act);
+    return 0;
+}
+
 /* Element-wise kdao_bf16_from_f64 over an array (test helper). */
 void kdao_bf16_from_f64_n(const double *x, uint16_t *out, int64_t n)
 {

@@ -12,6 +12,7 @@ import subprocess
 import pytest
 
 import oracle
+from tests import test_oracle_packed_fused as pf
 from tests import test_oracle_pins as pins
 
 MUTANTS = [
@@ -56,6 +57,24 @@ MUTANTS = [
     ("rms uses sum", "ms /= (double)KD;", "ms /= 1.0;"),
     ("norm gate not squashed", "sigmoid(bf16_to_f64(ogate[vec + j]))", "bf16_to_f64(ogate[vec + j])"),
     ("fused slot 0 live", "int null_row = idx <= 0 ||", "int null_row = idx < 0 ||"),
+    ("packed fused starts from column 0",
+     "int32_t src = (a >= 1 && a <= max_tokens) ? cols[a - 1] : -1;",
+     "int32_t src = (a >= 1 && a <= max_tokens) ? cols[0] : -1;"),
+    ("packed fused conv window not advanced", "                win[c] = win[C3 + c];\n",
+     "                win[c] = win[c];\n"),
+    ("packed fused checkpoint columns reversed", "int32_t dst = j < max_tokens ? cols[j] : -1;",
+     "int32_t dst = j < max_tokens ? cols[max_tokens - 1 - j] : -1;"),
+    ("packed fused state re-read every token",
+     "        for (int64_t r = t0; r < t1; ++r) {\n            const int64_t j = r - t0;",
+     "        for (int64_t r = t0; r < t1; ++r) {\n            for (int64_t h = 0; h < H; ++h)\n"
+     "                gather_state(state, state_dtype, ((size_t)src * H + h) * head_elems, S[h]);\n"
+     "            const int64_t j = r - t0;"),
+    ("packed fused padding rows not zero", "        if (out64) out64[i] = 0.0;", "        if (out64) out64[i] = 1.0;"),
+    ("packed fused slot 0 live", "if (src <= 0 || (int64_t)src >= num_slots || t1 <= t0) continue;",
+     "if (src < 0 || (int64_t)src >= num_slots || t1 <= t0) continue;"),
+    ("packed fused checkpoint skips slot filter",
+     "if (dst > 0 && (int64_t)dst < num_slots) {\n                memcpy",
+     "if (dst >= 0 && (int64_t)dst < num_slots) {\n                memcpy"),
     ("bf16 rounding truncates", "double q = nearbyint(m * 256.0);", "double q = trunc(m * 256.0);"),
     ("bf16 ties away", "double q = nearbyint(m * 256.0);", "double q = round(m * 256.0);"),
 ]
@@ -84,6 +103,13 @@ PINS = [
     lambda: pins.test_verify_caches_rebuild_every_checkpoint("in_kernel"),
     lambda: pins.test_verify_caches_rebuild_every_checkpoint("precomputed"),
     pins.test_verify_caches_positions_and_null_rows,
+    pf.test_chain_of_single_token_fused_calls,
+    pf.test_single_token_rows_equal_the_fused_call,
+    pf.test_conv_window_runs_across_tokens,
+    pf.test_frozen_state_checkpoints_and_readout,
+    pf.test_unit_decay_beta_one_stores_every_value,
+    pf.test_bf16_checkpoints_round_an_unrounded_carry,
+    pf.test_padding_null_sequences_and_checkpoint_columns,
 ]
 
 
