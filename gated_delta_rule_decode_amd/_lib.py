@@ -74,9 +74,22 @@ class FusedArgs(ctypes.Structure):
     ]
 
 
-EXPORTS = ["kda_recurrent", "kda_packed_decode", "kda_fused_decode", "kda_recurrent_plan",
-           "kda_packed_plan", "kda_fused_plan", "kda_status_string", "kda_last_error",
-           "kda_version", "kda_check_device"]
+class PackedFusedArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", _U32), ("n_rows", _I32), ("n_seqs", _I32), ("H", _I32), ("max_tokens", _I32),
+        ("x", _P), ("x_stride", _I64), ("weight", _P), ("conv_state", _P),
+        ("conv_slot_stride", _I64), ("raw_gate", _P), ("gate_stride", _I64), ("raw_beta", _P),
+        ("beta_stride", _I64), ("A_log", _P), ("dt_bias", _P), ("gate_mode", _I32),
+        ("lower_bound", _F32), ("state_indices", _P), ("indices_stride", _I64),
+        ("query_start_loc", _P), ("num_accepted_tokens", _P), ("state", _P), ("state_dtype", _I32),
+        ("num_slots", _I64), ("slot_stride", _I64), ("output_gate", _P), ("ogate_stride", _I64),
+        ("norm_weight", _P), ("norm_eps", _F32), ("out", _P),
+    ]
+
+
+EXPORTS = ["kda_recurrent", "kda_packed_decode", "kda_fused_decode", "kda_packed_fused_decode",
+           "kda_recurrent_plan", "kda_packed_plan", "kda_fused_plan", "kda_packed_fused_plan",
+           "kda_status_string", "kda_last_error", "kda_version", "kda_check_device"]
 
 _lib = None
 
@@ -98,6 +111,8 @@ def load(path: str = LIB_PATH):
                        ("kda_recurrent_plan", [ctypes.POINTER(RecurrentArgs), ctypes.POINTER(LaunchPlan)]),
                        ("kda_packed_plan", [ctypes.POINTER(PackedArgs), ctypes.POINTER(LaunchPlan)]),
                        ("kda_fused_plan", [ctypes.POINTER(FusedArgs), ctypes.POINTER(LaunchPlan)]),
+                       ("kda_packed_fused_decode", [ctypes.POINTER(PackedFusedArgs), _P]),
+                       ("kda_packed_fused_plan", [ctypes.POINTER(PackedFusedArgs), ctypes.POINTER(LaunchPlan)]),
                        ("kda_check_device", [ctypes.c_int])):
         fn = getattr(lib, name)
         fn.argtypes = argt

@@ -259,23 +259,14 @@ def packed_kda_decode(mixed_qkv, raw_gate, raw_beta, A_log, dt_bias, state, stat
     return output
 
 
-def fused_kda_decode(x, weight, conv_state, raw_gate, raw_beta, A_log, dt_bias, state_indices,
-                     state, output_gate, norm_weight, lower_bound=None, norm_eps=1e-5, output=None):
-    """Fused decode ("flashinfer.kda_decode.fused_kda_decode"): width-4
-    depthwise causal conv + SiLU over x, one KDA update, gated RMSNorm.
-
-    x bf16 [rows, 3*H*128]; weight fp32 [3, 4, H*128]; conv_state bf16
-    [num_slots, 3*H*128, 3] with strides [slot_stride, 1, 3*H*128]; raw_gate
-    bf16 [1, rows, H, 128] or [rows, H, 128]; raw_beta bf16 [1, rows, H] or
-    [rows, H]; state_indices int32 [rows] (non-positive = null); state
-    [num_slots, H, 128, 128] fp32/bf16; output_gate bf16 [rows, H, 128] or
-    [1, rows, H, 128]; norm_weight fp32 [128].  Returns bf16 [1, rows, H, 128].
-    """
+def _fused_inputs(x, weight, conv_state, raw_gate, raw_beta, A_log, dt_bias, state, output_gate,
+                  norm_weight, norm_eps, output):
+    """Checks shared by the fused calls; returns (H, rows, raw_gate, raw_beta,
+    output_gate as [rows, width] views, output)."""
     H = A_log.numel()
     HC = H * D
     rows = x.shape[0]
     _check_pool(state, H)
-    _check_indices(state_indices, rows)
     _need(x.dtype == torch.bfloat16 and x.dim() == 2 and x.shape[1] == 3 * HC and x.stride(1) == 1,
           "x must be bf16 [rows, 3*H*128] with contiguous channels")
     _need(weight.dtype == torch.float32 and weight.is_contiguous() and tuple(weight.shape) == (3, 4, HC),
@@ -307,6 +298,24 @@ def fused_kda_decode(x, weight, conv_state, raw_gate, raw_beta, A_log, dt_bias, 
     else:
         _need(output.dtype == torch.bfloat16 and output.is_contiguous() and output.numel() == rows * HC,
               "output must be contiguous bf16 [1, rows, H, 128]")
+    return H, rows, rg, rb, og, output
+
+
+def fused_kda_decode(x, weight, conv_state, raw_gate, raw_beta, A_log, dt_bias, state_indices,
+                     state, output_gate, norm_weight, lower_bound=None, norm_eps=1e-5, output=None):
+    """Fused decode ("flashinfer.kda_decode.fused_kda_decode"): width-4
+    depthwise causal conv + SiLU over x, one KDA update, gated RMSNorm.
+
+    x bf16 [rows, 3*H*128]; weight fp32 [3, 4, H*128]; conv_state bf16
+    [num_slots, 3*H*128, 3] with strides [slot_stride, 1, 3*H*128]; raw_gate
+    bf16 [1, rows, H, 128] or [rows, H, 128]; raw_beta bf16 [1, rows, H] or
+    [rows, H]; state_indices int32 [rows] (non-positive = null); state
+    [num_slots, H, 128, 128] fp32/bf16; output_gate bf16 [rows, H, 128] or
+    [1, rows, H, 128]; norm_weight fp32 [128].  Returns bf16 [1, rows, H, 128].
+    """
+    H, rows, rg, rb, og, output = _fused_inputs(x, weight, conv_state, raw_gate, raw_beta, A_log, dt_bias,
+                                                state, output_gate, norm_weight, norm_eps, output)
+    _check_indices(state_indices, rows)
     gm, lb = _gate_mode(lower_bound)
     a = _lib.FusedArgs()
     a.struct_size = ctypes.sizeof(_lib.FusedArgs)
@@ -327,4 +336,55 @@ def fused_kda_decode(x, weight, conv_state, raw_gate, raw_beta, A_log, dt_bias, 
     lib = _lib.load()
     with torch.cuda.device(x.device):
         _lib.check(lib.kda_fused_decode(ctypes.byref(a), _stream(x.device)))
+    return output
+
+
+def packed_fused_kda_decode(x, weight, conv_state, raw_gate, raw_beta, A_log, dt_bias, state_indices,
+                            state, output_gate, norm_weight, lower_bound=None, norm_eps=1e-5, output=None,
+                            *, query_start_loc, num_accepted_tokens):
+    """Packed fused decode with T >= 1 tokens per sequence ("feat(kda): add
+    fused speculative decode kernel").
+
+    The fused step (conv + SiLU, KDA, gated RMSNorm) over packed rows: x
+    [rows, 3*H*128], raw_gate, raw_beta, output_gate per row as in
+    fused_kda_decode.  ``query_start_loc`` int32 [N+1] (non-decreasing): the
+    rows of sequence i; ``state_indices`` int32 [N, max_tokens] (or [N]):
+    column j is the slot that receives the conv window and the state after
+    token j (non-positive: not written); ``num_accepted_tokens`` int32 [N]:
+    sequence i starts from the slot in column num_accepted_tokens[i] - 1 (a
+    non-positive start slot makes the sequence null).  Rows of null sequences
+    and rows outside every sequence give zeros.  A bf16 pool holds each
+    checkpoint rounded; the recurrence itself stays fp32 across the tokens.
+    Returns bf16 [1, rows, H, 128].
+    """
+    H, rows, rg, rb, og, output = _fused_inputs(x, weight, conv_state, raw_gate, raw_beta, A_log, dt_bias,
+                                                state, output_gate, norm_weight, norm_eps, output)
+    si = state_indices if state_indices.dim() == 2 else state_indices.reshape(-1, 1)
+    _need(si.dtype == torch.int32 and si.is_cuda and si.dim() == 2 and si.stride(1) == 1,
+          "state_indices must be an int32 device tensor [N, max_tokens] with contiguous columns")
+    N, max_tokens = si.shape
+    for name, t, n in (("query_start_loc", query_start_loc, N + 1), ("num_accepted_tokens", num_accepted_tokens, N)):
+        _need(t.dtype == torch.int32 and t.is_cuda and t.is_contiguous() and t.numel() == n,
+              f"{name} must be a contiguous int32 device tensor with {n} elements")
+    gm, lb = _gate_mode(lower_bound)
+    a = _lib.PackedFusedArgs()
+    a.struct_size = ctypes.sizeof(_lib.PackedFusedArgs)
+    a.n_rows, a.n_seqs, a.H, a.max_tokens = rows, N, H, max_tokens
+    a.x, a.x_stride = _ptr(x), x.stride(0)
+    a.weight = _ptr(weight)
+    a.conv_state, a.conv_slot_stride = _ptr(conv_state), conv_state.stride(0)
+    a.raw_gate, a.gate_stride = _ptr(rg), rg.stride(0)
+    a.raw_beta, a.beta_stride = _ptr(rb), rb.stride(0)
+    a.A_log, a.dt_bias = _ptr(A_log), _ptr(dt_bias)
+    a.gate_mode, a.lower_bound = gm, lb
+    a.state_indices, a.indices_stride = _ptr(si), si.stride(0)
+    a.query_start_loc, a.num_accepted_tokens = _ptr(query_start_loc), _ptr(num_accepted_tokens)
+    a.state, a.state_dtype = _ptr(state), _state_dtype(state)
+    a.num_slots, a.slot_stride = state.shape[0], state.stride(0)
+    a.output_gate, a.ogate_stride = _ptr(og), og.stride(0)
+    a.norm_weight, a.norm_eps = _ptr(norm_weight), float(norm_eps)
+    a.out = _ptr(output)
+    lib = _lib.load()
+    with torch.cuda.device(x.device):
+        _lib.check(lib.kda_packed_fused_decode(ctypes.byref(a), _stream(x.device)))
     return output

@@ -411,6 +411,102 @@ int prepare_fused(const kda_fused_args *a, FusedParams *p, Launch *l)
     return ok();
 }
 
+// --------------------------------------------------------- packed fused ----
+
+int prepare_packed_fused(const kda_packed_fused_args *a, PackedFusedParams *p, Launch *l)
+{
+    if (!a) return fail(KDA_ERR_NULLPTR, "args is NULL");
+    if (a->struct_size != sizeof(kda_packed_fused_args))
+        return fail(KDA_ERR_ABI, "struct_size %u != %zu", a->struct_size, sizeof(kda_packed_fused_args));
+    if (a->H < 1) return fail(KDA_ERR_SHAPE, "H=%d must be >= 1", a->H);
+    if (a->n_seqs < 1) return fail(KDA_ERR_SHAPE, "n_seqs=%d must be >= 1", a->n_seqs);
+    if (a->n_rows < 0) return fail(KDA_ERR_SHAPE, "n_rows=%d < 0", a->n_rows);
+    if (a->max_tokens < 1) return fail(KDA_ERR_SHAPE, "max_tokens=%d must be >= 1", a->max_tokens);
+    int rc = check_gate(a->gate_mode);
+    if (rc) return rc;
+    if (!a->weight || !a->conv_state || !a->A_log || !a->dt_bias || !a->state_indices ||
+        !a->query_start_loc || !a->num_accepted_tokens || !a->state || !a->norm_weight)
+        return fail(KDA_ERR_NULLPTR, "a required pointer is NULL");
+    if (a->n_rows > 0 && (!a->x || !a->raw_gate || !a->raw_beta || !a->output_gate || !a->out))
+        return fail(KDA_ERR_NULLPTR, "a required per-row pointer is NULL");
+    const int64_t HC = (int64_t)a->H * KD;
+    const int64_t C3 = 3 * HC;
+    if (a->x_stride < C3) return fail(KDA_ERR_STRIDE, "x_stride must be >= 3*H*128");
+    if (a->conv_slot_stride < 3 * C3) return fail(KDA_ERR_STRIDE, "conv_slot_stride must be >= 3*3*H*128");
+    if (a->gate_stride < HC || a->ogate_stride < HC)
+        return fail(KDA_ERR_STRIDE, "raw_gate/output_gate row strides must be >= H*128");
+    if (a->beta_stride < a->H) return fail(KDA_ERR_STRIDE, "beta_stride must be >= H");
+    if (a->indices_stride < a->max_tokens) return fail(KDA_ERR_STRIDE, "indices_stride must be >= max_tokens");
+    if (!(a->norm_eps >= 0.0f)) return fail(KDA_ERR_SHAPE, "norm_eps must be >= 0");
+    if (!aligned2(a->x) || !aligned2(a->conv_state) || !aligned2(a->raw_gate) || !aligned2(a->raw_beta) ||
+        !aligned2(a->output_gate) || !aligned4(a->weight) || !aligned4(a->A_log) || !aligned4(a->dt_bias) ||
+        !aligned4(a->norm_weight) || !aligned4(a->state_indices) || !aligned4(a->query_start_loc) ||
+        !aligned4(a->num_accepted_tokens))
+        return fail(KDA_ERR_ALIGN, "inputs must be aligned to their element size");
+    if (!aligned16(a->out)) return fail(KDA_ERR_ALIGN, "out must be 16-byte aligned");
+    rc = check_pool(a->state, a->state_dtype, a->num_slots, a->slot_stride, a->H);
+    if (rc) return rc;
+    const int64_t R = a->n_rows;
+    const int64_t N = a->n_seqs;
+    Range w[3] = {span(a->out, (uint64_t)R * HC * 2, "out"),
+                  span(a->state, pool_bytes(a->state_dtype, a->num_slots, a->slot_stride, a->H), "state"),
+                  span(a->conv_state, rows_extent(a->num_slots, a->conv_slot_stride, 3 * C3) * 2,
+                       "conv_state")};
+    Range r[12] = {span(a->x, rows_extent(R, a->x_stride, C3) * 2, "x"),
+                   span(a->weight, (uint64_t)12 * HC * 4, "weight"),
+                   span(a->raw_gate, rows_extent(R, a->gate_stride, HC) * 2, "raw_gate"),
+                   span(a->raw_beta, rows_extent(R, a->beta_stride, a->H) * 2, "raw_beta"),
+                   span(a->A_log, (uint64_t)a->H * 4, "A_log"),
+                   span(a->dt_bias, (uint64_t)HC * 4, "dt_bias"),
+                   span(a->state_indices, rows_extent(N, a->indices_stride, a->max_tokens) * 4, "state_indices"),
+                   span(a->query_start_loc, (uint64_t)(N + 1) * 4, "query_start_loc"),
+                   span(a->num_accepted_tokens, (uint64_t)N * 4, "num_accepted_tokens"),
+                   span(a->output_gate, rows_extent(R, a->ogate_stride, HC) * 2, "output_gate"),
+                   span(a->norm_weight, (uint64_t)KD * 4, "norm_weight"),
+                   Range{0, 0, ""}};
+    rc = check_alias(w, 3, r, 11);
+    if (rc) return rc;
+    const int64_t items = N * a->H;
+    if (items > 0x7fffffffLL) return fail(KDA_ERR_SHAPE, "too many work items");
+    l->family = KERNEL_PACKED_FUSED;
+    l->vsplit = 1;
+    l->rows_per_block = KD;
+    l->grid = (int32_t)items;
+    l->block = 256;
+    l->bf16_state = a->state_dtype == KDA_DTYPE_BF16;
+
+    p->x = static_cast<const uint16_t *>(a->x);
+    p->x_stride = a->x_stride;
+    p->weight = a->weight;
+    p->conv_state = static_cast<uint16_t *>(a->conv_state);
+    p->conv_slot_stride = a->conv_slot_stride;
+    p->graw = static_cast<const uint16_t *>(a->raw_gate);
+    p->g_stride = a->gate_stride;
+    p->braw = static_cast<const uint16_t *>(a->raw_beta);
+    p->beta_stride = a->beta_stride;
+    p->A_log = a->A_log;
+    p->dt_bias = a->dt_bias;
+    p->state_indices = a->state_indices;
+    p->indices_stride = a->indices_stride;
+    p->qsl = a->query_start_loc;
+    p->accepted = a->num_accepted_tokens;
+    p->state = a->state;
+    p->num_slots = a->num_slots;
+    p->slot_stride = a->slot_stride;
+    p->ogate = static_cast<const uint16_t *>(a->output_gate);
+    p->ogate_stride = a->ogate_stride;
+    p->norm_weight = a->norm_weight;
+    p->norm_eps = a->norm_eps;
+    p->scale = 1.0f / sqrtf((float)KD);
+    p->l2_eps = 1e-6f;
+    p->out = static_cast<uint16_t *>(a->out);
+    p->n_rows = a->n_rows;
+    p->n_seqs = a->n_seqs;
+    p->H = a->H;
+    p->max_tokens = a->max_tokens;
+    return ok();
+}
+
 int check_current_device()
 {
     int dev = -1;
@@ -487,6 +583,27 @@ KDA_API int kda_fused_decode(const kda_fused_args *args, void *stream)
     rc = check_current_device();
     if (rc) return rc;
     return launched(launch_fused(p, l, stream));
+}
+
+KDA_API int kda_packed_fused_plan(const kda_packed_fused_args *args, kda_launch_plan *plan)
+{
+    PackedFusedParams p;
+    Launch l;
+    int rc = prepare_packed_fused(args, &p, &l);
+    if (rc) return rc;
+    fill_plan(plan, l, (int64_t)args->n_seqs * args->H);
+    return KDA_OK;
+}
+
+KDA_API int kda_packed_fused_decode(const kda_packed_fused_args *args, void *stream)
+{
+    PackedFusedParams p;
+    Launch l;
+    int rc = prepare_packed_fused(args, &p, &l);
+    if (rc) return rc;
+    rc = check_current_device();
+    if (rc) return rc;
+    return launched(launch_packed_fused(p, l, stream));
 }
 
 KDA_API const char *kda_status_string(int status)

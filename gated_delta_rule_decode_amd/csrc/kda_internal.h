@@ -11,6 +11,7 @@ enum KernelFamily : int32_t {
     KERNEL_RECURRENT_T1 = 1,   // one token per sequence
     KERNEL_RECURRENT_VARLEN = 2,  // ragged token loop with the state held in registers
     KERNEL_FUSED = 3,          // conv + SiLU -> KDA -> gated RMSNorm
+    KERNEL_PACKED_FUSED = 4,   // the fused step over packed ragged rows, T >= 1 per sequence
 };
 
 // Recurrence over (sequence, value head, value slice) work items; serves
@@ -65,6 +66,33 @@ struct FusedParams {
     int32_t rows, H;
 };
 
+// Packed fused decode: one workgroup per (sequence, head), token loop with
+// the state and the conv window in registers, one checkpoint per token.
+struct PackedFusedParams {
+    const uint16_t *x;
+    int64_t x_stride;
+    const float *weight;         // [3][4][H*128]
+    uint16_t *conv_state;        // [slot][3][3*H*128], slot stride conv_slot_stride
+    int64_t conv_slot_stride;
+    const uint16_t *graw;
+    int64_t g_stride;
+    const uint16_t *braw;
+    int64_t beta_stride;
+    const float *A_log, *dt_bias;
+    const int32_t *state_indices;  // [n_seqs][max_tokens], row stride indices_stride
+    int64_t indices_stride;
+    const int32_t *qsl;            // [n_seqs + 1]
+    const int32_t *accepted;       // [n_seqs]
+    void *state;
+    int64_t num_slots, slot_stride;
+    const uint16_t *ogate;
+    int64_t ogate_stride;
+    const float *norm_weight;
+    float norm_eps, scale, l2_eps;
+    uint16_t *out;               // bf16 [n_rows][H][128]
+    int32_t n_rows, n_seqs, H, max_tokens;
+};
+
 struct Launch {
     int32_t family;
     int32_t rows_per_block;  // 16 * G
@@ -77,6 +105,7 @@ struct Launch {
 // Implemented in kda_kernels.hip.  Return 0 or a negative kda_status.
 int launch_recurrent(const RecParams &p, const Launch &l, void *stream);
 int launch_fused(const FusedParams &p, const Launch &l, void *stream);
+int launch_packed_fused(const PackedFusedParams &p, const Launch &l, void *stream);
 int current_device_is_gfx950(int *device_out);  // 1 yes, 0 no, <0 HIP error
 int device_is_gfx950(int device);
 const char *last_hip_error();

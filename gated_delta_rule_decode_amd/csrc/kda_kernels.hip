@@ -695,6 +695,197 @@ __global__ void __launch_bounds__(256) kda_fused_kernel(const FusedParams p)
     }
 }
 
+// ------------------------------------------------- packed fused kernel ----
+//
+// The fused step over packed ragged rows with T >= 1 tokens per sequence.
+// One workgroup per (sequence, head) with the full V=128.  The sequence
+// starts from the checkpoint slot of its last accepted token; the head's
+// state (G=8 value rows per DPP row, as in the fused kernel) and the conv
+// window of the head's 384 channels (three positions per channel, in the
+// registers of the thread that owns the channel) are loaded once and carried
+// across the tokens in fp32.  Per token: conv + SiLU and the gate into LDS,
+// one barrier, the update and the readout, a second barrier for the RMSNorm
+// sum, then the output and, if the token's checkpoint column names a live
+// slot, the state (rounded to bf16 for a bf16 pool) and the conv window are
+// stored there.  Two barriers per token also keep the single LDS buffers
+// safe: every read of a token's activations precedes the second barrier,
+// every write of the next token's follows it.
+
+// One channel of the conv: window (oldest first, bf16 bits) and taps.
+struct ConvChan {
+    uint32_t c0, c1, c2;
+    float w0, w1, w2, w3;
+};
+
+__device__ __forceinline__ int conv_channel(int cl, int h, int HC)
+{
+    return (cl >> 7) * HC + h * KD + (cl & (KD - 1));
+}
+
+__device__ __forceinline__ ConvChan load_chan(const uint16_t *cs, const float *weight, int cl, int h, int HC,
+                                              int C3)
+{
+    const int c = conv_channel(cl, h, HC);
+    ConvChan ch;
+    ch.c0 = cs[c];
+    ch.c1 = cs[C3 + c];
+    ch.c2 = cs[2 * C3 + c];
+    const float *w = weight + (int64_t)(cl >> 7) * 4 * HC + h * KD + (cl & (KD - 1));
+    ch.w0 = w[0];
+    ch.w1 = w[HC];
+    ch.w2 = w[2 * HC];
+    ch.w3 = w[3 * HC];
+    return ch;
+}
+
+// Conv + SiLU of one token; the window advances by x.
+__device__ __forceinline__ float conv_step(ConvChan &ch, uint32_t x)
+{
+    float y = ch.w0 * bf16_bits_to_f32(ch.c0);
+    y = fmaf(ch.w1, bf16_bits_to_f32(ch.c1), y);
+    y = fmaf(ch.w2, bf16_bits_to_f32(ch.c2), y);
+    y = fmaf(ch.w3, bf16_bits_to_f32(x), y);
+    ch.c0 = ch.c1;
+    ch.c1 = ch.c2;
+    ch.c2 = x;
+    return y * sigmoid_f(y);
+}
+
+__device__ __forceinline__ void store_window(uint16_t *cs, const ConvChan &ch, int c, int C3)
+{
+    cs[c] = (uint16_t)ch.c0;
+    cs[C3 + c] = (uint16_t)ch.c1;
+    cs[2 * C3 + c] = (uint16_t)ch.c2;
+}
+
+template <bool BF16>
+__global__ void __launch_bounds__(256) kda_packed_fused_kernel(const PackedFusedParams p)
+{
+    using IO = StateIO<BF16>;
+    constexpr int G = 8;
+
+    __shared__ float s_act[3 * KD];
+    __shared__ float s_d[KD];
+    __shared__ float s_red[16];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int m = lane & 15;
+    const int qd = lane >> 4;
+    const int seq = blockIdx.x / p.H;
+    const int h = blockIdx.x - seq * p.H;
+    const int r_base = wave * (4 * G) + qd * G;
+    const int HC = p.H * KD;
+    const int C3 = 3 * HC;
+    auto out_at = [&](int r) { return p.out + ((int64_t)r * p.H + h) * KD + r_base; };
+
+    const int t0 = min(max(p.qsl[seq], 0), p.n_rows);
+    const int t1 = min(max(p.qsl[seq + 1], t0), p.n_rows);
+    // Rows that belong to no sequence: before the first one, after the last.
+    if (m == 0) {
+        if (seq == 0)
+            for (int r = 0; r < t0; ++r) store_zero_bf16<G>(out_at(r));
+        if (seq == p.n_seqs - 1)
+            for (int r = t1; r < p.n_rows; ++r) store_zero_bf16<G>(out_at(r));
+    }
+    const int32_t *cols = p.state_indices + (int64_t)seq * p.indices_stride;
+    const int acc = p.accepted[seq];
+    const int src = (acc >= 1 && acc <= p.max_tokens) ? cols[acc - 1] : -1;
+    if (src <= 0 || (int64_t)src >= p.num_slots) {
+        if (m == 0)
+            for (int r = t0; r < t1; ++r) store_zero_bf16<G>(out_at(r));
+        return;
+    }
+    if (t1 <= t0) return;
+
+    // Channel inputs first: conv window and taps, the first token, the gate.
+    const int c_lo = tid & (KD - 1);
+    const int ca = conv_channel(tid, h, HC);
+    const int cb = conv_channel(256 + c_lo, h, HC);  // used by tid < 128
+    const uint16_t *cs_src = p.conv_state + (int64_t)src * p.conv_slot_stride;
+    ConvChan cha = load_chan(cs_src, p.weight, tid, h, HC, C3);
+    ConvChan chb = load_chan(cs_src, p.weight, 256 + c_lo, h, HC, C3);
+    const float dt = p.dt_bias[(int64_t)h * KD + c_lo];
+    const float a_h = __expf(p.A_log[h]);
+    const uint16_t *xr = p.x + (int64_t)t0 * p.x_stride;
+    uint32_t xa = xr[ca], xb = xr[cb];
+    uint32_t graw = p.graw[(int64_t)t0 * p.g_stride + h * KD + c_lo];
+    uint32_t braw = p.braw[(int64_t)t0 * p.beta_stride + h];
+    __builtin_amdgcn_sched_barrier(0);
+
+    const size_t es = BF16 ? 2 : 4;
+    const int64_t head_elems = (int64_t)h * (KD * KD);
+    const char *head = reinterpret_cast<const char *>(p.state) + ((int64_t)src * p.slot_stride + head_elems) * es;
+    typename IO::Raw raw[G];
+    uint32_t off[G];
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi) {
+        off[gi] = IO::off(r_base + gi, m);
+        raw[gi] = IO::load(head, off[gi]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    float st[G][8];
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi) IO::unpack(raw[gi], st[gi]);
+    float nw[G];
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi) nw[gi] = p.norm_weight[r_base + gi];
+
+    for (int t = t0; t < t1; ++t) {
+        const int j = t - t0;
+        const int dst = j < p.max_tokens ? cols[j] : -1;
+        s_act[tid] = conv_step(cha, xa);
+        if (tid < KD) {
+            s_act[256 + tid] = conv_step(chb, xb);
+            s_d[tid] = __expf(-a_h * softplus_f(bf16_bits_to_f32(graw) + dt));
+        }
+        const float beta = sigmoid_f(bf16_bits_to_f32(braw));
+        uint32_t og[G];
+        const uint16_t *gate = p.ogate + (int64_t)t * p.ogate_stride + h * KD + r_base;
+#pragma unroll
+        for (int gi = 0; gi < G; ++gi) og[gi] = gate[gi];
+        if (t + 1 < t1) {  // next token's inputs while this one is computed
+            const uint16_t *xn = p.x + (int64_t)(t + 1) * p.x_stride;
+            xa = xn[ca];
+            xb = xn[cb];
+            graw = p.graw[(int64_t)(t + 1) * p.g_stride + h * KD + c_lo];
+            braw = p.braw[(int64_t)(t + 1) * p.beta_stride + h];
+        }
+        __syncthreads();
+
+        TokenOps ops;
+        read_token_ops<BF16>(ops, s_act, s_act + KD, s_d, nullptr, m, p.scale, p.l2_eps, beta);
+        float o[G];
+        float ss = 0.f;
+#pragma unroll
+        for (int gi = 0; gi < G; ++gi) {
+            o[gi] = row_update(st[gi], ops, s_act[2 * KD + r_base + gi]);
+            ss = fmaf(o[gi], o[gi], ss);
+        }
+        if (m == 0) s_red[wave * 4 + qd] = ss;
+        __syncthreads();
+        float tot = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) tot += s_red[i];
+        const float inv = rsqrtf(tot * (1.0f / KD) + p.norm_eps);
+        if (m == 0) {
+            float y[G];
+#pragma unroll
+            for (int gi = 0; gi < G; ++gi) y[gi] = o[gi] * inv * nw[gi] * sigmoid_f(bf16_bits_to_f32(og[gi]));
+            store_out_bf16<G>(out_at(t), y);
+        }
+        if (dst > 0 && (int64_t)dst < p.num_slots) {
+            char *ck = reinterpret_cast<char *>(p.state) + ((int64_t)dst * p.slot_stride + head_elems) * es;
+#pragma unroll
+            for (int gi = 0; gi < G; ++gi) IO::store(ck, off[gi], IO::pack(st[gi]));
+            uint16_t *cs_dst = p.conv_state + (int64_t)dst * p.conv_slot_stride;
+            store_window(cs_dst, cha, ca, C3);
+            if (tid < KD) store_window(cs_dst, chb, cb, C3);
+        }
+    }
+}
+
 // ------------------------------------------------------------ dispatch ----
 
 template <int G, bool BF16>
@@ -751,6 +942,17 @@ int launch_fused(const FusedParams &p, const Launch &l, void *stream)
         hipLaunchKernelGGL(kda_fused_kernel<true>, dim3(l.grid), dim3(l.block), 0, s, p);
     else
         hipLaunchKernelGGL(kda_fused_kernel<false>, dim3(l.grid), dim3(l.block), 0, s, p);
+    return record(hipGetLastError());
+}
+
+int launch_packed_fused(const PackedFusedParams &p, const Launch &l, void *stream)
+{
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    if (l.bf16_state)
+        hipLaunchKernelGGL(kda_packed_fused_kernel<true>, dim3(l.grid), dim3(l.block), 0, s, p);
+    else
+        hipLaunchKernelGGL(kda_packed_fused_kernel<false>, dim3(l.grid), dim3(l.block), 0, s, p);
     return record(hipGetLastError());
 }
 

@@ -294,16 +294,83 @@ typedef struct kda_fused_args {
     void *out;
 } kda_fused_args;
 
+/*
+ * packed_fused_kda_decode ("feat(kda): add fused speculative decode kernel":
+ * the fused conv + KDA + gated RMSNorm step over packed ragged rows with
+ * T >= 1 tokens per sequence; caches updated from accepted-token metadata,
+ * one conv and state checkpoint per token, empty and padding rows; its
+ * bf16-pool follow-up: the recurrence stays fp32 across the tokens and each
+ * checkpoint is rounded to bf16 when stored).
+ *
+ *  n_rows            packed token rows, >= 0.
+ *  n_seqs            sequences, >= 1.
+ *  max_tokens        columns of state_indices, >= 1.
+ *  x, weight, conv_state, raw_gate, raw_beta, A_log, dt_bias, state,
+ *  output_gate, norm_weight, norm_eps, out, gate_mode
+ *                    as in kda_fused_args, per packed row (rows = n_rows).
+ *  state_indices     int32 [n_seqs, max_tokens], row stride indices_stride
+ *                    (>= max_tokens).  Column j of sequence i is the slot that
+ *                    receives the conv window and the state after token j of
+ *                    the sequence; a column <= 0 or >= num_slots (and any
+ *                    token j >= max_tokens) writes no checkpoint.
+ *  query_start_loc   int32 [n_seqs + 1], non-decreasing: sequence i owns rows
+ *                    [qsl[i], qsl[i+1]) (clipped to [0, n_rows)).
+ *  num_accepted_tokens
+ *                    int32 [n_seqs]: sequence i starts from the conv window
+ *                    and state of slot state_indices[i, a-1], a = this value.
+ *                    A start slot <= 0 or >= num_slots, or a outside
+ *                    1..max_tokens, makes the sequence null: its rows give +0
+ *                    and it writes nothing.
+ *  Rows that belong to no sequence give +0.  All metadata is read on the
+ *  device, so a captured graph may be replayed with new values.  Slots must
+ *  not be shared between sequences of one call (they would race).
+ */
+typedef struct kda_packed_fused_args {
+    uint32_t struct_size;
+    int32_t n_rows;
+    int32_t n_seqs;
+    int32_t H;
+    int32_t max_tokens;
+    const void *x;
+    int64_t x_stride;
+    const float *weight;
+    void *conv_state;
+    int64_t conv_slot_stride;
+    const void *raw_gate;
+    int64_t gate_stride;
+    const void *raw_beta;
+    int64_t beta_stride;
+    const float *A_log;
+    const float *dt_bias;
+    int32_t gate_mode;
+    float lower_bound;
+    const int32_t *state_indices;
+    int64_t indices_stride;
+    const int32_t *query_start_loc;
+    const int32_t *num_accepted_tokens;
+    void *state;
+    int32_t state_dtype;
+    int64_t num_slots;
+    int64_t slot_stride;
+    const void *output_gate;
+    int64_t ogate_stride;
+    const float *norm_weight;
+    float norm_eps;
+    void *out;
+} kda_packed_fused_args;
+
 /* Validate and enqueue.  Return KDA_OK or a negative kda_status. */
 KDA_API int kda_recurrent(const kda_recurrent_args *args, void *stream);
 KDA_API int kda_packed_decode(const kda_packed_args *args, void *stream);
 KDA_API int kda_fused_decode(const kda_fused_args *args, void *stream);
+KDA_API int kda_packed_fused_decode(const kda_packed_fused_args *args, void *stream);
 
 /* Validate only (no HIP call, no device access) and report the launch
  * geometry the matching entry point would use.  `plan` may be NULL. */
 KDA_API int kda_recurrent_plan(const kda_recurrent_args *args, kda_launch_plan *plan);
 KDA_API int kda_packed_plan(const kda_packed_args *args, kda_launch_plan *plan);
 KDA_API int kda_fused_plan(const kda_fused_args *args, kda_launch_plan *plan);
+KDA_API int kda_packed_fused_plan(const kda_packed_fused_args *args, kda_launch_plan *plan);
 
 /* Static text of a status code. */
 KDA_API const char *kda_status_string(int status);

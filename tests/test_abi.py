@@ -364,3 +364,69 @@ def test_verify_cache_rules():
     a = with_caches(rec_args(), corr=False)
     a.kg_cache = a.q  # nor an input
     expect(plan_rec(a), -6, "kg_cache")
+
+
+def packed_fused_args(rows=10, N=3, T=4, H=12, slots=32, bf16=False):
+    A = Arena()
+    C3 = 3 * H * D
+    a = _lib.PackedFusedArgs()
+    a.struct_size = ctypes.sizeof(_lib.PackedFusedArgs)
+    a.n_rows, a.n_seqs, a.H, a.max_tokens = rows, N, H, T
+    a.x, a.x_stride = A.take(rows * C3 * 2), C3
+    a.weight = A.take(12 * H * D * 4)
+    a.conv_state, a.conv_slot_stride = A.take(slots * 3 * C3 * 2), 3 * C3
+    a.raw_gate, a.gate_stride = A.take(rows * H * D * 2), H * D
+    a.raw_beta, a.beta_stride = A.take(rows * H * 2), H
+    a.A_log, a.dt_bias = A.take(H * 4), A.take(H * D * 4)
+    a.state_indices, a.indices_stride = A.take(N * T * 4), T
+    a.query_start_loc = A.take((N + 1) * 4)
+    a.num_accepted_tokens = A.take(N * 4)
+    es = 2 if bf16 else 4
+    a.state, a.state_dtype = A.take(slots * H * D * D * es), 1 if bf16 else 0
+    a.num_slots, a.slot_stride = slots, H * D * D
+    a.output_gate, a.ogate_stride = A.take(rows * H * D * 2), H * D
+    a.norm_weight, a.norm_eps = A.take(D * 4), 1e-5
+    a.out = A.take(rows * H * D * 2)
+    return a
+
+
+def plan_pf(a):
+    p = _lib.LaunchPlan()
+    rc = lib().kda_packed_fused_plan(ctypes.byref(a), ctypes.byref(p))
+    return rc, p
+
+
+def test_packed_fused_plan_and_validation():
+    rc, p = plan_pf(packed_fused_args())
+    assert rc == 0, err()
+    assert (p.kernel, p.grid_x, p.block, p.rows_per_block) == (4, 3 * 12, 256, 128)
+    assert plan_pf(packed_fused_args(bf16=True))[0] == 0, err()
+    a = packed_fused_args(rows=0)  # no rows at all: every sequence is empty
+    a.x = a.raw_gate = a.raw_beta = a.output_gate = a.out = None
+    assert plan_pf(a)[0] == 0, err()
+    a = packed_fused_args()
+    a.struct_size -= 8
+    expect(plan_pf(a), -10)
+    expect(plan_pf(packed_fused_args(N=0)), -2, "n_seqs")
+    expect(plan_pf(packed_fused_args(T=0)), -2, "max_tokens")
+    a = packed_fused_args()
+    a.indices_stride = 3
+    expect(plan_pf(a), -4, "indices_stride")
+    a = packed_fused_args()
+    a.gate_mode = 1
+    expect(plan_pf(a), -7)
+    a = packed_fused_args()
+    a.query_start_loc = None
+    expect(plan_pf(a), -1)
+    a = packed_fused_args()
+    a.out += 2
+    expect(plan_pf(a), -5, "out")
+    a = packed_fused_args()
+    a.out = a.x  # output over an input
+    expect(plan_pf(a), -6)
+    a = packed_fused_args()
+    a.conv_state = a.state  # the two caches may not overlap
+    expect(plan_pf(a), -6)
+    a = packed_fused_args()
+    a.query_start_loc = a.state_indices  # metadata over metadata is fine (both read-only)
+    assert plan_pf(a)[0] == 0, err()
