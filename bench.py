@@ -75,6 +75,17 @@ def modes_bytes(n_live_seqs, tokens, H, HV, state_bytes, *, write_state=True, ga
     return b
 
 
+def packed_fused_bytes(N, T, H, state_bytes):
+    """Packed fused call, N live sequences of T tokens: per (sequence, head)
+    the state and the conv window are read once and written once per token
+    (checkpoints); per token and head x, raw gate, beta, output gate and
+    output; per sequence its metadata; per call the weights."""
+    head = D * D * state_bytes
+    win = 3 * 3 * D * 2
+    per_item = head + T * head + win + T * win + T * (3 * D * 2 + D * 2 + 2 + D * 2 + D * 2)
+    return N * H * per_item + N * (8 + 4 * T) + 4 + 12 * H * D * 4 + H * D * 4 + H * 4 + D * 4
+
+
 def varlen_bytes(lengths, H, state_bytes, ckpt=True):
     live_seqs = sum(1 for n in lengths if n > 0)
     T = sum(lengths)
@@ -219,6 +230,14 @@ def time_cold(torch, fn, n, flush_buf):
 
 # --------------------------------------------------------- other workloads ----
 
+def n_sets(state_bytes_per_call, available, lo=4, cycle=1 << 30):
+    """Disjoint slot sets to rotate over so that one cycle touches at least
+    `cycle` bytes of state (L2 is 8 x 4 MiB, the MALL 256 MiB): every call
+    then finds its state cold, as with a flush before each launch."""
+    need = -(-cycle // max(1, state_bytes_per_call))
+    return int(max(min(lo, available), min(need, available)))
+
+
 def rotating(torch, timer, calls, reps=8):
     """Average GPU time per call of `calls` (each touching its own slots, so
     consecutive calls find their state cold in L2 and the MALL), captured once
@@ -242,11 +261,13 @@ def rotating(torch, timer, calls, reps=8):
 
 
 def extra_workloads(torch, dev, timer, pool32):
-    from gated_delta_rule_decode_amd import fused_kda_decode, packed_kda_decode, recurrent_kda, synth
+    from gated_delta_rule_decode_amd import (fused_kda_decode, packed_fused_kda_decode, packed_kda_decode,
+                                             recurrent_kda, synth)
     out = {}
     H = 32
     SLOTS = pool32.shape[0]
-    # H=32 fp32 batch sweep on the 8 GiB pool: 4 disjoint slot sets per B
+    # H=32 fp32 batch sweep on the 8 GiB pool: disjoint slot sets per B, a
+    # cycle of >= 1 GiB of state
     sweep = []
     g2 = torch.Generator(device=dev)
     for Bs in (1, 8, 32, 128, 256, 512):
@@ -256,7 +277,7 @@ def extra_workloads(torch, dev, timer, pool32):
         o = torch.empty((Bs, 1, H, D), dtype=torch.bfloat16, device=dev)
         r4 = lambda t, n=Bs: t.reshape(n, 1, H, D)  # noqa: E731
         calls = []
-        for j in range(4):
+        for j in range(n_sets(Bs * H * D * D * 4, SLOTS // Bs)):
             ids = perm[j * Bs:(j + 1) * Bs].contiguous()
             calls.append(lambda cs=cs, ids=ids, o=o, r4=r4, n=Bs: recurrent_kda(
                 r4(cs.q), r4(cs.k), r4(cs.v), r4(cs.g), cs.beta.reshape(n, 1, H), cs.A_log,
@@ -271,7 +292,7 @@ def extra_workloads(torch, dev, timer, pool32):
     out["recurrent_t1_h32_fp32"] = sweep
 
     # packed H=12, bf16 pool [8192,12,128,128] (3 GiB), 1/8 of the rows inactive,
-    # 8 disjoint slot sets per B
+    # disjoint slot sets per B, a cycle of >= 1 GiB of state
     pcase = synth.packed_case(2000, B=512, H=12, num_slots=8192, device=dev)
     perm = torch.randperm(8192 - 1, generator=g2, device=dev).to(torch.int32) + 1
     sweep = []
@@ -279,7 +300,7 @@ def extra_workloads(torch, dev, timer, pool32):
         nnull = Bs // 8
         o = torch.empty((Bs, 1, 12, D), dtype=torch.bfloat16, device=dev)
         calls = []
-        for j in range(8):
+        for j in range(n_sets((Bs - nnull) * 12 * D * D * 2, 8191 // Bs, lo=8)):
             ids = perm[j * Bs:(j + 1) * Bs].clone()
             ids[:nnull] = -1
             calls.append(lambda ids=ids, o=o, n=Bs: packed_kda_decode(
@@ -322,9 +343,9 @@ def extra_workloads(torch, dev, timer, pool32):
     torch.cuda.empty_cache()
 
     # ragged T>=2: H=16, N=64, lengths U{0..6}, fp32 checkpoints; the pool has
-    # 4 disjoint slot sets
+    # 16 disjoint slot sets (1 GiB of state per cycle)
     lengths = synth.ragged_lengths(4000, 64, 0, 6)
-    vc = synth.recurrent_case(4000, n_seqs=64, H=16, num_slots=4 * 64 + 1, device=dev,
+    vc = synth.recurrent_case(4000, n_seqs=64, H=16, num_slots=16 * 64 + 1, device=dev,
                               lengths=lengths, slot_lo=1)
     T = sum(lengths)
     ck = torch.empty((T, 16, D, D), dtype=torch.float32, device=dev)
@@ -333,7 +354,7 @@ def extra_workloads(torch, dev, timer, pool32):
     calls = [lambda ids=(vc.state_indices + 64 * j).contiguous(): recurrent_kda(
         r1(vc.q), r1(vc.k), r1(vc.v), r1(vc.g), r1(vc.beta), vc.A_log, vc.dt_bias,
         initial_state=vc.state, state_indices=ids, cu_seqlens=vc.cu_seqlens, output=o,
-        intermediate_states=ck) for j in range(4)]
+        intermediate_states=ck) for j in range(16)]
     t_us = rotating(torch, timer, calls)
     bts = varlen_bytes(lengths, 16, 4)
     out["varlen_h16_n64_fp32_ckpt"] = {"us": t_us, "tokens": T, "tokens_per_s": T / (t_us * 1e-6),
@@ -391,6 +412,40 @@ def extra_workloads(torch, dev, timer, pool32):
     modes_entry("verify_caches_b64_t4_h32_fp32", calls,
                 modes_bytes(Bv, Bv * Tv, 32, 32, 4, write_state=False) + Bv * Tv * 32 * 3 * D * 4, Bv)
     del corr, kgc
+    torch.cuda.empty_cache()
+
+    # packed fused speculative decode, T=5 tokens per sequence, one accepted
+    # token; disjoint checkpoint-slot sets per call
+    pf = []
+    for Hs, Ns_list in ((12, (1, 8, 32, 128)), (24, (8, 128))):
+        for sdt, sb in ((torch.float32, 4), (torch.bfloat16, 2)):
+            T = 5
+            pool_slots = 4 * 128 * T + 1
+            pc = synth.packed_fused_case(8500 + Hs, lengths=[T] * 128, H=Hs, num_slots=pool_slots,
+                                         max_tokens=T, state_dtype=sdt, device=dev, accepted="one")
+            g2.manual_seed(8500 + Hs)
+            pperm = torch.randperm(pool_slots - 1, generator=g2, device=dev).to(torch.int32) + 1
+            for Ns in Ns_list:
+                rows = Ns * T
+                o = torch.empty((1, rows, Hs, D), dtype=torch.bfloat16, device=dev)
+                qsl = (torch.arange(Ns + 1, dtype=torch.int32, device=dev) * T).contiguous()
+                acc = torch.ones(Ns, dtype=torch.int32, device=dev)
+                nset = n_sets(Ns * Hs * (1 + T) * D * D * sb, (pool_slots - 1) // (Ns * T))
+                calls = [lambda ids=pperm[k * Ns * T:(k + 1) * Ns * T].reshape(Ns, T).contiguous(), o=o, rows=rows,
+                         qsl=qsl, acc=acc: packed_fused_kda_decode(
+                             pc.x[:rows], pc.weight, pc.conv_state, pc.raw_gate[:rows], pc.raw_beta[:rows], pc.A_log,
+                             pc.dt_bias, ids, pc.state, pc.output_gate[:rows], pc.norm_weight, output=o,
+                             query_start_loc=qsl, num_accepted_tokens=acc)
+                         for k in range(nset)]
+                t_us = rotating(torch, timer, calls)
+                bts = packed_fused_bytes(Ns, T, Hs, sb)
+                pf.append({"H": Hs, "N": Ns, "T": T, "state": "bf16" if sb == 2 else "fp32", "us": t_us,
+                           "GBps": bts / (t_us * 1e-6) / 1e9, "frac": bts / (t_us * 1e-6) / 1e9 / HBM_PEAK_GBPS})
+                log(f"packed fused H={Hs} N={Ns} T={T} {pf[-1]['state']}: {t_us:.1f} us, "
+                    f"{pf[-1]['GBps']:.0f} GB/s")
+            del pc
+            torch.cuda.empty_cache()
+    out["packed_fused_t5_accept1"] = pf
     return out
 
 

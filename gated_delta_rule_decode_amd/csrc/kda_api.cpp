@@ -126,10 +126,17 @@ uint64_t pool_bytes(int32_t dtype, int64_t num_slots, int64_t slot_stride, int32
 #define KDA_FORCE_VSPLIT 0  // build-time override used when tuning the policy
 #endif
 
-int choose_vsplit(int64_t items, bool bf16)
+// The token loop (T >= 2 per sequence) is bound by per-token arithmetic and
+// latency rather than by the single pass over the state: splitting a head
+// over workgroups repeats the token staging in every split, so it pays only
+// while the grid is small.  Measured on MI355X (read-only batched T=4 calls,
+// H=12 and 32, fp32 and bf16 pools): 4 splits below ~96 items, 2 up to ~1024,
+// none above.
+int choose_vsplit(int64_t items, bool bf16, bool token_loop)
 {
     if (KDA_FORCE_VSPLIT == 1 || KDA_FORCE_VSPLIT == 2 || KDA_FORCE_VSPLIT == 4 || KDA_FORCE_VSPLIT == 8)
         return KDA_FORCE_VSPLIT;
+    if (token_loop) return items < 96 ? 4 : (items < 1024 ? 2 : 1);
     if (bf16 && items >= 512 && items < 1536) return 2;
     return 4;
 }
@@ -234,9 +241,10 @@ int prepare_recurrent(const kda_recurrent_args *a, RecParams *p, Launch *l)
     if (rc) return rc;
 
     const int64_t items = (int64_t)a->n_seqs * a->HV;
-    const int vsplit = choose_vsplit(items, a->state_dtype == KDA_DTYPE_BF16);
+    const bool token_loop = ragged || tps > 1;
+    const int vsplit = choose_vsplit(items, a->state_dtype == KDA_DTYPE_BF16, token_loop);
     if (items * vsplit > 0x7ffffff0LL) return fail(KDA_ERR_SHAPE, "too many work items");
-    l->family = (ragged || tps > 1) ? KERNEL_RECURRENT_VARLEN : KERNEL_RECURRENT_T1;
+    l->family = token_loop ? KERNEL_RECURRENT_VARLEN : KERNEL_RECURRENT_T1;
     l->vsplit = vsplit;
     l->rows_per_block = KD / vsplit;
     l->grid = (int32_t)((items * vsplit + 7) & ~7LL);  // padded to whole XCD rounds

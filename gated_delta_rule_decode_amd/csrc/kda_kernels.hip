@@ -61,6 +61,20 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
            ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
 
+// s_waitcnt vmcnt(0): every vector memory access of this wave has completed
+// (gfx9 encoding: vmcnt 0, expcnt 7, lgkmcnt 15 are "no wait" for the others).
+__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Tokens staged per chunk by the token loops (measured on MI355X: the
+// recurrent loop keeps the next chunk's inputs in registers through the
+// current chunk, and two tokens per chunk keep it at 4 waves per SIMD; the
+// packed fused loop has two barriers per chunk and prefers longer chunks).
+#ifndef KDA_CHUNK
+#define KDA_CHUNK 2  // build-time override used when tuning
+#endif
+constexpr int CHUNK = KDA_CHUNK;
+constexpr int PF_CHUNK = 8;
+
 // ---------------------------------------------------------- reductions ----
 
 template <int CTRL>
@@ -321,27 +335,39 @@ __device__ __forceinline__ void store_f32(float *dst, const float *x)
 }
 
 // One token's channel inputs, held in registers between their load and the
-// LDS stage.  Every thread loads channel tid & 127 of q, k, v, the raw gate
-// and dt_bias (no divergent branch around the loads, so the compiler does
-// not wait on them before the state loads are issued); threads 0..127 then
-// stage q, k and the decay, threads 128..255 stage v.
+// LDS stage.  Every thread loads channel tid & 127 of q, k, v and the raw
+// gate (no divergent branch around the loads, so the compiler does not wait
+// on them before the state loads are issued); threads 0..127 then stage q,
+// k and the decay, threads 128..255 stage v.  A gate or beta that may be
+// fp32 or bf16 is fetched as two 16-bit halves whose addresses (not values)
+// depend on the format, and is assembled only when staged: a select on the
+// loaded values would make the compiler wait for the loads right away.
 struct StageIn {
     uint32_t q, k, v;  // bf16 bits
-    uint32_t g;        // bf16 or fp32 bits
-    float dt;
+    uint32_t g_lo, g_hi;  // fp32: the two halves; bf16: the value (g_hi unused)
 };
 
+// Two 16-bit halves of an fp32 or bf16 element at byte address `at`.
+__device__ __forceinline__ void load_halves(const char *at, bool is_f32, uint32_t &lo, uint32_t &hi)
+{
+    lo = *reinterpret_cast<const uint16_t *>(at);
+    hi = *reinterpret_cast<const uint16_t *>(at + (is_f32 ? 2 : 0));
+}
+
+__device__ __forceinline__ float halves_value(uint32_t lo, uint32_t hi, bool is_f32)
+{
+    return is_f32 ? __uint_as_float((hi << 16) | lo) : bf16_bits_to_f32(lo);
+}
+
 __device__ __forceinline__ StageIn load_stage(int tid, const uint16_t *q, const uint16_t *k,
-                                              const uint16_t *v, const void *g, bool g_f32,
-                                              const float *dt_bias_h)
+                                              const uint16_t *v, const char *g, bool g_f32)
 {
     const int c = tid & (KD - 1);
     StageIn s;
     s.q = q[c];
     s.k = k[c];
     s.v = v[c];
-    s.g = g_f32 ? static_cast<const uint32_t *>(g)[c] : static_cast<const uint16_t *>(g)[c];
-    s.dt = dt_bias_h ? dt_bias_h[c] : 0.f;
+    load_halves(g + c * (g_f32 ? 4 : 2), g_f32, s.g_lo, s.g_hi);
     return s;
 }
 
@@ -355,7 +381,7 @@ __device__ __forceinline__ float input_value(uint32_t bits, bool is_f32)
 // norm sums (|q|^2, |k|^2, q.k) over their wave, writing one partial per
 // wave to norms[4 * (wave - 2) + {0, 1, 2}].
 // With a precomputed gate, g already is the log-decay: decay = exp(g).
-__device__ __forceinline__ void write_stage(int tid, const StageIn &s, float a_h, bool g_f32,
+__device__ __forceinline__ void write_stage(int tid, const StageIn &s, float a_h, float dt, bool g_f32,
                                             bool precomputed, float *sq, float *sk, float *sd,
                                             float *sv, float *norms)
 {
@@ -364,8 +390,8 @@ __device__ __forceinline__ void write_stage(int tid, const StageIn &s, float a_h
     if (tid < KD) {
         sq[tid] = q;
         sk[tid] = k;
-        const float g = input_value(s.g, g_f32);
-        sd[tid] = precomputed ? __expf(g) : __expf(-a_h * softplus_f(g + s.dt));
+        const float g = halves_value(s.g_lo, s.g_hi, g_f32);
+        sd[tid] = precomputed ? __expf(g) : __expf(-a_h * softplus_f(g + dt));
     } else {
         sv[tid - KD] = bf16_bits_to_f32(s.v);
         float pq = q * q, pk = k * k, pqk = q * k;
@@ -388,11 +414,12 @@ __device__ __forceinline__ void store_kg(void *kg, bool kg_f32, int64_t row, int
     if (kg_f32) {
         float *d = static_cast<float *>(kg) + at;
         d[0] = bf16_bits_to_f32(s.k);
-        d[KD] = input_value(s.g, g_f32);
+        d[KD] = halves_value(s.g_lo, s.g_hi, g_f32);
     } else {
         uint16_t *d = static_cast<uint16_t *>(kg) + at;
         d[0] = (uint16_t)s.k;
-        d[KD] = g_f32 ? (uint16_t)(pack_bf16x2(__uint_as_float(s.g), 0.0f) & 0xffffu) : (uint16_t)s.g;
+        d[KD] = g_f32 ? (uint16_t)(pack_bf16x2(halves_value(s.g_lo, s.g_hi, true), 0.0f) & 0xffffu)
+                      : (uint16_t)s.g_lo;
     }
 }
 
@@ -404,8 +431,12 @@ __global__ void __launch_bounds__(256) kda_recurrent_kernel(const RecParams p)
     using IO = StateIO<BF16>;
     constexpr int VT = 16 * G;  // value rows per workgroup
 
-    __shared__ float s_q[2][KD], s_k[2][KD], s_d[2][KD], s_v[2][KD];
-    __shared__ float s_norm[2][8];
+    // T=1: one token stage.  Token loop: a chunk of CHUNK tokens is staged at
+    // once (one round of loads and one barrier per chunk).
+    constexpr int NB = VARLEN ? CHUNK : 1;
+    __shared__ float s_q[NB][KD], s_k[NB][KD], s_d[NB][KD], s_v[NB][KD];
+    __shared__ float s_norm[NB][8];
+    __shared__ float s_beta[NB];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -453,7 +484,7 @@ __global__ void __launch_bounds__(256) kda_recurrent_kernel(const RecParams p)
     const bool precomputed = p.precomputed != 0;
     const bool g_f32 = p.g_f32 != 0;
     const bool beta_f32 = p.beta_f32 != 0;
-    const float *dtb = precomputed ? nullptr : p.dt_bias + (int64_t)hv * KD;
+    const float dt = precomputed ? 0.f : p.dt_bias[(int64_t)hv * KD + (tid & (KD - 1))];
     const int64_t oq = (int64_t)hq * KD;
     const int64_t ov = (int64_t)hv * KD;
     const char *gbase = static_cast<const char *>(p.g);
@@ -461,15 +492,26 @@ __global__ void __launch_bounds__(256) kda_recurrent_kernel(const RecParams p)
     const int g_es = g_f32 ? 4 : 2;
     const int b_es = beta_f32 ? 4 : 2;
     auto g_at = [&](int64_t t) { return gbase + (t * p.g_stride + ov) * g_es; };
-    auto beta_at = [&](int64_t t) -> uint32_t {
-        const char *b = bbase + (t * p.beta_stride + hv) * b_es;
-        return beta_f32 ? *reinterpret_cast<const uint32_t *>(b) : *reinterpret_cast<const uint16_t *>(b);
+    auto beta_at = [&](int64_t t, uint32_t &lo, uint32_t &hi) {
+        load_halves(bbase + (t * p.beta_stride + hv) * b_es, beta_f32, lo, hi);
     };
 
-    // Token inputs first: waiting for them later must not wait for the state.
-    StageIn in = load_stage(tid, p.q + (int64_t)t0 * p.q_stride + oq, p.k + (int64_t)t0 * p.k_stride + oq,
-                            p.v + (int64_t)t0 * p.v_stride + ov, g_at(t0), g_f32, dtb);
-    uint32_t braw = beta_at(t0);
+    // Token inputs first (the first chunk's in the token loop): waiting for
+    // them later must not wait for the state.  Token indices are clamped to
+    // the sequence, so every load is in bounds and unconditional.
+    constexpr int NC = VARLEN ? CHUNK : 1;
+    StageIn cin[NC];
+    uint32_t blo[NC], bhi[NC];
+    auto load_chunk = [&](int c0) {
+#pragma unroll
+        for (int i = 0; i < NC; ++i) {
+            const int64_t n = min(c0 + i, t1 - 1);
+            cin[i] = load_stage(tid, p.q + n * p.q_stride + oq, p.k + n * p.k_stride + oq,
+                                p.v + n * p.v_stride + ov, g_at(n), g_f32);
+            beta_at(n, blo[i], bhi[i]);
+        }
+    };
+    load_chunk(t0);
     const float a_h = precomputed ? 0.f : __expf(p.A_log[hv]);
     __builtin_amdgcn_sched_barrier(0);
 
@@ -484,16 +526,17 @@ __global__ void __launch_bounds__(256) kda_recurrent_kernel(const RecParams p)
     __builtin_amdgcn_sched_barrier(0);
 
     // beta: sigmoid of the logits, or the precomputed value itself
-    auto beta_of = [&](uint32_t bits) {
-        const float b = input_value(bits, beta_f32);
+    auto beta_of = [&](uint32_t lo, uint32_t hi) {
+        const float b = halves_value(lo, hi, beta_f32);
         return precomputed ? b : sigmoid_f(b);
     };
     const bool update = p.update_state != 0;
 
     if constexpr (!VARLEN) {
         // T=1: the gate transform and the norms overlap the state fetch.
-        write_stage(tid, in, a_h, g_f32, precomputed, s_q[0], s_k[0], s_d[0], s_v[0], s_norm[0]);
-        const float beta = beta_of(braw);
+        const StageIn &in = cin[0];
+        write_stage(tid, in, a_h, dt, g_f32, precomputed, s_q[0], s_k[0], s_d[0], s_v[0], s_norm[0]);
+        const float beta = beta_of(blo[0], bhi[0]);
         __syncthreads();
         TokenOps ops;
         read_token_ops<BF16>(ops, s_q[0], s_k[0], s_d[0], s_norm[0], m, p.scale, p.l2_eps, beta);
@@ -512,42 +555,50 @@ __global__ void __launch_bounds__(256) kda_recurrent_kernel(const RecParams p)
             if (p.kg && vs == 0 && tid < KD) store_kg(p.kg, p.kg_f32 != 0, row, tid, in, g_f32);
         }
     } else {
-        // Token loop: the state stays in registers across the tokens of the
-        // sequence; the next token's inputs are fetched while the current one
-        // is computed; after each token the checkpoint (if requested) and the
-        // output are written; the pool slot is written once at the end
-        // (unless the pool is read only).
+        // Token loop in chunks of up to CHUNK tokens: the inputs of a whole
+        // chunk are loaded at once (the first chunk's before the state, each
+        // next one while the current one is computed), staged in LDS (gate
+        // transform, norm partials, beta), then, after one barrier, the
+        // tokens run back to back from LDS with the state in registers: a
+        // token needs no barrier, its reductions stay inside DPP rows.  After
+        // each token the output, the verify-cache rows and the checkpoint are
+        // written; the pool slot once at the end (unless the pool is read
+        // only).
         float st[G][8];
 #pragma unroll
         for (int gi = 0; gi < G; ++gi) IO::unpack(raw[gi], st[gi]);
-        for (int t = t0; t < t1; ++t) {
-            const int buf = (t - t0) & 1;
-            write_stage(tid, in, a_h, g_f32, precomputed, s_q[buf], s_k[buf], s_d[buf], s_v[buf],
-                        s_norm[buf]);
-            const float beta = beta_of(braw);
-            const int pos = t - t0;
-            const bool cache = pos < p.t_max;  // t_max is 0 without verify caches
-            const int64_t crow = ((int64_t)idx * p.HV + hv) * p.t_max + pos;
-            if (cache && p.kg && vs == 0 && tid < KD) store_kg(p.kg, p.kg_f32 != 0, crow, tid, in, g_f32);
-            if (t + 1 < t1) {
-                const int64_t n = t + 1;
-                in = load_stage(tid, p.q + n * p.q_stride + oq, p.k + n * p.k_stride + oq,
-                                p.v + n * p.v_stride + ov, g_at(n), g_f32, dtb);
-                braw = beta_at(n);
+        const int64_t crow0 = ((int64_t)idx * p.HV + hv) * p.t_max;  // verify-cache row of token t0
+        for (int c0 = t0; c0 < t1; c0 += CHUNK) {
+            const int nc = min(CHUNK, t1 - c0);
+            if (c0 != t0) __syncthreads();  // the previous chunk's stage has been read
+#pragma unroll
+            for (int i = 0; i < CHUNK; ++i) {
+                if (i < nc) {
+                    write_stage(tid, cin[i], a_h, dt, g_f32, precomputed, s_q[i], s_k[i], s_d[i], s_v[i],
+                                s_norm[i]);
+                    if (tid == 0) s_beta[i] = beta_of(blo[i], bhi[i]);
+                    const int pos = c0 - t0 + i;
+                    if (pos < p.t_max && p.kg && vs == 0 && tid < KD)
+                        store_kg(p.kg, p.kg_f32 != 0, crow0 + pos, tid, cin[i], g_f32);
+                }
             }
             __syncthreads();
-            TokenOps ops;
-            read_token_ops<BF16>(ops, s_q[buf], s_k[buf], s_d[buf], s_norm[buf], m, p.scale, p.l2_eps,
-                                 beta);
-            float o[G], c[G];
+            load_chunk(c0 + CHUNK);  // the next chunk (past the end: the last token again, unused)
+            for (int i = 0; i < nc; ++i) {
+                const int t = c0 + i;
+                const int pos = t - t0;
+                TokenOps ops;
+                read_token_ops<BF16>(ops, s_q[i], s_k[i], s_d[i], s_norm[i], m, p.scale, p.l2_eps, s_beta[i]);
+                float o[G], c[G];
 #pragma unroll
-            for (int gi = 0; gi < G; ++gi) o[gi] = row_update(st[gi], ops, s_v[buf][r_base + gi], c[gi]);
-            if (m == 0) store_out_bf16<G>(p.out + ((int64_t)t * p.HV + hv) * KD + r_base, o);
-            if (cache && p.corr && m == 0) store_f32<G>(p.corr + crow * KD + r_base, c);
-            if (p.ckpt) {
-                char *ck = reinterpret_cast<char *>(p.ckpt) + ((int64_t)t * p.HV + hv) * (KD * KD) * es;
+                for (int gi = 0; gi < G; ++gi) o[gi] = row_update(st[gi], ops, s_v[i][r_base + gi], c[gi]);
+                if (m == 0) store_out_bf16<G>(p.out + ((int64_t)t * p.HV + hv) * KD + r_base, o);
+                if (pos < p.t_max && p.corr && m == 0) store_f32<G>(p.corr + (crow0 + pos) * KD + r_base, c);
+                if (p.ckpt) {
+                    char *ck = reinterpret_cast<char *>(p.ckpt) + ((int64_t)t * p.HV + hv) * (KD * KD) * es;
 #pragma unroll
-                for (int gi = 0; gi < G; ++gi) IO::store(ck, off[gi], IO::pack(st[gi]));
+                    for (int gi = 0; gi < G; ++gi) IO::store(ck, off[gi], IO::pack(st[gi]));
+                }
             }
         }
         if (update) {
@@ -703,13 +754,20 @@ __global__ void __launch_bounds__(256) kda_fused_kernel(const FusedParams p)
 // state (G=8 value rows per DPP row, as in the fused kernel) and the conv
 // window of the head's 384 channels (three positions per channel, in the
 // registers of the thread that owns the channel) are loaded once and carried
-// across the tokens in fp32.  Per token: conv + SiLU and the gate into LDS,
-// one barrier, the update and the readout, a second barrier for the RMSNorm
-// sum, then the output and, if the token's checkpoint column names a live
-// slot, the state (rounded to bf16 for a bf16 pool) and the conv window are
-// stored there.  Two barriers per token also keep the single LDS buffers
-// safe: every read of a token's activations precedes the second barrier,
-// every write of the next token's follows it.
+// across the tokens in fp32.
+//
+// Tokens go in chunks of up to PF_CHUNK: the chunk's inputs are loaded at once
+// (one memory round trip); each thread runs its channels' conv over the
+// chunk's tokens in order and stages the activations, decays and per-token
+// scalars in LDS (a token whose checkpoint column names a live slot stores
+// the conv window right there); after one barrier the tokens run back to
+// back, each writing its unnormalised output and its RMS partial sums to LDS
+// and storing its state checkpoint (rounded to bf16 for a bf16 pool); after
+// a second barrier the gated RMSNorm of every token of the chunk is applied
+// and stored, one (token, value) per thread.  Two barriers per chunk: every
+// read of a chunk's stage precedes the second barrier and the next chunk's
+// stage is written after it; every read of the outputs precedes the next
+// chunk's first barrier, after which they are written again.
 
 // One channel of the conv: window (oldest first, bf16 bits) and taps.
 struct ConvChan {
@@ -764,9 +822,13 @@ __global__ void __launch_bounds__(256) kda_packed_fused_kernel(const PackedFused
     using IO = StateIO<BF16>;
     constexpr int G = 8;
 
-    __shared__ float s_act[3 * KD];
-    __shared__ float s_d[KD];
-    __shared__ float s_red[16];
+    __shared__ float s_act[PF_CHUNK][3 * KD];  // q | k | v activations per token
+    __shared__ float s_d[PF_CHUNK][KD];
+    __shared__ float s_o[PF_CHUNK][KD];        // unnormalised outputs
+    __shared__ float s_red[PF_CHUNK][16];      // RMS partial sums
+    __shared__ float s_beta[PF_CHUNK];
+    __shared__ int s_dst[PF_CHUNK];            // checkpoint slot, or -1
+    __shared__ float s_nw[KD];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -799,7 +861,7 @@ __global__ void __launch_bounds__(256) kda_packed_fused_kernel(const PackedFused
     }
     if (t1 <= t0) return;
 
-    // Channel inputs first: conv window and taps, the first token, the gate.
+    // Conv windows and taps, gate parameters, then the state.
     const int c_lo = tid & (KD - 1);
     const int ca = conv_channel(tid, h, HC);
     const int cb = conv_channel(256 + c_lo, h, HC);  // used by tid < 128
@@ -808,10 +870,7 @@ __global__ void __launch_bounds__(256) kda_packed_fused_kernel(const PackedFused
     ConvChan chb = load_chan(cs_src, p.weight, 256 + c_lo, h, HC, C3);
     const float dt = p.dt_bias[(int64_t)h * KD + c_lo];
     const float a_h = __expf(p.A_log[h]);
-    const uint16_t *xr = p.x + (int64_t)t0 * p.x_stride;
-    uint32_t xa = xr[ca], xb = xr[cb];
-    uint32_t graw = p.graw[(int64_t)t0 * p.g_stride + h * KD + c_lo];
-    uint32_t braw = p.braw[(int64_t)t0 * p.beta_stride + h];
+    if (tid < KD) s_nw[tid] = p.norm_weight[tid];
     __builtin_amdgcn_sched_barrier(0);
 
     const size_t es = BF16 ? 2 : 4;
@@ -824,64 +883,93 @@ __global__ void __launch_bounds__(256) kda_packed_fused_kernel(const PackedFused
         off[gi] = IO::off(r_base + gi, m);
         raw[gi] = IO::load(head, off[gi]);
     }
-    __builtin_amdgcn_sched_barrier(0);
     float st[G][8];
 #pragma unroll
     for (int gi = 0; gi < G; ++gi) IO::unpack(raw[gi], st[gi]);
-    float nw[G];
-#pragma unroll
-    for (int gi = 0; gi < G; ++gi) nw[gi] = p.norm_weight[r_base + gi];
 
-    for (int t = t0; t < t1; ++t) {
-        const int j = t - t0;
-        const int dst = j < p.max_tokens ? cols[j] : -1;
-        s_act[tid] = conv_step(cha, xa);
-        if (tid < KD) {
-            s_act[256 + tid] = conv_step(chb, xb);
-            s_d[tid] = __expf(-a_h * softplus_f(bf16_bits_to_f32(graw) + dt));
-        }
-        const float beta = sigmoid_f(bf16_bits_to_f32(braw));
-        uint32_t og[G];
-        const uint16_t *gate = p.ogate + (int64_t)t * p.ogate_stride + h * KD + r_base;
+    const int ov = tid & (KD - 1);   // output phase: this thread's value index
+    const int otk = tid >> 7;        // ... and its first token of the chunk (0 or 1)
+    for (int c0 = t0; c0 < t1; c0 += PF_CHUNK) {
+        const int nc = min(PF_CHUNK, t1 - c0);
+        // the chunk's inputs, all at once (indices clamped in bounds; unused past nc)
+        uint32_t xa[PF_CHUNK], xb[PF_CHUNK], gr[PF_CHUNK], br[PF_CHUNK], og[PF_CHUNK / 2];
+        int col[PF_CHUNK];
 #pragma unroll
-        for (int gi = 0; gi < G; ++gi) og[gi] = gate[gi];
-        if (t + 1 < t1) {  // next token's inputs while this one is computed
-            const uint16_t *xn = p.x + (int64_t)(t + 1) * p.x_stride;
-            xa = xn[ca];
-            xb = xn[cb];
-            graw = p.graw[(int64_t)(t + 1) * p.g_stride + h * KD + c_lo];
-            braw = p.braw[(int64_t)(t + 1) * p.beta_stride + h];
+        for (int i = 0; i < PF_CHUNK; ++i) {
+            const int64_t n = c0 + min(i, nc - 1);
+            const uint16_t *xn = p.x + n * p.x_stride;
+            xa[i] = xn[ca];
+            xb[i] = xn[cb];
+            gr[i] = p.graw[n * p.g_stride + h * KD + c_lo];
+            br[i] = p.braw[n * p.beta_stride + h];
+            col[i] = cols[min(c0 - t0 + i, p.max_tokens - 1)];
+        }
+#pragma unroll
+        for (int k = 0; k < PF_CHUNK / 2; ++k)
+            og[k] = p.ogate[(int64_t)(c0 + min(2 * k + otk, nc - 1)) * p.ogate_stride + h * KD + ov];
+
+        // stage: conv in token order, decays, scalars; conv checkpoints
+#pragma unroll
+        for (int i = 0; i < PF_CHUNK; ++i) {
+            if (i < nc) {
+                const int j = c0 - t0 + i;
+                const int dst = (j < p.max_tokens && col[i] > 0 && (int64_t)col[i] < p.num_slots) ? col[i] : -1;
+                s_act[i][tid] = conv_step(cha, xa[i]);
+                if (tid < KD) {
+                    s_act[i][256 + tid] = conv_step(chb, xb[i]);
+                    s_d[i][tid] = __expf(-a_h * softplus_f(bf16_bits_to_f32(gr[i]) + dt));
+                }
+                if (tid == 0) {
+                    s_beta[i] = sigmoid_f(bf16_bits_to_f32(br[i]));
+                    s_dst[i] = dst;
+                }
+                if (dst > 0) {
+                    uint16_t *cs_dst = p.conv_state + (int64_t)dst * p.conv_slot_stride;
+                    store_window(cs_dst, cha, ca, C3);
+                    if (tid < KD) store_window(cs_dst, chb, cb, C3);
+                }
+            }
         }
         __syncthreads();
 
-        TokenOps ops;
-        read_token_ops<BF16>(ops, s_act, s_act + KD, s_d, nullptr, m, p.scale, p.l2_eps, beta);
-        float o[G];
-        float ss = 0.f;
+        // the tokens, back to back
+        for (int i = 0; i < nc; ++i) {
+            TokenOps ops;
+            read_token_ops<BF16>(ops, s_act[i], s_act[i] + KD, s_d[i], nullptr, m, p.scale, p.l2_eps,
+                                 s_beta[i]);
+            float o[G];
+            float ss = 0.f;
 #pragma unroll
-        for (int gi = 0; gi < G; ++gi) {
-            o[gi] = row_update(st[gi], ops, s_act[2 * KD + r_base + gi]);
-            ss = fmaf(o[gi], o[gi], ss);
+            for (int gi = 0; gi < G; ++gi) {
+                o[gi] = row_update(st[gi], ops, s_act[i][2 * KD + r_base + gi]);
+                ss = fmaf(o[gi], o[gi], ss);
+            }
+            if (m == 0) {
+                s_red[i][wave * 4 + qd] = ss;
+#pragma unroll
+                for (int gi = 0; gi < G; ++gi) s_o[i][r_base + gi] = o[gi];
+            }
+            const int dst = s_dst[i];
+            if (dst > 0) {
+                char *ck = reinterpret_cast<char *>(p.state) + ((int64_t)dst * p.slot_stride + head_elems) * es;
+#pragma unroll
+                for (int gi = 0; gi < G; ++gi) IO::store(ck, off[gi], IO::pack(st[gi]));
+            }
         }
-        if (m == 0) s_red[wave * 4 + qd] = ss;
         __syncthreads();
-        float tot = 0.f;
+
+        // gated RMSNorm of the chunk: thread (otk, ov) handles tokens otk, otk+2, ...
 #pragma unroll
-        for (int i = 0; i < 16; ++i) tot += s_red[i];
-        const float inv = rsqrtf(tot * (1.0f / KD) + p.norm_eps);
-        if (m == 0) {
-            float y[G];
+        for (int k = 0; k < PF_CHUNK / 2; ++k) {
+            const int i = 2 * k + otk;
+            if (i < nc) {
+                float tot = 0.f;
 #pragma unroll
-            for (int gi = 0; gi < G; ++gi) y[gi] = o[gi] * inv * nw[gi] * sigmoid_f(bf16_bits_to_f32(og[gi]));
-            store_out_bf16<G>(out_at(t), y);
-        }
-        if (dst > 0 && (int64_t)dst < p.num_slots) {
-            char *ck = reinterpret_cast<char *>(p.state) + ((int64_t)dst * p.slot_stride + head_elems) * es;
-#pragma unroll
-            for (int gi = 0; gi < G; ++gi) IO::store(ck, off[gi], IO::pack(st[gi]));
-            uint16_t *cs_dst = p.conv_state + (int64_t)dst * p.conv_slot_stride;
-            store_window(cs_dst, cha, ca, C3);
-            if (tid < KD) store_window(cs_dst, chb, cb, C3);
+                for (int w = 0; w < 16; ++w) tot += s_red[i][w];
+                const float inv = rsqrtf(tot * (1.0f / KD) + p.norm_eps);
+                const float y = s_o[i][ov] * inv * s_nw[ov] * sigmoid_f(bf16_bits_to_f32(og[k]));
+                p.out[((int64_t)(c0 + i) * p.H + h) * KD + ov] = (uint16_t)(pack_bf16x2(y, 0.0f) & 0xffffu);
+            }
         }
     }
 }

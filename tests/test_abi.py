@@ -162,6 +162,16 @@ def test_recurrent_plan_geometry(N, H, bf16, vsplit):
     assert p.kernel == 1
 
 
+@pytest.mark.parametrize("N,H,vsplit", [(2, 32, 4), (2, 47, 4), (2, 48, 2), (8, 12, 2), (31, 32, 2), (32, 32, 1),
+                                        (64, 16, 1), (64, 32, 1)])
+def test_token_loop_plan_geometry(N, H, vsplit):
+    """The token loop splits a head over workgroups only while the grid is small."""
+    rc, p = plan_rec(rec_args(N=N, H=H, T=3 * N, slots=max(N, 8), varlen=True))
+    assert rc == 0, err()
+    assert (p.kernel, p.vsplit, p.rows_per_block) == (2, vsplit, D // vsplit)
+    assert p.grid_x == (N * H * vsplit + 7) // 8 * 8
+
+
 def test_varlen_and_fused_plans():
     rc, p = plan_rec(rec_args(N=64, H=16, T=190, slots=65, varlen=True))
     assert rc == 0, err()
