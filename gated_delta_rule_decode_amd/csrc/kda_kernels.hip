@@ -816,16 +816,23 @@ __device__ __forceinline__ void store_window(uint16_t *cs, const ConvChan &ch, i
     cs[2 * C3 + c] = (uint16_t)ch.c2;
 }
 
-template <bool BF16>
-__global__ void __launch_bounds__(256) kda_packed_fused_kernel(const PackedFusedParams p)
+// G value rows per DPP row, 2048/G threads per workgroup: G=8 (256 threads)
+// for large grids, G=4 (512 threads) halves each lane's per-token work for
+// smaller ones.
+template <bool BF16, int G>
+__global__ void __launch_bounds__(2048 / G) kda_packed_fused_kernel(const PackedFusedParams p)
 {
     using IO = StateIO<BF16>;
-    constexpr int G = 8;
+    constexpr int NT = 2048 / G;                 // threads
+    constexpr int NCH = (3 * KD + NT - 1) / NT;  // conv channels per thread
+    constexpr int NR = NT / 16;                  // DPP rows (RMS partials per token)
+    constexpr int TP = NT / KD;                  // tokens per pass of the output phase
+    constexpr int NOP = (PF_CHUNK + TP - 1) / TP;  // output passes per chunk
 
     __shared__ float s_act[PF_CHUNK][3 * KD];  // q | k | v activations per token
     __shared__ float s_d[PF_CHUNK][KD];
     __shared__ float s_o[PF_CHUNK][KD];        // unnormalised outputs
-    __shared__ float s_red[PF_CHUNK][16];      // RMS partial sums
+    __shared__ float s_red[PF_CHUNK][NR];      // RMS partial sums
     __shared__ float s_beta[PF_CHUNK];
     __shared__ int s_dst[PF_CHUNK];            // checkpoint slot, or -1
     __shared__ float s_nw[KD];
@@ -861,13 +868,22 @@ __global__ void __launch_bounds__(256) kda_packed_fused_kernel(const PackedFused
     }
     if (t1 <= t0) return;
 
-    // Conv windows and taps, gate parameters, then the state.
+    // Conv windows and taps of this thread's channels (local channel tid +
+    // k*NT of the head's 384; a thread past the last one loads channel 383
+    // and never stores), gate parameters, then the state.
     const int c_lo = tid & (KD - 1);
-    const int ca = conv_channel(tid, h, HC);
-    const int cb = conv_channel(256 + c_lo, h, HC);  // used by tid < 128
+    ConvChan ch[NCH];
+    int gch[NCH];
+    bool own[NCH];
     const uint16_t *cs_src = p.conv_state + (int64_t)src * p.conv_slot_stride;
-    ConvChan cha = load_chan(cs_src, p.weight, tid, h, HC, C3);
-    ConvChan chb = load_chan(cs_src, p.weight, 256 + c_lo, h, HC, C3);
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) {
+        const int cl = tid + k * NT;
+        own[k] = cl < 3 * KD;
+        const int clc = own[k] ? cl : 3 * KD - 1;
+        gch[k] = conv_channel(clc, h, HC);
+        ch[k] = load_chan(cs_src, p.weight, clc, h, HC, C3);
+    }
     const float dt = p.dt_bias[(int64_t)h * KD + c_lo];
     const float a_h = __expf(p.A_log[h]);
     if (tid < KD) s_nw[tid] = p.norm_weight[tid];
@@ -888,25 +904,25 @@ __global__ void __launch_bounds__(256) kda_packed_fused_kernel(const PackedFused
     for (int gi = 0; gi < G; ++gi) IO::unpack(raw[gi], st[gi]);
 
     const int ov = tid & (KD - 1);   // output phase: this thread's value index
-    const int otk = tid >> 7;        // ... and its first token of the chunk (0 or 1)
+    const int otk = tid >> 7;        // ... and its first token of the chunk
     for (int c0 = t0; c0 < t1; c0 += PF_CHUNK) {
         const int nc = min(PF_CHUNK, t1 - c0);
         // the chunk's inputs, all at once (indices clamped in bounds; unused past nc)
-        uint32_t xa[PF_CHUNK], xb[PF_CHUNK], gr[PF_CHUNK], br[PF_CHUNK], og[PF_CHUNK / 2];
+        uint32_t xin[PF_CHUNK][NCH], gr[PF_CHUNK], br[PF_CHUNK], og[NOP];
         int col[PF_CHUNK];
 #pragma unroll
         for (int i = 0; i < PF_CHUNK; ++i) {
             const int64_t n = c0 + min(i, nc - 1);
             const uint16_t *xn = p.x + n * p.x_stride;
-            xa[i] = xn[ca];
-            xb[i] = xn[cb];
+#pragma unroll
+            for (int k = 0; k < NCH; ++k) xin[i][k] = xn[gch[k]];
             gr[i] = p.graw[n * p.g_stride + h * KD + c_lo];
             br[i] = p.braw[n * p.beta_stride + h];
             col[i] = cols[min(c0 - t0 + i, p.max_tokens - 1)];
         }
 #pragma unroll
-        for (int k = 0; k < PF_CHUNK / 2; ++k)
-            og[k] = p.ogate[(int64_t)(c0 + min(2 * k + otk, nc - 1)) * p.ogate_stride + h * KD + ov];
+        for (int k = 0; k < NOP; ++k)
+            og[k] = p.ogate[(int64_t)(c0 + min(k * TP + otk, nc - 1)) * p.ogate_stride + h * KD + ov];
 
         // stage: conv in token order, decays, scalars; conv checkpoints
 #pragma unroll
@@ -914,19 +930,21 @@ __global__ void __launch_bounds__(256) kda_packed_fused_kernel(const PackedFused
             if (i < nc) {
                 const int j = c0 - t0 + i;
                 const int dst = (j < p.max_tokens && col[i] > 0 && (int64_t)col[i] < p.num_slots) ? col[i] : -1;
-                s_act[i][tid] = conv_step(cha, xa[i]);
-                if (tid < KD) {
-                    s_act[i][256 + tid] = conv_step(chb, xb[i]);
-                    s_d[i][tid] = __expf(-a_h * softplus_f(bf16_bits_to_f32(gr[i]) + dt));
+#pragma unroll
+                for (int k = 0; k < NCH; ++k) {
+                    const float a = conv_step(ch[k], xin[i][k]);
+                    if (own[k]) s_act[i][tid + k * NT] = a;
                 }
+                if (tid < KD) s_d[i][tid] = __expf(-a_h * softplus_f(bf16_bits_to_f32(gr[i]) + dt));
                 if (tid == 0) {
                     s_beta[i] = sigmoid_f(bf16_bits_to_f32(br[i]));
                     s_dst[i] = dst;
                 }
                 if (dst > 0) {
                     uint16_t *cs_dst = p.conv_state + (int64_t)dst * p.conv_slot_stride;
-                    store_window(cs_dst, cha, ca, C3);
-                    if (tid < KD) store_window(cs_dst, chb, cb, C3);
+#pragma unroll
+                    for (int k = 0; k < NCH; ++k)
+                        if (own[k]) store_window(cs_dst, ch[k], gch[k], C3);
                 }
             }
         }
@@ -958,14 +976,14 @@ __global__ void __launch_bounds__(256) kda_packed_fused_kernel(const PackedFused
         }
         __syncthreads();
 
-        // gated RMSNorm of the chunk: thread (otk, ov) handles tokens otk, otk+2, ...
+        // gated RMSNorm of the chunk: thread (otk, ov) handles tokens otk, otk+TP, ...
 #pragma unroll
-        for (int k = 0; k < PF_CHUNK / 2; ++k) {
-            const int i = 2 * k + otk;
+        for (int k = 0; k < NOP; ++k) {
+            const int i = k * TP + otk;
             if (i < nc) {
                 float tot = 0.f;
 #pragma unroll
-                for (int w = 0; w < 16; ++w) tot += s_red[i][w];
+                for (int w = 0; w < NR; ++w) tot += s_red[i][w];
                 const float inv = rsqrtf(tot * (1.0f / KD) + p.norm_eps);
                 const float y = s_o[i][ov] * inv * s_nw[ov] * sigmoid_f(bf16_bits_to_f32(og[k]));
                 p.out[((int64_t)(c0 + i) * p.H + h) * KD + ov] = (uint16_t)(pack_bf16x2(y, 0.0f) & 0xffffu);
@@ -1037,10 +1055,14 @@ int launch_packed_fused(const PackedFusedParams &p, const Launch &l, void *strea
 {
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
-    if (l.bf16_state)
-        hipLaunchKernelGGL(kda_packed_fused_kernel<true>, dim3(l.grid), dim3(l.block), 0, s, p);
-    else
-        hipLaunchKernelGGL(kda_packed_fused_kernel<false>, dim3(l.grid), dim3(l.block), 0, s, p);
+    const dim3 grid(l.grid), block(l.block);
+    switch (l.block * 2 + l.bf16_state) {
+    case 256 * 2 + 0: hipLaunchKernelGGL((kda_packed_fused_kernel<false, 8>), grid, block, 0, s, p); break;
+    case 256 * 2 + 1: hipLaunchKernelGGL((kda_packed_fused_kernel<true, 8>), grid, block, 0, s, p); break;
+    case 512 * 2 + 0: hipLaunchKernelGGL((kda_packed_fused_kernel<false, 4>), grid, block, 0, s, p); break;
+    case 512 * 2 + 1: hipLaunchKernelGGL((kda_packed_fused_kernel<true, 4>), grid, block, 0, s, p); break;
+    default: return record(hipErrorInvalidValue);
+    }
     return record(hipGetLastError());
 }
 

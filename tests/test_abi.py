@@ -409,7 +409,10 @@ def plan_pf(a):
 def test_packed_fused_plan_and_validation():
     rc, p = plan_pf(packed_fused_args())
     assert rc == 0, err()
-    assert (p.kernel, p.grid_x, p.block, p.rows_per_block) == (4, 3 * 12, 256, 128)
+    assert (p.kernel, p.grid_x, p.block, p.rows_per_block) == (4, 3 * 12, 512, 128)
+    rc, p = plan_pf(packed_fused_args(N=128, T=5, rows=640, slots=700))
+    assert rc == 0, err()
+    assert (p.grid_x, p.block) == (128 * 12, 256)
     assert plan_pf(packed_fused_args(bf16=True))[0] == 0, err()
     a = packed_fused_args(rows=0)  # no rows at all: every sequence is empty
     a.x = a.raw_gate = a.raw_beta = a.output_gate = a.out = None

@@ -95,10 +95,17 @@ def test_padding_null_sequences_and_checkpoint_columns():
         assert torch.equal(P.bits(o[row].cpu()), torch.zeros(4 * D, dtype=torch.int16)), row
 
 
+@pytest.mark.parametrize("rows", [37, 128])
 @pytest.mark.parametrize("state_dtype", [torch.float32, torch.bfloat16])
-def test_single_token_rows_equal_fused_decode_bitwise(state_dtype):
-    say(f"packed fused T=1 vs fused_kda_decode H=8 {state_dtype} seed=8200")
-    fc = synth.fused_case(8200, rows=37, H=8, num_slots=64, state_dtype=state_dtype, device=DEV,
+def test_single_token_rows_equal_fused_decode(state_dtype, rows):
+    """One token per row, start column = the fused call's index: the state and
+    conv caches equal fused_kda_decode's bit for bit (the per-row arithmetic
+    is the same).  At 128 rows x 8 heads both calls use 8 value rows per lane
+    and the outputs are bitwise equal too; at 37 rows the packed call uses 4
+    per lane, whose RMS partial sums are added in another order, so outputs
+    may differ by one bf16 ulp."""
+    say(f"packed fused T=1 vs fused_kda_decode H=8 rows={rows} {state_dtype} seed=8200")
+    fc = synth.fused_case(8200, rows=rows, H=8, num_slots=192, state_dtype=state_dtype, device=DEV,
                           null_zero=2, null_neg=2)
     st0, cs0 = fc.state.clone(), fc.conv_state.clone()
     o_f = fused_kda_decode(fc.x, fc.weight, fc.conv_state, fc.raw_gate, fc.raw_beta, fc.A_log, fc.dt_bias,
@@ -107,13 +114,19 @@ def test_single_token_rows_equal_fused_decode_bitwise(state_dtype):
     fc.state.copy_(st0)
     fc.conv_state.copy_(cs0)
     o_p = packed_fused_kda_decode(fc.x, fc.weight, fc.conv_state, fc.raw_gate, fc.raw_beta, fc.A_log,
-                                  fc.dt_bias, fc.state_indices.reshape(37, 1), fc.state, fc.output_gate,
-                                  fc.norm_weight, query_start_loc=torch.arange(38, dtype=torch.int32, device=DEV),
-                                  num_accepted_tokens=torch.ones(37, dtype=torch.int32, device=DEV))
+                                  fc.dt_bias, fc.state_indices.reshape(rows, 1), fc.state, fc.output_gate,
+                                  fc.norm_weight,
+                                  query_start_loc=torch.arange(rows + 1, dtype=torch.int32, device=DEV),
+                                  num_accepted_tokens=torch.ones(rows, dtype=torch.int32, device=DEV))
     torch.cuda.synchronize()
-    assert torch.equal(P.bits(o_f), P.bits(o_p))
     assert torch.equal(P.bits(s_f), P.bits(fc.state))
     assert torch.equal(P.bits(c_f), P.bits(fc.conv_state))
+    if rows == 128:
+        assert torch.equal(P.bits(o_f), P.bits(o_p))
+    else:
+        a = o_f.float().cpu().numpy().astype(np.float64).ravel()
+        b = o_p.float().cpu().numpy().astype(np.float64).ravel()
+        assert np.all(np.abs(a - b) <= P.bf16_ulp(a)), "outputs differ by more than one bf16 ulp"
 
 
 def test_tokens_equal_chained_single_token_calls_bitwise():
