@@ -260,109 +260,118 @@ def rotating(torch, timer, calls, reps=8):
     return timer.run(graph.replay, reps) / len(calls)
 
 
-def extra_workloads(torch, dev, timer, pool32):
+def extra_workloads(torch, dev, timer, pool32, only=None):
     from gated_delta_rule_decode_amd import (fused_kda_decode, packed_fused_kda_decode, packed_kda_decode,
                                              recurrent_kda, synth)
     out = {}
+    want = lambda name: only is None or only in name  # noqa: E731
+    g2 = torch.Generator(device=dev)
+    g2.manual_seed(7)
+    # slot order of the T=1 mode and verify workloads on the headline pool
+    mperm = torch.randperm(pool32.shape[0], generator=g2, device=dev).to(torch.int32)
     H = 32
     SLOTS = pool32.shape[0]
-    # H=32 fp32 batch sweep on the 8 GiB pool: disjoint slot sets per B, a
-    # cycle of >= 1 GiB of state
-    sweep = []
-    g2 = torch.Generator(device=dev)
-    for Bs in (1, 8, 32, 128, 256, 512):
-        cs = synth.recurrent_case(1000 + Bs, n_seqs=Bs, H=H, num_slots=1, device=dev)
-        g2.manual_seed(1000 + Bs)
-        perm = torch.randperm(SLOTS, generator=g2, device=dev).to(torch.int32)
-        o = torch.empty((Bs, 1, H, D), dtype=torch.bfloat16, device=dev)
-        r4 = lambda t, n=Bs: t.reshape(n, 1, H, D)  # noqa: E731
-        calls = []
-        for j in range(n_sets(Bs * H * D * D * 4, SLOTS // Bs)):
-            ids = perm[j * Bs:(j + 1) * Bs].contiguous()
-            calls.append(lambda cs=cs, ids=ids, o=o, r4=r4, n=Bs: recurrent_kda(
-                r4(cs.q), r4(cs.k), r4(cs.v), r4(cs.g), cs.beta.reshape(n, 1, H), cs.A_log,
-                cs.dt_bias, initial_state=pool32, state_indices=ids, output=o))
+    if want("recurrent_t1_h32_fp32"):
+        # H=32 fp32 batch sweep on the 8 GiB pool: disjoint slot sets per B, a
+        # cycle of >= 1 GiB of state
+        sweep = []
+        g2 = torch.Generator(device=dev)
+        for Bs in (1, 8, 32, 128, 256, 512):
+            cs = synth.recurrent_case(1000 + Bs, n_seqs=Bs, H=H, num_slots=1, device=dev)
+            g2.manual_seed(1000 + Bs)
+            perm = torch.randperm(SLOTS, generator=g2, device=dev).to(torch.int32)
+            o = torch.empty((Bs, 1, H, D), dtype=torch.bfloat16, device=dev)
+            r4 = lambda t, n=Bs: t.reshape(n, 1, H, D)  # noqa: E731
+            calls = []
+            for j in range(n_sets(Bs * H * D * D * 4, SLOTS // Bs)):
+                ids = perm[j * Bs:(j + 1) * Bs].contiguous()
+                calls.append(lambda cs=cs, ids=ids, o=o, r4=r4, n=Bs: recurrent_kda(
+                    r4(cs.q), r4(cs.k), r4(cs.v), r4(cs.g), cs.beta.reshape(n, 1, H), cs.A_log,
+                    cs.dt_bias, initial_state=pool32, state_indices=ids, output=o))
+            t_us = rotating(torch, timer, calls)
+            bts = t1_bytes(Bs, 0, H, 4)
+            sweep.append({"B": Bs, "us": t_us, "rows_per_s": Bs / (t_us * 1e-6),
+                          "state_GBps": t1_state_bytes(Bs, H, 4) / (t_us * 1e-6) / 1e9,
+                          "GBps": bts / (t_us * 1e-6) / 1e9,
+                          "frac": bts / (t_us * 1e-6) / 1e9 / HBM_PEAK_GBPS})
+            log(f"H=32 fp32 B={Bs}: {t_us:.1f} us, {sweep[-1]['GBps']:.0f} GB/s")
+        out["recurrent_t1_h32_fp32"] = sweep
+
+    if want("packed_t1_h12_bf16"):
+        # packed H=12, bf16 pool [8192,12,128,128] (3 GiB), 1/8 of the rows inactive,
+        # disjoint slot sets per B, a cycle of >= 1 GiB of state
+        pcase = synth.packed_case(2000, B=512, H=12, num_slots=8192, device=dev)
+        pperm = torch.randperm(8192 - 1, generator=g2, device=dev).to(torch.int32) + 1
+        sweep = []
+        for Bs in (1, 8, 16, 31, 32, 64, 128, 256, 512):
+            nnull = Bs // 8
+            o = torch.empty((Bs, 1, 12, D), dtype=torch.bfloat16, device=dev)
+            calls = []
+            for j in range(n_sets((Bs - nnull) * 12 * D * D * 2, 8191 // Bs, lo=8)):
+                ids = pperm[j * Bs:(j + 1) * Bs].clone()
+                ids[:nnull] = -1
+                calls.append(lambda ids=ids, o=o, n=Bs: packed_kda_decode(
+                    pcase.mixed_qkv[:n], pcase.raw_gate[:n], pcase.raw_beta[:n], pcase.A_log,
+                    pcase.dt_bias, pcase.state, ids, output=o))
+            t_us = rotating(torch, timer, calls)
+            live = Bs - nnull
+            bts = t1_bytes(live, nnull, 12, 2)
+            sweep.append({"B": Bs, "live": live, "us": t_us, "rows_per_s": live / (t_us * 1e-6),
+                          "state_GBps": t1_state_bytes(live, 12, 2) / (t_us * 1e-6) / 1e9,
+                          "GBps": bts / (t_us * 1e-6) / 1e9,
+                          "frac": bts / (t_us * 1e-6) / 1e9 / HBM_PEAK_GBPS})
+            log(f"packed H=12 bf16 B={Bs} ({live} live): {t_us:.1f} us, {sweep[-1]['GBps']:.0f} GB/s")
+        out["packed_t1_h12_bf16"] = sweep
+        del pcase
+        torch.cuda.empty_cache()
+
+    if want("fused_h32_rows256_fp32"):
+        # fused, rows=256, H=32, fp32 pool [2048,32,128,128], 16 null rows; two
+        # disjoint slot sets
+        fc = synth.fused_case(3000, rows=256, H=32, num_slots=2048, device=dev, null_zero=8, null_neg=8)
+        idx2 = fc.state_indices.clone()
+        live_mask = idx2 > 0
+        free = torch.ones(2048, dtype=torch.bool, device=dev)
+        free[0] = False
+        free[idx2[live_mask].long()] = False
+        spare = torch.nonzero(free).flatten()[:int(live_mask.sum())].to(torch.int32)
+        idx2[live_mask] = spare
+        o = torch.empty((1, 256, 32, D), dtype=torch.bfloat16, device=dev)
+        calls = [lambda ids=ids: fused_kda_decode(fc.x, fc.weight, fc.conv_state, fc.raw_gate, fc.raw_beta,
+                                                  fc.A_log, fc.dt_bias, ids, fc.state, fc.output_gate,
+                                                  fc.norm_weight, output=o)
+                 for ids in (fc.state_indices, idx2)]
         t_us = rotating(torch, timer, calls)
-        bts = t1_bytes(Bs, 0, H, 4)
-        sweep.append({"B": Bs, "us": t_us, "rows_per_s": Bs / (t_us * 1e-6),
-                      "state_GBps": t1_state_bytes(Bs, H, 4) / (t_us * 1e-6) / 1e9,
-                      "GBps": bts / (t_us * 1e-6) / 1e9,
-                      "frac": bts / (t_us * 1e-6) / 1e9 / HBM_PEAK_GBPS})
-        log(f"H=32 fp32 B={Bs}: {t_us:.1f} us, {sweep[-1]['GBps']:.0f} GB/s")
-    out["recurrent_t1_h32_fp32"] = sweep
+        bts = fused_bytes(240, 16, 32, 4)
+        out["fused_h32_rows256_fp32"] = {"us": t_us, "rows_per_s": 240 / (t_us * 1e-6),
+                                         "GBps": bts / (t_us * 1e-6) / 1e9,
+                                         "frac": bts / (t_us * 1e-6) / 1e9 / HBM_PEAK_GBPS}
+        log(f"fused H=32 rows=256: {t_us:.1f} us, {bts / (t_us * 1e-6) / 1e9:.0f} GB/s")
+        del fc
+        torch.cuda.empty_cache()
 
-    # packed H=12, bf16 pool [8192,12,128,128] (3 GiB), 1/8 of the rows inactive,
-    # disjoint slot sets per B, a cycle of >= 1 GiB of state
-    pcase = synth.packed_case(2000, B=512, H=12, num_slots=8192, device=dev)
-    perm = torch.randperm(8192 - 1, generator=g2, device=dev).to(torch.int32) + 1
-    sweep = []
-    for Bs in (1, 8, 16, 31, 32, 64, 128, 256, 512):
-        nnull = Bs // 8
-        o = torch.empty((Bs, 1, 12, D), dtype=torch.bfloat16, device=dev)
-        calls = []
-        for j in range(n_sets((Bs - nnull) * 12 * D * D * 2, 8191 // Bs, lo=8)):
-            ids = perm[j * Bs:(j + 1) * Bs].clone()
-            ids[:nnull] = -1
-            calls.append(lambda ids=ids, o=o, n=Bs: packed_kda_decode(
-                pcase.mixed_qkv[:n], pcase.raw_gate[:n], pcase.raw_beta[:n], pcase.A_log,
-                pcase.dt_bias, pcase.state, ids, output=o))
+    if want("varlen_h16_n64_fp32_ckpt"):
+        # ragged T>=2: H=16, N=64, lengths U{0..6}, fp32 checkpoints; the pool has
+        # 16 disjoint slot sets (1 GiB of state per cycle)
+        lengths = synth.ragged_lengths(4000, 64, 0, 6)
+        vc = synth.recurrent_case(4000, n_seqs=64, H=16, num_slots=16 * 64 + 1, device=dev,
+                                  lengths=lengths, slot_lo=1)
+        T = sum(lengths)
+        ck = torch.empty((T, 16, D, D), dtype=torch.float32, device=dev)
+        o = torch.empty((1, T, 16, D), dtype=torch.bfloat16, device=dev)
+        r1 = lambda t: t.reshape(1, T, *t.shape[1:])  # noqa: E731
+        calls = [lambda ids=(vc.state_indices + 64 * j).contiguous(): recurrent_kda(
+            r1(vc.q), r1(vc.k), r1(vc.v), r1(vc.g), r1(vc.beta), vc.A_log, vc.dt_bias,
+            initial_state=vc.state, state_indices=ids, cu_seqlens=vc.cu_seqlens, output=o,
+            intermediate_states=ck) for j in range(16)]
         t_us = rotating(torch, timer, calls)
-        live = Bs - nnull
-        bts = t1_bytes(live, nnull, 12, 2)
-        sweep.append({"B": Bs, "live": live, "us": t_us, "rows_per_s": live / (t_us * 1e-6),
-                      "state_GBps": t1_state_bytes(live, 12, 2) / (t_us * 1e-6) / 1e9,
-                      "GBps": bts / (t_us * 1e-6) / 1e9,
-                      "frac": bts / (t_us * 1e-6) / 1e9 / HBM_PEAK_GBPS})
-        log(f"packed H=12 bf16 B={Bs} ({live} live): {t_us:.1f} us, {sweep[-1]['GBps']:.0f} GB/s")
-    out["packed_t1_h12_bf16"] = sweep
-    del pcase
-    torch.cuda.empty_cache()
-
-    # fused, rows=256, H=32, fp32 pool [2048,32,128,128], 16 null rows; two
-    # disjoint slot sets
-    fc = synth.fused_case(3000, rows=256, H=32, num_slots=2048, device=dev, null_zero=8, null_neg=8)
-    idx2 = fc.state_indices.clone()
-    live_mask = idx2 > 0
-    free = torch.ones(2048, dtype=torch.bool, device=dev)
-    free[0] = False
-    free[idx2[live_mask].long()] = False
-    spare = torch.nonzero(free).flatten()[:int(live_mask.sum())].to(torch.int32)
-    idx2[live_mask] = spare
-    o = torch.empty((1, 256, 32, D), dtype=torch.bfloat16, device=dev)
-    calls = [lambda ids=ids: fused_kda_decode(fc.x, fc.weight, fc.conv_state, fc.raw_gate, fc.raw_beta,
-                                              fc.A_log, fc.dt_bias, ids, fc.state, fc.output_gate,
-                                              fc.norm_weight, output=o)
-             for ids in (fc.state_indices, idx2)]
-    t_us = rotating(torch, timer, calls)
-    bts = fused_bytes(240, 16, 32, 4)
-    out["fused_h32_rows256_fp32"] = {"us": t_us, "rows_per_s": 240 / (t_us * 1e-6),
-                                     "GBps": bts / (t_us * 1e-6) / 1e9,
-                                     "frac": bts / (t_us * 1e-6) / 1e9 / HBM_PEAK_GBPS}
-    log(f"fused H=32 rows=256: {t_us:.1f} us, {bts / (t_us * 1e-6) / 1e9:.0f} GB/s")
-    del fc
-    torch.cuda.empty_cache()
-
-    # ragged T>=2: H=16, N=64, lengths U{0..6}, fp32 checkpoints; the pool has
-    # 16 disjoint slot sets (1 GiB of state per cycle)
-    lengths = synth.ragged_lengths(4000, 64, 0, 6)
-    vc = synth.recurrent_case(4000, n_seqs=64, H=16, num_slots=16 * 64 + 1, device=dev,
-                              lengths=lengths, slot_lo=1)
-    T = sum(lengths)
-    ck = torch.empty((T, 16, D, D), dtype=torch.float32, device=dev)
-    o = torch.empty((1, T, 16, D), dtype=torch.bfloat16, device=dev)
-    r1 = lambda t: t.reshape(1, T, *t.shape[1:])  # noqa: E731
-    calls = [lambda ids=(vc.state_indices + 64 * j).contiguous(): recurrent_kda(
-        r1(vc.q), r1(vc.k), r1(vc.v), r1(vc.g), r1(vc.beta), vc.A_log, vc.dt_bias,
-        initial_state=vc.state, state_indices=ids, cu_seqlens=vc.cu_seqlens, output=o,
-        intermediate_states=ck) for j in range(16)]
-    t_us = rotating(torch, timer, calls)
-    bts = varlen_bytes(lengths, 16, 4)
-    out["varlen_h16_n64_fp32_ckpt"] = {"us": t_us, "tokens": T, "tokens_per_s": T / (t_us * 1e-6),
-                                       "GBps": bts / (t_us * 1e-6) / 1e9,
-                                       "frac": bts / (t_us * 1e-6) / 1e9 / HBM_PEAK_GBPS}
-    log(f"varlen H=16 N=64 T={T}: {t_us:.1f} us, {bts / (t_us * 1e-6) / 1e9:.0f} GB/s")
-    del vc, ck
-    torch.cuda.empty_cache()
+        bts = varlen_bytes(lengths, 16, 4)
+        out["varlen_h16_n64_fp32_ckpt"] = {"us": t_us, "tokens": T, "tokens_per_s": T / (t_us * 1e-6),
+                                           "GBps": bts / (t_us * 1e-6) / 1e9,
+                                           "frac": bts / (t_us * 1e-6) / 1e9 / HBM_PEAK_GBPS}
+        log(f"varlen H=16 N=64 T={T}: {t_us:.1f} us, {bts / (t_us * 1e-6) / 1e9:.0f} GB/s")
+        del vc, ck
+        torch.cuda.empty_cache()
 
     def modes_entry(name, calls, bts, rows):
         t = rotating(torch, timer, calls)
@@ -370,82 +379,86 @@ def extra_workloads(torch, dev, timer, pool32):
                      "frac": bts / (t * 1e-6) / 1e9 / HBM_PEAK_GBPS}
         log(f"{name}: {t:.1f} us, {out[name]['GBps']:.0f} GB/s")
 
-    # grouped value heads: H=16 q/k heads, HV=32 value heads, fp32 pool, T=1, B=256
     B = 256
-    gc = synth.recurrent_case(7000, n_seqs=B, H=16, HV=32, num_slots=1, device=dev)
-    perm = torch.randperm(SLOTS, generator=g2, device=dev).to(torch.int32)
-    o = torch.empty((B, 1, 32, D), dtype=torch.bfloat16, device=dev)
+    o1 = torch.empty((B, 1, 32, D), dtype=torch.bfloat16, device=dev)
     r = lambda t: t.reshape(B, 1, *t.shape[1:])  # noqa: E731
-    calls = [lambda ids=perm[j * B:(j + 1) * B].contiguous(): recurrent_kda(
-        r(gc.q), r(gc.k), r(gc.v), r(gc.g), r(gc.beta), gc.A_log, gc.dt_bias, initial_state=pool32,
-        state_indices=ids, output=o) for j in range(4)]
-    modes_entry("grouped_t1_h16_hv32_fp32_b256", calls, modes_bytes(B, B, 16, 32, 4), B)
+    if want("grouped_t1_h16_hv32_fp32_b256"):
+        # grouped value heads: H=16 q/k heads, HV=32 value heads, fp32 pool, T=1, B=256
+        gc = synth.recurrent_case(7000, n_seqs=B, H=16, HV=32, num_slots=1, device=dev)
+        calls = [lambda ids=mperm[j * B:(j + 1) * B].contiguous(): recurrent_kda(
+            r(gc.q), r(gc.k), r(gc.v), r(gc.g), r(gc.beta), gc.A_log, gc.dt_bias, initial_state=pool32,
+            state_indices=ids, output=o1) for j in range(4)]
+        modes_entry("grouped_t1_h16_hv32_fp32_b256", calls, modes_bytes(B, B, 16, 32, 4), B)
 
-    # precomputed gate (fp32 log-decay and beta), H=32, fp32 pool, T=1, B=256
-    pc = synth.recurrent_case(7100, n_seqs=B, H=32, num_slots=1, device=dev, gate="precomputed")
-    calls = [lambda ids=perm[j * B:(j + 1) * B].contiguous(): recurrent_kda(
-        r(pc.q), r(pc.k), r(pc.v), r(pc.g), r(pc.beta), initial_state=pool32, state_indices=ids,
-        output=o) for j in range(4)]
-    modes_entry("precomputed_t1_h32_fp32_b256", calls,
-                modes_bytes(B, B, 32, 32, 4, gate_bytes=4, beta_bytes=4, gate_params=False), B)
+    if want("precomputed_t1_h32_fp32_b256"):
+        # precomputed gate (fp32 log-decay and beta), H=32, fp32 pool, T=1, B=256
+        pc = synth.recurrent_case(7100, n_seqs=B, H=32, num_slots=1, device=dev, gate="precomputed")
+        calls = [lambda ids=mperm[j * B:(j + 1) * B].contiguous(): recurrent_kda(
+            r(pc.q), r(pc.k), r(pc.v), r(pc.g), r(pc.beta), initial_state=pool32, state_indices=ids,
+            output=o1) for j in range(4)]
+        modes_entry("precomputed_t1_h32_fp32_b256", calls,
+                    modes_bytes(B, B, 32, 32, 4, gate_bytes=4, beta_bytes=4, gate_params=False), B)
 
-    # speculative verify: read-only pool, batched [64, 4, 32, 128], H=32 fp32
     Bv, Tv = 64, 4
     vv = synth.recurrent_case(7200, n_seqs=Bv, H=32, num_slots=1, device=dev, lengths=[Tv] * Bv)
     ov = torch.empty((Bv, Tv, 32, D), dtype=torch.bfloat16, device=dev)
     rb = lambda t: t.reshape(Bv, Tv, *t.shape[1:])  # noqa: E731
-    calls = [lambda ids=perm[j * Bv:(j + 1) * Bv].contiguous(): recurrent_kda(
-        rb(vv.q), rb(vv.k), rb(vv.v), rb(vv.g), rb(vv.beta), vv.A_log, vv.dt_bias,
-        initial_state=pool32, state_indices=ids, output=ov, disable_state_update=True)
-        for j in range(8)]
-    modes_entry("verify_readonly_b64_t4_h32_fp32", calls,
-                modes_bytes(Bv, Bv * Tv, 32, 32, 4, write_state=False), Bv)
+    if want("verify_readonly_b64_t4_h32_fp32"):
+        # speculative verify: read-only pool, batched [64, 4, 32, 128], H=32 fp32
+        calls = [lambda ids=mperm[j * Bv:(j + 1) * Bv].contiguous(): recurrent_kda(
+            rb(vv.q), rb(vv.k), rb(vv.v), rb(vv.g), rb(vv.beta), vv.A_log, vv.dt_bias,
+            initial_state=pool32, state_indices=ids, output=ov, disable_state_update=True)
+            for j in range(8)]
+        modes_entry("verify_readonly_b64_t4_h32_fp32", calls,
+                    modes_bytes(Bv, Bv * Tv, 32, 32, 4, write_state=False), Bv)
 
-    # the same verify call recording the per-token corrections (fp32) and raw
-    # key | gate (fp32) into slot-indexed caches
-    corr = torch.empty((SLOTS, 32, Tv, D), dtype=torch.float32, device=dev)
-    kgc = torch.empty((SLOTS, 32, Tv, 2 * D), dtype=torch.float32, device=dev)
-    calls = [lambda ids=perm[j * Bv:(j + 1) * Bv].contiguous(): recurrent_kda(
-        rb(vv.q), rb(vv.k), rb(vv.v), rb(vv.g), rb(vv.beta), vv.A_log, vv.dt_bias,
-        initial_state=pool32, state_indices=ids, output=ov, disable_state_update=True,
-        correction_cache=corr, kg_cache=kgc) for j in range(8)]
-    modes_entry("verify_caches_b64_t4_h32_fp32", calls,
-                modes_bytes(Bv, Bv * Tv, 32, 32, 4, write_state=False) + Bv * Tv * 32 * 3 * D * 4, Bv)
-    del corr, kgc
-    torch.cuda.empty_cache()
+    if want("verify_caches_b64_t4_h32_fp32"):
+        # the same verify call recording the per-token corrections (fp32) and raw
+        # key | gate (fp32) into slot-indexed caches
+        corr = torch.empty((SLOTS, 32, Tv, D), dtype=torch.float32, device=dev)
+        kgc = torch.empty((SLOTS, 32, Tv, 2 * D), dtype=torch.float32, device=dev)
+        calls = [lambda ids=mperm[j * Bv:(j + 1) * Bv].contiguous(): recurrent_kda(
+            rb(vv.q), rb(vv.k), rb(vv.v), rb(vv.g), rb(vv.beta), vv.A_log, vv.dt_bias,
+            initial_state=pool32, state_indices=ids, output=ov, disable_state_update=True,
+            correction_cache=corr, kg_cache=kgc) for j in range(8)]
+        modes_entry("verify_caches_b64_t4_h32_fp32", calls,
+                    modes_bytes(Bv, Bv * Tv, 32, 32, 4, write_state=False) + Bv * Tv * 32 * 3 * D * 4, Bv)
+        del corr, kgc
+        torch.cuda.empty_cache()
 
-    # packed fused speculative decode, T=5 tokens per sequence, one accepted
-    # token; disjoint checkpoint-slot sets per call
-    pf = []
-    for Hs, Ns_list in ((12, (1, 8, 32, 128)), (24, (8, 128))):
-        for sdt, sb in ((torch.float32, 4), (torch.bfloat16, 2)):
-            T = 5
-            pool_slots = 4 * 128 * T + 1
-            pc = synth.packed_fused_case(8500 + Hs, lengths=[T] * 128, H=Hs, num_slots=pool_slots,
-                                         max_tokens=T, state_dtype=sdt, device=dev, accepted="one")
-            g2.manual_seed(8500 + Hs)
-            pperm = torch.randperm(pool_slots - 1, generator=g2, device=dev).to(torch.int32) + 1
-            for Ns in Ns_list:
-                rows = Ns * T
-                o = torch.empty((1, rows, Hs, D), dtype=torch.bfloat16, device=dev)
-                qsl = (torch.arange(Ns + 1, dtype=torch.int32, device=dev) * T).contiguous()
-                acc = torch.ones(Ns, dtype=torch.int32, device=dev)
-                nset = n_sets(Ns * Hs * (1 + T) * D * D * sb, (pool_slots - 1) // (Ns * T))
-                calls = [lambda ids=pperm[k * Ns * T:(k + 1) * Ns * T].reshape(Ns, T).contiguous(), o=o, rows=rows,
-                         qsl=qsl, acc=acc: packed_fused_kda_decode(
-                             pc.x[:rows], pc.weight, pc.conv_state, pc.raw_gate[:rows], pc.raw_beta[:rows], pc.A_log,
-                             pc.dt_bias, ids, pc.state, pc.output_gate[:rows], pc.norm_weight, output=o,
-                             query_start_loc=qsl, num_accepted_tokens=acc)
-                         for k in range(nset)]
-                t_us = rotating(torch, timer, calls)
-                bts = packed_fused_bytes(Ns, T, Hs, sb)
-                pf.append({"H": Hs, "N": Ns, "T": T, "state": "bf16" if sb == 2 else "fp32", "us": t_us,
-                           "GBps": bts / (t_us * 1e-6) / 1e9, "frac": bts / (t_us * 1e-6) / 1e9 / HBM_PEAK_GBPS})
-                log(f"packed fused H={Hs} N={Ns} T={T} {pf[-1]['state']}: {t_us:.1f} us, "
-                    f"{pf[-1]['GBps']:.0f} GB/s")
-            del pc
-            torch.cuda.empty_cache()
-    out["packed_fused_t5_accept1"] = pf
+    if want("packed_fused_t5_accept1"):
+        # packed fused speculative decode, T=5 tokens per sequence, one accepted
+        # token; disjoint checkpoint-slot sets per call
+        pf = []
+        for Hs, Ns_list in ((12, (1, 8, 32, 128)), (24, (8, 128))):
+            for sdt, sb in ((torch.float32, 4), (torch.bfloat16, 2)):
+                T = 5
+                pool_slots = 4 * 128 * T + 1
+                pc = synth.packed_fused_case(8500 + Hs, lengths=[T] * 128, H=Hs, num_slots=pool_slots,
+                                             max_tokens=T, state_dtype=sdt, device=dev, accepted="one")
+                g2.manual_seed(8500 + Hs)
+                pperm = torch.randperm(pool_slots - 1, generator=g2, device=dev).to(torch.int32) + 1
+                for Ns in Ns_list:
+                    rows = Ns * T
+                    o = torch.empty((1, rows, Hs, D), dtype=torch.bfloat16, device=dev)
+                    qsl = (torch.arange(Ns + 1, dtype=torch.int32, device=dev) * T).contiguous()
+                    acc = torch.ones(Ns, dtype=torch.int32, device=dev)
+                    nset = n_sets(Ns * Hs * (1 + T) * D * D * sb, (pool_slots - 1) // (Ns * T))
+                    calls = [lambda ids=pperm[k * Ns * T:(k + 1) * Ns * T].reshape(Ns, T).contiguous(), o=o, rows=rows,
+                             qsl=qsl, acc=acc: packed_fused_kda_decode(
+                                 pc.x[:rows], pc.weight, pc.conv_state, pc.raw_gate[:rows], pc.raw_beta[:rows], pc.A_log,
+                                 pc.dt_bias, ids, pc.state, pc.output_gate[:rows], pc.norm_weight, output=o,
+                                 query_start_loc=qsl, num_accepted_tokens=acc)
+                             for k in range(nset)]
+                    t_us = rotating(torch, timer, calls)
+                    bts = packed_fused_bytes(Ns, T, Hs, sb)
+                    pf.append({"H": Hs, "N": Ns, "T": T, "state": "bf16" if sb == 2 else "fp32", "us": t_us,
+                               "GBps": bts / (t_us * 1e-6) / 1e9, "frac": bts / (t_us * 1e-6) / 1e9 / HBM_PEAK_GBPS})
+                    log(f"packed fused H={Hs} N={Ns} T={T} {pf[-1]['state']}: {t_us:.1f} us, "
+                        f"{pf[-1]['GBps']:.0f} GB/s")
+                del pc
+                torch.cuda.empty_cache()
+        out["packed_fused_t5_accept1"] = pf
     return out
 
 
@@ -459,6 +472,8 @@ def main():
     ap.add_argument("--B", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="headline workload only")
+    ap.add_argument("--extra-only", default=None,
+                    help="run only the extra workloads whose name contains this text (for profiling)")
     ap.add_argument("--copy-calibrate", action="store_true",
                     help="also run a 1 GiB device copy (for counter scaling under rocprofv3)")
     args = ap.parse_args()
@@ -556,7 +571,7 @@ def main():
     }
 
     if not args.no_extra:
-        result["workloads"] = extra_workloads(torch, dev, timer, pool)
+        result["workloads"] = extra_workloads(torch, dev, timer, pool, args.extra_only)
 
     print(json.dumps(result), flush=True)
 
