@@ -39,16 +39,24 @@ int ok()
     return KDA_OK;
 }
 
+// Extents are computed in 128-bit arithmetic from validated (non-negative)
+// sizes and strides, so no product can wrap; a buffer that would span more
+// than 2^48 bytes (or past the end of the address space) is an error.
+typedef unsigned __int128 u128;
+constexpr u128 MAX_BYTES = (u128)1 << 48;
+
 // Byte range [lo, hi) of a buffer; empty when lo == hi.
 struct Range {
     uintptr_t lo, hi;
     const char *name;
+    bool too_large;
 };
 
-Range span(const void *p, uint64_t bytes, const char *name)
+Range span(const void *p, u128 bytes, const char *name)
 {
-    uintptr_t lo = reinterpret_cast<uintptr_t>(p);
-    return Range{lo, lo + (uintptr_t)bytes, name};
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    if (bytes > MAX_BYTES || (u128)lo + bytes > (u128)UINTPTR_MAX) return Range{lo, lo, name, true};
+    return Range{lo, lo + (uintptr_t)bytes, name, false};
 }
 
 bool overlap(const Range &a, const Range &b)
@@ -60,6 +68,10 @@ bool overlap(const Range &a, const Range &b)
 // Each written range must not overlap any other range (written or read).
 int check_alias(const Range *w, int nw, const Range *r, int nr)
 {
+    for (int i = 0; i < nw + nr; ++i) {
+        const Range &x = i < nw ? w[i] : r[i - nw];
+        if (x.too_large) return fail(KDA_ERR_SHAPE, "%s would span more than 2^48 bytes", x.name);
+    }
     for (int i = 0; i < nw; ++i) {
         for (int j = i + 1; j < nw; ++j)
             if (overlap(w[i], w[j]))
@@ -80,11 +92,14 @@ constexpr int64_t MAX_INDEX = 0x7fffffffLL;
 
 int elem_size(int32_t dtype) { return dtype == KDA_DTYPE_F32 ? 4 : 2; }
 
-// Extent in elements of a row-strided [rows, width] tensor.
-uint64_t rows_extent(int64_t rows, int64_t stride, int64_t width)
+// Extent in elements of a row-strided [rows, width] tensor (stride >= width >= 0).
+u128 rows_extent(int64_t rows, int64_t stride, int64_t width)
 {
-    return rows <= 0 ? 0 : (uint64_t)(rows - 1) * (uint64_t)stride + (uint64_t)width;
+    return rows <= 0 ? 0 : (u128)(uint64_t)(rows - 1) * (uint64_t)stride + (uint64_t)width;
 }
+
+// Largest row / slot stride accepted, in elements (checked before any product).
+constexpr int64_t MAX_STRIDE = (int64_t)1 << 44;
 
 int check_gate(int32_t mode)
 {
@@ -102,17 +117,17 @@ int check_pool(const void *state, int32_t dtype, int64_t num_slots, int64_t slot
         return fail(KDA_ERR_DTYPE, "state_dtype %d is neither F32 nor BF16", (int)dtype);
     if (num_slots < 1 || num_slots > MAX_INDEX)
         return fail(KDA_ERR_SHAPE, "num_slots %lld out of range", (long long)num_slots);
-    if (slot_stride < (int64_t)H * HEAD_ELEMS)
-        return fail(KDA_ERR_STRIDE, "slot_stride %lld < H*128*128", (long long)slot_stride);
+    if (slot_stride < (int64_t)H * HEAD_ELEMS || slot_stride > MAX_STRIDE)
+        return fail(KDA_ERR_STRIDE, "slot_stride %lld must be in [H*128*128, 2^44]", (long long)slot_stride);
     if (!aligned16(state) || ((slot_stride * elem_size(dtype)) & 15) != 0)
         return fail(KDA_ERR_ALIGN, "state base and slot stride must be 16-byte aligned");
     return KDA_OK;
 }
 
-uint64_t pool_bytes(int32_t dtype, int64_t num_slots, int64_t slot_stride, int32_t H)
+u128 pool_bytes(int32_t dtype, int64_t num_slots, int64_t slot_stride, int32_t H)
 {
-    return ((uint64_t)(num_slots - 1) * (uint64_t)slot_stride + (uint64_t)H * HEAD_ELEMS) *
-           (uint64_t)elem_size(dtype);
+    return ((u128)(uint64_t)(num_slots - 1) * (uint64_t)slot_stride + (u128)(uint64_t)H * HEAD_ELEMS) *
+           (u128)elem_size(dtype);
 }
 
 // Value rows per workgroup.  A (row, head) item is split into vsplit
@@ -217,13 +232,13 @@ int prepare_recurrent(const kda_recurrent_args *a, RecParams *p, Launch *l)
         if (!aligned16(a->correction_cache) || !aligned4(a->kg_cache))
             return fail(KDA_ERR_ALIGN, "correction_cache must be 16-byte and kg_cache 4-byte aligned");
     }
-    const uint64_t cache_rows = caches ? (uint64_t)a->num_slots * a->HV * a->cache_t_max : 0;
+    const u128 cache_rows = caches ? (u128)(uint64_t)a->num_slots * (uint64_t)a->HV * (uint64_t)a->cache_t_max : 0;
     const int kg_es = a->kg_dtype == KDA_DTYPE_F32 ? 4 : 2;
     const int64_t T = a->n_tokens;
     const int es = elem_size(a->state_dtype);
     const Range state_r = span(a->state, pool_bytes(a->state_dtype, a->num_slots, a->slot_stride, a->HV), "state");
-    Range w[5] = {span(a->out, (uint64_t)T * HVC * 2, "out"),
-                  span(a->checkpoints, a->checkpoints ? (uint64_t)T * a->HV * HEAD_ELEMS * es : 0, "checkpoints"),
+    Range w[5] = {span(a->out, (u128)T * HVC * 2, "out"),
+                  span(a->checkpoints, a->checkpoints ? (u128)T * a->HV * HEAD_ELEMS * es : 0, "checkpoints"),
                   update ? state_r : Range{0, 0, ""},
                   span(a->correction_cache, a->correction_cache ? cache_rows * KD * 4 : 0, "correction_cache"),
                   span(a->kg_cache, a->kg_cache ? cache_rows * 2 * KD * kg_es : 0, "kg_cache")};
@@ -232,10 +247,10 @@ int prepare_recurrent(const kda_recurrent_args *a, RecParams *p, Launch *l)
                    span(a->v, rows_extent(T, a->v_stride, HVC) * 2, "v"),
                    span(a->g, rows_extent(T, a->g_stride, HVC) * g_es, "g"),
                    span(a->beta, rows_extent(T, a->beta_stride, a->HV) * b_es, "beta"),
-                   span(a->A_log, a->A_log ? (uint64_t)a->HV * 4 : 0, "A_log"),
-                   span(a->dt_bias, a->dt_bias ? (uint64_t)HVC * 4 : 0, "dt_bias"),
-                   span(a->state_indices, (uint64_t)a->n_seqs * 4, "state_indices"),
-                   span(a->cu_seqlens, ragged ? (uint64_t)(a->n_seqs + 1) * 4 : 0, "cu_seqlens"),
+                   span(a->A_log, a->A_log ? (u128)a->HV * 4 : 0, "A_log"),
+                   span(a->dt_bias, a->dt_bias ? (u128)HVC * 4 : 0, "dt_bias"),
+                   span(a->state_indices, (u128)a->n_seqs * 4, "state_indices"),
+                   span(a->cu_seqlens, ragged ? ((u128)(uint64_t)a->n_seqs + 1) * 4 : 0, "cu_seqlens"),
                    update ? Range{0, 0, ""} : state_r};
     rc = check_alias(w, 5, r, 10);
     if (rc) return rc;
@@ -367,19 +382,19 @@ int prepare_fused(const kda_fused_args *a, FusedParams *p, Launch *l)
     rc = check_pool(a->state, a->state_dtype, a->num_slots, a->slot_stride, a->H);
     if (rc) return rc;
     const int64_t R = a->rows;
-    Range w[3] = {span(a->out, (uint64_t)R * HC * 2, "out"),
+    Range w[3] = {span(a->out, (u128)R * HC * 2, "out"),
                   span(a->state, pool_bytes(a->state_dtype, a->num_slots, a->slot_stride, a->H), "state"),
                   span(a->conv_state, rows_extent(a->num_slots, a->conv_slot_stride, 3 * C3) * 2,
                        "conv_state")};
     Range r[10] = {span(a->x, rows_extent(R, a->x_stride, C3) * 2, "x"),
-                   span(a->weight, (uint64_t)12 * HC * 4, "weight"),
+                   span(a->weight, (u128)12 * HC * 4, "weight"),
                    span(a->raw_gate, rows_extent(R, a->gate_stride, HC) * 2, "raw_gate"),
                    span(a->raw_beta, rows_extent(R, a->beta_stride, a->H) * 2, "raw_beta"),
-                   span(a->A_log, (uint64_t)a->H * 4, "A_log"),
-                   span(a->dt_bias, (uint64_t)HC * 4, "dt_bias"),
-                   span(a->state_indices, (uint64_t)R * 4, "state_indices"),
+                   span(a->A_log, (u128)a->H * 4, "A_log"),
+                   span(a->dt_bias, (u128)HC * 4, "dt_bias"),
+                   span(a->state_indices, (u128)R * 4, "state_indices"),
                    span(a->output_gate, rows_extent(R, a->ogate_stride, HC) * 2, "output_gate"),
-                   span(a->norm_weight, (uint64_t)KD * 4, "norm_weight"),
+                   span(a->norm_weight, (u128)KD * 4, "norm_weight"),
                    Range{0, 0, ""}};
     rc = check_alias(w, 3, r, 9);
     if (rc) return rc;
@@ -472,21 +487,21 @@ int prepare_packed_fused(const kda_packed_fused_args *a, PackedFusedParams *p, L
     if (rc) return rc;
     const int64_t R = a->n_rows;
     const int64_t N = a->n_seqs;
-    Range w[3] = {span(a->out, (uint64_t)R * HC * 2, "out"),
+    Range w[3] = {span(a->out, (u128)R * HC * 2, "out"),
                   span(a->state, pool_bytes(a->state_dtype, a->num_slots, a->slot_stride, a->H), "state"),
                   span(a->conv_state, rows_extent(a->num_slots, a->conv_slot_stride, 3 * C3) * 2,
                        "conv_state")};
     Range r[12] = {span(a->x, rows_extent(R, a->x_stride, C3) * 2, "x"),
-                   span(a->weight, (uint64_t)12 * HC * 4, "weight"),
+                   span(a->weight, (u128)12 * HC * 4, "weight"),
                    span(a->raw_gate, rows_extent(R, a->gate_stride, HC) * 2, "raw_gate"),
                    span(a->raw_beta, rows_extent(R, a->beta_stride, a->H) * 2, "raw_beta"),
-                   span(a->A_log, (uint64_t)a->H * 4, "A_log"),
-                   span(a->dt_bias, (uint64_t)HC * 4, "dt_bias"),
+                   span(a->A_log, (u128)a->H * 4, "A_log"),
+                   span(a->dt_bias, (u128)HC * 4, "dt_bias"),
                    span(a->state_indices, rows_extent(N, a->indices_stride, a->max_tokens) * 4, "state_indices"),
-                   span(a->query_start_loc, (uint64_t)(N + 1) * 4, "query_start_loc"),
-                   span(a->num_accepted_tokens, (uint64_t)N * 4, "num_accepted_tokens"),
+                   span(a->query_start_loc, (u128)(N + 1) * 4, "query_start_loc"),
+                   span(a->num_accepted_tokens, (u128)N * 4, "num_accepted_tokens"),
                    span(a->output_gate, rows_extent(R, a->ogate_stride, HC) * 2, "output_gate"),
-                   span(a->norm_weight, (uint64_t)KD * 4, "norm_weight"),
+                   span(a->norm_weight, (u128)KD * 4, "norm_weight"),
                    Range{0, 0, ""}};
     rc = check_alias(w, 3, r, 11);
     if (rc) return rc;

@@ -443,3 +443,23 @@ def test_packed_fused_plan_and_validation():
     a = packed_fused_args()
     a.query_start_loc = a.state_indices  # metadata over metadata is fine (both read-only)
     assert plan_pf(a)[0] == 0, err()
+
+
+def test_sizes_that_would_overflow_are_rejected():
+    """Extents are computed without wrap-around: strides and sizes whose
+    buffers would exceed 2^48 bytes are errors, never silently small ranges."""
+    a = rec_args()
+    a.slot_stride = (1 << 44) + 16
+    expect(plan_rec(a), -4, "slot_stride")
+    a = rec_args()
+    a.q_stride = 1 << 62
+    expect(plan_rec(a), -2, "2^48")
+    a = rec_args(varlen=True, T=8)
+    a.n_seqs = 2 ** 31 - 1
+    assert plan_rec(a)[0] < 0
+    a = with_caches(rec_args())
+    a.num_slots, a.cache_t_max = 1 << 20, 2 ** 31 - 1   # 2^53 cache rows
+    expect(plan_rec(a), -2, "2^48")
+    f = packed_fused_args()
+    f.indices_stride = 1 << 61
+    expect(plan_pf(f), -2, "2^48")
