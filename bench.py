@@ -126,6 +126,11 @@ def cpu_baseline(budget_s=12.0, rows_per_worker=8, H=32):
         sample.append(tuple(oracle.as_np(t) for t in (c.q, c.k, c.v, c.g, c.beta, c.A_log,
                                                       c.dt_bias, c.state, c.state_indices)))
     _SAMPLE = sample
+    # one thread first (this process), then every worker
+    t0, one = time.perf_counter(), 0
+    while time.perf_counter() - t0 < 2.0:
+        one += _oracle_slice(0)
+    one_rate = one / (time.perf_counter() - t0)
     ctx = mp.get_context("fork")
     done_rows = 0
     with ctx.Pool(workers) as pool:
@@ -138,7 +143,8 @@ def cpu_baseline(budget_s=12.0, rows_per_worker=8, H=32):
     return {"value": done_rows / wall, "unit": "rows/s", "cores": workers, "kind": "oracle",
             "sample": f"{done_rows} rows of T=1 H=32 fp32-state decode ({done_rows * H} head "
                       f"updates) in {wall:.1f} s: {workers} worker processes, each repeating "
-                      f"its own {rows_per_worker} rows; gcc -O2 fp64 oracle"}
+                      f"its own {rows_per_worker} rows; gcc -O2 fp64 oracle",
+            "single_thread_rows_per_s": one_rate}
 
 
 # ---------------------------------------------------------- GPU helpers ----
@@ -530,6 +536,18 @@ def main():
     log(f"B={B}: {us:.1f} us/step, {achieved:.0f} GB/s algorithmic "
         f"({100 * achieved / HBM_PEAK_GBPS:.1f}% of 8 TB/s), wall {t_wall:.3f}s")
 
+    # per-launch distribution (after the timed region, not part of `value`)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(50)]
+    for a_ev, b_ev in evs:
+        a_ev.record(stream)
+        step()
+        b_ev.record(stream)
+    torch.cuda.synchronize()
+    per = sorted(a_ev.elapsed_time(b_ev) * 1e3 for a_ev, b_ev in evs)
+    dist = {"n": len(per), "median_us": per[len(per) // 2], "p10_us": per[len(per) // 10],
+            "p90_us": per[(9 * len(per)) // 10]}
+    log(f"per-launch: median {dist['median_us']:.1f} us, p10 {dist['p10_us']:.1f}, p90 {dist['p90_us']:.1f}")
+
     if args.copy_calibrate:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
@@ -559,6 +577,7 @@ def main():
                                f"[4096,32,128,128], B={B} random unique slots, softplus gate",
                    "B": B, "H": H, "state_dtype": "fp32", "num_slots": SLOTS},
         "state_GBps": state_bytes / (us * 1e-6) / 1e9,
+        "launch_distribution": dist,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": None if traffic_bytes is None else traffic_bytes / (us * 1e-6) / 1e9,
