@@ -498,16 +498,6 @@ __global__ void __launch_bounds__(256) kda_recurrent_kernel(const RecParams p)
         t1 = seq + 1;
     }
     const int idx = p.state_indices[seq];
-    if (idx < 0 || (int64_t)idx >= p.num_slots) {
-        if (m == 0)
-            for (int t = t0; t < t1; ++t)
-                store_zero_bf16<G>(p.out + ((int64_t)t * p.HV + hv) * KD + r_base);
-        return;
-    }
-    if (t1 <= t0) return;
-
-    const size_t es = BF16 ? 2 : 4;
-    char *head = reinterpret_cast<char *>(p.state) + ((int64_t)idx * p.slot_stride + (int64_t)hv * (KD * KD)) * es;
     const bool precomputed = p.precomputed != 0;
     const bool g_f32 = p.g_f32 != 0;
     const bool beta_f32 = p.beta_f32 != 0;
@@ -523,16 +513,19 @@ __global__ void __launch_bounds__(256) kda_recurrent_kernel(const RecParams p)
         load_halves(bbase + (t * p.beta_stride + hv) * b_es, beta_f32, lo, hi);
     };
 
-    // Token inputs first (the first chunk's in the token loop): waiting for
-    // them later must not wait for the state.  Token indices are clamped to
-    // the sequence, so every load is in bounds and unconditional.
+    // Token inputs first (the first chunk's in the token loop), even before
+    // the slot index is known: they do not depend on it, so their latency
+    // overlaps that of the index; waiting for them later must not wait for
+    // the state either.  Token indices are clamped into [0, t1), so every
+    // load is in bounds (n_tokens >= 1 whenever the kernel runs) and
+    // unconditional; a null or empty sequence simply discards them.
     constexpr int NC = VARLEN ? CHUNK : 1;
     StageIn cin[NC];
     uint32_t blo[NC], bhi[NC];
     auto load_chunk = [&](int c0) {
 #pragma unroll
         for (int i = 0; i < NC; ++i) {
-            const int64_t n = min(c0 + i, t1 - 1);
+            const int64_t n = max(min(c0 + i, t1 - 1), 0);
             cin[i] = load_stage(tid, p.q + n * p.q_stride + oq, p.k + n * p.k_stride + oq,
                                 p.v + n * p.v_stride + ov, g_at(n), g_f32);
             beta_at(n, blo[i], bhi[i]);
@@ -540,6 +533,15 @@ __global__ void __launch_bounds__(256) kda_recurrent_kernel(const RecParams p)
     };
     load_chunk(t0);
     const float a_h = precomputed ? 0.f : __expf(p.A_log[hv]);
+    if (idx < 0 || (int64_t)idx >= p.num_slots) {
+        if (m == 0)
+            for (int t = t0; t < t1; ++t)
+                store_zero_bf16<G>(p.out + ((int64_t)t * p.HV + hv) * KD + r_base);
+        return;
+    }
+    if (t1 <= t0) return;
+    const size_t es = BF16 ? 2 : 4;
+    char *head = reinterpret_cast<char *>(p.state) + ((int64_t)idx * p.slot_stride + (int64_t)hv * (KD * KD)) * es;
     __builtin_amdgcn_sched_barrier(0);
 
     // Then every state load of this lane.
@@ -807,20 +809,21 @@ __device__ __forceinline__ int conv_channel(int cl, int h, int HC)
     return (cl >> 7) * HC + h * KD + (cl & (KD - 1));
 }
 
-__device__ __forceinline__ ConvChan load_chan(const uint16_t *cs, const float *weight, int cl, int h, int HC,
-                                              int C3)
+__device__ __forceinline__ void load_taps(ConvChan &ch, const float *weight, int cl, int h, int HC)
 {
-    const int c = conv_channel(cl, h, HC);
-    ConvChan ch;
-    ch.c0 = cs[c];
-    ch.c1 = cs[C3 + c];
-    ch.c2 = cs[2 * C3 + c];
     const float *w = weight + (int64_t)(cl >> 7) * 4 * HC + h * KD + (cl & (KD - 1));
     ch.w0 = w[0];
     ch.w1 = w[HC];
     ch.w2 = w[2 * HC];
     ch.w3 = w[3 * HC];
-    return ch;
+}
+
+// The cached window of channel c (global index) in one slot's cache.
+__device__ __forceinline__ void load_window(ConvChan &ch, const uint16_t *cs, int c, int C3)
+{
+    ch.c0 = cs[c];
+    ch.c1 = cs[C3 + c];
+    ch.c2 = cs[2 * C3 + c];
 }
 
 // Conv + SiLU of one token; the window advances by x.
@@ -885,35 +888,40 @@ __global__ void __launch_bounds__(2048 / G) kda_packed_fused_kernel(const Packed
         if (seq == p.n_seqs - 1)
             for (int r = t1; r < p.n_rows; ++r) store_zero_bf16<G>(out_at(r));
     }
+    if (t1 <= t0) return;  // an empty sequence touches nothing
     const int32_t *cols = p.state_indices + (int64_t)seq * p.indices_stride;
     const int acc = p.accepted[seq];
-    const int src = (acc >= 1 && acc <= p.max_tokens) ? cols[acc - 1] : -1;
-    if (src <= 0 || (int64_t)src >= p.num_slots) {
-        if (m == 0)
-            for (int r = t0; r < t1; ++r) store_zero_bf16<G>(out_at(r));
-        return;
-    }
-    if (t1 <= t0) return;
 
-    // Conv windows and taps of this thread's channels (local channel tid +
-    // k*NT of the head's 384; a thread past the last one loads channel 383
-    // and never stores), gate parameters, then the state.
+    // What does not depend on the start slot is issued before it is known:
+    // the conv taps of this thread's channels (local channel tid + k*NT of
+    // the head's 384; a thread past the last one uses channel 383 and never
+    // stores), the gate parameters and the norm weight.  Then the slot, the
+    // conv windows and the state; the token inputs per chunk.
     const int c_lo = tid & (KD - 1);
     ConvChan ch[NCH];
     int gch[NCH];
     bool own[NCH];
-    const uint16_t *cs_src = p.conv_state + (int64_t)src * p.conv_slot_stride;
 #pragma unroll
     for (int k = 0; k < NCH; ++k) {
         const int cl = tid + k * NT;
         own[k] = cl < 3 * KD;
         const int clc = own[k] ? cl : 3 * KD - 1;
         gch[k] = conv_channel(clc, h, HC);
-        ch[k] = load_chan(cs_src, p.weight, clc, h, HC, C3);
+        load_taps(ch[k], p.weight, clc, h, HC);
     }
     const float dt = p.dt_bias[(int64_t)h * KD + c_lo];
     const float a_h = __expf(p.A_log[h]);
     if (tid < KD) s_nw[tid] = p.norm_weight[tid];
+
+    const int src = (acc >= 1 && acc <= p.max_tokens) ? cols[acc - 1] : -1;
+    if (src <= 0 || (int64_t)src >= p.num_slots) {
+        if (m == 0)
+            for (int r = t0; r < t1; ++r) store_zero_bf16<G>(out_at(r));
+        return;
+    }
+    const uint16_t *cs_src = p.conv_state + (int64_t)src * p.conv_slot_stride;
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) load_window(ch[k], cs_src, gch[k], C3);
     __builtin_amdgcn_sched_barrier(0);
 
     const size_t es = BF16 ? 2 : 4;
@@ -934,7 +942,7 @@ __global__ void __launch_bounds__(2048 / G) kda_packed_fused_kernel(const Packed
     const int otk = tid >> 7;        // ... and its first token of the chunk
     for (int c0 = t0; c0 < t1; c0 += PF_CHUNK) {
         const int nc = min(PF_CHUNK, t1 - c0);
-        // the chunk's inputs, all at once (indices clamped in bounds; unused past nc)
+        // the chunk's inputs, all at once (rows clamped into [t0, t1); unused past nc)
         uint32_t xin[PF_CHUNK][NCH], gr[PF_CHUNK], br[PF_CHUNK], og[NOP];
         int col[PF_CHUNK];
 #pragma unroll
