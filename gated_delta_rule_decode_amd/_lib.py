@@ -83,7 +83,8 @@ class PackedFusedArgs(ctypes.Structure):
         ("lower_bound", _F32), ("state_indices", _P), ("indices_stride", _I64),
         ("query_start_loc", _P), ("num_accepted_tokens", _P), ("state", _P), ("state_dtype", _I32),
         ("num_slots", _I64), ("slot_stride", _I64), ("output_gate", _P), ("ogate_stride", _I64),
-        ("norm_weight", _P), ("norm_eps", _F32), ("out", _P),
+        ("norm_weight", _P), ("norm_eps", _F32), ("out", _P), ("split_counters", _P),
+        ("split_partials", _P),
     ]
 
 

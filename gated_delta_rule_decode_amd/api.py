@@ -339,9 +339,46 @@ def fused_kda_decode(x, weight, conv_state, raw_gate, raw_beta, A_log, dt_bias, 
     return output
 
 
+class PackedFusedWorkspace:
+    """Workspace that lets packed_fused_kda_decode spread the work of one
+    (sequence, head) over several workgroups when there are few of them:
+    int32 arrival counters (zero between calls; the kernel leaves them zero)
+    and fp32 unnormalised outputs.  It grows on demand (never inside graph
+    capture).  Calls that share one must not overlap in time: use one per
+    stream when calls run concurrently."""
+
+    def __init__(self, device):
+        self.device = torch.device(device)
+        self.counters = torch.zeros(0, dtype=torch.int32, device=self.device)
+        self.partials = torch.empty(0, dtype=torch.float32, device=self.device)
+
+    def reserve(self, n_seqs, H, n_rows):
+        nc, npart = n_seqs * H, max(n_rows, 1) * H * D
+        if self.counters.numel() < nc or self.partials.numel() < npart:
+            _need(not torch.cuda.is_current_stream_capturing(),
+                  "the packed fused workspace must grow, which cannot happen during graph capture: "
+                  "run the call once before capturing it, or pass workspace=None")
+            if self.counters.numel() < nc:
+                self.counters = torch.zeros(nc, dtype=torch.int32, device=self.device)
+            if self.partials.numel() < npart:
+                self.partials = torch.empty(npart, dtype=torch.float32, device=self.device)
+        return self.counters, self.partials
+
+
+_AUTO_WORKSPACE = {}
+
+
+def _auto_workspace(device):
+    key = torch.device(device).index
+    ws = _AUTO_WORKSPACE.get(key)
+    if ws is None:
+        ws = _AUTO_WORKSPACE[key] = PackedFusedWorkspace(device)
+    return ws
+
+
 def packed_fused_kda_decode(x, weight, conv_state, raw_gate, raw_beta, A_log, dt_bias, state_indices,
                             state, output_gate, norm_weight, lower_bound=None, norm_eps=1e-5, output=None,
-                            *, query_start_loc, num_accepted_tokens):
+                            *, query_start_loc, num_accepted_tokens, workspace="auto"):
     """Packed fused decode with T >= 1 tokens per sequence ("feat(kda): add
     fused speculative decode kernel").
 
@@ -355,7 +392,9 @@ def packed_fused_kda_decode(x, weight, conv_state, raw_gate, raw_beta, A_log, dt
     non-positive start slot makes the sequence null).  Rows of null sequences
     and rows outside every sequence give zeros.  A bf16 pool holds each
     checkpoint rounded; the recurrence itself stays fp32 across the tokens.
-    Returns bf16 [1, rows, H, 128].
+    ``workspace``: "auto" (a per-device PackedFusedWorkspace, shared by
+    every call on that device), a PackedFusedWorkspace, or None (one
+    workgroup per (sequence, head)).  Returns bf16 [1, rows, H, 128].
     """
     H, rows, rg, rb, og, output = _fused_inputs(x, weight, conv_state, raw_gate, raw_beta, A_log, dt_bias,
                                                 state, output_gate, norm_weight, norm_eps, output)
@@ -384,6 +423,14 @@ def packed_fused_kda_decode(x, weight, conv_state, raw_gate, raw_beta, A_log, dt
     a.output_gate, a.ogate_stride = _ptr(og), og.stride(0)
     a.norm_weight, a.norm_eps = _ptr(norm_weight), float(norm_eps)
     a.out = _ptr(output)
+    if isinstance(workspace, str):
+        _need(workspace == "auto", 'workspace must be "auto", a PackedFusedWorkspace or None')
+        workspace = _auto_workspace(x.device)
+    if workspace is not None:
+        _need(isinstance(workspace, PackedFusedWorkspace) and workspace.device == x.device,
+              "workspace must be a PackedFusedWorkspace on the device of x")
+        cnt, part = workspace.reserve(N, H, rows)
+        a.split_counters, a.split_partials = _ptr(cnt), _ptr(part)
     lib = _lib.load()
     with torch.cuda.device(x.device):
         _lib.check(lib.kda_packed_fused_decode(ctypes.byref(a), _stream(x.device)))

@@ -437,19 +437,38 @@ int prepare_fused(const kda_fused_args *a, FusedParams *p, Launch *l)
 // --------------------------------------------------------- packed fused ----
 
 #ifndef KDA_FORCE_PF_BLOCK
-#define KDA_FORCE_PF_BLOCK 0  // build-time override used when tuning the policy
+#define KDA_FORCE_PF_BLOCK 0  // build-time overrides used when tuning the policy
+#endif
+#ifndef KDA_FORCE_PF_SPLIT
+#define KDA_FORCE_PF_SPLIT 0
 #endif
 
-// Threads per (sequence, head) workgroup of the packed fused decode.
-// Measured on MI355X (H=12 and 24, T=5, fp32 and bf16 pools): 512 threads
-// (4 value rows per lane) are 5-10% faster up to ~1000 items, 256 (8 rows
-// per lane) are on par above; 1024 threads are never faster (the per-token
-// work of a head is then bound by its CU's VALU issue, and each extra lane
-// repeats the token's norm reductions).
-int packed_fused_block(int64_t items)
+struct PfGeometry {
+    int vs, block;
+};
+
+// Workgroups per (sequence, head) and threads per workgroup of the packed
+// fused decode.  Unsplit (measured on MI355X, H=12 and 24, T=5, fp32 and
+// bf16 pools): 512 threads (4 value rows per lane) are 5-10% faster up to
+// ~1000 items, 256 (8 rows per lane) are on par above; 1024 threads are
+// never faster (the per-token work of a head is then bound by its CU's VALU
+// issue, and each extra lane repeats the token's norm reductions).  Split
+// (kernel durations at H=12, T=5): one sequence runs 4 parts of 512 threads
+// in 10.0/10.2 us (fp32/bf16 pool) against 11.9/12.3 unsplit; 8 sequences
+// 2 parts in 12.8/12.6 against 12.8/13.4; from 32 sequences on the CUs are
+// busy and splitting only adds the exchange (+3 to +16 us).
+PfGeometry packed_fused_geometry(int64_t items, bool can_split)
 {
-    if (KDA_FORCE_PF_BLOCK == 256 || KDA_FORCE_PF_BLOCK == 512) return KDA_FORCE_PF_BLOCK;
-    return items < 1024 ? 512 : 256;
+    PfGeometry g{1, items < 1024 ? 512 : 256};
+    if (can_split) {
+        if (items < 64) g = PfGeometry{4, 512};
+        else if (items < 128) g = PfGeometry{2, 512};
+    }
+    if (KDA_FORCE_PF_SPLIT == 1 || (can_split && (KDA_FORCE_PF_SPLIT == 2 || KDA_FORCE_PF_SPLIT == 4)))
+        g.vs = KDA_FORCE_PF_SPLIT;
+    if (KDA_FORCE_PF_BLOCK == 256 || KDA_FORCE_PF_BLOCK == 512) g.block = KDA_FORCE_PF_BLOCK;
+    if (g.vs > 1) g.block = 512;  // the split kernels are built for 512 threads
+    return g;
 }
 
 int prepare_packed_fused(const kda_packed_fused_args *a, PackedFusedParams *p, Launch *l)
@@ -483,14 +502,21 @@ int prepare_packed_fused(const kda_packed_fused_args *a, PackedFusedParams *p, L
         !aligned4(a->num_accepted_tokens))
         return fail(KDA_ERR_ALIGN, "inputs must be aligned to their element size");
     if (!aligned16(a->out)) return fail(KDA_ERR_ALIGN, "out must be 16-byte aligned");
+    if (!a->split_counters != !a->split_partials)
+        return fail(KDA_ERR_NULLPTR, "split_counters and split_partials are given together or not at all");
+    const bool can_split = a->split_counters != nullptr;
+    if (can_split && (!aligned4(a->split_counters) || !aligned16(a->split_partials)))
+        return fail(KDA_ERR_ALIGN, "split_counters must be 4-byte and split_partials 16-byte aligned");
     rc = check_pool(a->state, a->state_dtype, a->num_slots, a->slot_stride, a->H);
     if (rc) return rc;
     const int64_t R = a->n_rows;
     const int64_t N = a->n_seqs;
-    Range w[3] = {span(a->out, (u128)R * HC * 2, "out"),
+    Range w[5] = {span(a->out, (u128)R * HC * 2, "out"),
                   span(a->state, pool_bytes(a->state_dtype, a->num_slots, a->slot_stride, a->H), "state"),
                   span(a->conv_state, rows_extent(a->num_slots, a->conv_slot_stride, 3 * C3) * 2,
-                       "conv_state")};
+                       "conv_state"),
+                  span(a->split_counters, can_split ? (u128)N * a->H * 4 : 0, "split_counters"),
+                  span(a->split_partials, can_split ? (u128)R * HC * 4 : 0, "split_partials")};
     Range r[12] = {span(a->x, rows_extent(R, a->x_stride, C3) * 2, "x"),
                    span(a->weight, (u128)12 * HC * 4, "weight"),
                    span(a->raw_gate, rows_extent(R, a->gate_stride, HC) * 2, "raw_gate"),
@@ -503,15 +529,16 @@ int prepare_packed_fused(const kda_packed_fused_args *a, PackedFusedParams *p, L
                    span(a->output_gate, rows_extent(R, a->ogate_stride, HC) * 2, "output_gate"),
                    span(a->norm_weight, (u128)KD * 4, "norm_weight"),
                    Range{0, 0, ""}};
-    rc = check_alias(w, 3, r, 11);
+    rc = check_alias(w, 5, r, 11);
     if (rc) return rc;
     const int64_t items = N * a->H;
-    if (items > 0x7fffffffLL) return fail(KDA_ERR_SHAPE, "too many work items");
+    const PfGeometry geo = packed_fused_geometry(items, can_split);
+    if (items * geo.vs > 0x7fffffffLL) return fail(KDA_ERR_SHAPE, "too many work items");
     l->family = KERNEL_PACKED_FUSED;
-    l->vsplit = 1;
-    l->rows_per_block = KD;
-    l->grid = (int32_t)items;
-    l->block = packed_fused_block(items);
+    l->vsplit = geo.vs;
+    l->rows_per_block = KD / geo.vs;
+    l->grid = (int32_t)(items * geo.vs);
+    l->block = geo.block;
     l->bf16_state = a->state_dtype == KDA_DTYPE_BF16;
 
     p->x = static_cast<const uint16_t *>(a->x);
@@ -539,6 +566,8 @@ int prepare_packed_fused(const kda_packed_fused_args *a, PackedFusedParams *p, L
     p->scale = 1.0f / sqrtf((float)KD);
     p->l2_eps = 1e-6f;
     p->out = static_cast<uint16_t *>(a->out);
+    p->counters = a->split_counters;
+    p->partials = a->split_partials;
     p->n_rows = a->n_rows;
     p->n_seqs = a->n_seqs;
     p->H = a->H;

@@ -90,6 +90,8 @@ struct PackedFusedParams {
     const float *norm_weight;
     float norm_eps, scale, l2_eps;
     uint16_t *out;               // bf16 [n_rows][H][128]
+    int32_t *counters;           // [n_seqs][H] arrivals per head (split heads); zero between calls
+    float *partials;             // fp32 [n_rows][H][128] unnormalised outputs (split heads)
     int32_t n_rows, n_seqs, H, max_tokens;
 };
 

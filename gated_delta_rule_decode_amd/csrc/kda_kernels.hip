@@ -846,41 +846,99 @@ __device__ __forceinline__ void store_window(uint16_t *cs, const ConvChan &ch, i
     cs[2 * C3 + c] = (uint16_t)ch.c2;
 }
 
-// G value rows per DPP row, 2048/G threads per workgroup: G=8 (256 threads)
-// for large grids, G=4 (512 threads) halves each lane's per-token work for
-// smaller ones.
-template <bool BF16, int G>
-__global__ void __launch_bounds__(2048 / G) kda_packed_fused_kernel(const PackedFusedParams p)
+// Device-coherent (relaxed, device-scope atomic) accesses: written through
+// to, and read from, the level of the memory system shared by all chiplets,
+// so a store that has completed is seen by a later such load from any CU.
+__device__ __forceinline__ void store_coherent(float *p, float v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ float load_coherent(const float *p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Sum over the 64 lanes of a wave; wave-uniform result.
+__device__ __forceinline__ float wave_sum(float x)
+{
+    x = row_sum16(x);
+    return (lane_value(x, 0) + lane_value(x, 16)) + (lane_value(x, 32) + lane_value(x, 48));
+}
+
+// A (sequence, head) is covered by VS workgroups, each owning RW = 128/VS
+// value rows, G value rows per DPP row: 2048/(G*VS) threads.  VS=1: G=8
+// (256 threads) for large grids, G=4 (512 threads) halves each lane's
+// per-token work for smaller ones.  VS>1 spreads one head's per-token work
+// over VS compute units when there are too few heads to fill the chip: each
+// part runs the conv of all q and k channels (every part needs the full
+// normalised q and k) and of its own v channels, updates its rows of the
+// state and writes its unnormalised outputs to `partials`; the last part of
+// the head to arrive (a per-head counter) applies the gated RMSNorm to the
+// whole head and sets the counter back to zero.  No part waits for another.
+template <bool BF16, int G, int VS>
+__global__ void __launch_bounds__(2048 / (G * VS)) kda_packed_fused_kernel(const PackedFusedParams p)
 {
     using IO = StateIO<BF16>;
-    constexpr int NT = 2048 / G;                 // threads
-    constexpr int NCH = (3 * KD + NT - 1) / NT;  // conv channels per thread
+    constexpr int RW = KD / VS;                  // value rows of this workgroup
+    constexpr int NT = 2048 / (G * VS);          // threads
+    constexpr int NCL = 2 * KD + RW;             // conv channels: q, k and this part's v
+    constexpr int NCH = (NCL + NT - 1) / NT;     // conv channels per thread
     constexpr int NR = NT / 16;                  // DPP rows (RMS partials per token)
     constexpr int TP = NT / KD;                  // tokens per pass of the output phase
     constexpr int NOP = (PF_CHUNK + TP - 1) / TP;  // output passes per chunk
+    constexpr bool SPLIT = VS > 1;
+    static_assert(RW % (4 * G) == 0 && NT % KD == 0 && NT <= 1024, "bad packed fused geometry");
 
-    __shared__ float s_act[PF_CHUNK][3 * KD];  // q | k | v activations per token
+    __shared__ float s_act[PF_CHUNK][NCL];    // q | k | v activations per token
     __shared__ float s_d[PF_CHUNK][KD];
-    __shared__ float s_o[PF_CHUNK][KD];        // unnormalised outputs
-    __shared__ float s_red[PF_CHUNK][NR];      // RMS partial sums
+    __shared__ float s_o[SPLIT ? 1 : PF_CHUNK][KD];    // unnormalised outputs
+    __shared__ float s_red[SPLIT ? 1 : PF_CHUNK][NR];  // RMS partial sums
     __shared__ float s_beta[PF_CHUNK];
     __shared__ int s_dst[PF_CHUNK];            // checkpoint slot, or -1
     __shared__ float s_nw[KD];
+    __shared__ float s_fin[SPLIT ? NOP : 1][NT / 64];  // split heads: per-wave sums of squares
+    __shared__ int s_last;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int m = lane & 15;
     const int qd = lane >> 4;
-    const int seq = blockIdx.x / p.H;
-    const int h = blockIdx.x - seq * p.H;
-    const int r_base = wave * (4 * G) + qd * G;
+    const int item = blockIdx.x / VS;
+    const int part = blockIdx.x - item * VS;
+    const int seq = item / p.H;
+    const int h = item - seq * p.H;
+    const int r_loc = wave * (4 * G) + qd * G;  // this lane's first value row in the part
+    const int r_base = part * RW + r_loc;       // ... and in the head
     const int HC = p.H * KD;
     const int C3 = 3 * HC;
     auto out_at = [&](int r) { return p.out + ((int64_t)r * p.H + h) * KD + r_base; };
 
-    const int t0 = min(max(p.qsl[seq], 0), p.n_rows);
-    const int t1 = min(max(p.qsl[seq + 1], t0), p.n_rows);
+    // The row range, the accepted count and the first PF_CHUNK columns of
+    // the row are fetched together and the start column is picked from
+    // registers (a dependent load only for a start column past them): one
+    // round trip before the state's, not three.  The column index is clamped
+    // into the row; its validity is checked below.
+    const int q0 = p.qsl[seq];
+    const int q1 = p.qsl[seq + 1];
+    const int acc = p.accepted[seq];
+    const int32_t *cols = p.state_indices + (int64_t)seq * p.indices_stride;
+    int head_cols[PF_CHUNK];
+#pragma unroll
+    for (int j = 0; j < PF_CHUNK; ++j) head_cols[j] = cols[min(j, p.max_tokens - 1)];
+    // (the empty asm keeps the compiler from turning the pick below back into
+    // one load whose address waits for the accepted count)
+#pragma unroll
+    for (int j = 0; j < PF_CHUNK; ++j) asm volatile("" : "+s"(head_cols[j]));
+    const int a1 = min(max(acc, 1), p.max_tokens) - 1;
+    int col_start = head_cols[0];
+#pragma unroll
+    for (int j = 1; j < PF_CHUNK; ++j)
+        if (a1 == j) col_start = head_cols[j];
+    if (a1 >= PF_CHUNK) col_start = cols[a1];
+    const int t0 = min(max(q0, 0), p.n_rows);
+    const int t1 = min(max(q1, t0), p.n_rows);
     // Rows that belong to no sequence: before the first one, after the last.
     if (m == 0) {
         if (seq == 0)
@@ -889,31 +947,42 @@ __global__ void __launch_bounds__(2048 / G) kda_packed_fused_kernel(const Packed
             for (int r = t1; r < p.n_rows; ++r) store_zero_bf16<G>(out_at(r));
     }
     if (t1 <= t0) return;  // an empty sequence touches nothing
-    const int32_t *cols = p.state_indices + (int64_t)seq * p.indices_stride;
-    const int acc = p.accepted[seq];
 
     // What does not depend on the start slot is issued before it is known:
-    // the conv taps of this thread's channels (local channel tid + k*NT of
-    // the head's 384; a thread past the last one uses channel 383 and never
-    // stores), the gate parameters and the norm weight.  Then the slot, the
-    // conv windows and the state; the token inputs per chunk.
+    // the conv taps of this thread's channels (local channel cl = tid + k*NT:
+    // q and k channels first, then this part's v channels; a thread past the
+    // last one repeats it and never stores), the gate parameters and the norm
+    // weight.  Then the slot, the conv windows and the state; the token
+    // inputs per chunk.
+    //
+    // Conv checkpoints of split heads: a part's v channels and state rows are
+    // its own, but every part reads the q and k windows of the start slot.
+    // They are checkpointed by the part whose share of those 256 channels
+    // they fall in, except into the start slot itself (the token in the
+    // start column): there they wait in registers for the last part to
+    // arrive, when every part has read the slot.
     const int c_lo = tid & (KD - 1);
     ConvChan ch[NCH];
     int gch[NCH];
-    bool own[NCH];
+    bool own[NCH], keep[NCH], is_v[NCH];
 #pragma unroll
     for (int k = 0; k < NCH; ++k) {
         const int cl = tid + k * NT;
-        own[k] = cl < 3 * KD;
-        const int clc = own[k] ? cl : 3 * KD - 1;
-        gch[k] = conv_channel(clc, h, HC);
-        load_taps(ch[k], p.weight, clc, h, HC);
+        own[k] = cl < NCL;
+        const int clc = own[k] ? cl : NCL - 1;
+        const int hc = clc < 2 * KD ? clc : clc + part * RW;  // channel in the head's 384
+        is_v[k] = own[k] && clc >= 2 * KD;
+        keep[k] = own[k] && (clc >= 2 * KD || (clc * VS) / (2 * KD) == part);
+        gch[k] = conv_channel(hc, h, HC);
+        load_taps(ch[k], p.weight, hc, h, HC);
     }
+    uint32_t held[SPLIT ? NCH : 1][3];  // split heads: q/k windows bound for the start slot
+    bool hold = false;
     const float dt = p.dt_bias[(int64_t)h * KD + c_lo];
     const float a_h = __expf(p.A_log[h]);
     if (tid < KD) s_nw[tid] = p.norm_weight[tid];
 
-    const int src = (acc >= 1 && acc <= p.max_tokens) ? cols[acc - 1] : -1;
+    const int src = (acc >= 1 && acc <= p.max_tokens) ? col_start : -1;
     if (src <= 0 || (int64_t)src >= p.num_slots) {
         if (m == 0)
             for (int r = t0; r < t1; ++r) store_zero_bf16<G>(out_at(r));
@@ -939,11 +1008,11 @@ __global__ void __launch_bounds__(2048 / G) kda_packed_fused_kernel(const Packed
     for (int gi = 0; gi < G; ++gi) IO::unpack(raw[gi], st[gi]);
 
     const int ov = tid & (KD - 1);   // output phase: this thread's value index
-    const int otk = tid >> 7;        // ... and its first token of the chunk
+    const int otk = tid >> 7;        // ... and its first token of the pass
     for (int c0 = t0; c0 < t1; c0 += PF_CHUNK) {
         const int nc = min(PF_CHUNK, t1 - c0);
         // the chunk's inputs, all at once (rows clamped into [t0, t1); unused past nc)
-        uint32_t xin[PF_CHUNK][NCH], gr[PF_CHUNK], br[PF_CHUNK], og[NOP];
+        uint32_t xin[PF_CHUNK][NCH], gr[PF_CHUNK], br[PF_CHUNK], og[SPLIT ? 1 : NOP];
         int col[PF_CHUNK];
 #pragma unroll
         for (int i = 0; i < PF_CHUNK; ++i) {
@@ -955,9 +1024,11 @@ __global__ void __launch_bounds__(2048 / G) kda_packed_fused_kernel(const Packed
             br[i] = p.braw[n * p.beta_stride + h];
             col[i] = cols[min(c0 - t0 + i, p.max_tokens - 1)];
         }
+        if constexpr (!SPLIT) {
 #pragma unroll
-        for (int k = 0; k < NOP; ++k)
-            og[k] = p.ogate[(int64_t)(c0 + min(k * TP + otk, nc - 1)) * p.ogate_stride + h * KD + ov];
+            for (int k = 0; k < NOP; ++k)
+                og[k] = p.ogate[(int64_t)(c0 + min(k * TP + otk, nc - 1)) * p.ogate_stride + h * KD + ov];
+        }
 
         // stage: conv in token order, decays, scalars; conv checkpoints
 #pragma unroll
@@ -977,9 +1048,20 @@ __global__ void __launch_bounds__(2048 / G) kda_packed_fused_kernel(const Packed
                 }
                 if (dst > 0) {
                     uint16_t *cs_dst = p.conv_state + (int64_t)dst * p.conv_slot_stride;
+                    if (!SPLIT || dst != src) {
 #pragma unroll
-                    for (int k = 0; k < NCH; ++k)
-                        if (own[k]) store_window(cs_dst, ch[k], gch[k], C3);
+                        for (int k = 0; k < NCH; ++k)
+                            if (keep[k]) store_window(cs_dst, ch[k], gch[k], C3);
+                    } else {
+                        hold = true;
+#pragma unroll
+                        for (int k = 0; k < (SPLIT ? NCH : 0); ++k) {
+                            if (is_v[k]) store_window(cs_dst, ch[k], gch[k], C3);
+                            held[k][0] = ch[k].c0;
+                            held[k][1] = ch[k].c1;
+                            held[k][2] = ch[k].c2;
+                        }
+                    }
                 }
             }
         }
@@ -994,13 +1076,19 @@ __global__ void __launch_bounds__(2048 / G) kda_packed_fused_kernel(const Packed
             float ss = 0.f;
 #pragma unroll
             for (int gi = 0; gi < G; ++gi) {
-                o[gi] = row_update(st[gi], ops, s_act[i][2 * KD + r_base + gi]);
+                o[gi] = row_update(st[gi], ops, s_act[i][2 * KD + r_loc + gi]);
                 ss = fmaf(o[gi], o[gi], ss);
             }
             if (m == 0) {
-                s_red[i][wave * 4 + qd] = ss;
+                if constexpr (SPLIT) {
+                    float *po = p.partials + ((int64_t)(c0 + i) * p.H + h) * KD + r_base;
 #pragma unroll
-                for (int gi = 0; gi < G; ++gi) s_o[i][r_base + gi] = o[gi];
+                    for (int gi = 0; gi < G; ++gi) store_coherent(po + gi, o[gi]);
+                } else {
+                    s_red[i][wave * 4 + qd] = ss;
+#pragma unroll
+                    for (int gi = 0; gi < G; ++gi) s_o[i][r_base + gi] = o[gi];
+                }
             }
             const int dst = s_dst[i];
             if (dst > 0) {
@@ -1011,18 +1099,81 @@ __global__ void __launch_bounds__(2048 / G) kda_packed_fused_kernel(const Packed
         }
         __syncthreads();
 
-        // gated RMSNorm of the chunk: thread (otk, ov) handles tokens otk, otk+TP, ...
+        if constexpr (!SPLIT) {
+            // gated RMSNorm of the chunk: thread (otk, ov) handles tokens otk, otk+TP, ...
 #pragma unroll
-        for (int k = 0; k < NOP; ++k) {
-            const int i = k * TP + otk;
-            if (i < nc) {
-                float tot = 0.f;
+            for (int k = 0; k < NOP; ++k) {
+                const int i = k * TP + otk;
+                if (i < nc) {
+                    float tot = 0.f;
 #pragma unroll
-                for (int w = 0; w < NR; ++w) tot += s_red[i][w];
-                const float inv = rsqrtf(tot * (1.0f / KD) + p.norm_eps);
-                const float y = s_o[i][ov] * inv * s_nw[ov] * sigmoid_f(bf16_bits_to_f32(og[k]));
-                p.out[((int64_t)(c0 + i) * p.H + h) * KD + ov] = (uint16_t)(pack_bf16x2(y, 0.0f) & 0xffffu);
+                    for (int w = 0; w < NR; ++w) tot += s_red[i][w];
+                    const float inv = rsqrtf(tot * (1.0f / KD) + p.norm_eps);
+                    const float y = s_o[i][ov] * inv * s_nw[ov] * sigmoid_f(bf16_bits_to_f32(og[k]));
+                    p.out[((int64_t)(c0 + i) * p.H + h) * KD + ov] = (uint16_t)(pack_bf16x2(y, 0.0f) & 0xffffu);
+                }
             }
+        }
+    }
+
+    if constexpr (SPLIT) {
+        // Arrival: every wave waits until its device-coherent output stores
+        // are complete, then one thread counts the part in; the part that
+        // finds VS-1 earlier arrivals is the last, and its device-coherent
+        // loads see every part's outputs.  (Device-scope fences would do the
+        // same by writing back and invalidating the whole L2 of each wave's
+        // chiplet, which costs microseconds while the checkpoint stores are
+        // in flight.)
+        wait_vm_all();
+        __syncthreads();
+        if (tid == 0) {
+            const int prev = __hip_atomic_fetch_add(p.counters + item, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            s_last = prev == VS - 1;
+        }
+        __syncthreads();
+        if (!s_last) return;
+        if (tid == 0) __hip_atomic_store(p.counters + item, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (hold) {  // every q/k channel's window after the last token whose column is the start slot
+            uint16_t *cs_start = p.conv_state + (int64_t)src * p.conv_slot_stride;
+#pragma unroll
+            for (int k = 0; k < NCH; ++k) {
+                if (own[k] && !is_v[k]) {
+                    cs_start[gch[k]] = (uint16_t)held[k][0];
+                    cs_start[C3 + gch[k]] = (uint16_t)held[k][1];
+                    cs_start[2 * C3 + gch[k]] = (uint16_t)held[k][2];
+                }
+            }
+        }
+        // Gated RMSNorm of the head, PF_CHUNK tokens at a time: thread
+        // (otk, ov) takes tokens otk, otk+TP, ... of the chunk, all of whose
+        // loads go out together; two waves per token.
+        for (int c0 = t0; c0 < t1; c0 += PF_CHUNK) {
+            const int nc = min(PF_CHUNK, t1 - c0);
+            float o[NOP];
+            uint32_t g[NOP];
+#pragma unroll
+            for (int k = 0; k < NOP; ++k) {
+                const int64_t t = c0 + min(k * TP + otk, nc - 1);
+                o[k] = load_coherent(p.partials + (t * p.H + h) * KD + ov);
+                g[k] = p.ogate[t * p.ogate_stride + h * KD + ov];
+            }
+#pragma unroll
+            for (int k = 0; k < NOP; ++k) {
+                const float s = wave_sum(o[k] * o[k]);
+                if (lane == 0) s_fin[k][wave] = s;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int k = 0; k < NOP; ++k) {
+                if (k * TP + otk < nc) {
+                    const float tot = s_fin[k][2 * otk] + s_fin[k][2 * otk + 1];
+                    const float inv = rsqrtf(tot * (1.0f / KD) + p.norm_eps);
+                    const float y = o[k] * inv * s_nw[ov] * sigmoid_f(bf16_bits_to_f32(g[k]));
+                    p.out[((int64_t)(c0 + k * TP + otk) * p.H + h) * KD + ov] =
+                        (uint16_t)(pack_bf16x2(y, 0.0f) & 0xffffu);
+                }
+            }
+            __syncthreads();  // s_fin is rewritten by the next chunk
         }
     }
 }
@@ -1091,13 +1242,18 @@ int launch_packed_fused(const PackedFusedParams &p, const Launch &l, void *strea
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     const dim3 grid(l.grid), block(l.block);
-    switch (l.block * 2 + l.bf16_state) {
-    case 256 * 2 + 0: hipLaunchKernelGGL((kda_packed_fused_kernel<false, 8>), grid, block, 0, s, p); break;
-    case 256 * 2 + 1: hipLaunchKernelGGL((kda_packed_fused_kernel<true, 8>), grid, block, 0, s, p); break;
-    case 512 * 2 + 0: hipLaunchKernelGGL((kda_packed_fused_kernel<false, 4>), grid, block, 0, s, p); break;
-    case 512 * 2 + 1: hipLaunchKernelGGL((kda_packed_fused_kernel<true, 4>), grid, block, 0, s, p); break;
+#define KDA_PF_CASE(VS_, NT_, B_)                                                                         \
+    case (VS_ * 2048 + NT_) * 2 + B_:                                                                     \
+        hipLaunchKernelGGL((kda_packed_fused_kernel<B_ != 0, 2048 / (NT_ * VS_), VS_>), grid, block, 0, s, p); \
+        break
+    switch ((l.vsplit * 2048 + l.block) * 2 + l.bf16_state) {
+        KDA_PF_CASE(1, 256, 0); KDA_PF_CASE(1, 256, 1);
+        KDA_PF_CASE(1, 512, 0); KDA_PF_CASE(1, 512, 1);
+        KDA_PF_CASE(2, 512, 0); KDA_PF_CASE(2, 512, 1);
+        KDA_PF_CASE(4, 512, 0); KDA_PF_CASE(4, 512, 1);
     default: return record(hipErrorInvalidValue);
     }
+#undef KDA_PF_CASE
     return record(hipGetLastError());
 }
 

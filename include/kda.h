@@ -52,7 +52,7 @@ extern "C" {
 #endif
 
 #define KDA_API __attribute__((visibility("default")))
-#define KDA_ABI_VERSION 3
+#define KDA_ABI_VERSION 4
 #define KDA_HEAD_DIM 128
 
 typedef enum kda_status {
@@ -321,6 +321,20 @@ typedef struct kda_fused_args {
  *                    A start slot <= 0 or >= num_slots, or a outside
  *                    1..max_tokens, makes the sequence null: its rows give +0
  *                    and it writes nothing.
+ *  split_counters, split_partials
+ *                    optional workspace, both or neither, owned by the caller.
+ *                    With it, the work of one (sequence, head) may be spread
+ *                    over several workgroups when there are too few pairs to
+ *                    fill the device (kda_packed_fused_plan reports the split
+ *                    as vsplit): int32 [n_seqs*H] arrival counters, which
+ *                    must be zero when the call starts and are zero again
+ *                    when it completes (zero-fill them once after
+ *                    allocating), and fp32 [n_rows*H*128], 16-byte aligned,
+ *                    for unnormalised outputs.  Calls that share them must
+ *                    not overlap in time.  NULL: one workgroup per pair.  The
+ *                    split changes only the summation order of the RMS norm
+ *                    (outputs may move by one bf16 ulp); pools, conv caches
+ *                    and everything else are identical bit for bit.
  *  Rows that belong to no sequence give +0.  All metadata is read on the
  *  device, so a captured graph may be replayed with new values.  Slots must
  *  not be shared between sequences of one call (they would race).
@@ -357,6 +371,8 @@ typedef struct kda_packed_fused_args {
     const float *norm_weight;
     float norm_eps;
     void *out;
+    int32_t *split_counters;
+    float *split_partials;
 } kda_packed_fused_args;
 
 /* Validate and enqueue.  Return KDA_OK or a negative kda_status. */

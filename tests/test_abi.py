@@ -30,7 +30,7 @@ def test_header_symbols_exported():
 
 def test_version_and_status_strings():
     L = lib()
-    assert L.kda_version() == 3
+    assert L.kda_version() == 4
     for code in _lib.STATUS:
         assert L.kda_status_string(code).decode()
     assert L.kda_status_string(12345).decode() == "unknown status"
@@ -443,6 +443,52 @@ def test_packed_fused_plan_and_validation():
     a = packed_fused_args()
     a.query_start_loc = a.state_indices  # metadata over metadata is fine (both read-only)
     assert plan_pf(a)[0] == 0, err()
+
+
+def with_split(a, rows, N, H):
+    A = Arena()
+    A.next = 1 << 40  # clear of the other buffers
+    a.split_counters = A.take(N * H * 4)
+    a.split_partials = A.take(max(rows, 1) * H * D * 4)
+    return a
+
+
+def test_packed_fused_split_plan():
+    """With the split workspace, few (sequence, head) pairs spread each head
+    over 4 or 2 workgroups (grid = pairs x split, 128/split value rows each);
+    many pairs, or no workspace, keep one workgroup per pair."""
+    for N, H, vs, block in ((1, 12, 4, 512), (3, 12, 4, 512), (8, 12, 2, 512), (10, 12, 2, 512),
+                            (32, 12, 1, 512), (128, 12, 1, 256), (1, 64, 2, 512), (2, 64, 1, 512)):
+        rows = 5 * N
+        rc, p = plan_pf(with_split(packed_fused_args(rows=rows, N=N, T=5, H=H, slots=2 * N + 2), rows, N, H))
+        assert rc == 0, err()
+        assert (p.vsplit, p.grid_x, p.block, p.rows_per_block, p.items) == (vs, N * H * vs, block, 128 // vs, N * H)
+        rc, p = plan_pf(packed_fused_args(rows=rows, N=N, T=5, H=H, slots=2 * N + 2))
+        assert rc == 0 and p.vsplit == 1 and p.grid_x == N * H, err()
+
+
+def test_packed_fused_split_validation():
+    a = with_split(packed_fused_args(), 10, 3, 12)
+    a.split_partials = None  # both or neither
+    expect(plan_pf(a), -1, "split_counters and split_partials")
+    a = with_split(packed_fused_args(), 10, 3, 12)
+    a.split_counters = None
+    expect(plan_pf(a), -1, "split_counters and split_partials")
+    a = with_split(packed_fused_args(), 10, 3, 12)
+    a.split_partials += 4  # 16-byte alignment
+    expect(plan_pf(a), -5, "split_partials")
+    a = with_split(packed_fused_args(), 10, 3, 12)
+    a.split_counters += 2
+    expect(plan_pf(a), -5, "split_counters")
+    a = with_split(packed_fused_args(), 10, 3, 12)
+    a.split_partials = a.out  # scratch over the output
+    expect(plan_pf(a), -6, "split_partials")
+    a = with_split(packed_fused_args(), 10, 3, 12)
+    a.split_counters = a.query_start_loc  # counters are written: not over metadata
+    expect(plan_pf(a), -6, "split_counters")
+    a = with_split(packed_fused_args(), 10, 3, 12)
+    a.split_counters = a.split_partials + 10 * 12 * D * 4 - 4  # last partial = first counter
+    expect(plan_pf(a), -6, "split_counters")
 
 
 def test_sizes_that_would_overflow_are_rejected():

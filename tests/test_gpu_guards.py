@@ -8,8 +8,8 @@ every kernel's bounds handling is exercised next to poisoned memory.
 import pytest
 import torch
 
-from gated_delta_rule_decode_amd import (fused_kda_decode, packed_fused_kda_decode, packed_kda_decode,
-                                         recurrent_kda, synth)
+from gated_delta_rule_decode_amd import (PackedFusedWorkspace, fused_kda_decode, packed_fused_kda_decode,
+                                         packed_kda_decode, recurrent_kda, synth)
 from tests import parity as P
 
 pytestmark = pytest.mark.gpu
@@ -131,9 +131,10 @@ def test_fused_decode_guards():
     out.check("output")
 
 
+@pytest.mark.parametrize("split", [False, True], ids=["unsplit", "split"])
 @pytest.mark.parametrize("state_dtype", [torch.float32, torch.bfloat16])
-def test_packed_fused_guards(state_dtype):
-    say(f"guards packed fused {state_dtype}")
+def test_packed_fused_guards(state_dtype, split):
+    say(f"guards packed fused {state_dtype} split={split}")
     H, S = 4, 48
     c = synth.packed_fused_case(9900, lengths=[4, 0, 3, 1, 2], H=H, num_slots=S, max_tokens=3,
                                 state_dtype=state_dtype, device=DEV, pad_rows=2)
@@ -148,10 +149,20 @@ def test_packed_fused_guards(state_dtype):
     C3 = 3 * H * D
     cs = Guarded((S, 3, C3), torch.bfloat16, fill=c.conv_state.transpose(1, 2), pad=3 * C3 * 2)
     out = Guarded((1, rows, H, D), torch.bfloat16)
+    ws = None
+    if split:  # the split workspace, exactly sized, between canaries too
+        ws = PackedFusedWorkspace(DEV)
+        cnt = Guarded((5 * H,), torch.int32, fill=torch.zeros(5 * H, dtype=torch.int32))
+        part = Guarded((rows * H * D,), torch.float32)
+        ws.counters, ws.partials = cnt.t, part.t
     packed_fused_kda_decode(c.x, c.weight, cs.t.transpose(1, 2), c.raw_gate, c.raw_beta, c.A_log, c.dt_bias, si,
                             pool.t, c.output_gate, c.norm_weight, output=out.t, query_start_loc=c.query_start_loc,
-                            num_accepted_tokens=acc)
+                            num_accepted_tokens=acc, workspace=ws)
     torch.cuda.synchronize()
     pool.check("state pool")
     cs.check("conv cache")
     out.check("output")
+    if split:
+        cnt.check("split counters")
+        part.check("split partials")
+        assert int(cnt.t.abs().sum()) == 0, "split counters not left at zero"

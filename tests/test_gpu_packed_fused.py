@@ -33,12 +33,13 @@ def np_(t):
     return None if t is None else oracle.as_np(t.detach().cpu())
 
 
-def gpu_call(c, *, si=None, acc=None, qsl=None, out=None):
+def gpu_call(c, *, si=None, acc=None, qsl=None, out=None, ws="auto"):
     return packed_fused_kda_decode(c.x, c.weight, c.conv_state, c.raw_gate, c.raw_beta, c.A_log, c.dt_bias,
                                    c.state_indices if si is None else si, c.state, c.output_gate,
                                    c.norm_weight, output=out,
                                    query_start_loc=c.query_start_loc if qsl is None else qsl,
-                                   num_accepted_tokens=c.num_accepted_tokens if acc is None else acc)
+                                   num_accepted_tokens=c.num_accepted_tokens if acc is None else acc,
+                                   workspace=ws)
 
 
 def ref_call(c, st0, cs0, *, si=None, acc=None):
@@ -59,24 +60,26 @@ def check_all(c, out, want, st0):
                                             else torch.from_numpy(st0.view(np.int16)))[unchanged])
 
 
+@pytest.mark.parametrize("ws", ["auto", None], ids=["split", "unsplit"])
 @pytest.mark.parametrize("state_dtype", [torch.float32, torch.bfloat16])
-def test_ragged_random_accepted(state_dtype):
-    say(f"packed fused ragged H=4 {state_dtype} seed=8000")
+def test_ragged_random_accepted(state_dtype, ws):
+    say(f"packed fused ragged H=4 {state_dtype} workspace={ws} seed=8000")
     c = synth.packed_fused_case(8000, lengths=[3, 1, 0, 5, 2], H=4, num_slots=40, max_tokens=5,
                                 state_dtype=state_dtype, device=DEV, pad_rows=2)
     st0, cs0 = np_(c.state).copy(), np_(c.conv_state).copy()
     want = ref_call(c, st0, cs0)
     out = torch.full((1, c.x.shape[0], 4, D), float("nan"), dtype=torch.bfloat16, device=DEV)
-    gpu_call(c, out=out)
+    gpu_call(c, out=out, ws=ws)
     torch.cuda.synchronize()
     check_all(c, out, want, st0)
 
 
-def test_padding_null_sequences_and_checkpoint_columns():
+@pytest.mark.parametrize("ws", ["auto", None], ids=["split", "unsplit"])
+def test_padding_null_sequences_and_checkpoint_columns(ws):
     """The oracle pin's layout on the GPU: a sequence longer than max_tokens,
     a slot-0 and a -1 checkpoint column, an empty sequence, a slot-0 start,
     no accepted token, and two trailing rows (outputs pre-filled with NaN)."""
-    say("packed fused padding/null H=4 fp32 seed=8100")
+    say(f"packed fused padding/null H=4 fp32 workspace={ws} seed=8100")
     c = synth.packed_fused_case(8100, lengths=[4, 0, 3, 1, 2], H=4, num_slots=24, max_tokens=3,
                                 device=DEV, pad_rows=2)
     si = c.state_indices.clone()
@@ -87,7 +90,7 @@ def test_padding_null_sequences_and_checkpoint_columns():
     st0, cs0 = np_(c.state).copy(), np_(c.conv_state).copy()
     want = ref_call(c, st0, cs0, si=np_(si), acc=np_(acc))
     out = torch.full((1, 12, 4, D), float("nan"), dtype=torch.bfloat16, device=DEV)
-    gpu_call(c, si=si, acc=acc, out=out)
+    gpu_call(c, si=si, acc=acc, out=out, ws=ws)
     torch.cuda.synchronize()
     check_all(c, out, want, st0)
     o = out.reshape(12, -1)
@@ -101,9 +104,9 @@ def test_single_token_rows_equal_fused_decode(state_dtype, rows):
     """One token per row, start column = the fused call's index: the state and
     conv caches equal fused_kda_decode's bit for bit (the per-row arithmetic
     is the same).  At 128 rows x 8 heads both calls use 8 value rows per lane
-    and the outputs are bitwise equal too; at 37 rows the packed call uses 4
-    per lane, whose RMS partial sums are added in another order, so outputs
-    may differ by one bf16 ulp."""
+    and the outputs are bitwise equal too; at 37 rows the packed call splits
+    each head over two workgroups, whose RMS sum is added in another order,
+    so outputs may differ by one bf16 ulp."""
     say(f"packed fused T=1 vs fused_kda_decode H=8 rows={rows} {state_dtype} seed=8200")
     fc = synth.fused_case(8200, rows=rows, H=8, num_slots=192, state_dtype=state_dtype, device=DEV,
                           null_zero=2, null_neg=2)
