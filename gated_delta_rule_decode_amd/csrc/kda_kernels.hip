@@ -778,12 +778,13 @@ __global__ void __launch_bounds__(256) kda_fused_kernel(const FusedParams p)
 // ------------------------------------------------- packed fused kernel ----
 //
 // The fused step over packed ragged rows with T >= 1 tokens per sequence.
-// One workgroup per (sequence, head) with the full V=128.  The sequence
-// starts from the checkpoint slot of its last accepted token; the head's
-// state (G=8 value rows per DPP row, as in the fused kernel) and the conv
-// window of the head's 384 channels (three positions per channel, in the
-// registers of the thread that owns the channel) are loaded once and carried
-// across the tokens in fp32.
+// One workgroup per (sequence, head) with the full V=128, or, when there are
+// few heads, VS workgroups per head that share it by value rows (see the
+// kernel).  The sequence starts from the checkpoint slot of its last
+// accepted token; the head's state (G value rows per DPP row) and the conv
+// windows of its channels (three positions per channel, in the registers of
+// the thread that owns the channel) are loaded once and carried across the
+// tokens in fp32.
 //
 // Tokens go in chunks of up to PF_CHUNK: the chunk's inputs are loaded at once
 // (one memory round trip); each thread runs its channels' conv over the
@@ -791,9 +792,11 @@ __global__ void __launch_bounds__(256) kda_fused_kernel(const FusedParams p)
 // scalars in LDS (a token whose checkpoint column names a live slot stores
 // the conv window right there); after one barrier the tokens run back to
 // back, each writing its unnormalised output and its RMS partial sums to LDS
-// and storing its state checkpoint (rounded to bf16 for a bf16 pool); after
-// a second barrier the gated RMSNorm of every token of the chunk is applied
-// and stored, one (token, value) per thread.  Two barriers per chunk: every
+// (split heads: its outputs to the caller's scratch) and storing its state
+// checkpoint (rounded to bf16 for a bf16 pool); after a second barrier the
+// gated RMSNorm of every token of the chunk is applied and stored, one
+// (token, value) per thread (split heads: by the last part, at the end).
+// Two barriers per chunk: every
 // read of a chunk's stage precedes the second barrier and the next chunk's
 // stage is written after it; every read of the outputs precedes the next
 // chunk's first barrier, after which they are written again.
