@@ -66,6 +66,7 @@ makers = [
     (lambda: T.packed_args(), lib.kda_packed_plan),
     (lambda: T.fused_args(), lib.kda_fused_plan),
     (lambda: T.packed_fused_args(), lib.kda_packed_fused_plan),
+    (lambda: T.with_split(T.packed_fused_args(), 10, 3, 12), lib.kda_packed_fused_plan),
 ]
 for make, fn in makers:
     base = make()
