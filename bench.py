@@ -485,7 +485,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path "
+        print(f"bench.py measures one GPU: the library has no multi-GPU path "
               f"(requested --gpus {args.gpus}); the decode shards with no communication "
               f"(rows or heads per GPU), so run one process per GPU.", file=sys.stderr)
         sys.exit(2)
