@@ -225,3 +225,21 @@ def test_speculative_workload_h12_n128_t5(state_dtype):
     P.check_bf16_out(out, want["out64"])
     P.check_state(c.state, want["state"])
     assert np.array_equal(np_(c.conv_state), want["conv_state"])
+
+
+@pytest.mark.parametrize("ws", ["auto", None], ids=["split", "unsplit"])
+@pytest.mark.parametrize("state_dtype", [torch.float32, torch.bfloat16])
+def test_start_columns_past_the_first_eight(state_dtype, ws):
+    """max_tokens 12: start columns 9 and 12 (past the first 8 columns, which
+    the kernel prefetches with the accepted count) and 1, sequences of 10, 12
+    and 3 tokens (two chunks of 8)."""
+    say(f"packed fused start columns > 8 H=4 {state_dtype} workspace={ws} seed=8150")
+    c = synth.packed_fused_case(8150, lengths=[10, 12, 3], H=4, num_slots=48, max_tokens=12,
+                                state_dtype=state_dtype, device=DEV, pad_rows=1)
+    acc = torch.tensor([9, 12, 1], dtype=torch.int32, device=DEV)
+    st0, cs0 = np_(c.state).copy(), np_(c.conv_state).copy()
+    want = ref_call(c, st0, cs0, acc=np_(acc))
+    out = torch.full((1, c.x.shape[0], 4, D), float("nan"), dtype=torch.bfloat16, device=DEV)
+    gpu_call(c, acc=acc, out=out, ws=ws)
+    torch.cuda.synchronize()
+    check_all(c, out, want, st0)
