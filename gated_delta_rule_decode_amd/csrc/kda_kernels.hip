@@ -19,10 +19,18 @@
 //    lanes covers 256 contiguous bytes of one value row; for bf16 a lane owns
 //    {8m..8m+7} and one instruction covers a whole 256-byte value row.
 //  * Per token, threads 0..255 stage q, k, v and the per-channel decay in
-//    LDS (the gate transform is evaluated once per channel), one barrier,
-//    then every lane reads its 8 channels.  The L2 norms reduce in the DPP
-//    row as well.  The LDS stage is double-buffered by token parity, so the
-//    ragged token loop needs one barrier per token.
+//    LDS (the gate transform is evaluated once per channel) and two waves
+//    reduce the L2 norm sums of q and k into LDS partials; after one barrier
+//    every lane reads its 8 channels.  The token loop (ragged, batched and
+//    verify calls) stages CHUNK tokens at a time: one round of loads and one
+//    barrier per chunk, then the chunk's tokens back to back.
+//  * The fused kernels (conv + SiLU -> KDA -> gated RMSNorm) give each thread
+//    its conv channels' windows in registers, reduce the norm sums in the
+//    DPP rows and the RMS over the head's 128 outputs in LDS; the packed
+//    fused kernel carries the state and the conv windows across a
+//    sequence's tokens and, when few heads are live, splits a head over
+//    2-4 workgroups that exchange unnormalised outputs through caller
+//    scratch (the last to arrive normalises).
 //  * The slot base is one 64-bit pointer per workgroup; everything inside a
 //    head is 32-bit offsets.
 //  * Null rows (index below the call's first live index, or >= num_slots)
