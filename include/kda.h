@@ -29,7 +29,9 @@
  *    alignment.  State dtype is fp32 or bf16; the recurrence runs in fp32 and
  *    a bf16 state is rounded to nearest-even when written back
  *    ("fused_kda_decode" Parameters: state).
- *  - state_indices is a contiguous int32 array, one per row / sequence.
+ *  - state_indices is a contiguous int32 array, one per row / sequence (the
+ *    packed fused call takes a table of checkpoint columns per sequence,
+ *    described with its arguments).
  *    Null rows produce +0 outputs and leave every cache untouched
  *    ("Serving-native packed Kimi K3 decode": -1 is inactive padding;
  *    "fused_kda_decode" Parameters: non-positive indices are null, slot 0 is
