@@ -31,7 +31,8 @@ METRIC = "decode rows/sec and achieved state HBM GB/s (% of peak), H=12/32, B=1.
 HBM_PEAK_GBPS = 8000.0
 D = 128
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_recurrent_t1_h32_fp32_b256.json")
-KERNEL_SRC = os.path.join(ROOT, "gated_delta_rule_decode_amd", "csrc", "kda_kernels.hip")
+# the sources that decide what the measured kernel does: its code and its launch policy
+KERNEL_SRCS = [os.path.join(ROOT, "gated_delta_rule_decode_amd", "csrc", n) for n in ("kda_kernels.hip", "kda_api.cpp")]
 
 
 def log(*a):
@@ -149,20 +150,24 @@ def cpu_baseline(budget_s=12.0, rows_per_worker=8, H=32):
 
 # ---------------------------------------------------------- GPU helpers ----
 
-def sha256_of(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def sha256_of(paths):
+    """sha256 over the concatenated bytes of the files."""
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def load_traffic(bytes_per_launch):
     """HBM traffic measured with rocprofv3 counters, if it was taken on the
-    current kernel source."""
+    current kernel source and launch policy."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
-        if t.get("kernel_source_sha256") != sha256_of(KERNEL_SRC):
+        if t.get("kernel_source_sha256") != sha256_of(KERNEL_SRCS):
             return None
         return float(t["hbm_bytes_per_launch"])
     except Exception:

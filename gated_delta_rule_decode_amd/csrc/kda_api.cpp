@@ -152,8 +152,15 @@ int choose_vsplit(int64_t items, bool bf16, bool token_loop)
     if (KDA_FORCE_VSPLIT == 1 || KDA_FORCE_VSPLIT == 2 || KDA_FORCE_VSPLIT == 4 || KDA_FORCE_VSPLIT == 8)
         return KDA_FORCE_VSPLIT;
     if (token_loop) return items < 96 ? 4 : (items < 1024 ? 2 : 1);
-    if (bf16 && items >= 512 && items < 1536) return 2;
-    return 4;
+    // T=1.  fp32 pools (H=12 and 32, B=1..512, graph replays over cold slot
+    // sets): 16 value rows per workgroup (vsplit 8) below ~100 items (lower
+    // latency: more CUs per head) and from ~320 items on (2.5-7% faster at
+    // B>=128: smaller tiles stream better at the same 8 waves per SIMD);
+    // 32 rows in between, where vsplit 8 measured 4-8% slower.  bf16 pools:
+    // vsplit 8 only for a handful of items; 64 rows measured 4-6% faster at
+    // 512-1535 items.
+    if (bf16) return items < 64 ? 8 : (items >= 512 && items < 1536 ? 2 : 4);
+    return (items < 112 || items >= 320) ? 8 : 4;
 }
 
 void fill_plan(kda_launch_plan *plan, const Launch &l, int64_t items)
