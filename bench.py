@@ -590,7 +590,9 @@ def main():
                      "algorithmic_bytes_per_launch": bytes_launch,
                      "kernel": f"kda_recurrent_kernel (T=1, fp32 state, {plan['rows_per_block']} value "
                                f"rows per workgroup, {plan['grid_x']} workgroups)",
-                     "practical_ceiling_GBps": 6100.0},
+                     "practical_ceiling_GBps": 6600.0,
+                     "practical_ceiling": "in-place read-modify-write probe over 1 GiB, 4 KiB per workgroup, "
+                                          "nontemporal dwordx4 (measured on this MI355X)"},
         "cpu_baseline": cpu,
     }
 
