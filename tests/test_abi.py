@@ -174,6 +174,19 @@ def test_token_loop_plan_geometry(N, H, vsplit):
     assert p.grid_x == (N * H * vsplit + 7) // 8 * 8
 
 
+@pytest.mark.parametrize("bf16,vsplit", [(False, 4), (True, 1)])
+def test_token_loop_with_checkpoints_plan_geometry(bf16, vsplit):
+    """A token loop writing fp32 checkpoints streams them in 32-row tiles at
+    any size; bf16 checkpoints keep the size rule (whole heads at 1024 items)."""
+    a = rec_args(N=64, H=16, T=190, slots=65, varlen=True, bf16=bf16)
+    A = Arena()
+    A.next = 1 << 40
+    a.checkpoints = A.take(190 * 16 * D * D * (2 if bf16 else 4))
+    rc, p = plan_rec(a)
+    assert rc == 0, err()
+    assert (p.kernel, p.vsplit, p.rows_per_block) == (2, vsplit, D // vsplit)
+
+
 def test_varlen_and_fused_plans():
     rc, p = plan_rec(rec_args(N=64, H=16, T=190, slots=65, varlen=True))
     assert rc == 0, err()
