@@ -45,6 +45,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "kda_internal.h"
 
 namespace kda_detail {
@@ -1270,9 +1272,14 @@ int launch_packed_fused(const PackedFusedParams &p, const Launch &l, void *strea
 
 int device_is_gfx950(int device)
 {
-    static int known[64];  // 0 unknown, 1 gfx950, 2 other
+    // 0 unknown, 1 gfx950, 2 other; calls from several host threads may race
+    // to fill an entry, all with the same value
+    static std::atomic<int> known[64];
     if (device < 0) return -1;
-    if (device < 64 && known[device]) return known[device] == 1;
+    if (device < 64) {
+        const int k = known[device].load(std::memory_order_relaxed);
+        if (k) return k == 1;
+    }
     hipDeviceProp_t prop;
     hipError_t e = hipGetDeviceProperties(&prop, device);
     if (e != hipSuccess) {
@@ -1283,7 +1290,7 @@ int device_is_gfx950(int device)
     const char want[] = "gfx950";
     for (int i = 0; i < 6; ++i)
         if (prop.gcnArchName[i] != want[i]) ok = 0;
-    if (device < 64) known[device] = ok ? 1 : 2;
+    if (device < 64) known[device].store(ok ? 1 : 2, std::memory_order_relaxed);
     return ok;
 }
 
