@@ -524,3 +524,35 @@ def test_sizes_that_would_overflow_are_rejected():
     f = packed_fused_args()
     f.indices_stride = 1 << 61
     expect(plan_pf(f), -2, "2^48")
+
+
+def test_validation_is_thread_safe_and_errors_are_thread_local():
+    """Eight host threads call the plan entry points at once (ctypes drops the
+    GIL around foreign calls), half with a valid argument set and half with
+    an invalid one: every thread sees its own status and its own message."""
+    import threading
+    L = lib()
+    errors = []
+
+    def worker(bad, n=400):
+        try:
+            for _ in range(n):
+                a = rec_args(N=8, H=4)
+                if bad:
+                    a.H = 0
+                p = _lib.LaunchPlan()
+                rc = L.kda_recurrent_plan(ctypes.byref(a), ctypes.byref(p))
+                msg = L.kda_last_error().decode()
+                if bad and (rc != -2 or "H" not in msg):
+                    errors.append(("bad", rc, msg))
+                if not bad and (rc != 0 or msg != ""):
+                    errors.append(("good", rc, msg))
+        except Exception as e:  # pragma: no cover - reported below
+            errors.append(("exception", repr(e)))
+
+    threads = [threading.Thread(target=worker, args=(i % 2 == 1,)) for i in range(8)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors[:5]
