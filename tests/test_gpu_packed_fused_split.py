@@ -160,3 +160,49 @@ def test_checkpoints_into_the_start_slot(state_dtype, H):
     assert torch.equal(P.bits(s_s), P.bits(c.state))
     assert torch.equal(P.bits(c_s), P.bits(c.conv_state))
     assert within_one_ulp(out_u, out)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_configurations(seed):
+    """Seeded random packed fused calls against the oracle, split and
+    unsplit: H in 1..24, 1..12 sequences of 0..11 tokens, 1..9 checkpoint
+    columns, accepted counts in 0..columns+1 (0 and columns+1 make a sequence
+    null), some columns repeating the start slot or set to 0/-1, 0..2 padding
+    rows, fp32 or bf16 pools."""
+    import random
+    rng = random.Random(5000 + seed)
+    H = rng.choice([1, 2, 4, 8, 12, 16, 24])
+    N = rng.randint(1, 12)
+    lengths = [rng.choice([0, 1, 2, 3, 5, 8, 9, 11]) for _ in range(N)]
+    T_max = rng.randint(1, 9)
+    dtype = rng.choice([torch.float32, torch.bfloat16])
+    pad = rng.randint(0, 2)
+    say(f"packed fused random seed={seed} H={H} lengths={lengths} max_tokens={T_max} {dtype} pad={pad}")
+    c = synth.packed_fused_case(5000 + seed, lengths=lengths, H=H, num_slots=N * T_max + 8, max_tokens=T_max,
+                                state_dtype=dtype, device=DEV, pad_rows=pad)
+    si = c.state_indices.clone()
+    acc = torch.tensor([rng.randint(0, T_max + 1) for _ in range(N)], dtype=torch.int32)
+    for i in range(N):
+        r = rng.random()
+        a = int(acc[i])
+        if r < 0.2 and 1 <= a <= T_max:
+            si[i, rng.randrange(T_max)] = si[i, a - 1]       # a column repeats the start slot
+        elif r < 0.35:
+            si[i, rng.randrange(T_max)] = rng.choice([0, -1])  # a column that checkpoints nothing
+    c.state_indices.copy_(si)
+    c.num_accepted_tokens.copy_(acc.to(DEV))
+    st0, cs0 = c.state.clone(), c.conv_state.clone()
+    want = ref_call(c, np_(st0).copy(), np_(cs0).copy())
+    results = []
+    for ws in (PackedFusedWorkspace(DEV), None):
+        c.state.copy_(st0)
+        c.conv_state.copy_(cs0)
+        out = gpu_call(c, ws)
+        torch.cuda.synchronize()
+        check_vs_oracle(c, out, want)
+        results.append((out.clone(), P.bits(c.state).clone(), P.bits(c.conv_state).clone()))
+        if ws is not None:
+            assert int(ws.counters.abs().sum()) == 0
+    (o_s, s_s, c_s), (o_u, s_u, c_u) = results
+    assert torch.equal(s_s, s_u) and torch.equal(c_s, c_u), "split and unsplit caches differ"
+    assert within_one_ulp(o_u, o_s)
