@@ -348,7 +348,10 @@ class PackedFusedWorkspace:
     stream when calls run concurrently."""
 
     def __init__(self, device):
-        self.device = torch.device(device)
+        dev = torch.device(device)
+        if dev.type == "cuda" and dev.index is None:
+            dev = torch.device("cuda", torch.cuda.current_device())
+        self.device = dev
         self.counters = torch.zeros(0, dtype=torch.int32, device=self.device)
         self.partials = torch.empty(0, dtype=torch.float32, device=self.device)
 
