@@ -195,6 +195,55 @@ def test_recurrent_h32_untouched_slots_bitwise(pool_h32):
     del before
 
 
+def test_row_permutation_at_full_size_is_bitwise(pool_h32):
+    """Rows are independent at any size: the full B=256, H=32 fp32 call with
+    its rows and slot indices permuted gives the permuted outputs and the same
+    touched slots, bit for bit (checks every output and slot of the launch
+    the benchmark times, where the oracle compares the same call)."""
+    say("recurrent H=32 fp32 B=256 row permutation bitwise seed=1300")
+    B, H = 256, 32
+    c = synth.recurrent_case(1300, n_seqs=B, H=H, num_slots=1, device=DEV)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(1300)
+    idx = synth.unique_slots(gen, B, 0, 4096, DEV)
+    perm = torch.randperm(B, generator=gen, device=DEV)
+    before = pool_h32.index_select(0, idx)
+    r4 = lambda t: t.reshape(B, 1, *t.shape[1:])  # noqa: E731
+    args = [r4(c.q), r4(c.k), r4(c.v), r4(c.g), r4(c.beta)]
+    out1 = recurrent_kda(*args, c.A_log, c.dt_bias, initial_state=pool_h32, state_indices=idx)
+    torch.cuda.synchronize()
+    after1 = pool_h32.index_select(0, idx)
+    pool_h32.index_copy_(0, idx.long(), before)
+    out2 = recurrent_kda(*[a[perm].contiguous() for a in args], c.A_log, c.dt_bias, initial_state=pool_h32,
+                         state_indices=idx[perm].contiguous())
+    torch.cuda.synchronize()
+    assert torch.equal(P.bits(out2), P.bits(out1[perm]))
+    assert torch.equal(P.bits(pool_h32.index_select(0, idx)), P.bits(after1))
+    del before, after1
+
+
+def test_packed_row_permutation_b512_is_bitwise():
+    """The same for packed_kda_decode at H=12, B=512, bf16, 64 inactive rows."""
+    say("packed H=12 B=512 bf16 row permutation bitwise seed=2512")
+    B = 512
+    c = synth.packed_case(2512, B=B, H=12, num_slots=1024, device=DEV, null_rows=64)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(2512)
+    perm = torch.randperm(B, generator=gen, device=DEV)
+    pool0 = c.state.clone()
+    out1 = packed_kda_decode(c.mixed_qkv, c.raw_gate, c.raw_beta, c.A_log, c.dt_bias, c.state, c.state_indices)
+    torch.cuda.synchronize()
+    pool1 = c.state.clone()
+    c.state.copy_(pool0)
+    out2 = packed_kda_decode(c.mixed_qkv[perm].contiguous(), c.raw_gate[perm].contiguous(),
+                             c.raw_beta[perm].contiguous(), c.A_log, c.dt_bias, c.state,
+                             c.state_indices[perm].contiguous())
+    torch.cuda.synchronize()
+    assert torch.equal(P.bits(out2), P.bits(out1[perm]))
+    assert torch.equal(P.bits(c.state), P.bits(pool1))
+    del pool0, pool1
+
+
 # --------------------------------------------------- config: fused decode -------
 
 @pytest.mark.parametrize("state_dtype,rows,H,slots", [

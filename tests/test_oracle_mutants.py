@@ -75,6 +75,12 @@ MUTANTS = [
     ("packed fused checkpoint skips slot filter",
      "if (dst > 0 && (int64_t)dst < num_slots) {\n                memcpy",
      "if (dst >= 0 && (int64_t)dst < num_slots) {\n                memcpy"),
+    ("gate read from the sequence's first token",
+     "for (int j = 0; j < KD; ++j) gv[j] = load_in(g, g_f32, vh + j);",
+     "for (int j = 0; j < KD; ++j) gv[j] = load_in(g, g_f32, ((size_t)t0 * HV + hv) * KD + j);"),
+    ("state gathered from the row position",
+     "size_t head_base = ((size_t)idx * HV + hv) * head_elems;",
+     "size_t head_base = ((size_t)(i % num_slots) * HV + hv) * head_elems;"),
     ("bf16 rounding truncates", "double q = nearbyint(m * 256.0);", "double q = trunc(m * 256.0);"),
     ("bf16 ties away", "double q = nearbyint(m * 256.0);", "double q = round(m * 256.0);"),
 ]
@@ -91,6 +97,8 @@ PINS = [
     pins.test_two_tokens_orthogonal_keys_closed_form,
     pins.test_same_key_beta_one_overwrites,
     pins.test_product_form_cross_formulation,
+    pins.test_beta_zero_tokens_read_out_the_cumulatively_decayed_state,
+    pins.test_row_permutation_permutes_outputs_and_keeps_pool,
     pins.test_conv_one_hot_taps_reproduce_lagged_inputs,
     pins.test_conv_output_feeds_recurrence_as_qkv,
     pins.test_gated_rmsnorm_invariants,

@@ -291,6 +291,64 @@ def test_product_form_cross_formulation():
     np.testing.assert_allclose(r["state"], pool, rtol=1e-10, atol=1e-14)
 
 
+def test_beta_zero_tokens_read_out_the_cumulatively_decayed_state():
+    """beta=0 over a ragged batch: no write ever happens, so after token t of a
+    sequence the state is the initial one scaled by the product of that
+    sequence's decays so far (per key channel), o_t = scale * q_hat_t^T of that
+    state, and the final slot holds the product over all its tokens."""
+    lengths = [4, 1, 0, 3]
+    c = _case(seed=41, n=4, H=2, slots=6, indices="random", lengths=lengths)
+    T, H = c.q.shape[0], c.H
+    st = _np(c.state).astype(np.float64)
+    r = _run(c, state=st, beta=np.full((T, H), NEG_INF_BF16))
+    q = _np(c.q.float()).astype(np.float64)
+    gr = _np(c.g.float()).astype(np.float64)
+    A = _np(c.A_log).astype(np.float64)
+    dtb = _np(c.dt_bias).astype(np.float64).reshape(H, D)
+    cu = _np(c.cu_seqlens)
+    want_pool = st.copy()
+    for i in range(4):
+        slot = int(c.state_indices[i])
+        toks = np.arange(cu[i], cu[i + 1])
+        if toks.size == 0:
+            continue
+        for h in range(H):
+            # log-decay per token and key channel, summed along the sequence
+            logd = -np.exp(A[h]) * np.logaddexp(0.0, gr[toks, h] + dtb[h])
+            cum = np.exp(np.cumsum(logd, axis=0))          # [tokens, K]
+            for j, t in enumerate(toks):
+                S_t = st[slot, h] * cum[j][None, :]          # pool orientation [v][k]
+                np.testing.assert_allclose(r["out64"][t, h], SCALE * (S_t @ _unit(q[t, h])),
+                                           rtol=1e-11, atol=1e-16)
+            want_pool[slot, h] = st[slot, h] * cum[-1][None, :]
+    np.testing.assert_allclose(r["state"], want_pool, rtol=1e-11, atol=0)
+
+
+def test_row_permutation_permutes_outputs_and_keeps_pool():
+    """Rows are independent: permuting the rows of a call together with their
+    slot indices permutes the outputs and leaves every slot of the pool (and
+    the conv cache of the fused call) bit for bit the same."""
+    c = _case(seed=42, n=7, H=2, slots=10, indices="random", null_rows=2)
+    st = _np(c.state).astype(np.float64)
+    perm = np.array([3, 6, 0, 5, 1, 4, 2])
+    r1 = _run(c, state=st)
+    r2 = _run(c, state=st, q=_np(c.q)[perm], k=_np(c.k)[perm], v=_np(c.v)[perm],
+              g=_np(c.g)[perm], beta=_np(c.beta)[perm], state_indices=_np(c.state_indices)[perm])
+    np.testing.assert_array_equal(r2["out64"], r1["out64"][perm])
+    np.testing.assert_array_equal(r2["state"], r1["state"])
+
+    f = _fcase(seed=43, rows=5, H=2, slots=8)
+    fperm = np.array([4, 2, 0, 3, 1])
+    idx = np.array([3, 0, 7, -1, 5], np.int32)
+    f1 = _frun(f, state_indices=idx)
+    rows = lambda a: _np(a)[fperm]  # noqa: E731
+    f2 = _frun(f, x=rows(f.x), raw_gate=rows(f.raw_gate), raw_beta=rows(f.raw_beta),
+               output_gate=rows(f.output_gate), state_indices=idx[fperm])
+    np.testing.assert_array_equal(f2["out64"].reshape(5, -1), f1["out64"].reshape(5, -1)[fperm])
+    np.testing.assert_array_equal(f2["state"], f1["state"])
+    np.testing.assert_array_equal(f2["conv_state"], f1["conv_state"])
+
+
 def test_varlen_equals_successive_single_steps():
     """A T-token packed step equals T successive T=1 calls (fp64 state: exact),
     and the checkpoints are the successive states."""
