@@ -137,6 +137,10 @@ u128 pool_bytes(int32_t dtype, int64_t num_slots, int64_t slot_stride, int32_t H
 // and value row group, eight waves per SIMD) is best or within 3% of best
 // almost everywhere; bf16 pools with 512..1535 items are 4-6% faster at 64
 // rows per workgroup.
+#ifndef KDA_VERIFY_CHUNK
+#define KDA_VERIFY_CHUNK 1  // build-time switch used when measuring
+#endif
+
 #ifndef KDA_FORCE_VSPLIT
 #define KDA_FORCE_VSPLIT 0  // build-time override used when tuning the policy
 #endif
@@ -270,10 +274,14 @@ int prepare_recurrent(const kda_recurrent_args *a, RecParams *p, Launch *l)
 
     const int64_t items = (int64_t)a->n_seqs * a->HV;
     const bool token_loop = ragged || tps > 1;
-    const int vsplit = choose_vsplit(items, a->state_dtype == KDA_DTYPE_BF16, token_loop,
-                                     a->checkpoints != nullptr && a->state_dtype == KDA_DTYPE_F32);
+    // Read-only batched calls with a few tokens and no checkpoints: the
+    // tokens' reads of the initial state become one matrix product per head.
+    const bool chunk = KDA_VERIFY_CHUNK && !update && !ragged && tps >= 2 && tps <= VERIFY_CHUNK_MAX_T &&
+                       !a->checkpoints;
+    const int vsplit = chunk ? 1 : choose_vsplit(items, a->state_dtype == KDA_DTYPE_BF16, token_loop,
+                                                 a->checkpoints != nullptr && a->state_dtype == KDA_DTYPE_F32);
     if (items * vsplit > 0x7ffffff0LL) return fail(KDA_ERR_SHAPE, "too many work items");
-    l->family = token_loop ? KERNEL_RECURRENT_VARLEN : KERNEL_RECURRENT_T1;
+    l->family = chunk ? KERNEL_VERIFY_CHUNK : token_loop ? KERNEL_RECURRENT_VARLEN : KERNEL_RECURRENT_T1;
     l->vsplit = vsplit;
     l->rows_per_block = KD / vsplit;
     l->grid = (int32_t)((items * vsplit + 7) & ~7LL);  // padded to whole XCD rounds

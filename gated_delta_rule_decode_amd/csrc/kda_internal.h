@@ -12,7 +12,10 @@ enum KernelFamily : int32_t {
     KERNEL_RECURRENT_VARLEN = 2,  // ragged token loop with the state held in registers
     KERNEL_FUSED = 3,          // conv + SiLU -> KDA -> gated RMSNorm
     KERNEL_PACKED_FUSED = 4,   // the fused step over packed ragged rows, T >= 1 per sequence
+    KERNEL_VERIFY_CHUNK = 5,   // read-only batched calls, 2..VERIFY_CHUNK_MAX_T tokens: one MFMA product per head
 };
+
+constexpr int VERIFY_CHUNK_MAX_T = 8;  // tokens per sequence the chunked verify kernel takes
 
 // Recurrence over (sequence, value head, value slice) work items; serves
 // recurrent_kda (T=1, uniform batches, ragged T>=0, grouped value heads,

@@ -31,6 +31,11 @@
 //    sequence's tokens and, when few heads are live, splits a head over
 //    2-4 workgroups that exchange unnormalised outputs through caller
 //    scratch (the last to arrive normalises).
+//  * Read-only batched calls with a few tokens (speculative verify) are the
+//    exception: every token's product with the state is a product with the
+//    same initial state, so they run as one small matrix product per head on
+//    the fp32 matrix cores (kda_verify_chunk_kernel) plus a forward
+//    substitution per value row.
 //  * The slot base is one 64-bit pointer per workgroup; everything inside a
 //    head is 32-bit offsets.
 //  * Null rows (index below the call's first live index, or >= num_slots)
@@ -406,11 +411,6 @@ __device__ __forceinline__ StageIn load_stage(int tid, const uint16_t *q, const 
     s.v = v[c];
     load_halves(g + c * (g_f32 ? 4 : 2), g_f32, s.g_lo, s.g_hi);
     return s;
-}
-
-__device__ __forceinline__ float input_value(uint32_t bits, bool is_f32)
-{
-    return is_f32 ? __uint_as_float(bits) : bf16_bits_to_f32(bits);
 }
 
 // Gate transform once per channel, decay = exp(-exp(A_log) * softplus(g +
@@ -1191,6 +1191,244 @@ __global__ void __launch_bounds__(2048 / (G * VS)) kda_packed_fused_kernel(const
     }
 }
 
+// --------------------------------------------- chunked verify kernel ----
+//
+// Read-only calls in the batched form ("Frozen / speculative-verify mode":
+// the pool is never written back) with 2..VERIFY_CHUNK_MAX_T tokens per
+// sequence and no checkpoints.  Every token then reads the state through the
+// slot's initial state S0 (K x V), and the recurrence unrolls per value row.
+// With L_t the log-decay of tokens 0..t summed per key channel, E_t =
+// exp(L_t), W_ts = exp(L_t - L_s) (s <= t), k^ and q^ the L2-normalised key
+// and query and b_s = beta_s u_s:
+//   u_t = v_t - k^_t.(E_t * S0) - sum_{s<t} (k^_t . W_ts k^_s) b_s
+//   o_t = scale [ q^_t.(E_t * S0) + sum_{s<=t} (q^_t . W_ts k^_s) b_s ]
+// which equals T sequential steps up to rounding.  The products with S0 are
+// one matrix product per head: the 16 x 128 matrix of rows k_t*E_t (rows t)
+// and q_t*E_t (rows 8+t), zero-padded, times S0, on the fp32 matrix cores
+// (16x16x4 MFMA) straight from the state registers; the T x T coefficients
+// are reduced once per head and the rest is a forward substitution per value
+// row.  This replaces T passes of vector arithmetic over the whole state.
+//
+// Layout: wave w owns value rows 32w..32w+31 as two 16-row tiles.  MFMA
+// lane l supplies row (l & 15) of a tile and K slot (l >> 4); the K order
+// inside the product is free, so lane l feeds the MFMAs (jj, e) with the
+// e-th value of its jj-th 16-byte access, which reads key channels
+// jj*4*VPL + (l>>4)*VPL + [0, VPL) of its row: the four lanes of one row
+// read 64 contiguous bytes per instruction.  The B operand uses the same
+// channel order from LDS.  MFMA outputs: lane l holds rows 4*(l>>4) + r of
+// the tile at column (l & 15).
+template <bool BF16>
+__global__ void __launch_bounds__(256) kda_verify_chunk_kernel(const RecParams p)
+{
+    constexpr int TM = VERIFY_CHUNK_MAX_T;
+    constexpr int VPL = BF16 ? 8 : 4;       // state values per 16-byte access
+    constexpr int NJ = 32 / VPL;            // 16-byte accesses per lane and tile
+    constexpr uint32_t ROW_BYTES = KD * (BF16 ? 2 : 4);
+    constexpr int NS = 2 + 2 * TM;          // sums per token: |q|^2, |k|^2, q.W k_s, k.W k_s
+    static_assert(TM <= 8, "two 8-row halves of the 16-column operand");
+    constexpr int RSW = (ROW_BYTES + 16) / 4;  // words per padded tile row in LDS
+    __shared__ float s_B[16][KD];
+    __shared__ uint32_t s_T[4][16 * RSW];   // per wave: one state tile, then its MFMA outputs
+    __shared__ float s_v[TM][KD];
+    __shared__ float s_part[TM][NS][8];     // per DPP row of the staging waves
+    __shared__ float s_sum[TM][NS];
+    __shared__ float s_beta[TM];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int work = (int)(blockIdx.x & 7u) * (int)(gridDim.x >> 3) + (int)(blockIdx.x >> 3);
+    if (work >= p.n_work) return;
+    const int seq = work / p.HV;
+    const int hv = work - seq * p.HV;
+    const int hq = hv / p.group;
+    const int T = p.tps;
+    const int64_t tok0 = (int64_t)seq * T;
+    const int c = tid & (KD - 1);
+    const bool g_f32 = p.g_f32 != 0;
+    const bool beta_f32 = p.beta_f32 != 0;
+    const bool precomputed = p.precomputed != 0;
+    const int g_es = g_f32 ? 4 : 2;
+    const int b_es = beta_f32 ? 4 : 2;
+
+    // Token inputs first: waves 0-1 take q, k and the gate of channel c,
+    // waves 2-3 v of channel c, and lanes t < T of wave 2 the beta of token t.
+    uint32_t xa[TM], xb[TM], glo[TM], ghi[TM];
+    uint32_t blo = 0, bhi = 0;
+#pragma unroll
+    for (int t = 0; t < TM; ++t) {
+        const int64_t n = tok0 + min(t, T - 1);
+        if (tid < KD) {
+            xa[t] = p.q[n * p.q_stride + (int64_t)hq * KD + c];
+            xb[t] = p.k[n * p.k_stride + (int64_t)hq * KD + c];
+            load_halves(static_cast<const char *>(p.g) + (n * p.g_stride + (int64_t)hv * KD + c) * g_es, g_f32,
+                        glo[t], ghi[t]);
+        } else {
+            xa[t] = p.v[n * p.v_stride + (int64_t)hv * KD + c];
+        }
+    }
+    if (wave == 2 && lane < T)
+        load_halves(static_cast<const char *>(p.beta) + ((tok0 + lane) * p.beta_stride + hv) * b_es, beta_f32, blo,
+                    bhi);
+    const float a_h = precomputed ? 0.f : __expf(p.A_log[hv]);
+    const float dtc = precomputed ? 0.f : p.dt_bias[(int64_t)hv * KD + c];
+
+    const int idx = p.state_indices[seq];
+    if (idx < 0 || (int64_t)idx >= p.num_slots) {
+        for (int i = tid; i < T * KD; i += 256)
+            p.out[((tok0 + i / KD) * p.HV + hv) * KD + (i & (KD - 1))] = 0;
+        return;
+    }
+    const char *head = static_cast<const char *>(p.state) +
+                       ((int64_t)idx * p.slot_stride + (int64_t)hv * (KD * KD)) * (BF16 ? 2 : 4);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // This wave's two 16-row state tiles, coalesced: access jj of a tile
+    // covers RPA whole rows (1 KiB).
+    constexpr int LPR = ROW_BYTES / 16;  // lanes per row
+    constexpr int RPA = 64 / LPR;        // rows per access
+    const int n16 = lane & 15;
+    const int grp = lane >> 4;
+    const int lrow = lane / LPR;
+    const int lcol = lane % LPR;
+    u32x4 raw[2][NJ];
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj)
+            raw[tau][jj] = ld_nt<u32x4>(head, (uint32_t)(32 * wave + 16 * tau + RPA * jj + lrow) * ROW_BYTES + 16u * lcol);
+    __builtin_amdgcn_sched_barrier(0);
+
+    if (tid < KD) {
+        // B operand rows, the cumulative log-decay, and the per-token sums
+        // reduced over the head's 128 channels (one partial per wave).
+        float qf[TM], kf[TM], Lt[TM];
+        float L = 0.f;
+#pragma unroll
+        for (int t = 0; t < TM; ++t) {
+            qf[t] = bf16_bits_to_f32(xa[t]);
+            kf[t] = bf16_bits_to_f32(xb[t]);
+            const float gv = halves_value(glo[t], ghi[t], g_f32);
+            L += precomputed ? gv : -a_h * softplus_f(gv + dtc);
+            Lt[t] = L;
+            const float E = __expf(L);
+            s_B[t][c] = t < T ? kf[t] * E : 0.f;  // rows past the last token are zero
+            s_B[TM + t][c] = t < T ? qf[t] * E : 0.f;
+        }
+#pragma unroll
+        for (int t = 0; t < TM; ++t) {
+            if (t < T) {
+                float v[NS];
+                v[0] = qf[t] * qf[t];
+                v[1] = kf[t] * kf[t];
+#pragma unroll
+                for (int s = 0; s <= t; ++s) {
+                    const float w = s == t ? 1.f : __expf(Lt[t] - Lt[s]);
+                    v[2 + s] = qf[t] * kf[s] * w;
+                    if (s < t) v[2 + TM + s] = kf[t] * kf[s] * w;
+                }
+#pragma unroll
+                for (int j = 0; j < NS; ++j) {
+                    if (j < 2 || (j < 2 + TM && j - 2 <= t) || (j >= 2 + TM && j - 2 - TM < t)) {
+                        const float r = row_sum16(v[j]);
+                        if ((lane & 15) == 0) s_part[t][j][tid >> 4] = r;
+                    }
+                }
+                if (p.kg && t < p.t_max) {
+                    StageIn si;
+                    si.k = xb[t];
+                    si.g_lo = glo[t];
+                    si.g_hi = ghi[t];
+                    store_kg(p.kg, p.kg_f32 != 0, ((int64_t)idx * p.HV + hv) * p.t_max + t, c, si, g_f32);
+                }
+            }
+        }
+    } else {
+#pragma unroll
+        for (int t = 0; t < TM; ++t)
+            if (t < T) s_v[t][c] = bf16_bits_to_f32(xa[t]);
+        if (wave == 2 && lane < T) {
+            const float b = halves_value(blo, bhi, beta_f32);
+            s_beta[lane] = precomputed ? b : sigmoid_f(b);
+        }
+    }
+    __syncthreads();
+
+    // The per-token sums: one thread per (token, sum) adds the 8 partials.
+    if (tid < T * NS) {
+        const int t = tid / NS, j = tid - (tid / NS) * NS;
+        float r = 0.f;
+#pragma unroll
+        for (int w = 0; w < 8; ++w) r += s_part[t][j][w];
+        s_sum[t][j] = r;
+    }
+
+    // [k_t*E_t ; q_t*E_t] x S0 for this wave's two tiles.  Each tile goes
+    // through the wave's LDS buffer (rows padded by 16 bytes, so the MFMA
+    // order's 16 rows fall on distinct banks) into the A-operand order: lane
+    // l takes row (l & 15) and, for the MFMAs (jj, e), key channel
+    // jj*4*VPL + (l>>4)*VPL + e; the B operand uses the same channel order.
+    float bop[NJ][VPL];
+#pragma unroll
+    for (int jj = 0; jj < NJ; ++jj)
+#pragma unroll
+        for (int e = 0; e < VPL; ++e) bop[jj][e] = s_B[n16][jj * 4 * VPL + grp * VPL + e];
+    uint32_t *tile = s_T[wave];
+    f32x4 acc[2];
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) {
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj)
+            *reinterpret_cast<u32x4 *>(tile + (RPA * jj + lrow) * RSW + 4 * lcol) = raw[tau][jj];
+        acc[tau] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj) {
+            const u32x4 wv = *reinterpret_cast<const u32x4 *>(tile + n16 * RSW + 16 * jj + 4 * grp);
+#pragma unroll
+            for (int e = 0; e < VPL; ++e) {
+                const uint32_t w = wv[BF16 ? e >> 1 : e];
+                const float a = BF16 ? ((e & 1) ? bf16_hi(w) : bf16_lo(w)) : __uint_as_float(w);
+                acc[tau] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bop[jj][e], acc[tau], 0, 0, 0);
+            }
+        }
+    }
+    // MFMA outputs (lane l: rows 4*(l>>4) + r of the tile, column l & 15) into
+    // the wave's buffer as [row][column]: s_C(v, n) = tile of wave v/32 at
+    // ((v & 31) * 16 + n).
+    float *outs = reinterpret_cast<float *>(tile);
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) outs[(16 * tau + 4 * grp + r) * 16 + n16] = acc[tau][r];
+    __syncthreads();
+
+    // Forward substitution per value row.
+    if (tid < KD) {
+        const int v = tid;
+        const float *cv = reinterpret_cast<const float *>(s_T[v >> 5]) + (v & 31) * 16;  // row v's 16 columns
+        float rk[TM], bu[TM];
+        const int64_t crow0 = ((int64_t)idx * p.HV + hv) * p.t_max;
+#pragma unroll
+        for (int t = 0; t < TM; ++t) {
+            if (t < T) {
+                const float *sm = s_sum[t];
+                rk[t] = rsqrtf(sm[1] + p.l2_eps);
+                const float rqs = rsqrtf(sm[0] + p.l2_eps) * p.scale;
+                float a = rk[t] * cv[t];
+#pragma unroll
+                for (int s = 0; s < t; ++s) a = fmaf(rk[t] * rk[s] * sm[2 + TM + s], bu[s], a);
+                bu[t] = s_beta[t] * (s_v[t][v] - a);
+                float o = cv[TM + t];
+#pragma unroll
+                for (int s = 0; s <= t; ++s) o = fmaf(rk[s] * sm[2 + s], bu[s], o);
+                o *= rqs;
+                p.out[((tok0 + t) * p.HV + hv) * KD + v] = (uint16_t)(pack_bf16x2(o, 0.0f) & 0xffffu);
+                if (p.corr && t < p.t_max) p.corr[(crow0 + t) * KD + v] = bu[t];
+            }
+        }
+    }
+}
+
 // ------------------------------------------------------------ dispatch ----
 
 template <int G, bool BF16>
@@ -1235,6 +1473,13 @@ int launch_recurrent(const RecParams &p, const Launch &l, void *stream)
 {
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();  // a stale error must not be blamed on this launch
+    if (l.family == KERNEL_VERIFY_CHUNK) {
+        if (l.bf16_state)
+            hipLaunchKernelGGL(kda_verify_chunk_kernel<true>, dim3(l.grid), dim3(l.block), 0, s, p);
+        else
+            hipLaunchKernelGGL(kda_verify_chunk_kernel<false>, dim3(l.grid), dim3(l.block), 0, s, p);
+        return record(hipGetLastError());
+    }
     hipError_t e = l.bf16_state ? launch_rec_dt<true>(p, l, s) : launch_rec_dt<false>(p, l, s);
     return record(e);
 }

@@ -145,7 +145,11 @@ typedef struct kda_launch_plan {
  *  g_dtype, beta_dtype  kda_dtype of g and beta (bf16 or fp32).
  *  tokens_per_seq    without cu_seqlens: 0 or 1 is T=1, T > 1 is the uniform
  *                    batched form (sequence i owns tokens [i*T, (i+1)*T)).
- *  flags             KDA_FLAG_NO_STATE_UPDATE: the pool is only read.
+ *  flags             KDA_FLAG_NO_STATE_UPDATE: the pool is only read.  The
+ *                    outputs are those of the updating call; read-only calls
+ *                    in the batched form with 2..8 tokens and no checkpoints
+ *                    evaluate them in another order (one matrix product per
+ *                    head), equal up to rounding.
  *  correction_cache  NULL or fp32 [num_slots, HV, cache_t_max, 128], contiguous,
  *                    16-byte aligned ("Frozen / speculative-verify mode":
  *                    slot-indexed per-token delta-rule corrections): for token

@@ -352,6 +352,41 @@ def test_batched_form_and_flags():
     assert plan_rec(a)[0] == 0, err()
 
 
+@pytest.mark.parametrize("tps", [2, 4, 8])
+@pytest.mark.parametrize("bf16", [False, True])
+def test_read_only_batched_calls_take_the_chunked_verify_kernel(tps, bf16):
+    """Read-only batched calls with 2..8 tokens and no checkpoints run as one
+    matrix product per head (family 5): whole heads, 256 threads."""
+    a = rec_args(N=64, H=32, tps=tps, slots=128, bf16=bf16)
+    a.flags = 1
+    rc, p = plan_rec(with_caches(a, t_max=tps))
+    assert rc == 0, err()
+    assert (p.kernel, p.vsplit, p.rows_per_block, p.block) == (5, 1, D, 256)
+    assert p.grid_x == 64 * 32 and p.items == 64 * 32
+
+
+def test_calls_outside_the_chunked_verify_kernel_keep_the_token_loop():
+    """Updating pools, more than 8 tokens, ragged rows and checkpoints stay on
+    the sequential token loop (family 2); T=1 on the T=1 kernel."""
+    a = rec_args(N=8, tps=4)
+    assert plan_rec(a)[1].kernel == 2  # updating
+    a = rec_args(N=8, tps=9)
+    a.flags = 1
+    assert plan_rec(a)[1].kernel == 2  # 9 tokens
+    a = rec_args(N=8, T=24, varlen=True)
+    a.flags = 1
+    assert plan_rec(a)[1].kernel == 2  # ragged
+    a = rec_args(N=8, tps=4)
+    a.flags = 1
+    A = Arena()
+    A.next = 1 << 40
+    a.checkpoints = A.take(32 * 4 * D * D * 4)
+    assert plan_rec(a)[1].kernel == 2  # checkpoints
+    a = rec_args(N=8)
+    a.flags = 1
+    assert plan_rec(a)[1].kernel == 1  # one token
+
+
 def test_read_only_pool_still_may_not_alias_outputs():
     a = rec_args(varlen=True, T=4)
     a.flags = 1

@@ -1,0 +1,147 @@
+"""GPU parity of the chunked verify kernel ("flashinfer.kda_decode", Frozen /
+speculative-verify mode): read-only batched calls with 2..8 tokens per
+sequence and no checkpoints, where the tokens' products with the slot's
+initial state are one matrix product per head and the rest a forward
+substitution.  Against the fp64 oracle on every output, cache entry and pool
+bit: token counts 2..8, fp32 and bf16 pools, in-kernel and precomputed gates
+(bf16 and fp32), grouped value heads, null rows and an index past the pool,
+caches shorter than, equal to and longer than the token count, and decays so
+strong that the cumulative decay underflows.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gated_delta_rule_decode_amd import _lib, recurrent_kda, synth
+from tests import parity as P
+from tests.test_gpu_verify import call, check_caches, np_, recorded_mask, reference
+
+pytestmark = pytest.mark.gpu
+D = 128
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+def chunk_plan_kernel(n, T, H, HV, slots, bf16):
+    """Kernel family the library plans for a read-only batched call of this shape."""
+    import ctypes
+    a = _lib.RecurrentArgs()
+    a.struct_size = ctypes.sizeof(_lib.RecurrentArgs)
+    a.n_seqs, a.n_tokens, a.H, a.HV, a.K, a.V = n, n * T, H, HV, D, D
+    base = 1 << 36
+    nxt = [base]
+
+    def take(nb):
+        p = nxt[0]
+        nxt[0] += (nb + 4096 + 255) & ~255
+        return p
+    for f, hh in (("q", H), ("k", H), ("v", HV), ("g", HV)):
+        setattr(a, f, take(n * T * hh * D * 2))
+        setattr(a, f + "_stride", hh * D)
+    a.beta, a.beta_stride = take(n * T * HV * 2), HV
+    a.A_log, a.dt_bias = take(HV * 4), take(HV * D * 4)
+    a.scale, a.l2_eps = 0.08838834764831845, 1e-6
+    a.state = take(slots * HV * D * D * (2 if bf16 else 4))
+    a.state_dtype = a.ckpt_dtype = 1 if bf16 else 0
+    a.num_slots, a.slot_stride = slots, HV * D * D
+    a.state_indices = take(n * 4)
+    a.out = take(n * T * HV * D * 2)
+    a.g_dtype = a.beta_dtype = 1
+    a.tokens_per_seq, a.flags = T, 1
+    plan = _lib.LaunchPlan()
+    plan.struct_size = ctypes.sizeof(_lib.LaunchPlan)
+    assert _lib.load().kda_recurrent_plan(ctypes.byref(a), ctypes.byref(plan)) == 0
+    return plan.kernel
+
+
+CASES = [  # T, state dtype, gate, gate dtype, H, HV, cache length
+    (2, torch.float32, "in_kernel", torch.bfloat16, 4, 4, 2),
+    (3, torch.bfloat16, "in_kernel", torch.bfloat16, 4, 8, 5),
+    (4, torch.float32, "precomputed", torch.float32, 2, 8, 3),
+    (5, torch.bfloat16, "precomputed", torch.bfloat16, 4, 4, 5),
+    (6, torch.float32, "in_kernel", torch.float32, 8, 8, 8),
+    (7, torch.float32, "precomputed", torch.float32, 4, 12, 7),
+    (8, torch.bfloat16, "in_kernel", torch.bfloat16, 4, 8, 8),
+    (8, torch.float32, "in_kernel", torch.bfloat16, 6, 12, 6),
+]
+
+
+@pytest.mark.parametrize("T,state_dtype,gate,gate_dtype,H,HV,t_max", CASES,
+                         ids=[f"T{c[0]}-{'bf16' if c[1] == torch.bfloat16 else 'fp32'}-{c[2]}-H{c[4]}HV{c[5]}"
+                              f"-tmax{c[6]}" for c in CASES])
+def test_chunked_verify_against_oracle(T, state_dtype, gate, gate_dtype, H, HV, t_max):
+    seed = 7600 + 10 * T + HV
+    n, slots = 11, 24
+    say(f"chunked verify T={T} {state_dtype} gate={gate}/{gate_dtype} H={H} HV={HV} t_max={t_max} seed={seed}")
+    assert chunk_plan_kernel(n, T, H, HV, slots, state_dtype == torch.bfloat16) == 5
+    c = synth.recurrent_case(seed, n_seqs=n, H=H, HV=HV, num_slots=slots, state_dtype=state_dtype, device=DEV,
+                             indices="random", lengths=[T] * n, null_rows=2, gate=gate, gate_dtype=gate_dtype)
+    c.state_indices[4] = slots + 5  # past the pool: null
+    st0 = c.state.clone()
+    want = reference(c, np_(st0), t_max=t_max, ragged=False, read_only=True, tps=T)
+    kg_dtype = torch.float32 if T % 2 else torch.bfloat16
+    out, corr, kg, _ = call(c, form="batched", t_max=t_max, kg_dtype=kg_dtype, read_only=True, tps=T)
+    assert torch.equal(P.bits(st0), P.bits(c.state)), "read-only pool changed"
+    e1 = P.check_bf16_out(out, want["out64"])
+    e2 = check_caches(corr, kg, want, recorded_mask(c, [T] * n, t_max))
+    idx = c.state_indices.cpu().numpy()
+    o = P.bits(out.reshape(n, T, HV, D).cpu())
+    for i in range(n):
+        if not (0 <= idx[i] < slots):
+            assert not o[i].any(), "null rows must produce +0"
+    say(f"out err {e1:.3e} corr err {e2:.3e}")
+
+
+def test_chunked_verify_with_underflowing_decay():
+    """Log-decays of -20..-90 per token: the cumulative decay underflows to
+    zero in fp32 within a token or two; outputs and corrections stay finite
+    and match the oracle."""
+    T, n, H, slots = 6, 7, 4, 12
+    say(f"chunked verify underflowing decay T={T} H={H} seed=7700")
+    c = synth.recurrent_case(7700, n_seqs=n, H=H, num_slots=slots, device=DEV, indices="random", lengths=[T] * n,
+                             gate="precomputed", gate_dtype=torch.float32)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(7700)
+    c.g.copy_(-(20.0 + 70.0 * torch.rand(c.g.shape, generator=gen, device=DEV)))
+    st0 = c.state.clone()
+    want = reference(c, np_(st0), t_max=T, ragged=False, read_only=True, tps=T)
+    out, corr, kg, _ = call(c, form="batched", t_max=T, kg_dtype=torch.float32, read_only=True, tps=T)
+    assert torch.isfinite(out.float()).all() and torch.isfinite(corr).all()
+    P.check_bf16_out(out, want["out64"])
+    check_caches(corr, kg, want, recorded_mask(c, [T] * n, T))
+
+
+def test_chunked_and_sequential_forms_agree():
+    """The same tokens through the chunked read-only kernel and through the
+    sequential token loop (an updating call on a copy of the pool) give
+    outputs within the bf16 bar of each other, and the read-only call leaves
+    its pool untouched."""
+    T, n, H = 4, 16, 8
+    say(f"chunked vs sequential T={T} H={H} seed=7800")
+    c = synth.recurrent_case(7800, n_seqs=n, H=H, num_slots=20, device=DEV, indices="random", lengths=[T] * n)
+    st0 = c.state.clone()
+    shp = lambda t: t.reshape(n, T, *t.shape[1:])  # noqa: E731
+    args = [shp(c.q), shp(c.k), shp(c.v), shp(c.g), shp(c.beta), c.A_log, c.dt_bias]
+    o_chunk = recurrent_kda(*args, initial_state=c.state, state_indices=c.state_indices,
+                            disable_state_update=True)
+    pool2 = st0.clone()
+    o_seq = recurrent_kda(*args, initial_state=pool2, state_indices=c.state_indices)
+    torch.cuda.synchronize()
+    assert torch.equal(P.bits(st0), P.bits(c.state))
+    want = oracle.recurrent(np_(c.q), np_(c.k), np_(c.v), np_(c.g), np_(c.beta), np_(c.A_log), np_(c.dt_bias),
+                            np_(st0), np_(c.state_indices), None, update_state=False, tokens_per_seq=T)
+    P.check_bf16_out(o_chunk, want["out64"])
+    P.check_bf16_out(o_seq, want["out64"])
+    diff = (o_chunk.float() - o_seq.float()).abs().max().item()
+    assert diff <= 2 * P.OUT_ATOL, diff
+    assert np.isfinite(diff)
