@@ -98,6 +98,32 @@ def test_recurrent_ragged_checkpoint_and_cache_guards(state_dtype):
         g.check(n)
 
 
+@pytest.mark.parametrize("state_dtype,T,TM", [(torch.float32, 8, 5), (torch.bfloat16, 3, 6)])
+def test_chunked_verify_guards(state_dtype, T, TM):
+    """Read-only batched calls with 2..8 tokens (the chunked matrix-core
+    kernel): output and both verify caches guarded, the pool guarded and
+    unchanged, with a null row and an index past the pool."""
+    say(f"guards chunked verify T={T} cache {TM} {state_dtype}")
+    n, H, HV, S = 6, 2, 4, 12
+    c = synth.recurrent_case(9650 + T, n_seqs=n, H=H, HV=HV, num_slots=S, state_dtype=state_dtype, device=DEV,
+                             indices="random", lengths=[T] * n, null_rows=1)
+    idx = c.state_indices.clone()
+    idx[2] = S + 3
+    pool = guarded_pool(c.state)
+    before = pool.t.clone()
+    out = Guarded((n, T, HV, D), torch.bfloat16)
+    corr = Guarded((S, HV, TM, D), torch.float32)
+    kg = Guarded((S, HV, TM, 2 * D), torch.float32)
+    b = lambda t: t.reshape(n, T, *t.shape[1:])  # noqa: E731
+    recurrent_kda(b(c.q), b(c.k), b(c.v), b(c.g), b(c.beta), c.A_log, c.dt_bias, initial_state=pool.t,
+                  state_indices=idx, output=out.t, disable_state_update=True, correction_cache=corr.t,
+                  kg_cache=kg.t)
+    torch.cuda.synchronize()
+    for g, nm in ((pool, "state pool"), (out, "output"), (corr, "correction cache"), (kg, "kg cache")):
+        g.check(nm)
+    assert torch.equal(P.bits(pool.t), P.bits(before)), "read-only pool changed"
+
+
 def test_packed_decode_guards():
     say("guards packed decode H=12 bf16")
     B, H, S = 40, 12, 64

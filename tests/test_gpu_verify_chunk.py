@@ -145,3 +145,38 @@ def test_chunked_and_sequential_forms_agree():
     diff = (o_chunk.float() - o_seq.float()).abs().max().item()
     assert diff <= 2 * P.OUT_ATOL, diff
     assert np.isfinite(diff)
+
+
+def test_chunked_verify_graph_replay_with_new_inputs_and_indices():
+    """A captured read-only T=4 call replays with new token inputs and slot
+    indices written into its buffers (metadata is read on the device):
+    every replay equals the same call made eagerly, bit for bit."""
+    T, n, H, slots = 4, 12, 4, 40
+    say(f"chunked verify graph replay T={T} H={H} seed=7900")
+    c = synth.recurrent_case(7900, n_seqs=n, H=H, num_slots=slots, device=DEV, indices="random", lengths=[T] * n)
+    shp = lambda t: t.reshape(n, T, *t.shape[1:])  # noqa: E731
+    bufs = [shp(c.q).clone(), shp(c.k).clone(), shp(c.v).clone(), shp(c.g).clone(), shp(c.beta).clone()]
+    idx = c.state_indices.clone()
+    out = torch.empty((n, T, H, D), dtype=torch.bfloat16, device=DEV)
+
+    def run(o):
+        return recurrent_kda(*bufs, c.A_log, c.dt_bias, initial_state=c.state, state_indices=idx, output=o,
+                             disable_state_update=True)
+    run(out)  # warm up outside the capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run(out)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(7901)
+    for rep in range(3):
+        for b in bufs:
+            b.copy_(torch.randn(b.shape, generator=gen, device=DEV).to(b.dtype))
+        idx.copy_(torch.randperm(slots, generator=gen, device=DEV)[:n].to(torch.int32))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        eager = torch.empty_like(out)
+        run(eager)
+        torch.cuda.synchronize()
+        assert torch.equal(P.bits(out), P.bits(eager)), f"replay {rep} differs from the eager call"
