@@ -1205,18 +1205,20 @@ __global__ void __launch_bounds__(2048 / (G * VS)) kda_packed_fused_kernel(const
 // which equals T sequential steps up to rounding.  The products with S0 are
 // one matrix product per head: the 16 x 128 matrix of rows k_t*E_t (rows t)
 // and q_t*E_t (rows 8+t), zero-padded, times S0, on the fp32 matrix cores
-// (16x16x4 MFMA) straight from the state registers; the T x T coefficients
-// are reduced once per head and the rest is a forward substitution per value
-// row.  This replaces T passes of vector arithmetic over the whole state.
+// (16x16x4 MFMA); the T x T coefficients are reduced once per head and the
+// rest is a forward substitution per value row.  This replaces T passes of
+// vector arithmetic over the whole state.
 //
-// Layout: wave w owns value rows 32w..32w+31 as two 16-row tiles.  MFMA
-// lane l supplies row (l & 15) of a tile and K slot (l >> 4); the K order
-// inside the product is free, so lane l feeds the MFMAs (jj, e) with the
-// e-th value of its jj-th 16-byte access, which reads key channels
-// jj*4*VPL + (l>>4)*VPL + [0, VPL) of its row: the four lanes of one row
-// read 64 contiguous bytes per instruction.  The B operand uses the same
-// channel order from LDS.  MFMA outputs: lane l holds rows 4*(l>>4) + r of
-// the tile at column (l & 15).
+// Layout: wave w owns value rows 32w..32w+31 as two 16-row tiles, loaded
+// with coalesced 16-byte accesses (whole rows per instruction).  MFMA lane l
+// supplies row (l & 15) of a tile and K slot (l >> 4); the K order inside
+// the product is free, so lane l feeds the MFMAs (jj, e) with key channel
+// jj*4*VPL + (l>>4)*VPL + e.  Reading the state from memory in that order
+// (16 rows x 64 bytes per instruction) was measured slower than loading
+// whole rows and transposing each tile through a per-wave LDS buffer, which
+// is what happens here.  The B operand uses the same channel order from
+// LDS.  MFMA outputs: lane l holds rows 4*(l>>4) + r of the tile at column
+// (l & 15).
 template <bool BF16>
 __global__ void __launch_bounds__(256) kda_verify_chunk_kernel(const RecParams p)
 {
@@ -1335,7 +1337,7 @@ __global__ void __launch_bounds__(256) kda_verify_chunk_kernel(const RecParams p
                     }
                 }
                 if (p.kg && t < p.t_max) {
-                    StageIn si;
+                    StageIn si{};
                     si.k = xb[t];
                     si.g_lo = glo[t];
                     si.g_hi = ghi[t];
