@@ -1209,16 +1209,18 @@ __global__ void __launch_bounds__(2048 / (G * VS)) kda_packed_fused_kernel(const
 // rest is a forward substitution per value row.  This replaces T passes of
 // vector arithmetic over the whole state.
 //
-// Layout: wave w owns value rows 32w..32w+31 as two 16-row tiles, loaded
-// with coalesced 16-byte accesses (whole rows per instruction).  MFMA lane l
-// supplies row (l & 15) of a tile and K slot (l >> 4); the K order inside
-// the product is free, so lane l feeds the MFMAs (jj, e) with key channel
-// jj*4*VPL + (l>>4)*VPL + e.  Reading the state from memory in that order
-// (16 rows x 64 bytes per instruction) was measured slower than loading
-// whole rows and transposing each tile through a per-wave LDS buffer, which
-// is what happens here.  The B operand uses the same channel order from
-// LDS.  MFMA outputs: lane l holds rows 4*(l>>4) + r of the tile at column
-// (l & 15).
+// Layout: wave w owns value rows 32w..32w+31 as two 16-row tiles.  MFMA
+// lane l supplies row (l & 15) of a tile and K slot (l >> 4); the K order
+// inside the product is free, so lane l feeds the MFMAs (jj, e) with key
+// channel jj*4*VPL + (l>>4)*VPL + e, the e-th value of 16 contiguous bytes.
+// Loading a tile in that order reads 16 rows x 64 bytes per instruction,
+// which streams worse from HBM than whole rows; loading whole rows and
+// transposing through LDS costs LDS bandwidth instead.  Each wave does one
+// of each (tile 0 direct, tile 1 through its LDS buffer, rows padded by 16
+// bytes so the 16 rows of one read fall on distinct banks): measured faster
+// than either alone, as the two costs overlap.  The B operand uses the same
+// channel order from LDS.  MFMA outputs: lane l holds rows 4*(l>>4) + r of
+// the tile at column (l & 15).
 template <bool BF16>
 __global__ void __launch_bounds__(256) kda_verify_chunk_kernel(const RecParams p)
 {
@@ -1285,8 +1287,9 @@ __global__ void __launch_bounds__(256) kda_verify_chunk_kernel(const RecParams p
                        ((int64_t)idx * p.slot_stride + (int64_t)hv * (KD * KD)) * (BF16 ? 2 : 4);
     __builtin_amdgcn_sched_barrier(0);
 
-    // This wave's two 16-row state tiles, coalesced: access jj of a tile
-    // covers RPA whole rows (1 KiB).
+    // This wave's two 16-row state tiles: tile 0 in the MFMA order (access jj
+    // of lane l: 16 bytes of row l & 15 at byte 64*jj + 16*(l >> 4)), tile 1
+    // coalesced (access jj covers RPA whole rows, 1 KiB).
     constexpr int LPR = ROW_BYTES / 16;  // lanes per row
     constexpr int RPA = 64 / LPR;        // rows per access
     const int n16 = lane & 15;
@@ -1295,10 +1298,11 @@ __global__ void __launch_bounds__(256) kda_verify_chunk_kernel(const RecParams p
     const int lcol = lane % LPR;
     u32x4 raw[2][NJ];
 #pragma unroll
-    for (int tau = 0; tau < 2; ++tau)
+    for (int jj = 0; jj < NJ; ++jj)
+        raw[0][jj] = ld_nt<u32x4>(head, (uint32_t)(32 * wave + n16) * ROW_BYTES + 64u * jj + 16u * grp);
 #pragma unroll
-        for (int jj = 0; jj < NJ; ++jj)
-            raw[tau][jj] = ld_nt<u32x4>(head, (uint32_t)(32 * wave + 16 * tau + RPA * jj + lrow) * ROW_BYTES + 16u * lcol);
+    for (int jj = 0; jj < NJ; ++jj)
+        raw[1][jj] = ld_nt<u32x4>(head, (uint32_t)(32 * wave + 16 + RPA * jj + lrow) * ROW_BYTES + 16u * lcol);
     __builtin_amdgcn_sched_barrier(0);
 
     if (tid < KD) {
@@ -1365,11 +1369,8 @@ __global__ void __launch_bounds__(256) kda_verify_chunk_kernel(const RecParams p
         s_sum[t][j] = r;
     }
 
-    // [k_t*E_t ; q_t*E_t] x S0 for this wave's two tiles.  Each tile goes
-    // through the wave's LDS buffer (rows padded by 16 bytes, so the MFMA
-    // order's 16 rows fall on distinct banks) into the A-operand order: lane
-    // l takes row (l & 15) and, for the MFMAs (jj, e), key channel
-    // jj*4*VPL + (l>>4)*VPL + e; the B operand uses the same channel order.
+    // [k_t*E_t ; q_t*E_t] x S0 for this wave's two tiles, tile 1 transposed
+    // into the A-operand order through the wave's LDS buffer.
     float bop[NJ][VPL];
 #pragma unroll
     for (int jj = 0; jj < NJ; ++jj)
@@ -1378,14 +1379,14 @@ __global__ void __launch_bounds__(256) kda_verify_chunk_kernel(const RecParams p
     uint32_t *tile = s_T[wave];
     f32x4 acc[2];
 #pragma unroll
-    for (int tau = 0; tau < 2; ++tau) {
+    for (int jj = 0; jj < NJ; ++jj)
+        *reinterpret_cast<u32x4 *>(tile + (RPA * jj + lrow) * RSW + 4 * lcol) = raw[1][jj];
 #pragma unroll
-        for (int jj = 0; jj < NJ; ++jj)
-            *reinterpret_cast<u32x4 *>(tile + (RPA * jj + lrow) * RSW + 4 * lcol) = raw[tau][jj];
+    for (int tau = 0; tau < 2; ++tau) {
         acc[tau] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int jj = 0; jj < NJ; ++jj) {
-            const u32x4 wv = *reinterpret_cast<const u32x4 *>(tile + n16 * RSW + 16 * jj + 4 * grp);
+            const u32x4 wv = tau == 0 ? raw[0][jj] : *reinterpret_cast<const u32x4 *>(tile + n16 * RSW + 16 * jj + 4 * grp);
 #pragma unroll
             for (int e = 0; e < VPL; ++e) {
                 const uint32_t w = wv[BF16 ? e >> 1 : e];
