@@ -1204,10 +1204,13 @@ __global__ void __launch_bounds__(2048 / (G * VS)) kda_packed_fused_kernel(const
 //   o_t = scale [ q^_t.(E_t * S0) + sum_{s<=t} (q^_t . W_ts k^_s) b_s ]
 // which equals T sequential steps up to rounding.  The products with S0 are
 // one matrix product per head: the 16 x 128 matrix of rows k_t*E_t (rows t)
-// and q_t*E_t (rows 8+t), zero-padded, times S0, on the fp32 matrix cores
+// and q_t*E_t (rows TM+t), zero-padded, times S0, on the fp32 matrix cores
 // (16x16x4 MFMA); the T x T coefficients are reduced once per head and the
 // rest is a forward substitution per value row.  This replaces T passes of
-// vector arithmetic over the whole state.
+// vector arithmetic over the whole state.  TM, the token slots the kernel
+// is built for (4 or 8, the smallest that holds T), sizes the input
+// registers and LDS: with TM = 4 an fp32 workgroup fits in 108 VGPRs and
+// 40 KB of LDS, four workgroups per CU instead of three.
 //
 // Layout: wave w owns value rows 32w..32w+31 as two 16-row tiles.  MFMA
 // lane l supplies row (l & 15) of a tile and K slot (l >> 4); the K order
@@ -1216,23 +1219,23 @@ __global__ void __launch_bounds__(2048 / (G * VS)) kda_packed_fused_kernel(const
 // Loading a tile in that order reads 16 rows x 64 bytes per instruction,
 // which streams worse from HBM than whole rows; loading whole rows and
 // transposing through LDS costs LDS bandwidth instead.  Each wave does one
-// of each (tile 0 direct, tile 1 through its LDS buffer, rows padded by 16
-// bytes so the 16 rows of one read fall on distinct banks): measured faster
-// than either alone, as the two costs overlap.  The B operand uses the same
+// of each (tile 0 direct, tile 1 through its LDS buffer, the 16-byte
+// columns of row r stored at column ^ (r & 15), so the 16 rows of one read
+// fall on distinct banks without padding): measured faster than either
+// alone, as the two costs overlap.  The B operand uses the same
 // channel order from LDS.  MFMA outputs: lane l holds rows 4*(l>>4) + r of
 // the tile at column (l & 15).
-template <bool BF16>
+template <bool BF16, int TM>
 __global__ void __launch_bounds__(256) kda_verify_chunk_kernel(const RecParams p)
 {
-    constexpr int TM = VERIFY_CHUNK_MAX_T;
     constexpr int VPL = BF16 ? 8 : 4;       // state values per 16-byte access
     constexpr int NJ = 32 / VPL;            // 16-byte accesses per lane and tile
     constexpr uint32_t ROW_BYTES = KD * (BF16 ? 2 : 4);
     constexpr int NS = 2 + 2 * TM;          // sums per token: |q|^2, |k|^2, q.W k_s, k.W k_s
-    static_assert(TM <= 8, "two 8-row halves of the 16-column operand");
-    constexpr int RSW = (ROW_BYTES + 16) / 4;  // words per padded tile row in LDS
-    __shared__ float s_B[16][KD];
-    __shared__ uint32_t s_T[4][16 * RSW];   // per wave: one state tile, then its MFMA outputs
+    static_assert(TM <= VERIFY_CHUNK_MAX_T && 2 * TM <= 16, "k and q rows of the 16-column operand");
+    constexpr int RSW = ROW_BYTES / 4;      // words per tile row in LDS
+    __shared__ float s_B[2 * TM][KD];       // operand rows k_t*E_t (t), q_t*E_t (TM + t); rows past 2 TM are zero
+    __shared__ uint32_t s_T[4][16 * RSW];   // per wave: one state tile (16-byte columns XOR-swizzled by row), then its MFMA outputs
     __shared__ float s_v[TM][KD];
     __shared__ float s_part[TM][NS][8];     // per DPP row of the staging waves
     __shared__ float s_sum[TM][NS];
@@ -1375,18 +1378,18 @@ __global__ void __launch_bounds__(256) kda_verify_chunk_kernel(const RecParams p
 #pragma unroll
     for (int jj = 0; jj < NJ; ++jj)
 #pragma unroll
-        for (int e = 0; e < VPL; ++e) bop[jj][e] = s_B[n16][jj * 4 * VPL + grp * VPL + e];
+        for (int e = 0; e < VPL; ++e) bop[jj][e] = n16 < 2 * TM ? s_B[n16 < 2 * TM ? n16 : 0][jj * 4 * VPL + grp * VPL + e] : 0.f;
     uint32_t *tile = s_T[wave];
     f32x4 acc[2];
 #pragma unroll
     for (int jj = 0; jj < NJ; ++jj)
-        *reinterpret_cast<u32x4 *>(tile + (RPA * jj + lrow) * RSW + 4 * lcol) = raw[1][jj];
+        *reinterpret_cast<u32x4 *>(tile + (RPA * jj + lrow) * RSW + 4 * (lcol ^ ((RPA * jj + lrow) & 15))) = raw[1][jj];
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau) {
         acc[tau] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int jj = 0; jj < NJ; ++jj) {
-            const u32x4 wv = tau == 0 ? raw[0][jj] : *reinterpret_cast<const u32x4 *>(tile + n16 * RSW + 16 * jj + 4 * grp);
+            const u32x4 wv = tau == 0 ? raw[0][jj] : *reinterpret_cast<const u32x4 *>(tile + n16 * RSW + 4 * ((4 * jj + grp) ^ n16));
 #pragma unroll
             for (int e = 0; e < VPL; ++e) {
                 const uint32_t w = wv[BF16 ? e >> 1 : e];
@@ -1477,10 +1480,15 @@ int launch_recurrent(const RecParams &p, const Launch &l, void *stream)
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();  // a stale error must not be blamed on this launch
     if (l.family == KERNEL_VERIFY_CHUNK) {
-        if (l.bf16_state)
-            hipLaunchKernelGGL(kda_verify_chunk_kernel<true>, dim3(l.grid), dim3(l.block), 0, s, p);
-        else
-            hipLaunchKernelGGL(kda_verify_chunk_kernel<false>, dim3(l.grid), dim3(l.block), 0, s, p);
+        // token slots sized to the call: 4 for up to 4 tokens, else 8
+        const dim3 grid(l.grid), block(l.block);
+        if (p.tps <= 4) {
+            if (l.bf16_state) hipLaunchKernelGGL((kda_verify_chunk_kernel<true, 4>), grid, block, 0, s, p);
+            else hipLaunchKernelGGL((kda_verify_chunk_kernel<false, 4>), grid, block, 0, s, p);
+        } else {
+            if (l.bf16_state) hipLaunchKernelGGL((kda_verify_chunk_kernel<true, 8>), grid, block, 0, s, p);
+            else hipLaunchKernelGGL((kda_verify_chunk_kernel<false, 8>), grid, block, 0, s, p);
+        }
         return record(hipGetLastError());
     }
     hipError_t e = l.bf16_state ? launch_rec_dt<true>(p, l, s) : launch_rec_dt<false>(p, l, s);
