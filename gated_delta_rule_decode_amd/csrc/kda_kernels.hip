@@ -1234,10 +1234,14 @@ __global__ void __launch_bounds__(256) kda_verify_chunk_kernel(const RecParams p
     constexpr int NS = 2 + 2 * TM;          // sums per token: |q|^2, |k|^2, q.W k_s, k.W k_s
     static_assert(TM <= VERIFY_CHUNK_MAX_T && 2 * TM <= 16, "k and q rows of the 16-column operand");
     constexpr int RSW = ROW_BYTES / 4;      // words per tile row in LDS
-    __shared__ float s_B[2 * TM][KD];       // operand rows k_t*E_t (t), q_t*E_t (TM + t); rows past 2 TM are zero
+    // operand rows k_t*E_t (t), q_t*E_t (TM + t), rows past 2 TM zero; padded
+    // by 16 bytes so that the 16 rows read by one instruction spread over the
+    // banks
+    __shared__ float s_B[2 * TM][KD + 4];
+    constexpr int OSTR = 20;                // floats per row of the MFMA outputs in LDS (16 + 4 padding)
     __shared__ uint32_t s_T[4][16 * RSW];   // per wave: one state tile (16-byte columns XOR-swizzled by row), then its MFMA outputs
     __shared__ float s_v[TM][KD];
-    __shared__ float s_part[TM][NS][8];     // per DPP row of the staging waves
+    __shared__ float s_part[8][TM * NS];    // [DPP row of the staging waves][token * NS + sum]
     __shared__ float s_sum[TM][NS];
     __shared__ float s_beta[TM];
 
@@ -1340,7 +1344,7 @@ __global__ void __launch_bounds__(256) kda_verify_chunk_kernel(const RecParams p
                 for (int j = 0; j < NS; ++j) {
                     if (j < 2 || (j < 2 + TM && j - 2 <= t) || (j >= 2 + TM && j - 2 - TM < t)) {
                         const float r = row_sum16(v[j]);
-                        if ((lane & 15) == 0) s_part[t][j][tid >> 4] = r;
+                        if ((lane & 15) == 0) s_part[tid >> 4][t * NS + j] = r;
                     }
                 }
                 if (p.kg && t < p.t_max) {
@@ -1368,7 +1372,7 @@ __global__ void __launch_bounds__(256) kda_verify_chunk_kernel(const RecParams p
         const int t = tid / NS, j = tid - (tid / NS) * NS;
         float r = 0.f;
 #pragma unroll
-        for (int w = 0; w < 8; ++w) r += s_part[t][j][w];
+        for (int w = 0; w < 8; ++w) r += s_part[w][tid];
         s_sum[t][j] = r;
     }
 
@@ -1400,18 +1404,19 @@ __global__ void __launch_bounds__(256) kda_verify_chunk_kernel(const RecParams p
     }
     // MFMA outputs (lane l: rows 4*(l>>4) + r of the tile, column l & 15) into
     // the wave's buffer as [row][column]: s_C(v, n) = tile of wave v/32 at
-    // ((v & 31) * 16 + n).
+    // ((v & 31) * OSTR + n); the padded row keeps the substitution's reads of
+    // one row per lane on distinct banks.
     float *outs = reinterpret_cast<float *>(tile);
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) outs[(16 * tau + 4 * grp + r) * 16 + n16] = acc[tau][r];
+        for (int r = 0; r < 4; ++r) outs[(16 * tau + 4 * grp + r) * OSTR + n16] = acc[tau][r];
     __syncthreads();
 
     // Forward substitution per value row.
     if (tid < KD) {
         const int v = tid;
-        const float *cv = reinterpret_cast<const float *>(s_T[v >> 5]) + (v & 31) * 16;  // row v's 16 columns
+        const float *cv = reinterpret_cast<const float *>(s_T[v >> 5]) + (v & 31) * OSTR;  // row v's 16 columns
         float rk[TM], bu[TM];
         const int64_t crow0 = ((int64_t)idx * p.HV + hv) * p.t_max;
 #pragma unroll
