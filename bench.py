@@ -437,6 +437,25 @@ def extra_workloads(torch, dev, timer, pool32, only=None):
         del corr, kgc
         torch.cuda.empty_cache()
 
+    if want("verify_tsweep_b64_h32_fp32"):
+        # read-only batched calls B=64 H=32 fp32 over the token count (2..8 tokens
+        # take the chunked kernel): the state read is the same for every T
+        sweep = []
+        for Tv2 in (2, 6, 8):
+            vt = synth.recurrent_case(7200 + Tv2, n_seqs=Bv, H=32, num_slots=1, device=dev, lengths=[Tv2] * Bv)
+            ot = torch.empty((Bv, Tv2, 32, D), dtype=torch.bfloat16, device=dev)
+            rt = lambda t, n=Tv2: t.reshape(Bv, n, *t.shape[1:])  # noqa: E731
+            calls = [lambda ids=mperm[j * Bv:(j + 1) * Bv].contiguous(), vt=vt, ot=ot, rt=rt: recurrent_kda(
+                rt(vt.q), rt(vt.k), rt(vt.v), rt(vt.g), rt(vt.beta), vt.A_log, vt.dt_bias,
+                initial_state=pool32, state_indices=ids, output=ot, disable_state_update=True)
+                for j in range(8)]
+            t_us = rotating(torch, timer, calls)
+            bts = modes_bytes(Bv, Bv * Tv2, 32, 32, 4, write_state=False)
+            sweep.append({"B": Bv, "T": Tv2, "us": t_us, "GBps": bts / (t_us * 1e-6) / 1e9,
+                          "frac": bts / (t_us * 1e-6) / 1e9 / HBM_PEAK_GBPS})
+            log(f"verify read-only B={Bv} T={Tv2} H=32 fp32: {t_us:.1f} us, {sweep[-1]['GBps']:.0f} GB/s")
+        out["verify_tsweep_b64_h32_fp32"] = sweep
+
     if want("packed_fused_t5_accept1"):
         # packed fused speculative decode, T=5 tokens per sequence, one accepted
         # token; disjoint checkpoint-slot sets per call
