@@ -167,9 +167,11 @@ int choose_vsplit(int64_t items, bool bf16, bool token_loop, bool f32_checkpoint
     // latency: more CUs per head) and from ~320 items on (2.5-7% faster at
     // B>=128: smaller tiles stream better at the same 8 waves per SIMD);
     // 32 rows in between, where vsplit 8 measured 4-8% slower.  bf16 pools:
-    // vsplit 8 only for a handful of items; 64 rows measured 4-6% faster at
-    // 512-1535 items.
-    if (bf16) return items < 64 ? 8 : (items >= 512 && items < 1536 ? 2 : 4);
+    // vsplit 8 only for a handful of items; 64 rows from 240 to 1535 items
+    // (against 32 rows, H=12 and 32: 9-13% faster at 252-256 and 384 items,
+    // 4-6% at 504-768, even at 288, 3.5% slower only at H=32 B=14; 7%
+    // slower at 192 items).
+    if (bf16) return items < 64 ? 8 : (items >= 240 && items < 1536 ? 2 : 4);
     return (items < 112 || items >= 320) ? 8 : 4;
 }
 

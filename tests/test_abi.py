@@ -153,7 +153,8 @@ def err():
 @pytest.mark.parametrize("N,H,bf16,vsplit", [(1, 32, False, 8), (4, 32, False, 4), (8, 32, False, 4),
                                              (12, 32, False, 8), (256, 32, False, 8), (8, 12, False, 8),
                                              (16, 12, False, 4), (512, 12, True, 4), (64, 12, True, 2),
-                                             (42, 12, True, 4), (96, 12, True, 2), (128, 12, True, 4),
+                                             (42, 12, True, 2), (96, 12, True, 2), (128, 12, True, 4),
+                                             (16, 12, True, 4), (20, 12, True, 2),
                                              (1, 12, True, 8), (8, 12, True, 4), (4, 4, False, 8)])
 def test_recurrent_plan_geometry(N, H, bf16, vsplit):
     rc, p = plan_rec(rec_args(N=N, H=H, slots=max(N, 8), bf16=bf16))
