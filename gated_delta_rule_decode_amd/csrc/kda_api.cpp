@@ -172,6 +172,10 @@ int choose_vsplit(int64_t items, bool bf16, bool token_loop, bool f32_checkpoint
     // 4-6% at 504-768, even at 288, 3.5% slower only at H=32 B=14; 7%
     // slower at 192 items).
     if (bf16) return items < 64 ? 8 : (items >= 240 && items < 1536 ? 2 : 4);
+    // fp32 at 224-287 items: 64 rows (H=32 B=8: 7.23 against 7.64 us for 32
+    // rows and 8.11 for 16; H=12 B=20: 7.60 against 7.89), two workgroups
+    // per CU with the whole grid resident.
+    if (items >= 224 && items < 288) return 2;
     return (items < 112 || items >= 320) ? 8 : 4;
 }
 

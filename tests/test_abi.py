@@ -150,7 +150,8 @@ def err():
 
 # ---- launch geometry ---------------------------------------------------------------------
 
-@pytest.mark.parametrize("N,H,bf16,vsplit", [(1, 32, False, 8), (4, 32, False, 4), (8, 32, False, 4),
+@pytest.mark.parametrize("N,H,bf16,vsplit", [(1, 32, False, 8), (4, 32, False, 4), (8, 32, False, 2), (6, 32, False, 4), (9, 32, False, 4),
+                                             (10, 32, False, 8), (20, 12, False, 2), (7, 32, False, 2),
                                              (12, 32, False, 8), (256, 32, False, 8), (8, 12, False, 8),
                                              (16, 12, False, 4), (512, 12, True, 4), (64, 12, True, 2),
                                              (42, 12, True, 2), (96, 12, True, 2), (128, 12, True, 4),
