@@ -481,16 +481,20 @@ struct PfGeometry {
 // ~1000 items, 256 (8 rows per lane) are on par above; 1024 threads are
 // never faster (the per-token work of a head is then bound by its CU's VALU
 // issue, and each extra lane repeats the token's norm reductions).  Split
-// (kernel durations at H=12, T=5): one sequence runs 4 parts of 512 threads
-// in 10.0/10.2 us (fp32/bf16 pool) against 11.9/12.3 unsplit; 8 sequences
-// 2 parts in 12.8/12.6 against 12.8/13.4; from 32 sequences on the CUs are
-// busy and splitting only adds the exchange (+3 to +16 us).
-PfGeometry packed_fused_geometry(int64_t items, bool can_split)
+// (graph replays, H=12 and 24, T=5, N=1..32): bf16 pools are fastest with 4
+// parts below 64 items (N=1: 9.7 against 11.8 us unsplit) and 2 parts below
+// 128 (N=8: 12.3 against 12.8); fp32 pools, whose parts move twice the
+// bytes, with 4 parts below 32 items (N=1: 9.7 against 10.4 with 2 and 11.1
+// unsplit), 2 parts below 80 (N=3..6: 3-7% faster than 4 parts) and none
+// from 96 (N=8: 12.4 against 12.9 with 2 parts).  From 32 sequences on the
+// CUs are busy and splitting only adds the exchange (+3 to +16 us).
+PfGeometry packed_fused_geometry(int64_t items, bool can_split, bool bf16)
 {
     PfGeometry g{1, items < 1024 ? 512 : 256};
     if (can_split) {
-        if (items < 64) g = PfGeometry{4, 512};
-        else if (items < 128) g = PfGeometry{2, 512};
+        const int64_t four = bf16 ? 64 : 32, two = bf16 ? 128 : 80;
+        if (items < four) g = PfGeometry{4, 512};
+        else if (items < two) g = PfGeometry{2, 512};
     }
     if (KDA_FORCE_PF_SPLIT == 1 || (can_split && (KDA_FORCE_PF_SPLIT == 2 || KDA_FORCE_PF_SPLIT == 4)))
         g.vs = KDA_FORCE_PF_SPLIT;
@@ -560,7 +564,7 @@ int prepare_packed_fused(const kda_packed_fused_args *a, PackedFusedParams *p, L
     rc = check_alias(w, 5, r, 11);
     if (rc) return rc;
     const int64_t items = N * a->H;
-    const PfGeometry geo = packed_fused_geometry(items, can_split);
+    const PfGeometry geo = packed_fused_geometry(items, can_split, a->state_dtype == KDA_DTYPE_BF16);
     if (items * geo.vs > 0x7fffffffLL) return fail(KDA_ERR_SHAPE, "too many work items");
     l->family = KERNEL_PACKED_FUSED;
     l->vsplit = geo.vs;

@@ -505,17 +505,25 @@ def with_split(a, rows, N, H):
     return a
 
 
-def test_packed_fused_split_plan():
+@pytest.mark.parametrize("bf16,cases", [
+    (True, ((1, 12, 4, 512), (3, 12, 4, 512), (5, 12, 4, 512), (6, 12, 2, 512), (8, 12, 2, 512),
+            (10, 12, 2, 512), (11, 12, 1, 512), (32, 12, 1, 512), (128, 12, 1, 256), (1, 64, 2, 512),
+            (2, 64, 1, 512))),
+    (False, ((1, 12, 4, 512), (2, 12, 4, 512), (3, 12, 2, 512), (6, 12, 2, 512), (7, 12, 1, 512),
+             (8, 12, 1, 512), (32, 12, 1, 512), (128, 12, 1, 256), (1, 64, 2, 512), (2, 64, 1, 512))),
+])
+def test_packed_fused_split_plan(bf16, cases):
     """With the split workspace, few (sequence, head) pairs spread each head
-    over 4 or 2 workgroups (grid = pairs x split, 128/split value rows each);
-    many pairs, or no workspace, keep one workgroup per pair."""
-    for N, H, vs, block in ((1, 12, 4, 512), (3, 12, 4, 512), (8, 12, 2, 512), (10, 12, 2, 512),
-                            (32, 12, 1, 512), (128, 12, 1, 256), (1, 64, 2, 512), (2, 64, 1, 512)):
+    over 4 or 2 workgroups (grid = pairs x split, 128/split value rows each;
+    bf16 pools split up to more pairs than fp32 ones); many pairs, or no
+    workspace, keep one workgroup per pair."""
+    for N, H, vs, block in cases:
         rows = 5 * N
-        rc, p = plan_pf(with_split(packed_fused_args(rows=rows, N=N, T=5, H=H, slots=2 * N + 2), rows, N, H))
+        args = packed_fused_args(rows=rows, N=N, T=5, H=H, slots=2 * N + 2, bf16=bf16)
+        rc, p = plan_pf(with_split(args, rows, N, H))
         assert rc == 0, err()
         assert (p.vsplit, p.grid_x, p.block, p.rows_per_block, p.items) == (vs, N * H * vs, block, 128 // vs, N * H)
-        rc, p = plan_pf(packed_fused_args(rows=rows, N=N, T=5, H=H, slots=2 * N + 2))
+        rc, p = plan_pf(packed_fused_args(rows=rows, N=N, T=5, H=H, slots=2 * N + 2, bf16=bf16))
         assert rc == 0 and p.vsplit == 1 and p.grid_x == N * H, err()
 
 

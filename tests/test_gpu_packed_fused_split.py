@@ -67,7 +67,8 @@ def within_one_ulp(a_t, b_t):
 @pytest.mark.parametrize("state_dtype", [torch.float32, torch.bfloat16])
 def test_split_matches_oracle_and_unsplit(state_dtype, N):
     """H=12, N sequences of 5 tokens with random accepted counts (the small
-    batches of the speculative benchmark: 4-, 4- and 2-way splits)."""
+    batches of the speculative benchmark: 4-, 4- and 2-way splits with a
+    bf16 pool, 4-, 2-way and unsplit with fp32)."""
     say(f"packed fused split H=12 N={N} T=5 {state_dtype} seed={8600 + N}")
     c = synth.packed_fused_case(8600 + N, lengths=[5] * N, H=12, num_slots=5 * N + 1, max_tokens=5,
                                 state_dtype=state_dtype, device=DEV)
