@@ -151,7 +151,7 @@ u128 pool_bytes(int32_t dtype, int64_t num_slots, int64_t slot_stride, int32_t H
 // while the grid is small.  Measured on MI355X (read-only batched T=4 calls,
 // H=12 and 32, fp32 and bf16 pools): 4 splits below ~96 items, 2 up to ~1024,
 // none above.
-int choose_vsplit(int64_t items, bool bf16, bool token_loop, bool f32_checkpoints)
+int choose_vsplit(int64_t items, bool bf16, bool token_loop, bool f32_checkpoints, bool update)
 {
     if (KDA_FORCE_VSPLIT == 1 || KDA_FORCE_VSPLIT == 2 || KDA_FORCE_VSPLIT == 4 || KDA_FORCE_VSPLIT == 8)
         return KDA_FORCE_VSPLIT;
@@ -161,6 +161,13 @@ int choose_vsplit(int64_t items, bool bf16, bool token_loop, bool f32_checkpoint
     // 59.6 us; 2 splits 58.4, 8 splits 62.5), while bf16 checkpoints (36.6
     // against 40.7 us) and calls without checkpoints keep the rule below.
     if (token_loop && f32_checkpoints) return 4;
+    // Updating token loops over an fp32 pool write back twice the bytes of a
+    // bf16 one and stream them best in 32-row tiles up to ~380 items (batched
+    // T=4, H=32: 7.81 against 8.15 us at 128 items, 10.68 against 10.99 at
+    // 256; 2 splits win from 512); read-only and bf16 calls keep the rule
+    // below (read-only ragged fp32: 9.75 us with 2 splits against 9.99 with 4
+    // at 256 items).
+    if (token_loop && update && !bf16 && items < 384) return 4;
     if (token_loop) return items < 96 ? 4 : (items < 1024 ? 2 : 1);
     // T=1.  fp32 pools (H=12 and 32, B=1..512, graph replays over cold slot
     // sets): 16 value rows per workgroup (vsplit 8) below ~100 items (lower
@@ -285,7 +292,7 @@ int prepare_recurrent(const kda_recurrent_args *a, RecParams *p, Launch *l)
     const bool chunk = KDA_VERIFY_CHUNK && !update && !ragged && tps >= 2 && tps <= VERIFY_CHUNK_MAX_T &&
                        !a->checkpoints;
     const int vsplit = chunk ? 1 : choose_vsplit(items, a->state_dtype == KDA_DTYPE_BF16, token_loop,
-                                                 a->checkpoints != nullptr && a->state_dtype == KDA_DTYPE_F32);
+                                                 a->checkpoints != nullptr && a->state_dtype == KDA_DTYPE_F32, update);
     if (items * vsplit > 0x7ffffff0LL) return fail(KDA_ERR_SHAPE, "too many work items");
     l->family = chunk ? KERNEL_VERIFY_CHUNK : token_loop ? KERNEL_RECURRENT_VARLEN : KERNEL_RECURRENT_T1;
     l->vsplit = vsplit;

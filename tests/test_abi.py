@@ -166,11 +166,19 @@ def test_recurrent_plan_geometry(N, H, bf16, vsplit):
     assert p.kernel == 1
 
 
-@pytest.mark.parametrize("N,H,vsplit", [(2, 32, 4), (2, 47, 4), (2, 48, 2), (8, 12, 2), (31, 32, 2), (32, 32, 1),
-                                        (64, 16, 1), (64, 32, 1)])
-def test_token_loop_plan_geometry(N, H, vsplit):
-    """The token loop splits a head over workgroups only while the grid is small."""
-    rc, p = plan_rec(rec_args(N=N, H=H, T=3 * N, slots=max(N, 8), varlen=True))
+@pytest.mark.parametrize("N,H,bf16,read_only,vsplit", [
+    (2, 32, False, False, 4), (2, 47, False, False, 4), (2, 48, False, False, 4), (8, 12, False, False, 4),
+    (8, 32, False, False, 4), (12, 32, False, False, 2), (31, 32, False, False, 2), (32, 32, False, False, 1),
+    (64, 16, False, False, 1), (64, 32, False, False, 1),
+    (2, 47, False, True, 4), (2, 48, False, True, 2), (8, 32, False, True, 2), (32, 32, False, True, 1),
+    (2, 47, True, False, 4), (2, 48, True, False, 2), (8, 32, True, False, 2), (32, 32, True, False, 1)])
+def test_token_loop_plan_geometry(N, H, bf16, read_only, vsplit):
+    """The token loop splits a head over workgroups only while the grid is
+    small; an updating fp32 pool keeps 4 splits up to more items."""
+    a = rec_args(N=N, H=H, T=3 * N, slots=max(N, 8), bf16=bf16, varlen=True)
+    if read_only:
+        a.flags = _lib.FLAG_NO_STATE_UPDATE
+    rc, p = plan_rec(a)
     assert rc == 0, err()
     assert (p.kernel, p.vsplit, p.rows_per_block) == (2, vsplit, D // vsplit)
     assert p.grid_x == (N * H * vsplit + 7) // 8 * 8
