@@ -144,6 +144,24 @@ def test_batched_form_matches_ragged_bitwise(state_dtype):
     P.check_state(c.state, want["state"])
 
 
+@pytest.mark.parametrize("B", [3, 8, 12])
+@pytest.mark.parametrize("state_dtype", [torch.float32, torch.bfloat16])
+def test_updating_batched_token_loop_geometries(state_dtype, B):
+    """Updating batched calls without checkpoints, H=32, 3 tokens: 96, 256
+    and 384 (sequence, head) items, i.e. 4 value-row splits (fp32 pool up
+    to 383 items), 2 splits (bf16 from 96 items, fp32 at 384), against the
+    oracle, with random slots and null rows."""
+    say(f"updating batched T=3 H=32 B={B} {state_dtype} seed={6400 + B}")
+    T = 3
+    c = synth.recurrent_case(6400 + B, n_seqs=B, H=32, num_slots=B + 4, state_dtype=state_dtype,
+                             device=DEV, indices="random", lengths=[T] * B, null_rows=1)
+    st0 = c.state.clone()
+    o, _ = run(c, form="batched", tps=T)
+    want = ref(c, np_(st0), tps=T)
+    P.check_bf16_out(o, want["out64"])
+    P.check_state(c.state, want["state"])
+
+
 @pytest.mark.parametrize("form", ["t1", "ragged", "batched"])
 def test_read_only_pool(form):
     """disable_state_update: the pool is bit-identical afterwards; outputs and
