@@ -1208,7 +1208,7 @@ __global__ void __launch_bounds__(2048 / (G * VS)) kda_packed_fused_kernel(const
 // (16x16x4 MFMA); the T x T coefficients are reduced once per head and the
 // rest is a forward substitution per value row.  This replaces T passes of
 // vector arithmetic over the whole state.  TM, the token slots the kernel
-// is built for (4 or 8, the smallest that holds T), sizes the input
+// is built for (2, 4 or 8, the smallest that holds T), sizes the input
 // registers and LDS: with TM = 4 an fp32 workgroup fits in 108 VGPRs and
 // 40 KB of LDS, four workgroups per CU instead of three.
 //
@@ -1485,9 +1485,12 @@ int launch_recurrent(const RecParams &p, const Launch &l, void *stream)
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();  // a stale error must not be blamed on this launch
     if (l.family == KERNEL_VERIFY_CHUNK) {
-        // token slots sized to the call: 4 for up to 4 tokens, else 8
+        // token slots sized to the call: 2, 4 or 8, the smallest that holds T
         const dim3 grid(l.grid), block(l.block);
-        if (p.tps <= 4) {
+        if (p.tps <= 2) {
+            if (l.bf16_state) hipLaunchKernelGGL((kda_verify_chunk_kernel<true, 2>), grid, block, 0, s, p);
+            else hipLaunchKernelGGL((kda_verify_chunk_kernel<false, 2>), grid, block, 0, s, p);
+        } else if (p.tps <= 4) {
             if (l.bf16_state) hipLaunchKernelGGL((kda_verify_chunk_kernel<true, 4>), grid, block, 0, s, p);
             else hipLaunchKernelGGL((kda_verify_chunk_kernel<false, 4>), grid, block, 0, s, p);
         } else {
