@@ -1239,7 +1239,18 @@ __global__ void __launch_bounds__(256) kda_verify_chunk_kernel(const RecParams p
     // banks
     __shared__ float s_B[2 * TM][KD + 4];
     constexpr int OSTR = 20;                // floats per row of the MFMA outputs in LDS (16 + 4 padding)
-    __shared__ uint32_t s_T[4][16 * RSW];   // per wave: one state tile (16-byte columns XOR-swizzled by row), then its MFMA outputs
+    // fp32 pools at 8 token slots transpose tile 1 in two halves of K (its
+    // loads issued after the staging): a quarter of the LDS and fewer VGPRs,
+    // so four workgroups fit per CU instead of three
+    constexpr bool HALF = !BF16 && TM == 8;
+    constexpr int LPR = ROW_BYTES / 16;     // lanes per row
+    constexpr int RPA = 64 / LPR;           // rows per access
+    constexpr int HC = LPR / 2;             // 16-byte columns per half row
+    constexpr int HRW = 4 * HC;             // words per half row
+    constexpr int BUFW = HALF ? (16 * HRW > 32 * OSTR ? 16 * HRW : 32 * OSTR) : 16 * RSW;
+    // per wave: one state tile, or half of one, (16-byte columns XOR-swizzled
+    // by row), then the wave's MFMA outputs
+    __shared__ uint32_t s_T[4][BUFW];
     __shared__ float s_v[TM][KD];
     __shared__ float s_part[8][TM * NS];    // [DPP row of the staging waves][token * NS + sum]
     __shared__ float s_sum[TM][NS];
@@ -1297,8 +1308,6 @@ __global__ void __launch_bounds__(256) kda_verify_chunk_kernel(const RecParams p
     // This wave's two 16-row state tiles: tile 0 in the MFMA order (access jj
     // of lane l: 16 bytes of row l & 15 at byte 64*jj + 16*(l >> 4)), tile 1
     // coalesced (access jj covers RPA whole rows, 1 KiB).
-    constexpr int LPR = ROW_BYTES / 16;  // lanes per row
-    constexpr int RPA = 64 / LPR;        // rows per access
     const int n16 = lane & 15;
     const int grp = lane >> 4;
     const int lrow = lane / LPR;
@@ -1307,9 +1316,12 @@ __global__ void __launch_bounds__(256) kda_verify_chunk_kernel(const RecParams p
 #pragma unroll
     for (int jj = 0; jj < NJ; ++jj)
         raw[0][jj] = ld_nt<u32x4>(head, (uint32_t)(32 * wave + n16) * ROW_BYTES + 64u * jj + 16u * grp);
+    auto load_tile1 = [&]() {
 #pragma unroll
-    for (int jj = 0; jj < NJ; ++jj)
-        raw[1][jj] = ld_nt<u32x4>(head, (uint32_t)(32 * wave + 16 + RPA * jj + lrow) * ROW_BYTES + 16u * lcol);
+        for (int jj = 0; jj < NJ; ++jj)
+            raw[1][jj] = ld_nt<u32x4>(head, (uint32_t)(32 * wave + 16 + RPA * jj + lrow) * ROW_BYTES + 16u * lcol);
+    };
+    if constexpr (!HALF) load_tile1();
     __builtin_amdgcn_sched_barrier(0);
 
     if (tid < KD) {
@@ -1365,6 +1377,11 @@ __global__ void __launch_bounds__(256) kda_verify_chunk_kernel(const RecParams p
             s_beta[lane] = precomputed ? b : sigmoid_f(b);
         }
     }
+    if constexpr (HALF) {
+        // tile 1 after the staging, whose registers are free by now
+        __builtin_amdgcn_sched_barrier(0);
+        load_tile1();
+    }
     __syncthreads();
 
     // The per-token sums: one thread per (token, sum) adds the 8 partials.
@@ -1378,30 +1395,76 @@ __global__ void __launch_bounds__(256) kda_verify_chunk_kernel(const RecParams p
 
     // [k_t*E_t ; q_t*E_t] x S0 for this wave's two tiles, tile 1 transposed
     // into the A-operand order through the wave's LDS buffer.
-    float bop[NJ][VPL];
-#pragma unroll
-    for (int jj = 0; jj < NJ; ++jj)
-#pragma unroll
-        for (int e = 0; e < VPL; ++e) bop[jj][e] = n16 < 2 * TM ? s_B[n16 < 2 * TM ? n16 : 0][jj * 4 * VPL + grp * VPL + e] : 0.f;
     uint32_t *tile = s_T[wave];
-    f32x4 acc[2];
+    f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    if constexpr (HALF) {
 #pragma unroll
-    for (int jj = 0; jj < NJ; ++jj)
-        *reinterpret_cast<u32x4 *>(tile + (RPA * jj + lrow) * RSW + 4 * (lcol ^ ((RPA * jj + lrow) & 15))) = raw[1][jj];
+        for (int h = 0; h < 2; ++h) {
+            // Half h of tile 1 (16-byte columns [h*HC, (h+1)*HC) of every row)
+            // into the buffer from the lanes that hold it; other lanes of the
+            // wave read it (and, for h = 1, it overwrites what they read): the
+            // wave barriers keep the compiler from moving LDS accesses across
+            // the exchange, and one wave's LDS accesses complete in order.
+            if (h == 1) __builtin_amdgcn_wave_barrier();
+            if (lcol / HC == h) {
 #pragma unroll
-    for (int tau = 0; tau < 2; ++tau) {
-        acc[tau] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int jj = 0; jj < NJ; ++jj) {
+                    const int row = RPA * jj + lrow;
+                    *reinterpret_cast<u32x4 *>(tile + row * HRW + 4 * ((lcol - h * HC) ^ (row % HC))) = raw[1][jj];
+                }
+            }
+            __builtin_amdgcn_wave_barrier();
+            // the K groups of that half on both tiles, B-operand values read per group
 #pragma unroll
-        for (int jj = 0; jj < NJ; ++jj) {
-            const u32x4 wv = tau == 0 ? raw[0][jj] : *reinterpret_cast<const u32x4 *>(tile + n16 * RSW + 4 * ((4 * jj + grp) ^ n16));
+            for (int jj = h * NJ / 2; jj < (h + 1) * NJ / 2; ++jj) {
+                float b[VPL];
 #pragma unroll
-            for (int e = 0; e < VPL; ++e) {
-                const uint32_t w = wv[BF16 ? e >> 1 : e];
-                const float a = BF16 ? ((e & 1) ? bf16_hi(w) : bf16_lo(w)) : __uint_as_float(w);
-                acc[tau] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bop[jj][e], acc[tau], 0, 0, 0);
+                for (int e = 0; e < VPL; ++e)
+                    b[e] = n16 < 2 * TM ? s_B[n16 < 2 * TM ? n16 : 0][jj * 4 * VPL + grp * VPL + e] : 0.f;
+                const u32x4 w1 =
+                    *reinterpret_cast<const u32x4 *>(tile + n16 * HRW + 4 * ((4 * jj + grp - h * HC) ^ (n16 % HC)));
+#pragma unroll
+                for (int tau = 0; tau < 2; ++tau) {
+                    const u32x4 wv = tau == 0 ? raw[0][jj] : w1;
+#pragma unroll
+                    for (int e = 0; e < VPL; ++e) {
+                        const uint32_t w = wv[BF16 ? e >> 1 : e];
+                        const float a = BF16 ? ((e & 1) ? bf16_hi(w) : bf16_lo(w)) : __uint_as_float(w);
+                        acc[tau] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b[e], acc[tau], 0, 0, 0);
+                    }
+                }
+            }
+        }
+    } else {
+        float bop[NJ][VPL];
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj)
+#pragma unroll
+            for (int e = 0; e < VPL; ++e) bop[jj][e] = n16 < 2 * TM ? s_B[n16 < 2 * TM ? n16 : 0][jj * 4 * VPL + grp * VPL + e] : 0.f;
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj)
+            *reinterpret_cast<u32x4 *>(tile + (RPA * jj + lrow) * RSW + 4 * (lcol ^ ((RPA * jj + lrow) & 15))) = raw[1][jj];
+        // other lanes of the wave read what these wrote: the wave barrier keeps
+        // the compiler from moving LDS accesses across the exchange (one wave's
+        // LDS accesses complete in order)
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int tau = 0; tau < 2; ++tau) {
+            acc[tau] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int jj = 0; jj < NJ; ++jj) {
+                const u32x4 wv = tau == 0 ? raw[0][jj] : *reinterpret_cast<const u32x4 *>(tile + n16 * RSW + 4 * ((4 * jj + grp) ^ n16));
+#pragma unroll
+                for (int e = 0; e < VPL; ++e) {
+                    const uint32_t w = wv[BF16 ? e >> 1 : e];
+                    const float a = BF16 ? ((e & 1) ? bf16_hi(w) : bf16_lo(w)) : __uint_as_float(w);
+                    acc[tau] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bop[jj][e], acc[tau], 0, 0, 0);
+                }
             }
         }
     }
+    // the outputs overwrite the buffer other lanes of the wave read above
+    __builtin_amdgcn_wave_barrier();
     // MFMA outputs (lane l: rows 4*(l>>4) + r of the tile, column l & 15) into
     // the wave's buffer as [row][column]: s_C(v, n) = tile of wave v/32 at
     // ((v & 31) * OSTR + n); the padded row keeps the substitution's reads of
