@@ -103,15 +103,18 @@ def test_recurrent_t1_shapes(N, H, state_dtype):
 
 # ------------------------------------------- config: packed H=12 bf16 serving ----
 
-@pytest.mark.parametrize("row_pad", [0, 64])
-def test_packed_h12_b64_bf16(row_pad):
-    """packed_kda_decode T=1, H=12, B=64, bf16 pool [1024,12,128,128], unique
-    slots in [1,1024), 8 rows -1; plain and padded QKV row stride."""
-    say(f"packed H=12 B=64 bf16 row_pad={row_pad} seed=2064")
-    c = synth.packed_case(2064, B=64, H=12, num_slots=1024, device=DEV, null_rows=8, row_pad=row_pad)
+@pytest.mark.parametrize("B,nulls,row_pad", [(64, 8, 0), (64, 8, 64), (256, 32, 0), (512, 64, 0)])
+def test_packed_h12_bf16(B, nulls, row_pad):
+    """packed_kda_decode T=1, H=12, bf16 pool [1024,12,128,128], unique slots
+    in [1,1024), 1/8 of the rows -1: B=64 with a plain and a padded QKV row
+    stride, and the two batch sizes the benchmark times (B=256 and B=512,
+    the launch geometry of its packed sweep)."""
+    seed = 2000 + B
+    say(f"packed H=12 B={B} bf16 row_pad={row_pad} nulls={nulls} seed={seed}")
+    c = synth.packed_case(seed, B=B, H=12, num_slots=1024, device=DEV, null_rows=nulls, row_pad=row_pad)
     idx = c.state_indices.cpu()
     live = sorted(int(i) for i in idx.tolist() if i >= 0)
-    assert len(live) == 56
+    assert len(live) == B - nulls
     before_live = c.state[torch.tensor(live, device=DEV)].cpu()
     pool_before = c.state.clone()
     sub = {s: j for j, s in enumerate(live)}
@@ -122,7 +125,7 @@ def test_packed_h12_b64_bf16(row_pad):
     out = packed_kda_decode(c.mixed_qkv, c.raw_gate, c.raw_beta, c.A_log, c.dt_bias, c.state,
                             c.state_indices)
     torch.cuda.synchronize()
-    assert tuple(out.shape) == (64, 1, 12, D)
+    assert tuple(out.shape) == (B, 1, 12, D)
     e1 = P.check_bf16_out(out, want["out64"])
     e2 = P.check_state(c.state[live], want["state"])
     assert set(P.changed_slots(pool_before, c.state)) <= set(live)
@@ -130,7 +133,7 @@ def test_packed_h12_b64_bf16(row_pad):
     untouched[live] = False
     ut = torch.nonzero(untouched).flatten().to(DEV)
     assert torch.equal(P.bits(c.state.index_select(0, ut)), P.bits(pool_before.index_select(0, ut)))
-    o = out.reshape(64, -1)
+    o = out.reshape(B, -1)
     assert not P.bits(o[idx.to(DEV) < 0]).any(), "inactive rows must be +0"
     say(f"out err {e1:.3e} state err {e2:.3e}")
 

@@ -4,11 +4,13 @@ Each case plants one mistake in a copy of oracle/kda_oracle.c (on the CPU),
 builds it, routes the oracle wrapper to that build and runs the pins: at
 least one pin must fail.  This shows the pins constrain every part of the
 oracle (orientation, decay, gate, delta rule, readout, conv, norm, null
-rows, rounding), not only its happy path.
+rows, rounding), not only its happy path.  The packed call's q|k|v row split
+lives in the Python wrapper, so its planted mistakes replace the wrapper.
 """
 import os
 import subprocess
 
+import numpy as np
 import pytest
 
 import oracle
@@ -119,6 +121,45 @@ PINS = [
     pf.test_bf16_checkpoints_round_an_unrounded_carry,
     pf.test_padding_null_sequences_and_checkpoint_columns,
 ]
+
+
+PACKED_PINS = [
+    pins.test_packed_row_split_zero_state_closed_form,
+    pins.test_packed_equals_recurrent_on_hand_sliced_rows,
+]
+
+# Planted mistakes of the packed wrapper's row split: which third of the
+# q|k|v row each of q, k and v is read from.
+PACKED_MUTANTS = [
+    ("packed k and v swapped", (0, 2, 1)),
+    ("packed q and k swapped", (1, 0, 2)),
+    ("packed v read from q", (0, 1, 0)),
+]
+
+
+def _packed_with_split(order):
+    def packed(mixed_qkv, raw_gate, raw_beta, A_log, dt_bias, state, state_indices):
+        qkv = oracle.as_np(mixed_qkv)
+        B = qkv.shape[0]
+        H = np.asarray(oracle.as_np(A_log)).shape[0]
+        HC = H * oracle.D
+        q, k, v = (np.ascontiguousarray(qkv[:, j * HC:(j + 1) * HC]).reshape(B, H, oracle.D) for j in order)
+        return oracle.recurrent(q, k, v, oracle.as_np(raw_gate).reshape(B, H, oracle.D),
+                                oracle.as_np(raw_beta).reshape(B, H), A_log, dt_bias, state, state_indices)
+    return packed
+
+
+def test_packed_wrapper_as_written_passes():
+    for pin in PACKED_PINS:
+        pin()
+
+
+@pytest.mark.parametrize("name,order", PACKED_MUTANTS, ids=[m[0] for m in PACKED_MUTANTS])
+def test_planted_packed_split_mistake_is_caught(name, order, monkeypatch):
+    monkeypatch.setattr(oracle, "packed", _packed_with_split(order))
+    for pin in PACKED_PINS:
+        with pytest.raises(AssertionError):
+            pin()
 
 
 @pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])

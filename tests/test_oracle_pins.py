@@ -139,6 +139,68 @@ def test_zero_state_closed_form():
                                        rtol=1e-12, atol=1e-15)
 
 
+def _packed_row_case(seed, B, H):
+    """Random inputs of the packed T=1 call: bf16 q|k|v rows, raw gate and
+    beta logits, gate parameters."""
+    rng = np.random.default_rng(seed)
+    HC = H * D
+    return dict(mixed_qkv=_bf16(rng.standard_normal((B, 3 * HC))),
+                raw_gate=_bf16(rng.standard_normal((B, HC))),
+                raw_beta=_bf16(rng.standard_normal((B, H))),
+                A_log=rng.uniform(-2.0, 0.0, H).astype(np.float32),
+                dt_bias=(rng.standard_normal(HC) * 0.1).astype(np.float32))
+
+
+def test_packed_row_split_zero_state_closed_form():
+    """The packed call's projection row holds q at [0, H*128), k at
+    [H*128, 2*H*128) and v at [2*H*128, 3*H*128), head-major inside each
+    ("Serving-native packed Kimi K3 decode", and the Exact contract of the
+    serving-native packed decode PR).  With a zero state the update is
+    S' = beta k_hat v^T and o = scale beta (q_hat . k_hat) v; both are
+    evaluated here from slices of the row taken by hand, so a q/k/v slice
+    mix-up in the wrapper (k and v swapped, say) fails."""
+    B, H = 3, 2
+    HC = H * D
+    c = _packed_row_case(11, B, H)
+    idx = np.array([2, 0, 3], np.int32)
+    st = np.zeros((4, H, D, D), np.float64)
+    r = oracle.packed(c["mixed_qkv"], c["raw_gate"], c["raw_beta"], c["A_log"], c["dt_bias"], st, idx)
+    x = oracle.bf16_to_f64(c["mixed_qkv"])
+    braw = oracle.bf16_to_f64(c["raw_beta"])
+    for b in range(B):
+        for h in range(H):
+            q = x[b, h * D:(h + 1) * D]
+            k = x[b, HC + h * D:HC + (h + 1) * D]
+            v = x[b, 2 * HC + h * D:2 * HC + (h + 1) * D]
+            beta = 1.0 / (1.0 + math.exp(-braw[b, h]))
+            qh, kh = _unit(q), _unit(k)
+            np.testing.assert_allclose(r["state"][idx[b], h], beta * np.outer(v, kh), rtol=1e-12, atol=1e-15)
+            np.testing.assert_allclose(r["out64"][b, h], SCALE * beta * (qh @ kh) * v, rtol=1e-12, atol=1e-15)
+    assert not r["state"][1].any(), "a slot no row names stays zero"
+
+
+def test_packed_equals_recurrent_on_hand_sliced_rows():
+    """On a random pool with an inactive (-1) row, the packed call equals the
+    recurrent call on q, k, v sliced by hand from the row (and the raw gate
+    and beta reshaped to [B, H, 128] and [B, H]), bit for bit."""
+    B, H = 4, 3
+    HC = H * D
+    c = _packed_row_case(12, B, H)
+    rng = np.random.default_rng(13)
+    st = (rng.standard_normal((6, H, D, D)) * 0.05).astype(np.float32)
+    idx = np.array([5, -1, 0, 2], np.int32)
+    got = oracle.packed(c["mixed_qkv"], c["raw_gate"], c["raw_beta"], c["A_log"], c["dt_bias"], st, idx)
+    qkv = c["mixed_qkv"]
+    want = oracle.recurrent(np.ascontiguousarray(qkv[:, 0:HC]).reshape(B, H, D),
+                            np.ascontiguousarray(qkv[:, HC:2 * HC]).reshape(B, H, D),
+                            np.ascontiguousarray(qkv[:, 2 * HC:3 * HC]).reshape(B, H, D),
+                            c["raw_gate"].reshape(B, H, D), c["raw_beta"], c["A_log"], c["dt_bias"], st, idx)
+    np.testing.assert_array_equal(got["out64"], want["out64"])
+    np.testing.assert_array_equal(got["out_bf16"], want["out_bf16"])
+    np.testing.assert_array_equal(got["state"], want["state"])
+    assert not got["out64"][1].any()
+
+
 def test_decay_is_per_key_channel_along_the_contiguous_dim():
     """beta=0, raw gate 0 and a dt_bias that varies over k: every stored
     element pool[v][k] is scaled by exp(-exp(A_log) * softplus(dt_bias[k]))
