@@ -47,12 +47,28 @@ def _state_dtype(state):
     raise ValueError(f"state dtype must be float32 or bfloat16, got {state.dtype}")
 
 
+# Every tensor argument must live on one HIP device: a host tensor's address
+# handed to a kernel would make the GPU fault instead of raising.
+_DEVICE_TYPE = "cuda"
+
+
+def _check_devices(ref, **named):
+    """ref and every non-None tensor in ``named`` on ref's device, which must
+    be a HIP device.  Returns that device."""
+    dev = ref.device
+    _need(dev.type == _DEVICE_TYPE, f"tensors must be on a HIP ({_DEVICE_TYPE}) device, got {dev}")
+    for name, t in named.items():
+        if t is not None:
+            _need(isinstance(t, torch.Tensor) and t.device == dev, f"{name} must be a tensor on {dev}, "
+                  f"got {t.device if isinstance(t, torch.Tensor) else type(t).__name__}")
+    return dev
+
+
 def _check_pool(state, H):
     _need(state.dim() == 4 and tuple(state.shape[1:]) == (H, D, D),
           f"state must be [num_slots, {H}, 128, 128], got {tuple(state.shape)}")
     _need(state.stride(3) == 1 and state.stride(2) == D and state.stride(1) == D * D,
           "each slot's [H, 128, 128] block must be contiguous")
-    _need(state.is_cuda, "state must be a device tensor")
 
 
 def _check_indices(idx, n):
@@ -128,6 +144,10 @@ def recurrent_kda(q, k, v, g, beta, A_log=None, dt_bias=None, *, initial_state, 
     Returns the bf16 output [.., HV, 128].
     """
     _need(use_qk_l2norm_in_kernel, "only the in-kernel q/k L2 normalisation is implemented")
+    _check_devices(q, k=k, v=v, g=g, beta=beta, A_log=A_log, dt_bias=dt_bias, initial_state=initial_state,
+                   state_indices=state_indices, cu_seqlens=cu_seqlens, output=output,
+                   intermediate_states=intermediate_states, correction_cache=correction_cache,
+                   kg_cache=kg_cache)
     if use_gate_in_kernel is None:
         use_gate_in_kernel = A_log is not None
     H = q.shape[-2]
@@ -141,8 +161,7 @@ def recurrent_kda(q, k, v, g, beta, A_log=None, dt_bias=None, *, initial_state, 
         _need(cu_seqlens.dtype == torch.int32 and cu_seqlens.is_contiguous() and cu_seqlens.numel() == N + 1,
               "cu_seqlens must be a contiguous int32 tensor with N+1 elements")
     for name, t in (("q", q), ("k", k), ("v", v)):
-        _need(t.dtype == torch.bfloat16 and t.is_cuda, f"{name} must be a bf16 device tensor")
-    _need(g.is_cuda and beta.is_cuda, "g and beta must be device tensors")
+        _need(t.dtype == torch.bfloat16, f"{name} must be a bf16 tensor")
     T, tps, sq = _tokens(q, "q", H, D, ragged)
     views = [_tokens(t, n, hh, D, ragged) for n, t, hh in (("k", k, H), ("v", v, HV), ("g", g, HV))]
     views.append(_tokens(beta, "beta", HV, None, ragged))
@@ -176,7 +195,7 @@ def recurrent_kda(q, k, v, g, beta, A_log=None, dt_bias=None, *, initial_state, 
     for name, c, w in (("correction_cache", correction_cache, D), ("kg_cache", kg_cache, 2 * D)):
         if c is None:
             continue
-        _need(c.is_cuda and c.is_contiguous() and c.dim() == 4 and c.shape[0] == state.shape[0]
+        _need(c.is_contiguous() and c.dim() == 4 and c.shape[0] == state.shape[0]
               and c.shape[1] == HV and c.shape[3] == w,
               f"{name} must be contiguous [num_slots, HV, T_max, {w}]")
         _need(t_max is None or c.shape[2] == t_max, "the verify caches must share T_max")
@@ -220,6 +239,8 @@ def packed_kda_decode(mixed_qkv, raw_gate, raw_beta, A_log, dt_bias, state, stat
     dt_bias fp32 [H*128], state [num_slots, H, 128, 128] (bf16 or fp32),
     state_indices int32 [B] (-1 inactive).  Returns bf16 [B, 1, H, 128].
     """
+    _check_devices(mixed_qkv, raw_gate=raw_gate, raw_beta=raw_beta, A_log=A_log, dt_bias=dt_bias, state=state,
+                   state_indices=state_indices, output=output)
     H = A_log.numel()
     B = mixed_qkv.shape[0]
     _check_pool(state, H)
@@ -263,6 +284,8 @@ def _fused_inputs(x, weight, conv_state, raw_gate, raw_beta, A_log, dt_bias, sta
                   norm_weight, norm_eps, output):
     """Checks shared by the fused calls; returns (H, rows, raw_gate, raw_beta,
     output_gate as [rows, width] views, output)."""
+    _check_devices(x, weight=weight, conv_state=conv_state, raw_gate=raw_gate, raw_beta=raw_beta, A_log=A_log,
+                   dt_bias=dt_bias, state=state, output_gate=output_gate, norm_weight=norm_weight, output=output)
     H = A_log.numel()
     HC = H * D
     rows = x.shape[0]
@@ -313,6 +336,7 @@ def fused_kda_decode(x, weight, conv_state, raw_gate, raw_beta, A_log, dt_bias, 
     [num_slots, H, 128, 128] fp32/bf16; output_gate bf16 [rows, H, 128] or
     [1, rows, H, 128]; norm_weight fp32 [128].  Returns bf16 [1, rows, H, 128].
     """
+    _check_devices(x, state_indices=state_indices)
     H, rows, rg, rb, og, output = _fused_inputs(x, weight, conv_state, raw_gate, raw_beta, A_log, dt_bias,
                                                 state, output_gate, norm_weight, norm_eps, output)
     _check_indices(state_indices, rows)
@@ -343,9 +367,11 @@ class PackedFusedWorkspace:
     """Workspace that lets packed_fused_kda_decode spread the work of one
     (sequence, head) over several workgroups when there are few of them:
     int32 arrival counters (zero between calls; the kernel leaves them zero)
-    and fp32 unnormalised outputs.  It grows on demand (never inside graph
-    capture).  Calls that share one must not overlap in time: use one per
-    stream when calls run concurrently."""
+    and fp32 unnormalised outputs.  It grows on demand, by at least doubling,
+    and never frees a buffer it has handed out: a graph captured with an
+    earlier, smaller buffer keeps using that memory when it is replayed.
+    Calls that share one workspace must not overlap in time (use one per
+    stream when calls run concurrently)."""
 
     def __init__(self, device):
         dev = torch.device(device)
@@ -354,28 +380,38 @@ class PackedFusedWorkspace:
         self.device = dev
         self.counters = torch.zeros(0, dtype=torch.int32, device=self.device)
         self.partials = torch.empty(0, dtype=torch.float32, device=self.device)
+        self._retired = []  # buffers replaced by larger ones, kept allocated
 
     def reserve(self, n_seqs, H, n_rows):
         nc, npart = n_seqs * H, max(n_rows, 1) * H * D
-        if self.counters.numel() < nc or self.partials.numel() < npart:
-            _need(not torch.cuda.is_current_stream_capturing(),
-                  "the packed fused workspace must grow, which cannot happen during graph capture: "
-                  "run the call once before capturing it, or pass workspace=None")
-            if self.counters.numel() < nc:
-                self.counters = torch.zeros(nc, dtype=torch.int32, device=self.device)
-            if self.partials.numel() < npart:
-                self.partials = torch.empty(npart, dtype=torch.float32, device=self.device)
+        if self.counters.numel() < nc:
+            self._retired.append(self.counters)
+            self.counters = torch.zeros(max(nc, 2 * self.counters.numel()), dtype=torch.int32, device=self.device)
+        if self.partials.numel() < npart:
+            self._retired.append(self.partials)
+            self.partials = torch.empty(max(npart, 2 * self.partials.numel()), dtype=torch.float32,
+                                        device=self.device)
         return self.counters, self.partials
 
 
+# Default workspaces: one per (device, stream) for eager calls, so that calls
+# on different streams never share arrival counters; a call made while a
+# graph is being captured gets a workspace of its own (allocated in the
+# capture), kept for the life of the process because the graph refers to it.
 _AUTO_WORKSPACE = {}
+_CAPTURED_WORKSPACES = []
 
 
 def _auto_workspace(device):
-    key = torch.device(device).index
+    dev = torch.device(device)
+    if torch.cuda.is_current_stream_capturing():
+        ws = PackedFusedWorkspace(dev)
+        _CAPTURED_WORKSPACES.append(ws)
+        return ws
+    key = (dev.index, torch.cuda.current_stream(dev).cuda_stream)
     ws = _AUTO_WORKSPACE.get(key)
     if ws is None:
-        ws = _AUTO_WORKSPACE[key] = PackedFusedWorkspace(device)
+        ws = _AUTO_WORKSPACE[key] = PackedFusedWorkspace(dev)
     return ws
 
 
@@ -395,19 +431,22 @@ def packed_fused_kda_decode(x, weight, conv_state, raw_gate, raw_beta, A_log, dt
     non-positive start slot makes the sequence null).  Rows of null sequences
     and rows outside every sequence give zeros.  A bf16 pool holds each
     checkpoint rounded; the recurrence itself stays fp32 across the tokens.
-    ``workspace``: "auto" (a per-device PackedFusedWorkspace, shared by
-    every call on that device), a PackedFusedWorkspace, or None (one
-    workgroup per (sequence, head)).  Returns bf16 [1, rows, H, 128].
+    ``workspace``: "auto" (a PackedFusedWorkspace per device and stream for
+    eager calls, and a private one for each call made during graph capture),
+    a PackedFusedWorkspace, or None (one workgroup per (sequence, head)).
+    Returns bf16 [1, rows, H, 128].
     """
+    _check_devices(x, state_indices=state_indices, query_start_loc=query_start_loc,
+                   num_accepted_tokens=num_accepted_tokens)
     H, rows, rg, rb, og, output = _fused_inputs(x, weight, conv_state, raw_gate, raw_beta, A_log, dt_bias,
                                                 state, output_gate, norm_weight, norm_eps, output)
     si = state_indices if state_indices.dim() == 2 else state_indices.reshape(-1, 1)
-    _need(si.dtype == torch.int32 and si.is_cuda and si.dim() == 2 and si.stride(1) == 1,
-          "state_indices must be an int32 device tensor [N, max_tokens] with contiguous columns")
+    _need(si.dtype == torch.int32 and si.dim() == 2 and si.stride(1) == 1,
+          "state_indices must be an int32 tensor [N, max_tokens] with contiguous columns")
     N, max_tokens = si.shape
     for name, t, n in (("query_start_loc", query_start_loc, N + 1), ("num_accepted_tokens", num_accepted_tokens, N)):
-        _need(t.dtype == torch.int32 and t.is_cuda and t.is_contiguous() and t.numel() == n,
-              f"{name} must be a contiguous int32 device tensor with {n} elements")
+        _need(t.dtype == torch.int32 and t.is_contiguous() and t.numel() == n,
+              f"{name} must be a contiguous int32 tensor with {n} elements")
     gm, lb = _gate_mode(lower_bound)
     a = _lib.PackedFusedArgs()
     a.struct_size = ctypes.sizeof(_lib.PackedFusedArgs)

@@ -76,6 +76,18 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
            ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
 
+// Lanes of one wave hand data to each other through LDS: the release fence
+// orders this lane's earlier LDS accesses before the barrier and the acquire
+// fence its later ones after it, in the compiler's memory model (at wavefront
+// scope neither emits an instruction; one wave's LDS accesses complete in
+// order).  A bare wave barrier does not order memory accesses.
+__device__ __forceinline__ void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // s_waitcnt vmcnt(0): every vector memory access of this wave has completed
 // (gfx9 encoding: vmcnt 0, expcnt 7, lgkmcnt 15 are "no wait" for the others).
 __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
@@ -1405,7 +1417,7 @@ __global__ void __launch_bounds__(256) kda_verify_chunk_kernel(const RecParams p
             // wave read it (and, for h = 1, it overwrites what they read): the
             // wave barriers keep the compiler from moving LDS accesses across
             // the exchange, and one wave's LDS accesses complete in order.
-            if (h == 1) __builtin_amdgcn_wave_barrier();
+            if (h == 1) wave_lds_sync();
             if (lcol / HC == h) {
 #pragma unroll
                 for (int jj = 0; jj < NJ; ++jj) {
@@ -1413,7 +1425,7 @@ __global__ void __launch_bounds__(256) kda_verify_chunk_kernel(const RecParams p
                     *reinterpret_cast<u32x4 *>(tile + row * HRW + 4 * ((lcol - h * HC) ^ (row % HC))) = raw[1][jj];
                 }
             }
-            __builtin_amdgcn_wave_barrier();
+            wave_lds_sync();
             // the K groups of that half on both tiles, B-operand values read per group
 #pragma unroll
             for (int jj = h * NJ / 2; jj < (h + 1) * NJ / 2; ++jj) {
@@ -1444,10 +1456,8 @@ __global__ void __launch_bounds__(256) kda_verify_chunk_kernel(const RecParams p
 #pragma unroll
         for (int jj = 0; jj < NJ; ++jj)
             *reinterpret_cast<u32x4 *>(tile + (RPA * jj + lrow) * RSW + 4 * (lcol ^ ((RPA * jj + lrow) & 15))) = raw[1][jj];
-        // other lanes of the wave read what these wrote: the wave barrier keeps
-        // the compiler from moving LDS accesses across the exchange (one wave's
-        // LDS accesses complete in order)
-        __builtin_amdgcn_wave_barrier();
+        // other lanes of the wave read what these wrote
+        wave_lds_sync();
 #pragma unroll
         for (int tau = 0; tau < 2; ++tau) {
             acc[tau] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1464,7 +1474,7 @@ __global__ void __launch_bounds__(256) kda_verify_chunk_kernel(const RecParams p
         }
     }
     // the outputs overwrite the buffer other lanes of the wave read above
-    __builtin_amdgcn_wave_barrier();
+    wave_lds_sync();
     // MFMA outputs (lane l: rows 4*(l>>4) + r of the tile, column l & 15) into
     // the wave's buffer as [row][column]: s_C(v, n) = tile of wave v/32 at
     // ((v & 31) * OSTR + n); the padded row keeps the substitution's reads of

@@ -207,3 +207,50 @@ def test_random_configurations(seed):
     (o_s, s_s, c_s), (o_u, s_u, c_u) = results
     assert torch.equal(s_s, s_u) and torch.equal(c_s, c_u), "split and unsplit caches differ"
     assert within_one_ulp(o_u, o_s)
+
+
+@pytest.mark.parametrize("ws_kind", ["explicit", "auto"])
+def test_captured_call_survives_a_larger_eager_call(ws_kind):
+    """A small split call is captured into a graph; then a larger eager call
+    makes the workspace grow (the explicit workspace is the same object; the
+    default one is per stream, and a captured call gets its own), and other
+    allocations of the freed sizes follow; every replay of the graph still
+    matches the oracle."""
+    say(f"packed fused graph capture then workspace growth ws={ws_kind} H=12 N=2 seed=8950")
+    small = synth.packed_fused_case(8950, lengths=[5, 4], H=12, num_slots=16, max_tokens=5, device=DEV)
+    st0, cs0 = small.state.clone(), small.conv_state.clone()
+    want = ref_call(small, np_(st0).copy(), np_(cs0).copy())
+    ws = PackedFusedWorkspace(DEV) if ws_kind == "explicit" else "auto"
+    out = torch.zeros((1, small.x.shape[0], 12, D), dtype=torch.bfloat16, device=DEV)
+
+    def call():
+        packed_fused_kda_decode(small.x, small.weight, small.conv_state, small.raw_gate, small.raw_beta,
+                                small.A_log, small.dt_bias, small.state_indices, small.state, small.output_gate,
+                                small.norm_weight, output=out, query_start_loc=small.query_start_loc,
+                                num_accepted_tokens=small.num_accepted_tokens, workspace=ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    big = synth.packed_fused_case(8951, lengths=[5] * 8, H=12, num_slots=48, max_tokens=5,
+                                  state_dtype=torch.bfloat16, device=DEV)
+    want_big = ref_call(big, np_(big.state).copy(), np_(big.conv_state).copy())
+    for rep in range(3):
+        if rep == 1:
+            out_big = gpu_call(big, ws)  # 96 pairs of a bf16 pool: a 2-way split with more rows
+            torch.cuda.synchronize()
+            check_vs_oracle(big, out_big, want_big)
+            junk = [torch.full((n,), 7.0, device=DEV) for n in (24, 12 * 10 * D, 96, 40 * 12 * D)]
+        small.state.copy_(st0)
+        small.conv_state.copy_(cs0)
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        check_vs_oracle(small, out, want)
+    del junk

@@ -66,6 +66,7 @@ def chunk_plan_kernel(n, T, H, HV, slots, bf16):
 
 CASES = [  # T, state dtype, gate, gate dtype, H, HV, cache length
     (2, torch.float32, "in_kernel", torch.bfloat16, 4, 4, 2),
+    (2, torch.bfloat16, "in_kernel", torch.bfloat16, 4, 4, 3),
     (3, torch.bfloat16, "in_kernel", torch.bfloat16, 4, 8, 5),
     (4, torch.float32, "precomputed", torch.float32, 2, 8, 3),
     (5, torch.bfloat16, "precomputed", torch.bfloat16, 4, 4, 5),
