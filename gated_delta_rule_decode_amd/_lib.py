@@ -89,6 +89,7 @@ class PackedFusedArgs(ctypes.Structure):
 
 
 EXPORTS = ["kda_recurrent", "kda_packed_decode", "kda_fused_decode", "kda_packed_fused_decode",
+           "kda_packed_fused_decode_noalloc",
            "kda_recurrent_plan", "kda_packed_plan", "kda_fused_plan", "kda_packed_fused_plan",
            "kda_status_string", "kda_last_error", "kda_version", "kda_check_device"]
 
@@ -113,6 +114,7 @@ def load(path: str = LIB_PATH):
                        ("kda_packed_plan", [ctypes.POINTER(PackedArgs), ctypes.POINTER(LaunchPlan)]),
                        ("kda_fused_plan", [ctypes.POINTER(FusedArgs), ctypes.POINTER(LaunchPlan)]),
                        ("kda_packed_fused_decode", [ctypes.POINTER(PackedFusedArgs), _P]),
+                       ("kda_packed_fused_decode_noalloc", [ctypes.POINTER(PackedFusedArgs), _P]),
                        ("kda_packed_fused_plan", [ctypes.POINTER(PackedFusedArgs), ctypes.POINTER(LaunchPlan)]),
                        ("kda_check_device", [ctypes.c_int])):
         fn = getattr(lib, name)

@@ -415,27 +415,11 @@ def _auto_workspace(device):
     return ws
 
 
-def packed_fused_kda_decode(x, weight, conv_state, raw_gate, raw_beta, A_log, dt_bias, state_indices,
-                            state, output_gate, norm_weight, lower_bound=None, norm_eps=1e-5, output=None,
-                            *, query_start_loc, num_accepted_tokens, workspace="auto"):
-    """Packed fused decode with T >= 1 tokens per sequence ("feat(kda): add
-    fused speculative decode kernel").
-
-    The fused step (conv + SiLU, KDA, gated RMSNorm) over packed rows: x
-    [rows, 3*H*128], raw_gate, raw_beta, output_gate per row as in
-    fused_kda_decode.  ``query_start_loc`` int32 [N+1] (non-decreasing): the
-    rows of sequence i; ``state_indices`` int32 [N, max_tokens] (or [N]):
-    column j is the slot that receives the conv window and the state after
-    token j (non-positive: not written); ``num_accepted_tokens`` int32 [N]:
-    sequence i starts from the slot in column num_accepted_tokens[i] - 1 (a
-    non-positive start slot makes the sequence null).  Rows of null sequences
-    and rows outside every sequence give zeros.  A bf16 pool holds each
-    checkpoint rounded; the recurrence itself stays fp32 across the tokens.
-    ``workspace``: "auto" (a PackedFusedWorkspace per device and stream for
-    eager calls, and a private one for each call made during graph capture),
-    a PackedFusedWorkspace, or None (one workgroup per (sequence, head)).
-    Returns bf16 [1, rows, H, 128].
-    """
+def _packed_fused_args(x, weight, conv_state, raw_gate, raw_beta, A_log, dt_bias, state_indices, state,
+                       output_gate, norm_weight, lower_bound, norm_eps, output, query_start_loc,
+                       num_accepted_tokens):
+    """Checked argument struct of the packed fused calls (no split scratch
+    set); returns (args, output, N, H, rows)."""
     _check_devices(x, state_indices=state_indices, query_start_loc=query_start_loc,
                    num_accepted_tokens=num_accepted_tokens)
     H, rows, rg, rb, og, output = _fused_inputs(x, weight, conv_state, raw_gate, raw_beta, A_log, dt_bias,
@@ -465,6 +449,33 @@ def packed_fused_kda_decode(x, weight, conv_state, raw_gate, raw_beta, A_log, dt
     a.output_gate, a.ogate_stride = _ptr(og), og.stride(0)
     a.norm_weight, a.norm_eps = _ptr(norm_weight), float(norm_eps)
     a.out = _ptr(output)
+    return a, output, N, H, rows
+
+
+def packed_fused_kda_decode(x, weight, conv_state, raw_gate, raw_beta, A_log, dt_bias, state_indices,
+                            state, output_gate, norm_weight, lower_bound=None, norm_eps=1e-5, output=None,
+                            *, query_start_loc, num_accepted_tokens, workspace="auto"):
+    """Packed fused decode with T >= 1 tokens per sequence ("feat(kda): add
+    fused speculative decode kernel").
+
+    The fused step (conv + SiLU, KDA, gated RMSNorm) over packed rows: x
+    [rows, 3*H*128], raw_gate, raw_beta, output_gate per row as in
+    fused_kda_decode.  ``query_start_loc`` int32 [N+1] (non-decreasing): the
+    rows of sequence i; ``state_indices`` int32 [N, max_tokens] (or [N]):
+    column j is the slot that receives the conv window and the state after
+    token j (non-positive: not written); ``num_accepted_tokens`` int32 [N]:
+    sequence i starts from the slot in column num_accepted_tokens[i] - 1 (a
+    non-positive start slot makes the sequence null).  Rows of null sequences
+    and rows outside every sequence give zeros.  A bf16 pool holds each
+    checkpoint rounded; the recurrence itself stays fp32 across the tokens.
+    ``workspace``: "auto" (a PackedFusedWorkspace per device and stream for
+    eager calls, and a private one for each call made during graph capture),
+    a PackedFusedWorkspace, or None (one workgroup per (sequence, head)).
+    Returns bf16 [1, rows, H, 128].
+    """
+    a, output, N, H, rows = _packed_fused_args(x, weight, conv_state, raw_gate, raw_beta, A_log, dt_bias,
+                                               state_indices, state, output_gate, norm_weight, lower_bound,
+                                               norm_eps, output, query_start_loc, num_accepted_tokens)
     if isinstance(workspace, str):
         _need(workspace == "auto", 'workspace must be "auto", a PackedFusedWorkspace or None')
         workspace = _auto_workspace(x.device)
@@ -476,4 +487,23 @@ def packed_fused_kda_decode(x, weight, conv_state, raw_gate, raw_beta, A_log, dt
     lib = _lib.load()
     with torch.cuda.device(x.device):
         _lib.check(lib.kda_packed_fused_decode(ctypes.byref(a), _stream(x.device)))
+    return output
+
+
+def packed_fused_kda_decode_noalloc(x, weight, conv_state, raw_gate, raw_beta, A_log, dt_bias, state_indices,
+                                    state, output_gate, norm_weight, lower_bound=None, norm_eps=1e-5, *,
+                                    output, query_start_loc, num_accepted_tokens):
+    """packed_fused_kda_decode for callers that cannot allocate: nothing is
+    allocated, neither here (``output`` is required) nor in the library,
+    whose split heads use a scratch array it holds per device.  Calls on one
+    device must not overlap in time (they share that array).  A call that
+    would split its heads over more than 1024 (sequence, head) pairs or 8192
+    (row, head) pairs is rejected (KDAError, KDA_ERR_SHAPE)."""
+    _need(output is not None, "output is required: this call allocates nothing")
+    a, output, _, _, _ = _packed_fused_args(x, weight, conv_state, raw_gate, raw_beta, A_log, dt_bias,
+                                            state_indices, state, output_gate, norm_weight, lower_bound,
+                                            norm_eps, output, query_start_loc, num_accepted_tokens)
+    lib = _lib.load()
+    with torch.cuda.device(x.device):
+        _lib.check(lib.kda_packed_fused_decode_noalloc(ctypes.byref(a), _stream(x.device)))
     return output

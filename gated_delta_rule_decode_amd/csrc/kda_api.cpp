@@ -713,6 +713,40 @@ KDA_API int kda_packed_fused_decode(const kda_packed_fused_args *args, void *str
     return launched(launch_packed_fused(p, l, stream));
 }
 
+KDA_API int kda_packed_fused_decode_noalloc(const kda_packed_fused_args *args, void *stream)
+{
+    if (!args) return fail(KDA_ERR_NULLPTR, "args is NULL");
+    if (args->struct_size != sizeof(kda_packed_fused_args))
+        return fail(KDA_ERR_ABI, "struct_size %u != %zu", args->struct_size, sizeof(kda_packed_fused_args));
+    if (args->split_counters || args->split_partials)
+        return fail(KDA_ERR_UNSUPPORTED,
+                    "kda_packed_fused_decode_noalloc uses the library's own split scratch: "
+                    "split_counters and split_partials must be NULL");
+    int rc = check_current_device();
+    if (rc) return rc;
+    void *scratch = nullptr;
+    if (noalloc_scratch(&scratch))
+        return fail(KDA_ERR_LAUNCH, "cannot locate the library's scratch array: %s", last_hip_error());
+    kda_packed_fused_args a = *args;
+    a.split_counters = static_cast<int32_t *>(scratch);
+    a.split_partials = reinterpret_cast<float *>(static_cast<char *>(scratch) + NOALLOC_COUNTER_BYTES);
+    PackedFusedParams p;
+    Launch l;
+    rc = prepare_packed_fused(&a, &p, &l);
+    if (rc) return rc;
+    if (l.vsplit > 1) {
+        const int64_t cb = (int64_t)a.n_seqs * a.H * 4;
+        const int64_t pb = (int64_t)a.n_rows * a.H * KD * 4;
+        if (cb > NOALLOC_COUNTER_BYTES || pb > NOALLOC_PARTIAL_BYTES)
+            return fail(KDA_ERR_SHAPE,
+                        "this call splits its heads and needs %lld bytes of counters and %lld of outputs; "
+                        "the allocation-free entry point holds %lld and %lld (n_rows*H <= %lld)",
+                        (long long)cb, (long long)pb, (long long)NOALLOC_COUNTER_BYTES,
+                        (long long)NOALLOC_PARTIAL_BYTES, (long long)(NOALLOC_PARTIAL_BYTES / (KD * 4)));
+    }
+    return launched(launch_packed_fused(p, l, stream));
+}
+
 KDA_API const char *kda_status_string(int status)
 {
     switch (status) {

@@ -98,6 +98,13 @@ struct PackedFusedParams {
     int32_t n_rows, n_seqs, H, max_tokens;
 };
 
+// Scratch of the allocation-free packed fused entry point, one array per
+// device held by the library: arrival counters of split heads (int32), then
+// their unnormalised outputs (fp32).
+constexpr int64_t NOALLOC_COUNTER_BYTES = 4096;          // 1024 (sequence, head) pairs
+constexpr int64_t NOALLOC_PARTIAL_BYTES = 4 << 20;       // 8192 (row, head) pairs of 128 values
+constexpr int64_t NOALLOC_SCRATCH_BYTES = NOALLOC_COUNTER_BYTES + NOALLOC_PARTIAL_BYTES;
+
 struct Launch {
     int32_t family;
     int32_t rows_per_block;  // 16 * G
@@ -111,6 +118,9 @@ struct Launch {
 int launch_recurrent(const RecParams &p, const Launch &l, void *stream);
 int launch_fused(const FusedParams &p, const Launch &l, void *stream);
 int launch_packed_fused(const PackedFusedParams &p, const Launch &l, void *stream);
+// Device address of the current device's copy of the allocation-free
+// scratch array (NOALLOC_SCRATCH_BYTES); 0 or a negative kda_status.
+int noalloc_scratch(void **ptr);
 int current_device_is_gfx950(int *device_out);  // 1 yes, 0 no, <0 HIP error
 int device_is_gfx950(int device);
 const char *last_hip_error();

@@ -1607,6 +1607,34 @@ int launch_packed_fused(const PackedFusedParams &p, const Launch &l, void *strea
     return record(hipGetLastError());
 }
 
+// The allocation-free packed fused entry point's split scratch: arrival
+// counters then unnormalised outputs.  Zero when the code object is loaded;
+// every split call returns each counter it uses to zero before it completes
+// (all parts of a head arrive, or none), so the counters are zero whenever no
+// call is running.  Host code never passes `scratch` itself to a kernel (on
+// the host it names a stand-in, not device memory): it takes the device
+// address of the current device's copy once, below.
+static __device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
+
+int noalloc_scratch(void **ptr)
+{
+    static std::atomic<void *> known[64];
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return record(e);
+    if (dev < 0 || dev >= 64) return record(hipErrorInvalidDevice);
+    void *p = known[dev].load(std::memory_order_acquire);
+    if (!p) {
+        // several host threads may race to fill the entry, all with the same value
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return record(e);
+        if (!p) return record(hipErrorInvalidSymbol);
+        known[dev].store(p, std::memory_order_release);
+    }
+    *ptr = p;
+    return 0;
+}
+
 int device_is_gfx950(int device)
 {
     // 0 unknown, 1 gfx950, 2 other; calls from several host threads may race

@@ -54,7 +54,7 @@ extern "C" {
 #endif
 
 #define KDA_API __attribute__((visibility("default")))
-#define KDA_ABI_VERSION 4
+#define KDA_ABI_VERSION 5
 #define KDA_HEAD_DIM 128
 
 typedef enum kda_status {
@@ -386,6 +386,26 @@ KDA_API int kda_recurrent(const kda_recurrent_args *args, void *stream);
 KDA_API int kda_packed_decode(const kda_packed_args *args, void *stream);
 KDA_API int kda_fused_decode(const kda_fused_args *args, void *stream);
 KDA_API int kda_packed_fused_decode(const kda_packed_fused_args *args, void *stream);
+
+/*
+ * Allocation-free packed fused decode, for callers that cannot allocate
+ * device memory or pass a workspace (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).  Same arguments, results
+ * and launch geometry as kda_packed_fused_decode, except that split_counters
+ * and split_partials must be NULL (else KDA_ERR_UNSUPPORTED): when the call
+ * splits its heads, their counters and unnormalised outputs live in a
+ * scratch array the library holds on each device for the life of the process
+ * (4 KiB of counters and 4 MiB of outputs per device).  A call that would
+ * split and needs more (n_seqs*H > 1024 or n_rows*H > 8192) is rejected with
+ * KDA_ERR_SHAPE before anything is launched; a call that does not split uses
+ * no scratch.  The counters are zero when the library is loaded and every
+ * call leaves them zero.  All calls on one device share that device's array:
+ * calls that overlap in time on one device (two streams, or a graph replayed
+ * beside an eager call) race on it and must not be made.  The call
+ * allocates nothing and synchronises nothing; its first call on a device
+ * looks up the device address of that device's copy of the array.
+ */
+KDA_API int kda_packed_fused_decode_noalloc(const kda_packed_fused_args *args, void *stream);
 
 /* Validate only (no HIP call, no device access) and report the launch
  * geometry the matching entry point would use.  `plan` may be NULL. */

@@ -16,6 +16,7 @@ int current_device_is_gfx950(int *device_out)
     return 0;
 }
 int device_is_gfx950(int) { return 0; }
+int noalloc_scratch(void **) { return -9; }
 const char *last_hip_error() { return "no device (host-only build)"; }
 
 }  // namespace kda_detail

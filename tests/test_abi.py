@@ -30,7 +30,7 @@ def test_header_symbols_exported():
 
 def test_version_and_status_strings():
     L = lib()
-    assert L.kda_version() == 4
+    assert L.kda_version() == 5
     for code in _lib.STATUS:
         assert L.kda_status_string(code).decode()
     assert L.kda_status_string(12345).decode() == "unknown status"
@@ -609,3 +609,18 @@ def test_validation_is_thread_safe_and_errors_are_thread_local():
     for t in threads:
         t.join()
     assert not errors, errors[:5]
+
+
+def test_noalloc_entry_point_refuses_caller_scratch():
+    """The allocation-free packed fused entry point takes its split scratch
+    from the library: caller scratch pointers are refused, and so is a NULL
+    or mis-sized argument struct, all before any HIP call."""
+    L = lib()
+    assert L.kda_packed_fused_decode_noalloc(None, None) == -1
+    a = _lib.PackedFusedArgs()
+    a.struct_size = ctypes.sizeof(_lib.PackedFusedArgs) + 8
+    assert L.kda_packed_fused_decode_noalloc(ctypes.byref(a), None) == -10
+    a.struct_size = ctypes.sizeof(_lib.PackedFusedArgs)
+    a.split_counters = 1 << 32
+    assert L.kda_packed_fused_decode_noalloc(ctypes.byref(a), None) == -7
+    assert b"split_counters" in L.kda_last_error()
