@@ -220,25 +220,6 @@ class Timer:
         return s.elapsed_time(e) / n * 1e3  # us per call
 
 
-def flush_l2(torch, buf):
-    buf.add_(1.0)  # streams 512 MiB through L2 and the MALL
-
-
-def time_cold(torch, fn, n, flush_buf):
-    """Per-call HIP-event time with the caches flushed before every call."""
-    tot = []
-    for _ in range(n):
-        flush_l2(torch, flush_buf)
-        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s.record()
-        fn()
-        e.record()
-        torch.cuda.synchronize()
-        tot.append(s.elapsed_time(e) * 1e3)
-    tot.sort()
-    return tot[len(tot) // 2]
-
-
 # --------------------------------------------------------- other workloads ----
 
 def n_sets(state_bytes_per_call, available, lo=4, cycle=1 << 30):

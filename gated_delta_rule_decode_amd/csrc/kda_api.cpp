@@ -137,14 +137,6 @@ u128 pool_bytes(int32_t dtype, int64_t num_slots, int64_t slot_stride, int32_t H
 // and value row group, eight waves per SIMD) is best or within 3% of best
 // almost everywhere; bf16 pools with 512..1535 items are 4-6% faster at 64
 // rows per workgroup.
-#ifndef KDA_VERIFY_CHUNK
-#define KDA_VERIFY_CHUNK 1  // build-time switch used when measuring
-#endif
-
-#ifndef KDA_FORCE_VSPLIT
-#define KDA_FORCE_VSPLIT 0  // build-time override used when tuning the policy
-#endif
-
 // The token loop (T >= 2 per sequence) is bound by per-token arithmetic and
 // latency rather than by the single pass over the state: splitting a head
 // over workgroups repeats the token staging in every split, so it pays only
@@ -153,8 +145,6 @@ u128 pool_bytes(int32_t dtype, int64_t num_slots, int64_t slot_stride, int32_t H
 // none above.
 int choose_vsplit(int64_t items, bool bf16, bool token_loop, bool f32_checkpoints, bool update)
 {
-    if (KDA_FORCE_VSPLIT == 1 || KDA_FORCE_VSPLIT == 2 || KDA_FORCE_VSPLIT == 4 || KDA_FORCE_VSPLIT == 8)
-        return KDA_FORCE_VSPLIT;
     // A token loop that writes fp32 checkpoints is bound by those writes, and
     // smaller state tiles stream them better: 32 rows measured 3.5% faster
     // than whole heads on the ragged H=16 N=64 workload (57.5 against
@@ -289,7 +279,7 @@ int prepare_recurrent(const kda_recurrent_args *a, RecParams *p, Launch *l)
     const bool token_loop = ragged || tps > 1;
     // Read-only batched calls with a few tokens and no checkpoints: the
     // tokens' reads of the initial state become one matrix product per head.
-    const bool chunk = KDA_VERIFY_CHUNK && !update && !ragged && tps >= 2 && tps <= VERIFY_CHUNK_MAX_T &&
+    const bool chunk = !update && !ragged && tps >= 2 && tps <= VERIFY_CHUNK_MAX_T &&
                        !a->checkpoints;
     const int vsplit = chunk ? 1 : choose_vsplit(items, a->state_dtype == KDA_DTYPE_BF16, token_loop,
                                                  a->checkpoints != nullptr && a->state_dtype == KDA_DTYPE_F32, update);
@@ -471,13 +461,6 @@ int prepare_fused(const kda_fused_args *a, FusedParams *p, Launch *l)
 
 // --------------------------------------------------------- packed fused ----
 
-#ifndef KDA_FORCE_PF_BLOCK
-#define KDA_FORCE_PF_BLOCK 0  // build-time overrides used when tuning the policy
-#endif
-#ifndef KDA_FORCE_PF_SPLIT
-#define KDA_FORCE_PF_SPLIT 0
-#endif
-
 struct PfGeometry {
     int vs, block;
 };
@@ -503,9 +486,6 @@ PfGeometry packed_fused_geometry(int64_t items, bool can_split, bool bf16)
         if (items < four) g = PfGeometry{4, 512};
         else if (items < two) g = PfGeometry{2, 512};
     }
-    if (KDA_FORCE_PF_SPLIT == 1 || (can_split && (KDA_FORCE_PF_SPLIT == 2 || KDA_FORCE_PF_SPLIT == 4)))
-        g.vs = KDA_FORCE_PF_SPLIT;
-    if (KDA_FORCE_PF_BLOCK == 256 || KDA_FORCE_PF_BLOCK == 512) g.block = KDA_FORCE_PF_BLOCK;
     if (g.vs > 1) g.block = 512;  // the split kernels are built for 512 threads
     return g;
 }

@@ -96,10 +96,7 @@ __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F7
 // recurrent loop keeps the next chunk's inputs in registers through the
 // current chunk, and two tokens per chunk keep it at 4 waves per SIMD; the
 // packed fused loop has two barriers per chunk and prefers longer chunks).
-#ifndef KDA_CHUNK
-#define KDA_CHUNK 2  // build-time override used when tuning
-#endif
-constexpr int CHUNK = KDA_CHUNK;
+constexpr int CHUNK = 2;
 constexpr int PF_CHUNK = 8;
 
 // ---------------------------------------------------------- reductions ----
@@ -172,26 +169,18 @@ template <bool BF16> struct StateIO;
 
 // Loads and stores address one head tile from its (workgroup-uniform) base
 // with 32-bit byte offsets, so the 64-bit slot address is formed once.
-// Cache policy of state traffic (1 = nontemporal), measured on MI355X:
+// Cache policy of state traffic, measured on MI355X:
 // pool loads and pool stores (in place, or checkpoints into pool slots)
 // nontemporal — plain ones cost 8-9% at T=1; stores into the contiguous
 // checkpoint buffer of the token loop plain — 13% faster than nontemporal
-// on the ragged H=16 workload.  Build-time switches for measuring.
-#ifndef KDA_LD_NT
-#define KDA_LD_NT 1
-#endif
-#ifndef KDA_ST_NT
-#define KDA_ST_NT 1
-#endif
-#ifndef KDA_CK_NT
-#define KDA_CK_NT 0
-#endif
+// on the ragged H=16 workload.
+constexpr bool ST_NT = true;   // pool stores
+constexpr bool CK_NT = false;  // stores into the contiguous checkpoint buffer
 
 template <typename V>
 __device__ __forceinline__ V ld_nt(const char *base, uint32_t off)
 {
-    if constexpr (KDA_LD_NT) return __builtin_nontemporal_load(reinterpret_cast<const V *>(base + off));
-    else return *reinterpret_cast<const V *>(base + off);
+    return __builtin_nontemporal_load(reinterpret_cast<const V *>(base + off));
 }
 template <typename V, bool NT>
 __device__ __forceinline__ void st_as(char *base, uint32_t off, V v)
@@ -225,7 +214,7 @@ template <> struct StateIO<false> {
         r.b = f32x4{s[4], s[5], s[6], s[7]};
         return r;
     }
-    template <bool NT = KDA_ST_NT>
+    template <bool NT = ST_NT>
     static __device__ __forceinline__ void store(char *head, uint32_t o, const Raw &r)
     {
         st_as<f32x4, NT>(head, o, r.a);
@@ -233,7 +222,7 @@ template <> struct StateIO<false> {
     }
     static __device__ __forceinline__ void store_ckpt(char *head, uint32_t o, const Raw &r)
     {
-        store<KDA_CK_NT>(head, o, r);
+        store<CK_NT>(head, o, r);
     }
 };
 
@@ -262,14 +251,14 @@ template <> struct StateIO<true> {
                     pack_bf16x2(s[4], s[5]), pack_bf16x2(s[6], s[7])};
         return r;
     }
-    template <bool NT = KDA_ST_NT>
+    template <bool NT = ST_NT>
     static __device__ __forceinline__ void store(char *head, uint32_t o, const Raw &r)
     {
         st_as<u32x4, NT>(head, o, r.w);
     }
     static __device__ __forceinline__ void store_ckpt(char *head, uint32_t o, const Raw &r)
     {
-        store<KDA_CK_NT>(head, o, r);
+        store<CK_NT>(head, o, r);
     }
 };
 

@@ -414,13 +414,22 @@ KDA_API int kda_packed_plan(const kda_packed_args *args, kda_launch_plan *plan);
 KDA_API int kda_fused_plan(const kda_fused_args *args, kda_launch_plan *plan);
 KDA_API int kda_packed_fused_plan(const kda_packed_fused_args *args, kda_launch_plan *plan);
 
+/*
+ * Status, error detail, version and device checks.  In the backend="cake"
+ * section of "flashinfer.kda_decode" each call checks its device and its
+ * argument contract before it launches and fails, rather than running some
+ * other implementation, when anything is outside that contract; these calls
+ * report how such a check ended.
+ */
 /* Static text of a status code. */
 KDA_API const char *kda_status_string(int status);
 /* Detail of the last failure on the calling thread ("" if none). */
 KDA_API const char *kda_last_error(void);
 /* KDA_ABI_VERSION of the loaded library. */
 KDA_API int kda_version(void);
-/* KDA_OK if HIP device `device` is a gfx950, else KDA_ERR_DEVICE. */
+/* KDA_OK if HIP device `device` is a gfx950 (the only architecture built),
+ * else KDA_ERR_DEVICE; every entry point makes the same check on the current
+ * device before it launches. */
 KDA_API int kda_check_device(int device);
 
 #ifdef __cplusplus
