@@ -244,7 +244,7 @@ def rotating(torch, timer, calls, reps=8):
     cur.wait_stream(side)
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
+    with torch.cuda.graph(graph, stream=side):  # the warm-up stream: its default workspaces are sized
         for f in calls:
             f()
     graph.replay()

@@ -89,7 +89,7 @@ class PackedFusedArgs(ctypes.Structure):
 
 
 EXPORTS = ["kda_recurrent", "kda_packed_decode", "kda_fused_decode", "kda_packed_fused_decode",
-           "kda_packed_fused_decode_noalloc",
+           "kda_packed_fused_decode_noalloc", "kda_packed_fused_workspace",
            "kda_recurrent_plan", "kda_packed_plan", "kda_fused_plan", "kda_packed_fused_plan",
            "kda_status_string", "kda_last_error", "kda_version", "kda_check_device"]
 
@@ -120,6 +120,9 @@ def load(path: str = LIB_PATH):
         fn = getattr(lib, name)
         fn.argtypes = argt
         fn.restype = ctypes.c_int
+    lib.kda_packed_fused_workspace.argtypes = [ctypes.POINTER(PackedFusedArgs), ctypes.POINTER(_I64),
+                                               ctypes.POINTER(_I64)]
+    lib.kda_packed_fused_workspace.restype = ctypes.c_int
     lib.kda_status_string.argtypes = [ctypes.c_int]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_last_error.argtypes = []

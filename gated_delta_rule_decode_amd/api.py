@@ -394,20 +394,17 @@ class PackedFusedWorkspace:
         return self.counters, self.partials
 
 
-# Default workspaces: one per (device, stream) for eager calls, so that calls
-# on different streams never share arrival counters; a call made while a
-# graph is being captured gets a workspace of its own (allocated in the
-# capture), kept for the life of the process because the graph refers to it.
+# Default workspaces, one per (device, stream), so that calls on different
+# streams never share arrival counters.  A call captured into a graph uses
+# the workspace of its capture stream; if that workspace has to grow during
+# the capture, the new buffers are allocated in the capture (a warm-up call on
+# the capture stream avoids that).  Old buffers are never freed, so a graph
+# keeps valid memory however the workspace grows later.
 _AUTO_WORKSPACE = {}
-_CAPTURED_WORKSPACES = []
 
 
 def _auto_workspace(device):
     dev = torch.device(device)
-    if torch.cuda.is_current_stream_capturing():
-        ws = PackedFusedWorkspace(dev)
-        _CAPTURED_WORKSPACES.append(ws)
-        return ws
     key = (dev.index, torch.cuda.current_stream(dev).cuda_stream)
     ws = _AUTO_WORKSPACE.get(key)
     if ws is None:
@@ -468,9 +465,10 @@ def packed_fused_kda_decode(x, weight, conv_state, raw_gate, raw_beta, A_log, dt
     non-positive start slot makes the sequence null).  Rows of null sequences
     and rows outside every sequence give zeros.  A bf16 pool holds each
     checkpoint rounded; the recurrence itself stays fp32 across the tokens.
-    ``workspace``: "auto" (a PackedFusedWorkspace per device and stream for
-    eager calls, and a private one for each call made during graph capture),
-    a PackedFusedWorkspace, or None (one workgroup per (sequence, head)).
+    ``workspace``: "auto" (a PackedFusedWorkspace per device and stream; a
+    captured call uses its capture stream's), a PackedFusedWorkspace, or
+    None (one workgroup per (sequence, head)); only calls that split their
+    heads take workspace memory.
     Returns bf16 [1, rows, H, 128].
     """
     a, output, N, H, rows = _packed_fused_args(x, weight, conv_state, raw_gate, raw_beta, A_log, dt_bias,
@@ -479,12 +477,16 @@ def packed_fused_kda_decode(x, weight, conv_state, raw_gate, raw_beta, A_log, dt
     if isinstance(workspace, str):
         _need(workspace == "auto", 'workspace must be "auto", a PackedFusedWorkspace or None')
         workspace = _auto_workspace(x.device)
+    lib = _lib.load()
     if workspace is not None:
         _need(isinstance(workspace, PackedFusedWorkspace) and workspace.device == x.device,
               "workspace must be a PackedFusedWorkspace on the device of x")
-        cnt, part = workspace.reserve(N, H, rows)
-        a.split_counters, a.split_partials = _ptr(cnt), _ptr(part)
-    lib = _lib.load()
+        # only a call that would split its heads takes (and may grow) the workspace
+        cb, pb = ctypes.c_int64(), ctypes.c_int64()
+        _lib.check(lib.kda_packed_fused_workspace(ctypes.byref(a), ctypes.byref(cb), ctypes.byref(pb)))
+        if cb.value:
+            cnt, part = workspace.reserve(N, H, rows)
+            a.split_counters, a.split_partials = _ptr(cnt), _ptr(part)
     with torch.cuda.device(x.device):
         _lib.check(lib.kda_packed_fused_decode(ctypes.byref(a), _stream(x.device)))
     return output

@@ -490,7 +490,10 @@ PfGeometry packed_fused_geometry(int64_t items, bool can_split, bool bf16)
     return g;
 }
 
-int prepare_packed_fused(const kda_packed_fused_args *a, PackedFusedParams *p, Launch *l)
+// assume_scratch: plan as if split scratch were given (for sizing it); the
+// call's own split pointers must then be NULL.
+int prepare_packed_fused(const kda_packed_fused_args *a, PackedFusedParams *p, Launch *l,
+                         bool assume_scratch = false)
 {
     if (!a) return fail(KDA_ERR_NULLPTR, "args is NULL");
     if (a->struct_size != sizeof(kda_packed_fused_args))
@@ -523,7 +526,7 @@ int prepare_packed_fused(const kda_packed_fused_args *a, PackedFusedParams *p, L
     if (!aligned16(a->out)) return fail(KDA_ERR_ALIGN, "out must be 16-byte aligned");
     if (!a->split_counters != !a->split_partials)
         return fail(KDA_ERR_NULLPTR, "split_counters and split_partials are given together or not at all");
-    const bool can_split = a->split_counters != nullptr;
+    const bool can_split = a->split_counters != nullptr || assume_scratch;
     if (can_split && (!aligned4(a->split_counters) || !aligned16(a->split_partials)))
         return fail(KDA_ERR_ALIGN, "split_counters must be 4-byte and split_partials 16-byte aligned");
     rc = check_pool(a->state, a->state_dtype, a->num_slots, a->slot_stride, a->H);
@@ -534,8 +537,8 @@ int prepare_packed_fused(const kda_packed_fused_args *a, PackedFusedParams *p, L
                   span(a->state, pool_bytes(a->state_dtype, a->num_slots, a->slot_stride, a->H), "state"),
                   span(a->conv_state, rows_extent(a->num_slots, a->conv_slot_stride, 3 * C3) * 2,
                        "conv_state"),
-                  span(a->split_counters, can_split ? (u128)N * a->H * 4 : 0, "split_counters"),
-                  span(a->split_partials, can_split ? (u128)R * HC * 4 : 0, "split_partials")};
+                  span(a->split_counters, a->split_counters ? (u128)N * a->H * 4 : 0, "split_counters"),
+                  span(a->split_partials, a->split_partials ? (u128)R * HC * 4 : 0, "split_partials")};
     Range r[12] = {span(a->x, rows_extent(R, a->x_stride, C3) * 2, "x"),
                    span(a->weight, (u128)12 * HC * 4, "weight"),
                    span(a->raw_gate, rows_extent(R, a->gate_stride, HC) * 2, "raw_gate"),
@@ -679,6 +682,24 @@ KDA_API int kda_packed_fused_plan(const kda_packed_fused_args *args, kda_launch_
     int rc = prepare_packed_fused(args, &p, &l);
     if (rc) return rc;
     fill_plan(plan, l, (int64_t)args->n_seqs * args->H);
+    return KDA_OK;
+}
+
+KDA_API int kda_packed_fused_workspace(const kda_packed_fused_args *args, int64_t *counter_bytes,
+                                      int64_t *partial_bytes)
+{
+    if (!counter_bytes || !partial_bytes) return fail(KDA_ERR_NULLPTR, "counter_bytes / partial_bytes is NULL");
+    *counter_bytes = *partial_bytes = 0;
+    if (args && (args->split_counters || args->split_partials))
+        return fail(KDA_ERR_UNSUPPORTED, "split_counters and split_partials must be NULL when sizing them");
+    PackedFusedParams p;
+    Launch l;
+    int rc = prepare_packed_fused(args, &p, &l, true);
+    if (rc) return rc;
+    if (l.vsplit > 1) {
+        *counter_bytes = (int64_t)args->n_seqs * args->H * 4;
+        *partial_bytes = (int64_t)args->n_rows * args->H * KD * 4;
+    }
     return KDA_OK;
 }
 

@@ -54,7 +54,7 @@ extern "C" {
 #endif
 
 #define KDA_API __attribute__((visibility("default")))
-#define KDA_ABI_VERSION 5
+#define KDA_ABI_VERSION 6
 #define KDA_HEAD_DIM 128
 
 typedef enum kda_status {
@@ -386,6 +386,18 @@ KDA_API int kda_recurrent(const kda_recurrent_args *args, void *stream);
 KDA_API int kda_packed_decode(const kda_packed_args *args, void *stream);
 KDA_API int kda_fused_decode(const kda_fused_args *args, void *stream);
 KDA_API int kda_packed_fused_decode(const kda_packed_fused_args *args, void *stream);
+
+/*
+ * Workspace a packed fused call would use (host only: no HIP call, no
+ * device access).  With split_counters and split_partials NULL in `args`
+ * (else KDA_ERR_UNSUPPORTED), validates the call as kda_packed_fused_decode
+ * does and reports the bytes of split counters and of split outputs it
+ * would use if given a workspace: both 0 when it would keep one workgroup
+ * per (sequence, head) anyway, so a caller need not pass (or allocate) a
+ * workspace for it.  On error both are 0.
+ */
+KDA_API int kda_packed_fused_workspace(const kda_packed_fused_args *args, int64_t *counter_bytes,
+                                       int64_t *partial_bytes);
 
 /*
  * Allocation-free packed fused decode, for callers that cannot allocate

@@ -30,7 +30,7 @@ def test_header_symbols_exported():
 
 def test_version_and_status_strings():
     L = lib()
-    assert L.kda_version() == 5
+    assert L.kda_version() == 6
     for code in _lib.STATUS:
         assert L.kda_status_string(code).decode()
     assert L.kda_status_string(12345).decode() == "unknown status"
@@ -624,3 +624,31 @@ def test_noalloc_entry_point_refuses_caller_scratch():
     a.split_counters = 1 << 32
     assert L.kda_packed_fused_decode_noalloc(ctypes.byref(a), None) == -7
     assert b"split_counters" in L.kda_last_error()
+
+
+def test_packed_fused_workspace_sizes():
+    """kda_packed_fused_workspace reports the split scratch a call would use:
+    N*H*4 bytes of counters and rows*H*128*4 of outputs when the plan with a
+    workspace splits its heads, nothing when it would not (many pairs), and
+    an error (sizes 0) for invalid arguments or caller scratch pointers."""
+    L = lib()
+
+    def sizes(a):
+        cb, pb = ctypes.c_int64(-1), ctypes.c_int64(-1)
+        rc = L.kda_packed_fused_workspace(ctypes.byref(a), ctypes.byref(cb), ctypes.byref(pb))
+        return rc, cb.value, pb.value
+
+    for N, H, bf16 in ((1, 12, False), (3, 12, True), (8, 12, True), (128, 12, False), (2, 64, False)):
+        a = packed_fused_args(rows=5 * N, N=N, T=5, H=H, slots=2 * N + 2, bf16=bf16)
+        rc, cb, pb = sizes(a)
+        assert rc == 0, err()
+        vs = plan_pf(with_split(packed_fused_args(rows=5 * N, N=N, T=5, H=H, slots=2 * N + 2, bf16=bf16),
+                                5 * N, N, H))[1].vsplit
+        if vs > 1:
+            assert (cb, pb) == (N * H * 4, 5 * N * H * D * 4), (N, H, bf16)
+        else:
+            assert (cb, pb) == (0, 0), (N, H, bf16)
+    a = packed_fused_args(N=0)
+    assert sizes(a) == (-2, 0, 0)
+    a = with_split(packed_fused_args(N=1, rows=5), 5, 1, 12)
+    assert sizes(a)[0] == -7 and b"must be NULL" in L.kda_last_error()

@@ -213,9 +213,9 @@ def test_random_configurations(seed):
 def test_captured_call_survives_a_larger_eager_call(ws_kind):
     """A small split call is captured into a graph; then a larger eager call
     makes the workspace grow (the explicit workspace is the same object; the
-    default one is per stream, and a captured call gets its own), and other
-    allocations of the freed sizes follow; every replay of the graph still
-    matches the oracle."""
+    default one is the capture stream's, grown here by an eager call on that
+    stream), and other allocations of the freed sizes follow; every replay of
+    the graph still matches the oracle."""
     say(f"packed fused graph capture then workspace growth ws={ws_kind} H=12 N=2 seed=8950")
     small = synth.packed_fused_case(8950, lengths=[5, 4], H=12, num_slots=16, max_tokens=5, device=DEV)
     st0, cs0 = small.state.clone(), small.conv_state.clone()
@@ -236,14 +236,17 @@ def test_captured_call_survives_a_larger_eager_call(ws_kind):
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
+    cap = torch.cuda.Stream()
+    with torch.cuda.graph(g, stream=cap):
         call()
     big = synth.packed_fused_case(8951, lengths=[5] * 8, H=12, num_slots=48, max_tokens=5,
                                   state_dtype=torch.bfloat16, device=DEV)
     want_big = ref_call(big, np_(big.state).copy(), np_(big.conv_state).copy())
     for rep in range(3):
         if rep == 1:
-            out_big = gpu_call(big, ws)  # 96 pairs of a bf16 pool: a 2-way split with more rows
+            cap.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(cap):  # the capture stream's default workspace grows
+                out_big = gpu_call(big, ws)  # 96 pairs of a bf16 pool: a 2-way split with more rows
             torch.cuda.synchronize()
             check_vs_oracle(big, out_big, want_big)
             junk = [torch.full((n,), 7.0, device=DEV) for n in (24, 12 * 10 * D, 96, 40 * 12 * D)]
