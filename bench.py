@@ -419,10 +419,10 @@ def extra_workloads(torch, dev, timer, pool32, only=None):
         torch.cuda.empty_cache()
 
     if want("verify_tsweep_b64_h32_fp32"):
-        # read-only batched calls B=64 H=32 fp32 over the token count (2..8 tokens
-        # take the chunked kernel): the state read is the same for every T
+        # read-only batched calls B=64 H=32 fp32 over the token count (the WY
+        # verify kernel takes 2..16 tokens): the state read is the same for every T
         sweep = []
-        for Tv2 in (2, 6, 8):
+        for Tv2 in (2, 6, 8, 12, 16):
             vt = synth.recurrent_case(7200 + Tv2, n_seqs=Bv, H=32, num_slots=1, device=dev, lengths=[Tv2] * Bv)
             ot = torch.empty((Bv, Tv2, 32, D), dtype=torch.bfloat16, device=dev)
             rt = lambda t, n=Tv2: t.reshape(Bv, n, *t.shape[1:])  # noqa: E731
@@ -436,6 +436,72 @@ def extra_workloads(torch, dev, timer, pool32, only=None):
                           "frac": bts / (t_us * 1e-6) / 1e9 / HBM_PEAK_GBPS})
             log(f"verify read-only B={Bv} T={Tv2} H=32 fp32: {t_us:.1f} us, {sweep[-1]['GBps']:.0f} GB/s")
         out["verify_tsweep_b64_h32_fp32"] = sweep
+
+    if want("verify_ragged_b64_h32_fp32"):
+        # read-only ragged calls (cu_seqlens), B=64 H=32 fp32, lengths U{1..8},
+        # the longest declared (8): the WY verify kernel
+        lengths = synth.ragged_lengths(7300, Bv, 1, 8)
+        rc_ = synth.recurrent_case(7300, n_seqs=Bv, H=32, num_slots=1, device=dev, lengths=lengths)
+        Tr = sum(lengths)
+        orr = torch.empty((1, Tr, 32, D), dtype=torch.bfloat16, device=dev)
+        r1 = lambda t: t.reshape(1, Tr, *t.shape[1:])  # noqa: E731
+        calls = [lambda ids=mperm[j * Bv:(j + 1) * Bv].contiguous(): recurrent_kda(
+            r1(rc_.q), r1(rc_.k), r1(rc_.v), r1(rc_.g), r1(rc_.beta), rc_.A_log, rc_.dt_bias,
+            initial_state=pool32, state_indices=ids, cu_seqlens=rc_.cu_seqlens, output=orr,
+            disable_state_update=True, max_seqlen=max(lengths)) for j in range(8)]
+        modes_entry("verify_ragged_b64_h32_fp32", calls, modes_bytes(Bv, Tr, 32, 32, 4, write_state=False), Bv)
+
+    if want("eager_host"):
+        # host cost per call: eager facade calls and prepared calls launched
+        # back to back (wall clock per call: the larger of the host's and the
+        # GPU's time per call) next to graph replays of the same calls
+        import time
+        from gated_delta_rule_decode_amd import prepare
+
+        def wall(fns, m=3000):
+            for f in fns:
+                f()
+            torch.cuda.synchronize()
+            t = time.perf_counter()
+            for i in range(m):
+                fns[i % len(fns)]()
+            torch.cuda.synchronize()
+            return (time.perf_counter() - t) / m * 1e6
+
+        rows = []
+        pk = synth.packed_case(2100, B=256, H=12, num_slots=4096, device=dev)
+        rk = synth.recurrent_case(1100, n_seqs=256, H=H, num_slots=1, device=dev)
+        g3 = torch.Generator(device=dev)
+        g3.manual_seed(11)
+        pperm2 = torch.randperm(4095, generator=g3, device=dev).to(torch.int32) + 1
+        for Bs in (1, 8, 256):
+            o = torch.empty((Bs, 1, 12, D), dtype=torch.bfloat16, device=dev)
+            pargs = [(pk.mixed_qkv[:Bs], pk.raw_gate[:Bs], pk.raw_beta[:Bs], pk.A_log, pk.dt_bias, pk.state,
+                      pperm2[j * Bs:(j + 1) * Bs].contiguous())
+                     for j in range(n_sets(Bs * 12 * D * D * 2, 4095 // Bs, lo=8))]
+            eager = [lambda a=a: packed_kda_decode(*a, output=o) for a in pargs]
+            prep = [prepare(packed_kda_decode, *a, output=o) for a in pargs]
+            row = {"call": "packed_kda_decode H=12 bf16", "B": Bs, "graph_us": rotating(torch, timer, eager),
+                   "eager_us": wall(eager), "prepared_us": wall(prep)}
+            rows.append(row)
+            log(f"eager/prepared/graph packed H=12 B={Bs}: {row['eager_us']:.1f} / {row['prepared_us']:.1f} / "
+                f"{row['graph_us']:.1f} us per call")
+            o2 = torch.empty((Bs, 1, H, D), dtype=torch.bfloat16, device=dev)
+            r4 = lambda t, n=Bs: t[:n].reshape(n, 1, *t.shape[1:])  # noqa: E731
+            rargs = [((r4(rk.q), r4(rk.k), r4(rk.v), r4(rk.g), r4(rk.beta), rk.A_log, rk.dt_bias),
+                      mperm[j * Bs:(j + 1) * Bs].contiguous())
+                     for j in range(n_sets(Bs * H * D * D * 4, SLOTS // Bs, lo=8))]
+            eager = [lambda a=a, ids=ids: recurrent_kda(*a, initial_state=pool32, state_indices=ids, output=o2)
+                     for a, ids in rargs]
+            prep = [prepare(recurrent_kda, *a, initial_state=pool32, state_indices=ids, output=o2) for a, ids in rargs]
+            row = {"call": "recurrent_kda T=1 H=32 fp32", "B": Bs, "graph_us": rotating(torch, timer, eager),
+                   "eager_us": wall(eager), "prepared_us": wall(prep)}
+            rows.append(row)
+            log(f"eager/prepared/graph recurrent H=32 B={Bs}: {row['eager_us']:.1f} / {row['prepared_us']:.1f} / "
+                f"{row['graph_us']:.1f} us per call")
+        out["eager_host"] = rows
+        del pk, rk
+        torch.cuda.empty_cache()
 
     if want("packed_fused_t5_accept1"):
         # packed fused speculative decode, T=5 tokens per sequence, one accepted

@@ -17,6 +17,7 @@ from __future__ import annotations
 
 import ctypes
 import math
+import threading
 
 import torch
 
@@ -30,8 +31,72 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else None
 
 
-def _stream(dev):
-    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+def _launch(fn, ref, dev, stream=None):
+    """Call the library entry point `fn` with the argument struct `ref` on
+    `stream` (default: the device's current stream), with `dev` current."""
+    h = (torch.cuda.current_stream(dev) if stream is None else stream).cuda_stream
+    if torch.cuda.current_device() == dev.index:
+        rc = fn(ref, h)
+    else:
+        with torch.cuda.device(dev):
+            rc = fn(ref, h)
+    if rc:
+        _lib.check(rc)
+
+
+class PreparedCall:
+    """One validated library call bound to its tensors (see ``prepare``).
+
+    Calling it enqueues the same kernel with the same arguments again, on
+    the device's current stream or the given one; the kernel reads the
+    tensors' contents at that time.  It holds references to every tensor the
+    call uses, which must stay where they are (no reallocation, no resize).
+    Returns the call's output tensor."""
+
+    __slots__ = ("_fn", "_args", "_ref", "_keep", "device", "output")
+
+    def __init__(self, fn, args, device, output, keep):
+        self._fn = fn
+        self._args = args
+        self._ref = ctypes.byref(args)
+        self._keep = keep
+        self.device = device
+        self.output = output
+
+    def __call__(self, stream=None):
+        _launch(self._fn, self._ref, self.device, stream)
+        return self.output
+
+
+_PREPARING = threading.local()
+
+
+def prepare(fn, *args, **kwargs):
+    """Validate one call of ``fn`` (recurrent_kda, packed_kda_decode,
+    fused_kda_decode, packed_fused_kda_decode or
+    packed_fused_kda_decode_noalloc) with these arguments, without launching
+    it, and return a PreparedCall that launches it.  The argument checks and
+    the marshalling into the library's struct happen once here; each launch
+    is then one library call (for eager serving loops whose buffers stay in
+    place).  An output the call would allocate is allocated here, once."""
+    _PREPARING.on = True
+    try:
+        call = fn(*args, **kwargs)
+    finally:
+        _PREPARING.on = False
+    _need(isinstance(call, PreparedCall), f"{getattr(fn, '__name__', fn)} cannot be prepared")
+    call._keep = (args, kwargs, call._keep)
+    return call
+
+
+def _run(name, a, dev, output, keep=()):
+    """Launch entry point `name` with struct `a`, or, inside ``prepare``,
+    return the PreparedCall that would."""
+    fn = getattr(_lib.load(), name)
+    if getattr(_PREPARING, "on", False):
+        return PreparedCall(fn, a, dev, output, keep)
+    _launch(fn, ctypes.byref(a), dev)
+    return output
 
 
 def _need(cond, msg):
@@ -121,7 +186,8 @@ def _tokens(t, name, heads, width, ragged):
 def recurrent_kda(q, k, v, g, beta, A_log=None, dt_bias=None, *, initial_state, state_indices,
                   cu_seqlens=None, n_tokens=None, scale=None, output=None, intermediate_states=None,
                   lower_bound=None, use_qk_l2norm_in_kernel=True, use_gate_in_kernel=None,
-                  disable_state_update=False, l2_eps=1e-6, correction_cache=None, kg_cache=None):
+                  disable_state_update=False, l2_eps=1e-6, correction_cache=None, kg_cache=None,
+                  max_seqlen=None):
     """Recurrent KDA decode ("flashinfer.kda_decode" function table).
 
     Forms: T=1 (q [B, 1, H, 128] or [B, H, 128]); batched T tokens per
@@ -141,6 +207,10 @@ def recurrent_kda(q, k, v, g, beta, A_log=None, dt_bias=None, *, initial_state, 
     [num_slots, HV, T_max, 128] receives beta*u of token j of the sequence
     in that slot, ``kg_cache`` [num_slots, HV, T_max, 256] (fp32 or bf16) its
     raw key | raw gate; tokens j >= T_max and null rows record nothing.
+    ``max_seqlen`` (ragged form only): the caller's bound on every sequence's
+    length; a read-only call without intermediate states that declares at
+    most 16 runs as one matrix product per head, and there the tokens of a
+    longer sequence past the bound give zeros and record nothing.
     Returns the bf16 output [.., HV, 128].
     """
     _need(use_qk_l2norm_in_kernel, "only the in-kernel q/k L2 normalisation is implemented")
@@ -169,6 +239,11 @@ def recurrent_kda(q, k, v, g, beta, A_log=None, dt_bias=None, *, initial_state, 
         _need(Tn == T and tpn == tps, f"{n} does not have the token layout of q")
     if ragged and n_tokens is not None:
         T = int(n_tokens)
+    if ragged:
+        _need(max_seqlen is None or int(max_seqlen) >= 0, "max_seqlen must be non-negative")
+        tps = 0 if max_seqlen is None else int(max_seqlen)
+    else:
+        _need(max_seqlen is None, "max_seqlen applies to the ragged (cu_seqlens) form only")
     if use_gate_in_kernel:
         _need(A_log is not None and dt_bias is not None, "the in-kernel gate needs A_log and dt_bias")
         _need(g.dtype == torch.bfloat16 and beta.dtype == torch.bfloat16,
@@ -224,10 +299,7 @@ def recurrent_kda(q, k, v, g, beta, A_log=None, dt_bias=None, *, initial_state, 
     a.correction_cache, a.kg_cache = _ptr(correction_cache), _ptr(kg_cache)
     a.kg_dtype = _dtype_code(kg_cache, "kg_cache") if kg_cache is not None else _lib.DTYPE_F32
     a.cache_t_max = t_max or 0
-    lib = _lib.load()
-    with torch.cuda.device(q.device):
-        _lib.check(lib.kda_recurrent(ctypes.byref(a), _stream(q.device)))
-    return output
+    return _run("kda_recurrent", a, q.device, output)
 
 
 def packed_kda_decode(mixed_qkv, raw_gate, raw_beta, A_log, dt_bias, state, state_indices,
@@ -274,10 +346,7 @@ def packed_kda_decode(mixed_qkv, raw_gate, raw_beta, A_log, dt_bias, state, stat
     a.num_slots, a.slot_stride = state.shape[0], state.stride(0)
     a.state_indices = _ptr(state_indices)
     a.out = _ptr(output)
-    lib = _lib.load()
-    with torch.cuda.device(mixed_qkv.device):
-        _lib.check(lib.kda_packed_decode(ctypes.byref(a), _stream(mixed_qkv.device)))
-    return output
+    return _run("kda_packed_decode", a, mixed_qkv.device, output)
 
 
 def _fused_inputs(x, weight, conv_state, raw_gate, raw_beta, A_log, dt_bias, state, output_gate,
@@ -357,10 +426,7 @@ def fused_kda_decode(x, weight, conv_state, raw_gate, raw_beta, A_log, dt_bias, 
     a.output_gate, a.ogate_stride = _ptr(og), og.stride(0)
     a.norm_weight, a.norm_eps = _ptr(norm_weight), float(norm_eps)
     a.out = _ptr(output)
-    lib = _lib.load()
-    with torch.cuda.device(x.device):
-        _lib.check(lib.kda_fused_decode(ctypes.byref(a), _stream(x.device)))
-    return output
+    return _run("kda_fused_decode", a, x.device, output)
 
 
 class PackedFusedWorkspace:
@@ -487,9 +553,7 @@ def packed_fused_kda_decode(x, weight, conv_state, raw_gate, raw_beta, A_log, dt
         if cb.value:
             cnt, part = workspace.reserve(N, H, rows)
             a.split_counters, a.split_partials = _ptr(cnt), _ptr(part)
-    with torch.cuda.device(x.device):
-        _lib.check(lib.kda_packed_fused_decode(ctypes.byref(a), _stream(x.device)))
-    return output
+    return _run("kda_packed_fused_decode", a, x.device, output, keep=(workspace,))
 
 
 def packed_fused_kda_decode_noalloc(x, weight, conv_state, raw_gate, raw_beta, A_log, dt_bias, state_indices,
@@ -505,7 +569,4 @@ def packed_fused_kda_decode_noalloc(x, weight, conv_state, raw_gate, raw_beta, A
     a, output, _, _, _ = _packed_fused_args(x, weight, conv_state, raw_gate, raw_beta, A_log, dt_bias,
                                             state_indices, state, output_gate, norm_weight, lower_bound,
                                             norm_eps, output, query_start_loc, num_accepted_tokens)
-    lib = _lib.load()
-    with torch.cuda.device(x.device):
-        _lib.check(lib.kda_packed_fused_decode_noalloc(ctypes.byref(a), _stream(x.device)))
-    return output
+    return _run("kda_packed_fused_decode_noalloc", a, x.device, output)

@@ -12,10 +12,12 @@ enum KernelFamily : int32_t {
     KERNEL_RECURRENT_VARLEN = 2,  // ragged token loop with the state held in registers
     KERNEL_FUSED = 3,          // conv + SiLU -> KDA -> gated RMSNorm
     KERNEL_PACKED_FUSED = 4,   // the fused step over packed ragged rows, T >= 1 per sequence
-    KERNEL_VERIFY_CHUNK = 5,   // read-only batched calls, 2..VERIFY_CHUNK_MAX_T tokens: one MFMA product per head
+    KERNEL_VERIFY_WY = 5,      // read-only calls, <= VERIFY_WY_MAX_T tokens per sequence: one MFMA product per head
+    KERNEL_VERIFY_CHUNK = 6,   // read-only batched calls, 2..VERIFY_CHUNK_MAX_T tokens: the same, smaller tiles
 };
 
-constexpr int VERIFY_CHUNK_MAX_T = 8;  // tokens per sequence the chunked verify kernel takes
+constexpr int VERIFY_WY_MAX_T = 16;   // tokens per sequence the WY verify kernel takes
+constexpr int VERIFY_CHUNK_MAX_T = 4;  // batched calls up to this many tokens take the chunked verify kernel
 
 // Recurrence over (sequence, value head, value slice) work items; serves
 // recurrent_kda (T=1, uniform batches, ragged T>=0, grouped value heads,
@@ -35,7 +37,8 @@ struct RecParams {
     uint16_t *out;               // bf16 [n_tokens][HV][128]
     int32_t n_seqs, n_tokens, H, HV;
     int32_t group;               // HV / H: value heads per q/k head
-    int32_t tps;                 // tokens per sequence without cu_seqlens (>= 1)
+    int32_t tps;                 // tokens per sequence without cu_seqlens (>= 1); with cu_seqlens
+                                 // in the WY verify kernel, the declared longest sequence
     int32_t g_f32, beta_f32;     // input dtypes of g and beta
     int32_t precomputed;         // 1: g is the log-decay and beta is beta itself
     int32_t update_state;        // 0: the pool is read only

@@ -31,11 +31,13 @@
 //    sequence's tokens and, when few heads are live, splits a head over
 //    2-4 workgroups that exchange unnormalised outputs through caller
 //    scratch (the last to arrive normalises).
-//  * Read-only batched calls with a few tokens (speculative verify) are the
+//  * Read-only calls with up to 16 tokens (speculative verify) are the
 //    exception: every token's product with the state is a product with the
 //    same initial state, so they run as one small matrix product per head on
-//    the fp32 matrix cores (kda_verify_chunk_kernel) plus a forward
-//    substitution per value row.
+//    the matrix cores plus a forward substitution per value row
+//    (kda_verify_chunk_kernel for batched calls of up to 4 tokens,
+//    kda_verify_wy_kernel for longer and ragged ones; half of each wave's
+//    state rows go straight into registers, half through LDS).
 //  * The slot base is one 64-bit pointer per workgroup; everything inside a
 //    head is 32-bit offsets.
 //  * Null rows (index below the call's first live index, or >= num_slots)
@@ -60,6 +62,7 @@ namespace {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 // ---------------------------------------------------------------- bf16 ----
 
@@ -92,6 +95,9 @@ __device__ __forceinline__ void wave_lds_sync()
 // (gfx9 encoding: vmcnt 0, expcnt 7, lgkmcnt 15 are "no wait" for the others).
 __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// s_waitcnt lgkmcnt(0): every LDS access of this wave has completed (vmcnt 63, expcnt 7).
+__device__ __forceinline__ void wait_lgkm_all() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
 // Tokens staged per chunk by the token loops (measured on MI355X: the
 // recurrent loop keeps the next chunk's inputs in registers through the
 // current chunk, and two tokens per chunk keep it at 4 waves per SIMD; the
@@ -117,6 +123,78 @@ __device__ __forceinline__ float row_sum16(float x)
     x += dpp_mov<0x141>(x);  // row_half_mirror
     x += dpp_mov<0x140>(x);  // row_mirror
     return x;
+}
+
+// Sum over the 64 lanes of a wave, complete in lane 63: the DPP-row sums,
+// then row 0 into row 1 and row 2 into row 3 (row_bcast:15), then rows 0-1
+// into rows 2-3 (row_bcast:31).
+__device__ __forceinline__ float wave_total(float x)
+{
+    x = row_sum16(x);
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x142, 0xA, 0xF, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x143, 0xC, 0xF, false));
+    return x;
+}
+
+// Transpose-reduce over the 64 lanes of a wave: x[0..P) in every lane (P a
+// power of two, 2 <= P <= 64) -> in lane l the wave total of value
+// l >> (6 - log2 P).  Each halving step exchanges half the values with the
+// partner lane at one distance (32 and 16: permlane swaps; 8, 4, 2, 1: DPP)
+// and keeps the other half, so P sums cost about 2P operations instead of
+// six each; distances left once one value remains reduce it in place.
+template <int CTRL, int N>
+__device__ __forceinline__ void halve_dpp(float *x, bool up)
+{
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const float a = x[i], b = x[i + N];
+        const float send = up ? a : b, keep = up ? b : a;
+        x[i] = keep + dpp_mov<CTRL>(send);
+    }
+}
+
+__device__ __forceinline__ float swap32_sum(float a, float b)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float swap16_sum(float a, float b)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// one step at a DPP distance: halve N values, or reduce the last one in place
+template <int CTRL, int N>
+__device__ __forceinline__ void transpose_step(float *x, bool up)
+{
+    if constexpr (N >= 2) halve_dpp<CTRL, N / 2>(x, up);
+    else x[0] += dpp_mov<CTRL>(x[0]);
+}
+
+template <int P>
+__device__ __forceinline__ float wave_transpose_sum(float *x, int lane)
+{
+    static_assert(P >= 2 && P <= 64 && (P & (P - 1)) == 0, "P: a power of two in 2..64");
+    constexpr int N1 = P / 2;                   // values left after distance 32
+    constexpr int N2 = N1 >= 2 ? N1 / 2 : 1;    // ... 16
+    constexpr int N3 = N2 >= 2 ? N2 / 2 : 1;    // ... 8
+    constexpr int N4 = N3 >= 2 ? N3 / 2 : 1;    // ... 4
+    constexpr int N5 = N4 >= 2 ? N4 / 2 : 1;    // ... 2
+#pragma unroll
+    for (int i = 0; i < N1; ++i) x[i] = swap32_sum(x[i], x[i + N1]);
+    if constexpr (N1 >= 2) {
+#pragma unroll
+        for (int i = 0; i < N1 / 2; ++i) x[i] = swap16_sum(x[i], x[i + N1 / 2]);
+    } else {
+        x[0] = swap16_sum(x[0], x[0]);
+    }
+    transpose_step<0x140, N2>(x, lane & 8);  // row_mirror: lane m <-> 15 - m
+    transpose_step<0x141, N3>(x, lane & 4);  // row_half_mirror: m <-> 7 - m
+    transpose_step<0x4E, N4>(x, lane & 2);   // quad_perm [2,3,0,1]
+    transpose_step<0xB1, N5>(x, lane & 1);   // quad_perm [1,0,3,2]
+    return x[0];
 }
 
 __device__ __forceinline__ void row_sum16x2(float &a, float &b)
@@ -1196,7 +1274,8 @@ __global__ void __launch_bounds__(2048 / (G * VS)) kda_packed_fused_kernel(const
 //
 // Read-only calls in the batched form ("Frozen / speculative-verify mode":
 // the pool is never written back) with 2..VERIFY_CHUNK_MAX_T tokens per
-// sequence and no checkpoints.  Every token then reads the state through the
+// sequence and no checkpoints (longer and ragged calls take the WY verify
+// kernel below, which this one outruns at these lengths on MI355X).  Every token then reads the state through the
 // slot's initial state S0 (K x V), and the recurrence unrolls per value row.
 // With L_t the log-decay of tokens 0..t summed per key channel, E_t =
 // exp(L_t), W_ts = exp(L_t - L_s) (s <= t), k^ and q^ the L2-normalised key
@@ -1209,9 +1288,9 @@ __global__ void __launch_bounds__(2048 / (G * VS)) kda_packed_fused_kernel(const
 // (16x16x4 MFMA); the T x T coefficients are reduced once per head and the
 // rest is a forward substitution per value row.  This replaces T passes of
 // vector arithmetic over the whole state.  TM, the token slots the kernel
-// is built for (2, 4 or 8, the smallest that holds T), sizes the input
-// registers and LDS: with TM = 4 an fp32 workgroup fits in 108 VGPRs and
-// 40 KB of LDS, four workgroups per CU instead of three.
+// is built for (2 or 4, the smallest that holds T; it also holds 8), sizes
+// the input registers and LDS: with TM = 4 an fp32 workgroup fits in 108
+// VGPRs and 40 KB of LDS, four workgroups per CU instead of three.
 //
 // Layout: wave w owns value rows 32w..32w+31 as two 16-row tiles.  MFMA
 // lane l supplies row (l & 15) of a tile and K slot (l >> 4); the K order
@@ -1233,7 +1312,7 @@ __global__ void __launch_bounds__(256) kda_verify_chunk_kernel(const RecParams p
     constexpr int NJ = 32 / VPL;            // 16-byte accesses per lane and tile
     constexpr uint32_t ROW_BYTES = KD * (BF16 ? 2 : 4);
     constexpr int NS = 2 + 2 * TM;          // sums per token: |q|^2, |k|^2, q.W k_s, k.W k_s
-    static_assert(TM <= VERIFY_CHUNK_MAX_T && 2 * TM <= 16, "k and q rows of the 16-column operand");
+    static_assert(TM <= 8, "k and q rows of the 16-column operand");
     constexpr int RSW = ROW_BYTES / 4;      // words per tile row in LDS
     // operand rows k_t*E_t (t), q_t*E_t (TM + t), rows past 2 TM zero; padded
     // by 16 bytes so that the 16 rows read by one instruction spread over the
@@ -1502,6 +1581,464 @@ __global__ void __launch_bounds__(256) kda_verify_chunk_kernel(const RecParams p
     }
 }
 
+// ------------------------------------------------- WY verify kernel ----
+//
+// Read-only calls ("Frozen / speculative-verify mode": the pool is never
+// written back) without checkpoints, with at most VERIFY_WY_MAX_T tokens per
+// sequence: the batched form, or the ragged form when the caller declares the
+// longest sequence.  Every token then reads the state through the slot's
+// initial state S0 (K x V) and the recurrence unrolls.  With L_t the
+// log-decay of tokens 0..t summed per key channel, E_t = exp(L_t),
+// W_ts = exp(L_t - L_s) (s <= t), k^ and q^ the L2-normalised key and query
+// and b_s = beta_s u_s:
+//   u_t = v_t - k^_t.(E_t * S0) - sum_{s<t} (k^_t . W_ts k^_s) b_s
+//   o_t = scale [ q^_t.(E_t * S0) + sum_{s<=t} (q^_t . W_ts k^_s) b_s ]
+// (the pages' WY-parallel form: decay folded into k*exp(cumsum g) and
+// q*exp(cumsum g) operands of a product with the state), which equals T
+// sequential steps up to rounding.
+//
+//  * The state goes straight from HBM into LDS (global_load_lds_dwordx4, no
+//    VGPRs): each wave moves its own 32 value rows, whole rows per 1 KiB
+//    instruction, and only waits for its own loads.  The 16-byte column c of
+//    row r lands at column c ^ (r & 15) (the lane order of the load chooses
+//    the global address of each LDS slot), so that the matrix-core operand
+//    reads, 16 rows at one column, fall on distinct banks.
+//  * The products [k_t E_t ; q_t E_t] x S0 (2T x 128 by 128 x 128 per head)
+//    run on the matrix cores: fp32 pools with fp32 MFMAs, bf16 pools with
+//    bf16 MFMAs on the exact state and the fp32 token operand split into a
+//    bf16 head and remainder (two products, ~2^-17 relative).
+//  * Overlapping the state loads, every channel's cumulative decay is
+//    evaluated once, and the T^2 W-weighted channel sums (and the norms) are
+//    split over the two wave pairs and reduced over each wave in registers.
+//  * Each wave then solves the forward substitution for its own rows (two
+//    lanes per row) from its own products: no barrier after the products
+//    other than the one that publishes the coefficients.
+// TM (2, 4, 8 or 16, the smallest that holds the declared length) sizes the
+// token registers and LDS; with TM = 16 an fp32 workgroup takes 77 KB of LDS,
+// two per CU.  Null rows give +0; in the ragged form, tokens past the
+// declared length give +0 and record nothing.
+constexpr int pow2_at_least(int x)
+{
+    int q = 2;
+    while (q < x) q *= 2;
+    return q;
+}
+
+// Channel sums of the WY verify kernel: layout A holds |q_t|^2 and
+// q_t.W_ts k_s (s <= t), t + 2 sums for token t; layout B |k_t|^2 and
+// k_t.W_ts k_s (s < t), t + 1 sums.  They are emitted in chunks of whole
+// tokens (TPC tokens per chunk), each reduced over the wave at once; in
+// chunk k, token t's sums start at off(t) (norm first, then s = 0, 1, ...).
+template <int TM>
+struct WyChunks {
+    static constexpr int TPC = TM > 4 ? 4 : TM;   // tokens per chunk
+    static constexpr int NCH = TM / TPC;
+    static constexpr int first(int k) { return k * TPC; }
+    // offset of token t in its chunk, layout A or B
+    static constexpr int off(int t, bool a)
+    {
+        int o = 0;
+        for (int u = (t / TPC) * TPC; u < t; ++u) o += u + (a ? 2 : 1);
+        return o;
+    }
+    static constexpr int size(int k)  // layout A, the larger
+    {
+        int o = 0;
+        for (int u = first(k); u < first(k) + TPC; ++u) o += u + 2;
+        return o;
+    }
+    static constexpr int P(int k) { return pow2_at_least(size(k)); }
+};
+
+// One layout of the channel sums, one key channel per lane, reduced over the
+// wave chunk by chunk: layout A (x = q) holds |q_t|^2 and q_t.W_ts k_s
+// (s <= t), layout B (x = k) |k_t|^2 and k_t.W_ts k_s (s < t).  kw[s]
+// carries k_s * W_ts across the chunks.
+template <int TM, int K, bool A>
+__device__ __forceinline__ float wy_chunk_layout(float *kw, const float *x, const float *kf, const float *d, int n,
+                                                 int lane)
+{
+    using C = WyChunks<TM>;
+    constexpr int P = C::P(K);
+    float cur[P];
+#pragma unroll
+    for (int i = 0; i < P; ++i) cur[i] = 0.f;
+#pragma unroll
+    for (int tt = 0; tt < C::TPC; ++tt) {
+        const int t = C::first(K) + tt;
+        const bool on = t < n;
+#pragma unroll
+        for (int s = 0; s < t; ++s) kw[s] *= d[t];  // k_s * W_ts
+        kw[t] = kf[t];
+        const int o = C::off(t, A);
+        cur[o] = on ? x[t] * x[t] : 0.f;
+#pragma unroll
+        for (int s = 0; s < (A ? t + 1 : t); ++s) cur[o + 1 + s] = on ? x[t] * kw[s] : 0.f;
+    }
+    return wave_transpose_sum<P>(cur, lane);
+}
+
+template <int TM, bool A>
+__device__ __forceinline__ void wy_layout_sums(float *r, const float *x, const float *kf, const float *d, int n,
+                                               int lane)
+{
+    constexpr int NCH = WyChunks<TM>::NCH;
+    float kw[TM];
+    r[0] = wy_chunk_layout<TM, 0, A>(kw, x, kf, d, n, lane);
+    if constexpr (NCH > 1) r[1] = wy_chunk_layout<TM, (NCH > 1 ? 1 : 0), A>(kw, x, kf, d, n, lane);
+    if constexpr (NCH > 2) r[2] = wy_chunk_layout<TM, (NCH > 2 ? 2 : 0), A>(kw, x, kf, d, n, lane);
+    if constexpr (NCH > 3) r[3] = wy_chunk_layout<TM, (NCH > 3 ? 3 : 0), A>(kw, x, kf, d, n, lane);
+}
+
+// Per-head metadata: the sequence's tokens, the pool slot, the heads.
+struct WyItem {
+    int seq, hv, hq, t0, len, n, idx, live;
+};
+
+__device__ __forceinline__ WyItem wy_item(const RecParams &p, int w)
+{
+    WyItem it;
+    it.seq = w / p.HV;
+    it.hv = w - it.seq * p.HV;
+    it.hq = it.hv / p.group;
+    it.idx = p.state_indices[it.seq];
+    if (p.cu_seqlens) {
+        it.t0 = min(max(p.cu_seqlens[it.seq], 0), p.n_tokens);
+        it.len = max(min(p.cu_seqlens[it.seq + 1], p.n_tokens) - it.t0, 0);
+    } else {
+        it.t0 = it.seq * p.tps;
+        it.len = p.tps;
+    }
+    it.n = min(it.len, p.tps);  // tokens evaluated (p.tps: the declared length, <= TM)
+    it.live = it.idx >= 0 && (int64_t)it.idx < p.num_slots && it.n > 0;
+    return it;
+}
+
+// Matrix-core operand layout of the WY verify kernel.  A product's K order
+// (the key channels) is free as long as both operands take the same one; it
+// is chosen so that each 16-byte piece a lane loads holds consecutive
+// channels and the four lane groups g = lane >> 4 read 64 contiguous bytes
+// of a state row per load:
+//  * bf16 pools, v_mfma_f32_16x16x32_bf16: K block j (32 channels), element
+//    e of group g is channel 32 j + 8 g + e;
+//  * fp32 pools, v_mfma_f32_16x16x4_f32: K group j (16 channels, four
+//    products), product e of group g takes channel 16 j + 4 g + e.
+template <bool BF16>
+struct WyLayout {
+    static constexpr int NJ = BF16 ? 4 : 8;     // K blocks / groups per row
+    static constexpr int CPJ = KD / NJ;         // channels per block / group
+    static constexpr int SW = BF16 ? 4 : 4;     // state words per lane and block / group (16 bytes)
+    __device__ static constexpr int channel(int j, int g) { return CPJ * j + (CPJ / 4) * g; }
+};
+
+// One workgroup (4 waves) per head; each wave owns 32 value rows of it, as
+// two 16-row tiles.
+//  1. The token inputs of the lane's key channel are loaded before the pool
+//     slot is known, and the lane's value row.
+//  2. Each wave loads its first tile straight into registers, in the layout
+//     the matrix cores take (16 rows x 64 contiguous bytes per load), and
+//     its second tile from HBM into its own LDS tile buffer (both streamed:
+//     non-temporal)
+//     (global_load_lds_dwordx4: whole rows, 1 KiB per instruction, no VGPRs;
+//     the 16-byte column c of row r lands at column c ^ (r & 15), so that
+//     the operand reads, 16 rows at one column, fall on distinct banks).
+//     Meanwhile the key channels, one per lane (waves 0-1 layout A with q,
+//     waves 2-3 layout B with k): cumulative decays, the token operand
+//     column of the channel (q_t E_t, or k_t E_t; zero past the tokens)
+//     into LDS once for the head (bf16 pools: as a bf16 head and
+//     remainder), and the W-weighted channel sums, each reduced over the
+//     wave in registers; one barrier.
+//  3. [k_t E_t ; q_t E_t] x S0 on the matrix cores, tile by tile (bf16
+//     pools: the exact state by the operand's head and remainder, two bf16
+//     products; fp32 pools: fp32 products), through LDS into a row-per-lane
+//     layout, then the forward substitution (lanes l and l + 32 own row
+//     l & 31 and store alternate tokens).
+// A workgroup holds one tile buffer per wave (8 KB fp32, 4 KB bf16) plus the
+// operand, sums and coefficients, so several share a compute unit and the
+// loads of one overlap the arithmetic of the others.  Consecutive heads
+// (which share their sequence's token rows) run on one XCD.
+template <bool BF16, int TM>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TM <= 8 ? 4 : 2)))
+kda_verify_wy_kernel(const RecParams p)
+{
+    using LY = WyLayout<BF16>;
+    constexpr int WROWS = 32;                    // value rows per wave
+    constexpr uint32_t ROW_BYTES = KD * (BF16 ? 2 : 4);
+    constexpr int LPR = ROW_BYTES / 16;          // 16-byte columns per row
+    constexpr int RPI = 1024 / ROW_BYTES;        // rows per 1 KiB load instruction
+    constexpr int NTI = 16 * ROW_BYTES / 1024;   // load instructions per 16-row tile
+    constexpr int NCT = (2 * TM + 15) / 16;      // 16-column tiles of the token operand
+    constexpr int NCOL = 2 * TM;                 // columns: k_t E_t at t, q_t E_t at TM + t
+    constexpr int OST = NCOL + 4;                // floats per row of the products in LDS
+    using CH = WyChunks<TM>;
+    constexpr int NCH = CH::NCH;                 // chunks of channel sums
+    constexpr int NJ = LY::NJ;
+    constexpr int SW = LY::SW;
+    constexpr int NCF = 2 * TM * TM + 3 * TM;    // per-wave coefficients
+    constexpr int TBW = 16 * ROW_BYTES / 4;      // words of a tile
+    constexpr int BUFW = TBW > WROWS * OST ? TBW : WROWS * OST;
+    constexpr int BST = BF16 ? KD / 2 + 4 : KD + 4;  // words per operand row (bf16: pairs), padded
+    static_assert(TM <= VERIFY_WY_MAX_T, "verify tokens");
+
+    __shared__ __align__(16) uint32_t s_T[4][BUFW];          // per wave: a state tile, then the products
+    __shared__ __align__(16) uint32_t s_B[BF16 ? 2 : 1][NCOL][BST];  // token operand (bf16: head, remainder)
+    __shared__ float s_sum[2][2][64 * NCH];                   // channel sums: layout, half of the channels
+    __shared__ float s_beta[TM];
+    __shared__ float s_cf[4][NCF];                            // per wave: C_ts, A'_ts, rk_t, scale*rq_t, beta_t
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = lane >> 4;
+    const int n16 = lane & 15;
+    const int rloc = lane & 31;
+    const int vrow = WROWS * wave + rloc;
+    const int work = (int)(blockIdx.x & 7u) * (int)(gridDim.x >> 3) + (int)(blockIdx.x >> 3);
+    if (work >= p.n_work) return;
+    const WyItem it = wy_item(p, work);
+    // token row t of the sequence (clamped to its last evaluated token); a
+    // sequence without tokens reads row 0, which exists (a call without any
+    // token launches nothing), and uses none of it
+    auto tok = [&](int t) { return it.n > 0 ? (int64_t)it.t0 + min(t, it.n - 1) : (int64_t)0; };
+
+    // 1. the token inputs of key channel c, and the value row
+    const bool A = wave < 2;
+    const int c = 64 * (wave & 1) + lane;
+    const bool g_f32 = p.g_f32 != 0;
+    const bool beta_f32 = p.beta_f32 != 0;
+    uint32_t xb[TM], kb[TM], glo[TM], ghi[TM], vb[TM];
+    uint32_t beta_lo = 0, beta_hi = 0;
+    {
+        // (layout B reads k twice rather than copy it: a copy would wait for the load)
+        const uint16_t *xs = A ? p.q : p.k;
+        const int64_t xstride = A ? p.q_stride : p.k_stride;
+#pragma unroll
+        for (int t = 0; t < TM; ++t) {
+            const int64_t n_ = tok(t);
+            kb[t] = p.k[n_ * p.k_stride + (int64_t)it.hq * KD + c];
+            xb[t] = xs[n_ * xstride + (int64_t)it.hq * KD + c];
+            load_halves(static_cast<const char *>(p.g) + (n_ * p.g_stride + (int64_t)it.hv * KD + c) * (g_f32 ? 4 : 2),
+                        g_f32, glo[t], ghi[t]);
+        }
+        // (every lane loads a beta, lanes t < TM of wave 2 keep token t's:
+        // a load under a lane condition would wait for its value at the join)
+        load_halves(static_cast<const char *>(p.beta) +
+                        (tok(min(lane, TM - 1)) * p.beta_stride + it.hv) * (beta_f32 ? 4 : 2),
+                    beta_f32, beta_lo, beta_hi);
+#pragma unroll
+        for (int t = 0; t < TM; ++t) vb[t] = p.v[tok(t) * p.v_stride + (int64_t)it.hv * KD + vrow];
+    }
+    if (!it.live) {  // a null head: +0 for each of its tokens
+        for (int i = tid; i < it.len * KD; i += 256)
+            p.out[((int64_t)(it.t0 + i / KD) * p.HV + it.hv) * KD + (i & (KD - 1))] = 0;
+        return;
+    }
+
+    // 2. the state: the first tile into registers, the second into the tile buffer
+    uint32_t *buf = s_T[wave];
+    const char *wrows = static_cast<const char *>(p.state) +
+                        ((int64_t)it.idx * p.slot_stride + (int64_t)it.hv * (KD * KD)) * (BF16 ? 2 : 4) +
+                        (int64_t)(WROWS * wave) * ROW_BYTES;
+    uint32_t st[NJ][SW];
+    {
+        const char *row = wrows + (int64_t)n16 * ROW_BYTES;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const u32x4 w = __builtin_nontemporal_load(
+                reinterpret_cast<const u32x4 *>(row + LY::channel(j, grp) * (BF16 ? 2 : 4)));
+            st[j][0] = w.x; st[j][1] = w.y; st[j][2] = w.z; st[j][3] = w.w;
+        }
+    }
+    // (the scheduling barriers keep other work, and the waits it would
+    // bring, from landing between the loads of the tile)
+    __builtin_amdgcn_sched_barrier(0);
+    {
+        const char *src = wrows + 16 * ROW_BYTES;
+#pragma unroll
+        for (int i = 0; i < NTI; ++i) {
+            const int r = RPI * i + lane / LPR;
+            const int col = (lane % LPR) ^ (r & 15);
+            __builtin_amdgcn_global_load_lds(src + r * ROW_BYTES + 16 * col, buf + i * 256, 16, 0, 2 /* nt */);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // the key channel: decays, the operand column, the channel sums
+    {
+        if (A && p.kg) {  // verify cache of the raw key and gate
+#pragma unroll
+            for (int t = 0; t < TM; ++t) {
+                if (t < it.n && t < p.t_max) {
+                    StageIn si{};
+                    si.k = kb[t];
+                    si.g_lo = glo[t];
+                    si.g_hi = ghi[t];
+                    store_kg(p.kg, p.kg_f32 != 0, ((int64_t)it.idx * p.HV + it.hv) * p.t_max + t, c, si, g_f32);
+                }
+            }
+        }
+        const bool precomputed = p.precomputed != 0;
+        const float a_h = precomputed ? 0.f : __expf(p.A_log[it.hv]);
+        const float dtc = precomputed ? 0.f : p.dt_bias[(int64_t)it.hv * KD + c];
+        float xf[TM], kf[TM], d[TM];
+        float L = 0.f;
+#pragma unroll
+        for (int t = 0; t < TM; ++t) {
+            const float gv = halves_value(glo[t], ghi[t], g_f32);
+            const float lg = precomputed ? gv : -a_h * softplus_f(gv + dtc);
+            L += lg;
+            d[t] = __expf(lg);
+            xf[t] = bf16_bits_to_f32(xb[t]);
+            kf[t] = bf16_bits_to_f32(kb[t]);
+            // operand column: q_t E_t (layout A) or k_t E_t (layout B)
+            const float ov = t < it.n ? xf[t] * __expf(L) : 0.f;
+            const int col = A ? TM + t : t;
+            if constexpr (BF16) {
+                const __bf16 hb = (__bf16)ov;
+                const __bf16 lb = (__bf16)(ov - (float)hb);
+                reinterpret_cast<__bf16 *>(s_B[0][col])[c] = hb;
+                reinterpret_cast<__bf16 *>(s_B[1][col])[c] = lb;
+            } else {
+                reinterpret_cast<float *>(s_B[0][col])[c] = ov;
+            }
+        }
+        float r[NCH];
+        if (A) wy_layout_sums<TM, true>(r, xf, kf, d, it.n, lane);
+        else wy_layout_sums<TM, false>(r, xf, kf, d, it.n, lane);
+        constexpr int S0 = 64 / CH::P(0), S1 = 64 / CH::P(NCH > 1 ? 1 : 0);
+        constexpr int S2 = 64 / CH::P(NCH > 2 ? 2 : 0), S3 = 64 / CH::P(NCH > 3 ? 3 : 0);
+#pragma unroll
+        for (int k = 0; k < NCH; ++k) {
+            const int sp = k == 0 ? S0 : k == 1 ? S1 : k == 2 ? S2 : S3;  // lanes holding one sum
+            if ((lane & (sp - 1)) == 0) s_sum[A ? 0 : 1][wave & 1][64 * k + lane / sp] = r[k];
+        }
+        if (wave == 2 && lane < TM) {
+            const float bv = halves_value(beta_lo, beta_hi, beta_f32);
+            s_beta[lane] = precomputed ? bv : sigmoid_f(bv);
+        }
+    }
+    __syncthreads();
+
+    // coefficients (each wave its own copy): (t, s) = (e / TM, e % TM);
+    // token t's first sum: its chunk, then the chunk's earlier tokens
+    float *cf = s_cf[wave];
+    {
+        auto slot = [&](int t, bool a) {
+            const int k = t / CH::TPC, f = k * CH::TPC;
+            return 64 * k + (t - f) * (f + t + (a ? 3 : 1)) / 2;
+        };
+        auto sum = [&](int a, int i) { return s_sum[a][0][i] + s_sum[a][1][i]; };
+        auto rk_of = [&](int t) { return rsqrtf(sum(1, slot(t, false)) + p.l2_eps); };
+#pragma unroll
+        for (int e = lane; e < TM * TM; e += 64) {
+            const int t = e / TM, s = e - (e / TM) * TM;
+            if (t < it.n) {
+                const float rks = rk_of(s);
+                cf[e] = s < t ? rk_of(t) * rks * sum(1, slot(t, false) + 1 + s) : 0.f;
+                cf[TM * TM + e] = s <= t ? rks * sum(0, slot(t, true) + 1 + s) : 0.f;
+            }
+        }
+        if (lane < TM && lane < it.n) {
+            cf[2 * TM * TM + lane] = rk_of(lane);
+            cf[2 * TM * TM + TM + lane] = rsqrtf(sum(0, slot(lane, true)) + p.l2_eps) * p.scale;
+            cf[2 * TM * TM + 2 * TM + lane] = s_beta[lane];
+        }
+    }
+
+    // 3. the products, tile by tile: column cc = 16 kc + (lane & 15) of the
+    // operand at the lane's channels (zero past the 2 TM columns)
+    f32x4 acc[2][NCT];
+    auto tile_products = [&](int tau) {
+#pragma unroll
+        for (int kc = 0; kc < NCT; ++kc) acc[tau][kc] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const int ch = LY::channel(j, grp);
+#pragma unroll
+            for (int kc = 0; kc < NCT; ++kc) {
+                const int cc = 16 * kc + n16;
+                const int ccr = cc < NCOL ? cc : NCOL - 1;
+                if constexpr (BF16) {  // exact bf16 state: two products
+                    u32x4 bh = *reinterpret_cast<const u32x4 *>(&s_B[0][ccr][ch / 2]);
+                    u32x4 bl = *reinterpret_cast<const u32x4 *>(&s_B[1][ccr][ch / 2]);
+                    if (cc >= NCOL) bh = bl = u32x4{0u, 0u, 0u, 0u};
+                    const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{st[j][0], st[j][1], st[j][2], st[j][3]});
+                    acc[tau][kc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, bh),
+                                                                          acc[tau][kc], 0, 0, 0);
+                    acc[tau][kc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, bl),
+                                                                          acc[tau][kc], 0, 0, 0);
+                } else {  // fp32 state, fp32 products
+                    f32x4 b = *reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(s_B[0][ccr]) + ch);
+                    if (cc >= NCOL) b = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        acc[tau][kc] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(st[j][e]), b[e],
+                                                                           acc[tau][kc], 0, 0, 0);
+                }
+            }
+        }
+    };
+    tile_products(0);
+    wait_vm_all();  // the second tile has landed in this wave's buffer
+    {
+        const uint32_t *row = buf + n16 * (ROW_BYTES / 4);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const int col = LY::channel(j, grp) / (BF16 ? 8 : 4);
+            const u32x4 w = *reinterpret_cast<const u32x4 *>(row + 4 * (col ^ n16));
+            st[j][0] = w.x; st[j][1] = w.y; st[j][2] = w.z; st[j][3] = w.w;
+        }
+    }
+    tile_products(1);
+
+    // the products to LDS (the tile buffer: every read of it is done, and a
+    // wave's LDS accesses are performed in order): row 16 tau + 4 g + r,
+    // column 16 kc + (lane & 15)
+    float *prod = reinterpret_cast<float *>(buf);
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+        for (int kc = 0; kc < NCT; ++kc)
+            if (16 * kc + n16 < NCOL)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) prod[(16 * tau + 4 * grp + r) * OST + 16 * kc + n16] = acc[tau][kc][r];
+    wave_lds_sync();
+
+    // forward substitution, row rloc of the wave
+    const float *pr = prod + rloc * OST;
+    float P[TM], Q[TM], bu[TM];
+#pragma unroll
+    for (int t2 = 0; t2 < TM; t2 += 2) {
+        const float2 x = *reinterpret_cast<const float2 *>(pr + t2);
+        const float2 y = *reinterpret_cast<const float2 *>(pr + TM + t2);
+        P[t2] = x.x; P[t2 + 1] = x.y;
+        Q[t2] = y.x; Q[t2 + 1] = y.y;
+    }
+    const int half = lane >> 5;
+    const int64_t crow0 = ((int64_t)it.idx * p.HV + it.hv) * p.t_max;
+    const float *Cm = cf, *Am = cf + TM * TM, *tk = cf + 2 * TM * TM;
+#pragma unroll
+    for (int t = 0; t < TM; ++t) {
+        if (t < it.n) {
+            float x = tk[t] * P[t];
+#pragma unroll
+            for (int s = 0; s < t; ++s) x = fmaf(Cm[t * TM + s], bu[s], x);
+            bu[t] = tk[2 * TM + t] * (bf16_bits_to_f32(vb[t]) - x);
+            if ((t & 1) == half) {
+                float y = Q[t];
+#pragma unroll
+                for (int s = 0; s <= t; ++s) y = fmaf(Am[t * TM + s], bu[s], y);
+                y *= tk[TM + t];
+                p.out[((int64_t)(it.t0 + t) * p.HV + it.hv) * KD + vrow] = (uint16_t)(pack_bf16x2(y, 0.0f) & 0xffffu);
+                if (p.corr && t < p.t_max) p.corr[(crow0 + t) * KD + vrow] = bu[t];
+            }
+        }
+    }
+    // tokens past the declared length: +0
+    for (int i = tid; i < (it.len - it.n) * KD; i += 256)
+        p.out[((int64_t)(it.t0 + it.n + i / KD) * p.HV + it.hv) * KD + (i & (KD - 1))] = 0;
+}
+
 // ------------------------------------------------------------ dispatch ----
 
 template <int G, bool BF16>
@@ -1547,18 +2084,30 @@ int launch_recurrent(const RecParams &p, const Launch &l, void *stream)
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();  // a stale error must not be blamed on this launch
     if (l.family == KERNEL_VERIFY_CHUNK) {
-        // token slots sized to the call: 2, 4 or 8, the smallest that holds T
+        // token slots sized to the call: 2 or 4, the smallest that holds T
         const dim3 grid(l.grid), block(l.block);
         if (p.tps <= 2) {
             if (l.bf16_state) hipLaunchKernelGGL((kda_verify_chunk_kernel<true, 2>), grid, block, 0, s, p);
             else hipLaunchKernelGGL((kda_verify_chunk_kernel<false, 2>), grid, block, 0, s, p);
-        } else if (p.tps <= 4) {
+        } else {
             if (l.bf16_state) hipLaunchKernelGGL((kda_verify_chunk_kernel<true, 4>), grid, block, 0, s, p);
             else hipLaunchKernelGGL((kda_verify_chunk_kernel<false, 4>), grid, block, 0, s, p);
-        } else {
-            if (l.bf16_state) hipLaunchKernelGGL((kda_verify_chunk_kernel<true, 8>), grid, block, 0, s, p);
-            else hipLaunchKernelGGL((kda_verify_chunk_kernel<false, 8>), grid, block, 0, s, p);
         }
+        return record(hipGetLastError());
+    }
+    if (l.family == KERNEL_VERIFY_WY) {
+        // token slots sized to the declared length: 2, 4, 8 or 16, the smallest that holds it
+        const dim3 grid(l.grid), block(l.block);
+#define KDA_WY(TM_)                                                                                      \
+    do {                                                                                                 \
+        if (l.bf16_state) hipLaunchKernelGGL((kda_verify_wy_kernel<true, TM_>), grid, block, 0, s, p);   \
+        else hipLaunchKernelGGL((kda_verify_wy_kernel<false, TM_>), grid, block, 0, s, p);               \
+    } while (0)
+        if (p.tps <= 2) KDA_WY(2);
+        else if (p.tps <= 4) KDA_WY(4);
+        else if (p.tps <= 8) KDA_WY(8);
+        else KDA_WY(16);
+#undef KDA_WY
         return record(hipGetLastError());
     }
     hipError_t e = l.bf16_state ? launch_rec_dt<true>(p, l, s) : launch_rec_dt<false>(p, l, s);

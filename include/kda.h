@@ -145,11 +145,20 @@ typedef struct kda_launch_plan {
  *  g_dtype, beta_dtype  kda_dtype of g and beta (bf16 or fp32).
  *  tokens_per_seq    without cu_seqlens: 0 or 1 is T=1, T > 1 is the uniform
  *                    batched form (sequence i owns tokens [i*T, (i+1)*T)).
+ *                    With cu_seqlens: 0, or the length of the longest
+ *                    sequence as declared by the caller (a caller contract).
+ *                    A read-only call without checkpoints that declares at
+ *                    most 16 takes the matrix-product form below; there, the
+ *                    tokens of a sequence past the declared length (a broken
+ *                    contract) give +0 outputs and record nothing.  Other
+ *                    ragged calls ignore it.
  *  flags             KDA_FLAG_NO_STATE_UPDATE: the pool is only read.  The
  *                    outputs are those of the updating call; read-only calls
- *                    in the batched form with 2..8 tokens and no checkpoints
- *                    evaluate them in another order (one matrix product per
- *                    head), equal up to rounding.
+ *                    without checkpoints whose sequences have at most 16
+ *                    tokens (batched T >= 2, or ragged with tokens_per_seq
+ *                    declared) evaluate them in another order (one matrix
+ *                    product per head, "Frozen / speculative-verify mode"),
+ *                    equal up to rounding.
  *  correction_cache  NULL or fp32 [num_slots, HV, cache_t_max, 128], contiguous,
  *                    16-byte aligned ("Frozen / speculative-verify mode":
  *                    slot-indexed per-token delta-rule corrections): for token

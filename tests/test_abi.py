@@ -85,7 +85,7 @@ def rec_args(N=4, H=4, T=None, slots=8, bf16=False, varlen=False, HV=None, tps=1
         a.cu_seqlens = A.take((N + 1) * 4)
     a.out = A.take(T * HV * D * 2)
     a.g_dtype = a.beta_dtype = 1
-    a.tokens_per_seq = tps
+    a.tokens_per_seq = 0 if varlen else tps  # ragged: no declared longest sequence
     return a
 
 
@@ -362,30 +362,55 @@ def test_batched_form_and_flags():
     assert plan_rec(a)[0] == 0, err()
 
 
-@pytest.mark.parametrize("tps", [2, 4, 8])
+@pytest.mark.parametrize("tps", [2, 3, 4, 5, 8, 9, 12, 16])
 @pytest.mark.parametrize("bf16", [False, True])
-def test_read_only_batched_calls_take_the_chunked_verify_kernel(tps, bf16):
-    """Read-only batched calls with 2..8 tokens and no checkpoints run as one
-    matrix product per head (family 5): whole heads, 256 threads."""
+def test_read_only_batched_calls_take_a_verify_kernel(tps, bf16):
+    """Read-only batched calls with 2..16 tokens and no checkpoints run as one
+    matrix product per head, one workgroup of 256 threads per head: the
+    chunked verify kernel (family 6) up to 4 tokens, the WY verify kernel
+    (family 5) above."""
     a = rec_args(N=64, H=32, tps=tps, slots=128, bf16=bf16)
     a.flags = 1
     rc, p = plan_rec(with_caches(a, t_max=tps))
     assert rc == 0, err()
-    assert (p.kernel, p.vsplit, p.rows_per_block, p.block) == (5, 1, D, 256)
+    assert (p.kernel, p.vsplit, p.rows_per_block, p.block) == (6 if tps <= 4 else 5, 1, D, 256)
     assert p.grid_x == 64 * 32 and p.items == 64 * 32
 
 
-def test_calls_outside_the_chunked_verify_kernel_keep_the_token_loop():
-    """Updating pools, more than 8 tokens, ragged rows and checkpoints stay on
-    the sequential token loop (family 2); T=1 on the T=1 kernel."""
+@pytest.mark.parametrize("declared", [1, 3, 8, 16])
+def test_read_only_ragged_calls_declaring_their_length_take_the_wy_verify_kernel(declared):
+    """A read-only ragged call that declares its longest sequence (at most 16
+    tokens) in tokens_per_seq runs as one matrix product per head."""
+    a = rec_args(N=8, T=24, varlen=True)
+    a.flags, a.tokens_per_seq = 1, declared
+    rc, p = plan_rec(a)
+    assert rc == 0, err()
+    assert (p.kernel, p.vsplit, p.grid_x) == (5, 1, 8 * 4)
+
+
+def test_calls_outside_the_wy_verify_kernel_keep_the_token_loop():
+    """Updating pools, more than 16 tokens, ragged rows without a declared
+    length (or one above 16) and checkpoints stay on the sequential token
+    loop (family 2); T=1 on the T=1 kernel."""
     a = rec_args(N=8, tps=4)
     assert plan_rec(a)[1].kernel == 2  # updating
-    a = rec_args(N=8, tps=9)
+    a = rec_args(N=8, tps=17)
     a.flags = 1
-    assert plan_rec(a)[1].kernel == 2  # 9 tokens
+    assert plan_rec(a)[1].kernel == 2  # 17 tokens
     a = rec_args(N=8, T=24, varlen=True)
     a.flags = 1
-    assert plan_rec(a)[1].kernel == 2  # ragged
+    assert plan_rec(a)[1].kernel == 2  # ragged, no declared length
+    a.tokens_per_seq = 17
+    assert plan_rec(a)[1].kernel == 2  # ragged, declared above 16
+    a = rec_args(N=8, T=24, varlen=True)
+    a.tokens_per_seq = 4
+    assert plan_rec(a)[1].kernel == 2  # ragged, declared, but updating
+    a = rec_args(N=8, tps=8)
+    a.flags = 1
+    a.q_stride += 4
+    a.k_stride += 4
+    a.k += 2
+    assert plan_rec(a)[0] == 0 and plan_rec(a)[1].kernel == 5  # q/k rows need no alignment
     a = rec_args(N=8, tps=4)
     a.flags = 1
     A = Arena()

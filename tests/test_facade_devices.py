@@ -8,8 +8,11 @@ from host tensors: with every tensor on the host the call passes validation
 and reaches the library loader (replaced by one that raises a sentinel, so
 nothing can launch); with any one tensor moved to another device (the meta
 device) the call raises ValueError naming that argument and never reaches
-the loader.
+the loader.  Prepared calls (``prepare``) launch exactly the struct an eager
+call builds.
 """
+import ctypes
+
 import pytest
 import torch
 
@@ -98,3 +101,42 @@ def test_a_call_off_the_hip_device_type_is_refused(make, monkeypatch):
     fn, args, first = make()
     with pytest.raises(ValueError, match="HIP"):
         fn(**args)
+
+
+class RecordingLib:
+    """Stands in for the library: records each entry point call's struct."""
+
+    def __init__(self):
+        self.calls = []
+
+    def __getattr__(self, name):
+        def fn(ref, *rest):
+            st = ctypes.cast(ref, ctypes.POINTER(_STRUCTS[name])).contents if name in _STRUCTS else None
+            self.calls.append((name, bytes(st) if st is not None else None))
+            return 0
+        return fn
+
+
+_STRUCTS = {"kda_recurrent": _lib.RecurrentArgs, "kda_packed_decode": _lib.PackedArgs,
+            "kda_fused_decode": _lib.FusedArgs, "kda_packed_fused_decode": _lib.PackedFusedArgs,
+            "kda_packed_fused_decode_noalloc": _lib.PackedFusedArgs}
+
+
+@pytest.mark.parametrize("make", CALLS, ids=lambda f: f.__name__.strip("_").replace("_args", ""))
+def test_prepared_call_launches_the_eager_struct(make, monkeypatch):
+    """prepare() validates and builds the struct without launching; each
+    call of the PreparedCall launches the same entry point with exactly the
+    struct an eager call builds, and the prepared call keeps its tensors."""
+    rec = RecordingLib()
+    monkeypatch.setattr(_lib, "load", lambda *a, **k: rec)
+    monkeypatch.setattr(api, "_launch", lambda fn, ref, dev, stream=None: fn(ref))
+    fn, args, _ = make()
+    call = api.prepare(fn, **args)
+    assert rec.calls == [] and isinstance(call, api.PreparedCall)
+    out = call()
+    call()
+    assert out is call.output and len(rec.calls) == 2 and rec.calls[0] == rec.calls[1]
+    fn(**args)
+    assert rec.calls[2] == rec.calls[0], "the prepared struct differs from the eager one"
+    held = [t for t in args.values() if isinstance(t, torch.Tensor)]
+    assert all(any(t is k for k in call._keep[1].values()) for t in held)

@@ -47,7 +47,7 @@ def recorded_mask(c, lengths, t_max):
     return mask
 
 
-def call(c, *, form, t_max, kg_dtype, read_only, ckpt=False, tps=None):
+def call(c, *, form, t_max, kg_dtype, read_only, ckpt=False, tps=None, max_seqlen=None):
     T, HV = c.q.shape[0], c.v.shape[1]
     S = c.state.shape[0]
     corr = torch.full((S, HV, t_max, D), SENTINEL, dtype=torch.float32, device=DEV)
@@ -65,7 +65,7 @@ def call(c, *, form, t_max, kg_dtype, read_only, ckpt=False, tps=None):
     out = recurrent_kda(shp(c.q), shp(c.k), shp(c.v), shp(c.g), shp(c.beta), c.A_log, c.dt_bias,
                         initial_state=c.state, state_indices=c.state_indices, cu_seqlens=cu,
                         intermediate_states=ck, disable_state_update=read_only,
-                        correction_cache=corr, kg_cache=kg)
+                        correction_cache=corr, kg_cache=kg, max_seqlen=max_seqlen)
     torch.cuda.synchronize()
     return out, corr, kg, ck
 

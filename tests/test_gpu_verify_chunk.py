@@ -1,12 +1,14 @@
-"""GPU parity of the chunked verify kernel ("flashinfer.kda_decode", Frozen /
-speculative-verify mode): read-only batched calls with 2..8 tokens per
-sequence and no checkpoints, where the tokens' products with the slot's
-initial state are one matrix product per head and the rest a forward
-substitution.  Against the fp64 oracle on every output, cache entry and pool
-bit: token counts 2..8, fp32 and bf16 pools, in-kernel and precomputed gates
+"""GPU parity of the WY verify kernel ("flashinfer.kda_decode", Frozen /
+speculative-verify mode): read-only calls without checkpoints and with at
+most 16 tokens per sequence (batched, or ragged with the longest sequence
+declared), where the tokens' products with the slot's initial state are one
+matrix product per head and the rest a forward substitution.  Against the
+fp64 oracle on every output, cache entry and pool bit: token counts 2..16,
+ragged lengths 0..16, fp32 and bf16 pools, in-kernel and precomputed gates
 (bf16 and fp32), grouped value heads, null rows and an index past the pool,
-caches shorter than, equal to and longer than the token count, and decays so
-strong that the cumulative decay underflows.
+caches shorter than, equal to and longer than the token count, decays so
+strong that the cumulative decay underflows, and a sequence longer than the
+declared length (its tokens past it give zeros and record nothing).
 """
 import numpy as np
 import pytest
@@ -74,6 +76,12 @@ CASES = [  # T, state dtype, gate, gate dtype, H, HV, cache length
     (7, torch.float32, "precomputed", torch.float32, 4, 12, 7),
     (8, torch.bfloat16, "in_kernel", torch.bfloat16, 4, 8, 8),
     (8, torch.float32, "in_kernel", torch.bfloat16, 6, 12, 6),
+    (10, torch.bfloat16, "in_kernel", torch.bfloat16, 2, 4, 16),
+    (12, torch.float32, "in_kernel", torch.bfloat16, 4, 8, 12),
+    (13, torch.float32, "precomputed", torch.bfloat16, 4, 12, 5),
+    (16, torch.bfloat16, "precomputed", torch.float32, 4, 4, 9),
+    (16, torch.float32, "in_kernel", torch.bfloat16, 8, 8, 16),
+    (16, torch.bfloat16, "in_kernel", torch.bfloat16, 4, 8, 16),
 ]
 
 
@@ -84,7 +92,7 @@ def test_chunked_verify_against_oracle(T, state_dtype, gate, gate_dtype, H, HV, 
     seed = 7600 + 10 * T + HV
     n, slots = 11, 24
     say(f"chunked verify T={T} {state_dtype} gate={gate}/{gate_dtype} H={H} HV={HV} t_max={t_max} seed={seed}")
-    assert chunk_plan_kernel(n, T, H, HV, slots, state_dtype == torch.bfloat16) == 5
+    assert chunk_plan_kernel(n, T, H, HV, slots, state_dtype == torch.bfloat16) == (6 if T <= 4 else 5)
     c = synth.recurrent_case(seed, n_seqs=n, H=H, HV=HV, num_slots=slots, state_dtype=state_dtype, device=DEV,
                              indices="random", lengths=[T] * n, null_rows=2, gate=gate, gate_dtype=gate_dtype)
     c.state_indices[4] = slots + 5  # past the pool: null
@@ -181,3 +189,106 @@ def test_chunked_verify_graph_replay_with_new_inputs_and_indices():
         run(eager)
         torch.cuda.synchronize()
         assert torch.equal(P.bits(out), P.bits(eager)), f"replay {rep} differs from the eager call"
+
+
+def ragged_plan_kernel(lengths, H, HV, slots, bf16, max_seqlen):
+    """Kernel family planned for a read-only ragged call declaring max_seqlen."""
+    import ctypes
+    n, T = len(lengths), int(sum(lengths))
+    a = _lib.RecurrentArgs()
+    a.struct_size = ctypes.sizeof(_lib.RecurrentArgs)
+    a.n_seqs, a.n_tokens, a.H, a.HV, a.K, a.V = n, T, H, HV, D, D
+    base, step = 1 << 36, 1 << 28
+    for i, f in enumerate(("q", "k", "v", "g", "beta", "A_log", "dt_bias", "state", "state_indices", "cu_seqlens",
+                           "out")):
+        setattr(a, f, base + i * step)
+    a.q_stride = a.k_stride = H * D
+    a.v_stride = a.g_stride = HV * D
+    a.beta_stride = HV
+    a.scale, a.l2_eps = 0.08838834764831845, 1e-6
+    a.state_dtype = a.ckpt_dtype = 1 if bf16 else 0
+    a.num_slots, a.slot_stride = slots, HV * D * D
+    a.g_dtype = a.beta_dtype = 1
+    a.tokens_per_seq, a.flags = max_seqlen, 1
+    plan = _lib.LaunchPlan()
+    plan.struct_size = ctypes.sizeof(_lib.LaunchPlan)
+    assert _lib.load().kda_recurrent_plan(ctypes.byref(a), ctypes.byref(plan)) == 0, _lib.load().kda_last_error()
+    return plan.kernel
+
+
+RAGGED = [  # max_seqlen, state dtype, gate, gate dtype, H, HV, cache length, seed
+    (3, torch.float32, "in_kernel", torch.bfloat16, 4, 4, 3, 7610),
+    (6, torch.bfloat16, "in_kernel", torch.bfloat16, 4, 8, 4, 7611),
+    (8, torch.float32, "precomputed", torch.float32, 2, 8, 8, 7612),
+    (12, torch.bfloat16, "precomputed", torch.bfloat16, 4, 4, 12, 7613),
+    (16, torch.float32, "in_kernel", torch.bfloat16, 4, 8, 7, 7614),
+    (16, torch.bfloat16, "in_kernel", torch.float32, 8, 8, 16, 7615),
+]
+
+
+@pytest.mark.parametrize("L,state_dtype,gate,gate_dtype,H,HV,t_max,seed", RAGGED,
+                         ids=[f"L{c[0]}-{'bf16' if c[1] == torch.bfloat16 else 'fp32'}-{c[2]}-HV{c[5]}" for c in RAGGED])
+def test_ragged_verify_against_oracle(L, state_dtype, gate, gate_dtype, H, HV, t_max, seed):
+    """Ragged read-only calls (cu_seqlens) declaring their longest sequence:
+    lengths 0..L (one sequence exactly L), null rows and an index past the
+    pool, verify caches; every output, cache entry and pool bit against the
+    oracle."""
+    import random
+    rng = random.Random(seed)
+    n, slots = 12, 30
+    lengths = [rng.randint(0, L) for _ in range(n)]
+    lengths[rng.randrange(n)] = L
+    say(f"ragged WY verify L={L} lengths={lengths} {state_dtype} gate={gate}/{gate_dtype} H={H} HV={HV} "
+        f"t_max={t_max} seed={seed}")
+    assert ragged_plan_kernel(lengths, H, HV, slots, state_dtype == torch.bfloat16, L) == 5
+    c = synth.recurrent_case(seed, n_seqs=n, H=H, HV=HV, num_slots=slots, state_dtype=state_dtype, device=DEV,
+                             indices="random", lengths=lengths, null_rows=2, gate=gate, gate_dtype=gate_dtype)
+    c.state_indices[3] = slots + 2  # past the pool: null
+    st0 = c.state.clone()
+    want = reference(c, np_(st0), t_max=t_max, ragged=True, read_only=True)
+    out, corr, kg, _ = call(c, form="ragged", t_max=t_max, kg_dtype=torch.float32, read_only=True, max_seqlen=L)
+    assert torch.equal(P.bits(st0), P.bits(c.state)), "read-only pool changed"
+    e1 = P.check_bf16_out(out, want["out64"])
+    e2 = check_caches(corr, kg, want, recorded_mask(c, lengths, t_max))
+    say(f"out err {e1:.3e} corr err {e2:.3e}")
+
+
+def test_ragged_verify_sequence_longer_than_declared():
+    """A ragged read-only call declaring 4 tokens with one sequence of 7: its
+    first 4 tokens and every other sequence match the oracle; its tokens 4..6
+    give +0 and record nothing in the caches."""
+    lengths = [3, 7, 0, 4, 2]
+    n, H, slots, t_max = len(lengths), 4, 12, 8
+    say(f"ragged WY verify with a sequence past the declared length lengths={lengths} seed=7620")
+    c = synth.recurrent_case(7620, n_seqs=n, H=H, num_slots=slots, device=DEV, indices="random", lengths=lengths)
+    st0 = c.state.clone()
+    want = reference(c, np_(st0), t_max=t_max, ragged=True, read_only=True)
+    out, corr, kg, _ = call(c, form="ragged", t_max=t_max, kg_dtype=torch.float32, read_only=True, max_seqlen=4)
+    cu = c.cu_seqlens.cpu().numpy()
+    over = np.zeros(int(cu[-1]), bool)
+    over[cu[1] + 4:cu[2]] = True  # tokens 4..6 of sequence 1
+    o = out.reshape(-1, H, D)
+    assert not P.bits(o[torch.from_numpy(over).to(DEV)]).any(), "tokens past the declared length must be +0"
+    P.check_bf16_out(o[torch.from_numpy(~over).to(DEV)], want["out64"][~over])
+    recorded = [min(x, 4) for x in lengths]
+    check_caches(corr, kg, {"corr": want["corr"], "kg": want["kg"]}, recorded_mask(c, recorded, t_max))
+    assert torch.equal(P.bits(st0), P.bits(c.state))
+
+
+def test_wy_verify_t16_with_underflowing_decay():
+    """Sixteen tokens with log-decays of -20..-90 each: the cumulative decay
+    underflows within a token or two; outputs and corrections stay finite and
+    match the oracle (batched, bf16 pool)."""
+    T, n, H, slots = 16, 5, 4, 8
+    say(f"WY verify underflowing decay T={T} H={H} seed=7710")
+    c = synth.recurrent_case(7710, n_seqs=n, H=H, num_slots=slots, state_dtype=torch.bfloat16, device=DEV,
+                             indices="random", lengths=[T] * n, gate="precomputed", gate_dtype=torch.float32)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(7710)
+    c.g.copy_(-(20.0 + 70.0 * torch.rand(c.g.shape, generator=gen, device=DEV)))
+    st0 = c.state.clone()
+    want = reference(c, np_(st0), t_max=T, ragged=False, read_only=True, tps=T)
+    out, corr, kg, _ = call(c, form="batched", t_max=T, kg_dtype=torch.float32, read_only=True, tps=T)
+    assert torch.isfinite(out.float()).all() and torch.isfinite(corr).all()
+    P.check_bf16_out(out, want["out64"])
+    check_caches(corr, kg, want, recorded_mask(c, [T] * n, T))
