@@ -252,7 +252,7 @@ def rotating(torch, timer, calls, reps=8):
     return timer.run(graph.replay, reps) / len(calls)
 
 
-def extra_workloads(torch, dev, timer, pool32, only=None):
+def extra_workloads(torch, dev, timer, pool32, only=None, packed_b=None):
     from gated_delta_rule_decode_amd import (fused_kda_decode, packed_fused_kda_decode, packed_kda_decode,
                                              recurrent_kda, synth)
     out = {}
@@ -295,7 +295,7 @@ def extra_workloads(torch, dev, timer, pool32, only=None):
         pcase = synth.packed_case(2000, B=512, H=12, num_slots=8192, device=dev)
         pperm = torch.randperm(8192 - 1, generator=g2, device=dev).to(torch.int32) + 1
         sweep = []
-        for Bs in (1, 8, 16, 31, 32, 64, 128, 256, 512):
+        for Bs in packed_b or (1, 8, 16, 31, 32, 64, 128, 256, 512):
             nnull = Bs // 8
             o = torch.empty((Bs, 1, 12, D), dtype=torch.bfloat16, device=dev)
             calls = []
@@ -553,6 +553,9 @@ def main():
                     help="run only the extra workloads whose name contains this text (for profiling)")
     ap.add_argument("--copy-calibrate", action="store_true",
                     help="also run a 1 GiB device copy (for counter scaling under rocprofv3)")
+    ap.add_argument("--packed-b", default=None,
+                    help="comma-separated batch sizes of the packed H=12 bf16 sweep (default: all; "
+                         "the small sizes replay thousands of calls per cycle, too many for a counter pass)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -663,7 +666,8 @@ def main():
     }
 
     if not args.no_extra:
-        result["workloads"] = extra_workloads(torch, dev, timer, pool, args.extra_only)
+        packed_b = tuple(int(b) for b in args.packed_b.split(",")) if args.packed_b else None
+        result["workloads"] = extra_workloads(torch, dev, timer, pool, args.extra_only, packed_b)
 
     print(json.dumps(result), flush=True)
 
