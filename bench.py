@@ -252,7 +252,7 @@ def rotating(torch, timer, calls, reps=8):
     return timer.run(graph.replay, reps) / len(calls)
 
 
-def extra_workloads(torch, dev, timer, pool32, only=None, packed_b=None):
+def extra_workloads(torch, dev, timer, pool32, only=None, packed_b=None, packed_fused_n=None):
     from gated_delta_rule_decode_amd import (fused_kda_decode, packed_fused_kda_decode, packed_kda_decode,
                                              recurrent_kda, synth)
     out = {}
@@ -508,6 +508,9 @@ def extra_workloads(torch, dev, timer, pool32, only=None, packed_b=None):
         # token; disjoint checkpoint-slot sets per call
         pf = []
         for Hs, Ns_list in ((12, (1, 8, 32, 128)), (24, (8, 128))):
+            Ns_list = tuple(n for n in Ns_list if packed_fused_n is None or n in packed_fused_n)
+            if not Ns_list:
+                continue
             for sdt, sb in ((torch.float32, 4), (torch.bfloat16, 2)):
                 T = 5
                 pool_slots = 4 * 128 * T + 1
@@ -539,6 +542,38 @@ def extra_workloads(torch, dev, timer, pool32, only=None, packed_b=None):
     return out
 
 
+def stream_ceilings(torch, dev, timer):
+    """Reference HBM streams timed with PyTorch's own kernels on 1 GiB
+    working sets (GB/s of bytes moved): what a read-modify-write stream, a
+    write-only stream and the packed fused call's one read to five writes of
+    64 KiB blocks reach on this device without any of this library's code."""
+    n = 1 << 28  # fp32 elements: 1 GiB
+    a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
+    b = torch.empty_like(a)
+    res = {}
+
+    def rate(fn, nbytes, reps=10):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        return nbytes / (timer.run(fn, reps) * 1e-6) / 1e9
+
+    res["write_only_fill_GBps"] = rate(lambda: b.fill_(2.0), 4 * n)
+    res["copy_GBps"] = rate(lambda: b.copy_(a), 8 * n)
+    res["inplace_rmw_GBps"] = rate(lambda: a.mul_(1.0), 8 * n)
+    blk = 1 << 14  # fp32 elements: 64 KiB blocks
+    nblk = (n // 6) // blk
+    src = a[: nblk * blk].view(nblk, 1, blk)
+    dst = b[: nblk * 5 * blk].view(nblk, 5, blk) if 5 * nblk * blk <= n else None
+    if dst is not None:
+        res["one_read_five_writes_64KiB_GBps"] = rate(lambda: dst.copy_(src.expand(nblk, 5, blk)), 6 * 4 * nblk * blk)
+    del a, b
+    torch.cuda.empty_cache()
+    for k, v in res.items():
+        log(f"ceiling {k}: {v:.0f}")
+    return res
+
+
 # ------------------------------------------------------------------ main ----
 
 def main():
@@ -553,6 +588,11 @@ def main():
                     help="run only the extra workloads whose name contains this text (for profiling)")
     ap.add_argument("--copy-calibrate", action="store_true",
                     help="also run a 1 GiB device copy (for counter scaling under rocprofv3)")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="also time reference HBM streams with PyTorch's own kernels (write-only, copy, "
+                         "in-place read-modify-write, one read to five writes in 64 KiB blocks)")
+    ap.add_argument("--packed-fused-n", default=None,
+                    help="comma-separated sequence counts of the packed fused sweep (default: all)")
     ap.add_argument("--packed-b", default=None,
                     help="comma-separated batch sizes of the packed H=12 bf16 sweep (default: all; "
                          "the small sizes replay thousands of calls per cycle, too many for a counter pass)")
@@ -632,6 +672,8 @@ def main():
         log(f"copy 1 GiB -> 1 GiB: {cus:.1f} us, {2 * (1 << 30) / (cus * 1e-6) / 1e9:.0f} GB/s")
         del src, dst
 
+    ceilings = stream_ceilings(torch, dev, timer) if args.ceilings else None
+
     traffic_bytes = load_traffic(bytes_launch)
     plan = launch_plan(c, idx, pool, out, B, H)
     result = {
@@ -664,10 +706,13 @@ def main():
                                           "nontemporal dwordx4 (measured on this MI355X)"},
         "cpu_baseline": cpu,
     }
+    if ceilings is not None:
+        result["ceilings"] = ceilings
 
     if not args.no_extra:
         packed_b = tuple(int(b) for b in args.packed_b.split(",")) if args.packed_b else None
-        result["workloads"] = extra_workloads(torch, dev, timer, pool, args.extra_only, packed_b)
+        packed_fused_n = tuple(int(n) for n in args.packed_fused_n.split(",")) if args.packed_fused_n else None
+        result["workloads"] = extra_workloads(torch, dev, timer, pool, args.extra_only, packed_b, packed_fused_n)
 
     print(json.dumps(result), flush=True)
 
