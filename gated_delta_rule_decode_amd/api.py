@@ -84,7 +84,7 @@ def prepare(fn, *args, **kwargs):
         call = fn(*args, **kwargs)
     finally:
         _PREPARING.on = False
-    _need(isinstance(call, PreparedCall), f"{getattr(fn, '__name__', fn)} cannot be prepared")
+    _need(isinstance(call, PreparedCall), lambda: f"{getattr(fn, '__name__', fn)} cannot be prepared")
     call._keep = (args, kwargs, call._keep)
     return call
 
@@ -100,8 +100,10 @@ def _run(name, a, dev, output, keep=()):
 
 
 def _need(cond, msg):
+    """Raise ValueError(msg) unless cond; msg may be a callable that builds
+    the message (so that a passing check formats nothing)."""
     if not cond:
-        raise ValueError(msg)
+        raise ValueError(msg() if callable(msg) else msg)
 
 
 def _state_dtype(state):
@@ -121,24 +123,28 @@ def _check_devices(ref, **named):
     """ref and every non-None tensor in ``named`` on ref's device, which must
     be a HIP device.  Returns that device."""
     dev = ref.device
-    _need(dev.type == _DEVICE_TYPE, f"tensors must be on a HIP ({_DEVICE_TYPE}) device, got {dev}")
+    _need(dev.type == _DEVICE_TYPE, lambda: f"tensors must be on a HIP ({_DEVICE_TYPE}) device, got {dev}")
+    # (on a HIP device: is_cuda and the device index, both plain attributes,
+    # rather than a torch.device object per tensor)
+    hip, index = dev.type == "cuda", ref.get_device()
     for name, t in named.items():
         if t is not None:
-            _need(isinstance(t, torch.Tensor) and t.device == dev, f"{name} must be a tensor on {dev}, "
+            _need(isinstance(t, torch.Tensor) and ((t.is_cuda and t.get_device() == index) if hip else t.device == dev),
+                  lambda: f"{name} must be a tensor on {dev}, "
                   f"got {t.device if isinstance(t, torch.Tensor) else type(t).__name__}")
     return dev
 
 
 def _check_pool(state, H):
     _need(state.dim() == 4 and tuple(state.shape[1:]) == (H, D, D),
-          f"state must be [num_slots, {H}, 128, 128], got {tuple(state.shape)}")
+          lambda: f"state must be [num_slots, {H}, 128, 128], got {tuple(state.shape)}")
     _need(state.stride(3) == 1 and state.stride(2) == D and state.stride(1) == D * D,
           "each slot's [H, 128, 128] block must be contiguous")
 
 
 def _check_indices(idx, n):
     _need(idx.dtype == torch.int32 and idx.is_contiguous() and idx.numel() == n,
-          f"state_indices must be a contiguous int32 tensor with {n} elements")
+          lambda: f"state_indices must be a contiguous int32 tensor with {n} elements")
 
 
 def _gate_mode(lower_bound):
@@ -162,25 +168,25 @@ def _tokens(t, name, heads, width, ragged):
     Accepted: [T, ...]; [B, T, ...] (T tokens per sequence, T=1 is plain
     decode; the [B, T] dims must collapse to one stride); [1, T, ...] with
     cu_seqlens."""
+    shape, st = t.shape, t.stride()
     inner = 1 if width is None else 2
     if width is None:
-        _need(t.shape[-1] == heads and t.stride(-1) == 1, f"{name} must end in a contiguous [{heads}] dim")
+        _need(shape[-1] == heads and st[-1] == 1, lambda: f"{name} must end in a contiguous [{heads}] dim")
     else:
-        _need(t.shape[-1] == width and t.shape[-2] == heads and t.stride(-1) == 1
-              and t.stride(-2) == width, f"{name} must end in a contiguous [{heads}, {width}] block")
-    lead = tuple(t.shape[:-inner])
-    strides = t.stride()[:len(lead)]
-    if len(lead) == 1:
-        return lead[0], 1, strides[0]
-    _need(len(lead) == 2, f"{name} has an unsupported rank")
-    B, T = lead
+        _need(shape[-1] == width and shape[-2] == heads and st[-1] == 1 and st[-2] == width,
+              lambda: f"{name} must end in a contiguous [{heads}, {width}] block")
+    nlead = len(shape) - inner
+    if nlead == 1:
+        return shape[0], 1, st[0]
+    _need(nlead == 2, lambda: f"{name} has an unsupported rank")
+    B, T = shape[0], shape[1]
     if ragged:
-        _need(B == 1, f"{name} must be [1, T, ...] with cu_seqlens")
-        return T, 1, strides[1]
+        _need(B == 1, lambda: f"{name} must be [1, T, ...] with cu_seqlens")
+        return T, 1, st[1]
     if T == 1:
-        return B, 1, strides[0]
-    _need(strides[0] == T * strides[1], f"{name}: the [B, T] dims must collapse to one token stride")
-    return B * T, T, strides[1]
+        return B, 1, st[0]
+    _need(st[0] == T * st[1], lambda: f"{name}: the [B, T] dims must collapse to one token stride")
+    return B * T, T, st[1]
 
 
 def recurrent_kda(q, k, v, g, beta, A_log=None, dt_bias=None, *, initial_state, state_indices,
@@ -231,12 +237,12 @@ def recurrent_kda(q, k, v, g, beta, A_log=None, dt_bias=None, *, initial_state, 
         _need(cu_seqlens.dtype == torch.int32 and cu_seqlens.is_contiguous() and cu_seqlens.numel() == N + 1,
               "cu_seqlens must be a contiguous int32 tensor with N+1 elements")
     for name, t in (("q", q), ("k", k), ("v", v)):
-        _need(t.dtype == torch.bfloat16, f"{name} must be a bf16 tensor")
+        _need(t.dtype == torch.bfloat16, lambda: f"{name} must be a bf16 tensor")
     T, tps, sq = _tokens(q, "q", H, D, ragged)
     views = [_tokens(t, n, hh, D, ragged) for n, t, hh in (("k", k, H), ("v", v, HV), ("g", g, HV))]
     views.append(_tokens(beta, "beta", HV, None, ragged))
     for (Tn, tpn, _), n in zip(views, ("k", "v", "g", "beta")):
-        _need(Tn == T and tpn == tps, f"{n} does not have the token layout of q")
+        _need(Tn == T and tpn == tps, lambda: f"{n} does not have the token layout of q")
     if ragged and n_tokens is not None:
         T = int(n_tokens)
     if ragged:
@@ -272,7 +278,7 @@ def recurrent_kda(q, k, v, g, beta, A_log=None, dt_bias=None, *, initial_state, 
             continue
         _need(c.is_contiguous() and c.dim() == 4 and c.shape[0] == state.shape[0]
               and c.shape[1] == HV and c.shape[3] == w,
-              f"{name} must be contiguous [num_slots, HV, T_max, {w}]")
+              lambda: f"{name} must be contiguous [num_slots, HV, T_max, {w}]")
         _need(t_max is None or c.shape[2] == t_max, "the verify caches must share T_max")
         t_max = c.shape[2]
     if correction_cache is not None:
@@ -352,7 +358,7 @@ def packed_kda_decode(mixed_qkv, raw_gate, raw_beta, A_log, dt_bias, state, stat
 def _fused_inputs(x, weight, conv_state, raw_gate, raw_beta, A_log, dt_bias, state, output_gate,
                   norm_weight, norm_eps, output):
     """Checks shared by the fused calls; returns (H, rows, raw_gate, raw_beta,
-    output_gate as [rows, width] views, output)."""
+    output_gate as (address, row stride) pairs, output)."""
     _check_devices(x, weight=weight, conv_state=conv_state, raw_gate=raw_gate, raw_beta=raw_beta, A_log=A_log,
                    dt_bias=dt_bias, state=state, output_gate=output_gate, norm_weight=norm_weight, output=output)
     H = A_log.numel()
@@ -370,11 +376,14 @@ def _fused_inputs(x, weight, conv_state, raw_gate, raw_beta, A_log, dt_bias, sta
     _need(conv_state.shape[0] == state.shape[0], "state and conv_state must have the same num_slots")
 
     def rows2d(t, name, width):
-        _need(t.dtype == torch.bfloat16, f"{name} must be bf16")
-        t2 = t.reshape(rows, width) if t.is_contiguous() else t
-        _need(t2.dim() == 2 and tuple(t2.shape) == (rows, width) and t2.stride(1) == 1,
-              f"{name} must be [rows, {width}] with a contiguous inner dimension")
-        return t2
+        """(address, row stride) of a [rows, width] bf16 input (any contiguous
+        tensor of rows*width elements, or a 2-D one with contiguous rows)."""
+        _need(t.dtype == torch.bfloat16, lambda: f"{name} must be bf16")
+        if t.is_contiguous() and t.numel() == rows * width:
+            return _ptr(t), width
+        _need(t.dim() == 2 and tuple(t.shape) == (rows, width) and t.stride(1) == 1,
+              lambda: f"{name} must be [rows, {width}] with a contiguous inner dimension")
+        return _ptr(t), t.stride(0)
 
     rg = rows2d(raw_gate, "raw_gate", HC)
     rb = rows2d(raw_beta, "raw_beta", H)
@@ -416,14 +425,14 @@ def fused_kda_decode(x, weight, conv_state, raw_gate, raw_beta, A_log, dt_bias, 
     a.x, a.x_stride = _ptr(x), x.stride(0)
     a.weight = _ptr(weight)
     a.conv_state, a.conv_slot_stride = _ptr(conv_state), conv_state.stride(0)
-    a.raw_gate, a.gate_stride = _ptr(rg), rg.stride(0)
-    a.raw_beta, a.beta_stride = _ptr(rb), rb.stride(0)
+    a.raw_gate, a.gate_stride = rg
+    a.raw_beta, a.beta_stride = rb
     a.A_log, a.dt_bias = _ptr(A_log), _ptr(dt_bias)
     a.gate_mode, a.lower_bound = gm, lb
     a.state_indices = _ptr(state_indices)
     a.state, a.state_dtype = _ptr(state), _state_dtype(state)
     a.num_slots, a.slot_stride = state.shape[0], state.stride(0)
-    a.output_gate, a.ogate_stride = _ptr(og), og.stride(0)
+    a.output_gate, a.ogate_stride = og
     a.norm_weight, a.norm_eps = _ptr(norm_weight), float(norm_eps)
     a.out = _ptr(output)
     return _run("kda_fused_decode", a, x.device, output)
@@ -493,7 +502,7 @@ def _packed_fused_args(x, weight, conv_state, raw_gate, raw_beta, A_log, dt_bias
     N, max_tokens = si.shape
     for name, t, n in (("query_start_loc", query_start_loc, N + 1), ("num_accepted_tokens", num_accepted_tokens, N)):
         _need(t.dtype == torch.int32 and t.is_contiguous() and t.numel() == n,
-              f"{name} must be a contiguous int32 tensor with {n} elements")
+              lambda: f"{name} must be a contiguous int32 tensor with {n} elements")
     gm, lb = _gate_mode(lower_bound)
     a = _lib.PackedFusedArgs()
     a.struct_size = ctypes.sizeof(_lib.PackedFusedArgs)
@@ -501,15 +510,15 @@ def _packed_fused_args(x, weight, conv_state, raw_gate, raw_beta, A_log, dt_bias
     a.x, a.x_stride = _ptr(x), x.stride(0)
     a.weight = _ptr(weight)
     a.conv_state, a.conv_slot_stride = _ptr(conv_state), conv_state.stride(0)
-    a.raw_gate, a.gate_stride = _ptr(rg), rg.stride(0)
-    a.raw_beta, a.beta_stride = _ptr(rb), rb.stride(0)
+    a.raw_gate, a.gate_stride = rg
+    a.raw_beta, a.beta_stride = rb
     a.A_log, a.dt_bias = _ptr(A_log), _ptr(dt_bias)
     a.gate_mode, a.lower_bound = gm, lb
     a.state_indices, a.indices_stride = _ptr(si), si.stride(0)
     a.query_start_loc, a.num_accepted_tokens = _ptr(query_start_loc), _ptr(num_accepted_tokens)
     a.state, a.state_dtype = _ptr(state), _state_dtype(state)
     a.num_slots, a.slot_stride = state.shape[0], state.stride(0)
-    a.output_gate, a.ogate_stride = _ptr(og), og.stride(0)
+    a.output_gate, a.ogate_stride = og
     a.norm_weight, a.norm_eps = _ptr(norm_weight), float(norm_eps)
     a.out = _ptr(output)
     return a, output, N, H, rows
