@@ -1597,25 +1597,11 @@ __global__ void __launch_bounds__(256) kda_verify_chunk_kernel(const RecParams p
 // q*exp(cumsum g) operands of a product with the state), which equals T
 // sequential steps up to rounding.
 //
-//  * The state goes straight from HBM into LDS (global_load_lds_dwordx4, no
-//    VGPRs): each wave moves its own 32 value rows, whole rows per 1 KiB
-//    instruction, and only waits for its own loads.  The 16-byte column c of
-//    row r lands at column c ^ (r & 15) (the lane order of the load chooses
-//    the global address of each LDS slot), so that the matrix-core operand
-//    reads, 16 rows at one column, fall on distinct banks.
-//  * The products [k_t E_t ; q_t E_t] x S0 (2T x 128 by 128 x 128 per head)
-//    run on the matrix cores: fp32 pools with fp32 MFMAs, bf16 pools with
-//    bf16 MFMAs on the exact state and the fp32 token operand split into a
-//    bf16 head and remainder (two products, ~2^-17 relative).
-//  * Overlapping the state loads, every channel's cumulative decay is
-//    evaluated once, and the T^2 W-weighted channel sums (and the norms) are
-//    split over the two wave pairs and reduced over each wave in registers.
-//  * Each wave then solves the forward substitution for its own rows (two
-//    lanes per row) from its own products: no barrier after the products
-//    other than the one that publishes the coefficients.
-// TM (2, 4, 8 or 16, the smallest that holds the declared length) sizes the
-// token registers and LDS; with TM = 16 an fp32 workgroup takes 77 KB of LDS,
-// two per CU.  Null rows give +0; in the ragged form, tokens past the
+// The products [k_t E_t ; q_t E_t] x S0 (2T x 128 by 128 x 128 per head) run
+// on the matrix cores; the T^2 W-weighted channel sums are reduced once per
+// head; each value row then runs a T-step forward substitution.  TM (2, 4, 8
+// or 16, the smallest that holds the declared length) sizes the token
+// registers and LDS.  Null rows give +0; in the ragged form, tokens past the
 // declared length give +0 and record nothing.
 constexpr int pow2_at_least(int x)
 {
@@ -1735,38 +1721,32 @@ struct WyLayout {
 // two 16-row tiles.
 //  1. The token inputs of the lane's key channel are loaded before the pool
 //     slot is known, and the lane's value row.
-//  2. Each wave loads its first tile straight into registers, in the layout
-//     the matrix cores take (16 rows x 64 contiguous bytes per load), and
-//     its second tile from HBM into its own LDS tile buffer (both streamed:
-//     non-temporal)
-//     (global_load_lds_dwordx4: whole rows, 1 KiB per instruction, no VGPRs;
-//     the 16-byte column c of row r lands at column c ^ (r & 15), so that
-//     the operand reads, 16 rows at one column, fall on distinct banks).
-//     Meanwhile the key channels, one per lane (waves 0-1 layout A with q,
-//     waves 2-3 layout B with k): cumulative decays, the token operand
-//     column of the channel (q_t E_t, or k_t E_t; zero past the tokens)
-//     into LDS once for the head (bf16 pools: as a bf16 head and
-//     remainder), and the W-weighted channel sums, each reduced over the
-//     wave in registers; one barrier.
+//  2. Each wave loads its first 16-row tile straight into registers, in the
+//     layout the matrix cores take (16 rows x 64 contiguous bytes per load,
+//     non-temporal).  Meanwhile the key channels, one per lane (waves 0-1
+//     layout A with q, waves 2-3 layout B with k): cumulative decays, the
+//     token operand column of the channel (q_t E_t, or k_t E_t; zero past
+//     the tokens) into LDS once for the head (bf16 pools: as a bf16 head
+//     and remainder), and the W-weighted channel sums, each reduced over
+//     the wave in registers.  Then the loads of the second tile (its
+//     registers were the channel phase's), and one barrier.
 //  3. [k_t E_t ; q_t E_t] x S0 on the matrix cores, tile by tile (bf16
 //     pools: the exact state by the operand's head and remainder, two bf16
 //     products; fp32 pools: fp32 products), through LDS into a row-per-lane
 //     layout, then the forward substitution (lanes l and l + 32 own row
 //     l & 31 and store alternate tokens).
-// A workgroup holds one tile buffer per wave (8 KB fp32, 4 KB bf16) plus the
-// operand, sums and coefficients, so several share a compute unit and the
-// loads of one overlap the arithmetic of the others.  Consecutive heads
-// (which share their sequence's token rows) run on one XCD.
+// The state lives in registers only; the LDS holds the operand, the sums,
+// the coefficients and the products (14 KB for fp32 at TM = 4), so four to
+// five workgroups share a compute unit (the VGPRs decide) and the loads of
+// one overlap the arithmetic of the others.  Consecutive heads (which share
+// their sequence's token rows) run on one XCD.
 template <bool BF16, int TM>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TM <= 8 ? 4 : 2)))
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TM <= 4 ? 5 : (TM <= 8 ? 4 : 2))))
 kda_verify_wy_kernel(const RecParams p)
 {
     using LY = WyLayout<BF16>;
     constexpr int WROWS = 32;                    // value rows per wave
     constexpr uint32_t ROW_BYTES = KD * (BF16 ? 2 : 4);
-    constexpr int LPR = ROW_BYTES / 16;          // 16-byte columns per row
-    constexpr int RPI = 1024 / ROW_BYTES;        // rows per 1 KiB load instruction
-    constexpr int NTI = 16 * ROW_BYTES / 1024;   // load instructions per 16-row tile
     constexpr int NCT = (2 * TM + 15) / 16;      // 16-column tiles of the token operand
     constexpr int NCOL = 2 * TM;                 // columns: k_t E_t at t, q_t E_t at TM + t
     constexpr int OST = NCOL + 4;                // floats per row of the products in LDS
@@ -1775,12 +1755,10 @@ kda_verify_wy_kernel(const RecParams p)
     constexpr int NJ = LY::NJ;
     constexpr int SW = LY::SW;
     constexpr int NCF = 2 * TM * TM + 3 * TM;    // per-wave coefficients
-    constexpr int TBW = 16 * ROW_BYTES / 4;      // words of a tile
-    constexpr int BUFW = TBW > WROWS * OST ? TBW : WROWS * OST;
     constexpr int BST = BF16 ? KD / 2 + 4 : KD + 4;  // words per operand row (bf16: pairs), padded
     static_assert(TM <= VERIFY_WY_MAX_T, "verify tokens");
 
-    __shared__ __align__(16) uint32_t s_T[4][BUFW];          // per wave: a state tile, then the products
+    __shared__ __align__(16) uint32_t s_T[4][WROWS * OST];   // per wave: its rows' products
     __shared__ __align__(16) uint32_t s_B[BF16 ? 2 : 1][NCOL][BST];  // token operand (bf16: head, remainder)
     __shared__ float s_sum[2][2][64 * NCH];                   // channel sums: layout, half of the channels
     __shared__ float s_beta[TM];
@@ -1834,7 +1812,7 @@ kda_verify_wy_kernel(const RecParams p)
         return;
     }
 
-    // 2. the state: the first tile into registers, the second into the tile buffer
+    // 2. the state: the first tile into registers (the second follows the channel phase)
     uint32_t *buf = s_T[wave];
     const char *wrows = static_cast<const char *>(p.state) +
                         ((int64_t)it.idx * p.slot_stride + (int64_t)it.hv * (KD * KD)) * (BF16 ? 2 : 4) +
@@ -1851,17 +1829,6 @@ kda_verify_wy_kernel(const RecParams p)
     }
     // (the scheduling barriers keep other work, and the waits it would
     // bring, from landing between the loads of the tile)
-    __builtin_amdgcn_sched_barrier(0);
-    {
-        const char *src = wrows + 16 * ROW_BYTES;
-#pragma unroll
-        for (int i = 0; i < NTI; ++i) {
-            const int r = RPI * i + lane / LPR;
-            const int col = (lane % LPR) ^ (r & 15);
-            __builtin_amdgcn_global_load_lds(src + r * ROW_BYTES + 16 * col, buf + i * 256, 16, 0, 2 /* nt */);
-        }
-    }
-    __builtin_amdgcn_sched_barrier(0);
 
     // the key channel: decays, the operand column, the channel sums
     {
@@ -1917,6 +1884,16 @@ kda_verify_wy_kernel(const RecParams p)
             s_beta[lane] = precomputed ? bv : sigmoid_f(bv);
         }
     }
+    uint32_t st1[NJ][SW];  // the second tile
+    {
+        const char *row = wrows + (int64_t)(16 + n16) * ROW_BYTES;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const u32x4 w = __builtin_nontemporal_load(
+                reinterpret_cast<const u32x4 *>(row + LY::channel(j, grp) * (BF16 ? 2 : 4)));
+            st1[j][0] = w.x; st1[j][1] = w.y; st1[j][2] = w.z; st1[j][3] = w.w;
+        }
+    }
     __syncthreads();
 
     // coefficients (each wave its own copy): (t, s) = (e / TM, e % TM);
@@ -1948,7 +1925,7 @@ kda_verify_wy_kernel(const RecParams p)
     // 3. the products, tile by tile: column cc = 16 kc + (lane & 15) of the
     // operand at the lane's channels (zero past the 2 TM columns)
     f32x4 acc[2][NCT];
-    auto tile_products = [&](int tau) {
+    auto tile_products = [&](int tau, const uint32_t (&sa)[NJ][SW]) {
 #pragma unroll
         for (int kc = 0; kc < NCT; ++kc) acc[tau][kc] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1962,7 +1939,7 @@ kda_verify_wy_kernel(const RecParams p)
                     u32x4 bh = *reinterpret_cast<const u32x4 *>(&s_B[0][ccr][ch / 2]);
                     u32x4 bl = *reinterpret_cast<const u32x4 *>(&s_B[1][ccr][ch / 2]);
                     if (cc >= NCOL) bh = bl = u32x4{0u, 0u, 0u, 0u};
-                    const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{st[j][0], st[j][1], st[j][2], st[j][3]});
+                    const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{sa[j][0], sa[j][1], sa[j][2], sa[j][3]});
                     acc[tau][kc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, bh),
                                                                           acc[tau][kc], 0, 0, 0);
                     acc[tau][kc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, bl),
@@ -1972,28 +1949,17 @@ kda_verify_wy_kernel(const RecParams p)
                     if (cc >= NCOL) b = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        acc[tau][kc] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(st[j][e]), b[e],
+                        acc[tau][kc] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(sa[j][e]), b[e],
                                                                            acc[tau][kc], 0, 0, 0);
                 }
             }
         }
     };
-    tile_products(0);
-    wait_vm_all();  // the second tile has landed in this wave's buffer
-    {
-        const uint32_t *row = buf + n16 * (ROW_BYTES / 4);
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-            const int col = LY::channel(j, grp) / (BF16 ? 8 : 4);
-            const u32x4 w = *reinterpret_cast<const u32x4 *>(row + 4 * (col ^ n16));
-            st[j][0] = w.x; st[j][1] = w.y; st[j][2] = w.z; st[j][3] = w.w;
-        }
-    }
-    tile_products(1);
+    tile_products(0, st);
+    tile_products(1, st1);
 
-    // the products to LDS (the tile buffer: every read of it is done, and a
-    // wave's LDS accesses are performed in order): row 16 tau + 4 g + r,
-    // column 16 kc + (lane & 15)
+    // the products to LDS, this wave's rows: row 16 tau + 4 g + r, column
+    // 16 kc + (lane & 15)
     float *prod = reinterpret_cast<float *>(buf);
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau)
