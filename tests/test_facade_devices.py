@@ -140,3 +140,36 @@ def test_prepared_call_launches_the_eager_struct(make, monkeypatch):
     assert rec.calls[2] == rec.calls[0], "the prepared struct differs from the eager one"
     held = [t for t in args.values() if isinstance(t, torch.Tensor)]
     assert all(any(t is k for k in call._keep[1].values()) for t in held)
+
+
+def test_max_seqlen_is_the_ragged_calls_declared_bound(monkeypatch):
+    """``max_seqlen`` (the longest sequence a ragged read-only call declares,
+    which selects the matrix-product verify form) reaches the library as
+    tokens_per_seq; without it a ragged call passes 0 (undeclared); it is
+    refused on the batched form and when negative."""
+    rec = RecordingLib()
+    monkeypatch.setattr(_lib, "load", lambda *a, **k: rec)
+    monkeypatch.setattr(api, "_launch", lambda fn, ref, dev, stream=None: fn(ref))
+    fn, args, _ = _recurrent_args()
+    args = {k: v for k, v in args.items() if k not in ("intermediate_states",)}
+
+    def tps_of(**kw):
+        rec.calls.clear()
+        fn(**args, disable_state_update=True, **kw)
+        st = _lib.RecurrentArgs.from_buffer_copy(rec.calls[-1][1])
+        return st.tokens_per_seq, st.flags
+
+    assert tps_of() == (0, _lib.FLAG_NO_STATE_UPDATE)
+    assert tps_of(max_seqlen=3) == (3, _lib.FLAG_NO_STATE_UPDATE)
+    assert tps_of(max_seqlen=16)[0] == 16
+    with pytest.raises(ValueError, match="max_seqlen"):
+        fn(**args, max_seqlen=-1)
+    c = synth.recurrent_case(5, n_seqs=2, H=2, num_slots=4, lengths=[3, 3])
+    r = lambda t: t.reshape(2, 3, *t.shape[1:])  # noqa: E731
+    batched = dict(q=r(c.q), k=r(c.k), v=r(c.v), g=r(c.g), beta=r(c.beta), A_log=c.A_log, dt_bias=c.dt_bias,
+                   initial_state=c.state, state_indices=c.state_indices)
+    with pytest.raises(ValueError, match="ragged"):
+        fn(**batched, max_seqlen=3)
+    rec.calls.clear()
+    fn(**batched, disable_state_update=True)
+    assert _lib.RecurrentArgs.from_buffer_copy(rec.calls[-1][1]).tokens_per_seq == 3
