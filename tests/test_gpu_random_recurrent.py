@@ -36,7 +36,7 @@ def np_(t):
     return None if t is None else oracle.as_np(t.detach().cpu())
 
 
-@pytest.mark.parametrize("seed", range(16))
+@pytest.mark.parametrize("seed", range(24))
 def test_random_recurrent_calls(seed):
     rng = random.Random(6000 + seed)
     H = rng.choice([1, 2, 4, 8, 16])
@@ -54,9 +54,17 @@ def test_random_recurrent_calls(seed):
     t_max = rng.choice([0, 0, 2, 4]) if ragged else rng.choice([0, 1])
     kg_dtype = rng.choice([torch.float32, torch.bfloat16])
     null_rows = rng.randint(0, min(3, N - 1)) if N > 1 else 0
+    declared = None  # a read-only ragged call may declare its longest sequence (up to 16 take the WY product)
+    if ragged and read_only and rng.random() < 0.6:
+        if rng.random() < 0.5:
+            lengths = [rng.randint(0, 16) for _ in range(N)]
+            if sum(lengths) == 0:
+                lengths[0] = 1
+        declared = max(lengths) + rng.choice([0, 0, 1, 4])
     S = N + 8
     say(f"random recurrent seed={seed} H={H} HV={HV} N={N} lengths={lengths} {state_dtype} gate={gate}/"
-        f"{gate_dtype} read_only={read_only} ckpt={ckpt} t_max={t_max} null_rows={null_rows}")
+        f"{gate_dtype} read_only={read_only} ckpt={ckpt} t_max={t_max} null_rows={null_rows} "
+        f"max_seqlen={declared}")
     c = synth.recurrent_case(6000 + seed, n_seqs=N, H=H, HV=HV, num_slots=S, state_dtype=state_dtype, device=DEV,
                              indices="random", lengths=lengths, null_rows=null_rows, gate=gate,
                              gate_dtype=gate_dtype)
@@ -74,7 +82,7 @@ def test_random_recurrent_calls(seed):
     out = recurrent_kda(shp(c.q), shp(c.k), shp(c.v), shp(c.g), shp(c.beta), c.A_log, c.dt_bias,
                         initial_state=c.state, state_indices=c.state_indices,
                         cu_seqlens=c.cu_seqlens if ragged else None, intermediate_states=ck,
-                        disable_state_update=read_only, correction_cache=corr, kg_cache=kg)
+                        disable_state_update=read_only, correction_cache=corr, kg_cache=kg, max_seqlen=declared)
     torch.cuda.synchronize()
     P.check_bf16_out(out, want["out64"])
     if read_only:
@@ -104,14 +112,15 @@ def test_random_recurrent_calls(seed):
 
 @pytest.mark.parametrize("seed", range(12))
 def test_random_batched_calls(seed):
-    """The batched [B, T, ...] form with 2..10 tokens: read-only calls of up
-    to 8 tokens without checkpoints take the chunked matrix-core kernel, the
-    rest the token loop; both against the oracle with the same bars."""
+    """The batched [B, T, ...] form with 2..16 tokens: read-only calls
+    without checkpoints take a matrix-core kernel (the chunk kernel up to 4
+    tokens, the WY product beyond), the rest the token loop; all against the
+    oracle with the same bars."""
     rng = random.Random(6100 + seed)
     H = rng.choice([1, 2, 4, 8])
     HV = H * rng.choice([1, 2, 3])
     N = rng.randint(1, 20)
-    T = rng.randint(2, 10)
+    T = rng.randint(2, 16)
     state_dtype = rng.choice([torch.float32, torch.bfloat16])
     gate = rng.choice(["in_kernel", "precomputed"])
     gate_dtype = rng.choice([torch.float32, torch.bfloat16])
