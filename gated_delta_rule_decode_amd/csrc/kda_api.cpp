@@ -280,17 +280,13 @@ int prepare_recurrent(const kda_recurrent_args *a, RecParams *p, Launch *l)
     // Read-only calls without checkpoints whose sequences have at most
     // VERIFY_WY_MAX_T tokens (batched: T >= 2; ragged: the length the caller
     // declares in tokens_per_seq): the tokens' reads of the initial state
-    // become one matrix product per head.  Batched calls of up to
-    // VERIFY_CHUNK_MAX_T tokens take the chunked verify kernel, the others
-    // the WY verify kernel.
+    // become one matrix product per head, on the WY verify kernel.
     const int64_t bound = ragged ? a->tokens_per_seq : tps;
-    const bool chunk = !update && !a->checkpoints && bound >= (ragged ? 1 : 2) && bound <= VERIFY_WY_MAX_T;
-    const bool small = chunk && !ragged && tps <= VERIFY_CHUNK_MAX_T;
-    const int vsplit = chunk ? 1 : choose_vsplit(items, a->state_dtype == KDA_DTYPE_BF16, token_loop,
+    const bool wy = !update && !a->checkpoints && bound >= (ragged ? 1 : 2) && bound <= VERIFY_WY_MAX_T;
+    const int vsplit = wy ? 1 : choose_vsplit(items, a->state_dtype == KDA_DTYPE_BF16, token_loop,
                                                  a->checkpoints != nullptr && a->state_dtype == KDA_DTYPE_F32, update);
     if (items * vsplit > 0x7ffffff0LL) return fail(KDA_ERR_SHAPE, "too many work items");
-    l->family = small ? KERNEL_VERIFY_CHUNK : chunk ? KERNEL_VERIFY_WY
-              : token_loop ? KERNEL_RECURRENT_VARLEN : KERNEL_RECURRENT_T1;
+    l->family = wy ? KERNEL_VERIFY_WY : token_loop ? KERNEL_RECURRENT_VARLEN : KERNEL_RECURRENT_T1;
     l->vsplit = vsplit;
     l->rows_per_block = KD / vsplit;
     l->grid = (int32_t)((items * vsplit + 7) & ~7LL);  // padded to whole XCD rounds
@@ -323,7 +319,7 @@ int prepare_recurrent(const kda_recurrent_args *a, RecParams *p, Launch *l)
     p->H = a->H;
     p->HV = a->HV;
     p->group = a->HV / a->H;
-    p->tps = (int32_t)(chunk ? bound : tps);
+    p->tps = (int32_t)(wy ? bound : tps);
     p->g_f32 = a->g_dtype == KDA_DTYPE_F32;
     p->beta_f32 = a->beta_dtype == KDA_DTYPE_F32;
     p->precomputed = precomputed;

@@ -13,11 +13,9 @@ enum KernelFamily : int32_t {
     KERNEL_FUSED = 3,          // conv + SiLU -> KDA -> gated RMSNorm
     KERNEL_PACKED_FUSED = 4,   // the fused step over packed ragged rows, T >= 1 per sequence
     KERNEL_VERIFY_WY = 5,      // read-only calls, <= VERIFY_WY_MAX_T tokens per sequence: one MFMA product per head
-    KERNEL_VERIFY_CHUNK = 6,   // read-only batched calls, 2..VERIFY_CHUNK_MAX_T tokens: the same, smaller tiles
 };
 
 constexpr int VERIFY_WY_MAX_T = 16;   // tokens per sequence the WY verify kernel takes
-constexpr int VERIFY_CHUNK_MAX_T = 4;  // batched calls up to this many tokens take the chunked verify kernel
 
 // Recurrence over (sequence, value head, value slice) work items; serves
 // recurrent_kda (T=1, uniform batches, ragged T>=0, grouped value heads,

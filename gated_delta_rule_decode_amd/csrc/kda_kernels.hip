@@ -35,9 +35,8 @@
 //    exception: every token's product with the state is a product with the
 //    same initial state, so they run as one small matrix product per head on
 //    the matrix cores plus a forward substitution per value row
-//    (kda_verify_chunk_kernel for batched calls of up to 4 tokens,
-//    kda_verify_wy_kernel for longer and ragged ones; half of each wave's
-//    state rows go straight into registers, half through LDS).
+//    (kda_verify_wy_kernel; the state is read as whole rows and reaches the
+//    matrix-core layout through LDS).
 //  * The slot base is one 64-bit pointer per workgroup; everything inside a
 //    head is 32-bit offsets.
 //  * Null rows (index below the call's first live index, or >= num_slots)
@@ -1270,317 +1269,6 @@ __global__ void __launch_bounds__(2048 / (G * VS)) kda_packed_fused_kernel(const
     }
 }
 
-// --------------------------------------------- chunked verify kernel ----
-//
-// Read-only calls in the batched form ("Frozen / speculative-verify mode":
-// the pool is never written back) with 2..VERIFY_CHUNK_MAX_T tokens per
-// sequence and no checkpoints (longer and ragged calls take the WY verify
-// kernel below, which this one outruns at these lengths on MI355X).  Every token then reads the state through the
-// slot's initial state S0 (K x V), and the recurrence unrolls per value row.
-// With L_t the log-decay of tokens 0..t summed per key channel, E_t =
-// exp(L_t), W_ts = exp(L_t - L_s) (s <= t), k^ and q^ the L2-normalised key
-// and query and b_s = beta_s u_s:
-//   u_t = v_t - k^_t.(E_t * S0) - sum_{s<t} (k^_t . W_ts k^_s) b_s
-//   o_t = scale [ q^_t.(E_t * S0) + sum_{s<=t} (q^_t . W_ts k^_s) b_s ]
-// which equals T sequential steps up to rounding.  The products with S0 are
-// one matrix product per head: the 16 x 128 matrix of rows k_t*E_t (rows t)
-// and q_t*E_t (rows TM+t), zero-padded, times S0, on the fp32 matrix cores
-// (16x16x4 MFMA); the T x T coefficients are reduced once per head and the
-// rest is a forward substitution per value row.  This replaces T passes of
-// vector arithmetic over the whole state.  TM, the token slots the kernel
-// is built for (2 or 4, the smallest that holds T; it also holds 8), sizes
-// the input registers and LDS: with TM = 4 an fp32 workgroup fits in 108
-// VGPRs and 40 KB of LDS, four workgroups per CU instead of three.
-//
-// Layout: wave w owns value rows 32w..32w+31 as two 16-row tiles.  MFMA
-// lane l supplies row (l & 15) of a tile and K slot (l >> 4); the K order
-// inside the product is free, so lane l feeds the MFMAs (jj, e) with key
-// channel jj*4*VPL + (l>>4)*VPL + e, the e-th value of 16 contiguous bytes.
-// Loading a tile in that order reads 16 rows x 64 bytes per instruction,
-// which streams worse from HBM than whole rows; loading whole rows and
-// transposing through LDS costs LDS bandwidth instead.  Each wave does one
-// of each (tile 0 direct, tile 1 through its LDS buffer, the 16-byte
-// columns of row r stored at column ^ (r & 15), so the 16 rows of one read
-// fall on distinct banks without padding): measured faster than either
-// alone, as the two costs overlap.  The B operand uses the same
-// channel order from LDS.  MFMA outputs: lane l holds rows 4*(l>>4) + r of
-// the tile at column (l & 15).
-template <bool BF16, int TM>
-__global__ void __launch_bounds__(256) kda_verify_chunk_kernel(const RecParams p)
-{
-    constexpr int VPL = BF16 ? 8 : 4;       // state values per 16-byte access
-    constexpr int NJ = 32 / VPL;            // 16-byte accesses per lane and tile
-    constexpr uint32_t ROW_BYTES = KD * (BF16 ? 2 : 4);
-    constexpr int NS = 2 + 2 * TM;          // sums per token: |q|^2, |k|^2, q.W k_s, k.W k_s
-    static_assert(TM <= 8, "k and q rows of the 16-column operand");
-    constexpr int RSW = ROW_BYTES / 4;      // words per tile row in LDS
-    // operand rows k_t*E_t (t), q_t*E_t (TM + t), rows past 2 TM zero; padded
-    // by 16 bytes so that the 16 rows read by one instruction spread over the
-    // banks
-    __shared__ float s_B[2 * TM][KD + 4];
-    constexpr int OSTR = 20;                // floats per row of the MFMA outputs in LDS (16 + 4 padding)
-    // fp32 pools at 8 token slots transpose tile 1 in two halves of K (its
-    // loads issued after the staging): a quarter of the LDS and fewer VGPRs,
-    // so four workgroups fit per CU instead of three
-    constexpr bool HALF = !BF16 && TM == 8;
-    constexpr int LPR = ROW_BYTES / 16;     // lanes per row
-    constexpr int RPA = 64 / LPR;           // rows per access
-    constexpr int HC = LPR / 2;             // 16-byte columns per half row
-    constexpr int HRW = 4 * HC;             // words per half row
-    constexpr int BUFW = HALF ? (16 * HRW > 32 * OSTR ? 16 * HRW : 32 * OSTR) : 16 * RSW;
-    // per wave: one state tile, or half of one, (16-byte columns XOR-swizzled
-    // by row), then the wave's MFMA outputs
-    __shared__ uint32_t s_T[4][BUFW];
-    __shared__ float s_v[TM][KD];
-    __shared__ float s_part[8][TM * NS];    // [DPP row of the staging waves][token * NS + sum]
-    __shared__ float s_sum[TM][NS];
-    __shared__ float s_beta[TM];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int work = (int)(blockIdx.x & 7u) * (int)(gridDim.x >> 3) + (int)(blockIdx.x >> 3);
-    if (work >= p.n_work) return;
-    const int seq = work / p.HV;
-    const int hv = work - seq * p.HV;
-    const int hq = hv / p.group;
-    const int T = p.tps;
-    const int64_t tok0 = (int64_t)seq * T;
-    const int c = tid & (KD - 1);
-    const bool g_f32 = p.g_f32 != 0;
-    const bool beta_f32 = p.beta_f32 != 0;
-    const bool precomputed = p.precomputed != 0;
-    const int g_es = g_f32 ? 4 : 2;
-    const int b_es = beta_f32 ? 4 : 2;
-
-    // Token inputs first: waves 0-1 take q, k and the gate of channel c,
-    // waves 2-3 v of channel c, and lanes t < T of wave 2 the beta of token t.
-    uint32_t xa[TM], xb[TM], glo[TM], ghi[TM];
-    uint32_t blo = 0, bhi = 0;
-#pragma unroll
-    for (int t = 0; t < TM; ++t) {
-        const int64_t n = tok0 + min(t, T - 1);
-        if (tid < KD) {
-            xa[t] = p.q[n * p.q_stride + (int64_t)hq * KD + c];
-            xb[t] = p.k[n * p.k_stride + (int64_t)hq * KD + c];
-            load_halves(static_cast<const char *>(p.g) + (n * p.g_stride + (int64_t)hv * KD + c) * g_es, g_f32,
-                        glo[t], ghi[t]);
-        } else {
-            xa[t] = p.v[n * p.v_stride + (int64_t)hv * KD + c];
-        }
-    }
-    if (wave == 2 && lane < T)
-        load_halves(static_cast<const char *>(p.beta) + ((tok0 + lane) * p.beta_stride + hv) * b_es, beta_f32, blo,
-                    bhi);
-    const float a_h = precomputed ? 0.f : __expf(p.A_log[hv]);
-    const float dtc = precomputed ? 0.f : p.dt_bias[(int64_t)hv * KD + c];
-
-    const int idx = p.state_indices[seq];
-    if (idx < 0 || (int64_t)idx >= p.num_slots) {
-        for (int i = tid; i < T * KD; i += 256)
-            p.out[((tok0 + i / KD) * p.HV + hv) * KD + (i & (KD - 1))] = 0;
-        return;
-    }
-    const char *head = static_cast<const char *>(p.state) +
-                       ((int64_t)idx * p.slot_stride + (int64_t)hv * (KD * KD)) * (BF16 ? 2 : 4);
-    __builtin_amdgcn_sched_barrier(0);
-
-    // This wave's two 16-row state tiles: tile 0 in the MFMA order (access jj
-    // of lane l: 16 bytes of row l & 15 at byte 64*jj + 16*(l >> 4)), tile 1
-    // coalesced (access jj covers RPA whole rows, 1 KiB).
-    const int n16 = lane & 15;
-    const int grp = lane >> 4;
-    const int lrow = lane / LPR;
-    const int lcol = lane % LPR;
-    u32x4 raw[2][NJ];
-#pragma unroll
-    for (int jj = 0; jj < NJ; ++jj)
-        raw[0][jj] = ld_nt<u32x4>(head, (uint32_t)(32 * wave + n16) * ROW_BYTES + 64u * jj + 16u * grp);
-    auto load_tile1 = [&]() {
-#pragma unroll
-        for (int jj = 0; jj < NJ; ++jj)
-            raw[1][jj] = ld_nt<u32x4>(head, (uint32_t)(32 * wave + 16 + RPA * jj + lrow) * ROW_BYTES + 16u * lcol);
-    };
-    if constexpr (!HALF) load_tile1();
-    __builtin_amdgcn_sched_barrier(0);
-
-    if (tid < KD) {
-        // B operand rows, the cumulative log-decay, and the per-token sums
-        // reduced over the head's 128 channels (one partial per wave).
-        float qf[TM], kf[TM], Lt[TM];
-        float L = 0.f;
-#pragma unroll
-        for (int t = 0; t < TM; ++t) {
-            qf[t] = bf16_bits_to_f32(xa[t]);
-            kf[t] = bf16_bits_to_f32(xb[t]);
-            const float gv = halves_value(glo[t], ghi[t], g_f32);
-            L += precomputed ? gv : -a_h * softplus_f(gv + dtc);
-            Lt[t] = L;
-            const float E = __expf(L);
-            s_B[t][c] = t < T ? kf[t] * E : 0.f;  // rows past the last token are zero
-            s_B[TM + t][c] = t < T ? qf[t] * E : 0.f;
-        }
-#pragma unroll
-        for (int t = 0; t < TM; ++t) {
-            if (t < T) {
-                float v[NS];
-                v[0] = qf[t] * qf[t];
-                v[1] = kf[t] * kf[t];
-#pragma unroll
-                for (int s = 0; s <= t; ++s) {
-                    const float w = s == t ? 1.f : __expf(Lt[t] - Lt[s]);
-                    v[2 + s] = qf[t] * kf[s] * w;
-                    if (s < t) v[2 + TM + s] = kf[t] * kf[s] * w;
-                }
-#pragma unroll
-                for (int j = 0; j < NS; ++j) {
-                    if (j < 2 || (j < 2 + TM && j - 2 <= t) || (j >= 2 + TM && j - 2 - TM < t)) {
-                        const float r = row_sum16(v[j]);
-                        if ((lane & 15) == 0) s_part[tid >> 4][t * NS + j] = r;
-                    }
-                }
-                if (p.kg && t < p.t_max) {
-                    StageIn si{};
-                    si.k = xb[t];
-                    si.g_lo = glo[t];
-                    si.g_hi = ghi[t];
-                    store_kg(p.kg, p.kg_f32 != 0, ((int64_t)idx * p.HV + hv) * p.t_max + t, c, si, g_f32);
-                }
-            }
-        }
-    } else {
-#pragma unroll
-        for (int t = 0; t < TM; ++t)
-            if (t < T) s_v[t][c] = bf16_bits_to_f32(xa[t]);
-        if (wave == 2 && lane < T) {
-            const float b = halves_value(blo, bhi, beta_f32);
-            s_beta[lane] = precomputed ? b : sigmoid_f(b);
-        }
-    }
-    if constexpr (HALF) {
-        // tile 1 after the staging, whose registers are free by now
-        __builtin_amdgcn_sched_barrier(0);
-        load_tile1();
-    }
-    __syncthreads();
-
-    // The per-token sums: one thread per (token, sum) adds the 8 partials.
-    if (tid < T * NS) {
-        const int t = tid / NS, j = tid - (tid / NS) * NS;
-        float r = 0.f;
-#pragma unroll
-        for (int w = 0; w < 8; ++w) r += s_part[w][tid];
-        s_sum[t][j] = r;
-    }
-
-    // [k_t*E_t ; q_t*E_t] x S0 for this wave's two tiles, tile 1 transposed
-    // into the A-operand order through the wave's LDS buffer.
-    uint32_t *tile = s_T[wave];
-    f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-    if constexpr (HALF) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            // Half h of tile 1 (16-byte columns [h*HC, (h+1)*HC) of every row)
-            // into the buffer from the lanes that hold it; other lanes of the
-            // wave read it (and, for h = 1, it overwrites what they read): the
-            // wave barriers keep the compiler from moving LDS accesses across
-            // the exchange, and one wave's LDS accesses complete in order.
-            if (h == 1) wave_lds_sync();
-            if (lcol / HC == h) {
-#pragma unroll
-                for (int jj = 0; jj < NJ; ++jj) {
-                    const int row = RPA * jj + lrow;
-                    *reinterpret_cast<u32x4 *>(tile + row * HRW + 4 * ((lcol - h * HC) ^ (row % HC))) = raw[1][jj];
-                }
-            }
-            wave_lds_sync();
-            // the K groups of that half on both tiles, B-operand values read per group
-#pragma unroll
-            for (int jj = h * NJ / 2; jj < (h + 1) * NJ / 2; ++jj) {
-                float b[VPL];
-#pragma unroll
-                for (int e = 0; e < VPL; ++e)
-                    b[e] = n16 < 2 * TM ? s_B[n16 < 2 * TM ? n16 : 0][jj * 4 * VPL + grp * VPL + e] : 0.f;
-                const u32x4 w1 =
-                    *reinterpret_cast<const u32x4 *>(tile + n16 * HRW + 4 * ((4 * jj + grp - h * HC) ^ (n16 % HC)));
-#pragma unroll
-                for (int tau = 0; tau < 2; ++tau) {
-                    const u32x4 wv = tau == 0 ? raw[0][jj] : w1;
-#pragma unroll
-                    for (int e = 0; e < VPL; ++e) {
-                        const uint32_t w = wv[BF16 ? e >> 1 : e];
-                        const float a = BF16 ? ((e & 1) ? bf16_hi(w) : bf16_lo(w)) : __uint_as_float(w);
-                        acc[tau] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b[e], acc[tau], 0, 0, 0);
-                    }
-                }
-            }
-        }
-    } else {
-        float bop[NJ][VPL];
-#pragma unroll
-        for (int jj = 0; jj < NJ; ++jj)
-#pragma unroll
-            for (int e = 0; e < VPL; ++e) bop[jj][e] = n16 < 2 * TM ? s_B[n16 < 2 * TM ? n16 : 0][jj * 4 * VPL + grp * VPL + e] : 0.f;
-#pragma unroll
-        for (int jj = 0; jj < NJ; ++jj)
-            *reinterpret_cast<u32x4 *>(tile + (RPA * jj + lrow) * RSW + 4 * (lcol ^ ((RPA * jj + lrow) & 15))) = raw[1][jj];
-        // other lanes of the wave read what these wrote
-        wave_lds_sync();
-#pragma unroll
-        for (int tau = 0; tau < 2; ++tau) {
-            acc[tau] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int jj = 0; jj < NJ; ++jj) {
-                const u32x4 wv = tau == 0 ? raw[0][jj] : *reinterpret_cast<const u32x4 *>(tile + n16 * RSW + 4 * ((4 * jj + grp) ^ n16));
-#pragma unroll
-                for (int e = 0; e < VPL; ++e) {
-                    const uint32_t w = wv[BF16 ? e >> 1 : e];
-                    const float a = BF16 ? ((e & 1) ? bf16_hi(w) : bf16_lo(w)) : __uint_as_float(w);
-                    acc[tau] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bop[jj][e], acc[tau], 0, 0, 0);
-                }
-            }
-        }
-    }
-    // the outputs overwrite the buffer other lanes of the wave read above
-    wave_lds_sync();
-    // MFMA outputs (lane l: rows 4*(l>>4) + r of the tile, column l & 15) into
-    // the wave's buffer as [row][column]: s_C(v, n) = tile of wave v/32 at
-    // ((v & 31) * OSTR + n); the padded row keeps the substitution's reads of
-    // one row per lane on distinct banks.
-    float *outs = reinterpret_cast<float *>(tile);
-#pragma unroll
-    for (int tau = 0; tau < 2; ++tau)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) outs[(16 * tau + 4 * grp + r) * OSTR + n16] = acc[tau][r];
-    __syncthreads();
-
-    // Forward substitution per value row.
-    if (tid < KD) {
-        const int v = tid;
-        const float *cv = reinterpret_cast<const float *>(s_T[v >> 5]) + (v & 31) * OSTR;  // row v's 16 columns
-        float rk[TM], bu[TM];
-        const int64_t crow0 = ((int64_t)idx * p.HV + hv) * p.t_max;
-#pragma unroll
-        for (int t = 0; t < TM; ++t) {
-            if (t < T) {
-                const float *sm = s_sum[t];
-                rk[t] = rsqrtf(sm[1] + p.l2_eps);
-                const float rqs = rsqrtf(sm[0] + p.l2_eps) * p.scale;
-                float a = rk[t] * cv[t];
-#pragma unroll
-                for (int s = 0; s < t; ++s) a = fmaf(rk[t] * rk[s] * sm[2 + TM + s], bu[s], a);
-                bu[t] = s_beta[t] * (s_v[t][v] - a);
-                float o = cv[TM + t];
-#pragma unroll
-                for (int s = 0; s <= t; ++s) o = fmaf(rk[s] * sm[2 + s], bu[s], o);
-                o *= rqs;
-                p.out[((tok0 + t) * p.HV + hv) * KD + v] = (uint16_t)(pack_bf16x2(o, 0.0f) & 0xffffu);
-                if (p.corr && t < p.t_max) p.corr[(crow0 + t) * KD + v] = bu[t];
-            }
-        }
-    }
-}
-
 // ------------------------------------------------- WY verify kernel ----
 //
 // Read-only calls ("Frozen / speculative-verify mode": the pool is never
@@ -1721,27 +1409,30 @@ struct WyLayout {
 // two 16-row tiles.
 //  1. The token inputs of the lane's key channel are loaded before the pool
 //     slot is known, and the lane's value row.
-//  2. Each wave loads its first 16-row tile straight into registers, in the
-//     layout the matrix cores take (16 rows x 64 contiguous bytes per load,
-//     non-temporal).  Meanwhile the key channels, one per lane (waves 0-1
-//     layout A with q, waves 2-3 layout B with k): cumulative decays, the
-//     token operand column of the channel (q_t E_t, or k_t E_t; zero past
-//     the tokens) into LDS once for the head (bf16 pools: as a bf16 head
-//     and remainder), and the W-weighted channel sums, each reduced over
-//     the wave in registers.  Then the loads of the second tile (its
-//     registers were the channel phase's), and one barrier.
-//  3. [k_t E_t ; q_t E_t] x S0 on the matrix cores, tile by tile (bf16
-//     pools: the exact state by the operand's head and remainder, two bf16
-//     products; fp32 pools: fp32 products), through LDS into a row-per-lane
-//     layout, then the forward substitution (lanes l and l + 32 own row
-//     l & 31 and store alternate tokens).
-// The state lives in registers only; the LDS holds the operand, the sums,
-// the coefficients and the products (14 KB for fp32 at TM = 4), so four to
-// five workgroups share a compute unit (the VGPRs decide) and the loads of
-// one overlap the arithmetic of the others.  Consecutive heads (which share
-// their sequence's token rows) run on one XCD.
+//  2. The state is read as whole rows: in each load instruction a wave
+//     reads 1 KB of consecutive rows (2 fp32 or 4 bf16 rows) and the four
+//     waves side by side 4 KB, so the head streams in order; measured on
+//     MI355X, loads in the matrix-core layout (16 rows x 64 bytes per
+//     instruction) stream 20-25% slower.  A wave's 32 rows are those of its
+//     own load instructions.  The first tile's loads go out first;
+//     meanwhile the key channels, one per lane (waves 0-1 layout A with q,
+//     waves 2-3 layout B with k): cumulative decays, the token operand
+//     column of the channel (q_t E_t, or k_t E_t; zero past the tokens)
+//     into LDS once for the head (bf16 pools: as a bf16 head and
+//     remainder), and the W-weighted channel sums, each reduced over the
+//     wave in registers.  Then the second tile's loads, and one barrier.
+//  3. [k_t E_t ; q_t E_t] x S0 on the matrix cores: each tile reaches the
+//     matrix-core layout through the wave's LDS buffer in passes of 16
+//     columns of 16 bytes (bf16 pools: the exact state by the operand's
+//     head and remainder, two bf16 products; fp32 pools: fp32 products,
+//     4x4x1 when at most 8 operand columns exist), the products through LDS
+//     into a row-per-lane layout, then the forward substitution (lanes l
+//     and l + 32 own row l & 31 and store alternate tokens).
+// Four to five workgroups share a compute unit (the VGPRs decide), so the
+// loads of one overlap the arithmetic of the others.  Consecutive heads
+// (which share their sequence's token rows) run on one XCD.
 template <bool BF16, int TM>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TM <= 4 ? 5 : (TM <= 8 ? 4 : 2))))
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TM <= 4 ? (BF16 ? 5 : 4) : (TM <= 8 ? 4 : 2))))
 kda_verify_wy_kernel(const RecParams p)
 {
     using LY = WyLayout<BF16>;
@@ -1758,7 +1449,14 @@ kda_verify_wy_kernel(const RecParams p)
     constexpr int BST = BF16 ? KD / 2 + 4 : KD + 4;  // words per operand row (bf16: pairs), padded
     static_assert(TM <= VERIFY_WY_MAX_T, "verify tokens");
 
-    __shared__ __align__(16) uint32_t s_T[4][WROWS * OST];   // per wave: its rows' products
+    constexpr int LPR = ROW_BYTES / 16;          // lanes per state row in a load instruction
+    constexpr int RPI = 64 / LPR;                // rows per load instruction of a wave
+    constexpr int NLD = 16 / RPI;                // load instructions per 16-row tile
+    constexpr int NPASS = LPR / 16;              // passes of 16 columns (16 bytes each) per tile
+    constexpr bool MF4 = !BF16 && 2 * TM <= 8;  // 4x4x1 products (see below)
+    constexpr int PASSW = MF4 ? 2048 : 1024;     // a pass of one tile, or of both (4x4x1)
+    constexpr int BUFW = WROWS * OST > PASSW ? WROWS * OST : PASSW;  // the passes, then the products
+    __shared__ __align__(16) uint32_t s_T[4][BUFW];          // per wave
     __shared__ __align__(16) uint32_t s_B[BF16 ? 2 : 1][NCOL][BST];  // token operand (bf16: head, remainder)
     __shared__ float s_sum[2][2][64 * NCH];                   // channel sums: layout, half of the channels
     __shared__ float s_beta[TM];
@@ -1770,7 +1468,11 @@ kda_verify_wy_kernel(const RecParams p)
     const int grp = lane >> 4;
     const int n16 = lane & 15;
     const int rloc = lane & 31;
-    const int vrow = WROWS * wave + rloc;
+    // Value row of row rho (0..15) of the wave's tile tau: the tile holds the
+    // rows of its load instructions NLD tau .. NLD tau + NLD - 1, in each of
+    // which the four waves read 4 RPI consecutive rows side by side.
+    auto vrow_of = [&](int tau, int rho) { return 4 * RPI * (NLD * tau + rho / RPI) + RPI * wave + rho % RPI; };
+    const int vrow = vrow_of(rloc >> 4, rloc & 15);
     const int work = (int)(blockIdx.x & 7u) * (int)(gridDim.x >> 3) + (int)(blockIdx.x >> 3);
     if (work >= p.n_work) return;
     const WyItem it = wy_item(p, work);
@@ -1814,19 +1516,17 @@ kda_verify_wy_kernel(const RecParams p)
 
     // 2. the state: the first tile into registers (the second follows the channel phase)
     uint32_t *buf = s_T[wave];
-    const char *wrows = static_cast<const char *>(p.state) +
-                        ((int64_t)it.idx * p.slot_stride + (int64_t)it.hv * (KD * KD)) * (BF16 ? 2 : 4) +
-                        (int64_t)(WROWS * wave) * ROW_BYTES;
-    uint32_t st[NJ][SW];
-    {
-        const char *row = wrows + (int64_t)n16 * ROW_BYTES;
+    const char *hstate = static_cast<const char *>(p.state) +
+                         ((int64_t)it.idx * p.slot_stride + (int64_t)it.hv * (KD * KD)) * (BF16 ? 2 : 4);
+    const uint32_t lcol = 16u * (uint32_t)(lane % LPR);  // the lane's 16 bytes of a row
+    auto load_tile = [&](int tau, u32x4 (&raw)[NLD]) {
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-            const u32x4 w = __builtin_nontemporal_load(
-                reinterpret_cast<const u32x4 *>(row + LY::channel(j, grp) * (BF16 ? 2 : 4)));
-            st[j][0] = w.x; st[j][1] = w.y; st[j][2] = w.z; st[j][3] = w.w;
-        }
-    }
+        for (int i = 0; i < NLD; ++i)
+            raw[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
+                hstate + (uint32_t)vrow_of(tau, RPI * i + lane / LPR) * ROW_BYTES + lcol));
+    };
+    u32x4 raw0[NLD];
+    load_tile(0, raw0);
     // (the scheduling barriers keep other work, and the waits it would
     // bring, from landing between the loads of the tile)
 
@@ -1884,16 +1584,8 @@ kda_verify_wy_kernel(const RecParams p)
             s_beta[lane] = precomputed ? bv : sigmoid_f(bv);
         }
     }
-    uint32_t st1[NJ][SW];  // the second tile
-    {
-        const char *row = wrows + (int64_t)(16 + n16) * ROW_BYTES;
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-            const u32x4 w = __builtin_nontemporal_load(
-                reinterpret_cast<const u32x4 *>(row + LY::channel(j, grp) * (BF16 ? 2 : 4)));
-            st1[j][0] = w.x; st1[j][1] = w.y; st1[j][2] = w.z; st1[j][3] = w.w;
-        }
-    }
+    u32x4 raw1[NLD];  // the second tile
+    load_tile(1, raw1);
     __syncthreads();
 
     // coefficients (each wave its own copy): (t, s) = (e / TM, e % TM);
@@ -1925,11 +1617,10 @@ kda_verify_wy_kernel(const RecParams p)
     // 3. the products, tile by tile: column cc = 16 kc + (lane & 15) of the
     // operand at the lane's channels (zero past the 2 TM columns)
     f32x4 acc[2][NCT];
-    auto tile_products = [&](int tau, const uint32_t (&sa)[NJ][SW]) {
-#pragma unroll
-        for (int kc = 0; kc < NCT; ++kc) acc[tau][kc] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
+    // K group j of a tile; sa: the lane's 16 bytes of it (row lane & 15)
+    auto kgroup = [&](int tau, int j, const u32x4 &sw) {
+        const uint32_t sa[SW] = {sw.x, sw.y, sw.z, sw.w};
+        {
             const int ch = LY::channel(j, grp);
 #pragma unroll
             for (int kc = 0; kc < NCT; ++kc) {
@@ -1939,7 +1630,7 @@ kda_verify_wy_kernel(const RecParams p)
                     u32x4 bh = *reinterpret_cast<const u32x4 *>(&s_B[0][ccr][ch / 2]);
                     u32x4 bl = *reinterpret_cast<const u32x4 *>(&s_B[1][ccr][ch / 2]);
                     if (cc >= NCOL) bh = bl = u32x4{0u, 0u, 0u, 0u};
-                    const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{sa[j][0], sa[j][1], sa[j][2], sa[j][3]});
+                    const bf16x8 a = __builtin_bit_cast(bf16x8, sw);
                     acc[tau][kc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, bh),
                                                                           acc[tau][kc], 0, 0, 0);
                     acc[tau][kc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, bl),
@@ -1949,25 +1640,118 @@ kda_verify_wy_kernel(const RecParams p)
                     if (cc >= NCOL) b = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        acc[tau][kc] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(sa[j][e]), b[e],
+                        acc[tau][kc] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(sa[e]), b[e],
                                                                            acc[tau][kc], 0, 0, 0);
                 }
             }
         }
     };
-    tile_products(0, st);
-    tile_products(1, st1);
+    // A tile reaches the matrix-core layout (row lane & 15, the 16 bytes
+    // of K group j) through the wave's buffer, 16 columns of 16 bytes per
+    // pass: column c of row rho at c ^ rho, so that the 16 rows read at one
+    // column fall on distinct banks.
+    auto tile_products = [&](int tau, const u32x4 (&raw)[NLD]) {
+#pragma unroll
+        for (int kc = 0; kc < NCT; ++kc) acc[tau][kc] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int hh = 0; hh < NPASS; ++hh) {
+            const int c = lane % LPR - 16 * hh;
+            if (NPASS == 1 || (c >= 0 && c < 16)) {
+#pragma unroll
+                for (int i = 0; i < NLD; ++i) {
+                    const int rho = RPI * i + lane / LPR;
+                    *reinterpret_cast<u32x4 *>(buf + 4 * (16 * rho + (c ^ rho))) = raw[i];
+                }
+            }
+            wave_lds_sync();
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int j = 4 * hh + jj;
+                kgroup(tau, j, *reinterpret_cast<const u32x4 *>(buf + 4 * (16 * n16 + ((4 * j + grp - 16 * hh) ^ n16))));
+            }
+            wave_lds_sync();
+        }
+    };
+    // fp32 pools with at most 4 token slots (4 or 8 operand columns) use the
+    // 4x4x1 products instead, 16 blocks of 4 rows by 4 columns, so that no
+    // operand column is padding: block 4 cp + rg (lanes 16 cp + 4 rg + 0..3)
+    // takes rows 4 rg .. 4 rg + 3 of a tile over channel part cp of the pass
+    // (its 16-byte columns 4 cp .. 4 cp + 3); both tiles go through the
+    // buffer in each pass, so that an operand read serves both; the four
+    // parts are then summed across the lanes.
+    constexpr int NCS = MF4 ? NCOL / 4 : 1;      // 4x4x1: sets of 4 operand columns
+    [[maybe_unused]] float mtot[2][NCS];         // 4x4x1: each lane's tile totals
+    if constexpr (MF4) {
+        f32x4 d[2][NCS];
+#pragma unroll
+        for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+            for (int cs = 0; cs < NCS; ++cs) d[tau][cs] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int cp = lane >> 4, rho = lane & 15;  // rho = 4 rg + (lane & 3)
+#pragma unroll
+        for (int hh = 0; hh < NPASS; ++hh) {
+            const int c = lane % LPR - 16 * hh;
+            if (c >= 0 && c < 16) {
+#pragma unroll
+                for (int i = 0; i < NLD; ++i) {
+                    const int rw = RPI * i + lane / LPR;
+                    *reinterpret_cast<u32x4 *>(buf + 4 * (16 * rw + (c ^ rw))) = raw0[i];
+                    *reinterpret_cast<u32x4 *>(buf + 1024 + 4 * (16 * rw + (c ^ rw))) = raw1[i];
+                }
+            }
+            wave_lds_sync();
+#pragma unroll
+            for (int sq = 0; sq < 4; ++sq) {
+                const int c16 = 4 * cp + sq;  // 16-byte column of the pass
+                f32x4 bv[NCS];
+#pragma unroll
+                for (int cs = 0; cs < NCS; ++cs)
+                    bv[cs] = *reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(s_B[0][4 * cs + (lane & 3)]) +
+                                                              64 * hh + 4 * c16);
+#pragma unroll
+                for (int tau = 0; tau < 2; ++tau) {
+                    const f32x4 a = *reinterpret_cast<const f32x4 *>(buf + 1024 * tau + 4 * (16 * rho + (c16 ^ rho)));
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+#pragma unroll
+                        for (int cs = 0; cs < NCS; ++cs)
+                            d[tau][cs] = __builtin_amdgcn_mfma_f32_4x4x1f32(a[e], bv[cs][e], d[tau][cs], 0, 0, 0);
+                }
+            }
+            wave_lds_sync();
+        }
+        // lane 16 cp + 4 rg + j holds rows 4 rg + r (r = 0..3) of column
+        // 4 cs + j over part cp; halving at distances 32 and 16 leaves it the
+        // total of row 4 rg + cp
+#pragma unroll
+        for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+            for (int cs = 0; cs < NCS; ++cs)
+                mtot[tau][cs] = swap16_sum(swap32_sum(d[tau][cs][0], d[tau][cs][2]),
+                                           swap32_sum(d[tau][cs][1], d[tau][cs][3]));
+    } else {
+        tile_products(0, raw0);
+        tile_products(1, raw1);
+    }
 
     // the products to LDS, this wave's rows: row 16 tau + 4 g + r, column
     // 16 kc + (lane & 15)
     float *prod = reinterpret_cast<float *>(buf);
+    if constexpr (MF4) {
 #pragma unroll
-    for (int tau = 0; tau < 2; ++tau)
+        for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
-        for (int kc = 0; kc < NCT; ++kc)
-            if (16 * kc + n16 < NCOL)
+            for (int cs = 0; cs < NCS; ++cs)
+                prod[(16 * tau + 4 * ((lane >> 2) & 3) + (lane >> 4)) * OST + 4 * cs + (lane & 3)] = mtot[tau][cs];
+    } else {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) prod[(16 * tau + 4 * grp + r) * OST + 16 * kc + n16] = acc[tau][kc][r];
+        for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+            for (int kc = 0; kc < NCT; ++kc)
+                if (16 * kc + n16 < NCOL)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) prod[(16 * tau + 4 * grp + r) * OST + 16 * kc + n16] = acc[tau][kc][r];
+    }
     wave_lds_sync();
 
     // forward substitution, row rloc of the wave
@@ -2049,18 +1833,6 @@ int launch_recurrent(const RecParams &p, const Launch &l, void *stream)
 {
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();  // a stale error must not be blamed on this launch
-    if (l.family == KERNEL_VERIFY_CHUNK) {
-        // token slots sized to the call: 2 or 4, the smallest that holds T
-        const dim3 grid(l.grid), block(l.block);
-        if (p.tps <= 2) {
-            if (l.bf16_state) hipLaunchKernelGGL((kda_verify_chunk_kernel<true, 2>), grid, block, 0, s, p);
-            else hipLaunchKernelGGL((kda_verify_chunk_kernel<false, 2>), grid, block, 0, s, p);
-        } else {
-            if (l.bf16_state) hipLaunchKernelGGL((kda_verify_chunk_kernel<true, 4>), grid, block, 0, s, p);
-            else hipLaunchKernelGGL((kda_verify_chunk_kernel<false, 4>), grid, block, 0, s, p);
-        }
-        return record(hipGetLastError());
-    }
     if (l.family == KERNEL_VERIFY_WY) {
         // token slots sized to the declared length: 2, 4, 8 or 16, the smallest that holds it
         const dim3 grid(l.grid), block(l.block);

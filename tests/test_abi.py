@@ -366,14 +366,13 @@ def test_batched_form_and_flags():
 @pytest.mark.parametrize("bf16", [False, True])
 def test_read_only_batched_calls_take_a_verify_kernel(tps, bf16):
     """Read-only batched calls with 2..16 tokens and no checkpoints run as one
-    matrix product per head, one workgroup of 256 threads per head: the
-    chunked verify kernel (family 6) up to 4 tokens, the WY verify kernel
-    (family 5) above."""
+    matrix product per head on the WY verify kernel (family 5), one workgroup
+    of 256 threads per head."""
     a = rec_args(N=64, H=32, tps=tps, slots=128, bf16=bf16)
     a.flags = 1
     rc, p = plan_rec(with_caches(a, t_max=tps))
     assert rc == 0, err()
-    assert (p.kernel, p.vsplit, p.rows_per_block, p.block) == (6 if tps <= 4 else 5, 1, D, 256)
+    assert (p.kernel, p.vsplit, p.rows_per_block, p.block) == (5, 1, D, 256)
     assert p.grid_x == 64 * 32 and p.items == 64 * 32
 
 

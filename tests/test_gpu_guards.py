@@ -98,12 +98,13 @@ def test_recurrent_ragged_checkpoint_and_cache_guards(state_dtype):
         g.check(n)
 
 
-@pytest.mark.parametrize("state_dtype,T,TM", [(torch.float32, 8, 5), (torch.bfloat16, 3, 6)])
-def test_chunked_verify_guards(state_dtype, T, TM):
-    """Read-only batched calls with 2..8 tokens (the chunked matrix-core
-    kernel): output and both verify caches guarded, the pool guarded and
-    unchanged, with a null row and an index past the pool."""
-    say(f"guards chunked verify T={T} cache {TM} {state_dtype}")
+@pytest.mark.parametrize("state_dtype,T,TM", [(torch.float32, 8, 5), (torch.bfloat16, 3, 6), (torch.float32, 2, 3)])
+def test_verify_wy_guards(state_dtype, T, TM):
+    """Read-only batched calls of a few tokens (the WY verify kernel; fp32
+    pools of up to 4 tokens take its 4x4x1 products): output and both verify
+    caches guarded, the pool guarded and unchanged, with a null row and an
+    index past the pool."""
+    say(f"guards WY verify T={T} cache {TM} {state_dtype}")
     n, H, HV, S = 6, 2, 4, 12
     c = synth.recurrent_case(9650 + T, n_seqs=n, H=H, HV=HV, num_slots=S, state_dtype=state_dtype, device=DEV,
                              indices="random", lengths=[T] * n, null_rows=1)

@@ -113,9 +113,8 @@ def test_random_recurrent_calls(seed):
 @pytest.mark.parametrize("seed", range(12))
 def test_random_batched_calls(seed):
     """The batched [B, T, ...] form with 2..16 tokens: read-only calls
-    without checkpoints take a matrix-core kernel (the chunk kernel up to 4
-    tokens, the WY product beyond), the rest the token loop; all against the
-    oracle with the same bars."""
+    without checkpoints take the WY verify kernel's matrix product, the rest
+    the token loop; both against the oracle with the same bars."""
     rng = random.Random(6100 + seed)
     H = rng.choice([1, 2, 4, 8])
     HV = H * rng.choice([1, 2, 3])

@@ -34,7 +34,7 @@ def say(*a):
     print("[case]", *a, flush=True)
 
 
-def chunk_plan_kernel(n, T, H, HV, slots, bf16):
+def wy_plan_kernel(n, T, H, HV, slots, bf16):
     """Kernel family the library plans for a read-only batched call of this shape."""
     import ctypes
     a = _lib.RecurrentArgs()
@@ -71,6 +71,8 @@ CASES = [  # T, state dtype, gate, gate dtype, H, HV, cache length
     (2, torch.bfloat16, "in_kernel", torch.bfloat16, 4, 4, 3),
     (3, torch.bfloat16, "in_kernel", torch.bfloat16, 4, 8, 5),
     (4, torch.float32, "precomputed", torch.float32, 2, 8, 3),
+    (3, torch.float32, "in_kernel", torch.bfloat16, 2, 4, 4),
+    (4, torch.bfloat16, "precomputed", torch.float32, 4, 4, 4),
     (5, torch.bfloat16, "precomputed", torch.bfloat16, 4, 4, 5),
     (6, torch.float32, "in_kernel", torch.float32, 8, 8, 8),
     (7, torch.float32, "precomputed", torch.float32, 4, 12, 7),
@@ -88,11 +90,11 @@ CASES = [  # T, state dtype, gate, gate dtype, H, HV, cache length
 @pytest.mark.parametrize("T,state_dtype,gate,gate_dtype,H,HV,t_max", CASES,
                          ids=[f"T{c[0]}-{'bf16' if c[1] == torch.bfloat16 else 'fp32'}-{c[2]}-H{c[4]}HV{c[5]}"
                               f"-tmax{c[6]}" for c in CASES])
-def test_chunked_verify_against_oracle(T, state_dtype, gate, gate_dtype, H, HV, t_max):
+def test_wy_verify_against_oracle(T, state_dtype, gate, gate_dtype, H, HV, t_max):
     seed = 7600 + 10 * T + HV
     n, slots = 11, 24
-    say(f"chunked verify T={T} {state_dtype} gate={gate}/{gate_dtype} H={H} HV={HV} t_max={t_max} seed={seed}")
-    assert chunk_plan_kernel(n, T, H, HV, slots, state_dtype == torch.bfloat16) == (6 if T <= 4 else 5)
+    say(f"WY verify T={T} {state_dtype} gate={gate}/{gate_dtype} H={H} HV={HV} t_max={t_max} seed={seed}")
+    assert wy_plan_kernel(n, T, H, HV, slots, state_dtype == torch.bfloat16) == 5
     c = synth.recurrent_case(seed, n_seqs=n, H=H, HV=HV, num_slots=slots, state_dtype=state_dtype, device=DEV,
                              indices="random", lengths=[T] * n, null_rows=2, gate=gate, gate_dtype=gate_dtype)
     c.state_indices[4] = slots + 5  # past the pool: null
@@ -111,12 +113,12 @@ def test_chunked_verify_against_oracle(T, state_dtype, gate, gate_dtype, H, HV, 
     say(f"out err {e1:.3e} corr err {e2:.3e}")
 
 
-def test_chunked_verify_with_underflowing_decay():
+def test_wy_verify_with_underflowing_decay():
     """Log-decays of -20..-90 per token: the cumulative decay underflows to
     zero in fp32 within a token or two; outputs and corrections stay finite
     and match the oracle."""
     T, n, H, slots = 6, 7, 4, 12
-    say(f"chunked verify underflowing decay T={T} H={H} seed=7700")
+    say(f"WY verify underflowing decay T={T} H={H} seed=7700")
     c = synth.recurrent_case(7700, n_seqs=n, H=H, num_slots=slots, device=DEV, indices="random", lengths=[T] * n,
                              gate="precomputed", gate_dtype=torch.float32)
     gen = torch.Generator(device=DEV)
@@ -130,18 +132,18 @@ def test_chunked_verify_with_underflowing_decay():
     check_caches(corr, kg, want, recorded_mask(c, [T] * n, T))
 
 
-def test_chunked_and_sequential_forms_agree():
-    """The same tokens through the chunked read-only kernel and through the
+def test_wy_and_sequential_forms_agree():
+    """The same tokens through the WY read-only kernel and through the
     sequential token loop (an updating call on a copy of the pool) give
     outputs within the bf16 bar of each other, and the read-only call leaves
     its pool untouched."""
     T, n, H = 4, 16, 8
-    say(f"chunked vs sequential T={T} H={H} seed=7800")
+    say(f"WY vs sequential T={T} H={H} seed=7800")
     c = synth.recurrent_case(7800, n_seqs=n, H=H, num_slots=20, device=DEV, indices="random", lengths=[T] * n)
     st0 = c.state.clone()
     shp = lambda t: t.reshape(n, T, *t.shape[1:])  # noqa: E731
     args = [shp(c.q), shp(c.k), shp(c.v), shp(c.g), shp(c.beta), c.A_log, c.dt_bias]
-    o_chunk = recurrent_kda(*args, initial_state=c.state, state_indices=c.state_indices,
+    o_wy = recurrent_kda(*args, initial_state=c.state, state_indices=c.state_indices,
                             disable_state_update=True)
     pool2 = st0.clone()
     o_seq = recurrent_kda(*args, initial_state=pool2, state_indices=c.state_indices)
@@ -149,19 +151,19 @@ def test_chunked_and_sequential_forms_agree():
     assert torch.equal(P.bits(st0), P.bits(c.state))
     want = oracle.recurrent(np_(c.q), np_(c.k), np_(c.v), np_(c.g), np_(c.beta), np_(c.A_log), np_(c.dt_bias),
                             np_(st0), np_(c.state_indices), None, update_state=False, tokens_per_seq=T)
-    P.check_bf16_out(o_chunk, want["out64"])
+    P.check_bf16_out(o_wy, want["out64"])
     P.check_bf16_out(o_seq, want["out64"])
-    diff = (o_chunk.float() - o_seq.float()).abs().max().item()
+    diff = (o_wy.float() - o_seq.float()).abs().max().item()
     assert diff <= 2 * P.OUT_ATOL, diff
     assert np.isfinite(diff)
 
 
-def test_chunked_verify_graph_replay_with_new_inputs_and_indices():
+def test_wy_verify_graph_replay_with_new_inputs_and_indices():
     """A captured read-only T=4 call replays with new token inputs and slot
     indices written into its buffers (metadata is read on the device):
     every replay equals the same call made eagerly, bit for bit."""
     T, n, H, slots = 4, 12, 4, 40
-    say(f"chunked verify graph replay T={T} H={H} seed=7900")
+    say(f"WY verify graph replay T={T} H={H} seed=7900")
     c = synth.recurrent_case(7900, n_seqs=n, H=H, num_slots=slots, device=DEV, indices="random", lengths=[T] * n)
     shp = lambda t: t.reshape(n, T, *t.shape[1:])  # noqa: E731
     bufs = [shp(c.q).clone(), shp(c.k).clone(), shp(c.v).clone(), shp(c.g).clone(), shp(c.beta).clone()]
