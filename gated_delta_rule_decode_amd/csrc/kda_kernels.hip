@@ -1446,18 +1446,25 @@ kda_verify_wy_kernel(const RecParams p)
     constexpr int NJ = LY::NJ;
     constexpr int SW = LY::SW;
     constexpr int NCF = 2 * TM * TM + 3 * TM;    // per-wave coefficients
-    constexpr int BST = BF16 ? KD / 2 + 4 : KD + 4;  // words per operand row (bf16: pairs), padded
+    // fp32 pools: 4x4x1 fp32 products when at most 8 operand columns exist
+    // (MF4); 16x16x4 fp32 products at 16 columns; at 32 columns bf16
+    // products on a bf16 head and remainder of the state and of the operand
+    // (SPL, three products per K block: a fifth of the matrix-core time for
+    // some vector work, measured faster only there)
+    constexpr bool MF4 = !BF16 && 2 * TM <= 8;
+    constexpr bool SPL = !BF16 && 2 * TM > 16;
+    constexpr bool OPB = BF16 || SPL;            // operand stored as bf16 head and remainder
+    constexpr int BST = OPB ? KD / 2 + 4 : KD + 4;  // words per operand row (bf16: pairs), padded
     static_assert(TM <= VERIFY_WY_MAX_T, "verify tokens");
 
     constexpr int LPR = ROW_BYTES / 16;          // lanes per state row in a load instruction
     constexpr int RPI = 64 / LPR;                // rows per load instruction of a wave
     constexpr int NLD = 16 / RPI;                // load instructions per 16-row tile
     constexpr int NPASS = LPR / 16;              // passes of 16 columns (16 bytes each) per tile
-    constexpr bool MF4 = !BF16 && 2 * TM <= 8;  // 4x4x1 products (see below)
     constexpr int PASSW = MF4 ? 2048 : 1024;     // a pass of one tile, or of both (4x4x1)
     constexpr int BUFW = WROWS * OST > PASSW ? WROWS * OST : PASSW;  // the passes, then the products
     __shared__ __align__(16) uint32_t s_T[4][BUFW];          // per wave
-    __shared__ __align__(16) uint32_t s_B[BF16 ? 2 : 1][NCOL][BST];  // token operand (bf16: head, remainder)
+    __shared__ __align__(16) uint32_t s_B[OPB ? 2 : 1][NCOL][BST];  // token operand (or its bf16 head, remainder)
     __shared__ float s_sum[2][2][64 * NCH];                   // channel sums: layout, half of the channels
     __shared__ float s_beta[TM];
     __shared__ float s_cf[4][NCF];                            // per wave: C_ts, A'_ts, rk_t, scale*rq_t, beta_t
@@ -1560,7 +1567,7 @@ kda_verify_wy_kernel(const RecParams p)
             // operand column: q_t E_t (layout A) or k_t E_t (layout B)
             const float ov = t < it.n ? xf[t] * __expf(L) : 0.f;
             const int col = A ? TM + t : t;
-            if constexpr (BF16) {
+            if constexpr (OPB) {
                 const __bf16 hb = (__bf16)ov;
                 const __bf16 lb = (__bf16)(ov - (float)hb);
                 reinterpret_cast<__bf16 *>(s_B[0][col])[c] = hb;
@@ -1664,10 +1671,42 @@ kda_verify_wy_kernel(const RecParams p)
                 }
             }
             wave_lds_sync();
+            if constexpr (SPL) {
+                // K blocks 2 hh and 2 hh + 1 (32 channels each): the lane's 8
+                // channels 32 jb + 8 g + 0..7 as a bf16 head and remainder
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const int j = 4 * hh + jj;
-                kgroup(tau, j, *reinterpret_cast<const u32x4 *>(buf + 4 * (16 * n16 + ((4 * j + grp - 16 * hh) ^ n16))));
+                for (int j2 = 0; j2 < 2; ++j2) {
+                    const int jb = 2 * hh + j2, c0 = 8 * j2 + 2 * grp;
+                    const f32x4 x0 = *reinterpret_cast<const f32x4 *>(buf + 4 * (16 * n16 + (c0 ^ n16)));
+                    const f32x4 x1 = *reinterpret_cast<const f32x4 *>(buf + 4 * (16 * n16 + ((c0 + 1) ^ n16)));
+                    bf16x8 ah, al;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float x = e < 4 ? x0[e] : x1[e - 4];
+                        const __bf16 h = (__bf16)x;
+                        ah[e] = h;
+                        al[e] = (__bf16)(x - (float)h);
+                    }
+#pragma unroll
+                    for (int kc = 0; kc < NCT; ++kc) {
+                        const int cc = 16 * kc + n16;
+                        const int ccr = cc < NCOL ? cc : NCOL - 1;
+                        u32x4 bh = *reinterpret_cast<const u32x4 *>(&s_B[0][ccr][16 * jb + 4 * grp]);
+                        u32x4 bl = *reinterpret_cast<const u32x4 *>(&s_B[1][ccr][16 * jb + 4 * grp]);
+                        if (cc >= NCOL) bh = bl = u32x4{0u, 0u, 0u, 0u};
+                        const bf16x8 bhv = __builtin_bit_cast(bf16x8, bh), blv = __builtin_bit_cast(bf16x8, bl);
+                        acc[tau][kc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bhv, acc[tau][kc], 0, 0, 0);
+                        acc[tau][kc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, blv, acc[tau][kc], 0, 0, 0);
+                        acc[tau][kc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bhv, acc[tau][kc], 0, 0, 0);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);  // (the next block's reads not hoisted: registers)
+                }
+            } else {
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int j = 4 * hh + jj;
+                    kgroup(tau, j, *reinterpret_cast<const u32x4 *>(buf + 4 * (16 * n16 + ((4 * j + grp - 16 * hh) ^ n16))));
+                }
             }
             wave_lds_sync();
         }
