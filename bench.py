@@ -16,6 +16,7 @@ ragged) with their own timings.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import math
@@ -574,6 +575,72 @@ def stream_ceilings(torch, dev, timer):
     return res
 
 
+FLOORS_LIB = os.path.join(ROOT, "libkda_floors.so")
+
+
+def access_floors(torch, dev, timer, pool32):
+    """The floor each benchmarked access pattern sets on this chip: kernels of
+    bench_floors.hip that move exactly a workload's state bytes in its access
+    pattern (random slots, tile per workgroup, lane layout) with one FMA per
+    element and nothing else, timed like the workloads (graph replays over
+    rotating slot sets).  Run after the workloads: the in-place floors
+    rewrite the slots they touch."""
+    if not os.path.exists(FLOORS_LIB):
+        log("floors: libkda_floors.so is not built (build() compiles it); skipped")
+        return None
+    lib = ctypes.CDLL(FLOORS_LIB)
+    vp, ci = ctypes.c_void_p, ctypes.c_int
+    lib.floor_read_heads.argtypes = [vp, vp, vp, ci, ci, ci, vp]
+    lib.floor_rmw_slices.argtypes = [vp, vp, ci, ci, ci, ci, vp]
+
+    def ok(rc):
+        if rc != 0:
+            raise RuntimeError(f"floor probe launch failed ({rc})")
+
+    cur = lambda: ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)  # noqa: E731
+    g = torch.Generator(device=dev)
+    g.manual_seed(11)
+    res = {}
+    perm = torch.randperm(pool32.shape[0], generator=g, device=dev).to(torch.int32)
+    Bv, H = 64, 32
+    sums = torch.empty(Bv * H, device=dev)
+    for layout, name in ((0, "whole_rows"), (1, "matrix_core_order")):
+        calls = [lambda ids=perm[j * Bv:(j + 1) * Bv].contiguous(), layout=layout: ok(lib.floor_read_heads(
+            pool32.data_ptr(), ids.data_ptr(), sums.data_ptr(), Bv, H, layout, cur())) for j in range(8)]
+        us = rotating(torch, timer, calls)
+        nb = Bv * H * D * D * 4
+        res[f"verify_state_read_b64_h32_fp32_{name}"] = {"us": us, "GBps": nb / (us * 1e-6) / 1e9}
+        log(f"floor verify state read ({name}): {us:.1f} us, {nb / (us * 1e-6) / 1e9:.0f} GB/s")
+    B = 256
+    calls = [lambda ids=perm[j * B:(j + 1) * B].contiguous(): ok(lib.floor_rmw_slices(
+        pool32.data_ptr(), ids.data_ptr(), B, H, D * D * 4, 8192, cur())) for j in range(pool32.shape[0] // B)]
+    us = rotating(torch, timer, calls)
+    nb = 2 * B * H * D * D * 4
+    res["headline_state_rmw_b256_h32_fp32_8KiB"] = {"us": us, "GBps": nb / (us * 1e-6) / 1e9}
+    log(f"floor headline state RMW: {us:.1f} us, {nb / (us * 1e-6) / 1e9:.0f} GB/s")
+    SL, Hp = 8192, 12
+    poolb = torch.zeros((SL, Hp, D, D), dtype=torch.bfloat16, device=dev)
+    permb = torch.randperm(SL, generator=g, device=dev).to(torch.int32)
+    for Bp in (256, 512):
+        live = Bp - Bp // 8
+        sets = []
+        for j in range(8):
+            ids = permb[j * Bp:(j + 1) * Bp].clone()
+            ids[live:] = -1
+            sets.append(ids.contiguous())
+        nb = 2 * live * Hp * D * D * 2
+        for sb in (4096, 8192, 16384, 32768, 4096, 8192):
+            calls = [lambda ids=ids, sb=sb, Bp=Bp: ok(lib.floor_rmw_slices(
+                poolb.data_ptr(), ids.data_ptr(), Bp, Hp, D * D * 2, sb, cur())) for ids in sets]
+            us = rotating(torch, timer, calls)
+            res[f"packed_state_rmw_b{Bp}_h12_bf16_{sb // 1024}KiB"] = {"us": us, "GBps": nb / (us * 1e-6) / 1e9}
+            log(f"floor packed H=12 bf16 B={Bp} state RMW, {sb // 1024} KiB tiles: {us:.1f} us, "
+                f"{nb / (us * 1e-6) / 1e9:.0f} GB/s")
+    del poolb
+    torch.cuda.empty_cache()
+    return res
+
+
 # ------------------------------------------------------------------ main ----
 
 def main():
@@ -588,6 +655,7 @@ def main():
                     help="run only the extra workloads whose name contains this text (for profiling)")
     ap.add_argument("--copy-calibrate", action="store_true",
                     help="also run a 1 GiB device copy (for counter scaling under rocprofv3)")
+    ap.add_argument("--no-floors", action="store_true", help="skip the access-pattern floors (bench_floors.hip)")
     ap.add_argument("--ceilings", action="store_true",
                     help="also time reference HBM streams with PyTorch's own kernels (write-only, copy, "
                          "in-place read-modify-write, one read to five writes in 64 KiB blocks)")
@@ -713,6 +781,10 @@ def main():
         packed_b = tuple(int(b) for b in args.packed_b.split(",")) if args.packed_b else None
         packed_fused_n = tuple(int(n) for n in args.packed_fused_n.split(",")) if args.packed_fused_n else None
         result["workloads"] = extra_workloads(torch, dev, timer, pool, args.extra_only, packed_b, packed_fused_n)
+    if not args.no_floors and not args.extra_only:
+        floors = access_floors(torch, dev, timer, pool)
+        if floors is not None:
+            result["floors"] = floors
 
     print(json.dumps(result), flush=True)
 
