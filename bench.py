@@ -638,6 +638,23 @@ def access_floors(torch, dev, timer, pool32):
                 f"{nb / (us * 1e-6) / 1e9:.0f} GB/s")
     del poolb
     torch.cuda.empty_cache()
+    # packed fused N=128 T=5 (one accepted token): each head read from the
+    # sequence's first slot and written to its five checkpoint slots
+    lib.floor_read1_write_k.argtypes = [vp, vp, ci, ci, ci, ci, vp]
+    N, T = 128, 5
+    slots = 4 * N * T + 1
+    for hb, dt, name in ((D * D * 4, torch.float32, "fp32"), (D * D * 2, torch.bfloat16, "bf16")):
+        poolf = torch.zeros((slots, Hp, D, D), dtype=dt, device=dev)
+        pp = torch.randperm(slots - 1, generator=g, device=dev).to(torch.int32) + 1
+        calls = [lambda ids=pp[k * N * T:(k + 1) * N * T].contiguous(), hb=hb, poolf=poolf: ok(lib.floor_read1_write_k(
+            poolf.data_ptr(), ids.data_ptr(), N, Hp, hb, T, cur())) for k in range((slots - 1) // (N * T))]
+        us = rotating(torch, timer, calls)
+        nb = N * Hp * (1 + T) * hb
+        res[f"packed_fused_state_read1_write5_n128_h12_{name}"] = {"us": us, "GBps": nb / (us * 1e-6) / 1e9}
+        log(f"floor packed fused H=12 N=128 T=5 {name} state (1 read, 5 writes): {us:.1f} us, "
+            f"{nb / (us * 1e-6) / 1e9:.0f} GB/s")
+        del poolf
+        torch.cuda.empty_cache()
     return res
 
 

@@ -16,6 +16,10 @@
 //  * floor_rmw_slices: in place, one 256-thread workgroup per slice of 4,
 //    8, 16 or 32 KiB of a head, each lane 16 bytes per 4 KiB; rows whose slot
 //    is negative are skipped (null rows).
+//  * floor_read1_write_k: the packed fused call's state traffic, one
+//    256-thread workgroup per (sequence, head): the head block of the
+//    sequence's first slot is read once and written to each of its K slots
+//    (one per token).
 //
 // All loads and stores are nontemporal dwordx4, like the library's state
 // traffic.  Workgroups are numbered XCD by XCD as in the library.
@@ -82,6 +86,29 @@ __global__ void __launch_bounds__(256) rmw_slices_kernel(char *pool, const int *
         __builtin_nontemporal_store(v[i] * 0.999f + 0.001f, reinterpret_cast<f32x4 *>(base + i * 4096 + t16));
 }
 
+template <int NP>
+__global__ void __launch_bounds__(256) read1_write_k_kernel(char *pool, const int *idx, int n_work, int H,
+                                                            int head_bytes, int K)
+{
+    const int work = xcd_work();
+    if (work >= n_work) return;
+    const int seq = work / H, h = work - (work / H) * H;
+    const int *row = idx + (int64_t)seq * K;
+    const uint32_t t16 = 16u * threadIdx.x;
+    const char *src = pool + ((int64_t)row[0] * H + h) * head_bytes;
+    f32x4 v[NP];
+#pragma unroll
+    for (int i = 0; i < NP; ++i) v[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(src + i * 4096 + t16));
+    for (int k = 0; k < K; ++k) {
+        char *dst = pool + ((int64_t)row[k] * H + h) * head_bytes;
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+            v[i] = v[i] * 0.999f + 0.001f;
+            __builtin_nontemporal_store(v[i], reinterpret_cast<f32x4 *>(dst + i * 4096 + t16));
+        }
+    }
+}
+
 }  // namespace
 
 // n_seqs x H heads of 64 KiB, head (s, h) at pool + ((idx[s] * H) + h) * 64 KiB;
@@ -117,5 +144,20 @@ extern "C" __attribute__((visibility("default"))) int floor_rmw_slices(void *poo
     case 32768: hipLaunchKernelGGL(rmw_slices_kernel<8>, grid, block, 0, s, p, idx, n_work, H, head_bytes, ns); break;
     default: return -1;
     }
+    return hipGetLastError() == hipSuccess ? 0 : -2;
+}
+
+// n_seqs x H heads of head_bytes (32 or 64 KiB); idx: n_seqs x K slots; head
+// (s, h) is read from slot idx[s][0] and written to idx[s][0..K).
+extern "C" __attribute__((visibility("default"))) int floor_read1_write_k(void *pool, const int *idx, int n_seqs, int H,
+                                                                          int head_bytes, int K, void *stream)
+{
+    if (!pool || !idx || n_seqs <= 0 || H <= 0 || K <= 0 || (head_bytes != 32768 && head_bytes != 65536)) return -1;
+    const int n_work = n_seqs * H;
+    const dim3 grid((unsigned)((n_work + 7) & ~7)), block(256);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char *p = static_cast<char *>(pool);
+    if (head_bytes == 65536) hipLaunchKernelGGL(read1_write_k_kernel<16>, grid, block, 0, s, p, idx, n_work, H, head_bytes, K);
+    else hipLaunchKernelGGL(read1_write_k_kernel<8>, grid, block, 0, s, p, idx, n_work, H, head_bytes, K);
     return hipGetLastError() == hipSuccess ? 0 : -2;
 }
