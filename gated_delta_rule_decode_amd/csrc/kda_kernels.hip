@@ -1461,7 +1461,7 @@ kda_verify_wy_kernel(const RecParams p)
     constexpr int RPI = 64 / LPR;                // rows per load instruction of a wave
     constexpr int NLD = 16 / RPI;                // load instructions per 16-row tile
     constexpr int NPASS = LPR / 16;              // passes of 16 columns (16 bytes each) per tile
-    constexpr int PASSW = MF4 ? 2048 : 1024;     // a pass of one tile, or of both (4x4x1)
+    constexpr int PASSW = MF4 ? 2048 : 1024;     // a pass of half a tile, or a whole tile (4x4x1)
     constexpr int BUFW = WROWS * OST > PASSW ? WROWS * OST : PASSW;  // the passes, then the products
     __shared__ __align__(16) uint32_t s_T[4][BUFW];          // per wave
     __shared__ __align__(16) uint32_t s_B[OPB ? 2 : 1][NCOL][BST];  // token operand (or its bf16 head, remainder)
@@ -1714,60 +1714,50 @@ kda_verify_wy_kernel(const RecParams p)
     // fp32 pools with at most 4 token slots (4 or 8 operand columns) use the
     // 4x4x1 products instead, 16 blocks of 4 rows by 4 columns, so that no
     // operand column is padding: block 4 cp + rg (lanes 16 cp + 4 rg + 0..3)
-    // takes rows 4 rg .. 4 rg + 3 of a tile over channel part cp of the pass
-    // (its 16-byte columns 4 cp .. 4 cp + 3); both tiles go through the
-    // buffer in each pass, so that an operand read serves both; the four
-    // parts are then summed across the lanes.
+    // takes rows 4 rg .. 4 rg + 3 of a tile over channel part cp (its 16-byte
+    // columns 8 cp .. 8 cp + 7); a whole tile goes through the buffer at once,
+    // so the first tile's registers are free before the second's products;
+    // the four parts are then summed across the lanes.
     constexpr int NCS = MF4 ? NCOL / 4 : 1;      // 4x4x1: sets of 4 operand columns
     [[maybe_unused]] float mtot[2][NCS];         // 4x4x1: each lane's tile totals
     if constexpr (MF4) {
-        f32x4 d[2][NCS];
-#pragma unroll
-        for (int tau = 0; tau < 2; ++tau)
-#pragma unroll
-            for (int cs = 0; cs < NCS; ++cs) d[tau][cs] = f32x4{0.f, 0.f, 0.f, 0.f};
         const int cp = lane >> 4, rho = lane & 15;  // rho = 4 rg + (lane & 3)
+        auto tile4 = [&](int tau, const u32x4 (&raw)[NLD]) {
+            f32x4 d[NCS];
 #pragma unroll
-        for (int hh = 0; hh < NPASS; ++hh) {
-            const int c = lane % LPR - 16 * hh;
-            if (c >= 0 && c < 16) {
+            for (int cs = 0; cs < NCS; ++cs) d[cs] = f32x4{0.f, 0.f, 0.f, 0.f};
+            // the whole tile: 16-byte column c of row r at c ^ r
 #pragma unroll
-                for (int i = 0; i < NLD; ++i) {
-                    const int rw = RPI * i + lane / LPR;
-                    *reinterpret_cast<u32x4 *>(buf + 4 * (16 * rw + (c ^ rw))) = raw0[i];
-                    *reinterpret_cast<u32x4 *>(buf + 1024 + 4 * (16 * rw + (c ^ rw))) = raw1[i];
-                }
+            for (int i = 0; i < NLD; ++i) {
+                const int rw = RPI * i + lane / LPR, c = lane % LPR;
+                *reinterpret_cast<u32x4 *>(buf + 4 * (32 * rw + (c ^ rw))) = raw[i];
             }
             wave_lds_sync();
 #pragma unroll
-            for (int sq = 0; sq < 4; ++sq) {
-                const int c16 = 4 * cp + sq;  // 16-byte column of the pass
+            for (int sq = 0; sq < 8; ++sq) {
+                const int c32 = 8 * cp + sq;  // 16-byte column of the row
                 f32x4 bv[NCS];
 #pragma unroll
                 for (int cs = 0; cs < NCS; ++cs)
                     bv[cs] = *reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(s_B[0][4 * cs + (lane & 3)]) +
-                                                              64 * hh + 4 * c16);
+                                                              4 * c32);
+                const f32x4 a = *reinterpret_cast<const f32x4 *>(buf + 4 * (32 * rho + (c32 ^ rho)));
 #pragma unroll
-                for (int tau = 0; tau < 2; ++tau) {
-                    const f32x4 a = *reinterpret_cast<const f32x4 *>(buf + 1024 * tau + 4 * (16 * rho + (c16 ^ rho)));
+                for (int e = 0; e < 4; ++e)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-#pragma unroll
-                        for (int cs = 0; cs < NCS; ++cs)
-                            d[tau][cs] = __builtin_amdgcn_mfma_f32_4x4x1f32(a[e], bv[cs][e], d[tau][cs], 0, 0, 0);
-                }
+                    for (int cs = 0; cs < NCS; ++cs)
+                        d[cs] = __builtin_amdgcn_mfma_f32_4x4x1f32(a[e], bv[cs][e], d[cs], 0, 0, 0);
             }
             wave_lds_sync();
-        }
-        // lane 16 cp + 4 rg + j holds rows 4 rg + r (r = 0..3) of column
-        // 4 cs + j over part cp; halving at distances 32 and 16 leaves it the
-        // total of row 4 rg + cp
-#pragma unroll
-        for (int tau = 0; tau < 2; ++tau)
+            // lane 16 cp + 4 rg + j holds rows 4 rg + r (r = 0..3) of column
+            // 4 cs + j over part cp; halving at distances 32 and 16 leaves it
+            // the total of row 4 rg + cp
 #pragma unroll
             for (int cs = 0; cs < NCS; ++cs)
-                mtot[tau][cs] = swap16_sum(swap32_sum(d[tau][cs][0], d[tau][cs][2]),
-                                           swap32_sum(d[tau][cs][1], d[tau][cs][3]));
+                mtot[tau][cs] = swap16_sum(swap32_sum(d[cs][0], d[cs][2]), swap32_sum(d[cs][1], d[cs][3]));
+        };
+        tile4(0, raw0);
+        tile4(1, raw1);
     } else {
         tile_products(0, raw0);
         tile_products(1, raw1);
