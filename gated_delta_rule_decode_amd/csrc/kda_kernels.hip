@@ -94,9 +94,6 @@ __device__ __forceinline__ void wave_lds_sync()
 // (gfx9 encoding: vmcnt 0, expcnt 7, lgkmcnt 15 are "no wait" for the others).
 __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-// s_waitcnt lgkmcnt(0): every LDS access of this wave has completed (vmcnt 63, expcnt 7).
-__device__ __forceinline__ void wait_lgkm_all() { __builtin_amdgcn_s_waitcnt(0xC07F); }
-
 // Tokens staged per chunk by the token loops (measured on MI355X: the
 // recurrent loop keeps the next chunk's inputs in registers through the
 // current chunk, and two tokens per chunk keep it at 4 waves per SIMD; the
@@ -121,17 +118,6 @@ __device__ __forceinline__ float row_sum16(float x)
     x += dpp_mov<0x4E>(x);   // quad_perm [2,3,0,1]
     x += dpp_mov<0x141>(x);  // row_half_mirror
     x += dpp_mov<0x140>(x);  // row_mirror
-    return x;
-}
-
-// Sum over the 64 lanes of a wave, complete in lane 63: the DPP-row sums,
-// then row 0 into row 1 and row 2 into row 3 (row_bcast:15), then rows 0-1
-// into rows 2-3 (row_bcast:31).
-__device__ __forceinline__ float wave_total(float x)
-{
-    x = row_sum16(x);
-    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x142, 0xA, 0xF, false));
-    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x143, 0xC, 0xF, false));
     return x;
 }
 
@@ -1443,7 +1429,6 @@ kda_verify_wy_kernel(const RecParams p)
     constexpr int OST = NCOL + 4;                // floats per row of the products in LDS
     using CH = WyChunks<TM>;
     constexpr int NCH = CH::NCH;                 // chunks of channel sums
-    constexpr int NJ = LY::NJ;
     constexpr int SW = LY::SW;
     constexpr int NCF = 2 * TM * TM + 3 * TM;    // per-wave coefficients
     // fp32 pools: 4x4x1 fp32 products when at most 8 operand columns exist
@@ -1521,7 +1506,7 @@ kda_verify_wy_kernel(const RecParams p)
         return;
     }
 
-    // 2. the state: the first tile into registers (the second follows the channel phase)
+    // 2. the state, as whole rows: the first tile (the second follows the channel phase)
     uint32_t *buf = s_T[wave];
     const char *hstate = static_cast<const char *>(p.state) +
                          ((int64_t)it.idx * p.slot_stride + (int64_t)it.hv * (KD * KD)) * (BF16 ? 2 : 4);
@@ -1534,8 +1519,6 @@ kda_verify_wy_kernel(const RecParams p)
     };
     u32x4 raw0[NLD];
     load_tile(0, raw0);
-    // (the scheduling barriers keep other work, and the waits it would
-    // bring, from landing between the loads of the tile)
 
     // the key channel: decays, the operand column, the channel sums
     {
