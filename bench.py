@@ -438,6 +438,29 @@ def extra_workloads(torch, dev, timer, pool32, only=None, packed_b=None, packed_
             log(f"verify read-only B={Bv} T={Tv2} H=32 fp32: {t_us:.1f} us, {sweep[-1]['GBps']:.0f} GB/s")
         out["verify_tsweep_b64_h32_fp32"] = sweep
 
+    if want("verify_tsweep_b64_h32_bf16"):
+        # the same read-only batched calls on a bf16 pool [4096,32,128,128]
+        gb = torch.Generator(device=dev)
+        gb.manual_seed(7201)
+        pool16 = synth._randn_big(gb, (SLOTS, 32, D, D), dev, 0.05, torch.bfloat16)
+        sweep = []
+        for Tv2 in (2, 4, 8, 16):
+            vt = synth.recurrent_case(7200 + Tv2, n_seqs=Bv, H=32, num_slots=1, device=dev, lengths=[Tv2] * Bv)
+            ot = torch.empty((Bv, Tv2, 32, D), dtype=torch.bfloat16, device=dev)
+            rt = lambda t, n=Tv2: t.reshape(Bv, n, *t.shape[1:])  # noqa: E731
+            calls = [lambda ids=mperm[j * Bv:(j + 1) * Bv].contiguous(), vt=vt, ot=ot, rt=rt: recurrent_kda(
+                rt(vt.q), rt(vt.k), rt(vt.v), rt(vt.g), rt(vt.beta), vt.A_log, vt.dt_bias,
+                initial_state=pool16, state_indices=ids, output=ot, disable_state_update=True)
+                for j in range(16)]
+            t_us = rotating(torch, timer, calls)
+            bts = modes_bytes(Bv, Bv * Tv2, 32, 32, 2, write_state=False)
+            sweep.append({"B": Bv, "T": Tv2, "us": t_us, "GBps": bts / (t_us * 1e-6) / 1e9,
+                          "frac": bts / (t_us * 1e-6) / 1e9 / HBM_PEAK_GBPS})
+            log(f"verify read-only B={Bv} T={Tv2} H=32 bf16: {t_us:.1f} us, {sweep[-1]['GBps']:.0f} GB/s")
+        out["verify_tsweep_b64_h32_bf16"] = sweep
+        del pool16
+        torch.cuda.empty_cache()
+
     if want("verify_ragged_b64_h32_fp32"):
         # read-only ragged calls (cu_seqlens), B=64 H=32 fp32, lengths U{1..8},
         # the longest declared (8): the WY verify kernel
