@@ -113,14 +113,17 @@ def test_wy_verify_against_oracle(T, state_dtype, gate, gate_dtype, H, HV, t_max
     say(f"out err {e1:.3e} corr err {e2:.3e}")
 
 
-def test_wy_verify_with_underflowing_decay():
+@pytest.mark.parametrize("T,state_dtype", [(2, torch.float32), (4, torch.float32), (6, torch.float32),
+                                           (6, torch.bfloat16), (16, torch.float32)])
+def test_wy_verify_with_underflowing_decay(T, state_dtype):
     """Log-decays of -20..-90 per token: the cumulative decay underflows to
     zero in fp32 within a token or two; outputs and corrections stay finite
-    and match the oracle."""
-    T, n, H, slots = 6, 7, 4, 12
-    say(f"WY verify underflowing decay T={T} H={H} seed=7700")
-    c = synth.recurrent_case(7700, n_seqs=n, H=H, num_slots=slots, device=DEV, indices="random", lengths=[T] * n,
-                             gate="precomputed", gate_dtype=torch.float32)
+    and match the oracle (every product form: fp32 4x4x1 at 2 and 4 tokens,
+    16x16x4 at 6, the bf16 split at 16, bf16 pools)."""
+    n, H, slots = 7, 4, 12
+    say(f"WY verify underflowing decay T={T} H={H} {state_dtype} seed=7700")
+    c = synth.recurrent_case(7700, n_seqs=n, H=H, num_slots=slots, state_dtype=state_dtype, device=DEV,
+                             indices="random", lengths=[T] * n, gate="precomputed", gate_dtype=torch.float32)
     gen = torch.Generator(device=DEV)
     gen.manual_seed(7700)
     c.g.copy_(-(20.0 + 70.0 * torch.rand(c.g.shape, generator=gen, device=DEV)))
