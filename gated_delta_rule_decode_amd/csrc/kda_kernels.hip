@@ -1416,8 +1416,10 @@ struct WyLayout {
 //     and l + 32 own row l & 31 and store alternate tokens).
 // Four to five workgroups share a compute unit (the VGPRs decide), so the
 // loads of one overlap the arithmetic of the others.  Consecutive heads
-// (which share their sequence's token rows) run on one XCD.
-template <bool BF16, int TM>
+// (which share their sequence's token rows) run on one XCD.  KGC: the call
+// records the raw key and gate cache (a kernel of its own, so that calls
+// without it carry none of its stores).
+template <bool BF16, int TM, bool KGC>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TM <= 4 ? (BF16 ? 5 : 4) : (TM <= 8 ? 4 : 2))))
 kda_verify_wy_kernel(const RecParams p)
 {
@@ -1520,9 +1522,14 @@ kda_verify_wy_kernel(const RecParams p)
     u32x4 raw0[NLD];
     load_tile(0, raw0);
 
-    // the key channel: decays, the operand column, the channel sums
-    {
-        if (A && p.kg) {  // verify cache of the raw key and gate
+    // verify cache of the raw key and gate (lanes of layout A, their channel).
+    // With at most 4 token slots these stores go after the outputs: issued
+    // earlier, they sit between the state loads and the waits for them (the
+    // in-order memory counter), which cost ~1 us at B=64 H=32; with more
+    // slots the registers they keep live cost more than that.
+    constexpr bool KG_LATE = TM <= 4;
+    auto store_kg_rows = [&]() {
+        if (KGC && A) {
 #pragma unroll
             for (int t = 0; t < TM; ++t) {
                 if (t < it.n && t < p.t_max) {
@@ -1534,6 +1541,11 @@ kda_verify_wy_kernel(const RecParams p)
                 }
             }
         }
+    };
+
+    // the key channel: decays, the operand column, the channel sums
+    {
+        if constexpr (!KG_LATE) store_kg_rows();
         const bool precomputed = p.precomputed != 0;
         const float a_h = precomputed ? 0.f : __expf(p.A_log[it.hv]);
         const float dtc = precomputed ? 0.f : p.dt_bias[(int64_t)it.hv * KD + c];
@@ -1796,6 +1808,7 @@ kda_verify_wy_kernel(const RecParams p)
             }
         }
     }
+    if constexpr (KG_LATE) store_kg_rows();
     // tokens past the declared length: +0
     for (int i = tid; i < (it.len - it.n) * KD; i += 256)
         p.out[((int64_t)(it.t0 + it.n + i / KD) * p.HV + it.hv) * KD + (i & (KD - 1))] = 0;
@@ -1850,8 +1863,13 @@ int launch_recurrent(const RecParams &p, const Launch &l, void *stream)
         const dim3 grid(l.grid), block(l.block);
 #define KDA_WY(TM_)                                                                                      \
     do {                                                                                                 \
-        if (l.bf16_state) hipLaunchKernelGGL((kda_verify_wy_kernel<true, TM_>), grid, block, 0, s, p);   \
-        else hipLaunchKernelGGL((kda_verify_wy_kernel<false, TM_>), grid, block, 0, s, p);               \
+        if (p.kg) {                                                                                      \
+            if (l.bf16_state) hipLaunchKernelGGL((kda_verify_wy_kernel<true, TM_, true>), grid, block, 0, s, p);  \
+            else hipLaunchKernelGGL((kda_verify_wy_kernel<false, TM_, true>), grid, block, 0, s, p);     \
+        } else {                                                                                         \
+            if (l.bf16_state) hipLaunchKernelGGL((kda_verify_wy_kernel<true, TM_, false>), grid, block, 0, s, p); \
+            else hipLaunchKernelGGL((kda_verify_wy_kernel<false, TM_, false>), grid, block, 0, s, p);    \
+        }                                                                                                \
     } while (0)
         if (p.tps <= 2) KDA_WY(2);
         else if (p.tps <= 4) KDA_WY(4);
