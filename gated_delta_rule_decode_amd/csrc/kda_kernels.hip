@@ -1482,6 +1482,8 @@ kda_verify_wy_kernel(const RecParams p)
     const bool beta_f32 = p.beta_f32 != 0;
     uint32_t xb[TM], kb[TM], glo[TM], ghi[TM], vb[TM];
     uint32_t beta_lo = 0, beta_hi = 0;
+    const bool precomputed = p.precomputed != 0;
+    float dtc_raw;
     {
         // (layout B reads k twice rather than copy it: a copy would wait for the load)
         const uint16_t *xs = A ? p.q : p.k;
@@ -1499,9 +1501,16 @@ kda_verify_wy_kernel(const RecParams p)
         load_halves(static_cast<const char *>(p.beta) +
                         (tok(min(lane, TM - 1)) * p.beta_stride + it.hv) * (beta_f32 ? 4 : 2),
                     beta_f32, beta_lo, beta_hi);
+        // the channel's dt_bias, loaded on every path (a precomputed gate has
+        // none: q's first word instead, unused) -- a load under the gate-mode
+        // branch made the decays wait for every load issued before them,
+        // the state's included
+        dtc_raw = precomputed ? *reinterpret_cast<const float *>(p.q) : p.dt_bias[(int64_t)it.hv * KD + c];
 #pragma unroll
         for (int t = 0; t < TM; ++t) vb[t] = p.v[tok(t) * p.v_stride + (int64_t)it.hv * KD + vrow];
     }
+    // (the token inputs stay ahead of the state's loads in the memory counter)
+    __builtin_amdgcn_sched_barrier(0);
     if (!it.live) {  // a null head: +0 for each of its tokens
         for (int i = tid; i < it.len * KD; i += 256)
             p.out[((int64_t)(it.t0 + i / KD) * p.HV + it.hv) * KD + (i & (KD - 1))] = 0;
@@ -1546,9 +1555,8 @@ kda_verify_wy_kernel(const RecParams p)
     // the key channel: decays, the operand column, the channel sums
     {
         if constexpr (!KG_LATE) store_kg_rows();
-        const bool precomputed = p.precomputed != 0;
         const float a_h = precomputed ? 0.f : __expf(p.A_log[it.hv]);
-        const float dtc = precomputed ? 0.f : p.dt_bias[(int64_t)it.hv * KD + c];
+        const float dtc = precomputed ? 0.f : dtc_raw;
         float xf[TM], kf[TM], d[TM];
         float L = 0.f;
 #pragma unroll
