@@ -644,12 +644,24 @@ __global__ void __launch_bounds__(256) kda_recurrent_kernel(const RecParams p)
         TokenOps ops;
         read_token_ops<BF16>(ops, s_q[0], s_k[0], s_d[0], s_norm[0], m, p.scale, p.l2_eps, beta);
         float o[G], c[G];
+        // bf16 pools: every row first, then the stores.  A store (counted
+        // with the loads in the in-order memory counter) under the read-only
+        // branch between two rows made the second row wait for the first
+        // row's store; measured 2-6% faster for H=12 bf16 at 64-512 rows.
+        // fp32 pools keep each row's store next to its update (storing at
+        // the end measured 13-15% slower for H=32 fp32 at 128-512 rows).
+        constexpr bool STORE_LAST = BF16;
 #pragma unroll
         for (int gi = 0; gi < G; ++gi) {
             float st[8];
             IO::unpack(raw[gi], st);
             o[gi] = row_update(st, ops, s_v[0][r_base + gi], c[gi]);
-            if (update) IO::store(head, off[gi], IO::pack(st));
+            raw[gi] = IO::pack(st);
+            if (!STORE_LAST && update) IO::store(head, off[gi], raw[gi]);
+        }
+        if (STORE_LAST && update) {
+#pragma unroll
+            for (int gi = 0; gi < G; ++gi) IO::store(head, off[gi], raw[gi]);
         }
         if (m == 0) store_out_bf16<G>(p.out + ((int64_t)t0 * p.HV + hv) * KD + r_base, o);
         if (p.t_max > 0) {
