@@ -1342,8 +1342,7 @@ struct WyChunks {
 // (s <= t), layout B (x = k) |k_t|^2 and k_t.W_ts k_s (s < t).  kw[s]
 // carries k_s * W_ts across the chunks.
 template <int TM, int K, bool A>
-__device__ __forceinline__ float wy_chunk_layout(float *kw, const float *x, const float *kf, const float *d, int n,
-                                                 int lane)
+__device__ __forceinline__ float wy_chunk_layout(float *kw, const float *x, const float *kf, const float *d, int lane)
 {
     using C = WyChunks<TM>;
     constexpr int P = C::P(K);
@@ -1353,28 +1352,26 @@ __device__ __forceinline__ float wy_chunk_layout(float *kw, const float *x, cons
 #pragma unroll
     for (int tt = 0; tt < C::TPC; ++tt) {
         const int t = C::first(K) + tt;
-        const bool on = t < n;
 #pragma unroll
         for (int s = 0; s < t; ++s) kw[s] *= d[t];  // k_s * W_ts
         kw[t] = kf[t];
         const int o = C::off(t, A);
-        cur[o] = on ? x[t] * x[t] : 0.f;
+        cur[o] = x[t] * x[t];
 #pragma unroll
-        for (int s = 0; s < (A ? t + 1 : t); ++s) cur[o + 1 + s] = on ? x[t] * kw[s] : 0.f;
+        for (int s = 0; s < (A ? t + 1 : t); ++s) cur[o + 1 + s] = x[t] * kw[s];
     }
     return wave_transpose_sum<P>(cur, lane);
 }
 
 template <int TM, bool A>
-__device__ __forceinline__ void wy_layout_sums(float *r, const float *x, const float *kf, const float *d, int n,
-                                               int lane)
+__device__ __forceinline__ void wy_layout_sums(float *r, const float *x, const float *kf, const float *d, int lane)
 {
     constexpr int NCH = WyChunks<TM>::NCH;
     float kw[TM];
-    r[0] = wy_chunk_layout<TM, 0, A>(kw, x, kf, d, n, lane);
-    if constexpr (NCH > 1) r[1] = wy_chunk_layout<TM, (NCH > 1 ? 1 : 0), A>(kw, x, kf, d, n, lane);
-    if constexpr (NCH > 2) r[2] = wy_chunk_layout<TM, (NCH > 2 ? 2 : 0), A>(kw, x, kf, d, n, lane);
-    if constexpr (NCH > 3) r[3] = wy_chunk_layout<TM, (NCH > 3 ? 3 : 0), A>(kw, x, kf, d, n, lane);
+    r[0] = wy_chunk_layout<TM, 0, A>(kw, x, kf, d, lane);
+    if constexpr (NCH > 1) r[1] = wy_chunk_layout<TM, (NCH > 1 ? 1 : 0), A>(kw, x, kf, d, lane);
+    if constexpr (NCH > 2) r[2] = wy_chunk_layout<TM, (NCH > 2 ? 2 : 0), A>(kw, x, kf, d, lane);
+    if constexpr (NCH > 3) r[3] = wy_chunk_layout<TM, (NCH > 3 ? 3 : 0), A>(kw, x, kf, d, lane);
 }
 
 // Per-head metadata: the sequence's tokens, the pool slot, the heads.
@@ -1585,17 +1582,17 @@ kda_verify_wy_kernel(const RecParams p)
         const float a_h = precomputed ? 0.f : __expf(p.A_log[it.hv]);
         const float dtc = precomputed ? 0.f : dtc_raw;
         float xf[TM], kf[TM], d[TM];
-        float L = 0.f;
+        float E = 1.f;
 #pragma unroll
         for (int t = 0; t < TM; ++t) {
             const float gv = halves_value(glo[t], ghi[t], g_f32);
             const float lg = precomputed ? gv : -a_h * softplus_f(gv + dtc);
-            L += lg;
             d[t] = __expf(lg);
+            E *= d[t];
             xf[t] = bf16_bits_to_f32(xb[t]);
             kf[t] = bf16_bits_to_f32(kb[t]);
             // operand column: q_t E_t (layout A) or k_t E_t (layout B)
-            const float ov = t < it.n ? xf[t] * __expf(L) : 0.f;
+            const float ov = t < it.n ? xf[t] * E : 0.f;
             const int col = A ? TM + t : t;
             if constexpr (OPB) {
                 const __bf16 hb = (__bf16)ov;
@@ -1607,8 +1604,8 @@ kda_verify_wy_kernel(const RecParams p)
             }
         }
         float r[NCH];
-        if (A) wy_layout_sums<TM, true>(r, xf, kf, d, it.n, lane);
-        else wy_layout_sums<TM, false>(r, xf, kf, d, it.n, lane);
+        if (A) wy_layout_sums<TM, true>(r, xf, kf, d, lane);
+        else wy_layout_sums<TM, false>(r, xf, kf, d, lane);
         constexpr int S0 = 64 / CH::P(0), S1 = 64 / CH::P(NCH > 1 ? 1 : 0);
         constexpr int S2 = 64 / CH::P(NCH > 2 ? 2 : 0), S3 = 64 / CH::P(NCH > 3 ? 3 : 0);
 #pragma unroll
@@ -1827,19 +1824,24 @@ kda_verify_wy_kernel(const RecParams p)
     const int64_t crow0 = ((int64_t)it.idx * p.HV + it.hv) * p.t_max;
     const float *Cm = cf, *Am = cf + TM * TM, *tk = cf + 2 * TM * TM;
 #pragma unroll
-    for (int t = 0; t < TM; ++t) {
-        if (t < it.n) {
-            float x = tk[t] * P[t];
+    for (int j = 0; j < TM / 2; ++j) {
+        if (2 * j < it.n) {
 #pragma unroll
-            for (int s = 0; s < t; ++s) x = fmaf(Cm[t * TM + s], bu[s], x);
-            bu[t] = tk[2 * TM + t] * (bf16_bits_to_f32(vb[t]) - x);
-            if ((t & 1) == half) {
-                float y = Q[t];
+            for (int t = 2 * j; t < 2 * j + 2; ++t) {
+                float x = tk[t] * P[t];
 #pragma unroll
-                for (int s = 0; s <= t; ++s) y = fmaf(Am[t * TM + s], bu[s], y);
-                y *= tk[TM + t];
-                p.out[((int64_t)(it.t0 + t) * p.HV + it.hv) * KD + vrow] = (uint16_t)(pack_bf16x2(y, 0.0f) & 0xffffu);
-                if (p.corr && t < p.t_max) p.corr[(crow0 + t) * KD + vrow] = bu[t];
+                for (int s = 0; s < t; ++s) x = fmaf(Cm[t * TM + s], bu[s], x);
+                bu[t] = t < it.n ? tk[2 * TM + t] * (bf16_bits_to_f32(vb[t]) - x) : 0.f;
+            }
+            const int th = 2 * j + half;
+            const float *ar = Am + th * TM;
+            float y = half ? Q[2 * j + 1] : Q[2 * j];
+#pragma unroll
+            for (int s = 0; s <= 2 * j + 1; ++s) y = fmaf(ar[s], bu[s], y);
+            y *= tk[TM + th];
+            if (th < it.n) {
+                p.out[((int64_t)(it.t0 + th) * p.HV + it.hv) * KD + vrow] = (uint16_t)(pack_bf16x2(y, 0.0f) & 0xffffu);
+                if (p.corr && th < p.t_max) p.corr[(crow0 + th) * KD + vrow] = half ? bu[2 * j + 1] : bu[2 * j];
             }
         }
     }
