@@ -1826,6 +1826,14 @@ kda_verify_wy_kernel(const RecParams p)
         Q[t2] = y.x; Q[t2 + 1] = y.y;
     }
     const int half = lane >> 5;
+    // the value of the lane's half of a token pair, by a bit select on an
+    // opaque mask (a plain select of two array elements became an indexed
+    // pick over the whole array, through a private array in scratch)
+    uint32_t hmask = 0u - (uint32_t)half;  // all ones in the upper half of the wave
+    asm("" : "+v"(hmask));
+    auto pick = [&](float a, float b) {
+        return __uint_as_float(__float_as_uint(a) ^ ((__float_as_uint(a) ^ __float_as_uint(b)) & hmask));
+    };
     const int64_t crow0 = ((int64_t)it.idx * p.HV + it.hv) * p.t_max;
     const float *Cm = cf, *Am = cf + TM * TM, *tk = cf + 2 * TM * TM;
 #pragma unroll
@@ -1840,13 +1848,13 @@ kda_verify_wy_kernel(const RecParams p)
             }
             const int th = 2 * j + half;
             const float *ar = Am + th * TM;
-            float y = half ? Q[2 * j + 1] : Q[2 * j];
+            float y = pick(Q[2 * j], Q[2 * j + 1]);
 #pragma unroll
             for (int s = 0; s <= 2 * j + 1; ++s) y = fmaf(ar[s], bu[s], y);
             y *= tk[TM + th];
             if (th < it.n) {
                 p.out[((int64_t)(it.t0 + th) * p.HV + it.hv) * KD + vrow] = (uint16_t)(pack_bf16x2(y, 0.0f) & 0xffffu);
-                if (p.corr && th < p.t_max) p.corr[(crow0 + th) * KD + vrow] = half ? bu[2 * j + 1] : bu[2 * j];
+                if (p.corr && th < p.t_max) p.corr[(crow0 + th) * KD + vrow] = pick(bu[2 * j], bu[2 * j + 1]);
             }
         }
     }
