@@ -282,7 +282,16 @@ int prepare_recurrent(const kda_recurrent_args *a, RecParams *p, Launch *l)
     // declares in tokens_per_seq): the tokens' reads of the initial state
     // become one matrix product per head, on the WY verify kernel.
     const int64_t bound = ragged ? a->tokens_per_seq : tps;
-    const bool wy = !update && !a->checkpoints && bound >= (ragged ? 1 : 2) && bound <= VERIFY_WY_MAX_T;
+    // (that kernel addresses a sequence's token rows by 32-bit byte offsets
+    // from its first row: every input's last row, at its widest lane, lies
+    // within 2^31 bytes of the first)
+    auto rows_fit = [&](int64_t stride, int64_t span, int64_t es) {
+        return (u128)(uint64_t)(bound - 1) * (uint64_t)stride * (uint64_t)es + (u128)(uint64_t)span * (uint64_t)es <
+               ((u128)1 << 31);
+    };
+    const bool wy = !update && !a->checkpoints && bound >= (ragged ? 1 : 2) && bound <= VERIFY_WY_MAX_T &&
+                    rows_fit(a->q_stride, HQ, 2) && rows_fit(a->k_stride, HQ, 2) && rows_fit(a->v_stride, HVC, 2) &&
+                    rows_fit(a->g_stride, HVC, g_es) && rows_fit(a->beta_stride, a->HV, b_es);
     const int vsplit = wy ? 1 : choose_vsplit(items, a->state_dtype == KDA_DTYPE_BF16, token_loop,
                                                  a->checkpoints != nullptr && a->state_dtype == KDA_DTYPE_F32, update);
     if (items * vsplit > 0x7ffffff0LL) return fail(KDA_ERR_SHAPE, "too many work items");

@@ -1499,10 +1499,16 @@ kda_verify_wy_kernel(const RecParams p)
     const int work = (int)(blockIdx.x & 7u) * (int)(gridDim.x >> 3) + (int)(blockIdx.x >> 3);
     if (work >= p.n_work) return;
     const WyItem it = wy_item(p, work);
-    // token row t of the sequence (clamped to its last evaluated token); a
+    // Token row t of the sequence, clamped to its last evaluated token; a
     // sequence without tokens reads row 0, which exists (a call without any
-    // token launches nothing), and uses none of it
-    auto tok = [&](int t) { return it.n > 0 ? (int64_t)it.t0 + min(t, it.n - 1) : (int64_t)0; };
+    // token launches nothing), and uses none of it.  Each input is addressed
+    // as a wave-uniform base at the sequence's first row plus a 32-bit
+    // per-lane offset (the host takes this kernel only when every input's
+    // last token row lies within 2^31 bytes of the first), which keeps the
+    // per-token address arithmetic to one multiply and one add.
+    const int64_t row0 = it.n > 0 ? (int64_t)it.t0 : 0;
+    const int last = it.n > 0 ? it.n - 1 : 0;
+    auto rel = [&](int t) { return (uint32_t)min(t, last); };  // row t relative to row0
 
     // 1. the token inputs of key channel c, and the value row
     const bool A = wave < 2;
@@ -1515,20 +1521,24 @@ kda_verify_wy_kernel(const RecParams p)
     float dtc_raw;
     {
         // (layout B reads k twice rather than copy it: a copy would wait for the load)
-        const uint16_t *xs = A ? p.q : p.k;
-        const int64_t xstride = A ? p.q_stride : p.k_stride;
+        const int ges = g_f32 ? 4 : 2, bes = beta_f32 ? 4 : 2;
+        const char *kq = reinterpret_cast<const char *>(p.k) + row0 * p.k_stride * 2;
+        const char *xq = reinterpret_cast<const char *>(A ? p.q : p.k) + row0 * (A ? p.q_stride : p.k_stride) * 2;
+        const char *gq = static_cast<const char *>(p.g) + row0 * p.g_stride * ges;
+        const uint32_t kst = (uint32_t)p.k_stride * 2, xst = (uint32_t)(A ? p.q_stride : p.k_stride) * 2;
+        const uint32_t gst = (uint32_t)p.g_stride * (uint32_t)ges;
+        const uint32_t kl = (uint32_t)(it.hq * KD + c) * 2, gl = (uint32_t)(it.hv * KD + c) * (uint32_t)ges;
 #pragma unroll
         for (int t = 0; t < TM; ++t) {
-            const int64_t n_ = tok(t);
-            kb[t] = p.k[n_ * p.k_stride + (int64_t)it.hq * KD + c];
-            xb[t] = xs[n_ * xstride + (int64_t)it.hq * KD + c];
-            load_halves(static_cast<const char *>(p.g) + (n_ * p.g_stride + (int64_t)it.hv * KD + c) * (g_f32 ? 4 : 2),
-                        g_f32, glo[t], ghi[t]);
+            const uint32_t r = rel(t);
+            kb[t] = *reinterpret_cast<const uint16_t *>(kq + (kl + r * kst));
+            xb[t] = *reinterpret_cast<const uint16_t *>(xq + (kl + r * xst));
+            load_halves(gq + (gl + r * gst), g_f32, glo[t], ghi[t]);
         }
         // (every lane loads a beta, lanes t < TM of wave 2 keep token t's:
         // a load under a lane condition would wait for its value at the join)
-        load_halves(static_cast<const char *>(p.beta) +
-                        (tok(min(lane, TM - 1)) * p.beta_stride + it.hv) * (beta_f32 ? 4 : 2),
+        load_halves(static_cast<const char *>(p.beta) + row0 * p.beta_stride * bes +
+                        (rel(min(lane, TM - 1)) * (uint32_t)p.beta_stride + (uint32_t)it.hv) * (uint32_t)bes,
                     beta_f32, beta_lo, beta_hi);
         // the channel's dt_bias, loaded on every path (a precomputed gate has
         // none: q's first word instead, unused) -- a load under the gate-mode
@@ -1536,7 +1546,9 @@ kda_verify_wy_kernel(const RecParams p)
         // the state's included
         dtc_raw = precomputed ? *reinterpret_cast<const float *>(p.q) : p.dt_bias[(int64_t)it.hv * KD + c];
 #pragma unroll
-        for (int t = 0; t < TM; ++t) vb[t] = p.v[tok(t) * p.v_stride + (int64_t)it.hv * KD + vrow];
+        for (int t = 0; t < TM; ++t)
+            vb[t] = *reinterpret_cast<const uint16_t *>(reinterpret_cast<const char *>(p.v) + row0 * p.v_stride * 2 +
+                                                        ((uint32_t)(it.hv * KD + vrow) * 2 + rel(t) * ((uint32_t)p.v_stride * 2)));
     }
     // (the token inputs stay ahead of the state's loads in the memory counter)
     __builtin_amdgcn_sched_barrier(0);

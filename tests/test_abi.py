@@ -419,6 +419,23 @@ def test_calls_outside_the_wy_verify_kernel_keep_the_token_loop():
     a = rec_args(N=8)
     a.flags = 1
     assert plan_rec(a)[1].kernel == 1  # one token
+    for f in ("q", "k", "v", "g", "beta"):
+        # an input whose last token row of a sequence lies 2^31 bytes or more
+        # past the first (the verify kernel's 32-bit row offsets)
+        a = rec_args(N=8, tps=4)
+        a.flags = 1
+        es = 4 if f == "beta" else 2  # beta as fp32, the others bf16
+        if f == "beta":
+            a.beta_dtype = 0
+        stride = (1 << 31) // (3 * es) + 1  # 3 rows past the first: just beyond 2^31 bytes
+        setattr(a, f + "_stride", stride)
+        A = Arena()
+        A.next = 1 << 44
+        setattr(a, f, A.take(32 * stride * 4))
+        assert plan_rec(a)[0] == 0, err()
+        assert plan_rec(a)[1].kernel == 2, f
+        setattr(a, f + "_stride", stride - 4096)  # within 2^31: the verify kernel again
+        assert plan_rec(a)[1].kernel == 5, f
 
 
 def test_read_only_pool_still_may_not_alias_outputs():
