@@ -1319,24 +1319,42 @@ constexpr int pow2_at_least(int x)
 // Channel sums of the WY verify kernel: layout A holds |q_t|^2 and
 // q_t.W_ts k_s (s <= t), t + 2 sums for token t; layout B |k_t|^2 and
 // k_t.W_ts k_s (s < t), t + 1 sums.  They are emitted in chunks of whole
-// tokens (TPC tokens per chunk), each reduced over the wave at once; in
-// chunk k, token t's sums start at off(t) (norm first, then s = 0, 1, ...).
-template <int TM>
+// tokens, each reduced over the wave at once; chunk k holds tokens
+// [first(k), first(k + 1)), and token t's sums start at off(t) in its chunk
+// (norm first, then s = 0, 1, ...).  Chunks of 4 tokens; with SIX (fp32
+// pools at 16 token slots) six chunks of at most 32 sums each instead: a
+// chunk of 64 sums keeps 32 more registers live while it is formed, which
+// there decides between two and three workgroups per compute unit (bf16
+// pools fit three with the four chunks, which take fewer instructions).
+template <int TM, bool SIX>
 struct WyChunks {
-    static constexpr int TPC = TM > 4 ? 4 : TM;   // tokens per chunk
-    static constexpr int NCH = TM / TPC;
-    static constexpr int first(int k) { return k * TPC; }
+    static_assert(!SIX || TM == 16, "six chunks: 16 token slots");
+    static constexpr int NCH = SIX ? 6 : (TM > 4 ? TM / 4 : 1);
+    static constexpr int first(int k)
+    {
+        if (SIX) {
+            constexpr int b[7] = {0, 6, 9, 11, 13, 15, 16};
+            return b[k];
+        }
+        return k * (TM > 4 ? 4 : TM);
+    }
+    static constexpr int chunk_of(int t)
+    {
+        int k = 0;
+        while (first(k + 1) <= t) ++k;
+        return k;
+    }
     // offset of token t in its chunk, layout A or B
     static constexpr int off(int t, bool a)
     {
         int o = 0;
-        for (int u = (t / TPC) * TPC; u < t; ++u) o += u + (a ? 2 : 1);
+        for (int u = first(chunk_of(t)); u < t; ++u) o += u + (a ? 2 : 1);
         return o;
     }
     static constexpr int size(int k)  // layout A, the larger
     {
         int o = 0;
-        for (int u = first(k); u < first(k) + TPC; ++u) o += u + 2;
+        for (int u = first(k); u < first(k + 1); ++u) o += u + 2;
         return o;
     }
     static constexpr int P(int k) { return pow2_at_least(size(k)); }
@@ -1346,17 +1364,16 @@ struct WyChunks {
 // wave chunk by chunk: layout A (x = q) holds |q_t|^2 and q_t.W_ts k_s
 // (s <= t), layout B (x = k) |k_t|^2 and k_t.W_ts k_s (s < t).  kw[s]
 // carries k_s * W_ts across the chunks.
-template <int TM, int K, bool A>
+template <int TM, bool SIX, int K, bool A>
 __device__ __forceinline__ float wy_chunk_layout(float *kw, const float *x, const float *kf, const float *d, int lane)
 {
-    using C = WyChunks<TM>;
+    using C = WyChunks<TM, SIX>;
     constexpr int P = C::P(K);
     float cur[P];
 #pragma unroll
     for (int i = 0; i < P; ++i) cur[i] = 0.f;
 #pragma unroll
-    for (int tt = 0; tt < C::TPC; ++tt) {
-        const int t = C::first(K) + tt;
+    for (int t = C::first(K); t < C::first(K + 1); ++t) {
 #pragma unroll
         for (int s = 0; s < t; ++s) kw[s] *= d[t];  // k_s * W_ts
         kw[t] = kf[t];
@@ -1368,15 +1385,17 @@ __device__ __forceinline__ float wy_chunk_layout(float *kw, const float *x, cons
     return wave_transpose_sum<P>(cur, lane);
 }
 
-template <int TM, bool A>
+template <int TM, bool SIX, bool A>
 __device__ __forceinline__ void wy_layout_sums(float *r, const float *x, const float *kf, const float *d, int lane)
 {
-    constexpr int NCH = WyChunks<TM>::NCH;
+    constexpr int NCH = WyChunks<TM, SIX>::NCH;
     float kw[TM];
-    r[0] = wy_chunk_layout<TM, 0, A>(kw, x, kf, d, lane);
-    if constexpr (NCH > 1) r[1] = wy_chunk_layout<TM, (NCH > 1 ? 1 : 0), A>(kw, x, kf, d, lane);
-    if constexpr (NCH > 2) r[2] = wy_chunk_layout<TM, (NCH > 2 ? 2 : 0), A>(kw, x, kf, d, lane);
-    if constexpr (NCH > 3) r[3] = wy_chunk_layout<TM, (NCH > 3 ? 3 : 0), A>(kw, x, kf, d, lane);
+    r[0] = wy_chunk_layout<TM, SIX, 0, A>(kw, x, kf, d, lane);
+    if constexpr (NCH > 1) r[1] = wy_chunk_layout<TM, SIX, (NCH > 1 ? 1 : 0), A>(kw, x, kf, d, lane);
+    if constexpr (NCH > 2) r[2] = wy_chunk_layout<TM, SIX, (NCH > 2 ? 2 : 0), A>(kw, x, kf, d, lane);
+    if constexpr (NCH > 3) r[3] = wy_chunk_layout<TM, SIX, (NCH > 3 ? 3 : 0), A>(kw, x, kf, d, lane);
+    if constexpr (NCH > 4) r[4] = wy_chunk_layout<TM, SIX, (NCH > 4 ? 4 : 0), A>(kw, x, kf, d, lane);
+    if constexpr (NCH > 5) r[5] = wy_chunk_layout<TM, SIX, (NCH > 5 ? 5 : 0), A>(kw, x, kf, d, lane);
 }
 
 // Per-head metadata: the sequence's tokens, the pool slot, the heads.
@@ -1449,7 +1468,7 @@ struct WyLayout {
 // records the raw key and gate cache (a kernel of its own, so that calls
 // without it carry none of its stores).
 template <bool BF16, int TM, bool KGC>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TM <= 4 ? (BF16 ? 5 : 4) : (TM <= 8 ? 4 : 2))))
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TM <= 4 ? (BF16 ? 5 : 4) : (TM <= 8 ? 4 : 3))))
 kda_verify_wy_kernel(const RecParams p)
 {
     using LY = WyLayout<BF16>;
@@ -1458,7 +1477,7 @@ kda_verify_wy_kernel(const RecParams p)
     constexpr int NCT = (2 * TM + 15) / 16;      // 16-column tiles of the token operand
     constexpr int NCOL = 2 * TM;                 // columns: k_t E_t at t, q_t E_t at TM + t
     constexpr int OST = NCOL + 4;                // floats per row of the products in LDS
-    using CH = WyChunks<TM>;
+    using CH = WyChunks<TM, !BF16 && TM == 16>;
     constexpr int NCH = CH::NCH;                 // chunks of channel sums
     constexpr int SW = LY::SW;
     constexpr int NCF = 2 * TM * TM + 3 * TM;    // per-wave coefficients
@@ -1516,6 +1535,16 @@ kda_verify_wy_kernel(const RecParams p)
     const bool g_f32 = p.g_f32 != 0;
     const bool beta_f32 = p.beta_f32 != 0;
     uint32_t xb[TM], kb[TM], glo[TM], ghi[TM], vb[TM];
+    // the value rows' inputs, used only by the forward substitution: at 16
+    // token slots loaded after the channel phase (with the second tile), so
+    // that they hold no registers through it
+    constexpr bool V_LATE = TM == 16;
+    auto load_v = [&]() {
+#pragma unroll
+        for (int t = 0; t < TM; ++t)
+            vb[t] = *reinterpret_cast<const uint16_t *>(reinterpret_cast<const char *>(p.v) + row0 * p.v_stride * 2 +
+                                                        ((uint32_t)(it.hv * KD + vrow) * 2 + rel(t) * ((uint32_t)p.v_stride * 2)));
+    };
     uint32_t beta_lo = 0, beta_hi = 0;
     const bool precomputed = p.precomputed != 0;
     float dtc_raw;
@@ -1545,10 +1574,7 @@ kda_verify_wy_kernel(const RecParams p)
         // branch made the decays wait for every load issued before them,
         // the state's included
         dtc_raw = precomputed ? *reinterpret_cast<const float *>(p.q) : p.dt_bias[(int64_t)it.hv * KD + c];
-#pragma unroll
-        for (int t = 0; t < TM; ++t)
-            vb[t] = *reinterpret_cast<const uint16_t *>(reinterpret_cast<const char *>(p.v) + row0 * p.v_stride * 2 +
-                                                        ((uint32_t)(it.hv * KD + vrow) * 2 + rel(t) * ((uint32_t)p.v_stride * 2)));
+        if constexpr (!V_LATE) load_v();
     }
     // (the token inputs stay ahead of the state's loads in the memory counter)
     __builtin_amdgcn_sched_barrier(0);
@@ -1621,13 +1647,14 @@ kda_verify_wy_kernel(const RecParams p)
             }
         }
         float r[NCH];
-        if (A) wy_layout_sums<TM, true>(r, xf, kf, d, lane);
-        else wy_layout_sums<TM, false>(r, xf, kf, d, lane);
-        constexpr int S0 = 64 / CH::P(0), S1 = 64 / CH::P(NCH > 1 ? 1 : 0);
-        constexpr int S2 = 64 / CH::P(NCH > 2 ? 2 : 0), S3 = 64 / CH::P(NCH > 3 ? 3 : 0);
+        if (A) wy_layout_sums<TM, !BF16 && TM == 16, true>(r, xf, kf, d, lane);
+        else wy_layout_sums<TM, !BF16 && TM == 16, false>(r, xf, kf, d, lane);
+        // lanes holding one sum of chunk k
+        constexpr int SP[6] = {64 / CH::P(0), 64 / CH::P(NCH > 1 ? 1 : 0), 64 / CH::P(NCH > 2 ? 2 : 0),
+                               64 / CH::P(NCH > 3 ? 3 : 0), 64 / CH::P(NCH > 4 ? 4 : 0), 64 / CH::P(NCH > 5 ? 5 : 0)};
 #pragma unroll
         for (int k = 0; k < NCH; ++k) {
-            const int sp = k == 0 ? S0 : k == 1 ? S1 : k == 2 ? S2 : S3;  // lanes holding one sum
+            const int sp = SP[k];
             if ((lane & (sp - 1)) == 0) s_sum[A ? 0 : 1][wave & 1][64 * k + lane / sp] = r[k];
         }
         if (wave == 2 && lane < TM) {
@@ -1637,6 +1664,7 @@ kda_verify_wy_kernel(const RecParams p)
     }
     u32x4 raw1[NLD];  // the second tile
     load_tile(1, raw1);
+    if constexpr (V_LATE) load_v();
     __syncthreads();
 
     // coefficients (each wave its own copy): (t, s) = (e / TM, e % TM);
@@ -1644,7 +1672,10 @@ kda_verify_wy_kernel(const RecParams p)
     float *cf = s_cf[wave];
     {
         auto slot = [&](int t, bool a) {
-            const int k = t / CH::TPC, f = k * CH::TPC;
+            int k = 0, f = 0;  // t's chunk and the chunk's first token
+#pragma unroll
+            for (int kk = 1; kk < NCH; ++kk)
+                if (t >= CH::first(kk)) k = kk, f = CH::first(kk);
             return 64 * k + (t - f) * (f + t + (a ? 3 : 1)) / 2;
         };
         auto sum = [&](int a, int i) { return s_sum[a][0][i] + s_sum[a][1][i]; };
