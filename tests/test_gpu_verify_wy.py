@@ -297,3 +297,70 @@ def test_wy_verify_t16_with_underflowing_decay():
     assert torch.isfinite(out.float()).all() and torch.isfinite(corr).all()
     P.check_bf16_out(out, want["out64"])
     check_caches(corr, kg, want, recorded_mask(c, [T] * n, T))
+
+
+STRIDED = [  # T, state dtype, ragged
+    (4, torch.float32, False),
+    (8, torch.float32, False),
+    (16, torch.float32, False),
+    (16, torch.bfloat16, False),
+    (12, torch.float32, True),
+]
+
+
+@pytest.mark.parametrize("T,state_dtype,ragged", STRIDED,
+                         ids=[f"T{c[0]}-{'bf16' if c[1] == torch.bfloat16 else 'fp32'}-{'ragged' if c[2] else 'batched'}"
+                              for c in STRIDED])
+def test_wy_verify_with_strided_inputs(T, state_dtype, ragged):
+    """Token inputs read through padded row strides: q, k, v and the gate
+    as column blocks of one bf16 row per token (with padding between
+    tokens), beta as the first HV entries of a wider row.  The kernel
+    addresses a sequence's rows by 32-bit offsets from its first row; the
+    results equal the oracle on the same values, and the pool is untouched."""
+    import random
+    n, H, HV, slots, t_max = 6, 4, 8, 16, T
+    seed = 7800 + T + (1 if ragged else 0)
+    if ragged:
+        rng = random.Random(seed)
+        lengths = [rng.randint(0, T) for _ in range(n)]
+        lengths[0] = T
+    else:
+        lengths = [T] * n
+    say(f"WY verify strided inputs T={T} {state_dtype} ragged={ragged} lengths={lengths} seed={seed}")
+    c = synth.recurrent_case(seed, n_seqs=n, H=H, HV=HV, num_slots=slots, state_dtype=state_dtype, device=DEV,
+                             indices="random", lengths=lengths, null_rows=1, gate="in_kernel",
+                             gate_dtype=torch.bfloat16)
+    Tt = c.q.shape[0]
+    HC, VC = H * D, HV * D
+    row = 2 * HC + 2 * VC + 96  # q | k | v | g | padding
+    buf = torch.full((Tt, row), float("nan"), dtype=torch.bfloat16, device=DEV)
+    q = buf[:, :HC].view(Tt, H, D)
+    k = buf[:, HC:2 * HC].view(Tt, H, D)
+    v = buf[:, 2 * HC:2 * HC + VC].view(Tt, HV, D)
+    g = buf[:, 2 * HC + VC:2 * HC + 2 * VC].view(Tt, HV, D)
+    for dst, src in ((q, c.q), (k, c.k), (v, c.v), (g, c.g)):
+        dst.copy_(src)
+    bbuf = torch.full((Tt, HV + 24), float("nan"), dtype=torch.bfloat16, device=DEV)
+    beta = bbuf[:, :HV]
+    beta.copy_(c.beta)
+    st0 = c.state.clone()
+    want = reference(c, np_(st0), t_max=t_max, ragged=ragged, read_only=True, tps=1 if ragged else T)
+    corr = torch.full((slots, HV, t_max, D), -777.0, dtype=torch.float32, device=DEV)
+    if ragged:
+        shp = lambda t: t.view(1, Tt, *t.shape[1:])  # noqa: E731
+        out = recurrent_kda(shp(q), shp(k), shp(v), shp(g), shp(beta), c.A_log, c.dt_bias, initial_state=c.state,
+                            state_indices=c.state_indices, cu_seqlens=c.cu_seqlens, disable_state_update=True,
+                            correction_cache=corr, max_seqlen=T)
+    else:
+        shp = lambda t: t.view(n, T, *t.shape[1:])  # noqa: E731
+        out = recurrent_kda(shp(q), shp(k), shp(v), shp(g), shp(beta), c.A_log, c.dt_bias, initial_state=c.state,
+                            state_indices=c.state_indices, disable_state_update=True, correction_cache=corr)
+    torch.cuda.synchronize()
+    assert torch.equal(P.bits(st0), P.bits(c.state)), "read-only pool changed"
+    e1 = P.check_bf16_out(out.reshape(Tt, HV, D), want["out64"])
+    m = recorded_mask(c, lengths, t_max)
+    got = corr.cpu().numpy().astype(np.float64)
+    mm = np.broadcast_to(m[:, None, :], got.shape[:3])
+    assert np.abs(got[mm] - want["corr"][mm]).max() <= P.F32_STATE_ATOL
+    assert np.all(got[~mm] == -777.0)
+    say(f"out err {e1:.3e}")
