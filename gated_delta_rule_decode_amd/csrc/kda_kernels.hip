@@ -1668,7 +1668,10 @@ kda_verify_wy_kernel(const RecParams p)
     __syncthreads();
 
     // coefficients (each wave its own copy): (t, s) = (e / TM, e % TM);
-    // token t's first sum: its chunk, then the chunk's earlier tokens
+    // token t's first sum: its chunk, then the chunk's earlier tokens.  The
+    // per-token scalars first (lanes t < TM), then the T^2 coefficients,
+    // which read 1/|k_s| and 1/|k_t| from them instead of evaluating both
+    // again for every coefficient.
     float *cf = s_cf[wave];
     {
         auto slot = [&](int t, bool a) {
@@ -1679,20 +1682,21 @@ kda_verify_wy_kernel(const RecParams p)
             return 64 * k + (t - f) * (f + t + (a ? 3 : 1)) / 2;
         };
         auto sum = [&](int a, int i) { return s_sum[a][0][i] + s_sum[a][1][i]; };
-        auto rk_of = [&](int t) { return rsqrtf(sum(1, slot(t, false)) + p.l2_eps); };
+        float *rk = cf + 2 * TM * TM;
+        if (lane < TM && lane < it.n) {
+            rk[lane] = rsqrtf(sum(1, slot(lane, false)) + p.l2_eps);
+            rk[TM + lane] = rsqrtf(sum(0, slot(lane, true)) + p.l2_eps) * p.scale;
+            rk[2 * TM + lane] = s_beta[lane];
+        }
+        wave_lds_sync();
 #pragma unroll
         for (int e = lane; e < TM * TM; e += 64) {
             const int t = e / TM, s = e - (e / TM) * TM;
             if (t < it.n) {
-                const float rks = rk_of(s);
-                cf[e] = s < t ? rk_of(t) * rks * sum(1, slot(t, false) + 1 + s) : 0.f;
+                const float rks = rk[s];
+                cf[e] = s < t ? rk[t] * rks * sum(1, slot(t, false) + 1 + s) : 0.f;
                 cf[TM * TM + e] = s <= t ? rks * sum(0, slot(t, true) + 1 + s) : 0.f;
             }
-        }
-        if (lane < TM && lane < it.n) {
-            cf[2 * TM * TM + lane] = rk_of(lane);
-            cf[2 * TM * TM + TM + lane] = rsqrtf(sum(0, slot(lane, true)) + p.l2_eps) * p.scale;
-            cf[2 * TM * TM + 2 * TM + lane] = s_beta[lane];
         }
     }
 
