@@ -69,13 +69,14 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// Two floats -> two bf16 (round to nearest even), low half first.
+// Two floats -> two bf16 (round to nearest even), low half first: built as
+// a two-element vector, which is one v_cvt_pk_bf16_f32 of both values (two
+// scalar conversions joined by a shift and an or took four instructions).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 {
-    const __bf16 a = (__bf16)lo;
-    const __bf16 b = (__bf16)hi;
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) |
-           ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+    const bf16x2 v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
 }
 
 // Lanes of one wave hand data to each other through LDS: the release fence
@@ -1758,14 +1759,19 @@ kda_verify_wy_kernel(const RecParams p)
                     const int jb = 2 * hh + j2, c0 = 8 * j2 + 2 * grp;
                     const f32x4 x0 = *reinterpret_cast<const f32x4 *>(buf + 4 * (16 * n16 + (c0 ^ n16)));
                     const f32x4 x1 = *reinterpret_cast<const f32x4 *>(buf + 4 * (16 * n16 + ((c0 + 1) ^ n16)));
-                    bf16x8 ah, al;
+                    // (a pair's heads packed once and unpacked by shifts:
+                    // converting each value on its own and packing again
+                    // took a third more instructions)
+                    u32x4 hw, lw;
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const float x = e < 4 ? x0[e] : x1[e - 4];
-                        const __bf16 h = (__bf16)x;
-                        ah[e] = h;
-                        al[e] = (__bf16)(x - (float)h);
+                    for (int e2 = 0; e2 < 4; ++e2) {
+                        const float xa = e2 < 2 ? x0[2 * e2] : x1[2 * e2 - 4];
+                        const float xb = e2 < 2 ? x0[2 * e2 + 1] : x1[2 * e2 - 3];
+                        const uint32_t h = pack_bf16x2(xa, xb);
+                        hw[e2] = h;
+                        lw[e2] = pack_bf16x2(xa - __uint_as_float(h << 16), xb - __uint_as_float(h & 0xffff0000u));
                     }
+                    const bf16x8 ah = __builtin_bit_cast(bf16x8, hw), al = __builtin_bit_cast(bf16x8, lw);
 #pragma unroll
                     for (int kc = 0; kc < NCT; ++kc) {
                         const int cc = 16 * kc + n16;
