@@ -1460,11 +1460,14 @@ struct WyLayout {
 //     matrix-core layout through the wave's LDS buffer in passes of 16
 //     columns of 16 bytes (bf16 pools: the exact state by the operand's
 //     head and remainder, two bf16 products; fp32 pools: fp32 products,
-//     4x4x1 when at most 8 operand columns exist), the products through LDS
-//     into a row-per-lane layout, then the forward substitution (lanes l
-//     and l + 32 own row l & 31 and store alternate tokens).
-// Four to five workgroups share a compute unit (the VGPRs decide), so the
-// loads of one overlap the arithmetic of the others.  Consecutive heads
+//     4x4x1 when at most 8 operand columns exist; at 16 token slots bf16
+//     heads and remainders of both, three bf16 products), the products
+//     through LDS into a row-per-lane layout, then the forward substitution
+//     (lanes l and l + 32 own row l & 31; in each pair of tokens both
+//     compute the two corrections, the lower half of the wave stores the
+//     even token's output and correction, the upper half the odd one's).
+// Three to eight workgroups share a compute unit (the VGPRs and the LDS
+// decide), so the loads of one overlap the arithmetic of the others.  Consecutive heads
 // (which share their sequence's token rows) run on one XCD.  KGC: the call
 // records the raw key and gate cache (a kernel of its own, so that calls
 // without it carry none of its stores).
