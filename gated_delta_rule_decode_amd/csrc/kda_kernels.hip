@@ -1306,8 +1306,8 @@ __global__ void __launch_bounds__(2048 / (G * VS)) kda_packed_fused_kernel(const
 //
 // The products [k_t E_t ; q_t E_t] x S0 (2T x 128 by 128 x 128 per head) run
 // on the matrix cores; the T^2 W-weighted channel sums are reduced once per
-// head; each value row then runs a T-step forward substitution.  TM (2, 4, 8
-// or 16, the smallest that holds the declared length) sizes the token
+// head; each value row then runs a T-step forward substitution.  TM (2, 4,
+// 8, 12 or 16, the smallest that holds the declared length) sizes the token
 // registers and LDS.  Null rows give +0; in the ragged form, tokens past the
 // declared length give +0 and record nothing.
 constexpr int pow2_at_least(int x)
@@ -1330,14 +1330,14 @@ constexpr int pow2_at_least(int x)
 template <int TM, bool SIX>
 struct WyChunks {
     static_assert(!SIX || TM == 16, "six chunks: 16 token slots");
-    static constexpr int NCH = SIX ? 6 : (TM > 4 ? TM / 4 : 1);
+    static constexpr int NCH = SIX ? 6 : (TM > 4 ? (TM + 3) / 4 : 1);
     static constexpr int first(int k)
     {
         if (SIX) {
             constexpr int b[7] = {0, 6, 9, 11, 13, 15, 16};
             return b[k];
         }
-        return k * (TM > 4 ? 4 : TM);
+        return TM > 4 ? (4 * k < TM ? 4 * k : TM) : k * TM;
     }
     static constexpr int chunk_of(int t)
     {
@@ -1460,7 +1460,7 @@ struct WyLayout {
 //     matrix-core layout through the wave's LDS buffer in passes of 16
 //     columns of 16 bytes (bf16 pools: the exact state by the operand's
 //     head and remainder, two bf16 products; fp32 pools: fp32 products,
-//     4x4x1 when at most 8 operand columns exist; at 16 token slots bf16
+//     4x4x1 when at most 8 operand columns exist; from 12 token slots bf16
 //     heads and remainders of both, three bf16 products), the products
 //     through LDS into a row-per-lane layout, then the forward substitution
 //     (lanes l and l + 32 own row l & 31; in each pair of tokens both
@@ -1539,10 +1539,10 @@ kda_verify_wy_kernel(const RecParams p)
     const bool g_f32 = p.g_f32 != 0;
     const bool beta_f32 = p.beta_f32 != 0;
     uint32_t xb[TM], kb[TM], glo[TM], ghi[TM], vb[TM];
-    // the value rows' inputs, used only by the forward substitution: at 16
-    // token slots loaded after the channel phase (with the second tile), so
-    // that they hold no registers through it
-    constexpr bool V_LATE = TM == 16;
+    // the value rows' inputs, used only by the forward substitution: from 12
+    // token slots on loaded after the channel phase (with the second tile),
+    // so that they hold no registers through it
+    constexpr bool V_LATE = TM >= 12;
     auto load_v = [&]() {
 #pragma unroll
         for (int t = 0; t < TM; ++t)
@@ -1965,7 +1965,9 @@ int launch_recurrent(const RecParams &p, const Launch &l, void *stream)
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();  // a stale error must not be blamed on this launch
     if (l.family == KERNEL_VERIFY_WY) {
-        // token slots sized to the declared length: 2, 4, 8 or 16, the smallest that holds it
+        // token slots sized to the declared length: 2, 4, 8, 12 or 16, the smallest that holds it
+        // (12 slots: T=12 fp32 41.6 against 45.1 us on 16, bf16 29.6 against 35.8; 6 slots measured
+        // no faster than 8)
         const dim3 grid(l.grid), block(l.block);
 #define KDA_WY(TM_)                                                                                      \
     do {                                                                                                 \
@@ -1980,6 +1982,7 @@ int launch_recurrent(const RecParams &p, const Launch &l, void *stream)
         if (p.tps <= 2) KDA_WY(2);
         else if (p.tps <= 4) KDA_WY(4);
         else if (p.tps <= 8) KDA_WY(8);
+        else if (p.tps <= 12) KDA_WY(12);
         else KDA_WY(16);
 #undef KDA_WY
         return record(hipGetLastError());
