@@ -78,8 +78,11 @@ CASES = [  # T, state dtype, gate, gate dtype, H, HV, cache length
     (7, torch.float32, "precomputed", torch.float32, 4, 12, 7),
     (8, torch.bfloat16, "in_kernel", torch.bfloat16, 4, 8, 8),
     (8, torch.float32, "in_kernel", torch.bfloat16, 6, 12, 6),
+    (9, torch.float32, "in_kernel", torch.float32, 4, 4, 9),
     (10, torch.bfloat16, "in_kernel", torch.bfloat16, 2, 4, 16),
+    (11, torch.bfloat16, "precomputed", torch.float32, 4, 8, 6),
     (12, torch.float32, "in_kernel", torch.bfloat16, 4, 8, 12),
+    (12, torch.bfloat16, "in_kernel", torch.float32, 8, 8, 12),
     (13, torch.float32, "precomputed", torch.bfloat16, 4, 12, 5),
     (16, torch.bfloat16, "precomputed", torch.float32, 4, 4, 9),
     (16, torch.float32, "in_kernel", torch.bfloat16, 8, 8, 16),
@@ -114,12 +117,12 @@ def test_wy_verify_against_oracle(T, state_dtype, gate, gate_dtype, H, HV, t_max
 
 
 @pytest.mark.parametrize("T,state_dtype", [(2, torch.float32), (4, torch.float32), (6, torch.float32),
-                                           (6, torch.bfloat16), (16, torch.float32)])
+                                           (6, torch.bfloat16), (11, torch.float32), (16, torch.float32)])
 def test_wy_verify_with_underflowing_decay(T, state_dtype):
     """Log-decays of -20..-90 per token: the cumulative decay underflows to
     zero in fp32 within a token or two; outputs and corrections stay finite
     and match the oracle (every product form: fp32 4x4x1 at 2 and 4 tokens,
-    16x16x4 at 6, the bf16 split at 16, bf16 pools)."""
+    16x16x4 at 6, the bf16 split at 11 (12 token slots) and 16, bf16 pools)."""
     n, H, slots = 7, 4, 12
     say(f"WY verify underflowing decay T={T} H={H} {state_dtype} seed=7700")
     c = synth.recurrent_case(7700, n_seqs=n, H=H, num_slots=slots, state_dtype=state_dtype, device=DEV,
@@ -226,6 +229,7 @@ RAGGED = [  # max_seqlen, state dtype, gate, gate dtype, H, HV, cache length, se
     (6, torch.bfloat16, "in_kernel", torch.bfloat16, 4, 8, 4, 7611),
     (8, torch.float32, "precomputed", torch.float32, 2, 8, 8, 7612),
     (12, torch.bfloat16, "precomputed", torch.bfloat16, 4, 4, 12, 7613),
+    (10, torch.float32, "in_kernel", torch.bfloat16, 4, 8, 10, 7616),
     (16, torch.float32, "in_kernel", torch.bfloat16, 4, 8, 7, 7614),
     (16, torch.bfloat16, "in_kernel", torch.float32, 8, 8, 16, 7615),
 ]
